@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+Metric: MoE-layer decode tokens/s + HBM GB/s (% of peak); prefill MFMA util.
+
+Workload (the step): one decode forward of the layer H=6144, I=2048, E=256 routed
+experts (top-8) + 1 shared expert, int4-g64 planar weights, T=1 fp32 token:
+router logits -> top-K + renormalised gates -> permute -> gate/up GEMV + SiLU*up ->
+down GEMV + gate-weighted combine + shared expert.  Inputs are resident in HBM
+before the timed region.  Steps rotate over 8 byte-identical replicas of the layer
+(43.7 GB) and a pool of 64 tokens, so the 256 MB Infinity Cache cannot serve the
+~191 MB a token touches.
+
+Printed: one JSON line (rank 0).  Extra fields: per-stage times and the roofline
+of the dominant kernel (gate/up GEMV, timed with HIP events on the library's
+stream), the T=32 Zipf decode batch, the T=2048 prefill (MFMA utilisation of the
+grouped GEMMs), and the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+METRIC = "MoE-layer decode tokens/s + HBM GB/s (% of peak); prefill MFMA util"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_layer(coli, W, cfg_id, replicas):
+    import torch
+    c = W.CONFIGS[cfg_id]
+    H, I, E, K = c["H"], c["I"], c["E"], c["K"]
+    experts, shared, nb = coli.alloc_layer_blobs(H, I, E)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for e in range(E + 1):
+        wg, wu, wd = W.expert_weights(cfg_id, e, "cuda")
+        ptr = shared.data_ptr() if e == E else experts.data_ptr() + e * nb
+        coli.coli_quant_expert(ptr, H, I, wg, wu, wd, status)
+        del wg, wu, wd
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    wr = W.router_weights(cfg_id, "cuda").contiguous()
+    b = W.router_bias(cfg_id)
+    bias = None if b is None else torch.from_numpy(b).cuda()
+    layers = [coli.MoELayer(H, I, E, K, wr, experts, shared, bias)]
+    for _ in range(replicas - 1):
+        layers.append(coli.MoELayer(H, I, E, K, wr.clone(), experts.clone(), shared.clone(),
+                                    None if bias is None else bias.clone()))
+    torch.cuda.synchronize()
+    return layers, nb
+
+
+class Caller:
+    """Pre-marshalled coli_moe_forward(_timed) calls (keeps host overhead small)."""
+
+    def __init__(self, coli, layer, mode, x, y, ws, idx, gates):
+        import torch
+        self.coli, self.layer, self.mode = coli, layer, mode
+        self.args = [ctypes.byref(layer.c), mode, ctypes.c_void_p(x.data_ptr()), x.shape[0],
+                     ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
+                     ctypes.c_void_p(gates.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                     ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)]
+
+    def __call__(self):
+        st = self.coli.lib.coli_moe_forward(*self.args)
+        if st:
+            raise RuntimeError(f"coli_moe_forward: {st}")
+
+    def timed(self, evarr, n):
+        st = self.coli.lib.coli_moe_forward_timed(*self.args, evarr, n)
+        if st:
+            raise RuntimeError(f"coli_moe_forward_timed: {st}")
+
+
+def make_events(n):
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev:
+        e.record()  # torch creates the HIP event on first record
+    arr = (ctypes.c_void_p * n)(*[ctypes.c_void_p(e.cuda_event) for e in ev])
+    return ev, arr
+
+
+def run_decode(coli, W, layers, cfg_id, T, steps, warmup, pool_n=64):
+    """Time `steps` decode forwards; returns dict with value and per-stage times."""
+    import torch
+    c = W.CONFIGS[cfg_id]
+    H, K = c["H"], c["K"]
+    pool = W.token_pool(cfg_id, pool_n * T, "cuda").reshape(pool_n, T, H).contiguous()
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(layers[0].workspace_bytes(T, coli.COLI_DECODE), dtype=torch.uint8,
+                     device="cuda")
+    R = len(layers)
+    callers = [[Caller(coli, layers[r], coli.COLI_DECODE, pool[p], y, ws, idx, gates)
+                for p in range(pool_n)] for r in range(R)]
+
+    def call(i):
+        callers[i % R][i % pool_n]()
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        call(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    # per-stage durations, HIP events recorded by the library between its stages
+    nst = min(steps, 400)
+    evs = [make_events(3) for _ in range(nst)]
+    st_start = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(50_000_000)  # let the host queue run ahead of the GPU
+    st_start.record()
+    for i in range(nst):
+        callers[i % R][i % pool_n].timed(evs[i][1], 3)
+    torch.cuda.synchronize()
+    stage = [0.0, 0.0, 0.0]
+    prev = st_start
+    for ev, _ in evs:
+        stage[0] += prev.elapsed_time(ev[0])
+        stage[1] += ev[0].elapsed_time(ev[1])
+        stage[2] += ev[1].elapsed_time(ev[2])
+        prev = ev[2]
+    stage = [s / nst for s in stage]
+    nu = int(torch.unique(idx).numel())
+    return dict(ms=ms, wall=wall, steps=steps, stage_ms=stage, T=T, n_unique_last=nu,
+                idx_last=idx.cpu())
+
+
+def decode_bytes(c, U, T):
+    """Algorithmic HBM bytes of one decode forward: router, unique experts + shared, x, y."""
+    H, I, E = c["H"], c["I"], c["E"]
+    blob = 3 * (I * (H // 64) * 32 + I * (H // 64) * 4)  # gate+up+down nibbles and scales
+    router = E * H * (2 if c["router"] == "bf16" else 4)
+    return router + (U + 1) * blob + 2 * T * H * 4
+
+
+def gateup_bytes(c, U, T):
+    H, I = c["H"], c["I"]
+    per = 2 * (I * (H // 64) * 32 + I * (H // 64) * 4)
+    return (U + 1) * per + T * H * 4 + (T * c["K"] + T) * I * 4
+
+
+def run_prefill(coli, W, layer, steps=10, warmup=2):
+    import torch
+    c = W.CONFIGS[3]
+    T, H, K = c["T"], c["H"], c["K"]
+    x = W.tokens(3, T, "cuda")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(layer.workspace_bytes(T, coli.COLI_PREFILL), dtype=torch.uint8,
+                     device="cuda")
+    call = Caller(coli, layer, coli.COLI_PREFILL, x, y, ws, idx, gates)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    stage = [0.0] * 5
+    for _ in range(steps):
+        s0 = torch.cuda.Event(enable_timing=True)
+        ev, arr = make_events(5)
+        s0.record()
+        call.timed(arr, 5)
+        torch.cuda.synchronize()
+        prev = s0
+        for i in range(5):
+            stage[i] += prev.elapsed_time(ev[i])
+            prev = ev[i]
+    stage = [s / steps for s in stage]
+    flops_routed = 2.0 * T * K * 3 * H * c["I"]
+    flops_shared = 2.0 * T * 3 * H * c["I"]
+    gemm_ms = stage[2] + stage[3]
+    tflops = (flops_routed + flops_shared) / (gemm_ms * 1e-3) / 1e12
+    return dict(ms_per_forward=round(ms, 4), tokens_per_s=round(T / (ms * 1e-3), 1),
+                stage_ms=dict(route=round(stage[0], 4), prep=round(stage[1], 4),
+                              gateup=round(stage[2], 4), down=round(stage[3], 4),
+                              combine=round(stage[4], 4)),
+                grouped_gemm_tflops=round(tflops, 1),
+                mfma_frac=round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                whole_forward_mfma_frac=round(
+                    (flops_routed + flops_shared + 2.0 * T * H * c["E"]) / (ms * 1e-3) / 1e12
+                    / MFMA_F16_PEAK_TFLOPS, 4),
+                flops=flops_routed + flops_shared, dtype="fp16 MFMA operands (bf16 I/O)")
+
+
+def cpu_baseline(coli, W, budget_s=12.0):
+    """The oracle (fp64, as committed) on a bounded sample of decode tokens."""
+    import numpy as np
+    import oracle
+    import torch
+    c = W.CONFIGS[1]
+    H, I, E, K = c["H"], c["I"], c["E"], c["K"]
+    wr = W.router_weights(1, "cuda")
+    wr_h = wr.cpu().view(torch.int16).numpy().view(np.uint16)
+    pool = W.token_pool(1, 64, "cuda").cpu().numpy()
+    # experts the sampled tokens need, quantised by the oracle itself (not timed)
+    n_tok = 24
+    logits = oracle.router_logits(pool[:n_tok], wr_h, None)
+    idx, _, _ = oracle.topk(logits, K)
+    need = sorted(set(idx.reshape(-1).tolist()))
+    experts = [None] * E
+    for e in need:
+        experts[e] = oracle.Expert.quantise(*(w.cpu().numpy() for w in W.expert_weights(1, e, "cuda")))
+    shared = oracle.Expert.quantise(*(w.cpu().numpy() for w in W.expert_weights(1, E, "cuda")))
+    done = 0
+    t0 = time.perf_counter()
+    while done < n_tok and (time.perf_counter() - t0) < budget_s:
+        oracle.moe_forward(pool[done:done + 1], wr_h, None, experts, shared, H, I, K)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{done} decode tokens (T=1 each) of the same layer, fp64, "
+                      f"{el:.1f} s; experts quantised by the oracle beforehand (untimed)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the T=32 and prefill legs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the expert-parallel design for more GPUs is described, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import int4_grouped_expert_amd as coli
+    import workloads as W
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    c = W.CONFIGS[1]
+
+    log(f"[bench] building layer ({args.replicas} replicas)")
+    layers, nb = build_layer(coli, W, 1, args.replicas)
+    log("[bench] decode T=1")
+    d = run_decode(coli, W, layers, 1, 1, args.steps, args.warmup)
+    ms_step = d["ms"] / d["steps"]
+    U = 8  # T=1, top-8: always 8 distinct routed experts + the shared one
+    step_bytes = decode_bytes(c, U, 1)
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    gu_bytes = gateup_bytes(c, U, 1)
+    gu_ms = d["stage_ms"][1]
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(1.0 / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode: MoE layer H=6144 I=2048, 256 routed experts top-8 + 1 "
+                               "shared, int4-g64 planar, T=1 fp32 token",
+                   "replicas": args.replicas, "token_pool": 64},
+        "hbm": {"bytes_per_step": step_bytes, "gbps": round(gbps, 1),
+                "frac": round(gbps / HBM_PEAK_GBS, 4)},
+        "stage_ms": {"route": round(d["stage_ms"][0], 5), "gateup": round(d["stage_ms"][1], 5),
+                     "down_combine": round(d["stage_ms"][2], 5)},
+        "roofline": {"kernel": "gateup_decode_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gu_bytes},
+    }
+    if not args.no_extras:
+        log("[bench] decode T=32 zipf")
+        zl, _ = build_layer_bias(coli, W, layers)
+        d32 = run_decode(coli, W, zl, 2, 32, max(200, args.steps // 10), 20)
+        U32 = int(torch.unique(d32["idx_last"]).numel())
+        ms32 = d32["ms"] / d32["steps"]
+        b32 = decode_bytes(W.CONFIGS[2], U32, 32)
+        result["decode_t32_zipf"] = {
+            "tokens_per_s": round(32 / (ms32 * 1e-3), 1), "ms_per_step": round(ms32, 4),
+            "unique_experts_last_step": U32,
+            "gbps": round(b32 / (ms32 * 1e-3) / 1e9, 1),
+            "frac": round(b32 / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stage_ms": [round(s, 4) for s in d32["stage_ms"]]}
+        del zl
+        log("[bench] prefill T=2048")
+        result["prefill"] = run_prefill(coli, W, layers[0])
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(coli, W)
+    print(json.dumps(result), flush=True)
+
+
+def build_layer_bias(coli, W, layers):
+    """The T=32 workload shares the decode layer's weights, with the Zipf router bias."""
+    import torch
+    b = torch.from_numpy(W.router_bias(2)).cuda()
+    out = []
+    for L in layers:
+        out.append(coli.MoELayer(L.H, L.I, L.E, L.K, L.w_router, L.experts, L.shared, b))
+    return out, None
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,250 @@
+/*
+ * coli.h -- C ABI of libcoli.so: the routed-expert MoE layer with int4-g64
+ * planar experts, on one AMD MI355X (gfx950).
+ *
+ * The layer (sources cited by page title and section):
+ *   route   -- page "Colibri 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
+ *              section 十一: the router picks the top-k experts of each token;
+ *              gates are the normalised values the layer applies (page
+ *              "colibri 路由遥测全解析", section 分离计数与追踪).
+ *   union   -- page "Colibri 深度解析", section 四: positions of a batch routed
+ *              to one expert are grouped so that the expert is read once.
+ *   experts -- page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
+ *              section 权重转换: int4 grouped weights, group 64, one fp32 scale
+ *              per group, q = clip(rint(w/s), -8, 7) stored as unsigned q+8,
+ *              planar nibbles (byte k of a 64-group: element k in the low
+ *              nibble, element k+32 in the high nibble); the expert FFN reads
+ *              these bytes directly.  An expert's gate, up and down matrices
+ *              sit side by side (page "Colibri 深度解析", section 四).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, unless a
+ *     comment says "host".  The library never allocates, frees or
+ *     synchronises; all work is enqueued on `stream` (a hipStream_t passed
+ *     as void*, NULL = the default stream) and is asynchronous.
+ *   - Fail closed (the pages' guard convention, page "Colibri 深度解析",
+ *     section 十五, and page "colibri 路由遥测全解析", section 测试与 CI 保障):
+ *     every argument check runs on the host before the first launch; on any
+ *     error the call returns a negative status and writes nothing.
+ *   - A launch failure reported by the HIP runtime returns COLI_EDEVICE.
+ *   - Row-major layouts throughout.  Calls are reentrant: the library has no
+ *     global mutable state; concurrent calls must not share output or
+ *     workspace buffers.
+ */
+#ifndef COLI_H
+#define COLI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    COLI_OK = 0,
+    COLI_EINVAL = -1,     /* NULL pointer or invalid enum / parameter value */
+    COLI_ESHAPE = -2,     /* a dimension is out of its valid range */
+    COLI_EALIGN = -3,     /* a pointer is not aligned as required */
+    COLI_EDTYPE = -4,     /* dtype not supported for this call / mode */
+    COLI_EWORKSPACE = -5, /* workspace NULL or smaller than required */
+    COLI_EDEVICE = -6     /* the HIP runtime reported a launch error */
+};
+
+typedef enum { COLI_F32 = 0, COLI_BF16 = 1 } coli_dtype;
+typedef enum { COLI_DECODE = 0, COLI_PREFILL = 1 } coli_mode;
+
+#define COLI_GROUP 64           /* elements per quantisation group */
+#define COLI_MAX_EXPERTS 1024   /* upper bound for E (and K) */
+#define COLI_MAX_DIM 65536      /* upper bound for H and I */
+#define COLI_MAX_TOKENS 65536   /* upper bound for T */
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *coli_strerror(int status);
+
+/* ---------------------------------------------------------------------- */
+/* int4-g64 planar format (page "从源码开始...", section 权重转换)          */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of packed nibbles for a [rows, cols] matrix: rows * ceil(cols/64) * 32.
+ * Returns 0 for rows < 0 or cols < 1 (no valid matrix). */
+size_t coli_int4_g64_packed_bytes(int64_t rows, int64_t cols);
+
+/* Number of fp32 scales for a [rows, cols] matrix: rows * ceil(cols/64). */
+size_t coli_int4_g64_scale_count(int64_t rows, int64_t cols);
+
+/*
+ * Quantise and pack one fp32 matrix W [rows, cols] (row-major).
+ *   packed [rows][ceil(cols/64)*32] u8  (16-byte aligned)
+ *   scales [rows][ceil(cols/64)]    f32
+ * Per row and per 64-group g along the columns (the last group is zero
+ * padded when cols is not a multiple of 64):
+ *   amax = max |w|, s = fl32(amax / 7) (IEEE fp32 divide),
+ *   q = clip(rint_half_even(fl32(w / s)), -8, 7), u = q + 8,
+ *   byte g*32+k = u[g*64+k] | u[g*64+k+32] << 4.
+ * A group whose scale is 0 stores nibbles 8.  A group holding NaN or Inf
+ * stores nibbles 8 and a NaN scale, and bit 0 of *status is OR-ed with 1
+ * (status: optional device int32; NULL to skip).  The output is bit-exact:
+ * same bytes and scale bits as the IEEE definition above.
+ * w must be 4-byte aligned; 16-byte rows (cols % 4 == 0) take the fast path.
+ * rows == 0 is a no-op (pointers may then be NULL).  Errors: EINVAL (NULL
+ * w/packed/scales with rows > 0), ESHAPE
+ * (rows < 0, cols < 1, rows*cols > 2^40), EALIGN.
+ */
+int coli_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
+                        uint8_t *packed, float *scales, int32_t *status,
+                        void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* route (page "Colibri 深度解析", section 十一)                           */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Router logits and top-K with renormalised gates for T tokens.
+ *   x        [T, H]  fp32 or bf16 (x_dtype), rows 16-byte aligned
+ *   w_router [E, H]  fp32 or bf16 (w_dtype)
+ *   bias     [E]     fp32, or NULL (added to the logits; used for selection
+ *                    and for the gates)
+ *   logits   [T, E]  fp32 output (required)
+ *   topk_idx [T, K]  int32 output: the K selected expert ids of each token
+ *                    in ascending id order
+ *   topk_gate[T, K]  fp32 output: softmax over the K selected logits (equal
+ *                    to the softmax over all E restricted to the selected
+ *                    and renormalised to sum 1), same order as topk_idx
+ * Selection: the K largest logits; on equal logits the lower id wins; NaN
+ * never wins.  A slot with no valid candidate (every remaining logit NaN)
+ * takes id k if free, else the lowest free id (page "colibri 路由遥测全解析",
+ * section 测试与 CI 保障); its gates are then unspecified.
+ * Requires H % 8 == 0.  Errors: EINVAL, ESHAPE (T outside [0, MAX_TOKENS],
+ * H outside [8, MAX_DIM] or H % 8, E outside [1, MAX_EXPERTS], K outside
+ * [1, E]), EDTYPE, EALIGN.  T == 0 is a no-op.
+ */
+int coli_router_topk(const void *x, coli_dtype x_dtype, int T, int H,
+                     const void *w_router, coli_dtype w_dtype, int E,
+                     const float *bias, int K, int32_t *topk_idx,
+                     float *topk_gate, float *logits, void *stream);
+
+/*
+ * Batch-union permute (page "Colibri 深度解析", section 四).
+ *   topk_idx [T, K] int32 input, ids in [0, E)
+ *   counts   [E]    int32: pairs (t, slot) routed to each expert
+ *   offsets  [E+1]  int32: exclusive running sum of counts
+ *   perm     [T*K]  int32: the pair indices p = t*K + slot sorted stably by
+ *                   expert id (expert e owns perm[offsets[e] .. offsets[e+1]))
+ *   unique   [E]    int32: experts with count > 0, ascending; entries past
+ *                   *n_unique are unspecified
+ *   n_unique [1]    int32
+ *   workspace: device scratch of coli_expert_permute_workspace_bytes(T, E)
+ *              bytes (0 for small T; then workspace may be NULL).
+ * Pairs whose id lies outside [0, E) are skipped (not counted, not placed);
+ * offsets[E] is the number of pairs placed.
+ * Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE.  T == 0 writes zero counts,
+ * zero offsets and n_unique = 0.
+ */
+size_t coli_expert_permute_workspace_bytes(int T, int E);
+int coli_expert_permute(const int32_t *topk_idx, int T, int K, int E,
+                        int32_t *counts, int32_t *offsets, int32_t *perm,
+                        int32_t *unique, int32_t *n_unique, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* the layer                                                               */
+/* ---------------------------------------------------------------------- */
+
+/* One quantised matrix: packed [rows][ceil(cols/64)*32] u8, scales
+ * [rows][ceil(cols/64)] f32. */
+typedef struct {
+    const uint8_t *q;
+    const float *s;
+} coli_q4;
+
+/*
+ * A MoE layer.  Host struct; the pointers in it are device pointers.
+ *   w_router [E, H] in router_dtype (fp32 or bf16); router_bias [E] or NULL.
+ *   experts: E expert blobs laid end to end, each coli_expert_blob_bytes(H,I)
+ *            bytes; shared: one blob of the same layout (the shared expert,
+ *            applied to every token with weight 1).  Both 256-byte aligned.
+ */
+typedef struct {
+    int H, I, E, K;
+    const void *w_router;
+    coli_dtype router_dtype;
+    const float *router_bias;
+    const uint8_t *experts;
+    const uint8_t *shared;
+} coli_moe_layer;
+
+/*
+ * Size of one expert blob.  Layout (each section starts on a 256-byte
+ * boundary): gate.q [I][GH*32] | up.q [I][GH*32] | down.q [H][GI*32] |
+ * gate.s [I][GH] | up.s [I][GH] | down.s [H][GI], with GH = ceil(H/64),
+ * GI = ceil(I/64).  gate/up are [I, H] (input dim H); down is [H, I].
+ * Returns 0 if H or I is outside [1, MAX_DIM].
+ */
+size_t coli_expert_blob_bytes(int H, int I);
+
+/* Views of the three matrices of the blob at `blob` (pure pointer
+ * arithmetic on the host; nothing is read).  Errors: EINVAL, ESHAPE. */
+int coli_expert_views(const uint8_t *blob, int H, int I, coli_q4 *gate,
+                      coli_q4 *up, coli_q4 *down);
+
+/* Workspace bytes coli_moe_forward needs for T tokens in `mode`
+ * (0 if the layer's shape is invalid). */
+size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int T, coli_mode mode);
+
+/*
+ * One forward pass of the layer for T tokens:
+ *   logits = x Wr^T + b; top-K with renormalised gates (as coli_router_topk);
+ *   batch-union permute (as coli_expert_permute);
+ *   per selected (token, expert): h = SiLU(Wg x) * (Wu x), o = Wd h, with
+ *     W = s * (u - 8) read from the planar bytes;
+ *   y[t] = sum_k gate[t,k] * o[t,k] + Wd_sh (SiLU(Wg_sh x) * (Wu_sh x)).
+ *   mode DECODE:  x, y fp32 [T, H]; h is held in fp32; aimed at small T,
+ *                 T <= 256.
+ *   mode PREFILL: x, y bf16 [T, H], T <= COLI_MAX_TOKENS; grouped GEMMs on
+ *                 the matrix cores with fp32 accumulation.  The products take
+ *                 fp16 operands: x converted from bf16 (exact for
+ *                 |x| in [2^-14, 65504]), weights s*(u-8) rounded once to
+ *                 fp16, h held in fp16; per-slot outputs are rounded to bf16
+ *                 before the combine.  Inputs or intermediates beyond the fp16
+ *                 range are outside this mode's contract.
+ *   topk_idx_out, topk_gate_out: optional [T, K] copies of the routing.
+ *   workspace: device scratch of at least coli_moe_workspace_bytes bytes,
+ *              256-byte aligned; its contents need no initialisation and are
+ *              undefined afterwards.
+ * Requires H % 64 == 0 and I % 64 == 0.  Errors: EINVAL, ESHAPE, EDTYPE,
+ * EALIGN (x, y 16-byte, blobs and workspace 256-byte), EWORKSPACE, EDEVICE.
+ * T == 0 is a no-op.
+ */
+int coli_moe_forward(const coli_moe_layer *L, coli_mode mode, const void *x,
+                     int T, void *y, int32_t *topk_idx_out,
+                     float *topk_gate_out, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
+ * coli_moe_forward with stage timestamps, for measurement: after each stage
+ * the call records events[i] (hipEvent_t values created by the caller, passed
+ * as void*) on `stream`.  Stages: DECODE 0 route (logits, top-K, permute),
+ * 1 gate/up, 2 down + combine; PREFILL 0 route, 1 activation conversion and
+ * tile list, 2 gate/up, 3 down, 4 combine.  n_events must be at least the
+ * stage count (3 or 5).  Same work and results as coli_moe_forward.
+ * Errors: as coli_moe_forward, plus EINVAL for a NULL or short event array.
+ */
+int coli_moe_forward_timed(const coli_moe_layer *L, coli_mode mode,
+                           const void *x, int T, void *y,
+                           int32_t *topk_idx_out, float *topk_gate_out,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream, void **events, int n_events);
+
+/*
+ * RMSNorm with unit weight between stacked layers:
+ *   y[t] = x[t] / sqrt(mean(x[t]^2) + eps), fp32 [T, H]; x == y allowed.
+ * Errors: EINVAL (NULL, eps < 0 or not finite), ESHAPE.  T == 0 is a no-op.
+ */
+int coli_rmsnorm_f32(const float *x, float *y, int T, int H, float eps,
+                     void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COLI_H */

@@ -1,0 +1,238 @@
+"""Python binding of libcoli.so: the routed-expert MoE layer with int4-g64 planar
+experts on one MI355X (gfx950).
+
+Argument marshalling only.  Every step of the layer runs in the library's HIP
+kernels; this module turns torch tensors into device pointers and sizes, passes
+the current HIP stream, and raises on a non-zero status.  There is no fallback:
+if ``libcoli.so`` is missing, importing this package fails.
+
+The functions carry the C names (see ``include/coli.h`` for the contracts and the
+citations of the passages each operation follows).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libcoli.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+
+lib = ctypes.CDLL(_LIB_PATH)
+
+COLI_OK, COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN = 0, -1, -2, -3
+COLI_EDTYPE, COLI_EWORKSPACE, COLI_EDEVICE = -4, -5, -6
+COLI_F32, COLI_BF16 = 0, 1
+COLI_DECODE, COLI_PREFILL = 0, 1
+COLI_MAX_EXPERTS = 1024
+COLI_MAX_DIM = 65536
+COLI_MAX_TOKENS = 65536
+COLI_MAX_DECODE_T = 256
+
+EXPORTS = [
+    "coli_strerror", "coli_int4_g64_packed_bytes", "coli_int4_g64_scale_count",
+    "coli_quant_int4_g64", "coli_router_topk", "coli_expert_permute_workspace_bytes",
+    "coli_expert_permute", "coli_expert_blob_bytes", "coli_expert_views",
+    "coli_moe_workspace_bytes", "coli_moe_forward", "coli_moe_forward_timed",
+    "coli_rmsnorm_f32",
+]
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class coli_q4(ctypes.Structure):
+    _fields_ = [("q", _p), ("s", _p)]
+
+
+class coli_moe_layer(ctypes.Structure):
+    _fields_ = [("H", _i), ("I", _i), ("E", _i), ("K", _i), ("w_router", _p),
+                ("router_dtype", _i), ("router_bias", _p), ("experts", _p), ("shared", _p)]
+
+
+def _proto(name, res, args):
+    f = getattr(lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_proto("coli_strerror", ctypes.c_char_p, [_i])
+_proto("coli_int4_g64_packed_bytes", _sz, [_i64, _i64])
+_proto("coli_int4_g64_scale_count", _sz, [_i64, _i64])
+_proto("coli_quant_int4_g64", _i, [_p, _i64, _i64, _p, _p, _p, _p])
+_proto("coli_router_topk", _i, [_p, _i, _i, _i, _p, _i, _i, _p, _i, _p, _p, _p, _p])
+_proto("coli_expert_permute_workspace_bytes", _sz, [_i, _i])
+_proto("coli_expert_permute", _i, [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p])
+_proto("coli_expert_blob_bytes", _sz, [_i, _i])
+_proto("coli_expert_views", _i, [_p, _i, _i, ctypes.POINTER(coli_q4), ctypes.POINTER(coli_q4),
+                                 ctypes.POINTER(coli_q4)])
+_proto("coli_moe_workspace_bytes", _sz, [ctypes.POINTER(coli_moe_layer), _i, _i])
+_proto("coli_moe_forward", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p, _p, _sz,
+                                _p])
+_proto("coli_moe_forward_timed", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p,
+                                      _p, _sz, _p, ctypes.POINTER(_p), _i])
+_proto("coli_rmsnorm_f32", _i, [_p, _p, _i, _i, ctypes.c_float, _p])
+
+
+class ColiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib.coli_strerror(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> int:
+    if status != COLI_OK:
+        raise ColiError(status, where)
+    return status
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return COLI_F32
+    if t.dtype == torch.bfloat16:
+        return COLI_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------- format helpers
+
+def coli_int4_g64_packed_bytes(rows: int, cols: int) -> int:
+    return int(lib.coli_int4_g64_packed_bytes(rows, cols))
+
+
+def coli_int4_g64_scale_count(rows: int, cols: int) -> int:
+    return int(lib.coli_int4_g64_scale_count(rows, cols))
+
+
+def coli_expert_blob_bytes(H: int, I: int) -> int:
+    return int(lib.coli_expert_blob_bytes(H, I))
+
+
+def coli_expert_views(blob_ptr: int, H: int, I: int):
+    """Device addresses of ((gate.q, gate.s), (up.q, up.s), (down.q, down.s))."""
+    g, u, d = coli_q4(), coli_q4(), coli_q4()
+    _check(lib.coli_expert_views(ctypes.c_void_p(blob_ptr), H, I, ctypes.byref(g),
+                                 ctypes.byref(u), ctypes.byref(d)), "coli_expert_views")
+    return (g.q, g.s), (u.q, u.s), (d.q, d.s)
+
+
+# ---------------------------------------------------------------- entry points
+
+def coli_quant_int4_g64(w, packed, scales, status=None, stream=None):
+    """w fp32 [rows, cols] (device) -> packed u8 [rows, G*32], scales f32 [rows, G]."""
+    rows, cols = w.shape
+    return _check(lib.coli_quant_int4_g64(_ptr(w), rows, cols, _ptr(packed), _ptr(scales),
+                                          _ptr(status), _stream(stream)), "coli_quant_int4_g64")
+
+
+def coli_router_topk(x, w_router, bias, K, topk_idx, topk_gate, logits, stream=None):
+    T, H = x.shape
+    E = w_router.shape[0]
+    return _check(lib.coli_router_topk(_ptr(x), _dtype(x), T, H, _ptr(w_router),
+                                       _dtype(w_router), E, _ptr(bias), K, _ptr(topk_idx),
+                                       _ptr(topk_gate), _ptr(logits), _stream(stream)),
+                  "coli_router_topk")
+
+
+def coli_expert_permute_workspace_bytes(T: int, E: int) -> int:
+    return int(lib.coli_expert_permute_workspace_bytes(T, E))
+
+
+def coli_expert_permute(topk_idx, E, counts, offsets, perm, unique, n_unique, workspace=None,
+                        stream=None):
+    T, K = topk_idx.shape
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return _check(lib.coli_expert_permute(_ptr(topk_idx), T, K, E, _ptr(counts), _ptr(offsets),
+                                          _ptr(perm), _ptr(unique), _ptr(n_unique),
+                                          _ptr(workspace), nbytes, _stream(stream)),
+                  "coli_expert_permute")
+
+
+class MoELayer:
+    """A layer's device tensors and the C struct describing them.
+
+    experts: uint8 tensor of E * coli_expert_blob_bytes(H, I) bytes (256-B aligned),
+    shared:  uint8 tensor of one blob; w_router: [E, H] fp32 or bf16; bias: [E] fp32 or None.
+    """
+
+    def __init__(self, H, I, E, K, w_router, experts, shared, bias=None):
+        self.H, self.I, self.E, self.K = H, I, E, K
+        self.w_router, self.experts, self.shared, self.bias = w_router, experts, shared, bias
+        self.c = coli_moe_layer(H, I, E, K, w_router.data_ptr(), _dtype(w_router),
+                                None if bias is None else bias.data_ptr(), experts.data_ptr(),
+                                shared.data_ptr())
+
+    def workspace_bytes(self, T: int, mode: int) -> int:
+        return int(lib.coli_moe_workspace_bytes(ctypes.byref(self.c), T, mode))
+
+
+def coli_moe_workspace_bytes(layer: MoELayer, T: int, mode: int) -> int:
+    return layer.workspace_bytes(T, mode)
+
+
+def coli_moe_forward(layer: MoELayer, mode: int, x, y, workspace, topk_idx=None,
+                     topk_gate=None, stream=None):
+    T = x.shape[0]
+    nbytes = workspace.numel() * workspace.element_size()
+    return _check(lib.coli_moe_forward(ctypes.byref(layer.c), mode, _ptr(x), T, _ptr(y),
+                                       _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace), nbytes,
+                                       _stream(stream)), "coli_moe_forward")
+
+
+def coli_moe_forward_timed(layer: MoELayer, mode: int, x, y, workspace, events, topk_idx=None,
+                           topk_gate=None, stream=None):
+    """events: torch.cuda.Event objects (timing enabled), 3 (decode) or 5 (prefill)."""
+    T = x.shape[0]
+    nbytes = workspace.numel() * workspace.element_size()
+    arr = (_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    return _check(lib.coli_moe_forward_timed(ctypes.byref(layer.c), mode, _ptr(x), T, _ptr(y),
+                                             _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace),
+                                             nbytes, _stream(stream), arr, len(events)),
+                  "coli_moe_forward_timed")
+
+
+def coli_rmsnorm_f32(x, y, eps=1e-6, stream=None):
+    T, H = x.shape
+    return _check(lib.coli_rmsnorm_f32(_ptr(x), _ptr(y), T, H, ctypes.c_float(eps),
+                                       _stream(stream)), "coli_rmsnorm_f32")
+
+
+# ---------------------------------------------------------------- layer assembly
+
+def coli_quant_expert(blob_ptr: int, H: int, I: int, wg, wu, wd, status=None, stream=None):
+    """Quantise fp32 gate [I,H], up [I,H], down [H,I] (device) into the blob at blob_ptr."""
+    views = coli_expert_views(blob_ptr, H, I)
+    st = _stream(stream)
+    for (qp, sp), w in zip(views, (wg, wu, wd)):
+        rows, cols = w.shape
+        _check(lib.coli_quant_int4_g64(_ptr(w), rows, cols, ctypes.c_void_p(qp),
+                                       ctypes.c_void_p(sp), _ptr(status), st),
+               "coli_quant_int4_g64")
+
+
+def alloc_layer_blobs(H: int, I: int, E: int, device="cuda"):
+    """Device storage for E routed expert blobs and one shared blob (uint8)."""
+    import torch
+    nb = coli_expert_blob_bytes(H, I)
+    experts = torch.empty(E * nb, dtype=torch.uint8, device=device)
+    shared = torch.empty(nb, dtype=torch.uint8, device=device)
+    assert experts.data_ptr() % 256 == 0 and shared.data_ptr() % 256 == 0
+    return experts, shared, nb

@@ -1,0 +1,109 @@
+// kernels.h -- internal launchers of libcoli (not part of the C ABI).
+//
+// Every launcher enqueues on `stream` and returns hipGetLastError() of its
+// launches.  Shapes have been validated by the caller (coli.cpp); each
+// launcher only re-derives grid sizes from them.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "coli.h"
+
+// lanes of a wave hold ceil(E/64) router logits each
+#define COLI_MAX_PER_LANE (COLI_MAX_EXPERTS / 64)
+// decode mode accumulates the combine of up to this many tokens on chip
+#define COLI_MAX_DECODE_T 256
+
+namespace coli {
+
+// ---- shared layout arithmetic -------------------------------------------
+inline int64_t groups_of(int64_t cols) { return (cols + 63) / 64; }
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Offsets of the six sections of an expert blob (see coli.h).
+struct BlobLayout {
+  size_t gq, uq, dq, gs, us, ds, bytes;
+  int64_t GH, GI;  // groups per row of gate/up (input H) and of down (input I)
+};
+inline BlobLayout blob_layout(int H, int I) {
+  BlobLayout b;
+  b.GH = groups_of(H);
+  b.GI = groups_of(I);
+  size_t o = 0;
+  b.gq = o; o += align256(size_t(I) * b.GH * 32);
+  b.uq = o; o += align256(size_t(I) * b.GH * 32);
+  b.dq = o; o += align256(size_t(H) * b.GI * 32);
+  b.gs = o; o += align256(size_t(I) * b.GH * 4);
+  b.us = o; o += align256(size_t(I) * b.GH * 4);
+  b.ds = o; o += align256(size_t(H) * b.GI * 4);
+  b.bytes = o;
+  return b;
+}
+
+// Device-side view of the routing products, all inside the workspace.
+struct Routing {
+  float *logits;     // [T, E]
+  int32_t *idx;      // [T, K]
+  float *gates;      // [T, K]
+  int32_t *counts;   // [E]
+  int32_t *offsets;  // [E + 1]
+  int32_t *perm;     // [T*K]
+  int32_t *unique;   // [E]
+  int32_t *n_unique; // [1]
+  int32_t *chunk;    // [n_chunks * E] per-chunk counts / bases (large T)
+};
+
+// One layer as the kernels see it.
+struct LayerDev {
+  int H, I, E, K;
+  const uint8_t *experts;
+  const uint8_t *shared;
+  BlobLayout lay;
+};
+
+// ---- quant.hip ----------------------------------------------------------
+hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
+                                 uint8_t *packed, float *scales,
+                                 int32_t *status, hipStream_t s);
+
+// ---- route.hip ----------------------------------------------------------
+// logits[t, e] = x[t] . Wr[e] + b[e]; x fp32 (x_bf16 = 0) or bf16.
+hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
+                                const void *wr, int w_bf16, int E,
+                                const float *bias, float *logits,
+                                hipStream_t s);
+// Prefill router: bf16 x and bf16 Wr through MFMA, top-K fused.
+hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
+                                   const uint16_t *wr, int E,
+                                   const float *bias, int K, float *logits,
+                                   int32_t *idx, float *gates, hipStream_t s);
+// top-K + gates from logits, one wave per token.
+hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *idx,
+                       float *gates, hipStream_t s);
+// top-K + gates from logits (do_topk), then the batch-union permute.  For
+// T above a small threshold the permute uses r.chunk, permute_chunk_ints()
+// ints of scratch.
+hipError_t launch_topk_permute(const Routing &r, int T, int E, int K,
+                               int do_topk, hipStream_t s);
+size_t permute_chunk_ints(int T, int E);
+
+// ---- ffn_decode.hip -----------------------------------------------------
+// ev: optional stage events (NULL or 2 entries: after gate/up, after down).
+hipError_t launch_ffn_decode(const LayerDev &L, const float *x, int T,
+                             const Routing &r, float *h, float *y,
+                             hipStream_t s, hipEvent_t *ev);
+
+// ---- ffn_prefill.hip ----------------------------------------------------
+// ev: optional stage events (NULL or 4 entries: after prep+tiles, gate/up,
+// down, combine).
+hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T,
+                              const Routing &r, uint16_t *h,
+                              uint16_t *slot_out, uint16_t *y, hipStream_t s,
+                              hipEvent_t *ev);
+
+// ---- rmsnorm.hip --------------------------------------------------------
+hipError_t launch_rmsnorm_f32(const float *x, float *y, int T, int H,
+                              float eps, hipStream_t s);
+
+}  // namespace coli

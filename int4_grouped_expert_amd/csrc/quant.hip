@@ -1,0 +1,114 @@
+// quant.hip -- the int4-g64 planar quantiser (HBM-bound streaming kernel).
+//
+// Format and rule: page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
+// section 权重转换 -- groups of 64 along the input dimension, qmax 7,
+// q = clip(rint(w/s), -8, 7) stored as unsigned q+8, one fp32 scale per group,
+// planar nibbles (byte k: element k low, element k+32 high).
+//
+// Mapping: a team of 8 lanes owns one 64-group.  Lane j of the team reads
+// elements 4j..4j+3 and 32+4j..32+4j+3 (two 16-byte loads), so its four
+// output bytes 4j..4j+3 are complete in registers and leave as one 32-bit
+// store; a team writes its group's 32 bytes contiguously and a wave covers 8
+// groups.  amax and the non-finite flag are reduced over the team with lane
+// shuffles.  Bit-exactness: s = amax / 7.0f and w / s are IEEE fp32 divides
+// (this translation unit is compiled without fast-math and with fp32
+// denormals preserved), rint is round-half-to-even (v_rndne_f32).
+#include "kernels.h"
+
+namespace coli {
+namespace {
+
+constexpr int kTeam = 8;     // lanes per 64-group
+constexpr int kBlock = 256;  // 32 groups per block
+
+__device__ inline float team_max(float v) {
+#pragma unroll
+  for (int m = 1; m < kTeam; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kTeam));
+  return v;
+}
+__device__ inline int team_or(int v) {
+#pragma unroll
+  for (int m = 1; m < kTeam; m <<= 1) v |= __shfl_xor(v, m, kTeam);
+  return v;
+}
+
+__device__ inline uint32_t nibble(float w, float s) {
+  float q = __builtin_rintf(w / s);
+  q = fminf(fmaxf(q, -8.0f), 7.0f);
+  return uint32_t(int(q) + 8);
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kBlock) void quant_int4_g64_kernel(
+    const float *__restrict__ w, int64_t rows, int64_t cols, int64_t G,
+    uint8_t *__restrict__ packed, float *__restrict__ scales,
+    int32_t *__restrict__ status) {
+  const int64_t unit = (int64_t(blockIdx.x) * kBlock + threadIdx.x) / kTeam;
+  const int j = threadIdx.x % kTeam;
+  const bool live = unit < rows * G;
+  const int64_t r = live ? unit / G : 0;
+  const int64_t g = live ? unit % G : 0;
+  const float *src = w + r * cols + g * 64;
+
+  float lo[4], hi[4];
+  if (kVec && live && g * 64 + 64 <= cols) {
+    const float4 a = *reinterpret_cast<const float4 *>(src + 4 * j);
+    const float4 b = *reinterpret_cast<const float4 *>(src + 32 + 4 * j);
+    lo[0] = a.x; lo[1] = a.y; lo[2] = a.z; lo[3] = a.w;
+    hi[0] = b.x; hi[1] = b.y; hi[2] = b.z; hi[3] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t cl = g * 64 + 4 * j + i, ch = cl + 32;
+      lo[i] = (live && cl < cols) ? src[4 * j + i] : 0.0f;  // zero pad
+      hi[i] = (live && ch < cols) ? src[32 + 4 * j + i] : 0.0f;
+    }
+  }
+
+  float amax = 0.0f;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    amax = fmaxf(amax, fmaxf(fabsf(lo[i]), fabsf(hi[i])));
+    bad |= !__builtin_isfinite(lo[i]) | !__builtin_isfinite(hi[i]);
+  }
+  amax = team_max(amax);
+  bad = team_or(bad);
+  if (!live) return;
+
+  const float s = bad ? __builtin_nanf("") : amax / 7.0f;
+  uint32_t word = 0x88888888u;
+  if (!bad && s != 0.0f) {
+    word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      word |= (nibble(lo[i], s) | (nibble(hi[i], s) << 4)) << (8 * i);
+  }
+  *reinterpret_cast<uint32_t *>(packed + r * G * 32 + g * 32 + 4 * j) = word;
+  if (j == 0) {
+    scales[r * G + g] = s;
+    if (bad && status) atomicOr(status, 1);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
+                                 uint8_t *packed, float *scales,
+                                 int32_t *status, hipStream_t s) {
+  const int64_t G = groups_of(cols);
+  const int64_t units = rows * G;
+  if (units == 0) return hipSuccess;
+  const int64_t per_block = kBlock / kTeam;
+  const int64_t blocks = (units + per_block - 1) / per_block;
+  const bool vec = (cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0);
+  if (vec)
+    quant_int4_g64_kernel<true><<<dim3(unsigned(blocks)), kBlock, 0, s>>>(
+        w, rows, cols, G, packed, scales, status);
+  else
+    quant_int4_g64_kernel<false><<<dim3(unsigned(blocks)), kBlock, 0, s>>>(
+        w, rows, cols, G, packed, scales, status);
+  return hipGetLastError();
+}
+
+}  // namespace coli

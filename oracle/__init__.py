@@ -33,7 +33,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "coli_oracle.c")
 _LIB = os.path.join(_HERE, "libcoli_oracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 _lib = None
 
@@ -93,7 +93,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:  # bf16 bit patterns
         return BF16
-    raise TypeError(f"oracle takes float32 or bf16-as-uint16, got {a.dtype}")
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle takes float32, float64 or bf16-as-uint16, got {a.dtype}")
 
 
 def groups(cols: int) -> int:

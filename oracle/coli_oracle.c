@@ -66,9 +66,11 @@ static double bf16_to_double(uint16_t b) {
     return (double)f;
 }
 
-/* dtype codes used by the oracle's entry points: 0 = fp32, 1 = bf16 */
+/* dtype codes used by the oracle's entry points: 0 = fp32, 1 = bf16,
+ * 2 = fp64 (activations carried between stacked layers) */
 static double load_elem(const void *base, int dtype, size_t i) {
     if (dtype == 0) return (double)((const float *)base)[i];
+    if (dtype == 2) return ((const double *)base)[i];
     return bf16_to_double(((const uint16_t *)base)[i]);
 }
 

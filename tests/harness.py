@@ -1,0 +1,176 @@
+"""Helpers shared by the GPU parity tests: build a quantised layer on the device from
+the seeded draws, build the oracle's own copy of the experts it needs from the same
+draws, apply the top-K margin filter with the oracle, and compare."""
+from __future__ import annotations
+
+import math
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+
+MARGIN = 1e-3
+DEC_TOL = 2e-3   # fp32-activation paths: max|gpu - ref| <= 2e-3 * max(1, rms(ref))
+PRE_TOL = 2e-2   # bf16 prefill: max|gpu - ref| <= 2e-2 * rms(ref)
+
+
+def log(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def host_array(t: torch.Tensor) -> np.ndarray:
+    """fp32 as float32, bf16 as its uint16 bit pattern (the oracle's dtype codes)."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.detach().cpu().contiguous().numpy()
+
+
+def x_as_f64(x: torch.Tensor) -> np.ndarray:
+    return x.detach().cpu().double().numpy()
+
+
+class DeviceLayer:
+    """One layer of a workload, quantised on the device by the library."""
+
+    def __init__(self, cfg_id: int, layer: int = 0, device="cuda"):
+        import int4_grouped_expert_amd as coli
+        c = W.CONFIGS[cfg_id]
+        self.cfg_id, self.layer, self.c = cfg_id, layer, c
+        H, I, E, K = c["H"], c["I"], c["E"], c["K"]
+        self.H, self.I, self.E, self.K = H, I, E, K
+        self.w_router = W.router_weights(cfg_id, device, layer).contiguous()
+        b = W.router_bias(cfg_id, layer)
+        self.bias_np = b
+        self.bias = None if b is None else torch.from_numpy(b).to(device)
+        self.experts, self.shared, self.blob = coli.alloc_layer_blobs(H, I, E, device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        for e in range(E + 1):
+            wg, wu, wd = W.expert_weights(cfg_id, e, device, layer)
+            ptr = (self.shared.data_ptr() if e == E else self.experts.data_ptr() + e * self.blob)
+            coli.coli_quant_expert(ptr, H, I, wg, wu, wd, self.status)
+            del wg, wu, wd
+        torch.cuda.synchronize()
+        assert int(self.status.item()) == 0
+        self.layer_c = coli.MoELayer(H, I, E, K, self.w_router, self.experts, self.shared,
+                                     self.bias)
+
+    def blob_bytes(self, e: int) -> np.ndarray:
+        t = self.shared if e == self.E else self.experts[e * self.blob:(e + 1) * self.blob]
+        return t.cpu().numpy()
+
+    def forward(self, x: torch.Tensor, mode: int, idx=None, gates=None):
+        import int4_grouped_expert_amd as coli
+        T = x.shape[0]
+        dtype = torch.float32 if mode == coli.COLI_DECODE else torch.bfloat16
+        y = torch.empty((T, self.H), dtype=dtype, device=x.device)
+        ws = torch.empty(max(self.layer_c.workspace_bytes(T, mode), 256), dtype=torch.uint8,
+                         device=x.device)
+        if idx is None:
+            idx = torch.empty((T, self.K), dtype=torch.int32, device=x.device)
+            gates = torch.empty((T, self.K), dtype=torch.float32, device=x.device)
+        coli.coli_moe_forward(self.layer_c, mode, x, y, ws, idx, gates)
+        return y, idx, gates
+
+
+def oracle_blob_sections(ex: oracle.Expert, H: int, I: int) -> dict:
+    return dict(gq=ex.gq, gs=ex.gs, uq=ex.uq, us=ex.us, dq=ex.dq, ds=ex.ds)
+
+
+def device_sections(blob: np.ndarray, H: int, I: int) -> dict:
+    """Slice a host copy of a device blob with the documented layout."""
+    GH, GI = -(-H // 64), -(-I // 64)
+
+    def a256(n):
+        return (n + 255) // 256 * 256
+    o = 0
+    out = {}
+    for name, rows, G in (("gq", I, GH), ("uq", I, GH), ("dq", H, GI)):
+        out[name] = blob[o:o + rows * G * 32].reshape(rows, G * 32)
+        o += a256(rows * G * 32)
+    for name, rows, G in (("gs", I, GH), ("us", I, GH), ("ds", H, GI)):
+        out[name] = blob[o:o + rows * G * 4].view(np.float32).reshape(rows, G)
+        o += a256(rows * G * 4)
+    return out
+
+
+def oracle_expert(cfg_id: int, e: int, layer: int = 0, device="cuda",
+                  check_against: DeviceLayer | None = None) -> oracle.Expert:
+    """The oracle's own quantisation of expert e from the same seeded draws.
+
+    If check_against is given, the device bytes of that expert are compared with
+    the oracle's bit for bit (full-size quantiser parity on the way)."""
+    wg, wu, wd = (w.cpu().numpy() for w in W.expert_weights(cfg_id, e, device, layer))
+    ex = oracle.Expert.quantise(wg, wu, wd)
+    if check_against is not None:
+        L = check_against
+        dev = device_sections(L.blob_bytes(e), L.H, L.I)
+        ref = oracle_blob_sections(ex, L.H, L.I)
+        for k in ("gq", "uq", "dq"):
+            assert np.array_equal(dev[k], ref[k]), (cfg_id, e, k)
+        for k in ("gs", "us", "ds"):
+            assert np.array_equal(dev[k].view(np.uint32), ref[k].view(np.uint32)), (cfg_id, e, k)
+    return ex
+
+
+def topk_gap(logits: np.ndarray, K: int) -> np.ndarray:
+    """Per token: K-th largest logit minus (K+1)-th largest (inf when K == E)."""
+    E = logits.shape[1]
+    if K >= E:
+        return np.full(logits.shape[0], np.inf)
+    s = -np.sort(-logits, axis=1)
+    return s[:, K - 1] - s[:, K]
+
+
+def margin_tokens(cfg_id: int, T: int, wr_host: np.ndarray, bias, K: int, device="cuda"):
+    """Draw T tokens whose oracle top-K gap is >= MARGIN (failing rows are redrawn)."""
+    x = W.tokens(cfg_id, T, device, 0)
+    logits = oracle.router_logits(host_array(x), wr_host, bias)
+    bad = np.nonzero(topk_gap(logits, K) < MARGIN)[0]
+    draw = 1
+    while bad.size:
+        if draw > 60:
+            raise RuntimeError("margin filter did not converge")
+        fresh = W.tokens(cfg_id, int(bad.size), device, draw)
+        fl = oracle.router_logits(host_array(fresh), wr_host, bias)
+        good = topk_gap(fl, K) >= MARGIN
+        n = int(min(good.sum(), bad.size))
+        if n:
+            rows = bad[:n]
+            x[torch.from_numpy(rows).to(x.device)] = fresh[torch.from_numpy(np.nonzero(good)[0][:n]).to(x.device)]
+            bad = bad[n:]
+        draw += 1
+    return x
+
+
+def assert_close(gpu: np.ndarray, ref: np.ndarray, tol: float, floor_one: bool = True,
+                 what: str = ""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    rms = math.sqrt(float(np.mean(ref * ref))) if ref.size else 0.0
+    scale = max(1.0, rms) if floor_one else rms
+    err = float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
+    assert np.all(np.isfinite(gpu)), what + ": non-finite GPU output"
+    assert err <= tol * scale, f"{what}: max err {err:.3e} > {tol:g} * {scale:.3e}"
+    return err / max(scale, 1e-300)
+
+
+class Timer:
+    def __init__(self, what):
+        self.what = what
+
+    def __enter__(self):
+        self.t = time.time()
+        log(f"[start] {self.what}")
+        return self
+
+    def __exit__(self, *a):
+        log(f"[done ] {self.what} {time.time() - self.t:.1f}s")

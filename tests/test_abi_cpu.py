@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every symbol
+include/coli.h declares, the format arithmetic is right, and argument errors are
+rejected on the host before any HIP call (fail closed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_grouped_expert_amd as coli
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "coli.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(coli_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(coli.lib, n), n
+    assert sorted(coli.EXPORTS) == names
+
+
+def test_strerror_covers_codes():
+    for c in range(-6, 1):
+        assert coli.lib.coli_strerror(c)
+    assert coli.lib.coli_strerror(-99) == b"unknown status"
+
+
+def test_format_sizes():
+    assert coli.coli_int4_g64_packed_bytes(2048, 6144) == 6291456
+    assert coli.coli_int4_g64_scale_count(2048, 6144) == 196608
+    assert coli.coli_int4_g64_packed_bytes(3, 65) == 3 * 2 * 32
+    assert coli.coli_int4_g64_packed_bytes(0, 10) == 0
+    assert coli.coli_int4_g64_packed_bytes(4, 0) == 0
+    # 21,233,664 bytes per expert at H=6144, I=2048 (nibbles + fp32 scales)
+    assert coli.coli_expert_blob_bytes(6144, 2048) == 21233664
+    assert coli.coli_expert_blob_bytes(256, 128) == 55296
+    assert coli.coli_expert_blob_bytes(0, 128) == 0
+
+
+def test_expert_views_offsets():
+    base = 1 << 40
+    (gq, gs), (uq, us), (dq, ds) = coli.coli_expert_views(base, 6144, 2048)
+    assert gq - base == 0 and uq - base == 6291456 and dq - base == 2 * 6291456
+    assert gs - base == 3 * 6291456 and us - gs == 786432 and ds - us == 786432
+    for a in (gq, gs, uq, us, dq, ds):
+        assert (a - base) % 256 == 0
+
+
+def test_workspace_bytes():
+    lay = coli.coli_moe_layer(6144, 2048, 256, 8, 1 << 20, coli.COLI_BF16, None, 1 << 30, 1 << 31)
+    d = coli.lib.coli_moe_workspace_bytes(ctypes.byref(lay), 1, coli.COLI_DECODE)
+    assert d >= (8 + 1) * 2048 * 4
+    p = coli.lib.coli_moe_workspace_bytes(ctypes.byref(lay), 2048, coli.COLI_PREFILL)
+    assert p >= (2048 * 9) * (2048 + 6144) * 2
+    assert coli.lib.coli_moe_workspace_bytes(ctypes.byref(lay), 257, coli.COLI_DECODE) == 0
+    bad = coli.coli_moe_layer(6144, 2048, 256, 300, 1, 1, None, 1, 1)
+    assert coli.lib.coli_moe_workspace_bytes(ctypes.byref(bad), 1, coli.COLI_DECODE) == 0
+
+
+P = ctypes.c_void_p
+
+
+def test_quant_rejects_before_launch():
+    L = coli.lib
+    a = P(4096)
+    assert L.coli_quant_int4_g64(None, 1, 64, a, a, None, None) == coli.COLI_EINVAL
+    assert L.coli_quant_int4_g64(None, 0, 64, None, None, None, None) == coli.COLI_OK
+    assert L.coli_quant_int4_g64(a, -1, 64, a, a, None, None) == coli.COLI_ESHAPE
+    assert L.coli_quant_int4_g64(a, 1, 0, a, a, None, None) == coli.COLI_ESHAPE
+    assert L.coli_quant_int4_g64(P(4098), 1, 64, a, a, None, None) == coli.COLI_EALIGN
+    assert L.coli_quant_int4_g64(a, 1, 64, P(4100), a, None, None) == coli.COLI_EALIGN
+    assert L.coli_quant_int4_g64(a, 0, 64, a, a, None, None) == coli.COLI_OK  # no-op
+
+
+def test_router_rejects_before_launch():
+    L = coli.lib
+    a = P(4096)
+    ok = dict(T=1, H=64, E=16, K=4)
+
+    def call(T=1, H=64, E=16, K=4, x=a, xd=0, wd=0, idx=a):
+        return L.coli_router_topk(x, xd, T, H, a, wd, E, None, K, idx, a, a, None)
+    assert call(x=None) == coli.COLI_EINVAL
+    assert call(idx=None) == coli.COLI_EINVAL
+    assert call(K=17) == coli.COLI_ESHAPE
+    assert call(K=0) == coli.COLI_ESHAPE
+    assert call(E=1025, K=4) == coli.COLI_ESHAPE
+    assert call(H=60) == coli.COLI_ESHAPE
+    assert call(T=-1) == coli.COLI_ESHAPE
+    assert call(xd=7) == coli.COLI_EDTYPE
+    assert call(x=P(4104)) == coli.COLI_EALIGN
+    assert call(T=0) == coli.COLI_OK
+    del ok
+
+
+def test_permute_rejects_before_launch():
+    L = coli.lib
+    a = P(4096)
+    assert L.coli_expert_permute(None, 1, 2, 8, a, a, a, a, a, None, 0, None) == coli.COLI_EINVAL
+    assert L.coli_expert_permute(a, 1, 9, 8, a, a, a, a, a, None, 0, None) == coli.COLI_ESHAPE
+    need = coli.coli_expert_permute_workspace_bytes(2048, 256)
+    assert need > 0 and coli.coli_expert_permute_workspace_bytes(32, 256) == 0
+    assert (L.coli_expert_permute(a, 2048, 8, 256, a, a, a, a, a, None, 0, None)
+            == coli.COLI_EWORKSPACE)
+    assert (L.coli_expert_permute(a, 2048, 8, 256, a, a, a, a, a, a, need - 4, None)
+            == coli.COLI_EWORKSPACE)
+
+
+def test_forward_rejects_before_launch():
+    L = coli.lib
+    a = P(1 << 20)
+    lay = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22)
+    need = L.coli_moe_workspace_bytes(ctypes.byref(lay), 1, coli.COLI_DECODE)
+
+    def call(layer=lay, mode=coli.COLI_DECODE, x=a, T=1, y=a, ws=a, nb=need):
+        return L.coli_moe_forward(ctypes.byref(layer), mode, x, T, y, None, None, ws, nb, None)
+    assert call(x=None) == coli.COLI_EINVAL
+    assert call(mode=5) == coli.COLI_EINVAL
+    assert call(T=257) == coli.COLI_ESHAPE
+    assert call(ws=None) == coli.COLI_EWORKSPACE
+    assert call(nb=need - 1) == coli.COLI_EWORKSPACE
+    assert call(x=P((1 << 20) + 8)) == coli.COLI_EALIGN
+    assert call(ws=P((1 << 20) + 128)) == coli.COLI_EALIGN
+    assert call(T=0) == coli.COLI_OK
+    assert call(T=0, x=None, y=None) == coli.COLI_OK
+    for H, I, E, K in [(250, 128, 16, 4), (256, 100, 16, 4), (256, 128, 0, 1), (256, 128, 16, 17),
+                       (256, 128, 2000, 4)]:
+        bad = coli.coli_moe_layer(H, I, E, K, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22)
+        assert call(layer=bad) == coli.COLI_ESHAPE
+    unal = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, coli.COLI_F32, None, (1 << 21) + 64,
+                               1 << 22)
+    assert call(layer=unal) == coli.COLI_EALIGN
+    badt = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, 3, None, 1 << 21, 1 << 22)
+    assert call(layer=badt) == coli.COLI_EDTYPE
+
+
+def test_rmsnorm_rejects():
+    L = coli.lib
+    a = P(4096)
+    assert L.coli_rmsnorm_f32(None, a, 1, 8, 1e-6, None) == coli.COLI_EINVAL
+    assert L.coli_rmsnorm_f32(a, a, 1, 8, -1.0, None) == coli.COLI_EINVAL
+    assert L.coli_rmsnorm_f32(a, a, 1, 8, float("nan"), None) == coli.COLI_EINVAL
+    assert L.coli_rmsnorm_f32(a, a, 1, 0, 1e-6, None) == coli.COLI_ESHAPE
+    assert L.coli_rmsnorm_f32(a, a, 0, 8, 1e-6, None) == coli.COLI_OK
+
+
+def test_product_does_not_import_oracle():
+    import sys
+    pkg = os.path.join(ROOT, "int4_grouped_expert_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.replace("oracle is", ""), f
+    assert "int4_grouped_expert_amd" in sys.modules

@@ -1,0 +1,231 @@
+"""GPU parity of the whole layer (coli_moe_forward), decode and prefill, and of the
+RMSNorm between stacked layers.
+
+Layer: route (page "Colibri 深度解析", section 十一) -> batch union (section 四) ->
+int4-g64 planar expert FFN (page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
+section 权重转换) -> gate-weighted combine with the normalised gates (page "colibri 路由
+遥测全解析", section 追踪流ROUTE_TRACE) + the shared expert.
+
+Every expert the oracle uses is quantised by the oracle itself from the same seeded
+fp32 draws; on the way its bytes are compared with the device blob (bit-exact).
+Bars: idx bit-exact; decode floats max|d| <= 2e-3 * max(1, rms); prefill (bf16)
+max|d| <= 2e-2 * rms.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.harness import (DEC_TOL, PRE_TOL, DeviceLayer, Timer, assert_close, host_array,
+                           log, margin_tokens, oracle_expert, topk_gap, MARGIN)
+
+pytestmark = pytest.mark.gpu
+
+DECODE, PREFILL = 0, 1
+
+_layers = {}
+
+
+def layer(cfg_id, l=0):
+    key = (cfg_id, l)
+    if key not in _layers:
+        if W.CONFIGS[cfg_id]["H"] >= 4096:  # keep one full-size layer resident at a time
+            for k in [k for k in _layers if W.CONFIGS[k[0]]["H"] >= 4096]:
+                del _layers[k]
+            torch.cuda.empty_cache()
+        with Timer(f"build layer cfg {cfg_id} l {l}"):
+            _layers[key] = DeviceLayer(cfg_id, l)
+    return _layers[key]
+
+
+def oracle_check(cfg_id, L, x, y, idx, gates, mode, rows=None, check_bytes=True, l=0):
+    """Compare (sampled rows of) a forward with the oracle."""
+    c = W.CONFIGS[cfg_id]
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    xh = host_array(x[torch.from_numpy(rows).to(x.device)])
+    wr = host_array(L.w_router)
+    logits = oracle.router_logits(xh, wr, L.bias_np)
+    ridx, rg, _ = oracle.topk(logits, c["K"])
+    need = sorted(set(ridx.reshape(-1).tolist()))
+    experts = [None] * c["E"]
+    with Timer(f"oracle experts {len(need)}"):
+        for e in need:
+            experts[e] = oracle_expert(cfg_id, e, l, "cuda", L if check_bytes else None)
+        shared = oracle_expert(cfg_id, c["E"], l, "cuda", L if check_bytes else None)
+    with Timer("oracle forward"):
+        yr, ridx2, rg2 = oracle.moe_forward(xh, wr, L.bias_np, experts, shared, c["H"], c["I"],
+                                            c["K"])
+    assert np.array_equal(ridx, ridx2)
+    gi = idx.cpu().numpy()[rows]
+    assert np.array_equal(gi, ridx), "top-K ids differ from the oracle"
+    assert_close(gates.cpu().numpy()[rows], rg, DEC_TOL, what="gates")
+    yg = y.float().cpu().numpy()[rows]
+    if mode == DECODE:
+        return assert_close(yg, yr, DEC_TOL, what="y")
+    return assert_close(yg, yr, PRE_TOL, floor_one=False, what="y")
+
+
+@pytest.mark.parametrize("cfg_id,T", [(0, 1), (0, 7), (101, 40), (102, 5), (103, 3), (106, 3),
+                                      (0, 256), (101, 1)])
+def test_decode_small(cfg_id, T):
+    log(f"decode small cfg {cfg_id} T {T}")
+    L = layer(cfg_id)
+    c = W.CONFIGS[cfg_id]
+    x = margin_tokens(cfg_id, T, host_array(L.w_router), L.bias_np, c["K"])
+    y, idx, gates = L.forward(x, DECODE)
+    torch.cuda.synchronize()
+    oracle_check(cfg_id, L, x, y, idx, gates, DECODE)
+
+
+@pytest.mark.parametrize("cfg_id,T", [(100, 333), (104, 200), (100, 1), (100, 64), (100, 65)])
+def test_prefill_small(cfg_id, T):
+    log(f"prefill small cfg {cfg_id} T {T}")
+    L = layer(cfg_id)
+    c = W.CONFIGS[cfg_id]
+    x = margin_tokens(cfg_id, T, host_array(L.w_router), L.bias_np, c["K"])
+    y, idx, gates = L.forward(x, PREFILL)
+    torch.cuda.synchronize()
+    oracle_check(cfg_id, L, x, y, idx, gates, PREFILL)
+
+
+def test_decode_full_size_t1():
+    """The decode workload: H=6144, I=2048, E=256, K=8, T=1, several tokens."""
+    L = layer(1)
+    c = W.CONFIGS[1]
+    xs = margin_tokens(1, 3, host_array(L.w_router), None, c["K"])
+    for t in range(3):
+        log(f"decode full T=1 token {t}")
+        x = xs[t:t + 1].contiguous()
+        y, idx, gates = L.forward(x, DECODE)
+        torch.cuda.synchronize()
+        oracle_check(1, L, x, y, idx, gates, DECODE, check_bytes=(t == 0))
+
+
+def test_decode_full_size_t32_zipf():
+    """The Zipf decode batch: T=32; every token's ids, sampled tokens' outputs."""
+    L = layer(2)
+    c = W.CONFIGS[2]
+    x = margin_tokens(2, 32, host_array(L.w_router), L.bias_np, c["K"])
+    y, idx, gates = L.forward(x, DECODE)
+    torch.cuda.synchronize()
+    # every token's routing
+    logits = oracle.router_logits(host_array(x), host_array(L.w_router), L.bias_np)
+    ridx, _, _ = oracle.topk(logits, c["K"])
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    U = len(set(ridx.reshape(-1).tolist()))
+    log(f"zipf T=32 unique experts U={U}")
+    assert U < 32 * 8
+    oracle_check(2, L, x, y, idx, gates, DECODE, rows=[0, 5, 17, 31])
+
+
+def test_prefill_full_size_sampled():
+    """The prefill workload: T=2048 bf16; all ids, sampled tokens' outputs."""
+    L = layer(3)
+    c = W.CONFIGS[3]
+    with Timer("margin tokens T=2048"):
+        x = margin_tokens(3, 2048, host_array(L.w_router), None, c["K"])
+    y, idx, gates = L.forward(x, PREFILL)
+    torch.cuda.synchronize()
+    with Timer("oracle routing T=2048"):
+        logits = oracle.router_logits(host_array(x), host_array(L.w_router), None)
+        ridx, rg, _ = oracle.topk(logits, c["K"])
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert_close(gates.cpu().numpy(), rg, DEC_TOL, what="gates")
+    counts = np.bincount(ridx.reshape(-1), minlength=c["E"])
+    log(f"prefill tokens per expert min {counts.min()} max {counts.max()}")
+    oracle_check(3, L, x, y, idx, gates, PREFILL, rows=[0, 777, 2047], check_bytes=False)
+
+
+def test_forward_deterministic_and_t0():
+    L = layer(0)
+    x = margin_tokens(0, 4, host_array(L.w_router), None, 4)
+    a = L.forward(x, DECODE)[0].cpu()
+    b = L.forward(x, DECODE)[0].cpu()
+    assert torch.equal(a, b)
+    Lp = layer(100)
+    xp = margin_tokens(100, 100, host_array(Lp.w_router), None, 6)
+    a = Lp.forward(xp, PREFILL)[0].cpu()
+    b = Lp.forward(xp, PREFILL)[0].cpu()
+    assert torch.equal(a, b)
+    y, _, _ = L.forward(x[:0], DECODE)  # T = 0: no-op, no error
+    assert y.shape == (0, 256)
+
+
+def test_rmsnorm_parity():
+    import int4_grouped_expert_amd as coli
+    g = torch.Generator(device="cuda").manual_seed(3)
+    x = torch.randn((9, 6144), generator=g, device="cuda") * 3.0
+    y = torch.empty_like(x)
+    coli.coli_rmsnorm_f32(x, y, 1e-6)
+    ref = oracle.rmsnorm(x.cpu().double().numpy(), 1e-6)
+    assert_close(y.cpu().numpy(), ref, 1e-5, what="rmsnorm")
+    coli.coli_rmsnorm_f32(x, x, 1e-6)  # in place
+    assert torch.equal(x, y)
+
+
+def stack_check(cfg_id, nlayers, T, rows_check=None):
+    """GPU: y_l = layer_l(x_l), x_{l+1} = RMSNorm(y_l); the oracle runs the same
+    chain in fp64 from the same x_0.  Tokens whose top-K gap falls under the
+    margin at any layer are redrawn (checked on the oracle chain)."""
+    import int4_grouped_expert_amd as coli
+    c = W.CONFIGS[cfg_id]
+    Ls = [DeviceLayer(cfg_id, l) for l in range(nlayers)]
+    ex = [[None] * c["E"] for _ in range(nlayers)]
+    sh = [None] * nlayers
+
+    def oexpert(l, e):
+        if e == c["E"]:
+            if sh[l] is None:
+                sh[l] = oracle_expert(cfg_id, e, l, "cuda")
+            return sh[l]
+        if ex[l][e] is None:
+            ex[l][e] = oracle_expert(cfg_id, e, l, "cuda")
+        return ex[l][e]
+
+    def ochain(xh):
+        cur = xh
+        gaps = []
+        for l in range(nlayers):
+            logits = oracle.router_logits(cur, host_array(Ls[l].w_router), Ls[l].bias_np)
+            gaps.append(topk_gap(logits, c["K"]))
+            ridx, _, _ = oracle.topk(logits, c["K"])
+            for e in set(ridx.reshape(-1).tolist()):
+                oexpert(l, e)
+            y, _, _ = oracle.moe_forward(cur, host_array(Ls[l].w_router), Ls[l].bias_np, ex[l],
+                                         oexpert(l, c["E"]), c["H"], c["I"], c["K"])
+            cur = oracle.rmsnorm(y, 1e-6) if l + 1 < nlayers else y
+        return cur, np.min(np.stack(gaps), axis=0)
+
+    x = W.tokens(cfg_id, T, "cuda", 0)
+    draw = 1
+    while True:
+        yr, gap = ochain(host_array(x))
+        bad = np.nonzero(gap < MARGIN)[0]
+        if bad.size == 0:
+            break
+        assert draw < 30
+        fresh = W.tokens(cfg_id, T, "cuda", draw)
+        x[torch.from_numpy(bad).cuda()] = fresh[: bad.size]
+        draw += 1
+    cur = x.clone()
+    for l in range(nlayers):
+        y, _, _ = Ls[l].forward(cur, DECODE)
+        if l + 1 < nlayers:
+            coli.coli_rmsnorm_f32(y, y, 1e-6)
+        cur = y
+    torch.cuda.synchronize()
+    return assert_close(cur.cpu().numpy(), yr, DEC_TOL, what=f"stack out ({nlayers} layers)")
+
+
+def test_stack_small_40_layers():
+    log("stack small 40 layers")
+    stack_check(105, 40, 8)
+
+
+def test_stack_full_size_two_layers():
+    log("stack full size, 2 layers")
+    for k in list(_layers):
+        del _layers[k]
+    torch.cuda.empty_cache()
+    stack_check(4, 2, 8)

@@ -1,0 +1,121 @@
+"""GPU parity of the quantiser and planar packer (bit-exact bytes and scale bits).
+
+Rule: page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战", section 权重转换.
+Every case compares coli_quant_int4_g64 with the oracle on the same fp32 input.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._golden import load_quant_case
+from tests.harness import log
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_quant(w_host: np.ndarray):
+    import int4_grouped_expert_amd as coli
+    rows, cols = w_host.shape
+    G = -(-cols // 64)
+    w = torch.from_numpy(np.ascontiguousarray(w_host)).cuda()
+    packed = torch.full((max(rows, 1), G * 32), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((max(rows, 1), G), 7.0, dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    coli.coli_quant_int4_g64(w, packed, scales, status)
+    torch.cuda.synchronize()
+    return packed.cpu().numpy()[:rows], scales.cpu().numpy()[:rows], int(status.item())
+
+
+def assert_same(w):
+    p, s, st = gpu_quant(w)
+    pr, sr, str_ = oracle.quant_int4_g64(w)
+    assert st == str_
+    assert np.array_equal(p, pr)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["quant_E1.txt", "quant_E2.txt", "quant_E3.txt",
+                                  "quant_E4.txt"])
+def test_golden(name):
+    log(f"quant golden {name}")
+    w, want, scale = load_quant_case(name)
+    p, s, st = gpu_quant(w)
+    assert st == 0
+    assert bytes(p[0]) == want
+    assert int(s[0, 0:1].view(np.uint32)[0]) == scale
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (7, 200), (33, 1), (5, 63), (3, 65),
+                                       (16, 130), (64, 6144), (300, 2048), (2, 4098)])
+def test_random_shapes(rows, cols):
+    log(f"quant random {rows}x{cols}")
+    rng = np.random.default_rng(rows * 1000 + cols)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    assert_same(w)
+
+
+def test_ties_and_scales():
+    """Exact ties after division for many power-of-two and non-power-of-two scales."""
+    rng = np.random.default_rng(1)
+    rows = 512
+    q = rng.integers(-7, 8, size=(rows, 64)).astype(np.float64)
+    q[:, 0] = 7
+    half = rng.random((rows, 64)) < 0.3
+    q = np.where(half, q + 0.5 * np.sign(rng.standard_normal((rows, 64))), q)
+    q[:, 0] = 7
+    s = rng.uniform(1e-3, 1.0, size=(rows, 1))
+    s[: rows // 2] = 2.0 ** rng.integers(-12, 3, size=(rows // 2, 1))
+    w = (q * s).astype(np.float32)
+    assert_same(w)
+
+
+def test_subnormal_and_extreme_magnitudes():
+    rng = np.random.default_rng(2)
+    bits = rng.integers(1, 0x7F7FFFFF, size=(256, 64), dtype=np.uint32)
+    bits[:64] = rng.integers(1, 0x00800000, size=(64, 64), dtype=np.uint32)  # subnormal
+    w = bits.view(np.float32) * np.where(rng.random((256, 64)) < 0.5, -1, 1).astype(np.float32)
+    assert_same(w)
+
+
+def test_nonfinite_groups_set_status():
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((4, 256)) * 0.02).astype(np.float32)
+    w[1, 70] = np.nan
+    w[2, 255] = np.inf
+    w[3, 0] = -np.inf
+    p, s, st = gpu_quant(w)
+    assert st == 1
+    pr, sr, _ = oracle.quant_int4_g64(w)
+    assert np.array_equal(p, pr)
+    assert np.array_equal(np.isnan(s), np.isnan(sr))
+    fin = ~np.isnan(sr)
+    assert np.array_equal(s[fin].view(np.uint32), sr[fin].view(np.uint32))
+    # finite input leaves the flag at 0
+    _, _, st2 = gpu_quant(w[0:1])
+    assert st2 == 0
+
+
+def test_zero_rows_is_noop():
+    import int4_grouped_expert_amd as coli
+    w = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
+    packed = torch.full((1, 32), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((1, 1), 7.0, device="cuda")
+    coli.coli_quant_int4_g64(w, packed, scales)
+    torch.cuda.synchronize()
+    assert torch.all(packed == 0x5A) and torch.all(scales == 7.0)
+
+
+def test_unaligned_rows_scalar_path():
+    """cols % 4 != 0 rows are not 16-byte aligned: the scalar load path."""
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((9, 131)) * 0.1).astype(np.float32)
+    assert_same(w)
+
+
+def test_deterministic_twice():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((128, 512)) * 0.02).astype(np.float32)
+    a = gpu_quant(w)
+    b = gpu_quant(w)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
