@@ -205,7 +205,7 @@ size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int T, coli_mode mode);
  *                 the matrix cores with fp32 accumulation.  The products take
  *                 fp16 operands: x converted from bf16 (exact for
  *                 |x| in [2^-14, 65504]), weights s*(u-8) rounded once to
- *                 fp16, h held in fp16; per-slot outputs are rounded to bf16
+ *                 fp16, h held in fp16; per-slot outputs are rounded to fp16
  *                 before the combine.  Inputs or intermediates beyond the fp16
  *                 range are outside this mode's contract.
  *   topk_idx_out, topk_gate_out: optional [T, K] copies of the routing.

@@ -29,7 +29,7 @@
 //
 // Kernels: prefill_prep (x bf16 -> fp16 in the perm8 layout), prefill_tiles
 // (M-chunk prefix over units), gateup_prefill (h = SiLU(gate)*up, fp16,
-// perm8 layout), down_prefill (gate-scaled per-slot outputs, bf16),
+// perm8 layout), down_prefill (gate-scaled per-slot outputs, fp16),
 // combine (y = sum of a token's slots + its shared output, bf16).
 #include "kernels.h"
 
@@ -257,7 +257,7 @@ __device__ inline int perm8_pos(int o) {
 // [I, H], N-tile = 128 output rows (per wave 32: gate rows in fragments 0-1,
 // up rows in 2-3), epilogue h = SiLU(gate) * up -> hp (fp16, perm8 layout).
 // !kGateUp: A = hp [T*K + T, I], B = down [H, I], N-tile = 256 output rows
-// (per wave 64), epilogue gate * out -> slot_out (bf16).
+// (per wave 64), epilogue gate * out -> slot_out (fp16).
 template <bool kGateUp>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
     LayerDev L, Routing r, int T, const uint16_t *__restrict__ A,
@@ -395,13 +395,9 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int o = it.ntile * 256 + wave * 64 + 16 * jj + n16;
-            if (o < Nrows) {
-              const float v = gate * acc[mf][jj][i];
-              // round to nearest even bf16
-              const uint32_t u = __float_as_uint(v);
-              const uint32_t rb = ((u >> 16) & 1u) + 0x7FFFu;
-              out[srow * Nrows + o] = uint16_t((u + rb) >> 16);
-            }
+            if (o < Nrows)
+              out[srow * Nrows + o] =
+                  __builtin_bit_cast(uint16_t, _Float16(gate * acc[mf][jj][i]));
           }
         }
       }
@@ -415,7 +411,8 @@ __device__ inline uint16_t f32_to_bf16_rne(float v) {
   return uint16_t((u + ((u >> 16) & 1u) + 0x7FFFu) >> 16);
 }
 
-// y[t] = sum_k slot[t*K + k] + slot[T*K + t]   (8 columns per thread)
+// y[t] = sum_k slot[t*K + k] + slot[T*K + t]   (fp16 slots, fp32 sum, bf16 y;
+// 8 columns per thread)
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ slot,
                                                       int T, int H, int K,
                                                       uint16_t *__restrict__ y) {
@@ -430,8 +427,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += __uint_as_float(w[q] << 16);
-      acc[2 * q + 1] += __uint_as_float(w[q] & 0xFFFF0000u);
+      const f16x2 hv = __builtin_bit_cast(f16x2, w[q]);
+      acc[2 * q] += float(hv[0]);
+      acc[2 * q + 1] += float(hv[1]);
     }
   }
   uint32_t o[4];

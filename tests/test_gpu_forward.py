@@ -164,10 +164,18 @@ def test_rmsnorm_parity():
     assert torch.equal(x, y)
 
 
-def stack_check(cfg_id, nlayers, T, rows_check=None):
-    """GPU: y_l = layer_l(x_l), x_{l+1} = RMSNorm(y_l); the oracle runs the same
-    chain in fp64 from the same x_0.  Tokens whose top-K gap falls under the
-    margin at any layer are redrawn (checked on the oracle chain)."""
+def stack_check(cfg_id, nlayers, T, e2e_layers):
+    """A stack of MoE layers with RMSNorm between them (no attention, no residual).
+
+    The layer-to-layer map amplifies perturbations (~1.4x per layer for these random
+    layers: a 1e-7 relative change of x_0 reaches O(1) after ~36 layers even in
+    fp64), so fp32 and fp64 chains cannot agree after 40 layers.  Checked instead:
+      * per layer: the GPU layer l on the oracle chain's own input x_l (rounded to
+        fp32) matches the oracle's y_l;
+      * end to end: the GPU chain matches the oracle chain for the first e2e_layers;
+      * the full GPU chain is finite, every normalised x has RMS sqrt(m/(m+eps))
+        (m the mean square before the norm), and two runs are bitwise identical.
+    Tokens whose top-K gap is under the margin at any layer are redrawn."""
     import int4_grouped_expert_amd as coli
     c = W.CONFIGS[cfg_id]
     Ls = [DeviceLayer(cfg_id, l) for l in range(nlayers)]
@@ -185,7 +193,7 @@ def stack_check(cfg_id, nlayers, T, rows_check=None):
 
     def ochain(xh):
         cur = xh
-        gaps = []
+        gaps, xs, ys = [], [], []
         for l in range(nlayers):
             logits = oracle.router_logits(cur, host_array(Ls[l].w_router), Ls[l].bias_np)
             gaps.append(topk_gap(logits, c["K"]))
@@ -194,13 +202,15 @@ def stack_check(cfg_id, nlayers, T, rows_check=None):
                 oexpert(l, e)
             y, _, _ = oracle.moe_forward(cur, host_array(Ls[l].w_router), Ls[l].bias_np, ex[l],
                                          oexpert(l, c["E"]), c["H"], c["I"], c["K"])
-            cur = oracle.rmsnorm(y, 1e-6) if l + 1 < nlayers else y
-        return cur, np.min(np.stack(gaps), axis=0)
+            xs.append(cur)
+            ys.append(y)
+            cur = oracle.rmsnorm(y, 1e-6)
+        return xs, ys, np.min(np.stack(gaps), axis=0)
 
     x = W.tokens(cfg_id, T, "cuda", 0)
     draw = 1
     while True:
-        yr, gap = ochain(host_array(x))
+        xs, ys, gap = ochain(host_array(x))
         bad = np.nonzero(gap < MARGIN)[0]
         if bad.size == 0:
             break
@@ -208,19 +218,39 @@ def stack_check(cfg_id, nlayers, T, rows_check=None):
         fresh = W.tokens(cfg_id, T, "cuda", draw)
         x[torch.from_numpy(bad).cuda()] = fresh[: bad.size]
         draw += 1
-    cur = x.clone()
+    worst = 0.0
     for l in range(nlayers):
-        y, _, _ = Ls[l].forward(cur, DECODE)
-        if l + 1 < nlayers:
-            coli.coli_rmsnorm_f32(y, y, 1e-6)
-        cur = y
-    torch.cuda.synchronize()
-    return assert_close(cur.cpu().numpy(), yr, DEC_TOL, what=f"stack out ({nlayers} layers)")
+        xl = torch.from_numpy(np.asarray(xs[l], dtype=np.float32)).cuda()
+        y, _, _ = Ls[l].forward(xl, DECODE)
+        torch.cuda.synchronize()
+        worst = max(worst, assert_close(y.cpu().numpy(), ys[l], DEC_TOL, what=f"layer {l}"))
+    log(f"stack per-layer worst rel err {worst:.2e}")
+
+    def gpu_chain(n):
+        cur = x.clone()
+        for l in range(n):
+            y, _, _ = Ls[l].forward(cur, DECODE)
+            if l + 1 < n:
+                m = y.double().pow(2).mean(1)
+                coli.coli_rmsnorm_f32(y, y, 1e-6)
+                rms = y.double().pow(2).mean(1).sqrt()
+                want = (m / (m + 1e-6)).sqrt()  # unit RMS up to the eps term
+                assert torch.all((rms - want).abs() < 1e-5), f"layer {l} rms {rms}"
+            cur = y
+        torch.cuda.synchronize()
+        return cur
+    e2e = gpu_chain(e2e_layers)
+    err = assert_close(e2e.cpu().numpy(), ys[e2e_layers - 1], DEC_TOL,
+                       what=f"stack out after {e2e_layers} layers")
+    log(f"stack end-to-end {e2e_layers} layers rel err {err:.2e}")
+    full = gpu_chain(nlayers)
+    assert torch.all(torch.isfinite(full))
+    assert torch.equal(full, gpu_chain(nlayers))
 
 
 def test_stack_small_40_layers():
     log("stack small 40 layers")
-    stack_check(105, 40, 8)
+    stack_check(105, 40, 8, e2e_layers=8)
 
 
 def test_stack_full_size_two_layers():
@@ -228,4 +258,4 @@ def test_stack_full_size_two_layers():
     for k in list(_layers):
         del _layers[k]
     torch.cuda.empty_cache()
-    stack_check(4, 2, 8)
+    stack_check(4, 2, 8, e2e_layers=2)
