@@ -30,7 +30,9 @@ bool layer_shape_ok(int H, int I, int E, int K) {
 
 // Workspace carve-up (byte offsets, each section 256-byte aligned).
 struct WsLayout {
-  size_t logits, idx, gates, counts, offsets, perm, unique, n_unique, chunk, h, slot, total;
+  size_t logits, idx, gates, counts, offsets, perm, unique, n_unique, chunk, h, slot;
+  size_t xh, xl, xsc, hh, hl, hsc, slotmap;  // decode only
+  size_t total;
 };
 WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
   WsLayout w;
@@ -47,9 +49,20 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
   size_t chunk = permute_chunk_ints(T, E);
   if (chunk < size_t(E) + 2) chunk = size_t(E) + 2;
   w.chunk = o; o += align256(chunk * 4);
-  w.h = o; o += align256((TK + T) * size_t(I) * (mode == COLI_DECODE ? 4 : 2));
-  w.slot = o;
-  if (mode == COLI_PREFILL) o += align256((TK + T) * size_t(H) * 2);
+  w.h = w.slot = w.xh = w.xl = w.xsc = w.hh = w.hl = w.hsc = w.slotmap = 0;
+  if (mode == COLI_PREFILL) {
+    w.h = o; o += align256((TK + T) * size_t(I) * 2);
+    w.slot = o; o += align256((TK + T) * size_t(H) * 2);
+  } else {
+    const size_t units = TK < size_t(E) ? TK : size_t(E);
+    w.xh = o; o += align256(size_t(T) * H * 2);
+    w.xl = o; o += align256(size_t(T) * H * 2);
+    w.xsc = o; o += align256(size_t(T) * 4);
+    w.hh = o; o += align256((TK + T) * size_t(I) * 2);
+    w.hl = o; o += align256((TK + T) * size_t(I) * 2);
+    w.hsc = o; o += align256((TK + T) * size_t(I / 32) * 4);
+    w.slotmap = o; o += align256(units * size_t(T) * 4);
+  }
   w.total = o;
   return w;
 }
@@ -125,7 +138,7 @@ int coli_router_topk(const void *x, coli_dtype x_dtype, int T, int H, const void
   if (T == 0) return COLI_OK;
   hipStream_t s = as_stream(stream);
   hipError_t e = launch_router_logits(x, x_dtype == COLI_BF16, T, H, w_router,
-                                      w_dtype == COLI_BF16, E, bias, logits, s);
+                                      w_dtype == COLI_BF16, E, bias, logits, nullptr, s);
   if (e != hipSuccess) return COLI_EDEVICE;
   return dev_status(launch_topk(logits, T, E, K, topk_idx, topk_gate, s));
 }
@@ -227,14 +240,21 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
 
   hipError_t e;
   if (mode == COLI_DECODE) {
-    e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, L->router_bias, r.logits, s);
+    DecodeBufs b;
+    b.xh = reinterpret_cast<uint16_t *>(ws + w.xh);
+    b.xl = reinterpret_cast<uint16_t *>(ws + w.xl);
+    b.xsc = reinterpret_cast<float *>(ws + w.xsc);
+    b.hh = reinterpret_cast<uint16_t *>(ws + w.hh);
+    b.hl = reinterpret_cast<uint16_t *>(ws + w.hl);
+    b.hsc = reinterpret_cast<float *>(ws + w.hsc);
+    b.slotmap = reinterpret_cast<int32_t *>(ws + w.slotmap);
+    e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, L->router_bias, r.logits,
+                             &b, s);
     if (e != hipSuccess) return COLI_EDEVICE;
-    e = launch_topk_permute(r, T, L->E, L->K, 1, s);
+    e = launch_route_decode(r, T, L->E, L->K, b.slotmap, s);
     if (e != hipSuccess) return COLI_EDEVICE;
     if (ev) (void)hipEventRecord(ev[0], s);
-    e = launch_ffn_decode(d, reinterpret_cast<const float *>(x), T, r,
-                          reinterpret_cast<float *>(ws + w.h), reinterpret_cast<float *>(y), s,
-                          ev ? ev + 1 : nullptr);
+    e = launch_ffn_decode(d, b, T, r, reinterpret_cast<float *>(y), s, ev ? ev + 1 : nullptr);
     return dev_status(e);
   }
   if (wbf) {
@@ -244,7 +264,8 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
     if (e != hipSuccess) return COLI_EDEVICE;
     e = launch_topk_permute(r, T, L->E, L->K, 0, s);
   } else {
-    e = launch_router_logits(x, 1, T, L->H, L->w_router, 0, L->E, L->router_bias, r.logits, s);
+    e = launch_router_logits(x, 1, T, L->H, L->w_router, 0, L->E, L->router_bias, r.logits,
+                             nullptr, s);
     if (e != hipSuccess) return COLI_EDEVICE;
     e = launch_topk_permute(r, T, L->E, L->K, 1, s);
   }

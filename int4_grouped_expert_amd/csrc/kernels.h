@@ -54,6 +54,19 @@ struct Routing {
   int32_t *chunk;    // [n_chunks * E] per-chunk counts / bases (large T)
 };
 
+// Decode-path activation buffers (inside the workspace).  xh/xl: x [T, H] as
+// fp16 hi/lo pairs (perm8 order inside 8-element runs), value = (hi + lo) *
+// xsc[t]; hh/hl/hsc: h' [T*K + T, I] likewise with one scale per 32 columns;
+// slotmap [n_units_max, T]: h row of (unit u, token t), -1 if t is not routed
+// to u.
+struct DecodeBufs {
+  uint16_t *xh, *xl;
+  float *xsc;
+  uint16_t *hh, *hl;
+  float *hsc;
+  int32_t *slotmap;
+};
+
 // One layer as the kernels see it.
 struct LayerDev {
   int H, I, E, K;
@@ -68,11 +81,12 @@ hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
                                  int32_t *status, hipStream_t s);
 
 // ---- route.hip ----------------------------------------------------------
-// logits[t, e] = x[t] . Wr[e] + b[e]; x fp32 (x_bf16 = 0) or bf16.
+// logits[t, e] = x[t] . Wr[e] + b[e]; x fp32 (x_bf16 = 0) or bf16.  If xb is
+// non-NULL (fp32 x only) the same launch also writes the split copy of x.
 hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
                                 const void *wr, int w_bf16, int E,
                                 const float *bias, float *logits,
-                                hipStream_t s);
+                                const DecodeBufs *xb, hipStream_t s);
 // Prefill router: bf16 x and bf16 Wr through MFMA, top-K fused.
 hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
                                    const uint16_t *wr, int E,
@@ -86,13 +100,18 @@ hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *idx,
 // ints of scratch.
 hipError_t launch_topk_permute(const Routing &r, int T, int E, int K,
                                int do_topk, hipStream_t s);
+// Decode: one block does top-K, the permute, the per-unit M-chunk prefix
+// (r.chunk, chunks of 32 tokens, the shared unit last) and the slot map.
+// Requires T <= COLI_MAX_DECODE_T.
+hipError_t launch_route_decode(const Routing &r, int T, int E, int K,
+                               int32_t *slotmap, hipStream_t s);
 size_t permute_chunk_ints(int T, int E);
 
 // ---- ffn_decode.hip -----------------------------------------------------
 // ev: optional stage events (NULL or 2 entries: after gate/up, after down).
-hipError_t launch_ffn_decode(const LayerDev &L, const float *x, int T,
-                             const Routing &r, float *h, float *y,
-                             hipStream_t s, hipEvent_t *ev);
+hipError_t launch_ffn_decode(const LayerDev &L, const DecodeBufs &b, int T,
+                             const Routing &r, float *y, hipStream_t s,
+                             hipEvent_t *ev);
 
 // ---- ffn_prefill.hip ----------------------------------------------------
 // ev: optional stage events (NULL or 4 entries: after prep+tiles, gate/up,

@@ -31,15 +31,103 @@ __device__ inline float bf16_to_f32(uint16_t b) {
   return __uint_as_float(uint32_t(b) << 16);
 }
 
+// Wave-wide reductions: an all-reduce inside each 16-lane DPP row (quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror pair every lane
+// with a disjoint partner set, doubling it each step), then the four row
+// results are read with v_readlane and combined in a fixed order, so every
+// lane gets the same, deterministic value.
+template <int kCtrl>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ inline float rdlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (rdlane_f(v, 0) + rdlane_f(v, 16)) + (rdlane_f(v, 32) + rdlane_f(v, 48));
 }
 __device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(rdlane_f(v, 0), rdlane_f(v, 16)), fmaxf(rdlane_f(v, 32), rdlane_f(v, 48)));
+}
+// (value, id) arg-max: larger value wins, equal values go to the lower id,
+// id < 0 marks "no candidate".
+__device__ inline void take_better(float &bv, int &bi, float ov, int oi) {
+  const bool take = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
+}
+__device__ inline void wave_argmax(float &bv, int &bi) {
+#define COLI_ARG_STEP(ctrl)                                                          \
+  {                                                                                  \
+    const float ov = dpp_f<ctrl>(bv);                                                \
+    const int oi = __builtin_amdgcn_update_dpp(-1, bi, ctrl, 0xF, 0xF, false);       \
+    take_better(bv, bi, ov, oi);                                                     \
+  }
+  COLI_ARG_STEP(0xB1)
+  COLI_ARG_STEP(0x4E)
+  COLI_ARG_STEP(0x141)
+  COLI_ARG_STEP(0x140)
+#undef COLI_ARG_STEP
+  float v = rdlane_f(bv, 0);
+  int i = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+  for (int r = 1; r < 4; ++r)
+    take_better(v, i, rdlane_f(bv, 16 * r), __builtin_amdgcn_readlane(bi, 16 * r));
+  bv = v;
+  bi = i;
+}
+
+// Split an fp32 row into fp16 hi/lo with one power-of-two scale:
+// row = (hi + lo) * sc, max|row| / sc in [2^14, 2^15); hi and lo are written
+// with perm8 applied inside each 8-element run (swap 1<->2 and 5<->6), the
+// order the expert kernels' nibble unpack produces.  Whole block, H % 8 == 0.
+__device__ void split_row(const float *__restrict__ xr, int H, uint16_t *__restrict__ hi,
+                          uint16_t *__restrict__ lo, float *__restrict__ sc, float *red4) {
+  float m = 0.0f;
+  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+    const float4 a = *reinterpret_cast<const float4 *>(xr + c);
+    const float4 b = *reinterpret_cast<const float4 *>(xr + c + 4);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+  }
+  m = wave_max(m);
+  if (threadIdx.x % kWave == 0) red4[threadIdx.x / kWave] = m;
+  __syncthreads();
+  m = red4[0];
+  for (int w = 1; w < int(blockDim.x / kWave); ++w) m = fmaxf(m, red4[w]);
+  __syncthreads();
+  int ex = 0;
+  (void)frexpf(m, &ex);
+  const int e = m > 0.0f ? max(ex - 15, -140) : 0;
+  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+    const float4 a = *reinterpret_cast<const float4 *>(xr + c);
+    const float4 b = *reinterpret_cast<const float4 *>(xr + c + 4);
+    const float v[8] = {a.x, a.z, a.y, a.w, b.x, b.z, b.y, b.w};  // perm8 order
+    uint16_t h16[8], l16[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float s = ldexpf(v[k], -e);
+      const _Float16 h = _Float16(s);
+      h16[k] = __builtin_bit_cast(uint16_t, h);
+      l16[k] = __builtin_bit_cast(uint16_t, _Float16(s - float(h)));
+    }
+    uint4 ho, lw;
+    ho.x = h16[0] | (uint32_t(h16[1]) << 16); ho.y = h16[2] | (uint32_t(h16[3]) << 16);
+    ho.z = h16[4] | (uint32_t(h16[5]) << 16); ho.w = h16[6] | (uint32_t(h16[7]) << 16);
+    lw.x = l16[0] | (uint32_t(l16[1]) << 16); lw.y = l16[2] | (uint32_t(l16[3]) << 16);
+    lw.z = l16[4] | (uint32_t(l16[5]) << 16); lw.w = l16[6] | (uint32_t(l16[7]) << 16);
+    *reinterpret_cast<uint4 *>(hi + c) = ho;
+    *reinterpret_cast<uint4 *>(lo + c) = lw;
+  }
+  if (threadIdx.x == 0) *sc = ldexpf(1.0f, e);
 }
 
 // Load 8 consecutive elements (fp32 or bf16) as floats.
@@ -65,11 +153,22 @@ __device__ inline void load8(const void *base, size_t i, float out[8]) {
 }
 
 // ---------------------------------------------------------------- logits (GEMV)
-// grid.x: groups of 4*RW expert rows; grid.y: groups of TT tokens.
+// grid.x: groups of 4*RW expert rows; grid.y: groups of TT tokens.  Each lane
+// issues the loads of up to kBatch 512-column chunks before using them.
+// With do_split, blocks of grid row 0 first write the split copy of x
+// (token t on block t % grid.x).
+constexpr int kBatch = 8;
+
 template <int RW, int TT, bool kXbf, bool kWbf>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const void *__restrict__ x, int T, int H, const void *__restrict__ wr,
-    int E, const float *__restrict__ bias, float *__restrict__ logits) {
+    int E, const float *__restrict__ bias, float *__restrict__ logits, DecodeBufs xb,
+    int do_split) {
+  __shared__ float red4[4];
+  if (!kXbf && do_split && blockIdx.y == 0)
+    for (int t = blockIdx.x; t < T; t += gridDim.x)
+      split_row(reinterpret_cast<const float *>(x) + size_t(t) * H, H, xb.xh + size_t(t) * H,
+                xb.xl + size_t(t) * H, xb.xsc + t, red4);
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int e0 = (blockIdx.x * 4 + wave) * RW;
@@ -81,24 +180,34 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[r][t] = 0.0f;
 
-  for (int c = lane * 8; c < H; c += kWave * 8) {
-    float wv[RW][8];
+  constexpr int kB = kBatch / RW > 0 ? kBatch / RW : 1;
+  for (int cb = 0; cb < H; cb += kB * kWave * 8) {
+    float wv[kB][RW][8];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      if (e0 + r < E) load8<kWbf>(wr, size_t(e0 + r) * H + c, wv[r]);
-      else
+    for (int b = 0; b < kB; ++b) {
+      const int c = cb + (b * kWave + lane) * 8;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) wv[r][k] = 0.0f;
+      for (int r = 0; r < RW; ++r) {
+        if (c < H && e0 + r < E) load8<kWbf>(wr, size_t(e0 + r) * H + c, wv[b][r]);
+        else
+#pragma unroll
+          for (int k = 0; k < 8; ++k) wv[b][r][k] = 0.0f;
+      }
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       if (t0 + t >= T) break;
-      float xv[8];
-      load8<kXbf>(x, size_t(t0 + t) * H + c, xv);
 #pragma unroll
-      for (int r = 0; r < RW; ++r)
+      for (int b = 0; b < kB; ++b) {
+        const int c = cb + (b * kWave + lane) * 8;
+        if (c >= H) break;
+        float xv[8];
+        load8<kXbf>(x, size_t(t0 + t) * H + c, xv);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[r][t] = fmaf(wv[r][k], xv[k], acc[r][t]);
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[r][t] = fmaf(wv[b][r][k], xv[k], acc[r][t]);
+      }
     }
   }
 #pragma unroll
@@ -182,14 +291,7 @@ __device__ void wave_topk(const float *__restrict__ lrow, int E, int K, int lane
         bi = e;
       }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, kWave);
-      const int oi = __shfl_xor(bi, m, kWave);
-      const bool take = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
-      bv = take ? ov : bv;
-      bi = take ? oi : bi;
-    }
+    wave_argmax(bv, bi);
     if (bi < 0) {
       // No valid candidate: id `round` if free, else the lowest free id.
       int free_lo = 0x7fffffff;
@@ -201,7 +303,7 @@ __device__ void wave_topk(const float *__restrict__ lrow, int E, int K, int lane
       int own_free = 0;
       if (round < E && (round % kWave) == lane) own_free = !((taken >> (round / kWave)) & 1u);
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
+      for (int m = 32; m >= 1; m >>= 1) {  // rare path (NaN logits)
         free_lo = min(free_lo, __shfl_xor(free_lo, m, kWave));
         own_free |= __shfl_xor(own_free, m, kWave);
       }
@@ -307,7 +409,7 @@ __device__ void place_chunk(const int32_t *__restrict__ idx, int T, int K, int E
 
 // Counts, offsets, unique list from per-expert totals held one per thread.
 __device__ void finish_counts(const Routing &r, int T, int K, int E, int cnt_e,
-                              int *wave_tot, int *total, int *excl_out) {
+                              int *wave_tot, int *total, int *excl_out, int *uidx = nullptr) {
   const int e = threadIdx.x;
   const int v = e < E ? cnt_e : 0;
   const int excl = block_exclusive_scan(v, wave_tot, total);
@@ -319,6 +421,7 @@ __device__ void finish_counts(const Routing &r, int T, int K, int E, int cnt_e,
   const int flag = (e < E && v > 0) ? 1 : 0;
   const int pos = block_exclusive_scan(flag, wave_tot, total);
   if (flag) r.unique[pos] = e;
+  if (uidx && e < E) uidx[e] = flag ? pos : -1;
   if (e == 0) *r.n_unique = *total;
   if (excl_out) *excl_out = excl;
 }
@@ -354,6 +457,59 @@ __global__ __launch_bounds__(1024) void topk_permute_small(Routing r, int T, int
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] += __popcll(bm[e]);
     __syncthreads();
+  }
+}
+
+// Decode: one block of 1024 threads does top-K, the permute, the per-unit
+// M-chunk prefix and the (unit, token) -> h-row map.
+constexpr int kDecMC = 32;  // tokens per M-chunk of the decode expert kernels
+
+__global__ __launch_bounds__(1024) void route_decode_kernel(Routing r, int T, int E, int K,
+                                                            int32_t *__restrict__ slotmap) {
+  __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
+  __shared__ int cursor[COLI_MAX_EXPERTS];
+  __shared__ int cnt[COLI_MAX_EXPERTS];
+  __shared__ int uidx[COLI_MAX_EXPERTS];
+  __shared__ int wave_tot[16];
+  __shared__ int total;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  for (int t = wave; t < T; t += blockDim.x / kWave)
+    wave_topk(r.logits + size_t(t) * E, E, K, lane, r.idx + size_t(t) * K,
+              r.gates + size_t(t) * K);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
+    const int e = r.idx[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  const int ce = threadIdx.x < E ? cnt[threadIdx.x] : 0;
+  int excl = 0;
+  finish_counts(r, T, K, E, ce, wave_tot, &total, &excl, uidx);
+  const int nr = total;
+  if (threadIdx.x < E) cursor[threadIdx.x] = excl;
+  // M-chunk prefix over units in unique order (ascending expert id)
+  const int nch = (threadIdx.x < E && ce > 0) ? (ce + kDecMC - 1) / kDecMC : 0;
+  const int cpos = block_exclusive_scan(nch, wave_tot, &total);
+  if (threadIdx.x < E && ce > 0) r.chunk[uidx[threadIdx.x]] = cpos;
+  if (threadIdx.x == 0) {
+    r.chunk[nr] = total;
+    r.chunk[nr + 1] = total + (T + kDecMC - 1) / kDecMC;
+  }
+  __syncthreads();
+  for (int t0 = 0; t0 < T; t0 += kChunk) {
+    build_bitmap(r.idx, T, K, E, t0, bm);
+    place_chunk(r.idx, T, K, E, t0, bm, cursor, r.perm);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] += __popcll(bm[e]);
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < nr * T; i += blockDim.x) slotmap[i] = -1;
+  __syncthreads();
+  const int placed = r.offsets[E];
+  for (int j = threadIdx.x; j < placed; j += blockDim.x) {
+    const int p = r.perm[j];
+    slotmap[size_t(uidx[r.idx[p]]) * T + p / K] = j;
   }
 }
 
@@ -405,18 +561,28 @@ size_t permute_chunk_ints(int T, int E) {
 hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
                                 const void *wr, int w_bf16, int E,
                                 const float *bias, float *logits,
-                                hipStream_t s) {
+                                const DecodeBufs *xb, hipStream_t s) {
+  DecodeBufs b;
+  int split = 0;
+  if (xb && !x_bf16) {
+    b = *xb;
+    split = 1;
+  } else {
+    b.xh = b.xl = b.hh = b.hl = nullptr;
+    b.xsc = b.hsc = nullptr;
+    b.slotmap = nullptr;
+  }
 #define COLI_ROUTER_CASE(RW, TT)                                                  \
   {                                                                               \
     dim3 grid((E + 4 * RW - 1) / (4 * RW), (T + TT - 1) / TT);                   \
     if (x_bf16 && w_bf16)                                                         \
-      router_logits_kernel<RW, TT, true, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);  \
+      router_logits_kernel<RW, TT, true, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, b, split);  \
     else if (x_bf16)                                                              \
-      router_logits_kernel<RW, TT, true, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits); \
+      router_logits_kernel<RW, TT, true, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, b, split); \
     else if (w_bf16)                                                              \
-      router_logits_kernel<RW, TT, false, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits); \
+      router_logits_kernel<RW, TT, false, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, b, split); \
     else                                                                          \
-      router_logits_kernel<RW, TT, false, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);\
+      router_logits_kernel<RW, TT, false, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, b, split);\
   }
   if (T <= 2) COLI_ROUTER_CASE(1, 2)
   else COLI_ROUTER_CASE(4, 4)
@@ -431,6 +597,12 @@ hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
   dim3 grid((T + 63) / 64, (E + 63) / 64);
   router_mfma_kernel<<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);
   topk_kernel<<<dim3((T + 3) / 4), 256, 0, s>>>(logits, T, E, K, idx, gates);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_decode(const Routing &r, int T, int E, int K, int32_t *slotmap,
+                               hipStream_t s) {
+  route_decode_kernel<<<1, 1024, 0, s>>>(r, T, E, K, slotmap);
   return hipGetLastError();
 }
 
