@@ -30,22 +30,24 @@
 // contiguous 16-byte load.
 //
 // Kernels
-//   gateup_decode  item = (unit, 32 output rows, <= 32 tokens); 4 waves split
-//                  the K groups; partial sums meet in LDS; the epilogue writes
-//                  h' = gate_weight * SiLU(gate) * up in the split form with a
-//                  scale per (row, 32 columns).
-//   down_decode    item = (32 output rows, <= 32 tokens), output-stationary:
-//                  8 waves split the K groups, each streams every unit of the
-//                  batch (routed experts, then the shared one) and accumulates
-//                  y directly -- the gates already sit in h', so the combine
-//                  is the accumulation itself, in a fixed order (no atomics).
+//   gateup_decode  item = (unit, 32 output rows, <= 16*NMF tokens); 4 waves
+//                  split the K groups; partial sums meet in LDS; the epilogue
+//                  writes h' = gate_weight * SiLU(gate) * up in the split form
+//                  with a scale per (row, 32 columns).
+//   down_decode    item = (16 output rows, <= 16*NMF tokens), output-
+//                  stationary: 8 waves split the K groups, each streams every
+//                  unit of the batch (routed experts, then the shared one) and
+//                  accumulates y directly -- the gates already sit in h', so
+//                  the combine is the accumulation itself, in a fixed order
+//                  (no atomics).
+// Both keep the weights of several groups in flight per wave (register ring)
+// and fetch the next step's activations while the current one multiplies.
 #include "kernels.h"
 
 namespace coli {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kMC = 32;    // tokens per M-chunk (2 MFMA row fragments)
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -120,15 +122,28 @@ __device__ inline Unit unit_of(const LayerDev &L, const Routing &r, int u, int n
 }
 
 // ------------------------------------------------------------------ gate/up
-// grid: persistent over items; block: 4 waves (K split).
+// grid: persistent over items; block: 4 waves (K split).  Everything a group
+// step reads from global memory -- weights and activation fragments -- sits in
+// a ring of kD + 1 register slots filled kD steps ahead.  (Vector-memory
+// counters retire in issue order, so a load needed soon must not be issued
+// after loads needed late; one ring keeps every load kD steps ahead of use.)
+// The fp32 group scales of the item are staged once in LDS, coalesced.
 constexpr int kGW = 4;
-constexpr int kPF = 2;  // groups of weights prefetched ahead of the one in use
+constexpr int kSW = 32;  // groups of scales staged per window
 
+template <int NMF>
+struct GUSlot {
+  uint2 w[4];
+  f16x8 ah[NMF][2], al[NMF][2];
+};
+
+template <int NMF, int kD>
 __global__ __launch_bounds__(kGW * kWave) void gateup_decode(
     const uint16_t *__restrict__ xh, const uint16_t *__restrict__ xl,
     const float *__restrict__ xsc, int T, LayerDev L, Routing r,
     uint16_t *__restrict__ hh, uint16_t *__restrict__ hl, float *__restrict__ hsc) {
-  __shared__ f32x4 red[kGW][2][4][kWave];
+  __shared__ f32x4 red[kGW][NMF][4][kWave];
+  __shared__ float ssc[kGW][4 * 16][kSW + 1];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int H = L.H, I = L.I, K = L.K;
   const int GH = int(L.lay.GH);
@@ -136,8 +151,9 @@ __global__ __launch_bounds__(kGW * kWave) void gateup_decode(
   const int nr = *r.n_unique;
   const int n_items = r.chunk[nr + 1] * n_nt;
   const int n16 = lane % 16, q = lane / 16;
-  // this wave's K groups
   const int g0 = (GH * wave) / kGW, g1 = (GH * (wave + 1)) / kGW;
+  const int ng = g1 - g0;
+  constexpr int MC = 16 * NMF;
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int c = item / n_nt, nt = item % n_nt;
@@ -147,101 +163,98 @@ __global__ __launch_bounds__(kGW * kWave) void gateup_decode(
       if (r.chunk[mid] <= c) lo = mid; else hi = mid - 1;
     }
     const Unit U = unit_of(L, r, lo, nr, T);
-    const int jb = U.jb + (c - r.chunk[lo]) * kMC;
-    const int je = min(U.je, jb + kMC);
+    const int jb = U.jb + (c - r.chunk[lo]) * MC;
+    const int je = min(U.je, jb + MC);
     const int nmf = (je - jb + 15) / 16;
 
-    // A rows of this lane: token row of j = jb + mf*16 + n16
-    int64_t arow[2];
+    // A rows of this lane.  Rows past the chunk read token 0: an MFMA result
+    // row depends only on its own A row, and those rows are never stored.
+    // (Every ring load is unconditional and nothing inspects loaded data
+    // before it is used, so the in-order load counters never force an early
+    // wait.)
+    int64_t arow[NMF];
 #pragma unroll
-    for (int mf = 0; mf < 2; ++mf) {
+    for (int mf = 0; mf < NMF; ++mf) {
       const int j = jb + mf * 16 + n16;
-      arow[mf] = (j < je) ? int64_t(U.shared ? j : r.perm[j] / K) * H : -1;
+      arow[mf] = (j < je) ? int64_t(U.shared ? j : r.perm[j] / K) * H : 0;
     }
-    // B rows: frags 0,1 gate rows nt*32 + {0..15, 16..31}, frags 2,3 up rows
     const uint8_t *bq[4];
-    const float *bs[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int row = nt * 32 + 16 * (f & 1) + n16;
       bq[f] = U.blob + (f < 2 ? L.lay.gq : L.lay.uq) + size_t(row) * GH * 32 + 8 * q;
-      bs[f] = reinterpret_cast<const float *>(U.blob + (f < 2 ? L.lay.gs : L.lay.us)) +
-              size_t(row) * GH;
     }
-
-    f32x4 acc[2][4];
+    // this wave's scales, kSW groups at a time: lane l stages row l % 16 of
+    // fragment l / 16 (one contiguous run of the row's scales)
+    __syncthreads();  // previous item's readers of red are done
+    const float *srow;
+    {
+      const int f = lane / 16, row = nt * 32 + 16 * (f & 1) + n16;
+      srow = reinterpret_cast<const float *>(U.blob + (f < 2 ? L.lay.gs : L.lay.us)) +
+             size_t(row) * GH + g0;
+    }
+    auto stage = [&](int w0) {
+      const int n = min(kSW, ng - w0);
+      for (int g = 0; g < n; ++g) ssc[wave][lane][g] = srow[w0 + g];
+    };
+    stage(0);
+    f32x4 acc[NMF][4];
 #pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
+    for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
       for (int f = 0; f < 4; ++f) acc[mf][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // weight prefetch ring of kPF + 1 groups
-    uint2 wq[kPF + 1][4];
-    float ws[kPF + 1][4];
+    GUSlot<NMF> ring[kD + 1];
+    // step si reads group g0 + min(si, ng - 1); steps past ng get scale 0
+    auto load = [&](GUSlot<NMF> &sl, int si) {
+      const int g = g0 + min(si, ng - 1);
 #pragma unroll
-    for (int p = 0; p < kPF; ++p) {
-      const int g = g0 + p;
+      for (int f = 0; f < 4; ++f) sl.w[f] = *reinterpret_cast<const uint2 *>(bq[f] + size_t(g) * 32);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (g < g1) {
-          wq[p][f] = *reinterpret_cast<const uint2 *>(bq[f] + size_t(g) * 32);
-          ws[p][f] = bs[f][g];
+      for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int64_t off = arow[mf] + int64_t(g) * 64 + 32 * st + 8 * q;
+          sl.ah[mf][st] = *reinterpret_cast<const f16x8 *>(xh + off);
+          sl.al[mf][st] = *reinterpret_cast<const f16x8 *>(xl + off);
         }
-      }
+    };
+    // A wave with no K groups (H < 64 * kGW) skips the ring: its clamped
+    // group index would point before the row.
+    const int nsteps = ng > 0 ? (ng + kD) / (kD + 1) * (kD + 1) : 0;
+    if (ng > 0) {
+#pragma unroll
+      for (int p = 0; p < kD; ++p) load(ring[p], p);
     }
-    for (int gb = g0; gb < g1; gb += kPF + 1) {
+    for (int sb = 0; sb < nsteps; sb += kD + 1) {
 #pragma unroll
-      for (int p = 0; p <= kPF; ++p) {
-        const int g = gb + p;
-        if (g >= g1) break;
-        // issue the load kPF groups ahead into the slot freed last step
-        const int gn = g + kPF;
-        const int sn = (p + kPF) % (kPF + 1);
-        if (gn < g1) {
-#pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            wq[sn][f] = *reinterpret_cast<const uint2 *>(bq[f] + size_t(gn) * 32);
-            ws[sn][f] = bs[f][gn];
-          }
-        }
-        // activations of this group: 2 steps x (hi, lo) per M fragment
-        f16x8 ah[2][2], al[2][2];
-#pragma unroll
-        for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            if (mf < nmf && arow[mf] >= 0) {
-              const int64_t off = arow[mf] + int64_t(g) * 64 + 32 * st + 8 * q;
-              ah[mf][st] = *reinterpret_cast<const f16x8 *>(xh + off);
-              al[mf][st] = *reinterpret_cast<const f16x8 *>(xl + off);
-            } else {
-              ah[mf][st] = f16x8{};
-              al[mf][st] = f16x8{};
-            }
-          }
+      for (int p = 0; p <= kD; ++p) {
+        const int si = sb + p;
+        load(ring[(p + kD) % (kD + 1)], si + kD);
+        if (si % kSW == 0 && si > 0 && si < ng) stage(si);
+        const GUSlot<NMF> &sl = ring[p];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const f16x8 b0 = unpack_step(wq[p][f].x, wq[p][f].y, 0);
-          const f16x8 b1 = unpack_step(wq[p][f].x, wq[p][f].y, 1);
+          const f16x8 b0 = unpack_step(sl.w[f].x, sl.w[f].y, 0);
+          const f16x8 b1 = unpack_step(sl.w[f].x, sl.w[f].y, 1);
+          const float sc = si < ng ? ssc[wave][f * 16 + n16][si % kSW] : 0.0f;
 #pragma unroll
-          for (int mf = 0; mf < 2; ++mf) {
+          for (int mf = 0; mf < NMF; ++mf) {
             if (mf < nmf) {
-              f32x4 P = mfma(ah[mf][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
-              P = mfma(al[mf][0], b0, P);
-              P = mfma(ah[mf][1], b1, P);
-              P = mfma(al[mf][1], b1, P);
-              const float s = ws[p][f];
+              f32x4 P = mfma(sl.ah[mf][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
+              P = mfma(sl.al[mf][0], b0, P);
+              P = mfma(sl.ah[mf][1], b1, P);
+              P = mfma(sl.al[mf][1], b1, P);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[mf][f][i] = fmaf(P[i], s, acc[mf][f][i]);
+              for (int i = 0; i < 4; ++i) acc[mf][f][i] = fmaf(P[i], sc, acc[mf][f][i]);
             }
           }
         }
       }
     }
     // K-split partials meet in LDS; wave mf finishes M fragment mf
-    __syncthreads();
 #pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
+    for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
       for (int f = 0; f < 4; ++f) red[wave][mf][f][lane] = acc[mf][f];
     __syncthreads();
@@ -297,104 +310,122 @@ __global__ __launch_bounds__(kGW * kWave) void gateup_decode(
 }
 
 // ------------------------------------------------------------------ down
-constexpr int kDW = 8;  // waves per down block (K split)
+// Output-stationary: item = (16 output rows, M-chunk of 16*NMF tokens); kDW
+// waves split the K groups; each wave streams (unit, group) steps over every
+// unit of the batch.  The ring holds, kD steps ahead, a step's weights and
+// group scale, its activation fragments and the activation scales of its
+// result rows.  Unit data (blob, h row of each chunk token) is staged in LDS
+// in batches of kUB units.
+constexpr int kDW = 8;
+constexpr int kUB = 64;
 
+template <int NMF>
+struct DSlot {
+  uint2 w;
+  float s;
+  f16x8 ah[NMF][2], al[NMF][2];
+  float cs[NMF][2][4];  // activation scales of the result rows
+  float on[NMF][4];     // 1 if the result row's token is routed to the unit
+};
+
+template <int NMF, int kD>
 __global__ __launch_bounds__(kDW * kWave) void down_decode(
     const uint16_t *__restrict__ hh, const uint16_t *__restrict__ hl,
     const float *__restrict__ hsc, int T, LayerDev L, Routing r,
     const int32_t *__restrict__ slotmap, float *__restrict__ y) {
-  __shared__ f32x4 red[kDW][2][2][kWave];
+  __shared__ f32x4 red[kDW][NMF][kWave];
+  __shared__ const uint8_t *ublob[kUB];
+  __shared__ int rmap[kUB][16 * NMF];
+  constexpr int MC = 16 * NMF;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int H = L.H, I = L.I, K = L.K;
   const int GI = int(L.lay.GI);
-  const int n_nt = H / 32;
-  const int n_mc = (T + kMC - 1) / kMC;
+  const int n_nt = H / 16;
+  const int n_mc = (T + MC - 1) / MC;
   const int n_items = n_nt * n_mc;
   const int nr = *r.n_unique;
+  const int nunits = nr + 1;
   const int n16 = lane % 16, q = lane / 16;
   const int g0 = (GI * wave) / kDW, g1 = (GI * (wave + 1)) / kDW;
-  const int HS = I / 32;  // h scales per row
+  const int ng = g1 - g0;
+  const int HS = I / 32;
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int mc = item / n_nt, nt = item % n_nt;
-    const int t0 = mc * kMC;
-    const int nmf = (min(T, t0 + kMC) - t0 + 15) / 16;
-    f32x4 acc[2][2];
+    const int t0 = mc * MC;
+    const int nmf = (min(T, t0 + MC) - t0 + 15) / 16;
+    const int row = nt * 16 + n16;
+    f32x4 acc[NMF];
 #pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-      for (int f = 0; f < 2; ++f) acc[mf][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int u = 0; u <= nr; ++u) {
-      const bool shared = u == nr;
-      const uint8_t *blob = shared ? L.shared : L.experts + size_t(r.unique[u]) * L.lay.bytes;
-      // h rows of this unit for the A lanes (row n16 of each M fragment) and for
-      // the C lanes (rows 4q + i); -1 where the token is not routed here
-      int64_t arow[2];
-      int crow[2][4];
-#pragma unroll
-      for (int mf = 0; mf < 2; ++mf) {
-        const int t = t0 + mf * 16 + n16;
+    for (int ub = 0; ub < nunits; ub += kUB) {
+      const int nb = min(kUB, nunits - ub);
+      __syncthreads();
+      for (int i = threadIdx.x; i < nb * MC; i += blockDim.x) {
+        const int ul = i / MC, m = i % MC;
+        const int u = ub + ul, t = t0 + m;
         int j = -1;
-        if (t < T) j = shared ? T * K + t : slotmap[size_t(u) * T + t];
-        arow[mf] = j >= 0 ? int64_t(j) * I : -1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tc = t0 + mf * 16 + 4 * q + i;
-          int jc = -1;
-          if (tc < T) jc = shared ? T * K + tc : slotmap[size_t(u) * T + tc];
-          crow[mf][i] = jc;
-        }
+        if (t < T) j = (u == nr) ? T * K + t : slotmap[size_t(u) * T + t];
+        rmap[ul][m] = j;
+        if (m == 0)
+          ublob[ul] = (u == nr) ? L.shared : L.experts + size_t(r.unique[u]) * L.lay.bytes;
       }
-      const uint8_t *bq[2];
-      const float *bs[2];
+      __syncthreads();
+      const int S = nb * ng;
+      DSlot<NMF> ring[kD + 1];
+      // step s reads (unit, group) of min(s, S - 1); steps past S get scale 0
+      auto load = [&](DSlot<NMF> &sl, int s) {
+        const int sc_ = min(s, S - 1);
+        const int ul = sc_ / ng, g = g0 + sc_ % ng;
+        const uint8_t *blob = ublob[ul];
+        sl.w = *reinterpret_cast<const uint2 *>(blob + L.lay.dq + (size_t(row) * GI + g) * 32 + 8 * q);
+        sl.s = reinterpret_cast<const float *>(blob + L.lay.ds)[size_t(row) * GI + g];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int row = nt * 32 + 16 * f + n16;
-        bq[f] = blob + L.lay.dq + size_t(row) * GI * 32 + 8 * q;
-        bs[f] = reinterpret_cast<const float *>(blob + L.lay.ds) + size_t(row) * GI;
-      }
-      for (int g = g0; g < g1; ++g) {
-        uint2 wq[2];
-        float ws[2];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          wq[f] = *reinterpret_cast<const uint2 *>(bq[f] + size_t(g) * 32);
-          ws[f] = bs[f][g];
-        }
-        f16x8 ah[2][2], al[2][2];
-        float cs[2][2][4];
-#pragma unroll
-        for (int mf = 0; mf < 2; ++mf)
+        for (int mf = 0; mf < NMF; ++mf) {
+          const int j = rmap[ul][mf * 16 + n16];
+          // rows of tokens not routed here read h row 0 (finite) and are
+          // multiplied by on = 0 below
+          const int64_t jrow = j >= 0 ? int64_t(j) * I : 0;
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            if (mf < nmf && arow[mf] >= 0) {
-              const int64_t off = arow[mf] + int64_t(g) * 64 + 32 * st + 8 * q;
-              ah[mf][st] = *reinterpret_cast<const f16x8 *>(hh + off);
-              al[mf][st] = *reinterpret_cast<const f16x8 *>(hl + off);
-            } else {
-              ah[mf][st] = f16x8{};
-              al[mf][st] = f16x8{};
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              cs[mf][st][i] = (mf < nmf && crow[mf][i] >= 0)
-                                  ? hsc[size_t(crow[mf][i]) * HS + 2 * g + st]
-                                  : 0.0f;
+            const int64_t off = jrow + int64_t(g) * 64 + 32 * st + 8 * q;
+            sl.ah[mf][st] = *reinterpret_cast<const f16x8 *>(hh + off);
+            sl.al[mf][st] = *reinterpret_cast<const f16x8 *>(hl + off);
           }
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
+          for (int i = 0; i < 4; ++i) {
+            const int jc = rmap[ul][mf * 16 + 4 * q + i];
+            const size_t jcr = jc >= 0 ? size_t(jc) : 0;
+            sl.on[mf][i] = (jc >= 0 && s < S) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) sl.cs[mf][st][i] = hsc[jcr * HS + 2 * g + st];
+          }
+        }
+      };
+      // A wave with no K groups (I < 64 * kDW) skips the ring (S == 0).
+      const int nsteps = S > 0 ? (S + kD) / (kD + 1) * (kD + 1) : 0;
+      if (S > 0) {
+#pragma unroll
+        for (int p = 0; p < kD; ++p) load(ring[p], p);
+      }
+      for (int sb = 0; sb < nsteps; sb += kD + 1) {
+#pragma unroll
+        for (int p = 0; p <= kD; ++p) {
+          const int si = sb + p;
+          load(ring[(p + kD) % (kD + 1)], si + kD);
+          const DSlot<NMF> &sl = ring[p];
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const f16x8 b = unpack_step(wq[f].x, wq[f].y, st);
+            const f16x8 b = unpack_step(sl.w.x, sl.w.y, st);
 #pragma unroll
-            for (int mf = 0; mf < 2; ++mf) {
+            for (int mf = 0; mf < NMF; ++mf) {
               if (mf < nmf) {
-                f32x4 P = mfma(ah[mf][st], b, f32x4{0.f, 0.f, 0.f, 0.f});
-                P = mfma(al[mf][st], b, P);
+                f32x4 P = mfma(sl.ah[mf][st], b, f32x4{0.f, 0.f, 0.f, 0.f});
+                P = mfma(sl.al[mf][st], b, P);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                  acc[mf][f][i] = fmaf(P[i], ws[f] * cs[mf][st][i], acc[mf][f][i]);
+                  acc[mf][i] = fmaf(P[i], sl.s * sl.cs[mf][st][i] * sl.on[mf][i], acc[mf][i]);
               }
             }
           }
@@ -403,21 +434,17 @@ __global__ __launch_bounds__(kDW * kWave) void down_decode(
     }
     __syncthreads();
 #pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-      for (int f = 0; f < 2; ++f) red[wave][mf][f][lane] = acc[mf][f];
+    for (int mf = 0; mf < NMF; ++mf) red[wave][mf][lane] = acc[mf];
     __syncthreads();
-    // waves 0..3 finish (mf, f) = (wave / 2, wave % 2)
-    if (wave < 4 && wave / 2 < nmf) {
-      const int mf = wave / 2, f = wave % 2;
-      f32x4 s = red[0][mf][f][lane];
+    if (wave < nmf) {
+      const int mf = wave;
+      f32x4 sum = red[0][mf][lane];
 #pragma unroll
-      for (int w = 1; w < kDW; ++w) s += red[w][mf][f][lane];
-      const int o = nt * 32 + 16 * f + n16;
+      for (int w = 1; w < kDW; ++w) sum += red[w][mf][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + mf * 16 + 4 * q + i;
-        if (t < T) y[int64_t(t) * H + o] = s[i];
+        if (t < T) y[int64_t(t) * H + row] = sum[i];
       }
     }
   }
@@ -427,17 +454,29 @@ __global__ __launch_bounds__(kDW * kWave) void down_decode(
 
 hipError_t launch_ffn_decode(const LayerDev &L, const DecodeBufs &b, int T,
                              const Routing &r, float *y, hipStream_t s, hipEvent_t *ev) {
-  // gate/up items: sum over units of ceil(n/32) chunks, times I/32 row tiles
+  // Every unit's token count is at most T, so T <= 16 needs one M fragment;
+  // the route kernel's chunk prefix (chunks of 32 tokens) then counts one
+  // chunk per unit, which equals the 16-token chunking.
+  const bool one = T <= 16;
+  const int mc = one ? 16 : 32;
   const int max_units = (T * L.K < L.E ? T * L.K : L.E) + 1;
-  const int64_t max_chunks = int64_t(T) * L.K / kMC + max_units + (T + kMC - 1) / kMC;
+  const int64_t max_chunks = int64_t(T) * L.K / mc + max_units + (T + mc - 1) / mc;
   const int64_t items = max_chunks * (L.I / 32);
   const int cap = 4096;
-  gateup_decode<<<unsigned(items < cap ? items : cap), kGW * kWave, 0, s>>>(
-      b.xh, b.xl, b.xsc, T, L, r, b.hh, b.hl, b.hsc);
+  const unsigned gblocks = unsigned(items < cap ? items : cap);
+  if (one)
+    gateup_decode<1, 4><<<gblocks, kGW * kWave, 0, s>>>(b.xh, b.xl, b.xsc, T, L, r, b.hh, b.hl,
+                                                       b.hsc);
+  else
+    gateup_decode<2, 2><<<gblocks, kGW * kWave, 0, s>>>(b.xh, b.xl, b.xsc, T, L, r, b.hh, b.hl,
+                                                       b.hsc);
   if (ev) (void)hipEventRecord(ev[0], s);
-  const int64_t ditems = int64_t(L.H / 32) * ((T + kMC - 1) / kMC);
-  down_decode<<<unsigned(ditems < cap ? ditems : cap), kDW * kWave, 0, s>>>(
-      b.hh, b.hl, b.hsc, T, L, r, b.slotmap, y);
+  const int64_t ditems = int64_t(L.H / 16) * ((T + mc - 1) / mc);
+  const unsigned dblocks = unsigned(ditems < cap ? ditems : cap);
+  if (one)
+    down_decode<1, 4><<<dblocks, kDW * kWave, 0, s>>>(b.hh, b.hl, b.hsc, T, L, r, b.slotmap, y);
+  else
+    down_decode<2, 2><<<dblocks, kDW * kWave, 0, s>>>(b.hh, b.hl, b.hsc, T, L, r, b.slotmap, y);
   if (ev) (void)hipEventRecord(ev[1], s);
   return hipGetLastError();
 }
