@@ -32,6 +32,7 @@ bool layer_shape_ok(int H, int I, int E, int K) {
 struct WsLayout {
   size_t logits, idx, gates, counts, offsets, perm, unique, n_unique, chunk, h, slot;
   size_t xh, xl, xsc, hh, hl, hsc, slotmap;  // decode only
+  size_t xdig, xcorr, nxsc, hn;               // decode, single-token path
   size_t total;
 };
 WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
@@ -50,6 +51,7 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
   if (chunk < size_t(E) + 2) chunk = size_t(E) + 2;
   w.chunk = o; o += align256(chunk * 4);
   w.h = w.slot = w.xh = w.xl = w.xsc = w.hh = w.hl = w.hsc = w.slotmap = 0;
+  w.xdig = w.xcorr = w.nxsc = w.hn = 0;
   if (mode == COLI_PREFILL) {
     w.h = o; o += align256((TK + T) * size_t(I) * 2);
     w.slot = o; o += align256((TK + T) * size_t(H) * 2);
@@ -62,6 +64,11 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
     w.hl = o; o += align256((TK + T) * size_t(I) * 2);
     w.hsc = o; o += align256((TK + T) * size_t(I / 32) * 4);
     w.slotmap = o; o += align256(units * size_t(T) * 4);
+    const size_t GH = size_t(groups_of(H));
+    w.xdig = o; o += align256(size_t(T) * GH * 256);
+    w.xcorr = o; o += align256(size_t(T) * GH * 16);
+    w.nxsc = o; o += align256(size_t(T) * 4);
+    w.hn = o; o += align256((units + 1) * size_t(I) * 4);
   }
   w.total = o;
   return w;
@@ -248,6 +255,19 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
     b.hl = reinterpret_cast<uint16_t *>(ws + w.hl);
     b.hsc = reinterpret_cast<float *>(ws + w.hsc);
     b.slotmap = reinterpret_cast<int32_t *>(ws + w.slotmap);
+    if (narrow_supported(d, T)) {
+      NarrowBufs nb;
+      nb.xdig = reinterpret_cast<int8_t *>(ws + w.xdig);
+      nb.xcorr = reinterpret_cast<int32_t *>(ws + w.xcorr);
+      nb.xsc = reinterpret_cast<float *>(ws + w.nxsc);
+      nb.hn = reinterpret_cast<float *>(ws + w.hn);
+      e = launch_router_narrow(reinterpret_cast<const float *>(x), T, L->H, L->w_router, wbf,
+                               L->E, L->router_bias, r.logits, nb, s);
+      if (e != hipSuccess) return COLI_EDEVICE;
+      if (ev) (void)hipEventRecord(ev[0], s);
+      return dev_status(launch_ffn_narrow(d, nb, r.logits, r.idx, r.gates,
+                                          reinterpret_cast<float *>(y), s, ev ? ev + 1 : nullptr));
+    }
     e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, L->router_bias, r.logits,
                              &b, s);
     if (e != hipSuccess) return COLI_EDEVICE;

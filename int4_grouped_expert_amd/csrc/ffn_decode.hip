@@ -193,9 +193,28 @@ __global__ __launch_bounds__(kGW * kWave) void gateup_decode(
       srow = reinterpret_cast<const float *>(U.blob + (f < 2 ? L.lay.gs : L.lay.us)) +
              size_t(row) * GH + g0;
     }
+    // all of a window's loads are issued before the first LDS store
+    const bool vec = ((GH | g0) & 3) == 0;
     auto stage = [&](int w0) {
       const int n = min(kSW, ng - w0);
-      for (int g = 0; g < n; ++g) ssc[wave][lane][g] = srow[w0 + g];
+      if (vec && n == kSW) {
+        float4 v[kSW / 4];
+#pragma unroll
+        for (int k = 0; k < kSW / 4; ++k) v[k] = reinterpret_cast<const float4 *>(srow + w0)[k];
+#pragma unroll
+        for (int k = 0; k < kSW / 4; ++k) {
+          ssc[wave][lane][4 * k] = v[k].x;
+          ssc[wave][lane][4 * k + 1] = v[k].y;
+          ssc[wave][lane][4 * k + 2] = v[k].z;
+          ssc[wave][lane][4 * k + 3] = v[k].w;
+        }
+      } else {
+        float v[kSW];
+#pragma unroll
+        for (int g = 0; g < kSW; ++g) v[g] = g < n ? srow[w0 + g] : 0.0f;
+#pragma unroll
+        for (int g = 0; g < kSW; ++g) ssc[wave][lane][g] = v[g];
+      }
     };
     stage(0);
     f32x4 acc[NMF][4];
@@ -233,21 +252,32 @@ __global__ __launch_bounds__(kGW * kWave) void gateup_decode(
         load(ring[(p + kD) % (kD + 1)], si + kD);
         if (si % kSW == 0 && si > 0 && si < ng) stage(si);
         const GUSlot<NMF> &sl = ring[p];
+        float sc[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) sc[f] = si < ng ? ssc[wave][f * 16 + n16][si % kSW] : 0.0f;
+        f16x8 b0[4], b1[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const f16x8 b0 = unpack_step(sl.w[f].x, sl.w[f].y, 0);
-          const f16x8 b1 = unpack_step(sl.w[f].x, sl.w[f].y, 1);
-          const float sc = si < ng ? ssc[wave][f * 16 + n16][si % kSW] : 0.0f;
+          b0[f] = unpack_step(sl.w[f].x, sl.w[f].y, 0);
+          b1[f] = unpack_step(sl.w[f].x, sl.w[f].y, 1);
+        }
 #pragma unroll
-          for (int mf = 0; mf < NMF; ++mf) {
-            if (mf < nmf) {
-              f32x4 P = mfma(sl.ah[mf][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
-              P = mfma(sl.al[mf][0], b0, P);
-              P = mfma(sl.ah[mf][1], b1, P);
-              P = mfma(sl.al[mf][1], b1, P);
+        for (int mf = 0; mf < NMF; ++mf) {
+          if (NMF == 1 || mf < nmf) {
+            // four independent chains, interleaved
+            f32x4 P[4];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[mf][f][i] = fmaf(P[i], sc, acc[mf][f][i]);
-            }
+            for (int f = 0; f < 4; ++f) P[f] = mfma(sl.ah[mf][0], b0[f], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int f = 0; f < 4; ++f) P[f] = mfma(sl.al[mf][0], b0[f], P[f]);
+#pragma unroll
+            for (int f = 0; f < 4; ++f) P[f] = mfma(sl.ah[mf][1], b1[f], P[f]);
+#pragma unroll
+            for (int f = 0; f < 4; ++f) P[f] = mfma(sl.al[mf][1], b1[f], P[f]);
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[mf][f][i] = fmaf(P[f][i], sc[f], acc[mf][f][i]);
           }
         }
       }

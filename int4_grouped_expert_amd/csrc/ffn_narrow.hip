@@ -1,0 +1,470 @@
+// ffn_narrow.hip -- the routed + shared expert FFN of one decode token:
+// int4-g64 planar weights streamed from HBM straight into int8 matrix-core
+// products.
+//
+// Method: page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
+// section 权重转换 -- the expert FFN reads the planar bytes as they are (byte k
+// of a 64-group: element k low nibble, element k+32 high nibble, u = q + 8;
+// weight = s * (u - 8)); SiLU(gate) * up, then down, then the gate-weighted
+// sum over the selected experts plus the shared expert (page "Colibri 深度解析",
+// sections 四 and 十一).  The token's top-K runs inside the gate/up kernel.
+//
+// Arithmetic.  An activation vector a is held in fixed point, a = A * 2^-e
+// with one power-of-two scale per vector and |A| <= 2^27, and A is split into
+// four balanced base-128 digits, A = d0 2^21 + d1 2^14 + d2 2^7 + d3, each in
+// [-64, 64] (int8).  A weight nibble u (0..15) is already an int8, so the
+// v_mfma_i32_16x16x64_i8 sum over a group, sum_k d_k u_k, is exact in int32;
+// the format's -8 enters as the accumulator's initial value, -8 * sum_k d_k,
+// stored with the digits.  Per group the four plane sums are recombined
+// exactly in int32 pairs, rounded once to fp32 and scaled by the fp32 group
+// scale.  Every element within a factor 16 of the vector's largest is
+// represented exactly, smaller ones to 2^-28 of it: the products are at least
+// as accurate as an fp32 dot product.  The unpack costs 3 32-bit operations
+// per 8 weights.
+//
+// MFMA layout (16x16x64 i8: lane l holds A row / B column l % 16 and 16
+// bytes of k for the k-quarter l / 16; the result lane l holds rows
+// 4*(l/16)+i, column l % 16).  One token leaves 15 of 16 A rows free; they
+// carry work instead.  A row m = 4 s + p is digit plane p of slot s, and slot
+// s = (kappa, j) = (s / 2, s % 2) names one of four groups.  B column
+// n = r + 8 kappa is weight row r of an 8-row fragment, and its lane quarter q
+// loads bytes 16 (q % 2) .. +15 of group 4c + 2 kappa + q / 2 (so the 8 lanes
+// of a row read one contiguous 128-byte run: groups 4c .. 4c+3).  A row m is
+// zero in the k-quarters whose group is not its slot's (q / 2 != j), so result
+// row 4 s + p of column n is the plane-p sum over group 4c + 2 kappa_s + j_s
+// of weight row r: meaningful where kappa_s = kappa(n), ignored elsewhere.
+// Each 16-byte lane load feeds two MFMAs, one per 8-byte half.
+//
+// Digit runs ("A order"): the 64 digits of a (vector, group, plane) are four
+// 16-byte runs; run rho holds the digits of elements 8 rho .. 8 rho + 7, then
+// 32 + 8 rho .. 32 + 8 rho + 7 -- the k order of the B half that holds group
+// bytes 8 rho .. 8 rho + 7 after the unpack {d0 & M, d1 & M, (d0 >> 4) & M,
+// (d1 >> 4) & M}, M = 0x0F0F0F0F (d0, d1 = the half's two dwords).
+//
+// Kernels
+//   gateup_narrow  persistent; item = (unit, 8 rows of I): a gate and an up
+//                  fragment.  The block's waves split the K groups; each wave
+//                  keeps the x digits of its K slice in registers for the
+//                  whole launch and a register ring one item deep of weight
+//                  loads.  Partials meet in LDS; one wave (rotating) writes
+//                  h' = gate_weight * SiLU(gate) * up in fp32.
+//   down_narrow    persistent, output-stationary; item = 8 rows of y, all
+//                  units.  Wave w owns K chunk w (256 columns of I) of every
+//                  unit: it turns its slices of h' into digits in its own LDS
+//                  area once, then streams (item, unit) steps through a ring
+//                  one item deep.  The gates sit in h', so the combine is the
+//                  accumulation itself, in a fixed order (no atomics).
+#include "kernels.h"
+#include "wave.h"
+
+namespace coli {
+namespace {
+
+constexpr int kW = 64;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ inline i32x4 mfma_i8(const i32x4 &a, const i32x4 &b, const i32x4 &c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// The B operand of one 8-byte half (dwords d0, d1 = bytes 8h .. 8h+7 of a
+// lane's 16): low nibbles of the 8 bytes, then high nibbles.
+__device__ inline i32x4 unpack_half(uint32_t d0, uint32_t d1) {
+  const uint32_t M = 0x0F0F0F0Fu;
+  return i32x4{int(d0 & M), int(d1 & M), int((d0 >> 4) & M), int((d1 >> 4) & M)};
+}
+
+// Plane sums r0..r3 (|r| < 2^17) -> one fp32 value
+// (r0 2^7 + r1) 2^14 + (r2 2^7 + r3); both halves are exact in fp32.
+__device__ inline float planes_to_f32(const i32x4 &r) {
+  const int hi = r[0] * 128 + r[1];
+  const int lo = r[2] * 128 + r[3];
+  return fmaf(float(hi), 16384.0f, float(lo));
+}
+
+template <int kCtrl>
+__device__ inline float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+// A register copy the compiler cannot fold away: the copy is made now, so the
+// source register is free for the slot's next load.
+__device__ inline float keep(float v) {
+  float o;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(o) : "v"(v));
+  return o;
+}
+
+// s_waitcnt vmcnt(0) as an instruction the compiler's wait tracking sees: after
+// it nothing is pending, so loads issued before a loop in an order the loop
+// does not follow cannot leave the loop waiting for all of them every trip.
+__device__ inline void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Step boundary of a ring: nothing is scheduled across it.  The refills must
+// leave in the order their slots are consumed and no slot may be touched
+// before its turn (the load counter retires in issue order, so an early use
+// of a late slot waits for nearly every load in flight).
+__device__ inline void step_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Barrier for LDS traffic only: vector-memory loads stay in flight.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Result lanes whose slot belongs to the lane's column (kappa_s = kappa(n)).
+__device__ inline bool result_valid(int lane) { return ((lane / 16) >> 1) == ((lane % 16) >> 3); }
+
+// Per-row total of a result value over the valid lanes of the wave: lane r
+// (r < 8) receives the sum for fragment row r.
+__device__ inline float fold_rows(float v, int lane) {
+  v = result_valid(lane) ? v : 0.0f;
+  v += dpp_row<0x128>(v);  // row_ror:8 -- columns r and r + 8
+  v += __shfl_xor(v, 16, kW);
+  v += __shfl_xor(v, 32, kW);
+  return v;
+}
+
+// ------------------------------------------------------------------ gate/up
+constexpr int kMaxWaves = 16;
+
+template <int NC>
+__global__ __launch_bounds__(kW * 8) __attribute__((amdgpu_waves_per_eu(3)))
+void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
+                   int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
+  __shared__ int32_t sidx[COLI_NARROW_MAX_K];
+  __shared__ float sgate[COLI_NARROW_MAX_K];
+  __shared__ float red[2][kMaxWaves][2][8];
+  const int lane = threadIdx.x % kW, wave = threadIdx.x / kW;
+  const int nw = blockDim.x / kW;
+  const int I = L.I, E = L.E, K = L.K;
+  const int GH = int(L.lay.GH);
+  const int nrb = I / 8;
+  const int n_items = (K + 1) * nrb;
+  if (int(blockIdx.x) >= n_items) return;
+
+  if (wave == 0) wave_topk(logits, E, K, lane, sidx, sgate);
+  lds_barrier();
+  if (blockIdx.x == 0 && int(threadIdx.x) < K) {
+    idx_out[threadIdx.x] = sidx[threadIdx.x];
+    gate_out[threadIdx.x] = sgate[threadIdx.x];
+  }
+
+  const int n = lane % 16, q = lane / 16;
+  const int r = n % 8, kap = n / 8;
+  // x digits of this wave's K slice (chunks wave*NC .. +NC-1), A rows
+  const int sA = n / 4, pA = n % 4;  // A row n: slot sA, plane pA
+  const int ksA = sA / 2, jsA = sA % 2;
+  const bool actA = (q / 2) == jsA;
+  const int rho0 = 2 * (q % 2);
+  i32x4 A[NC][2], C[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int g0 = 4 * (wave * NC + c);
+    const int8_t *base = nb.xdig + (size_t(g0 + 2 * ksA + jsA) * 4 + pA) * 64 + 16 * rho0;
+    const i32x4 z = {0, 0, 0, 0};
+    A[c][0] = actA ? *reinterpret_cast<const i32x4 *>(base) : z;
+    A[c][1] = actA ? *reinterpret_cast<const i32x4 *>(base + 16) : z;
+    C[c] = *reinterpret_cast<const i32x4 *>(nb.xcorr + size_t(g0 + q) * 4);
+  }
+  const float xs = nb.xsc[0];
+
+  // item -> this lane's weight and scale pointers (chunk 0 of its K slice).
+  // The weights are the B lane's (group 4c + 2 kappa + q / 2); the scale is
+  // the result lane's (slot q: group 4c + q).
+  const size_t goff = size_t(wave) * NC * 4 + 2 * kap + q / 2;
+  const size_t soff = size_t(wave) * NC * 4 + q;
+  struct Ptrs {
+    const uint8_t *wg, *wu;
+    const float *sg, *su;
+  };
+  auto ptrs = [&](int it) {
+    const int u = it / nrb, rb = it - u * nrb;
+    const uint8_t *blob = u < K ? L.experts + size_t(sidx[u]) * L.lay.bytes : L.shared;
+    const size_t row = size_t(rb) * 8 + r;
+    Ptrs p;
+    p.wg = blob + L.lay.gq + (row * GH + goff) * 32 + 16 * (q % 2);
+    p.wu = blob + L.lay.uq + (row * GH + goff) * 32 + 16 * (q % 2);
+    p.sg = reinterpret_cast<const float *>(blob + L.lay.gs) + row * GH + soff;
+    p.su = reinterpret_cast<const float *>(blob + L.lay.us) + row * GH + soff;
+    return p;
+  };
+
+  uint4 rw[2][NC];
+  float rs[2][NC];
+  int it = blockIdx.x;
+  {
+    const Ptrs p = ptrs(it);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      rw[0][c] = *reinterpret_cast<const uint4 *>(p.wg + 128 * c);
+      rs[0][c] = p.sg[4 * c];
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      rw[1][c] = *reinterpret_cast<const uint4 *>(p.wu + 128 * c);
+      rs[1][c] = p.su[4 * c];
+    }
+  }
+  wait_all_loads();
+  int buf = 0, k_it = 0;
+  for (; it < n_items; it += gridDim.x, ++k_it) {
+    // the next item's loads replace each slot as it is consumed; past the
+    // end they re-read the current item (valid addresses, never used)
+    const int nx = it + int(gridDim.x) < n_items ? it + int(gridDim.x) : it;
+    const Ptrs np = ptrs(nx);
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        // consume the slot before its refill is issued (the refill can then
+        // land in the same registers: no copies around the loop)
+        const i32x4 b0 = unpack_half(rw[f][c].x, rw[f][c].y);
+        const i32x4 b1 = unpack_half(rw[f][c].z, rw[f][c].w);
+        const float sv = keep(rs[f][c]);
+        rw[f][c] = *reinterpret_cast<const uint4 *>((f ? np.wu : np.wg) + 128 * c);
+        rs[f][c] = (f ? np.su : np.sg)[4 * c];
+        step_fence();
+        i32x4 P = mfma_i8(A[c][0], b0, C[c]);
+        P = mfma_i8(A[c][1], b1, P);
+        acc[f] = fmaf(planes_to_f32(P), sv, acc[f]);
+      }
+    const float vg = fold_rows(acc[0], lane);
+    const float vu = fold_rows(acc[1], lane);
+    if (lane < 8) {
+      red[buf][wave][0][lane] = vg;
+      red[buf][wave][1][lane] = vu;
+    }
+    lds_barrier();
+    if (wave == k_it % nw && lane < 16) {
+      const int f = lane / 8, rr = lane % 8;
+      float t = 0.0f;
+      for (int w = 0; w < nw; ++w) t += red[buf][w][f][rr];
+      const float upv = dpp_row<0x128>(t);  // lane rr <- lane rr + 8 (up)
+      if (lane < 8) {
+        const int u = it / nrb, rb = it - u * nrb;
+        const float gw = u < K ? sgate[u] : 1.0f;
+        const float h = gw * silu(t * xs) * (upv * xs);
+        nb.hn[size_t(u) * I + rb * 8 + rr] = h;
+      }
+    }
+    buf ^= 1;
+  }
+}
+
+// ------------------------------------------------------------------ down
+// Per-wave LDS area: digits [NU][4 planes][4 groups][64], corrections
+// [NU][4 groups][4 planes] int32, then 32 zero bytes (the A rows of inactive
+// k-quarters read them).
+template <int NU>
+constexpr int down_wave_bytes() { return NU * (1024 + 64) + 32; }
+
+constexpr int kDownMaxWaves = 8;
+
+template <int NU>
+__global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb, LayerDev L,
+                                                             const int32_t *__restrict__ idx,
+                                                             float *__restrict__ y) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  __shared__ float red[2][kMaxWaves][8];
+  const int lane = threadIdx.x % kW, wave = threadIdx.x / kW;
+  const int nw = blockDim.x / kW;
+  const int H = L.H, I = L.I, K = L.K;
+  const int GI = int(L.lay.GI);
+  const int n_items = H / 8;
+  if (int(blockIdx.x) >= n_items) return;
+  uint8_t *my = dyn + wave * down_wave_bytes<NU>();
+  int8_t *dig = reinterpret_cast<int8_t *>(my);
+  int32_t *corr = reinterpret_cast<int32_t *>(my + NU * 1024);
+  uint8_t *zero = my + NU * 1088;
+
+  const int n = lane % 16, q = lane / 16;
+  const int r = n % 8, kap = n / 8;
+  const uint8_t *blob[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    blob[u] = u < K ? L.experts + size_t(idx[u]) * L.lay.bytes : L.shared;
+
+  // weights: the B lane's group (4 wave + 2 kappa + q / 2); scale: the result
+  // lane's slot (group 4 wave + q)
+  const size_t goff = size_t(wave) * 4 + 2 * kap + q / 2;
+  const size_t soff = size_t(wave) * 4 + q;
+  auto loff = [&](int it) { return (size_t(it) * 8 + r) * GI + goff; };
+  auto sof = [&](int it) { return (size_t(it) * 8 + r) * GI + soff; };
+  uint4 rw[NU];
+  float rs[NU];
+  int it = blockIdx.x;
+  {
+    const size_t o = loff(it), so = sof(it);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      rw[u] = *reinterpret_cast<const uint4 *>(blob[u] + L.lay.dq + o * 32 + 16 * (q % 2));
+      rs[u] = reinterpret_cast<const float *>(blob[u] + L.lay.ds)[so];
+    }
+  }
+
+  // h' chunk `wave` of every unit -> digits in this wave's LDS area.  Lane l
+  // holds elements 4l .. 4l+3 of the chunk: group l / 16, element 4 (l % 16).
+  float sa[NU];
+  {
+    float4 hv[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      hv[u] = *reinterpret_cast<const float4 *>(nb.hn + size_t(u) * I + 256 * wave + 4 * lane);
+    if (lane < 8) reinterpret_cast<uint32_t *>(zero)[lane] = 0u;
+    const int gl = lane / 16, pos = aorder_pos(4 * (lane % 16));
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const float v[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+      float m = 0.0f;
+      bool bad = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, fabsf(v[i]));
+        bad |= !__builtin_isfinite(v[i]);
+      }
+      m = wave_max(m);
+      bad = __any(bad);
+      const int e = digit_exponent(m);
+      sa[u] = bad ? __builtin_nanf("") : ldexpf(1.0f, -e);
+      int d[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) digits4(v[i], e, d[i]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        *reinterpret_cast<uint32_t *>(dig + ((u * 4 + p) * 4 + gl) * 64 + pos) = pack_plane(d, p);
+        const int sum = row16_sum_i(d[0][p] + d[1][p] + d[2][p] + d[3][p]);
+        if ((lane % 16) == 0) corr[(u * 4 + gl) * 4 + p] = -8 * sum;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+
+  // A-row LDS addresses (inactive k-quarters read the zero bytes) and the
+  // correction of the result lane's slot (group q of the chunk)
+  const int sA = n / 4, pA = n % 4;
+  const bool actA = (q / 2) == (sA % 2);
+  const int gA = 2 * (sA / 2) + (sA % 2);
+  const int a_base = actA ? ((pA * 4 + gA) * 64 + 16 * (2 * (q % 2))) : NU * 1088;
+  const int a_step = actA ? 1024 : 0;
+
+  wait_all_loads();
+  int buf = 0, k_it = 0;
+  for (; it < n_items; it += gridDim.x, ++k_it) {
+    const int nx = it + int(gridDim.x) < n_items ? it + int(gridDim.x) : it;
+    const size_t o = loff(nx), so = sof(nx);
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const i32x4 b0 = unpack_half(rw[u].x, rw[u].y);
+      const i32x4 b1 = unpack_half(rw[u].z, rw[u].w);
+      const float sv = keep(rs[u]) * sa[u];
+      rw[u] = *reinterpret_cast<const uint4 *>(blob[u] + L.lay.dq + o * 32 + 16 * (q % 2));
+      rs[u] = reinterpret_cast<const float *>(blob[u] + L.lay.ds)[so];
+      step_fence();
+      const int8_t *ap = dig + a_base + u * a_step;
+      const i32x4 a0 = *reinterpret_cast<const i32x4 *>(ap);
+      const i32x4 a1 = *reinterpret_cast<const i32x4 *>(ap + 16);
+      const i32x4 c0 = *reinterpret_cast<const i32x4 *>(corr + (u * 4 + q) * 4);
+      i32x4 P = mfma_i8(a0, b0, c0);
+      P = mfma_i8(a1, b1, P);
+      acc = fmaf(planes_to_f32(P), sv, acc);
+    }
+    const float v = fold_rows(acc, lane);
+    if (lane < 8) red[buf][wave][lane] = v;
+    lds_barrier();
+    if (wave == k_it % nw && lane < 8) {
+      float t = 0.0f;
+      for (int w = 0; w < nw; ++w) t += red[buf][w][lane];
+      y[size_t(it) * 8 + lane] = t;
+    }
+    buf ^= 1;
+  }
+}
+
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  return n;
+}
+
+// Waves splitting the gate/up K groups: NCH = H / 256 chunks, NC = NCH / waves
+// chunks per wave (1..6).
+int gateup_waves(int H, int *nc) {
+  const int nch = H / 256;
+  const int pref[] = {4, 8, 2, 1};
+  for (int w : pref)
+    if (nch % w == 0 && nch / w >= 1 && nch / w <= 6) {
+      *nc = nch / w;
+      return w;
+    }
+  return 0;
+}
+
+template <int NU>
+hipError_t launch_down(const LayerDev &L, const NarrowBufs &nb, const int32_t *idx, float *y,
+                       int grid, hipStream_t s) {
+  const int nw = L.I / 256;
+  const size_t lds = size_t(nw) * down_wave_bytes<NU>();
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_narrow<NU>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  down_narrow<NU><<<grid, nw * kW, lds, s>>>(nb, L, idx, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool narrow_supported(const LayerDev &L, int T) {
+  if (T != 1 || L.H % 256 || L.I % 256 || L.K > COLI_NARROW_MAX_K) return false;
+  int nc = 0;
+  if (!gateup_waves(L.H, &nc)) return false;
+  const int nw = L.I / 256;
+  if (nw > kDownMaxWaves) return false;
+  const size_t lds = size_t(nw) * size_t((L.K + 1) * (1024 + 64) + 32);
+  return lds + sizeof(float) * 2 * kMaxWaves * 8 <= 160 * 1024;
+}
+
+hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const float *logits,
+                             int32_t *idx, float *gates, float *y, hipStream_t s,
+                             hipEvent_t *ev) {
+  const int cus = cu_count();
+  int nc = 0;
+  const int gw = gateup_waves(L.H, &nc);
+  const int n_items = (L.K + 1) * (L.I / 8);
+  const int ggrid = n_items < 3 * cus ? n_items : 3 * cus;
+#define COLI_GU(NC) \
+  case NC: gateup_narrow<NC><<<ggrid, gw * kW, 0, s>>>(nb, L, logits, idx, gates); break;
+  switch (nc) {
+    COLI_GU(1) COLI_GU(2) COLI_GU(3) COLI_GU(4) COLI_GU(5) COLI_GU(6)
+    default: return hipErrorInvalidValue;
+  }
+#undef COLI_GU
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev) (void)hipEventRecord(ev[0], s);
+  const int d_items = L.H / 8;
+  const int dgrid = d_items < cus ? d_items : cus;
+#define COLI_DN(NU) \
+  case NU: e = launch_down<NU>(L, nb, idx, y, dgrid, s); break;
+  switch (L.K + 1) {
+    COLI_DN(2) COLI_DN(3) COLI_DN(4) COLI_DN(5) COLI_DN(6) COLI_DN(7) COLI_DN(8) COLI_DN(9)
+    COLI_DN(10) COLI_DN(11) COLI_DN(12) COLI_DN(13) COLI_DN(14) COLI_DN(15) COLI_DN(16)
+    COLI_DN(17)
+    default: return hipErrorInvalidValue;
+  }
+#undef COLI_DN
+  if (e != hipSuccess) return e;
+  if (ev) (void)hipEventRecord(ev[1], s);
+  return hipSuccess;
+}
+
+}  // namespace coli

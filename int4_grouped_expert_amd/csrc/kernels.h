@@ -67,6 +67,20 @@ struct DecodeBufs {
   int32_t *slotmap;
 };
 
+// Single-token decode buffers (inside the workspace).  xdig: x as four int8
+// digit planes, [T][GH][4 planes][64] in "A order" (see ffn_narrow.hip), value
+// = digits * xsc[t]; xcorr [T][GH][4]: -8 * (sum of the group's digits) per
+// plane; xsc [T]: 2^-e, NaN if the token holds a non-finite value; hn
+// [units][I]: h' = gate_weight * SiLU(gate) * up in fp32, units in top-K order
+// then the shared expert.
+struct NarrowBufs {
+  int8_t *xdig;
+  int32_t *xcorr;
+  float *xsc;
+  float *hn;
+};
+#define COLI_NARROW_MAX_K 16
+
 // One layer as the kernels see it.
 struct LayerDev {
   int H, I, E, K;
@@ -106,11 +120,25 @@ hipError_t launch_topk_permute(const Routing &r, int T, int E, int K,
 hipError_t launch_route_decode(const Routing &r, int T, int E, int K,
                                int32_t *slotmap, hipStream_t s);
 size_t permute_chunk_ints(int T, int E);
+// Single-token decode router: logits [T, E] and x as digit planes (nb.xdig,
+// nb.xcorr, nb.xsc).  Requires H % 256 == 0, T <= 4.
+hipError_t launch_router_narrow(const float *x, int T, int H, const void *wr, int w_bf16,
+                                int E, const float *bias, float *logits,
+                                const NarrowBufs &nb, hipStream_t s);
 
 // ---- ffn_decode.hip -----------------------------------------------------
 // ev: optional stage events (NULL or 2 entries: after gate/up, after down).
 hipError_t launch_ffn_decode(const LayerDev &L, const DecodeBufs &b, int T,
                              const Routing &r, float *y, hipStream_t s,
+                             hipEvent_t *ev);
+
+// ---- ffn_narrow.hip -----------------------------------------------------
+// Whether the single-token int8 matrix-core path covers this layer and T.
+bool narrow_supported(const LayerDev &L, int T);
+// Top-K of the token (from logits; idx/gates written), gate/up -> nb.hn, down
+// -> y.  ev: optional (NULL or 2 entries: after gate/up, after down).
+hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const float *logits,
+                             int32_t *idx, float *gates, float *y, hipStream_t s,
                              hipEvent_t *ev);
 
 // ---- ffn_prefill.hip ----------------------------------------------------

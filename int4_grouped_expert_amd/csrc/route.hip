@@ -21,6 +21,7 @@
 //                         per-chunk (64 tokens) expert bitmaps, a scan over
 //                         chunks, then stable placement by bitmap popcount.
 #include "kernels.h"
+#include "wave.h"
 
 namespace coli {
 namespace {
@@ -29,60 +30,6 @@ constexpr int kWave = 64;
 
 __device__ inline float bf16_to_f32(uint16_t b) {
   return __uint_as_float(uint32_t(b) << 16);
-}
-
-// Wave-wide reductions: an all-reduce inside each 16-lane DPP row (quad_perm
-// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror pair every lane
-// with a disjoint partner set, doubling it each step), then the four row
-// results are read with v_readlane and combined in a fixed order, so every
-// lane gets the same, deterministic value.
-template <int kCtrl>
-__device__ inline float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-__device__ inline float rdlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-__device__ inline float wave_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  v += dpp_f<0x140>(v);
-  return (rdlane_f(v, 0) + rdlane_f(v, 16)) + (rdlane_f(v, 32) + rdlane_f(v, 48));
-}
-__device__ inline float wave_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  v = fmaxf(v, dpp_f<0x140>(v));
-  return fmaxf(fmaxf(rdlane_f(v, 0), rdlane_f(v, 16)), fmaxf(rdlane_f(v, 32), rdlane_f(v, 48)));
-}
-// (value, id) arg-max: larger value wins, equal values go to the lower id,
-// id < 0 marks "no candidate".
-__device__ inline void take_better(float &bv, int &bi, float ov, int oi) {
-  const bool take = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
-  bv = take ? ov : bv;
-  bi = take ? oi : bi;
-}
-__device__ inline void wave_argmax(float &bv, int &bi) {
-#define COLI_ARG_STEP(ctrl)                                                          \
-  {                                                                                  \
-    const float ov = dpp_f<ctrl>(bv);                                                \
-    const int oi = __builtin_amdgcn_update_dpp(-1, bi, ctrl, 0xF, 0xF, false);       \
-    take_better(bv, bi, ov, oi);                                                     \
-  }
-  COLI_ARG_STEP(0xB1)
-  COLI_ARG_STEP(0x4E)
-  COLI_ARG_STEP(0x141)
-  COLI_ARG_STEP(0x140)
-#undef COLI_ARG_STEP
-  float v = rdlane_f(bv, 0);
-  int i = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r)
-    take_better(v, i, rdlane_f(bv, 16 * r), __builtin_amdgcn_readlane(bi, 16 * r));
-  bv = v;
-  bi = i;
 }
 
 // Split an fp32 row into fp16 hi/lo with one power-of-two scale:
@@ -220,6 +167,111 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     }
 }
 
+// ---------------------------------------------------------------- logits (one token)
+// grid: E blocks of 256 threads; block e computes the logits of expert e for
+// every token (T <= 4): its 4 waves split H (16-byte loads, up to kNB per lane
+// issued before use, fp32 FMA), partial sums meet in a fixed order.  The same
+// launch writes x as digit planes (see ffn_narrow.hip): every block knows the
+// token's max |x| from its own loads; group g is digitised by block g % E,
+// token t by wave t (lanes 0..15, four elements each).
+constexpr int kNB = 8;
+
+template <bool kWbf>
+__device__ inline void load4(const void *base, size_t i, float out[4]) {
+  if (kWbf) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(base) + i);
+    out[0] = __uint_as_float(v.x << 16);
+    out[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    out[2] = __uint_as_float(v.y << 16);
+    out[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  } else {
+    const float4 a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + i);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  }
+}
+
+template <bool kWbf>
+__global__ __launch_bounds__(256) void router_narrow_kernel(
+    const float *__restrict__ x, int T, int H, const void *__restrict__ wr, int E,
+    const float *__restrict__ bias, float *__restrict__ logits, NarrowBufs nb) {
+  __shared__ float sdot[4][4], smax[4][4];
+  __shared__ int sbad[4][4];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int e = blockIdx.x;
+  const int Hq = H / 4;
+  const int cb = wave * Hq, ce = cb + Hq;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, mx[4] = {0.f, 0.f, 0.f, 0.f};
+  int bad[4] = {0, 0, 0, 0};
+  for (int c0 = cb + 4 * lane; c0 < ce; c0 += 4 * kWave * kNB) {
+    float wv[kNB][4];
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const int c = c0 + 4 * kWave * b;
+      if (c < ce) load4<kWbf>(wr, size_t(e) * H + c, wv[b]);
+      else
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wv[b][k] = 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t >= T) break;
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) {
+        const int c = c0 + 4 * kWave * b;
+        if (c >= ce) break;
+        const float4 xv = *reinterpret_cast<const float4 *>(x + size_t(t) * H + c);
+        const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[t] = fmaf(wv[b][k], xa[k], acc[t]);
+          mx[t] = fmaxf(mx[t], fabsf(xa[k]));
+          bad[t] |= !__builtin_isfinite(xa[k]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float d = wave_sum(acc[t]);
+    const float m = wave_max(mx[t]);
+    const int bd = __any(bad[t]);
+    if (lane == 0) {
+      sdot[wave][t] = d;
+      smax[wave][t] = m;
+      sbad[wave][t] = bd;
+    }
+  }
+  __syncthreads();
+  if (int(threadIdx.x) < T) {
+    const int t = threadIdx.x;
+    logits[size_t(t) * E + e] =
+        ((sdot[0][t] + sdot[1][t]) + (sdot[2][t] + sdot[3][t])) + (bias ? bias[e] : 0.0f);
+  }
+  if (wave < T && lane < 16) {
+    const int t = wave;
+    const float m = fmaxf(fmaxf(smax[0][t], smax[1][t]), fmaxf(smax[2][t], smax[3][t]));
+    const bool bd = sbad[0][t] | sbad[1][t] | sbad[2][t] | sbad[3][t];
+    const int ex = digit_exponent(m);
+    if (blockIdx.x == 0 && lane == 0) nb.xsc[t] = bd ? __builtin_nanf("") : ldexpf(1.0f, -ex);
+    const int GH = H / 64;
+    const int el = 4 * lane, pos = aorder_pos(el);
+    for (int g = blockIdx.x; g < GH; g += gridDim.x) {
+      const float4 v = *reinterpret_cast<const float4 *>(x + size_t(t) * H + 64 * g + el);
+      const float va[4] = {v.x, v.y, v.z, v.w};
+      int d[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) digits4(va[i], ex, d[i]);
+      const size_t gbase = (size_t(t) * GH + g) * 4;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        *reinterpret_cast<uint32_t *>(nb.xdig + (gbase + p) * 64 + pos) = pack_plane(d, p);
+        const int sum = row16_sum_i(d[0][p] + d[1][p] + d[2][p] + d[3][p]);
+        if (lane == 0) nb.xcorr[gbase + p] = -8 * sum;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- logits (MFMA)
 typedef short bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -262,76 +314,6 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
       const int m = m0 + (lane / 16) * 4 + i;
       if (m < T && n < E) logits[size_t(m) * E + n] = acc[j][i] + (bias ? bias[n] : 0.0f);
     }
-  }
-}
-
-// ---------------------------------------------------------------- top-K
-constexpr int kMaxPerLane = COLI_MAX_PER_LANE;
-
-// Wave-wide top-K of one token.  Writes idx/gates in ascending id order.
-__device__ void wave_topk(const float *__restrict__ lrow, int E, int K, int lane,
-                          int32_t *__restrict__ idx_out,
-                          float *__restrict__ gate_out) {
-  float v[kMaxPerLane];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    const int e = lane + kWave * j;
-    v[j] = e < E ? lrow[e] : 0.0f;
-  }
-  for (int round = 0; round < K; ++round) {
-    float bv = 0.0f;
-    int bi = -1;
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-      const int e = lane + kWave * j;
-      if (e < E && !((taken >> j) & 1u) && !__builtin_isnan(v[j]) &&
-          (bi < 0 || v[j] > bv)) {
-        bv = v[j];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
-    if (bi < 0) {
-      // No valid candidate: id `round` if free, else the lowest free id.
-      int free_lo = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j) {
-        const int e = lane + kWave * j;
-        if (e < E && !((taken >> j) & 1u)) { free_lo = min(free_lo, e); }
-      }
-      int own_free = 0;
-      if (round < E && (round % kWave) == lane) own_free = !((taken >> (round / kWave)) & 1u);
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {  // rare path (NaN logits)
-        free_lo = min(free_lo, __shfl_xor(free_lo, m, kWave));
-        own_free |= __shfl_xor(own_free, m, kWave);
-      }
-      bi = own_free ? round : free_lo;
-    }
-    if ((bi % kWave) == lane) taken |= 1u << (bi / kWave);
-  }
-  // selected max and normaliser (butterfly: identical on every lane)
-  float m = -__builtin_inff();
-#pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j)
-    if ((taken >> j) & 1u) m = fmaxf(m, v[j]);
-  m = wave_max(m);
-  float z = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j)
-    if ((taken >> j) & 1u) z += expf(v[j] - m);
-  z = wave_sum(z);
-  int before = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    const uint64_t bal = __ballot((taken >> j) & 1u);
-    if ((taken >> j) & 1u) {
-      const int rank = before + __popcll(bal & ((1ull << lane) - 1ull));
-      idx_out[rank] = lane + kWave * j;
-      gate_out[rank] = expf(v[j] - m) / z;
-    }
-    before += __popcll(bal);
   }
 }
 
@@ -587,6 +569,16 @@ hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
   if (T <= 2) COLI_ROUTER_CASE(1, 2)
   else COLI_ROUTER_CASE(4, 4)
 #undef COLI_ROUTER_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_router_narrow(const float *x, int T, int H, const void *wr, int w_bf16,
+                                int E, const float *bias, float *logits,
+                                const NarrowBufs &nb, hipStream_t s) {
+  if (w_bf16)
+    router_narrow_kernel<true><<<E, 256, 0, s>>>(x, T, H, wr, E, bias, logits, nb);
+  else
+    router_narrow_kernel<false><<<E, 256, 0, s>>>(x, T, H, wr, E, bias, logits, nb);
   return hipGetLastError();
 }
 

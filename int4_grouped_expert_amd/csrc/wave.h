@@ -1,0 +1,188 @@
+// wave.h -- wave-level building blocks shared by the routing and decode
+// kernels: DPP reductions (every lane gets the same value, combined in a
+// fixed order) and the per-token top-K with renormalised gates.
+//
+// Top-K: page "Colibri 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
+// section 十一 (per-token top-k experts); gates normalised over the selected
+// experts (page "colibri 路由遥测全解析", section 分离计数与追踪); NaN logits
+// never win (same page, section 测试与 CI 保障).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace coli {
+
+constexpr int kWaveLanes = 64;
+
+// Wave-wide reductions: an all-reduce inside each 16-lane DPP row (quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror pair every lane
+// with a disjoint partner set, doubling it each step), then the four row
+// results are read with v_readlane and combined in a fixed order, so every
+// lane gets the same, deterministic value.
+template <int kCtrl>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ inline float rdlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ inline float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (rdlane_f(v, 0) + rdlane_f(v, 16)) + (rdlane_f(v, 32) + rdlane_f(v, 48));
+}
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(rdlane_f(v, 0), rdlane_f(v, 16)), fmaxf(rdlane_f(v, 32), rdlane_f(v, 48)));
+}
+// (value, id) arg-max: larger value wins, equal values go to the lower id,
+// id < 0 marks "no candidate".
+__device__ inline void take_better(float &bv, int &bi, float ov, int oi) {
+  const bool take = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
+}
+__device__ inline void wave_argmax(float &bv, int &bi) {
+#define COLI_ARG_STEP(ctrl)                                                          \
+  {                                                                                  \
+    const float ov = dpp_f<ctrl>(bv);                                                \
+    const int oi = __builtin_amdgcn_update_dpp(-1, bi, ctrl, 0xF, 0xF, false);       \
+    take_better(bv, bi, ov, oi);                                                     \
+  }
+  COLI_ARG_STEP(0xB1)
+  COLI_ARG_STEP(0x4E)
+  COLI_ARG_STEP(0x141)
+  COLI_ARG_STEP(0x140)
+#undef COLI_ARG_STEP
+  float v = rdlane_f(bv, 0);
+  int i = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    take_better(v, i, rdlane_f(bv, 16 * r), __builtin_amdgcn_readlane(bi, 16 * r));
+  bv = v;
+  bi = i;
+}
+
+constexpr int kMaxPerLane = COLI_MAX_PER_LANE;
+
+// Wave-wide top-K of one token.  Writes idx/gates in ascending id order.
+__device__ inline void wave_topk(const float *__restrict__ lrow, int E, int K, int lane,
+                          int32_t *__restrict__ idx_out,
+                          float *__restrict__ gate_out) {
+  float v[kMaxPerLane];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    const int e = lane + kWaveLanes * j;
+    v[j] = e < E ? lrow[e] : 0.0f;
+  }
+  for (int round = 0; round < K; ++round) {
+    float bv = 0.0f;
+    int bi = -1;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      const int e = lane + kWaveLanes * j;
+      if (e < E && !((taken >> j) & 1u) && !__builtin_isnan(v[j]) &&
+          (bi < 0 || v[j] > bv)) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+    wave_argmax(bv, bi);
+    if (bi < 0) {
+      // No valid candidate: id `round` if free, else the lowest free id.
+      int free_lo = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < kMaxPerLane; ++j) {
+        const int e = lane + kWaveLanes * j;
+        if (e < E && !((taken >> j) & 1u)) { free_lo = min(free_lo, e); }
+      }
+      int own_free = 0;
+      if (round < E && (round % kWaveLanes) == lane) own_free = !((taken >> (round / kWaveLanes)) & 1u);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {  // rare path (NaN logits)
+        free_lo = min(free_lo, __shfl_xor(free_lo, m, kWaveLanes));
+        own_free |= __shfl_xor(own_free, m, kWaveLanes);
+      }
+      bi = own_free ? round : free_lo;
+    }
+    if ((bi % kWaveLanes) == lane) taken |= 1u << (bi / kWaveLanes);
+  }
+  // selected max and normaliser (butterfly: identical on every lane)
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j)
+    if ((taken >> j) & 1u) m = fmaxf(m, v[j]);
+  m = wave_max(m);
+  float z = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j)
+    if ((taken >> j) & 1u) z += expf(v[j] - m);
+  z = wave_sum(z);
+  int before = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    const uint64_t bal = __ballot((taken >> j) & 1u);
+    if ((taken >> j) & 1u) {
+      const int rank = before + __popcll(bal & ((1ull << lane) - 1ull));
+      idx_out[rank] = lane + kWaveLanes * j;
+      gate_out[rank] = expf(v[j] - m) / z;
+    }
+    before += __popcll(bal);
+  }
+}
+
+// ---- digit planes (single-token decode activations) ----------------------
+template <int kCtrl>
+__device__ inline int dpp_row_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+// Sum over the 16 lanes of each DPP row (every lane of the row gets it).
+__device__ inline int row16_sum_i(int v) {
+  v += dpp_row_i<0xB1>(v);
+  v += dpp_row_i<0x4E>(v);
+  v += dpp_row_i<0x141>(v);
+  v += dpp_row_i<0x140>(v);
+  return v;
+}
+
+// Four balanced base-128 digits of rint(v * 2^e) (|v * 2^e| <= 2^27; the
+// clamp only matters for non-finite v, whose result is flagged elsewhere).
+__device__ inline void digits4(float v, int e, int d[4]) {
+  const float sv = fminf(fmaxf(ldexpf(v, e), -134217728.0f), 134217728.0f);
+  int a = int(rintf(sv));
+  d[3] = ((a + 64) & 127) - 64;
+  a = (a - d[3]) >> 7;
+  d[2] = ((a + 64) & 127) - 64;
+  a = (a - d[2]) >> 7;
+  d[1] = ((a + 64) & 127) - 64;
+  a = (a - d[1]) >> 7;
+  d[0] = a;
+}
+
+// 4-element runs: digits of elements el .. el+3 (el % 4 == 0) of a 64-element
+// group sit at this byte offset of the group's 64-byte plane ("A order": run
+// rho = elements 8 rho .. 8 rho + 7, then 32 + 8 rho .. 32 + 8 rho + 7).
+__device__ inline int aorder_pos(int el) {
+  return el < 32 ? 16 * (el / 8) + (el % 8) : 16 * ((el - 32) / 8) + 8 + (el % 8);
+}
+// Pack plane p of four elements' digits into one little-endian word.
+__device__ inline uint32_t pack_plane(const int d[4][4], int p) {
+  return (uint32_t(d[0][p]) & 0xFFu) | ((uint32_t(d[1][p]) & 0xFFu) << 8) |
+         ((uint32_t(d[2][p]) & 0xFFu) << 16) | ((uint32_t(d[3][p]) & 0xFFu) << 24);
+}
+// Scale exponent e of a vector with max |v| = m: m * 2^e in [2^26, 2^27).
+__device__ inline int digit_exponent(float m) {
+  int ex = 0;
+  (void)frexpf(m, &ex);
+  return m > 0.0f ? 27 - ex : 0;
+}
+
+}  // namespace coli

@@ -78,6 +78,23 @@ def test_decode_small(cfg_id, T):
     oracle_check(cfg_id, L, x, y, idx, gates, DECODE)
 
 
+@pytest.mark.parametrize("cfg_id", [107, 108, 109, 110, 111, 112])
+def test_decode_one_token(cfg_id):
+    """Single-token decode on the int8 matrix-core path, several tokens per layer."""
+    L = layer(cfg_id)
+    c = W.CONFIGS[cfg_id]
+    xs = margin_tokens(cfg_id, 3, host_array(L.w_router), L.bias_np, c["K"])
+    for t in range(3):
+        log(f"one token cfg {cfg_id} token {t}")
+        x = xs[t:t + 1].contiguous()
+        y, idx, gates = L.forward(x, DECODE)
+        torch.cuda.synchronize()
+        oracle_check(cfg_id, L, x, y, idx, gates, DECODE, check_bytes=(t == 0))
+    a = L.forward(xs[:1].contiguous(), DECODE)[0].cpu()
+    b = L.forward(xs[:1].contiguous(), DECODE)[0].cpu()
+    assert torch.equal(a, b), "repeated forward differs"
+
+
 @pytest.mark.parametrize("cfg_id,T", [(100, 333), (104, 200), (100, 1), (100, 64), (100, 65)])
 def test_prefill_small(cfg_id, T):
     log(f"prefill small cfg {cfg_id} T {T}")

@@ -53,6 +53,20 @@ CONFIGS.update({
               bias="zipf", mode="decode", layers=40),
     106: dict(name="wide_decode", H=10240, I=320, E=12, K=3, T=3, router="bf16", x="f32",
               bias=None, mode="decode", layers=1),
+    # single-token shapes with H, I multiples of 256 (the int8 matrix-core decode path):
+    # K slices of 1..6 chunks per wave, 1..8 down waves, 2..17 units
+    107: dict(name="one_token_small", H=512, I=512, E=16, K=4, T=1, router="f32", x="f32",
+              bias=None, mode="decode", layers=1),
+    108: dict(name="one_token_mid", H=1536, I=768, E=40, K=6, T=1, router="bf16", x="f32",
+              bias="zipf", mode="decode", layers=1),
+    109: dict(name="one_token_k16", H=1024, I=256, E=64, K=16, T=1, router="bf16", x="f32",
+              bias=None, mode="decode", layers=1),
+    110: dict(name="one_token_wide", H=10240, I=512, E=12, K=3, T=1, router="bf16", x="f32",
+              bias=None, mode="decode", layers=1),
+    111: dict(name="one_token_h2048", H=2048, I=1024, E=32, K=8, T=1, router="f32", x="f32",
+              bias="zipf", mode="decode", layers=1),
+    112: dict(name="one_token_h4096", H=4096, I=2048, E=20, K=5, T=1, router="bf16", x="f32",
+              bias=None, mode="decode", layers=1),
 })
 
 WEIGHT_STD = 0.02
