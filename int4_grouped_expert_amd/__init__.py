@@ -21,6 +21,17 @@ if not os.path.exists(_LIB_PATH):
     raise ImportError(
         f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
 
+# One HIP runtime per process.  A PyTorch wheel carries its own HIP and HSA
+# runtimes and loads them into the global symbol scope; libcoli.so is linked
+# against the system ROCm HIP runtime.  Loaded after torch, that runtime binds
+# to torch's HSA runtime (the one that owns the device in this process);
+# loaded first, it would bring up a second HSA runtime, which then finds no
+# device once torch has opened it.  So torch, when installed, is imported first.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # pure C-ABI use without PyTorch
+    _torch = None
+
 lib = ctypes.CDLL(_LIB_PATH)
 
 COLI_OK, COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN = 0, -1, -2, -3

@@ -130,14 +130,17 @@ __device__ inline float fold_rows(float v, int lane) {
 
 // ------------------------------------------------------------------ gate/up
 constexpr int kMaxWaves = 16;
+constexpr int kGateupMaxWaves = 8;
 
 template <int NC>
-__global__ __launch_bounds__(kW * 8) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kW * 8) __attribute__((amdgpu_waves_per_eu(2)))
 void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
                    int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
   __shared__ int32_t sidx[COLI_NARROW_MAX_K];
   __shared__ float sgate[COLI_NARROW_MAX_K];
   __shared__ float red[2][kMaxWaves][2][8];
+  // per wave, double-buffered: the item's group scales [frag][row][4 NC]
+  __shared__ __align__(16) float ssc[kGateupMaxWaves][2][2][8][4 * NC];
   const int lane = threadIdx.x % kW, wave = threadIdx.x / kW;
   const int nw = blockDim.x / kW;
   const int I = L.I, E = L.E, K = L.K;
@@ -146,7 +149,11 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   const int n_items = (K + 1) * nrb;
   if (int(blockIdx.x) >= n_items) return;
 
-  if (wave == 0) wave_topk(logits, E, K, lane, sidx, sgate);
+  if (wave == 0) {
+    if (E <= 64) wave_topk_pl<1>(logits, E, K, lane, sidx, sgate);
+    else if (E <= 128) wave_topk_pl<2>(logits, E, K, lane, sidx, sgate);
+    else wave_topk_pl<4>(logits, E, K, lane, sidx, sgate);
+  }
   lds_barrier();
   if (blockIdx.x == 0 && int(threadIdx.x) < K) {
     idx_out[threadIdx.x] = sidx[threadIdx.x];
@@ -172,11 +179,12 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   }
   const float xs = nb.xsc[0];
 
-  // item -> this lane's weight and scale pointers (chunk 0 of its K slice).
-  // The weights are the B lane's (group 4c + 2 kappa + q / 2); the scale is
-  // the result lane's (slot q: group 4c + q).
+  // item -> this lane's weight pointers (chunk 0 of its K slice; B lane group
+  // 4c + 2 kappa + q / 2) and its scale run: lane (r, i = 4 kappa + q) loads
+  // the 4 scales of chunk min(i, NC - 1) of row r (one contiguous 16 bytes).
   const size_t goff = size_t(wave) * NC * 4 + 2 * kap + q / 2;
-  const size_t soff = size_t(wave) * NC * 4 + q;
+  const int si = 4 * kap + q;
+  const size_t soff = size_t(wave) * NC * 4 + 4 * size_t(si < NC ? si : NC - 1);
   struct Ptrs {
     const uint8_t *wg, *wu;
     const float *sg, *su;
@@ -194,20 +202,16 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   };
 
   uint4 rw[2][NC];
-  float rs[2][NC];
+  float4 scg, scu;
   int it = blockIdx.x;
   {
     const Ptrs p = ptrs(it);
+    scg = *reinterpret_cast<const float4 *>(p.sg);
+    scu = *reinterpret_cast<const float4 *>(p.su);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      rw[0][c] = *reinterpret_cast<const uint4 *>(p.wg + 128 * c);
-      rs[0][c] = p.sg[4 * c];
-    }
+    for (int c = 0; c < NC; ++c) rw[0][c] = *reinterpret_cast<const uint4 *>(p.wg + 128 * c);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      rw[1][c] = *reinterpret_cast<const uint4 *>(p.wu + 128 * c);
-      rs[1][c] = p.su[4 * c];
-    }
+    for (int c = 0; c < NC; ++c) rw[1][c] = *reinterpret_cast<const uint4 *>(p.wu + 128 * c);
   }
   wait_all_loads();
   int buf = 0, k_it = 0;
@@ -216,6 +220,19 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     // end they re-read the current item (valid addresses, never used)
     const int nx = it + int(gridDim.x) < n_items ? it + int(gridDim.x) : it;
     const Ptrs np = ptrs(nx);
+    // this item's scales -> LDS, then the next item's scale loads
+    if (si < NC) {
+      *reinterpret_cast<float4 *>(&ssc[wave][buf][0][r][4 * si]) = scg;
+      *reinterpret_cast<float4 *>(&ssc[wave][buf][1][r][4 * si]) = scu;
+    }
+    scg = *reinterpret_cast<const float4 *>(np.sg);
+    scu = *reinterpret_cast<const float4 *>(np.su);
+    step_fence();
+    float sv[2][NC];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sv[f][c] = ssc[wave][buf][f][r][4 * c + q];
     float acc[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int f = 0; f < 2; ++f)
@@ -225,13 +242,11 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
         // land in the same registers: no copies around the loop)
         const i32x4 b0 = unpack_half(rw[f][c].x, rw[f][c].y);
         const i32x4 b1 = unpack_half(rw[f][c].z, rw[f][c].w);
-        const float sv = keep(rs[f][c]);
         rw[f][c] = *reinterpret_cast<const uint4 *>((f ? np.wu : np.wg) + 128 * c);
-        rs[f][c] = (f ? np.su : np.sg)[4 * c];
         step_fence();
         i32x4 P = mfma_i8(A[c][0], b0, C[c]);
         P = mfma_i8(A[c][1], b1, P);
-        acc[f] = fmaf(planes_to_f32(P), sv, acc[f]);
+        acc[f] = fmaf(planes_to_f32(P), sv[f][c], acc[f]);
       }
     const float vg = fold_rows(acc[0], lane);
     const float vu = fold_rows(acc[1], lane);
@@ -424,7 +439,7 @@ hipError_t launch_down(const LayerDev &L, const NarrowBufs &nb, const int32_t *i
 }  // namespace
 
 bool narrow_supported(const LayerDev &L, int T) {
-  if (T != 1 || L.H % 256 || L.I % 256 || L.K > COLI_NARROW_MAX_K) return false;
+  if (T != 1 || L.H % 256 || L.I % 256 || L.K > COLI_NARROW_MAX_K || L.E > 256) return false;
   int nc = 0;
   if (!gateup_waves(L.H, &nc)) return false;
   const int nw = L.I / 256;
@@ -440,7 +455,7 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
   int nc = 0;
   const int gw = gateup_waves(L.H, &nc);
   const int n_items = (L.K + 1) * (L.I / 8);
-  const int ggrid = n_items < 3 * cus ? n_items : 3 * cus;
+  const int ggrid = n_items < 2 * cus ? n_items : 2 * cus;
 #define COLI_GU(NC) \
   case NC: gateup_narrow<NC><<<ggrid, gw * kW, 0, s>>>(nb, L, logits, idx, gates); break;
   switch (nc) {

@@ -70,39 +70,47 @@ __device__ inline void wave_argmax(float &bv, int &bi) {
   bi = i;
 }
 
-constexpr int kMaxPerLane = COLI_MAX_PER_LANE;
-
-// Wave-wide top-K of one token.  Writes idx/gates in ascending id order.
-__device__ inline void wave_topk(const float *__restrict__ lrow, int E, int K, int lane,
-                          int32_t *__restrict__ idx_out,
-                          float *__restrict__ gate_out) {
-  float v[kMaxPerLane];
-  uint32_t taken = 0;
+// Wave-wide top-K of one token, PL logits per lane (E <= 64 PL).  Writes
+// idx/gates in ascending id order.  Each lane keeps its best untaken
+// candidate; a round is one wave arg-max, after which only the winner's lane
+// rescans its PL values.
+template <int PL>
+__device__ __attribute__((always_inline)) inline void wave_topk_pl(
+    const float *__restrict__ lrow, int E, int K, int lane, int32_t *__restrict__ idx_out,
+    float *__restrict__ gate_out) {
+  float v[PL];
+  bool ok[PL];  // a valid id whose logit is not NaN
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
+  for (int j = 0; j < PL; ++j) {
     const int e = lane + kWaveLanes * j;
     v[j] = e < E ? lrow[e] : 0.0f;
+    ok[j] = e < E && !__builtin_isnan(v[j]);
   }
-  for (int round = 0; round < K; ++round) {
-    float bv = 0.0f;
-    int bi = -1;
+  uint32_t taken = 0;
+  float lv = 0.0f;
+  int li = -1;
+  auto rescan = [&]() {
+    lv = 0.0f;
+    li = -1;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-      const int e = lane + kWaveLanes * j;
-      if (e < E && !((taken >> j) & 1u) && !__builtin_isnan(v[j]) &&
-          (bi < 0 || v[j] > bv)) {
-        bv = v[j];
-        bi = e;
+    for (int j = 0; j < PL; ++j)
+      if (ok[j] && !((taken >> j) & 1u) && (li < 0 || v[j] > lv)) {
+        lv = v[j];
+        li = lane + kWaveLanes * j;
       }
-    }
+  };
+  rescan();
+  for (int round = 0; round < K; ++round) {
+    float bv = lv;
+    int bi = li;
     wave_argmax(bv, bi);
     if (bi < 0) {
       // No valid candidate: id `round` if free, else the lowest free id.
       int free_lo = 0x7fffffff;
 #pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j) {
+      for (int j = 0; j < PL; ++j) {
         const int e = lane + kWaveLanes * j;
-        if (e < E && !((taken >> j) & 1u)) { free_lo = min(free_lo, e); }
+        if (e < E && !((taken >> j) & 1u)) free_lo = min(free_lo, e);
       }
       int own_free = 0;
       if (round < E && (round % kWaveLanes) == lane) own_free = !((taken >> (round / kWaveLanes)) & 1u);
@@ -113,22 +121,25 @@ __device__ inline void wave_topk(const float *__restrict__ lrow, int E, int K, i
       }
       bi = own_free ? round : free_lo;
     }
-    if ((bi % kWaveLanes) == lane) taken |= 1u << (bi / kWaveLanes);
+    if ((bi % kWaveLanes) == lane) {
+      taken |= 1u << (bi / kWaveLanes);
+      rescan();
+    }
   }
   // selected max and normaliser (butterfly: identical on every lane)
   float m = -__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j)
+  for (int j = 0; j < PL; ++j)
     if ((taken >> j) & 1u) m = fmaxf(m, v[j]);
   m = wave_max(m);
   float z = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j)
+  for (int j = 0; j < PL; ++j)
     if ((taken >> j) & 1u) z += expf(v[j] - m);
   z = wave_sum(z);
   int before = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
+  for (int j = 0; j < PL; ++j) {
     const uint64_t bal = __ballot((taken >> j) & 1u);
     if ((taken >> j) & 1u) {
       const int rank = before + __popcll(bal & ((1ull << lane) - 1ull));
@@ -137,6 +148,17 @@ __device__ inline void wave_topk(const float *__restrict__ lrow, int E, int K, i
     }
     before += __popcll(bal);
   }
+}
+
+// Dispatch on the logits per lane, ceil(E / 64) rounded up to 1, 2, 4, 8, 16.
+__device__ __attribute__((always_inline)) inline void wave_topk(
+    const float *__restrict__ lrow, int E, int K, int lane, int32_t *__restrict__ idx_out,
+    float *__restrict__ gate_out) {
+  if (E <= 64) wave_topk_pl<1>(lrow, E, K, lane, idx_out, gate_out);
+  else if (E <= 128) wave_topk_pl<2>(lrow, E, K, lane, idx_out, gate_out);
+  else if (E <= 256) wave_topk_pl<4>(lrow, E, K, lane, idx_out, gate_out);
+  else if (E <= 512) wave_topk_pl<8>(lrow, E, K, lane, idx_out, gate_out);
+  else wave_topk_pl<16>(lrow, E, K, lane, idx_out, gate_out);
 }
 
 // ---- digit planes (single-token decode activations) ----------------------
