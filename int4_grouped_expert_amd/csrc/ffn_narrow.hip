@@ -131,6 +131,7 @@ __device__ inline float fold_rows(float v, int lane) {
 // ------------------------------------------------------------------ gate/up
 constexpr int kMaxWaves = 16;
 constexpr int kGateupMaxWaves = 8;
+constexpr int kMaxItems = 8;  // items per block (the grid is sized for it)
 
 template <int NC>
 __global__ __launch_bounds__(kW * 8) __attribute__((amdgpu_waves_per_eu(2)))
@@ -138,7 +139,7 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
                    int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
   __shared__ int32_t sidx[COLI_NARROW_MAX_K];
   __shared__ float sgate[COLI_NARROW_MAX_K];
-  __shared__ float red[2][kMaxWaves][2][8];
+  __shared__ float red[kMaxItems][kGateupMaxWaves][2][8];
   // per wave, double-buffered: the item's group scales [frag][row][4 NC]
   __shared__ __align__(16) float ssc[kGateupMaxWaves][2][2][8][4 * NC];
   const int lane = threadIdx.x % kW, wave = threadIdx.x / kW;
@@ -248,26 +249,27 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
         P = mfma_i8(A[c][1], b1, P);
         acc[f] = fmaf(planes_to_f32(P), sv[f][c], acc[f]);
       }
+    // per-row partials of this wave; the block reduces them once, at the end
     const float vg = fold_rows(acc[0], lane);
     const float vu = fold_rows(acc[1], lane);
     if (lane < 8) {
-      red[buf][wave][0][lane] = vg;
-      red[buf][wave][1][lane] = vu;
-    }
-    lds_barrier();
-    if (wave == k_it % nw && lane < 16) {
-      const int f = lane / 8, rr = lane % 8;
-      float t = 0.0f;
-      for (int w = 0; w < nw; ++w) t += red[buf][w][f][rr];
-      const float upv = dpp_row<0x128>(t);  // lane rr <- lane rr + 8 (up)
-      if (lane < 8) {
-        const int u = it / nrb, rb = it - u * nrb;
-        const float gw = u < K ? sgate[u] : 1.0f;
-        const float h = gw * silu(t * xs) * (upv * xs);
-        nb.hn[size_t(u) * I + rb * 8 + rr] = h;
-      }
+      red[k_it][wave][0][lane] = vg;
+      red[k_it][wave][1][lane] = vu;
     }
     buf ^= 1;
+  }
+  lds_barrier();
+  for (int i = threadIdx.x; i < k_it * 8; i += blockDim.x) {
+    const int k = i / 8, rr = i % 8;
+    float g = 0.0f, up = 0.0f;
+    for (int w = 0; w < nw; ++w) {
+      g += red[k][w][0][rr];
+      up += red[k][w][1][rr];
+    }
+    const int itk = int(blockIdx.x) + k * int(gridDim.x);
+    const int u = itk / nrb, rb = itk - u * nrb;
+    const float gw = u < K ? sgate[u] : 1.0f;
+    nb.hn[size_t(u) * I + rb * 8 + rr] = gw * silu(g * xs) * (up * xs);
   }
 }
 
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
                                                              const int32_t *__restrict__ idx,
                                                              float *__restrict__ y) {
   extern __shared__ __align__(16) uint8_t dyn[];
-  __shared__ float red[2][kMaxWaves][8];
+  __shared__ float red[kMaxItems][kDownMaxWaves][8];
   const int lane = threadIdx.x % kW, wave = threadIdx.x / kW;
   const int nw = blockDim.x / kW;
   const int H = L.H, I = L.I, K = L.K;
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
   const int a_step = actA ? 1024 : 0;
 
   wait_all_loads();
-  int buf = 0, k_it = 0;
+  int k_it = 0;
   for (; it < n_items; it += gridDim.x, ++k_it) {
     const int nx = it + int(gridDim.x) < n_items ? it + int(gridDim.x) : it;
     const size_t o = loff(nx), so = sof(nx);
@@ -392,14 +394,14 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
       acc = fmaf(planes_to_f32(P), sv, acc);
     }
     const float v = fold_rows(acc, lane);
-    if (lane < 8) red[buf][wave][lane] = v;
-    lds_barrier();
-    if (wave == k_it % nw && lane < 8) {
-      float t = 0.0f;
-      for (int w = 0; w < nw; ++w) t += red[buf][w][lane];
-      y[size_t(it) * 8 + lane] = t;
-    }
-    buf ^= 1;
+    if (lane < 8) red[k_it][wave][lane] = v;
+  }
+  lds_barrier();
+  for (int i = threadIdx.x; i < k_it * 8; i += blockDim.x) {
+    const int k = i / 8, rr = i % 8;
+    float t = 0.0f;
+    for (int w = 0; w < nw; ++w) t += red[k][w][rr];
+    y[(size_t(blockIdx.x) + size_t(k) * gridDim.x) * 8 + rr] = t;
   }
 }
 
@@ -455,7 +457,8 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
   int nc = 0;
   const int gw = gateup_waves(L.H, &nc);
   const int n_items = (L.K + 1) * (L.I / 8);
-  const int ggrid = n_items < 2 * cus ? n_items : 2 * cus;
+  int ggrid = n_items < 2 * cus ? n_items : 2 * cus;
+  if (ggrid < (n_items + kMaxItems - 1) / kMaxItems) ggrid = (n_items + kMaxItems - 1) / kMaxItems;
 #define COLI_GU(NC) \
   case NC: gateup_narrow<NC><<<ggrid, gw * kW, 0, s>>>(nb, L, logits, idx, gates); break;
   switch (nc) {
@@ -467,7 +470,8 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
   if (e != hipSuccess) return e;
   if (ev) (void)hipEventRecord(ev[0], s);
   const int d_items = L.H / 8;
-  const int dgrid = d_items < cus ? d_items : cus;
+  int dgrid = d_items < cus ? d_items : cus;
+  if (dgrid < (d_items + kMaxItems - 1) / kMaxItems) dgrid = (d_items + kMaxItems - 1) / kMaxItems;
 #define COLI_DN(NU) \
   case NU: e = launch_down<NU>(L, nb, idx, y, dgrid, s); break;
   switch (L.K + 1) {

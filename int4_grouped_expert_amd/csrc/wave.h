@@ -70,41 +70,66 @@ __device__ inline void wave_argmax(float &bv, int &bi) {
   bi = i;
 }
 
+// Arg-max keys: (order-preserving bits of the value) << 32 | ~id, so that the
+// unsigned maximum is the largest value and, among equal values, the lowest
+// id; 0 means "no candidate" (NaN values and ids >= E never get a key).
+__device__ inline uint64_t topk_key(float v, int id) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (uint64_t(o) << 32) | uint64_t(~uint32_t(id));
+}
+__device__ inline uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int kCtrl>
+__device__ inline uint64_t dpp_u64(uint64_t k) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(k)), kCtrl, 0xF, 0xF, false));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(k >> 32)), kCtrl, 0xF, 0xF, false));
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ inline uint64_t rdlane_u64(uint64_t k, int l) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(k)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(k >> 32)), l));
+  return (uint64_t(hi) << 32) | lo;
+}
+// Wave maximum of a key (same DPP pattern as wave_max; every lane gets it).
+__device__ inline uint64_t wave_max_key(uint64_t k) {
+  k = max_u64(k, dpp_u64<0xB1>(k));
+  k = max_u64(k, dpp_u64<0x4E>(k));
+  k = max_u64(k, dpp_u64<0x141>(k));
+  k = max_u64(k, dpp_u64<0x140>(k));
+  return max_u64(max_u64(rdlane_u64(k, 0), rdlane_u64(k, 16)),
+                 max_u64(rdlane_u64(k, 32), rdlane_u64(k, 48)));
+}
+
 // Wave-wide top-K of one token, PL logits per lane (E <= 64 PL).  Writes
-// idx/gates in ascending id order.  Each lane keeps its best untaken
-// candidate; a round is one wave arg-max, after which only the winner's lane
-// rescans its PL values.
+// idx/gates in ascending id order.  Each lane keeps the key of its best
+// untaken candidate; a round is one wave key maximum, after which only the
+// winner's lane rescans its PL values.
 template <int PL>
 __device__ __attribute__((always_inline)) inline void wave_topk_pl(
     const float *__restrict__ lrow, int E, int K, int lane, int32_t *__restrict__ idx_out,
     float *__restrict__ gate_out) {
   float v[PL];
-  bool ok[PL];  // a valid id whose logit is not NaN
 #pragma unroll
   for (int j = 0; j < PL; ++j) {
     const int e = lane + kWaveLanes * j;
     v[j] = e < E ? lrow[e] : 0.0f;
-    ok[j] = e < E && !__builtin_isnan(v[j]);
   }
   uint32_t taken = 0;
-  float lv = 0.0f;
-  int li = -1;
+  uint64_t lk = 0;
   auto rescan = [&]() {
-    lv = 0.0f;
-    li = -1;
+    lk = 0;
 #pragma unroll
-    for (int j = 0; j < PL; ++j)
-      if (ok[j] && !((taken >> j) & 1u) && (li < 0 || v[j] > lv)) {
-        lv = v[j];
-        li = lane + kWaveLanes * j;
-      }
+    for (int j = 0; j < PL; ++j) {
+      const int e = lane + kWaveLanes * j;
+      const bool cand = e < E && !__builtin_isnan(v[j]) && !((taken >> j) & 1u);
+      lk = max_u64(lk, cand ? topk_key(v[j], e) : 0ull);
+    }
   };
   rescan();
   for (int round = 0; round < K; ++round) {
-    float bv = lv;
-    int bi = li;
-    wave_argmax(bv, bi);
-    if (bi < 0) {
+    const uint64_t wk = wave_max_key(lk);
+    int bi = int(~uint32_t(wk));
+    if (wk == 0) {
       // No valid candidate: id `round` if free, else the lowest free id.
       int free_lo = 0x7fffffff;
 #pragma unroll
