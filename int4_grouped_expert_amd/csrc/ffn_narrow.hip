@@ -281,6 +281,7 @@ template <int NU>
 constexpr int down_wave_bytes() { return NU * (1024 + 64) + 32; }
 
 constexpr int kDownMaxWaves = 8;
+constexpr int kDownItems = 3;  // items per down block
 
 template <int NU>
 __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb, LayerDev L,
@@ -312,17 +313,30 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
   const size_t soff = size_t(wave) * 4 + q;
   auto loff = [&](int it) { return (size_t(it) * 8 + r) * GI + goff; };
   auto sof = [&](int it) { return (size_t(it) * 8 + r) * GI + soff; };
-  uint4 rw[NU];
-  float rs[NU];
-  int it = blockIdx.x;
-  {
-    const size_t o = loff(it), so = sof(it);
+  // Unit-major streaming: the block's items (at most kDownItems: b, b + G,
+  // b + 2G) are visited unit by unit, so that at any time the whole grid reads
+  // the rows of one or two experts (row-buffer locality).  Ring: the slots of
+  // two units (A: even units, B: odd), refilled with the unit two ahead.
+  const int G = gridDim.x;
+  const int nib = (n_items - int(blockIdx.x) + G - 1) / G;  // items of this block
+  size_t lo[kDownItems], so[kDownItems];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      rw[u] = *reinterpret_cast<const uint4 *>(blob[u] + L.lay.dq + o * 32 + 16 * (q % 2));
-      rs[u] = reinterpret_cast<const float *>(blob[u] + L.lay.ds)[so];
-    }
+  for (int k = 0; k < kDownItems; ++k) {
+    // items past the end re-read item 0's rows (cached, never stored)
+    const int itk = k < nib ? int(blockIdx.x) + k * G : int(blockIdx.x);
+    lo[k] = loff(itk) * 32 + 16 * (q % 2);
+    so[k] = sof(itk);
   }
+  uint4 rw[2][kDownItems];
+  float rs[2][kDownItems];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int k = 0; k < kDownItems; ++k) {
+      const int u = h < NU ? h : NU - 1;
+      rw[h][k] = *reinterpret_cast<const uint4 *>(blob[u] + L.lay.dq + lo[k]);
+      rs[h][k] = reinterpret_cast<const float *>(blob[u] + L.lay.ds)[so[k]];
+    }
 
   // h' chunk `wave` of every unit -> digits in this wave's LDS area.  Lane l
   // holds elements 4l .. 4l+3 of the chunk: group l / 16, element 4 (l % 16).
@@ -372,29 +386,35 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
   const int a_step = actA ? 1024 : 0;
 
   wait_all_loads();
-  int k_it = 0;
-  for (; it < n_items; it += gridDim.x, ++k_it) {
-    const int nx = it + int(gridDim.x) < n_items ? it + int(gridDim.x) : it;
-    const size_t o = loff(nx), so = sof(nx);
-    float acc = 0.0f;
+  float acc[kDownItems];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const i32x4 b0 = unpack_half(rw[u].x, rw[u].y);
-      const i32x4 b1 = unpack_half(rw[u].z, rw[u].w);
-      const float sv = keep(rs[u]) * sa[u];
-      rw[u] = *reinterpret_cast<const uint4 *>(blob[u] + L.lay.dq + o * 32 + 16 * (q % 2));
-      rs[u] = reinterpret_cast<const float *>(blob[u] + L.lay.ds)[so];
+  for (int k = 0; k < kDownItems; ++k) acc[k] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int h = u & 1;
+    const int un = u + 2 < NU ? u + 2 : NU - 1;  // refill: two units ahead
+    const int8_t *ap = dig + a_base + u * a_step;
+    const i32x4 a0 = *reinterpret_cast<const i32x4 *>(ap);
+    const i32x4 a1 = *reinterpret_cast<const i32x4 *>(ap + 16);
+    const i32x4 c0 = *reinterpret_cast<const i32x4 *>(corr + (u * 4 + q) * 4);
+#pragma unroll
+    for (int k = 0; k < kDownItems; ++k) {
+      const i32x4 b0 = unpack_half(rw[h][k].x, rw[h][k].y);
+      const i32x4 b1 = unpack_half(rw[h][k].z, rw[h][k].w);
+      const float sv = keep(rs[h][k]) * sa[u];
+      rw[h][k] = *reinterpret_cast<const uint4 *>(blob[un] + L.lay.dq + lo[k]);
+      rs[h][k] = reinterpret_cast<const float *>(blob[un] + L.lay.ds)[so[k]];
       step_fence();
-      const int8_t *ap = dig + a_base + u * a_step;
-      const i32x4 a0 = *reinterpret_cast<const i32x4 *>(ap);
-      const i32x4 a1 = *reinterpret_cast<const i32x4 *>(ap + 16);
-      const i32x4 c0 = *reinterpret_cast<const i32x4 *>(corr + (u * 4 + q) * 4);
       i32x4 P = mfma_i8(a0, b0, c0);
       P = mfma_i8(a1, b1, P);
-      acc = fmaf(planes_to_f32(P), sv, acc);
+      acc[k] = fmaf(planes_to_f32(P), sv, acc[k]);
     }
-    const float v = fold_rows(acc, lane);
-    if (lane < 8) red[k_it][wave][lane] = v;
+  }
+  const int k_it = nib;
+#pragma unroll
+  for (int k = 0; k < kDownItems; ++k) {
+    const float v = fold_rows(acc[k], lane);
+    if (k < nib && lane < 8) red[k][wave][lane] = v;
   }
   lds_barrier();
   for (int i = threadIdx.x; i < k_it * 8; i += blockDim.x) {
@@ -471,7 +491,7 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
   if (ev) (void)hipEventRecord(ev[0], s);
   const int d_items = L.H / 8;
   int dgrid = d_items < cus ? d_items : cus;
-  if (dgrid < (d_items + kMaxItems - 1) / kMaxItems) dgrid = (d_items + kMaxItems - 1) / kMaxItems;
+  if (dgrid < (d_items + kDownItems - 1) / kDownItems) dgrid = (d_items + kDownItems - 1) / kDownItems;
 #define COLI_DN(NU) \
   case NU: e = launch_down<NU>(L, nb, idx, y, dgrid, s); break;
   switch (L.K + 1) {
