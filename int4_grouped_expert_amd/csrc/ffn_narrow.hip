@@ -132,6 +132,7 @@ __device__ inline float fold_rows(float v, int lane) {
 constexpr int kMaxWaves = 16;
 constexpr int kGateupMaxWaves = 8;
 constexpr int kMaxItems = 8;  // items per block (the grid is sized for it)
+constexpr int kGateupItems = COLI_NARROW_MAX_K + 1;  // one per unit
 
 template <int NC>
 __global__ __launch_bounds__(kW * 8) __attribute__((amdgpu_waves_per_eu(2)))
@@ -139,7 +140,7 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
                    int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
   __shared__ int32_t sidx[COLI_NARROW_MAX_K];
   __shared__ float sgate[COLI_NARROW_MAX_K];
-  __shared__ float red[kMaxItems][kGateupMaxWaves][2][8];
+  __shared__ float red[kGateupItems][kGateupMaxWaves][2][8];
   // per wave, double-buffered: the item's group scales [frag][row][4 NC]
   __shared__ __align__(16) float ssc[kGateupMaxWaves][2][2][8][4 * NC];
   const int lane = threadIdx.x % kW, wave = threadIdx.x / kW;
@@ -150,16 +151,6 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   const int n_items = (K + 1) * nrb;
   if (int(blockIdx.x) >= n_items) return;
 
-  if (wave == 0) {
-    if (E <= 64) wave_topk_pl<1>(logits, E, K, lane, sidx, sgate);
-    else if (E <= 128) wave_topk_pl<2>(logits, E, K, lane, sidx, sgate);
-    else wave_topk_pl<4>(logits, E, K, lane, sidx, sgate);
-  }
-  lds_barrier();
-  if (blockIdx.x == 0 && int(threadIdx.x) < K) {
-    idx_out[threadIdx.x] = sidx[threadIdx.x];
-    gate_out[threadIdx.x] = sgate[threadIdx.x];
-  }
 
   const int n = lane % 16, q = lane / 16;
   const int r = n % 8, kap = n / 8;
@@ -190,9 +181,11 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     const uint8_t *wg, *wu;
     const float *sg, *su;
   };
+  // item it = (v, rb): unit v (0 = the shared expert, v >= 1 the routed
+  // expert sidx[v - 1]), rows 8 rb .. 8 rb + 7 of I
   auto ptrs = [&](int it) {
-    const int u = it / nrb, rb = it - u * nrb;
-    const uint8_t *blob = u < K ? L.experts + size_t(sidx[u]) * L.lay.bytes : L.shared;
+    const int v = it / nrb, rb = it - v * nrb;
+    const uint8_t *blob = v > 0 ? L.experts + size_t(sidx[v - 1]) * L.lay.bytes : L.shared;
     const size_t row = size_t(rb) * 8 + r;
     Ptrs p;
     p.wg = blob + L.lay.gq + (row * GH + goff) * 32 + 16 * (q % 2);
@@ -202,6 +195,10 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     return p;
   };
 
+  // the token's logits first: the top-K below then waits for them alone, not
+  // for the weight loads issued after them
+  float lg[4];
+  if (wave == 0) topk_load<4>(logits, E, lane, lg);
   uint4 rw[2][NC];
   float4 scg, scu;
   int it = blockIdx.x;
@@ -213,6 +210,14 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     for (int c = 0; c < NC; ++c) rw[0][c] = *reinterpret_cast<const uint4 *>(p.wg + 128 * c);
 #pragma unroll
     for (int c = 0; c < NC; ++c) rw[1][c] = *reinterpret_cast<const uint4 *>(p.wu + 128 * c);
+  }
+  // The first item is the shared expert's (the grid is I / 8 blocks), so its
+  // loads are in flight while wave 0 picks the token's experts.
+  if (wave == 0) topk_select<4>(lg, E, K, lane, sidx, sgate);
+  lds_barrier();
+  if (blockIdx.x == 0 && int(threadIdx.x) < K) {
+    idx_out[threadIdx.x] = sidx[threadIdx.x];
+    gate_out[threadIdx.x] = sgate[threadIdx.x];
   }
   wait_all_loads();
   int buf = 0, k_it = 0;
@@ -267,8 +272,9 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
       up += red[k][w][1][rr];
     }
     const int itk = int(blockIdx.x) + k * int(gridDim.x);
-    const int u = itk / nrb, rb = itk - u * nrb;
-    const float gw = u < K ? sgate[u] : 1.0f;
+    const int v = itk / nrb, rb = itk - v * nrb;
+    const int u = v > 0 ? v - 1 : K;  // h' rows: routed units in top-K order, shared last
+    const float gw = v > 0 ? sgate[v - 1] : 1.0f;
     nb.hn[size_t(u) * I + rb * 8 + rr] = gw * silu(g * xs) * (up * xs);
   }
 }
@@ -437,7 +443,7 @@ int cu_count() {
 // chunks per wave (1..6).
 int gateup_waves(int H, int *nc) {
   const int nch = H / 256;
-  const int pref[] = {4, 8, 2, 1};
+  const int pref[] = {8, 4, 2, 1};
   for (int w : pref)
     if (nch % w == 0 && nch / w >= 1 && nch / w <= 6) {
       *nc = nch / w;
@@ -477,8 +483,8 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
   int nc = 0;
   const int gw = gateup_waves(L.H, &nc);
   const int n_items = (L.K + 1) * (L.I / 8);
-  int ggrid = n_items < 2 * cus ? n_items : 2 * cus;
-  if (ggrid < (n_items + kMaxItems - 1) / kMaxItems) ggrid = (n_items + kMaxItems - 1) / kMaxItems;
+  // block b: row block b of every unit (unit-major in time, shared first)
+  const int ggrid = L.I / 8;
 #define COLI_GU(NC) \
   case NC: gateup_narrow<NC><<<ggrid, gw * kW, 0, s>>>(nb, L, logits, idx, gates); break;
   switch (nc) {

@@ -104,16 +104,22 @@ __device__ inline uint64_t wave_max_key(uint64_t k) {
 // idx/gates in ascending id order.  Each lane keeps the key of its best
 // untaken candidate; a round is one wave key maximum, after which only the
 // winner's lane rescans its PL values.
+// The token's logits, PL per lane (lane l holds ids l, l + 64, ...).
 template <int PL>
-__device__ __attribute__((always_inline)) inline void wave_topk_pl(
-    const float *__restrict__ lrow, int E, int K, int lane, int32_t *__restrict__ idx_out,
-    float *__restrict__ gate_out) {
-  float v[PL];
+__device__ __attribute__((always_inline)) inline void topk_load(const float *__restrict__ lrow,
+                                                                 int E, int lane, float (&v)[PL]) {
 #pragma unroll
   for (int j = 0; j < PL; ++j) {
     const int e = lane + kWaveLanes * j;
     v[j] = e < E ? lrow[e] : 0.0f;
   }
+}
+
+// Selection and gates from logits already in registers (see topk_load).
+template <int PL>
+__device__ __attribute__((always_inline)) inline void topk_select(
+    const float (&v)[PL], int E, int K, int lane, int32_t *__restrict__ idx_out,
+    float *__restrict__ gate_out) {
   uint32_t taken = 0;
   uint64_t lk = 0;
   auto rescan = [&]() {
@@ -173,6 +179,15 @@ __device__ __attribute__((always_inline)) inline void wave_topk_pl(
     }
     before += __popcll(bal);
   }
+}
+
+template <int PL>
+__device__ __attribute__((always_inline)) inline void wave_topk_pl(
+    const float *__restrict__ lrow, int E, int K, int lane, int32_t *__restrict__ idx_out,
+    float *__restrict__ gate_out) {
+  float v[PL];
+  topk_load<PL>(lrow, E, lane, v);
+  topk_select<PL>(v, E, K, lane, idx_out, gate_out);
 }
 
 // Dispatch on the logits per lane, ceil(E / 64) rounded up to 1, 2, 4, 8, 16.
