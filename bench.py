@@ -5,16 +5,17 @@ Metric: MoE-layer decode tokens/s + HBM GB/s (% of peak); prefill MFMA util.
 
 Workload (the step): one decode forward of the layer H=6144, I=2048, E=256 routed
 experts (top-8) + 1 shared expert, int4-g64 planar weights, T=1 fp32 token:
-router logits -> top-K + renormalised gates -> permute -> gate/up GEMV + SiLU*up ->
-down GEMV + gate-weighted combine + shared expert.  Inputs are resident in HBM
+router logits -> top-K + renormalised gates -> gate/up + SiLU*up -> down +
+gate-weighted combine + shared expert (three kernels on the int8 matrix cores).  Inputs are resident in HBM
 before the timed region.  Steps rotate over 8 byte-identical replicas of the layer
 (43.7 GB) and a pool of 64 tokens, so the 256 MB Infinity Cache cannot serve the
 ~191 MB a token touches.
 
 Printed: one JSON line (rank 0).  Extra fields: per-stage times and the roofline
-of the dominant kernel (gate/up GEMV, timed with HIP events on the library's
-stream), the T=32 Zipf decode batch, the T=2048 prefill (MFMA utilisation of the
-grouped GEMMs), and the fp64 CPU oracle on a bounded sample of the same workload.
+of the dominant kernel (the single-token gate/up kernel, timed with start/stop
+events stamped by its own launch on the library's stream), the T=32 Zipf decode
+batch, the T=2048 prefill (MFMA utilisation of the grouped GEMMs), and the fp64
+CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -123,25 +124,22 @@ def run_decode(coli, W, layers, cfg_id, T, steps, warmup, pool_n=64):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end)
-    # per-stage durations, HIP events recorded by the library between its stages
+    # per-stage durations: the library brackets each stage with a (start, stop)
+    # event pair on its stream; on the single-token path each stage is one
+    # kernel and the pair is stamped by that kernel's launch
     nst = min(steps, 400)
-    evs = [make_events(3) for _ in range(nst)]
-    st_start = torch.cuda.Event(enable_timing=True)
+    evs = [make_events(6) for _ in range(nst)]
     torch.cuda.synchronize()
     if hasattr(torch.cuda, "_sleep"):
         torch.cuda._sleep(50_000_000)  # let the host queue run ahead of the GPU
-    st_start.record()
     for i in range(nst):
-        callers[i % R][i % pool_n].timed(evs[i][1], 3)
+        callers[i % R][i % pool_n].timed(evs[i][1], 6)
     torch.cuda.synchronize()
     stage = [0.0, 0.0, 0.0]
-    prev = st_start
     for ev, _ in evs:
-        stage[0] += prev.elapsed_time(ev[0])
-        stage[1] += ev[0].elapsed_time(ev[1])
-        stage[2] += ev[1].elapsed_time(ev[2])
-        prev = ev[2]
-    stage = [s / nst for s in stage]
+        for s_ in range(3):
+            stage[s_] += ev[2 * s_].elapsed_time(ev[2 * s_ + 1])
+    stage = [s_ / nst for s_ in stage]
     nu = int(torch.unique(idx).numel())
     return dict(ms=ms, wall=wall, steps=steps, stage_ms=stage, T=T, n_unique_last=nu,
                 idx_last=idx.cpu())
@@ -184,16 +182,12 @@ def run_prefill(coli, W, layer, steps=10, warmup=2):
     ms = start.elapsed_time(end) / steps
     stage = [0.0] * 5
     for _ in range(steps):
-        s0 = torch.cuda.Event(enable_timing=True)
-        ev, arr = make_events(5)
-        s0.record()
-        call.timed(arr, 5)
+        ev, arr = make_events(10)
+        call.timed(arr, 10)
         torch.cuda.synchronize()
-        prev = s0
         for i in range(5):
-            stage[i] += prev.elapsed_time(ev[i])
-            prev = ev[i]
-    stage = [s / steps for s in stage]
+            stage[i] += ev[2 * i].elapsed_time(ev[2 * i + 1])
+    stage = [s_ / steps for s_ in stage]
     flops_routed = 2.0 * T * K * 3 * H * c["I"]
     flops_shared = 2.0 * T * 3 * H * c["I"]
     gemm_ms = stage[2] + stage[3]
@@ -210,8 +204,10 @@ def run_prefill(coli, W, layer, steps=10, warmup=2):
                 flops=flops_routed + flops_shared, dtype="fp16 MFMA operands (bf16 I/O)")
 
 
-def cpu_baseline(coli, W, budget_s=12.0):
-    """The oracle (fp64, as committed) on a bounded sample of decode tokens."""
+def cpu_baseline(coli, W, budget_s=12.0, n_tok=6):
+    """The oracle (fp64, as committed) on a bounded sample of the decode workload:
+    n_tok tokens of the pool (their experts quantised by the oracle beforehand,
+    untimed), cycled through single-token forwards for about budget_s seconds."""
     import numpy as np
     import oracle
     import torch
@@ -220,8 +216,6 @@ def cpu_baseline(coli, W, budget_s=12.0):
     wr = W.router_weights(1, "cuda")
     wr_h = wr.cpu().view(torch.int16).numpy().view(np.uint16)
     pool = W.token_pool(1, 64, "cuda").cpu().numpy()
-    # experts the sampled tokens need, quantised by the oracle itself (not timed)
-    n_tok = 24
     logits = oracle.router_logits(pool[:n_tok], wr_h, None)
     idx, _, _ = oracle.topk(logits, K)
     need = sorted(set(idx.reshape(-1).tolist()))
@@ -231,14 +225,39 @@ def cpu_baseline(coli, W, budget_s=12.0):
     shared = oracle.Expert.quantise(*(w.cpu().numpy() for w in W.expert_weights(1, E, "cuda")))
     done = 0
     t0 = time.perf_counter()
-    while done < n_tok and (time.perf_counter() - t0) < budget_s:
-        oracle.moe_forward(pool[done:done + 1], wr_h, None, experts, shared, H, I, K)
+    while (time.perf_counter() - t0) < budget_s:
+        k = done % n_tok
+        oracle.moe_forward(pool[k:k + 1], wr_h, None, experts, shared, H, I, K)
         done += 1
     el = time.perf_counter() - t0
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"{done} decode tokens (T=1 each) of the same layer, fp64, "
-                      f"{el:.1f} s; experts quantised by the oracle beforehand (untimed)"}
+            "sample": f"{done} single-token decode forwards of the same layer (H=6144, I=2048, "
+                      f"E=256, K=8 + shared), {n_tok} distinct tokens cycled, fp64, {el:.1f} s; "
+                      f"their {len(need)} experts + shared quantised by the oracle beforehand "
+                      f"(untimed)"}
+
+
+def profiled_traffic(kernel_src, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/<kernel>_decode_t1_traffic.md), or None when that summary was taken
+    on a different version of the kernel's source file."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_decode_t1_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    src = open(os.path.join(ROOT, kernel_src), "rb").read()
+    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -249,6 +268,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the T=32 and prefill legs")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first run a plain elementwise kernel (clamp) that reads and writes "
+                         "MIB MiB, the reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -261,6 +283,15 @@ def main():
     assert torch.cuda.is_available()
     torch.cuda.set_device(0)
     c = W.CONFIGS[1]
+    if args.copy_probe:
+        n = (args.copy_probe << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.clamp(a, min=-1e30, max=1e30, out=b)  # reads and writes copy_probe MiB
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: clamp kernel, {args.copy_probe} MiB read + written, 3 launches")
+        del a, b
 
     log(f"[bench] building layer ({args.replicas} replicas)")
     layers, nb = build_layer(coli, W, 1, args.replicas)
@@ -288,10 +319,12 @@ def main():
                 "frac": round(gbps / HBM_PEAK_GBS, 4)},
         "stage_ms": {"route": round(d["stage_ms"][0], 5), "gateup": round(d["stage_ms"][1], 5),
                      "down_combine": round(d["stage_ms"][2], 5)},
-        "roofline": {"kernel": "gateup_decode_kernel", "bound": "hbm",
+        "roofline": {"kernel": "gateup_narrow", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": gu_bytes},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic("int4_grouped_expert_amd/csrc/ffn_narrow.hip",
+                                                 "gateup_narrow"),
+                     "bytes_per_launch": gu_bytes, "avg_launch_ms": round(gu_ms, 5)},
     }
     if not args.no_extras:
         log("[bench] decode T=32 zipf")

@@ -222,12 +222,17 @@ int coli_moe_forward(const coli_moe_layer *L, coli_mode mode, const void *x,
                      size_t workspace_bytes, void *stream);
 
 /*
- * coli_moe_forward with stage timestamps, for measurement: after each stage
- * the call records events[i] (hipEvent_t values created by the caller, passed
- * as void*) on `stream`.  Stages: DECODE 0 route (logits, top-K, permute),
+ * coli_moe_forward with stage timestamps, for measurement.  events holds a
+ * (start, stop) pair of hipEvent_t values (created by the caller with timing
+ * enabled, passed as void*) per stage: events[2s] and events[2s + 1] bracket
+ * stage s on `stream`.  Stages: DECODE 0 route (logits, top-K, permute),
  * 1 gate/up, 2 down + combine; PREFILL 0 route, 1 activation conversion and
- * tile list, 2 gate/up, 3 down, 4 combine.  n_events must be at least the
- * stage count (3 or 5).  Same work and results as coli_moe_forward.
+ * tile list, 2 gate/up, 3 down, 4 combine.  Where a stage is a single kernel
+ * (the single-token decode path) the pair is stamped by that kernel's own
+ * launch, so elapsed(start, stop) is its execution time; elsewhere the events
+ * are recorded on the stream before and after the stage's launches.
+ * n_events must be at least 2 x the stage count (6 or 10).  Same work and
+ * results as coli_moe_forward.
  * Errors: as coli_moe_forward, plus EINVAL for a NULL or short event array.
  */
 int coli_moe_forward_timed(const coli_moe_layer *L, coli_mode mode,

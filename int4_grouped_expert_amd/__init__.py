@@ -210,7 +210,8 @@ def coli_moe_forward(layer: MoELayer, mode: int, x, y, workspace, topk_idx=None,
 
 def coli_moe_forward_timed(layer: MoELayer, mode: int, x, y, workspace, events, topk_idx=None,
                            topk_gate=None, stream=None):
-    """events: torch.cuda.Event objects (timing enabled), 3 (decode) or 5 (prefill)."""
+    """events: torch.cuda.Event objects (timing enabled): a (start, stop) pair per stage,
+    6 (decode) or 10 (prefill)."""
     T = x.shape[0]
     nbytes = workspace.numel() * workspace.element_size()
     arr = (_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])

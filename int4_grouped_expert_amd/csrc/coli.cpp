@@ -246,6 +246,7 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
   const int wbf = L->router_dtype == COLI_BF16;
 
   hipError_t e;
+  if (mode == COLI_PREFILL && ev) (void)hipEventRecord(ev[0], s);
   if (mode == COLI_DECODE) {
     DecodeBufs b;
     b.xh = reinterpret_cast<uint16_t *>(ws + w.xh);
@@ -261,20 +262,22 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
       nb.xcorr = reinterpret_cast<int32_t *>(ws + w.xcorr);
       nb.xsc = reinterpret_cast<float *>(ws + w.nxsc);
       nb.hn = reinterpret_cast<float *>(ws + w.hn);
+      // one kernel per stage: the events are stamped by the launches
       e = launch_router_narrow(reinterpret_cast<const float *>(x), T, L->H, L->w_router, wbf,
-                               L->E, L->router_bias, r.logits, nb, s);
+                               L->E, L->router_bias, r.logits, nb, s, ev ? ev[0] : nullptr,
+                               ev ? ev[1] : nullptr);
       if (e != hipSuccess) return COLI_EDEVICE;
-      if (ev) (void)hipEventRecord(ev[0], s);
       return dev_status(launch_ffn_narrow(d, nb, r.logits, r.idx, r.gates,
-                                          reinterpret_cast<float *>(y), s, ev ? ev + 1 : nullptr));
+                                          reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr));
     }
+    if (ev) (void)hipEventRecord(ev[0], s);
     e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, L->router_bias, r.logits,
                              &b, s);
     if (e != hipSuccess) return COLI_EDEVICE;
     e = launch_route_decode(r, T, L->E, L->K, b.slotmap, s);
     if (e != hipSuccess) return COLI_EDEVICE;
-    if (ev) (void)hipEventRecord(ev[0], s);
-    e = launch_ffn_decode(d, b, T, r, reinterpret_cast<float *>(y), s, ev ? ev + 1 : nullptr);
+    if (ev) (void)hipEventRecord(ev[1], s);
+    e = launch_ffn_decode(d, b, T, r, reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr);
     return dev_status(e);
   }
   if (wbf) {
@@ -290,11 +293,11 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
     e = launch_topk_permute(r, T, L->E, L->K, 1, s);
   }
   if (e != hipSuccess) return COLI_EDEVICE;
-  if (ev) (void)hipEventRecord(ev[0], s);
+  if (ev) (void)hipEventRecord(ev[1], s);
   e = launch_ffn_prefill(d, reinterpret_cast<const uint16_t *>(x), T, r,
                          reinterpret_cast<uint16_t *>(ws + w.h),
                          reinterpret_cast<uint16_t *>(ws + w.slot), reinterpret_cast<uint16_t *>(y),
-                         s, ev ? ev + 1 : nullptr);
+                         s, ev ? ev + 2 : nullptr);
   return dev_status(e);
 }
 
@@ -311,7 +314,7 @@ int coli_moe_forward_timed(const coli_moe_layer *L, coli_mode mode, const void *
                            void *y, int32_t *topk_idx_out, float *topk_gate_out,
                            void *workspace, size_t workspace_bytes, void *stream, void **events,
                            int n_events) {
-  const int need = mode == COLI_PREFILL ? 5 : 3;
+  const int need = 2 * (mode == COLI_PREFILL ? 5 : 3);
   if (!events || n_events < need) return COLI_EINVAL;
   for (int i = 0; i < need; ++i)
     if (!events[i]) return COLI_EINVAL;

@@ -494,20 +494,22 @@ hipError_t launch_ffn_decode(const LayerDev &L, const DecodeBufs &b, int T,
   const int64_t items = max_chunks * (L.I / 32);
   const int cap = 4096;
   const unsigned gblocks = unsigned(items < cap ? items : cap);
+  if (ev) (void)hipEventRecord(ev[0], s);
   if (one)
     gateup_decode<1, 4><<<gblocks, kGW * kWave, 0, s>>>(b.xh, b.xl, b.xsc, T, L, r, b.hh, b.hl,
                                                        b.hsc);
   else
     gateup_decode<2, 2><<<gblocks, kGW * kWave, 0, s>>>(b.xh, b.xl, b.xsc, T, L, r, b.hh, b.hl,
                                                        b.hsc);
-  if (ev) (void)hipEventRecord(ev[0], s);
+  if (ev) (void)hipEventRecord(ev[1], s);
   const int64_t ditems = int64_t(L.H / 16) * ((T + mc - 1) / mc);
   const unsigned dblocks = unsigned(ditems < cap ? ditems : cap);
+  if (ev) (void)hipEventRecord(ev[2], s);
   if (one)
     down_decode<1, 4><<<dblocks, kDW * kWave, 0, s>>>(b.hh, b.hl, b.hsc, T, L, r, b.slotmap, y);
   else
     down_decode<2, 2><<<dblocks, kDW * kWave, 0, s>>>(b.hh, b.hl, b.hsc, T, L, r, b.slotmap, y);
-  if (ev) (void)hipEventRecord(ev[1], s);
+  if (ev) (void)hipEventRecord(ev[3], s);
   return hipGetLastError();
 }
 

@@ -54,6 +54,8 @@
 //                  area once, then streams (item, unit) steps through a ring
 //                  one item deep.  The gates sit in h', so the combine is the
 //                  accumulation itself, in a fixed order (no atomics).
+#include <hip/hip_ext.h>
+
 #include "kernels.h"
 #include "wave.h"
 
@@ -454,13 +456,14 @@ int gateup_waves(int H, int *nc) {
 
 template <int NU>
 hipError_t launch_down(const LayerDev &L, const NarrowBufs &nb, const int32_t *idx, float *y,
-                       int grid, hipStream_t s) {
+                       int grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const int nw = L.I / 256;
   const size_t lds = size_t(nw) * down_wave_bytes<NU>();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_narrow<NU>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
-  down_narrow<NU><<<grid, nw * kW, lds, s>>>(nb, L, idx, y);
+  hipExtLaunchKernelGGL(down_narrow<NU>, dim3(grid), dim3(nw * kW), uint32_t(lds), s, start, stop,
+                        0, nb, L, idx, y);
   return hipGetLastError();
 }
 
@@ -485,8 +488,13 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
   const int n_items = (L.K + 1) * (L.I / 8);
   // block b: row block b of every unit (unit-major in time, shared first)
   const int ggrid = L.I / 8;
-#define COLI_GU(NC) \
-  case NC: gateup_narrow<NC><<<ggrid, gw * kW, 0, s>>>(nb, L, logits, idx, gates); break;
+  hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+  hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
+#define COLI_GU(NC)                                                                      \
+  case NC:                                                                               \
+    hipExtLaunchKernelGGL(gateup_narrow<NC>, dim3(ggrid), dim3(gw * kW), 0, s, e0, e1, 0, nb, L, \
+                          logits, idx, gates);                                           \
+    break;
   switch (nc) {
     COLI_GU(1) COLI_GU(2) COLI_GU(3) COLI_GU(4) COLI_GU(5) COLI_GU(6)
     default: return hipErrorInvalidValue;
@@ -494,12 +502,11 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
 #undef COLI_GU
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ev) (void)hipEventRecord(ev[0], s);
   const int d_items = L.H / 8;
   int dgrid = d_items < cus ? d_items : cus;
   if (dgrid < (d_items + kDownItems - 1) / kDownItems) dgrid = (d_items + kDownItems - 1) / kDownItems;
 #define COLI_DN(NU) \
-  case NU: e = launch_down<NU>(L, nb, idx, y, dgrid, s); break;
+  case NU: e = launch_down<NU>(L, nb, idx, y, dgrid, s, e2, e3); break;
   switch (L.K + 1) {
     COLI_DN(2) COLI_DN(3) COLI_DN(4) COLI_DN(5) COLI_DN(6) COLI_DN(7) COLI_DN(8) COLI_DN(9)
     COLI_DN(10) COLI_DN(11) COLI_DN(12) COLI_DN(13) COLI_DN(14) COLI_DN(15) COLI_DN(16)
@@ -507,9 +514,7 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
     default: return hipErrorInvalidValue;
   }
 #undef COLI_DN
-  if (e != hipSuccess) return e;
-  if (ev) (void)hipEventRecord(ev[1], s);
-  return hipSuccess;
+  return e;
 }
 
 }  // namespace coli

@@ -449,28 +449,32 @@ hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T,
   // first written by the down GEMM, after the gate/up GEMM has consumed xp.
   uint16_t *xp = slot_out;
   const int64_t n8 = int64_t(T) * L.H / 8;
+  if (ev) (void)hipEventRecord(ev[0], s);
   prefill_prep<<<dim3(unsigned((n8 + 255) / 256)), 256, 0, s>>>(x, n8, xp);
   prefill_tiles<<<1, 1024, 0, s>>>(r, T);
-  if (ev) (void)hipEventRecord(ev[0], s);
+  if (ev) (void)hipEventRecord(ev[1], s);
   const int max_units = (T * L.K < L.E ? T * L.K : L.E) + 1;
   // upper bound of M-chunks: every routed pair alone in its chunk is not
   // possible; sum ceil(n/64) <= T*K/64 + routed units, plus the shared chunks
   const int64_t max_chunks = int64_t(T) * L.K / kMC + max_units + (T + kMC - 1) / kMC;
   const int cap = 2048;
+  if (ev) (void)hipEventRecord(ev[2], s);
   {
     const int64_t items = max_chunks * ((L.I + 127) / 128);
     grouped_gemm_kernel<true><<<unsigned(items < cap ? items : cap), 256, 0, s>>>(L, r, T, xp, h);
   }
-  if (ev) (void)hipEventRecord(ev[1], s);
+  if (ev) (void)hipEventRecord(ev[3], s);
+  if (ev) (void)hipEventRecord(ev[4], s);
   {
     const int64_t items = max_chunks * ((L.H + 255) / 256);
     grouped_gemm_kernel<false><<<unsigned(items < cap ? items : cap), 256, 0, s>>>(L, r, T, h,
                                                                                   slot_out);
   }
-  if (ev) (void)hipEventRecord(ev[2], s);
+  if (ev) (void)hipEventRecord(ev[5], s);
   const int64_t nthr = int64_t(T) * (L.H / 8);
+  if (ev) (void)hipEventRecord(ev[6], s);
   combine_kernel<<<dim3(unsigned((nthr + 255) / 256)), 256, 0, s>>>(slot_out, T, L.H, L.K, y);
-  if (ev) (void)hipEventRecord(ev[3], s);
+  if (ev) (void)hipEventRecord(ev[7], s);
   return hipGetLastError();
 }
 

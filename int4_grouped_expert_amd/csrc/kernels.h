@@ -122,12 +122,14 @@ hipError_t launch_route_decode(const Routing &r, int T, int E, int K,
 size_t permute_chunk_ints(int T, int E);
 // Single-token decode router: logits [T, E] and x as digit planes (nb.xdig,
 // nb.xcorr, nb.xsc).  Requires H % 256 == 0, T <= 4.
+// start/stop: optional events stamped at the kernel's start and end.
 hipError_t launch_router_narrow(const float *x, int T, int H, const void *wr, int w_bf16,
                                 int E, const float *bias, float *logits,
-                                const NarrowBufs &nb, hipStream_t s);
+                                const NarrowBufs &nb, hipStream_t s, hipEvent_t start = nullptr,
+                                hipEvent_t stop = nullptr);
 
 // ---- ffn_decode.hip -----------------------------------------------------
-// ev: optional stage events (NULL or 2 entries: after gate/up, after down).
+// ev: optional stage events (NULL or 4: start and stop of gate/up, of down).
 hipError_t launch_ffn_decode(const LayerDev &L, const DecodeBufs &b, int T,
                              const Routing &r, float *y, hipStream_t s,
                              hipEvent_t *ev);
@@ -136,13 +138,14 @@ hipError_t launch_ffn_decode(const LayerDev &L, const DecodeBufs &b, int T,
 // Whether the single-token int8 matrix-core path covers this layer and T.
 bool narrow_supported(const LayerDev &L, int T);
 // Top-K of the token (from logits; idx/gates written), gate/up -> nb.hn, down
-// -> y.  ev: optional (NULL or 2 entries: after gate/up, after down).
+// -> y.  ev: optional (NULL or 4: start and stop of the gate/up kernel, of the
+// down kernel, stamped by the kernel launches themselves).
 hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const float *logits,
                              int32_t *idx, float *gates, float *y, hipStream_t s,
                              hipEvent_t *ev);
 
 // ---- ffn_prefill.hip ----------------------------------------------------
-// ev: optional stage events (NULL or 4 entries: after prep+tiles, gate/up,
+// ev: optional stage events (NULL or 8: start and stop of prep + tiles, gate/up,
 // down, combine).
 hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T,
                               const Routing &r, uint16_t *h,

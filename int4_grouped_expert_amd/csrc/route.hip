@@ -20,6 +20,8 @@
 //   permute_count/scan/place  the permute for large T in three launches:
 //                         per-chunk (64 tokens) expert bitmaps, a scan over
 //                         chunks, then stable placement by bitmap popcount.
+#include <hip/hip_ext.h>
+
 #include "kernels.h"
 #include "wave.h"
 
@@ -574,11 +576,14 @@ hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
 
 hipError_t launch_router_narrow(const float *x, int T, int H, const void *wr, int w_bf16,
                                 int E, const float *bias, float *logits,
-                                const NarrowBufs &nb, hipStream_t s) {
+                                const NarrowBufs &nb, hipStream_t s, hipEvent_t start,
+                                hipEvent_t stop) {
   if (w_bf16)
-    router_narrow_kernel<true><<<E, 256, 0, s>>>(x, T, H, wr, E, bias, logits, nb);
+    hipExtLaunchKernelGGL(router_narrow_kernel<true>, dim3(E), dim3(256), 0, s, start, stop, 0, x,
+                          T, H, wr, E, bias, logits, nb);
   else
-    router_narrow_kernel<false><<<E, 256, 0, s>>>(x, T, H, wr, E, bias, logits, nb);
+    hipExtLaunchKernelGGL(router_narrow_kernel<false>, dim3(E), dim3(256), 0, s, start, stop, 0,
+                          x, T, H, wr, E, bias, logits, nb);
   return hipGetLastError();
 }
 
