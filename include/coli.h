@@ -3,11 +3,11 @@
  * planar experts, on one AMD MI355X (gfx950).
  *
  * The layer (sources cited by page title and section):
- *   route   -- page "Colibri 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
+ *   route   -- page "Colibrì 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
  *              section 十一: the router picks the top-k experts of each token;
  *              gates are the normalised values the layer applies (page
- *              "colibri 路由遥测全解析", section 分离计数与追踪).
- *   union   -- page "Colibri 深度解析", section 四: positions of a batch routed
+ *              "colibrì 路由遥测全解析", section 分离计数与追踪).
+ *   union   -- page "Colibrì 深度解析", section 四: positions of a batch routed
  *              to one expert are grouped so that the expert is read once.
  *   experts -- page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
  *              section 权重转换: int4 grouped weights, group 64, one fp32 scale
@@ -15,15 +15,15 @@
  *              planar nibbles (byte k of a 64-group: element k in the low
  *              nibble, element k+32 in the high nibble); the expert FFN reads
  *              these bytes directly.  An expert's gate, up and down matrices
- *              sit side by side (page "Colibri 深度解析", section 四).
+ *              sit side by side (page "Colibrì 深度解析", section 四).
  *
  * Conventions for every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller, unless a
  *     comment says "host".  The library never allocates, frees or
  *     synchronises; all work is enqueued on `stream` (a hipStream_t passed
  *     as void*, NULL = the default stream) and is asynchronous.
- *   - Fail closed (the pages' guard convention, page "Colibri 深度解析",
- *     section 十五, and page "colibri 路由遥测全解析", section 测试与 CI 保障):
+ *   - Fail closed (the pages' guard convention, page "Colibrì 深度解析",
+ *     section 十五, and page "colibrì 路由遥测全解析", section 测试与 CI 保障):
  *     every argument check runs on the host before the first launch; on any
  *     error the call returns a negative status and writes nothing.
  *   - A launch failure reported by the HIP runtime returns COLI_EDEVICE.
@@ -96,7 +96,7 @@ int coli_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
                         void *stream);
 
 /* ---------------------------------------------------------------------- */
-/* route (page "Colibri 深度解析", section 十一)                           */
+/* route (page "Colibrì 深度解析", section 十一)                           */
 /* ---------------------------------------------------------------------- */
 
 /*
@@ -113,7 +113,7 @@ int coli_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
  *                    and renormalised to sum 1), same order as topk_idx
  * Selection: the K largest logits; on equal logits the lower id wins; NaN
  * never wins.  A slot with no valid candidate (every remaining logit NaN)
- * takes id k if free, else the lowest free id (page "colibri 路由遥测全解析",
+ * takes id k if free, else the lowest free id (page "colibrì 路由遥测全解析",
  * section 测试与 CI 保障); its gates are then unspecified.
  * Requires H % 8 == 0.  Errors: EINVAL, ESHAPE (T outside [0, MAX_TOKENS],
  * H outside [8, MAX_DIM] or H % 8, E outside [1, MAX_EXPERTS], K outside
@@ -125,7 +125,7 @@ int coli_router_topk(const void *x, coli_dtype x_dtype, int T, int H,
                      float *topk_gate, float *logits, void *stream);
 
 /*
- * Batch-union permute (page "Colibri 深度解析", section 四).
+ * Batch-union permute (page "Colibrì 深度解析", section 四).
  *   topk_idx [T, K] int32 input, ids in [0, E)
  *   counts   [E]    int32: pairs (t, slot) routed to each expert
  *   offsets  [E+1]  int32: exclusive running sum of counts

@@ -5,7 +5,7 @@
 // Method: page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
 // section 权重转换 -- the expert FFN consumes the planar bytes as they are
 // (byte k of a 64-group: element k low nibble, element k+32 high nibble,
-// u = q + 8; weight = s * (u - 8)).  Batch union (page "Colibri 深度解析",
+// u = q + 8; weight = s * (u - 8)).  Batch union (page "Colibrì 深度解析",
 // section 四): each unique expert of the batch is read once and applied to all
 // of its tokens.
 //

@@ -6,7 +6,7 @@
 // section 权重转换 -- the expert FFN reads the planar bytes as they are (byte k
 // of a 64-group: element k low nibble, element k+32 high nibble, u = q + 8;
 // weight = s * (u - 8)); SiLU(gate) * up, then down, then the gate-weighted
-// sum over the selected experts plus the shared expert (page "Colibri 深度解析",
+// sum over the selected experts plus the shared expert (page "Colibrì 深度解析",
 // sections 四 and 十一).  The token's top-K runs inside the gate/up kernel.
 //
 // Arithmetic.  An activation vector a is held in fixed point, a = A * 2^-e

@@ -3,7 +3,7 @@
 //
 // Method: page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
 // section 权重转换 (planar int4-g64 bytes consumed as they are; weight =
-// s * (u - 8)); batch union, page "Colibri 深度解析", section 四 (each unique
+// s * (u - 8)); batch union, page "Colibrì 深度解析", section 四 (each unique
 // expert is read once per batch and applied to all of its tokens).
 //
 // Work item = (unit, M-chunk of <= 64 of the unit's tokens, N-tile of output

@@ -1,11 +1,11 @@
 // route.hip -- router logits, top-K with renormalised gates, batch-union
 // permute.
 //
-// Route step: page "Colibri 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
+// Route step: page "Colibrì 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
 // section 十一 (the router selects the top-k experts per token); gates are the
-// normalised values applied by the layer (page "colibri 路由遥测全解析",
+// normalised values applied by the layer (page "colibrì 路由遥测全解析",
 // section 分离计数与追踪); NaN guard (same page, section 测试与 CI 保障).
-// Batch union: page "Colibri 深度解析", section 四.
+// Batch union: page "Colibrì 深度解析", section 四.
 //
 // Kernels
 //   router_logits_kernel  GEMV-shaped logits for small T (decode): one wave

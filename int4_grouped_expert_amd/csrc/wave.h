@@ -2,9 +2,9 @@
 // kernels: DPP reductions (every lane gets the same value, combined in a
 // fixed order) and the per-token top-K with renormalised gates.
 //
-// Top-K: page "Colibri 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
+// Top-K: page "Colibrì 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
 // section 十一 (per-token top-k experts); gates normalised over the selected
-// experts (page "colibri 路由遥测全解析", section 分离计数与追踪); NaN logits
+// experts (page "colibrì 路由遥测全解析", section 分离计数与追踪); NaN logits
 // never win (same page, section 测试与 CI 保障).
 #pragma once
 #include <hip/hip_runtime.h>

@@ -11,9 +11,9 @@ Every function names the passage it follows in the C source's comments:
 
 * quantiser and planar packer -- page "从源码开始colibri纯C引擎的编译、权重转换
   与.bin直映射实战", section 权重转换;
-* router top-K with renormalised gates -- page "Colibri 深度解析", section 十一,
-  and page "colibri 路由遥测全解析", sections 分离计数与追踪 and 测试与 CI 保障;
-* batch-union permute -- page "Colibri 深度解析", section 四;
+* router top-K with renormalised gates -- page "Colibrì 深度解析", section 十一,
+  and page "colibrì 路由遥测全解析", sections 分离计数与追踪 and 测试与 CI 保障;
+* batch-union permute -- page "Colibrì 深度解析", section 四;
 * expert FFN, combine, RMSNorm -- the readings listed in the design doc.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``

@@ -9,7 +9,7 @@
  * pages, in the pages' order, with no blocking, fusion or reordering.
  *
  * Sources (cited by page title and section):
- *   [P1] "Colibri 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
+ *   [P1] "Colibrì 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
  *        section 四 (batch union: positions routed to one expert read it once)
  *        and section 十一 (the five token stages; "route" selects top-k).
  *   [P2] "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
@@ -17,7 +17,7 @@
  *        clip to [-8,7], rint, +8 offset, one f32 scale per group, and the
  *        planar nibble layout of the expert FFN: byte k of a 64-group holds
  *        element k low and element k+32 high).
- *   [P4] "colibri 路由遥测全解析.coli_usage专家历史、ROUTE_TRACE追踪流与
+ *   [P4] "colibrì 路由遥测全解析.coli_usage专家历史、ROUTE_TRACE追踪流与
  *        route_trace.h统一格式", sections 分离计数与追踪 / 追踪流ROUTE_TRACE
  *        (the gates applied are the normalised ones) and 测试与 CI 保障
  *        (router NaN guard: a slot with no valid candidate falls back to a

@@ -1,7 +1,7 @@
 """GPU parity of the whole layer (coli_moe_forward), decode and prefill, and of the
 RMSNorm between stacked layers.
 
-Layer: route (page "Colibri 深度解析", section 十一) -> batch union (section 四) ->
+Layer: route (page "Colibrì 深度解析", section 十一) -> batch union (section 四) ->
 int4-g64 planar expert FFN (page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
 section 权重转换) -> gate-weighted combine with the normalised gates (page "colibri 路由
 遥测全解析", section 追踪流ROUTE_TRACE) + the shared expert.

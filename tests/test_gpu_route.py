@@ -1,7 +1,7 @@
 """GPU parity of the route stage: router logits, top-K with renormalised gates
-(page "Colibri 深度解析", section 十一; gates normalised as applied, page "colibri 路由
+(page "Colibrì 深度解析", section 十一; gates normalised as applied, page "colibri 路由
 遥测全解析", section 分离计数与追踪; NaN guard, same page, section 测试与 CI 保障) and the
-batch-union permute (page "Colibri 深度解析", section 四).
+batch-union permute (page "Colibrì 深度解析", section 四).
 
 Indices, counts, offsets, perm and the unique list are bit-exact; gates and logits
 within the fp32 tolerance.  Inputs pass the oracle's top-K margin filter (>= 1e-3).
@@ -68,7 +68,7 @@ def test_router_ties_lower_id_wins():
 
 
 def test_router_nan_fallback():
-    """All-NaN logits: slot k takes id k (page "colibri 路由遥测全解析", 测试与 CI 保障)."""
+    """All-NaN logits: slot k takes id k (page "colibrì 路由遥测全解析", 测试与 CI 保障)."""
     H, E, K = 64, 12, 4
     wr = torch.ones((E, H), device="cuda") * 0.01
     x = torch.full((2, H), float("nan"), device="cuda")

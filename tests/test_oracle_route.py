@@ -1,10 +1,10 @@
 """Pins for the oracle's router logits, top-K with renormalised gates, and permute.
 
-Route step: page "Colibri 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
+Route step: page "Colibrì 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
 section 十一 (the router selects the top-k experts of a token); the gates applied are
-the normalised ones (page "colibri 路由遥测全解析", section 分离计数与追踪); a NaN
+the normalised ones (page "colibrì 路由遥测全解析", section 分离计数与追踪); a NaN
 router falls back to deterministic ids (same page, section 测试与 CI 保障).
-Batch union: page "Colibri 深度解析", section 四 (positions routed to the same expert
+Batch union: page "Colibrì 深度解析", section 四 (positions routed to the same expert
 are grouped so the expert is read once).
 """
 import itertools
