@@ -31,6 +31,7 @@ bool layer_shape_ok(int H, int I, int E, int K) {
 // Workspace carve-up (byte offsets, each section 256-byte aligned).
 struct WsLayout {
   size_t logits, idx, gates, counts, offsets, perm, unique, n_unique, chunk, h, slot;
+  size_t xp, sx, sh;                          // prefill only
   size_t xh, xl, xsc, hh, hl, hsc, slotmap;  // decode only
   size_t xdig, xcorr, nxsc, hn;               // decode, single-token path
   size_t total;
@@ -50,10 +51,15 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
   size_t chunk = permute_chunk_ints(T, E);
   if (chunk < size_t(E) + 2) chunk = size_t(E) + 2;
   w.chunk = o; o += align256(chunk * 4);
+  w.xp = w.sx = w.sh = 0;
   w.h = w.slot = w.xh = w.xl = w.xsc = w.hh = w.hl = w.hsc = w.slotmap = 0;
   w.xdig = w.xcorr = w.nxsc = w.hn = 0;
   if (mode == COLI_PREFILL) {
-    w.h = o; o += align256((TK + T) * size_t(I) * 2);
+    const PrefillLayout pl = prefill_layout(H, I);
+    w.xp = o; o += align256(size_t(T) * pl.HP * 2);
+    w.sx = o; o += align256(size_t(T) * pl.CSX * 2);
+    w.h = o; o += align256((TK + T) * size_t(pl.IP) * 2);
+    w.sh = o; o += align256((TK + T) * size_t(pl.CSI) * 2);
     w.slot = o; o += align256((TK + T) * size_t(H) * 2);
   } else {
     const size_t units = TK < size_t(E) ? TK : size_t(E);
@@ -294,10 +300,14 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
   }
   if (e != hipSuccess) return COLI_EDEVICE;
   if (ev) (void)hipEventRecord(ev[1], s);
-  e = launch_ffn_prefill(d, reinterpret_cast<const uint16_t *>(x), T, r,
-                         reinterpret_cast<uint16_t *>(ws + w.h),
-                         reinterpret_cast<uint16_t *>(ws + w.slot), reinterpret_cast<uint16_t *>(y),
-                         s, ev ? ev + 2 : nullptr);
+  PrefillBufs pb;
+  pb.xp = reinterpret_cast<uint16_t *>(ws + w.xp);
+  pb.sx = reinterpret_cast<uint16_t *>(ws + w.sx);
+  pb.h = reinterpret_cast<uint16_t *>(ws + w.h);
+  pb.sh = reinterpret_cast<uint16_t *>(ws + w.sh);
+  pb.slot = reinterpret_cast<uint16_t *>(ws + w.slot);
+  e = launch_ffn_prefill(d, reinterpret_cast<const uint16_t *>(x), T, r, pb,
+                         reinterpret_cast<uint16_t *>(y), s, ev ? ev + 2 : nullptr);
   return dev_status(e);
 }
 

@@ -145,12 +145,22 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
                              hipEvent_t *ev);
 
 // ---- ffn_prefill.hip ----------------------------------------------------
+// Row strides (elements) of the prefill activation buffers: staged x and h
+// rows are padded to whole 256-column blocks; group-sum rows hold a hi/lo
+// fp16 pair per group, padded to whole 16-group blocks.
+struct PrefillLayout {
+  int HP, IP, CSX, CSI;
+};
+PrefillLayout prefill_layout(int H, int I);
+// Prefill buffers (inside the workspace): xp [T, HP] fp16, sx [T, CSX],
+// h [T*K + T, IP] fp16, sh [T*K + T, CSI], slot [T*K + T, H] fp16.
+struct PrefillBufs {
+  uint16_t *xp, *sx, *h, *sh, *slot;
+};
 // ev: optional stage events (NULL or 8: start and stop of prep + tiles, gate/up,
 // down, combine).
-hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T,
-                              const Routing &r, uint16_t *h,
-                              uint16_t *slot_out, uint16_t *y, hipStream_t s,
-                              hipEvent_t *ev);
+hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T, const Routing &r,
+                              const PrefillBufs &b, uint16_t *y, hipStream_t s, hipEvent_t *ev);
 
 // ---- rmsnorm.hip --------------------------------------------------------
 hipError_t launch_rmsnorm_f32(const float *x, float *y, int T, int H,
