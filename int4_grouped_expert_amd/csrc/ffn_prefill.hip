@@ -9,19 +9,20 @@
 // Work item = (unit, M-chunk of <= 128 of the unit's tokens, N-tile of 256
 // weight rows).  A unit is a unique routed expert of the batch or the shared
 // expert.  One block of 4 waves (one per SIMD) per CU walks its items; wave w
-// owns 64 weight rows (4 column fragments of 16) and all M fragments of the
-// chunk, on v_mfma_f32_16x16x32_f16.
+// owns 64 weight rows (2 column fragments of 32) and all 32-row M fragments of
+// the chunk, on v_mfma_f32_32x32x16_f16 (on gfx950 the 16x16x32 form needs far
+// more independent accumulators per wave to approach the matrix-core rate).
 //
 // Weight stream.  A super-step covers 256 k = 4 groups = 128 contiguous bytes
-// of every weight row.  Per fragment two 16-byte loads per lane cover rows
-// 0-7 and 8-15 of the fragment, 8 lanes per row, so each load instruction
-// reads 8 whole 128-byte lines (instructions that touch 16 half lines run at
-// less than half the HBM rate).  Two DPP half-row moves then give lane
-// (q, n) = (lane/16, lane%16) the 16-byte parts 2q and 2q+1 of row n: the two
-// halves of group 4*ss + q.  Scales: lane (q, n) loads groups 16i + 4q..+3 of
-// row n as one float4 per 4 super-steps; a 4x4 transpose over the lane rows
-// (v_permlane32_swap, v_permlane16_swap) hands it the scale of group
-// 4*ss + q for each of those super-steps.
+// of every weight row.  Per 32-row fragment four 16-byte loads per lane, load a
+// covering rows 8a..8a+7 with 8 lanes per row (each load instruction reads 8
+// whole 128-byte lines); lane (h, n) = (lane/32, lane%32) of load a takes row
+// 8a + n%8, part 4h + n/8.  A 4x4 exchange between the load index and lane
+// bits 3-4 (DPP half-row moves, then v_permlane16_swap) leaves part 4h + d of
+// row n in register d: lane (h, n) holds groups 2h, 2h+1 of the super-step.
+// Scales: lane (h, n) loads groups 16i + 8h .. +7 of row n as two float4 per 4
+// super-steps; v_permlane32_swap between lane halves regroups them so that the
+// lane holds groups 4c + 2h, 4c + 2h + 1 for each super-step c of the block.
 //
 // Dequant without the -8: for a 32-bit word d of nibbles, (d & 0x000F000F) |
 // 0x64006400 is the fp16 pair {1024 + u, 1024 + u'} and (d & 0x00F000F0) |
@@ -29,21 +30,22 @@
 // the exact constant -1024 s (or -64 s) gives s*u rounded once.  The -8 of
 // the code is folded into a correction GEMM: out -= 8 * sum_g s[n][g] *
 // S[m][g], S = per-group sums of the fp16 activations, held as fp16 hi + lo
-// pairs, run on the same MFMAs as extra k steps (one per 16 groups).
+// pairs, run on the same MFMAs as extra k steps (two per 16 groups).
 //
-// K order.  Word s (0..3) of half t (0, 1) of a group holds elements
-// o + {0, 2, 32, 34, 1, 3, 33, 35} with o = 16t + 4s, in that order after
-// the extraction above.  The activations are stored (fp16) in the matching
-// order, so an MFMA A operand is one contiguous 16-byte run: inside each
-// 256-k block, position 128t + 32q + 8s + i holds element 16t + 4s + sigma[i]
-// of group 4*block + q, sigma = {0, 2, 32, 34, 1, 3, 33, 35}.  Rows are
-// padded to whole 256-k blocks; the padding holds zeros.
+// K order.  Word w (0..3) of half t (0, 1) of a group holds elements
+// o + {0, 2, 32, 34, 1, 3, 33, 35} with o = 16t + 4w, in that order after the
+// extraction above; it feeds MFMA k-step 8 (g & 1) + 4t + w of its super-step,
+// k-half (g & 3) / 2.  The activations are stored (fp16) with every 64-group
+// contiguous in the matching order: position 8(4t + w) + i of group g holds
+// element 16t + 4w + sigma[i], sigma = {0, 2, 32, 34, 1, 3, 33, 35}, so an MFMA
+// A operand is one 16-byte run.  Rows are padded to whole 4-group blocks; the
+// padding holds zeros.
 //
 // Numerics: fp16 operands, fp32 accumulation.  Activations must lie in fp16
 // range and scales below 64 (|w| < 448).
 //
-// Kernels: pf_prep (x bf16 -> fp16 staged copy + group sums), pf_hpad (zero
-// the padding of the h rows), prefill_tiles (M-chunk prefix over units),
+// Kernels: pf_prep (x bf16 -> fp16 staged copy + group sums), pf_pads (zero
+// the padding of the h and h-sum rows), prefill_tiles (M-chunk prefix over units),
 // pf_gemm<true> (h = SiLU(gate) * up, fp16, staged order, + its group sums),
 // pf_gemm<false> (gate-scaled per-slot outputs, fp16), combine (y = sum of a
 // token's slots + its shared output, bf16).
@@ -58,29 +60,25 @@ constexpr int kWave = 64;
 constexpr int kWaves = 4;                      // one per SIMD
 constexpr int kThreads = kWave * kWaves;
 constexpr int kMC = 128;                       // tokens per M-chunk
-constexpr int kCorrOff = 512;                  // correction operand inside a staged row
-constexpr int kPitch = 512 + 64 + 16;          // LDS bytes per staged row
-constexpr int kStage = kMC * kPitch;
-constexpr int kLdsRowIdx = 2 * kStage;            // int[kMC]  A / S row of each chunk row
-constexpr int kLdsOutRow = kLdsRowIdx + kMC * 4;  // int[kMC]  output row
-constexpr int kLdsGate = kLdsOutRow + kMC * 4;    // float[kMC] gate (down)
-constexpr int kLdsRed = kLdsGate + kMC * 4;       // float[kWaves][kMC] (gate/up)
-constexpr int kLdsBytes = kLdsRed + kWaves * kMC * 4;
+constexpr int kRowB = 512;                     // staged bytes per chunk row per super-step
+constexpr int kStageB = kMC * kRowB;           // one activation stage
+constexpr int kCorrB = kMC * 64;               // one correction-operand stage
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ inline uint32_t pack_f16x2(_Float16 a, _Float16 b) {
   return uint32_t(__builtin_bit_cast(uint16_t, a)) |
          (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-// Position of element e (0..63) of group g in a staged activation row.
-__device__ inline int act_pos(int g, int e) {
-  const int t = (e >> 4) & 1, s = (e >> 2) & 3;
+// Position of element e (0..63) of a group inside the group's 64 staged slots.
+__device__ inline int grp_pos(int e) {
+  const int c = 4 * ((e >> 4) & 1) + ((e >> 2) & 3);
   const int i = ((e & 1) << 2) | (((e >> 5) & 1) << 1) | ((e >> 1) & 1);
-  return (g >> 2) * 256 + t * 128 + (g & 3) * 32 + s * 8 + i;
+  return 8 * c + i;
 }
 
 // hi + lo fp16 pair of a float (hi = fp16(v), lo = fp16(v - hi)).
@@ -104,7 +102,7 @@ __global__ __launch_bounds__(256) void pf_prep(const uint16_t *__restrict__ x, i
   const int64_t tg = i >> 3;
   if (tg >= int64_t(T) * GP) return;  // whole groups of 8 lanes leave together
   const int t = int(tg / GP), g = int(tg % GP);
-  const int tt = c >> 2, s = c & 3, o = 16 * tt + 4 * s;
+  const int o = 16 * (c >> 2) + 4 * (c & 3);
   uint4 out = uint4{0u, 0u, 0u, 0u};
   float sum = 0.0f;
   if (g < G) {
@@ -129,22 +127,23 @@ __global__ __launch_bounds__(256) void pf_prep(const uint16_t *__restrict__ x, i
   sum += __shfl_xor(sum, 1, 8);
   sum += __shfl_xor(sum, 2, 8);
   sum += __shfl_xor(sum, 4, 8);
-  *reinterpret_cast<uint4 *>(xp + int64_t(t) * HP + (g >> 2) * 256 + tt * 128 + (g & 3) * 32 +
-                             s * 8) = out;
+  *reinterpret_cast<uint4 *>(xp + int64_t(t) * HP + 64 * g + 8 * c) = out;
   if (c == 0 && g < G)
     *reinterpret_cast<uint32_t *>(sx + int64_t(t) * CSX + 2 * g) = split_f16(sum);
+  // the row's padding entries (groups G .. CSX/2 - 1) are zeros
+  if (c == 0 && g == 0)
+    for (int e = 2 * G; e < CSX; e += 2) *reinterpret_cast<uint32_t *>(sx + int64_t(t) * CSX + e) = 0u;
 }
 
-// Zero the padding groups (G..GP-1, all in the last 256-k block) of every h row.
-__global__ __launch_bounds__(256) void pf_hpad(uint16_t *__restrict__ h, int64_t rows, int G,
-                                               int IP) {
-  const int GP = IP / 64, per_row = (GP - G) * 8;  // 8 runs of 16 B per group
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= rows * per_row) return;
-  const int64_t row = i / per_row;
-  const int k = int(i % per_row), g = G + k / 8, c = k % 8;
-  *reinterpret_cast<uint4 *>(h + row * IP + (g >> 2) * 256 + (c >> 2) * 128 + (g & 3) * 32 +
-                             (c & 3) * 8) = uint4{0u, 0u, 0u, 0u};
+// Zero the padding of every h row (groups G..IP/64-1, all in the last 256-k
+// block) and of every h group-sum row (entries 2G..CSI-1).  One thread per row.
+__global__ __launch_bounds__(256) void pf_pads(uint16_t *__restrict__ h, uint16_t *__restrict__ sh,
+                                               int64_t rows, int G, int IP, int CSI) {
+  const int64_t row = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (row >= rows) return;
+  for (int k = 64 * G; k < IP; k += 8)
+    *reinterpret_cast<uint4 *>(h + row * IP + k) = uint4{0u, 0u, 0u, 0u};
+  for (int e = 2 * G; e < CSI; e += 2) *reinterpret_cast<uint32_t *>(sh + row * CSI + e) = 0u;
 }
 
 // ------------------------------------------------------------------ tiles
@@ -253,7 +252,11 @@ __device__ inline float row16_sum(float v) {
   return v;
 }
 
-__device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU with the hardware exp2 and reciprocal (relative error ~1e-6, far below
+// the fp16 rounding of h that follows)
+__device__ inline float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * z));
+}
 
 // Buffer resource over [p, p + bytes): raw buffer loads at offsets >= bytes
 // return zeros, so masked lanes take the offset kOff and no branch.
@@ -269,14 +272,33 @@ __device__ inline float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(float, uint32_t(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0)));
 }
 
-// One work item.  NMF = number of 16-row M fragments the chunk needs.  The
-// chunk's row tables are in LDS (see pf_gemm).
+// LDS of the GEMM kernels.  Two activation stages and two correction stages
+// as separate arrays: the stage being read and the stage being filled by DMA
+// are then distinct objects to the compiler, which keeps it from waiting for
+// the DMA before every read of the other stage.  Staged rows are XOR-swizzled
+// in 16-byte chunks (chunk c of row r sits at c ^ (r & 15), correction chunk c
+// at c ^ ((r >> 2) & 3)) so that the 16 rows an MFMA operand reads hit 16
+// different bank groups; each DMA instruction fills 1 KB of consecutive LDS.
+__shared__ __attribute__((aligned(16))) uint8_t g_st0[kStageB];
+__shared__ __attribute__((aligned(16))) uint8_t g_st1[kStageB];
+__shared__ __attribute__((aligned(16))) uint8_t g_sc0[kCorrB];
+__shared__ __attribute__((aligned(16))) uint8_t g_sc1[kCorrB];
+__shared__ int g_rowidx[kMC];   // A / S row of each chunk row (-1: padding)
+__shared__ int g_outrow[kMC];   // output row
+__shared__ float g_gate[kMC];   // gate (down)
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lds), 16, voff, soff, 0, 0);
+}
+
+// One work item.  NMF = number of 32-row M fragments the chunk needs (1..4).
 template <bool kGateUp, int NMF>
 __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L, const PfArgs &pa,
-                                                               const Item &it, uint8_t *lds) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int q = lane >> 4, n16 = lane & 15;
-  const int *rowidx_s = reinterpret_cast<const int *>(lds + kLdsRowIdx);
+                                                               const Item &it) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
+  const int h = lane >> 5, n = lane & 31;
   const int G = int(kGateUp ? L.lay.GH : L.lay.GI);
   const int nss = (G + 3) >> 2;
   const uint32_t rowB = uint32_t(G) * 32u;
@@ -285,7 +307,9 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(pa.A, pa.a_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(pa.S, pa.s_bytes);
 
-  // weight rows of this wave (all valid or all past the matrix: 64 | rows)
+  // weight rows of this wave (all valid or all past the matrix: 64 | rows);
+  // fragment jn = gate (0) / up (1) rows wrow0 .. +31 for gate/up, rows
+  // wrow0 + 32 jn .. +31 for down
   int wrow0;
   bool wvalid;
   if (kGateUp) {
@@ -295,310 +319,366 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
     wrow0 = it.ntile * 256 + 64 * wave;
     wvalid = wrow0 < L.H;
   }
-  uint32_t xoff[4], soff[4];
+  uint32_t xoff[2], soff[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int jn = 0; jn < 2; ++jn) {
     int row;
     uint32_t qsec, ssec;
     if (kGateUp) {
-      row = wrow0 + 16 * (j & 1);
-      qsec = uint32_t(j < 2 ? L.lay.gq : L.lay.uq);
-      ssec = uint32_t(j < 2 ? L.lay.gs : L.lay.us);
+      row = wrow0;
+      qsec = uint32_t(jn == 0 ? L.lay.gq : L.lay.uq);
+      ssec = uint32_t(jn == 0 ? L.lay.gs : L.lay.us);
     } else {
-      row = wrow0 + 16 * j;
+      row = wrow0 + 32 * jn;
       qsec = uint32_t(L.lay.dq);
       ssec = uint32_t(L.lay.ds);
     }
-    // load lane (a, b) = (q, n16): row b % 8 (+8 for the second load), part 2a + b/8.
-    // In the last super-step lanes past G read the next bytes of the blob (a q
-    // section is always followed by another section); their scale is 0.
-    xoff[j] = qsec + uint32_t(row + (n16 & 7)) * rowB + 16u * uint32_t(2 * q + (n16 >> 3));
-    soff[j] = ssec + uint32_t(row + n16) * uint32_t(G) * 4u + 16u * uint32_t(q);
+    // load a (0..3) of lane (h, n): row 8a + n%8, part 4h + n/8.  In the last
+    // super-step lanes past G read the next bytes of the blob (a q section is
+    // always followed by another section); their scale is 0.
+    xoff[jn] = qsec + uint32_t(row + (n & 7)) * rowB + 16u * uint32_t(4 * h + (n >> 3));
+    // scales of lane (h, n): row n, groups 16i + 8h ..
+    soff[jn] = ssec + uint32_t(row + n) * uint32_t(G) * 4u + 32u * uint32_t(h);
   }
 
-  // activation staging: run c16 of rows mrow + 16p; correction run c4 of rows crow + 64p
-  const int c16 = threadIdx.x & 15, mrow = threadIdx.x >> 4;
-  const int c4 = threadIdx.x & 3, crow = threadIdx.x >> 2;
-  uint32_t aoff[8], coff[2];
+  // DMA roles: instruction i of this wave fills staged rows 32w + 2i, 32w + 2i + 1
+  // (lane: row + lane/32, LDS chunk lane%32); correction instruction i fills
+  // rows 32w + 16i .. +15 (lane: row + lane/4, LDS chunk lane%4)
+  uint32_t aoff[16], coff[2];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int ri = rowidx_s[mrow + 16 * p];
-    aoff[p] = ri >= 0 ? (uint32_t(ri) * uint32_t(pa.AP) + 8u * uint32_t(c16)) * 2u : kOff;
+  for (int i = 0; i < 16; ++i) {
+    const int r = 32 * wave + 2 * i + (lane >> 5);
+    const int ri = g_rowidx[r];
+    const uint32_t chunk = uint32_t((lane & 31) ^ (r & 15));
+    aoff[i] = ri >= 0 ? uint32_t(ri) * uint32_t(pa.AP) * 2u + 16u * chunk : kOff;
   }
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int ri = rowidx_s[crow + 64 * p];
-    coff[p] = ri >= 0 ? (uint32_t(ri) * uint32_t(pa.CS) + 8u * uint32_t(c4)) * 2u : kOff;
+  for (int i = 0; i < 2; ++i) {
+    const int r = 32 * wave + 16 * i + (lane >> 2);
+    const int ri = g_rowidx[r];
+    const uint32_t chunk = uint32_t((lane & 3) ^ ((r >> 2) & 3));
+    coff[i] = ri >= 0 ? uint32_t(ri) * uint32_t(pa.CS) * 2u + 16u * chunk : kOff;
   }
-
-  auto load_a = [&](int ss, int hh, uint4(&v)[8]) {
+  auto dma_a = [&](int ss, uint8_t *st) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) v[p] = bload16(ra, aoff[p], uint32_t(512 * ss + 256 * hh));
+    for (int i = 0; i < 16; ++i)
+      dma16(ra, st + (32 * wave + 2 * i) * kRowB, aoff[i], uint32_t(512 * ss));
   };
-  auto store_a = [&](int buf, int hh, const uint4(&v)[8]) {
-    uint8_t *base = lds + buf * kStage + 256 * hh + 16 * c16;
+  // correction operand of block i: entries 32i .. 32i + 31 (groups 16i .. 16i + 15,
+  // hi and lo); entries past the groups are zeros in memory
+  auto dma_c = [&](int i, uint8_t *sc) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) *reinterpret_cast<uint4 *>(base + (mrow + 16 * p) * kPitch) = v[p];
+    for (int k = 0; k < 2; ++k) dma16(rs, sc + (32 * wave + 16 * k) * 64, coff[k], uint32_t(64 * i));
   };
-  // correction operand of block i: entries 32i + 8 c4 .. +7 = groups 16i + 4 c4 + d (hi, lo)
-  auto load_c = [&](int i, uint4(&v)[2]) {
-    const int g0 = 16 * i + 4 * c4;
+  auto load_b = [&](int ss, uint4(&R)[2][4]) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      uint4 w = bload16(rs, coff[p], uint32_t(64 * i));
-      if (g0 + 0 >= G) w.x = 0u;
-      if (g0 + 1 >= G) w.y = 0u;
-      if (g0 + 2 >= G) w.z = 0u;
-      if (g0 + 3 >= G) w.w = 0u;
-      v[p] = w;
-    }
+    for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        R[jn][a4] = bload16(rw, xoff[jn], 128u * uint32_t(ss) + 8u * uint32_t(a4) * rowB);
   };
-  auto store_c = [&](int buf, const uint4(&v)[2]) {
+  // scales of groups 16i + 8h + c (c = 0..7) of the lane's row; 0 past G
+  auto load_f = [&](int i, float (&F)[2][8]) {
+    const int g0 = 16 * i + 8 * h;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      *reinterpret_cast<uint4 *>(lds + buf * kStage + (crow + 64 * p) * kPitch + kCorrOff +
-                                 16 * c4) = v[p];
-  };
-  auto load_b = [&](int ss, uint4(&x)[4], uint4(&y)[4]) {
+    for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[j] = bload16(rw, xoff[j], 128u * uint32_t(ss));
-      y[j] = bload16(rw, xoff[j], 128u * uint32_t(ss) + 8u * rowB);
-    }
-  };
-  // scales of groups 16i + 4q + c (c = 0..3) of the lane's row; 0 past G
-  auto load_f = [&](int i, f32x4(&f)[4]) {
-    const int g0 = 16 * i + 4 * q;
+      for (int f4 = 0; f4 < 2; ++f4) {
+        const int gq = g0 + 4 * f4;
+        const uint32_t o = soff[jn] + 64u * uint32_t(i) + 16u * uint32_t(f4);
+        if ((G & 3) == 0) {
+          const uint4 w = bload16(rw, gq < G ? o : kOff, 0);
+          F[jn][4 * f4 + 0] = __uint_as_float(w.x);
+          F[jn][4 * f4 + 1] = __uint_as_float(w.y);
+          F[jn][4 * f4 + 2] = __uint_as_float(w.z);
+          F[jn][4 * f4 + 3] = __uint_as_float(w.w);
+        } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t o = soff[j] + 64u * uint32_t(i);
-      f32x4 v;
-      if ((G & 3) == 0) {
-        const uint4 w = bload16(rw, g0 < G ? o : kOff, 0);
-        v = f32x4{__builtin_bit_cast(float, w.x), __builtin_bit_cast(float, w.y),
-                  __builtin_bit_cast(float, w.z), __builtin_bit_cast(float, w.w)};
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = bload4f(rw, g0 + c < G ? o + 4u * c : kOff);
+          for (int c = 0; c < 4; ++c)
+            F[jn][4 * f4 + c] = bload4f(rw, gq + c < G ? o + 4u * c : kOff);
+        }
       }
-      f[j] = v;
-    }
   };
 
-  f32x4 acc[NMF][4];
+  f32x16 acc[NMF][2];
 #pragma unroll
   for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[mf][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jn = 0; jn < 2; ++jn) acc[mf][jn] = f32x16{};
 
-  // prologue: scales of block 0, weights and staged activations of super-step 0
-  // (zero-initialised: waves past the matrix never load them)
-  f32x4 F[4] = {};
-  uint4 bxr[4] = {}, byr[4] = {};
+  // prologue: stage 0 (activations, correction block 0), scales of block 0, weights of
+  // super-step 0
+  float F[2][8] = {};
+  uint4 R[2][4] = {};
+  dma_a(0, g_st0);
+  dma_c(0, g_sc0);
   if (wvalid) {
     load_f(0, F);
-    load_b(0, bxr, byr);
+    load_b(0, R);
   }
-  {
-    uint4 v[8], cv[2];
-    load_a(0, 0, v);
-    load_c(0, cv);
-    store_a(0, 0, v);
-    store_c(0, cv);
-    load_a(0, 1, v);
-    store_a(0, 1, v);
-  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();
 
-  float Ft[4][4] = {};
-  for (int ss = 0; ss < nss; ++ss) {
-    const int buf = ss & 1;
+  uint32_t m1, m2;
+  asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m1));
+  asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(m2));
+  // per-lane parts of the swizzled addresses: A row n (+32 mf), correction row n
+  const uint32_t abase = uint32_t(n * kRowB + 256 * h);
+  const uint32_t aswz = uint32_t(n & 15);
+  const uint32_t cbase = uint32_t(n * 64);
+  const uint32_t cswz = uint32_t((n >> 2) & 3);
+
+  // U[jn][0..7]: the block's scales in super-step order (pairs e = 0, 1 of
+  // super-step c at 2c, 2c + 1), rotated by two per super-step
+  float U[2][8] = {};
+  // one super-step: compute from (st, sc) while the DMA fills (stn, scn)
+  auto super_step = [&](int ss, const uint8_t *st, const uint8_t *sc, uint8_t *stn, uint8_t *scn) {
     const bool more = ss + 1 < nss;
-    const uint8_t *stage = lds + buf * kStage;
-    uint4 av[8];
-    if (more) load_a(ss + 1, 0, av);
+    if (more && ((ss + 1) & 3) == 0) dma_c((ss + 1) >> 2, scn);
     if (wvalid) {
-      // this super-step's weights into MFMA lane order; refill the raw slot
-      uint4 bx[4], by[4];
+      // this super-step's weights into MFMA lane order: register d of lane (h, n)
+      // = part 4h + d of row n (exchange of the load index with lane bits 3, 4)
+      uint4 D[2][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t xs[4] = {bxr[j].x, bxr[j].y, bxr[j].z, bxr[j].w};
-        const uint32_t ys[4] = {byr[j].x, byr[j].y, byr[j].z, byr[j].w};
-        uint32_t xo[4], yo[4];
+      for (int jn = 0; jn < 2; ++jn) {
+        uint4 Q[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          // lanes 8..15 of each row take the other load's lanes 0..7, and back
-          xo[d] = uint32_t(__builtin_amdgcn_update_dpp(int(xs[d]), int(ys[d]), 0x118, 0xF, 0xC, false));
-          yo[d] = uint32_t(__builtin_amdgcn_update_dpp(int(ys[d]), int(xs[d]), 0x108, 0xF, 0x3, false));
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t xs[4] = {R[jn][2 * e].x, R[jn][2 * e].y, R[jn][2 * e].z, R[jn][2 * e].w};
+          const uint32_t ys[4] = {R[jn][2 * e + 1].x, R[jn][2 * e + 1].y, R[jn][2 * e + 1].z,
+                                  R[jn][2 * e + 1].w};
+          uint32_t xo[4], yo[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            // lanes 8..15 of each 16-lane row take the other register's lanes 0..7, and back
+            xo[d] = uint32_t(__builtin_amdgcn_update_dpp(int(xs[d]), int(ys[d]), 0x118, 0xF, 0xC, false));
+            yo[d] = uint32_t(__builtin_amdgcn_update_dpp(int(ys[d]), int(xs[d]), 0x108, 0xF, 0x3, false));
+          }
+          Q[2 * e] = uint4{xo[0], xo[1], xo[2], xo[3]};
+          Q[2 * e + 1] = uint4{yo[0], yo[1], yo[2], yo[3]};
         }
-        bx[j] = uint4{xo[0], xo[1], xo[2], xo[3]};
-        by[j] = uint4{yo[0], yo[1], yo[2], yo[3]};
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const uint32_t qa[4] = {Q[x].x, Q[x].y, Q[x].z, Q[x].w};
+          const uint32_t qb[4] = {Q[2 + x].x, Q[2 + x].y, Q[2 + x].z, Q[2 + x].w};
+          uint32_t da[4], db[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            // odd 16-lane rows of the first register <-> even rows of the second
+            const auto sw = __builtin_amdgcn_permlane16_swap(qa[d], qb[d], false, false);
+            da[d] = uint32_t(sw[0]);
+            db[d] = uint32_t(sw[1]);
+          }
+          D[jn][x] = uint4{da[0], da[1], da[2], da[3]};
+          D[jn][2 + x] = uint4{db[0], db[1], db[2], db[3]};
+        }
       }
-      if (more) load_b(ss + 1, bxr, byr);
+      if (more) load_b(ss + 1, R);
       if ((ss & 3) == 0) {
-        // correction GEMM of block i = ss / 4: acc += S (hi, lo) x (-8 s, -8 s)
-        f16x8 bc[4];
+        // correction GEMM of block i = ss / 4: acc += S (hi, lo) x (-8 s, -8 s);
+        // k-step kc, k-half h covers groups 16i + 8h + 4kc .. +3
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const _Float16 h0 = _Float16(F[j][0]) * _Float16(-8.0f);
-          const _Float16 h1 = _Float16(F[j][1]) * _Float16(-8.0f);
-          const _Float16 h2 = _Float16(F[j][2]) * _Float16(-8.0f);
-          const _Float16 h3 = _Float16(F[j][3]) * _Float16(-8.0f);
-          bc[j] = f16x8{h0, h0, h1, h1, h2, h2, h3, h3};
+        for (int kc = 0; kc < 2; ++kc) {
+          f16x8 bc[2];
+#pragma unroll
+          for (int jn = 0; jn < 2; ++jn) {
+            const _Float16 h0 = _Float16(F[jn][4 * kc + 0]) * _Float16(-8.0f);
+            const _Float16 h1 = _Float16(F[jn][4 * kc + 1]) * _Float16(-8.0f);
+            const _Float16 h2 = _Float16(F[jn][4 * kc + 2]) * _Float16(-8.0f);
+            const _Float16 h3 = _Float16(F[jn][4 * kc + 3]) * _Float16(-8.0f);
+            bc[jn] = f16x8{h0, h0, h1, h1, h2, h2, h3, h3};
+          }
+#pragma unroll
+          for (int mf = 0; mf < NMF; ++mf) {
+            const f16x8 a = *reinterpret_cast<const f16x8 *>(
+                sc + cbase + mf * 32 * 64 + 16 * ((uint32_t(2 * h + kc)) ^ cswz));
+#pragma unroll
+            for (int jn = 0; jn < 2; ++jn)
+              acc[mf][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bc[jn], acc[mf][jn], 0, 0, 0);
+          }
         }
+        // regroup between lane halves: lane h then holds groups 4c + 2h, 4c + 2h + 1
 #pragma unroll
-        for (int mf = 0; mf < NMF; ++mf) {
-          const f16x8 a = *reinterpret_cast<const f16x8 *>(stage + (mf * 16 + n16) * kPitch +
-                                                           kCorrOff + 16 * q);
+        for (int jn = 0; jn < 2; ++jn) {
+          float T[8];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bc[j], acc[mf][j], 0, 0, 0);
-        }
-        // 4x4 transpose over the lane rows: Ft[j][c] = scale of group 16i + 4c + q
+          for (int c = 0; c < 8; ++c) T[c] = F[jn][c];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // elements read by value first: this compiler's SROA folds a bit_cast
-          // of an ext_vector element lvalue to element 0
-          const uint32_t r0 = __float_as_uint(float(F[j][0]));
-          const uint32_t r1 = __float_as_uint(float(F[j][1]));
-          const uint32_t r2 = __float_as_uint(float(F[j][2]));
-          const uint32_t r3 = __float_as_uint(float(F[j][3]));
-          const auto p02 = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
-          const auto p13 = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
-          const auto p01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
-          const auto p23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
-          Ft[j][0] = __builtin_bit_cast(float, uint32_t(p01[0]));
-          Ft[j][1] = __builtin_bit_cast(float, uint32_t(p01[1]));
-          Ft[j][2] = __builtin_bit_cast(float, uint32_t(p23[0]));
-          Ft[j][3] = __builtin_bit_cast(float, uint32_t(p23[1]));
+          for (int c = 0; c < 2; ++c) {
+            const auto p0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(T[c]), __float_as_uint(T[2 + c]), false, false);
+            const auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(T[4 + c]), __float_as_uint(T[6 + c]), false, false);
+            T[c] = __uint_as_float(uint32_t(p0[0]));
+            T[2 + c] = __uint_as_float(uint32_t(p0[1]));
+            T[4 + c] = __uint_as_float(uint32_t(p1[0]));
+            T[6 + c] = __uint_as_float(uint32_t(p1[1]));
+          }
+          // super-step order: c = 0: T0 T1, c = 1: T4 T5, c = 2: T2 T3, c = 3: T6 T7
+          U[jn][0] = T[0]; U[jn][1] = T[1]; U[jn][2] = T[4]; U[jn][3] = T[5];
+          U[jn][4] = T[2]; U[jn][5] = T[3]; U[jn][6] = T[6]; U[jn][7] = T[7];
         }
         if (ss + 4 < nss) load_f((ss >> 2) + 1, F);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          Ft[j][0] = Ft[j][1];
-          Ft[j][1] = Ft[j][2];
-          Ft[j][2] = Ft[j][3];
-        }
-      }
-      f16x2 s2[4], c10[4], c6[4];
+        for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const _Float16 h = _Float16(Ft[j][0]);
-        s2[j] = f16x2{h, h};
-        c10[j] = s2[j] * f16x2{_Float16(-1024.0f), _Float16(-1024.0f)};
-        c6[j] = s2[j] * f16x2{_Float16(-64.0f), _Float16(-64.0f)};
+          for (int c = 0; c < 6; ++c) U[jn][c] = U[jn][c + 2];
       }
-      // 8 MFMA steps k = 4t + s; the weights of step k + 1 are dequantised and
-      // its A fragments read while the MFMAs of step k run
-      uint32_t m1, m2;
-      asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m1));
-      asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(m2));
-      const uint8_t *abase = stage + n16 * kPitch + 64 * q;
-      f16x8 a[NMF], b[4];
+      // dequant constants per fragment and group half e of the super-step
+      f16x2 s2[2][2], c10[2][2], c6[2][2];
+#pragma unroll
+      for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const _Float16 hs = _Float16(U[jn][e]);
+          s2[jn][e] = f16x2{hs, hs};
+          c10[jn][e] = s2[jn][e] * f16x2{_Float16(-1024.0f), _Float16(-1024.0f)};
+          c6[jn][e] = s2[jn][e] * f16x2{_Float16(-64.0f), _Float16(-64.0f)};
+        }
+      // 16 MFMA k-steps; the weights of step k + 1 are dequantised and its A
+      // fragments read while the MFMAs of step k run (pinned with scheduling
+      // group barriers: left alone, the scheduler sinks each A read next to its
+      // first use and the LDS latency stalls every MFMA group).  The next
+      // stage's activations go out by DMA one instruction per step: issued in one
+      // burst after the barrier they would stall every wave on the address unit.
+      f16x8 a[NMF], b[2];
 #pragma unroll
       for (int mf = 0; mf < NMF; ++mf)
-        a[mf] = *reinterpret_cast<const f16x8 *>(abase + mf * 16 * kPitch);
+        a[mf] = *reinterpret_cast<const f16x8 *>(st + abase + mf * 32 * kRowB + 16 * (0 ^ aswz));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = dequant(bx[j].x, m1, m2, s2[j], c10[j], c6[j]);
+      for (int jn = 0; jn < 2; ++jn) b[jn] = dequant(D[jn][0].x, m1, m2, s2[jn][0], c10[jn][0], c6[jn][0]);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int t1 = (k + 1) >> 2, s1 = (k + 1) & 3;
-        f16x8 bn[4];
-        if (k < 7) {
+      for (int k = 0; k < 16; ++k) {
+        const int k1 = k + 1;
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 an[NMF], bn[2];
+        if (k < 15) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            bn[j] = dequant(word_of(t1 ? by[j] : bx[j], s1), m1, m2, s2[j], c10[j], c6[j]);
+          for (int mf = 0; mf < NMF; ++mf)
+            an[mf] = *reinterpret_cast<const f16x8 *>(st + abase + mf * 32 * kRowB +
+                                                      16 * (uint32_t(k1) ^ aswz));
+#pragma unroll
+          for (int jn = 0; jn < 2; ++jn)
+            bn[jn] = dequant(word_of(D[jn][k1 >> 2], k1 & 3), m1, m2, s2[jn][k1 >> 3],
+                             c10[jn][k1 >> 3], c6[jn][k1 >> 3]);
         }
 #pragma unroll
-        for (int mf = 0; mf < NMF; ++mf) {
+        for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mf], b[j], acc[mf][j], 0, 0, 0);
-          // refill the fragment for step k + 1 as soon as step k is done with it
-          if (k < 7)
-            a[mf] = *reinterpret_cast<const f16x8 *>(abase + mf * 16 * kPitch + 256 * t1 + 16 * s1);
-        }
-        if (k == 3 && more) {
-          store_a(buf ^ 1, 0, av);
-          load_a(ss + 1, 1, av);
-        }
-        if (k < 7) {
+          for (int jn = 0; jn < 2; ++jn)
+            acc[mf][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mf], b[jn], acc[mf][jn], 0, 0, 0);
+        // (no branch: a branch here would split the step's scheduling region; in
+        // the last super-step the instruction reads out of range and writes zeros
+        // into the unused stage, landed before the epilogue by the closing wait)
+        dma16(ra, stn + (32 * wave + 2 * k) * kRowB, more ? aoff[k] : kOff, uint32_t(512 * (ss + 1)));
+        if (k < 15) {
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM (DMA)
+          __builtin_amdgcn_sched_group_barrier(0x100, NMF, 0);  // DS reads
 #pragma unroll
-          for (int j = 0; j < 4; ++j) b[j] = bn[j];
+          for (int i = 0; i < 2 * NMF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 20 / (2 * NMF) + 1, 0);  // VALU
+          }
+#pragma unroll
+          for (int mf = 0; mf < NMF; ++mf) a[mf] = an[mf];
+#pragma unroll
+          for (int jn = 0; jn < 2; ++jn) b[jn] = bn[jn];
         }
       }
-      if (more) {
-        store_a(buf ^ 1, 1, av);
-        if (((ss + 1) & 3) == 0) {
-          uint4 cv[2];
-          load_c((ss + 1) >> 2, cv);
-          store_c(buf ^ 1, cv);
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
     } else if (more) {
       // rows past the matrix: staging only
-      store_a(buf ^ 1, 0, av);
-      load_a(ss + 1, 1, av);
-      store_a(buf ^ 1, 1, av);
-      if (((ss + 1) & 3) == 0) {
-        uint4 cv[2];
-        load_c((ss + 1) >> 2, cv);
-        store_c(buf ^ 1, cv);
-      }
+      dma_a(ss + 1, stn);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next stage's DMA and weights landed
     __syncthreads();
+  };
+  for (int ss = 0; ss < nss; ss += 2) {
+    super_step(ss, g_st0, g_sc0, g_st1, g_sc1);
+    if (ss + 1 < nss) super_step(ss + 1, g_st1, g_sc1, g_st0, g_sc0);
   }
 
-  // epilogue: lane holds rows m = 16 mf + 4 q + i of column n16 of each fragment
-  const int *outrow_s = reinterpret_cast<const int *>(lds + kLdsOutRow);
+  // epilogue through an LDS tile (the stages are free: the last super-step ended
+  // with a barrier), then 16-byte stores.  tid is made opaque so that the
+  // item-invariant addresses below are not hoisted to the kernel start (where
+  // they would be spilled and reloaded from scratch, once per stored row).
+  // acc[mf][jn][4j + i] is row 32 mf + 8j + 4h + i, column n of fragment jn.
+  uint8_t *tile = g_st0;
+  int tid = int(threadIdx.x);
+  asm volatile("" : "+v"(tid));
+  const int eh = (tid & 63) >> 5, en = tid & 31;
   if (kGateUp) {
-    float *red_s = reinterpret_cast<float *>(lds + kLdsRed);
+    // tile row m: the N-tile's 128 features of h in staged order (2 groups, 256 B)
+    if (wvalid) {
+      const int fl = 32 * wave + en;  // feature within the N-tile
+      const int tpos = 2 * (64 * (fl >> 6) + grp_pos(fl & 63));
 #pragma unroll
-    for (int mf = 0; mf < NMF; ++mf) {
+      for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mf * 16 + 4 * q + i;
-        float part = 0.0f;
-        if (wvalid && m < nrows) {
-          const int64_t hrow = outrow_s[m];
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int f = wrow0 + 16 * jj + n16;
-            const _Float16 hv = _Float16(silu(acc[mf][jj][i]) * acc[mf][jj + 2][i]);
-            pa.out[hrow * pa.OP + act_pos(f >> 6, f & 63)] = __builtin_bit_cast(uint16_t, hv);
-            part += float(hv);
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int m = 32 * mf + 8 * (v >> 2) + 4 * eh + (v & 3);
+          const _Float16 hv = _Float16(silu(acc[mf][0][v]) * acc[mf][1][v]);
+          *reinterpret_cast<_Float16 *>(tile + m * 256 + tpos) = hv;
         }
-        part = row16_sum(part);
-        if (n16 == 15) red_s[wave * kMC + m] = part;
-      }
     }
     __syncthreads();
-    // group sums of h: waves 2g' and 2g'+1 hold the halves of group 2 ntile + g'
-    const int m = threadIdx.x & (kMC - 1), gsel = threadIdx.x >> 7;
-    const int g = it.ntile * 2 + gsel;
-    if (m < nrows && m < NMF * 16 && 64 * g < L.I) {
-      const float sum = red_s[(2 * gsel) * kMC + m] + red_s[(2 * gsel + 1) * kMC + m];
-      *reinterpret_cast<uint32_t *>(pa.sout + int64_t(outrow_s[m]) * pa.SOP + 2 * g) =
-          split_f16(sum);
+    const int g0 = it.ntile * 2;
+    {
+      const int c = tid & 15;
+      if (64 * (g0 + (c >> 3)) < L.I) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int m = (tid >> 4) + 16 * p;
+          if (m < nrows) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile + m * 256 + 16 * c);
+            *reinterpret_cast<uint4 *>(pa.out + int64_t(g_outrow[m]) * pa.OP + 64 * g0 + 8 * c) = v;
+          }
+        }
+      }
+    }
+    // group sums of h: thread (m, gsel) adds the 64 fp16 values of its group
+    {
+      const int m = tid & (kMC - 1), gsel = tid >> 7;
+      if (m < nrows && 64 * (g0 + gsel) < L.I) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(tile + m * 256 + gsel * 128 + 16 * c);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const f16x2 hv = __builtin_bit_cast(f16x2, w[d]);
+            sum += float(hv[0]) + float(hv[1]);
+          }
+        }
+        *reinterpret_cast<uint32_t *>(pa.sout + int64_t(g_outrow[m]) * pa.SOP + 2 * (g0 + gsel)) =
+            split_f16(sum);
+      }
     }
   } else {
-    const float *gate_s = reinterpret_cast<const float *>(lds + kLdsGate);
+    // tile row m: the N-tile's 256 gate-scaled outputs
     if (wvalid) {
 #pragma unroll
-      for (int mf = 0; mf < NMF; ++mf) {
+      for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mf * 16 + 4 * q + i;
-          if (m >= nrows) continue;
-          const int64_t srow = outrow_s[m];
-          const float gate = gate_s[m];
+        for (int v = 0; v < 16; ++v) {
+          const int m = 32 * mf + 8 * (v >> 2) + 4 * eh + (v & 3);
+          const float gate = g_gate[m];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = wrow0 + 16 * j + n16;
-            pa.out[srow * pa.OP + n] = __builtin_bit_cast(uint16_t, _Float16(gate * acc[mf][j][i]));
-          }
+          for (int jn = 0; jn < 2; ++jn)
+            *reinterpret_cast<_Float16 *>(tile + m * 512 + 2 * (64 * wave + 32 * jn + en)) =
+                _Float16(gate * acc[mf][jn][v]);
+        }
+    }
+    __syncthreads();
+    const int c = tid & 31;
+    const int n0 = it.ntile * 256 + 8 * c;
+    if (n0 < L.H) {
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int m = (tid >> 5) + 8 * p;
+        if (m < nrows) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(tile + m * 512 + 16 * c);
+          *reinterpret_cast<uint4 *>(pa.out + int64_t(g_outrow[m]) * pa.OP + n0) = v;
         }
       }
     }
@@ -611,10 +691,6 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
 // so the N-tiles of one chunk, which share its activations, meet in one L2.
 template <bool kGateUp>
 __global__ __launch_bounds__(kThreads, 1) void pf_gemm(LayerDev L, Routing r, int T, PfArgs pa) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  int *rowidx_s = reinterpret_cast<int *>(lds + kLdsRowIdx);
-  int *outrow_s = reinterpret_cast<int *>(lds + kLdsOutRow);
-  float *gate_s = reinterpret_cast<float *>(lds + kLdsGate);
   const int K = L.K;
   const int n_nt = kGateUp ? (L.I + 127) / 128 : (L.H + 255) / 256;
   const int nu = *r.n_unique + 1;
@@ -665,21 +741,17 @@ __global__ __launch_bounds__(kThreads, 1) void pf_gemm(LayerDev L, Routing r, in
           }
         }
       }
-      rowidx_s[threadIdx.x] = ri;
-      outrow_s[threadIdx.x] = orow;
-      gate_s[threadIdx.x] = gate;
+      g_rowidx[threadIdx.x] = ri;
+      g_outrow[threadIdx.x] = orow;
+      g_gate[threadIdx.x] = gate;
     }
     __syncthreads();
-    const int nmf = (it.je - it.jb + 15) / 16;
+    const int nmf = (it.je - it.jb + 31) / 32;
     switch (nmf) {
-      case 1: run_item<kGateUp, 1>(L, pa, it, lds); break;
-      case 2: run_item<kGateUp, 2>(L, pa, it, lds); break;
-      case 3: run_item<kGateUp, 3>(L, pa, it, lds); break;
-      case 4: run_item<kGateUp, 4>(L, pa, it, lds); break;
-      case 5: run_item<kGateUp, 5>(L, pa, it, lds); break;
-      case 6: run_item<kGateUp, 6>(L, pa, it, lds); break;
-      case 7: run_item<kGateUp, 7>(L, pa, it, lds); break;
-      default: run_item<kGateUp, 8>(L, pa, it, lds); break;
+      case 1: run_item<kGateUp, 1>(L, pa, it); break;
+      case 2: run_item<kGateUp, 2>(L, pa, it); break;
+      case 3: run_item<kGateUp, 3>(L, pa, it); break;
+      default: run_item<kGateUp, 4>(L, pa, it); break;
     }
   }
 }
@@ -729,12 +801,9 @@ int cus_of_device() {
 template <bool kGateUp>
 hipError_t launch_gemm(const LayerDev &L, const Routing &r, int T, const PfArgs &pa,
                        int64_t max_items, hipStream_t s) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&pf_gemm<kGateUp>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (e != hipSuccess) return e;
   const int64_t cus = cus_of_device();
   const int64_t grid = max_items < cus ? max_items : cus;
-  pf_gemm<kGateUp><<<dim3(unsigned(grid)), dim3(kThreads), kLdsBytes, s>>>(L, r, T, pa);
+  pf_gemm<kGateUp><<<dim3(unsigned(grid)), dim3(kThreads), 0, s>>>(L, r, T, pa);
   return hipGetLastError();
 }
 
@@ -763,9 +832,10 @@ hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T, const
     const int64_t n = int64_t(T) * (pl.HP / 64) * 8;
     pf_prep<<<dim3(unsigned((n + 255) / 256)), 256, 0, s>>>(x, T, L.H, pl.HP, pl.CSX, b.xp, b.sx);
   }
-  if (L.I % 256) {
-    const int64_t n = (TK + T) * ((pl.IP - L.I) / 64) * 8;
-    pf_hpad<<<dim3(unsigned((n + 255) / 256)), 256, 0, s>>>(b.h, TK + T, L.I / 64, pl.IP);
+  if (pl.IP > L.I || pl.CSI > 2 * (L.I / 64)) {
+    const int64_t rows = TK + T;
+    pf_pads<<<dim3(unsigned((rows + 255) / 256)), 256, 0, s>>>(b.h, b.sh, rows, L.I / 64, pl.IP,
+                                                               pl.CSI);
   }
   prefill_tiles<<<1, 1024, 0, s>>>(r, T);
   if (ev) (void)hipEventRecord(ev[1], s);
