@@ -306,6 +306,8 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(it.blob, uint32_t(L.lay.bytes));
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(pa.A, pa.a_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(pa.S, pa.s_bytes);
+  // empty resource: every access reads zeros (loads of the last super-step)
+  const __amdgpu_buffer_rsrc_t rnull = make_rsrc(pa.A, 0);
 
   // weight rows of this wave (all valid or all past the matrix: 64 | rows);
   // fragment jn = gate (0) / up (1) rows wrow0 .. +31 for gate/up, rows
@@ -473,7 +475,9 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
           D[jn][2 + x] = uint4{db[0], db[1], db[2], db[3]};
         }
       }
-      if (more) load_b(ss + 1, R);
+      // the next super-step's weights go out one load per step in steps 0..7
+      // (issued in one burst the four waves queue on the address unit)
+      const __amdgpu_buffer_rsrc_t rwn = more ? rw : rnull;
       if ((ss & 3) == 0) {
         // correction GEMM of block i = ss / 4: acc += S (hi, lo) x (-8 s, -8 s);
         // k-step kc, k-half h covers groups 16i + 8h + 4kc .. +3
@@ -570,8 +574,11 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
         // the last super-step the instruction reads out of range and writes zeros
         // into the unused stage, landed before the epilogue by the closing wait)
         dma16(ra, stn + (32 * wave + 2 * k) * kRowB, more ? aoff[k] : kOff, uint32_t(512 * (ss + 1)));
+        if (k < 8)
+          R[k >> 2][k & 3] = bload16(rwn, xoff[k >> 2], 128u * uint32_t(ss + 1) + 8u * uint32_t(k & 3) * rowB);
         if (k < 15) {
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM (DMA)
+          if (k < 8) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM (DMA, weights)
+          else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, NMF, 0);  // DS reads
 #pragma unroll
           for (int i = 0; i < 2 * NMF; ++i) {

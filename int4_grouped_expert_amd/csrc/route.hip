@@ -170,11 +170,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 }
 
 // ---------------------------------------------------------------- logits (one token)
-// grid: E blocks of 256 threads; block e computes the logits of expert e for
-// every token (T <= 4): its 4 waves split H (16-byte loads, up to kNB per lane
-// issued before use, fp32 FMA), partial sums meet in a fixed order.  The same
-// launch writes x as digit planes (see ffn_narrow.hip): every block knows the
-// token's max |x| from its own loads; group g is digitised by block g % E,
+// grid: E + H/64 blocks of 256 threads.  Block e < E computes the logits of
+// expert e for every token (T <= 4): its 4 waves split H (16-byte loads, up to
+// kNB per lane issued before use, fp32 FMA), partial sums meet in a fixed
+// order.  Block E + g writes group g of x as digit planes (see ffn_narrow.hip),
+// in parallel with the logit blocks: it finds the token's max |x| itself,
 // token t by wave t (lanes 0..15, four elements each).
 constexpr int kNB = 8;
 
@@ -199,11 +199,54 @@ __global__ __launch_bounds__(256) void router_narrow_kernel(
   __shared__ float sdot[4][4], smax[4][4];
   __shared__ int sbad[4][4];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (int(blockIdx.x) >= E) {
+    // blocks E .. E + H/64 - 1: the x digit planes of group blockIdx.x - E, in
+    // parallel with the logit blocks (each finds the token maxima itself)
+    const int g = int(blockIdx.x) - E;
+    for (int t = 0; t < T; ++t) {
+      float m = 0.0f;
+      int bd = 0;
+      for (int c = 4 * int(threadIdx.x); c < H; c += 4 * int(blockDim.x)) {
+        const float4 xv = *reinterpret_cast<const float4 *>(x + size_t(t) * H + c);
+        m = fmaxf(fmaxf(m, fmaxf(fabsf(xv.x), fabsf(xv.y))), fmaxf(fabsf(xv.z), fabsf(xv.w)));
+        bd |= !__builtin_isfinite(xv.x) | !__builtin_isfinite(xv.y) | !__builtin_isfinite(xv.z) |
+              !__builtin_isfinite(xv.w);
+      }
+      m = wave_max(m);
+      bd = __any(bd);
+      if (lane == 0) {
+        smax[wave][t] = m;
+        sbad[wave][t] = bd;
+      }
+    }
+    __syncthreads();
+    if (wave < T && lane < 16) {
+      const int t = wave;
+      const float m = fmaxf(fmaxf(smax[0][t], smax[1][t]), fmaxf(smax[2][t], smax[3][t]));
+      const bool bd = sbad[0][t] | sbad[1][t] | sbad[2][t] | sbad[3][t];
+      const int ex = digit_exponent(m);
+      if (g == 0 && lane == 0) nb.xsc[t] = bd ? __builtin_nanf("") : ldexpf(1.0f, -ex);
+      const int GH = H / 64;
+      const int el = 4 * lane, pos = aorder_pos(el);
+      const float4 v = *reinterpret_cast<const float4 *>(x + size_t(t) * H + 64 * g + el);
+      const float va[4] = {v.x, v.y, v.z, v.w};
+      int d[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) digits4(va[i], ex, d[i]);
+      const size_t gbase = (size_t(t) * GH + g) * 4;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        *reinterpret_cast<uint32_t *>(nb.xdig + (gbase + p) * 64 + pos) = pack_plane(d, p);
+        const int sum = row16_sum_i(d[0][p] + d[1][p] + d[2][p] + d[3][p]);
+        if (lane == 0) nb.xcorr[gbase + p] = -8 * sum;
+      }
+    }
+    return;
+  }
   const int e = blockIdx.x;
   const int Hq = H / 4;
   const int cb = wave * Hq, ce = cb + Hq;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f}, mx[4] = {0.f, 0.f, 0.f, 0.f};
-  int bad[4] = {0, 0, 0, 0};
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = cb + 4 * lane; c0 < ce; c0 += 4 * kWave * kNB) {
     float wv[kNB][4];
 #pragma unroll
@@ -224,53 +267,20 @@ __global__ __launch_bounds__(256) void router_narrow_kernel(
         const float4 xv = *reinterpret_cast<const float4 *>(x + size_t(t) * H + c);
         const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          acc[t] = fmaf(wv[b][k], xa[k], acc[t]);
-          mx[t] = fmaxf(mx[t], fabsf(xa[k]));
-          bad[t] |= !__builtin_isfinite(xa[k]);
-        }
+        for (int k = 0; k < 4; ++k) acc[t] = fmaf(wv[b][k], xa[k], acc[t]);
       }
     }
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const float d = wave_sum(acc[t]);
-    const float m = wave_max(mx[t]);
-    const int bd = __any(bad[t]);
-    if (lane == 0) {
-      sdot[wave][t] = d;
-      smax[wave][t] = m;
-      sbad[wave][t] = bd;
-    }
+    if (lane == 0) sdot[wave][t] = d;
   }
   __syncthreads();
   if (int(threadIdx.x) < T) {
     const int t = threadIdx.x;
     logits[size_t(t) * E + e] =
         ((sdot[0][t] + sdot[1][t]) + (sdot[2][t] + sdot[3][t])) + (bias ? bias[e] : 0.0f);
-  }
-  if (wave < T && lane < 16) {
-    const int t = wave;
-    const float m = fmaxf(fmaxf(smax[0][t], smax[1][t]), fmaxf(smax[2][t], smax[3][t]));
-    const bool bd = sbad[0][t] | sbad[1][t] | sbad[2][t] | sbad[3][t];
-    const int ex = digit_exponent(m);
-    if (blockIdx.x == 0 && lane == 0) nb.xsc[t] = bd ? __builtin_nanf("") : ldexpf(1.0f, -ex);
-    const int GH = H / 64;
-    const int el = 4 * lane, pos = aorder_pos(el);
-    for (int g = blockIdx.x; g < GH; g += gridDim.x) {
-      const float4 v = *reinterpret_cast<const float4 *>(x + size_t(t) * H + 64 * g + el);
-      const float va[4] = {v.x, v.y, v.z, v.w};
-      int d[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) digits4(va[i], ex, d[i]);
-      const size_t gbase = (size_t(t) * GH + g) * 4;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        *reinterpret_cast<uint32_t *>(nb.xdig + (gbase + p) * 64 + pos) = pack_plane(d, p);
-        const int sum = row16_sum_i(d[0][p] + d[1][p] + d[2][p] + d[3][p]);
-        if (lane == 0) nb.xcorr[gbase + p] = -8 * sum;
-      }
-    }
   }
 }
 
@@ -579,10 +589,10 @@ hipError_t launch_router_narrow(const float *x, int T, int H, const void *wr, in
                                 const NarrowBufs &nb, hipStream_t s, hipEvent_t start,
                                 hipEvent_t stop) {
   if (w_bf16)
-    hipExtLaunchKernelGGL(router_narrow_kernel<true>, dim3(E), dim3(256), 0, s, start, stop, 0, x,
+    hipExtLaunchKernelGGL(router_narrow_kernel<true>, dim3(E + H / 64), dim3(256), 0, s, start, stop, 0, x,
                           T, H, wr, E, bias, logits, nb);
   else
-    hipExtLaunchKernelGGL(router_narrow_kernel<false>, dim3(E), dim3(256), 0, s, start, stop, 0,
+    hipExtLaunchKernelGGL(router_narrow_kernel<false>, dim3(E + H / 64), dim3(256), 0, s, start, stop, 0,
                           x, T, H, wr, E, bias, logits, nb);
   return hipGetLastError();
 }
