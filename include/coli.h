@@ -199,8 +199,12 @@ size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int T, coli_mode mode);
  *   per selected (token, expert): h = SiLU(Wg x) * (Wu x), o = Wd h, with
  *     W = s * (u - 8) read from the planar bytes;
  *   y[t] = sum_k gate[t,k] * o[t,k] + Wd_sh (SiLU(Wg_sh x) * (Wu_sh x)).
- *   mode DECODE:  x, y fp32 [T, H]; h is held in fp32; aimed at small T,
- *                 T <= 256.
+ *   mode DECODE:  x, y fp32 [T, H], T <= 256; fp32-class products on the
+ *                 matrix cores: weights as the exact integers u - 8 with the
+ *                 fp32 group scale applied per group, x and h split into
+ *                 fp16 hi + lo parts under a power-of-two scale per row
+ *                 (T = 1: int8 digit planes), h and the per-slot outputs
+ *                 held in fp32.
  *   mode PREFILL: x, y bf16 [T, H], T <= COLI_MAX_TOKENS; grouped GEMMs on
  *                 the matrix cores with fp32 accumulation.  The products take
  *                 fp16 operands: x converted from bf16 (exact for

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcoli.so")
 
-SOURCES = ["coli.cpp", "quant.hip", "route.hip", "ffn_decode.hip", "ffn_narrow.hip",
+SOURCES = ["coli.cpp", "quant.hip", "route.hip", "ffn_narrow.hip",
            "ffn_prefill.hip",
            "rmsnorm.hip"]
 

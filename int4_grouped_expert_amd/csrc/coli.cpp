@@ -32,8 +32,9 @@ bool layer_shape_ok(int H, int I, int E, int K) {
 struct WsLayout {
   size_t logits, idx, gates, counts, offsets, perm, unique, n_unique, chunk, h, slot;
   size_t xp, sx, sh;                          // prefill only
-  size_t xh, xl, xsc, hh, hl, hsc, slotmap;  // decode only
+  size_t slotmap;                             // decode only
   size_t xdig, xcorr, nxsc, hn;               // decode, single-token path
+  size_t bxp, bxs, bhf, bh16, bhs, bslot;     // decode batch path
   size_t total;
 };
 WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
@@ -52,8 +53,9 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
   if (chunk < size_t(E) + 2) chunk = size_t(E) + 2;
   w.chunk = o; o += align256(chunk * 4);
   w.xp = w.sx = w.sh = 0;
-  w.h = w.slot = w.xh = w.xl = w.xsc = w.hh = w.hl = w.hsc = w.slotmap = 0;
+  w.h = w.slot = w.slotmap = 0;
   w.xdig = w.xcorr = w.nxsc = w.hn = 0;
+  w.bxp = w.bxs = w.bhf = w.bh16 = w.bhs = w.bslot = 0;
   if (mode == COLI_PREFILL) {
     const PrefillLayout pl = prefill_layout(H, I);
     w.xp = o; o += align256(size_t(T) * pl.HP * 2);
@@ -63,18 +65,20 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
     w.slot = o; o += align256((TK + T) * size_t(H) * 2);
   } else {
     const size_t units = TK < size_t(E) ? TK : size_t(E);
-    w.xh = o; o += align256(size_t(T) * H * 2);
-    w.xl = o; o += align256(size_t(T) * H * 2);
-    w.xsc = o; o += align256(size_t(T) * 4);
-    w.hh = o; o += align256((TK + T) * size_t(I) * 2);
-    w.hl = o; o += align256((TK + T) * size_t(I) * 2);
-    w.hsc = o; o += align256((TK + T) * size_t(I / 32) * 4);
     w.slotmap = o; o += align256(units * size_t(T) * 4);
     const size_t GH = size_t(groups_of(H));
     w.xdig = o; o += align256(size_t(T) * GH * 256);
     w.xcorr = o; o += align256(size_t(T) * GH * 16);
     w.nxsc = o; o += align256(size_t(T) * 4);
     w.hn = o; o += align256((units + 1) * size_t(I) * 4);
+    const PrefillLayout pl = prefill_layout(H, I);
+    const size_t R = TK + T;
+    w.bxp = o; o += align256(2 * size_t(T) * pl.HP * 2);
+    w.bxs = o; o += align256(size_t(T) * 4);
+    w.bhf = o; o += align256(R * size_t(I) * 4);
+    w.bh16 = o; o += align256(2 * R * size_t(pl.IP) * 2);
+    w.bhs = o; o += align256(R * 4);
+    w.bslot = o; o += align256(R * size_t(H) * 4);
   }
   w.total = o;
   return w;
@@ -151,7 +155,7 @@ int coli_router_topk(const void *x, coli_dtype x_dtype, int T, int H, const void
   if (T == 0) return COLI_OK;
   hipStream_t s = as_stream(stream);
   hipError_t e = launch_router_logits(x, x_dtype == COLI_BF16, T, H, w_router,
-                                      w_dtype == COLI_BF16, E, bias, logits, nullptr, s);
+                                      w_dtype == COLI_BF16, E, bias, logits, s);
   if (e != hipSuccess) return COLI_EDEVICE;
   return dev_status(launch_topk(logits, T, E, K, topk_idx, topk_gate, s));
 }
@@ -254,14 +258,7 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
   hipError_t e;
   if (mode == COLI_PREFILL && ev) (void)hipEventRecord(ev[0], s);
   if (mode == COLI_DECODE) {
-    DecodeBufs b;
-    b.xh = reinterpret_cast<uint16_t *>(ws + w.xh);
-    b.xl = reinterpret_cast<uint16_t *>(ws + w.xl);
-    b.xsc = reinterpret_cast<float *>(ws + w.xsc);
-    b.hh = reinterpret_cast<uint16_t *>(ws + w.hh);
-    b.hl = reinterpret_cast<uint16_t *>(ws + w.hl);
-    b.hsc = reinterpret_cast<float *>(ws + w.hsc);
-    b.slotmap = reinterpret_cast<int32_t *>(ws + w.slotmap);
+    int32_t *slotmap = reinterpret_cast<int32_t *>(ws + w.slotmap);
     if (narrow_supported(d, T)) {
       NarrowBufs nb;
       nb.xdig = reinterpret_cast<int8_t *>(ws + w.xdig);
@@ -277,13 +274,20 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
                                           reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr));
     }
     if (ev) (void)hipEventRecord(ev[0], s);
-    e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, L->router_bias, r.logits,
-                             &b, s);
+    e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, L->router_bias, r.logits, s);
     if (e != hipSuccess) return COLI_EDEVICE;
-    e = launch_route_decode(r, T, L->E, L->K, b.slotmap, s);
+    e = launch_route_decode(r, T, L->E, L->K, slotmap, s);
     if (e != hipSuccess) return COLI_EDEVICE;
     if (ev) (void)hipEventRecord(ev[1], s);
-    e = launch_ffn_decode(d, b, T, r, reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr);
+    BatchBufs bb;
+    bb.xp = reinterpret_cast<uint16_t *>(ws + w.bxp);
+    bb.xs = reinterpret_cast<float *>(ws + w.bxs);
+    bb.hf = reinterpret_cast<float *>(ws + w.bhf);
+    bb.h16 = reinterpret_cast<uint16_t *>(ws + w.bh16);
+    bb.hs = reinterpret_cast<float *>(ws + w.bhs);
+    bb.slot = reinterpret_cast<float *>(ws + w.bslot);
+    e = launch_ffn_batch(d, reinterpret_cast<const float *>(x), T, r, bb,
+                         reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr);
     return dev_status(e);
   }
   if (wbf) {
@@ -293,8 +297,7 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
     if (e != hipSuccess) return COLI_EDEVICE;
     e = launch_topk_permute(r, T, L->E, L->K, 0, s);
   } else {
-    e = launch_router_logits(x, 1, T, L->H, L->w_router, 0, L->E, L->router_bias, r.logits,
-                             nullptr, s);
+    e = launch_router_logits(x, 1, T, L->H, L->w_router, 0, L->E, L->router_bias, r.logits, s);
     if (e != hipSuccess) return COLI_EDEVICE;
     e = launch_topk_permute(r, T, L->E, L->K, 1, s);
   }

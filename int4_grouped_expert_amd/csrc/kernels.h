@@ -54,18 +54,6 @@ struct Routing {
   int32_t *chunk;    // [n_chunks * E] per-chunk counts / bases (large T)
 };
 
-// Decode-path activation buffers (inside the workspace).  xh/xl: x [T, H] as
-// fp16 hi/lo pairs (perm8 order inside 8-element runs), value = (hi + lo) *
-// xsc[t]; hh/hl/hsc: h' [T*K + T, I] likewise with one scale per 32 columns;
-// slotmap [n_units_max, T]: h row of (unit u, token t), -1 if t is not routed
-// to u.
-struct DecodeBufs {
-  uint16_t *xh, *xl;
-  float *xsc;
-  uint16_t *hh, *hl;
-  float *hsc;
-  int32_t *slotmap;
-};
 
 // Single-token decode buffers (inside the workspace).  xdig: x as four int8
 // digit planes, [T][GH][4 planes][64] in "A order" (see ffn_narrow.hip), value
@@ -95,12 +83,10 @@ hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
                                  int32_t *status, hipStream_t s);
 
 // ---- route.hip ----------------------------------------------------------
-// logits[t, e] = x[t] . Wr[e] + b[e]; x fp32 (x_bf16 = 0) or bf16.  If xb is
-// non-NULL (fp32 x only) the same launch also writes the split copy of x.
+// logits[t, e] = x[t] . Wr[e] + b[e]; x fp32 (x_bf16 = 0) or bf16.
 hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
                                 const void *wr, int w_bf16, int E,
-                                const float *bias, float *logits,
-                                const DecodeBufs *xb, hipStream_t s);
+                                const float *bias, float *logits, hipStream_t s);
 // Prefill router: bf16 x and bf16 Wr through MFMA, top-K fused.
 hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
                                    const uint16_t *wr, int E,
@@ -127,12 +113,6 @@ hipError_t launch_router_narrow(const float *x, int T, int H, const void *wr, in
                                 int E, const float *bias, float *logits,
                                 const NarrowBufs &nb, hipStream_t s, hipEvent_t start = nullptr,
                                 hipEvent_t stop = nullptr);
-
-// ---- ffn_decode.hip -----------------------------------------------------
-// ev: optional stage events (NULL or 4: start and stop of gate/up, of down).
-hipError_t launch_ffn_decode(const LayerDev &L, const DecodeBufs &b, int T,
-                             const Routing &r, float *y, hipStream_t s,
-                             hipEvent_t *ev);
 
 // ---- ffn_narrow.hip -----------------------------------------------------
 // Whether the single-token int8 matrix-core path covers this layer and T.
@@ -161,6 +141,23 @@ struct PrefillBufs {
 // down, combine).
 hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T, const Routing &r,
                               const PrefillBufs &b, uint16_t *y, hipStream_t s, hipEvent_t *ev);
+
+// Decode batch (1 < T <= 256) on the same grouped-GEMM weight stream:
+// xp: x as staged fp16 hi/lo rows [2T][HP] (hi rows first), xs [T] row scales;
+// hf: h = SiLU(gate) * up fp32 [T*K + T][I]; h16 [2 (T*K + T)][IP], hs: its
+// staged hi/lo rows and scales; slot [T*K + T][H] fp32 gate-scaled outputs.
+struct BatchBufs {
+  uint16_t *xp;
+  float *xs;
+  float *hf;
+  uint16_t *h16;
+  float *hs;
+  float *slot;
+};
+// r: routing with 32-token M-chunk prefix (launch_route_decode).  ev: optional
+// (NULL or 4: start and stop of the gate/up step, of the down step).
+hipError_t launch_ffn_batch(const LayerDev &L, const float *x, int T, const Routing &r,
+                            const BatchBufs &b, float *y, hipStream_t s, hipEvent_t *ev);
 
 // ---- rmsnorm.hip --------------------------------------------------------
 hipError_t launch_rmsnorm_f32(const float *x, float *y, int T, int H,

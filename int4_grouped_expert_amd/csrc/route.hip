@@ -34,51 +34,6 @@ __device__ inline float bf16_to_f32(uint16_t b) {
   return __uint_as_float(uint32_t(b) << 16);
 }
 
-// Split an fp32 row into fp16 hi/lo with one power-of-two scale:
-// row = (hi + lo) * sc, max|row| / sc in [2^14, 2^15); hi and lo are written
-// with perm8 applied inside each 8-element run (swap 1<->2 and 5<->6), the
-// order the expert kernels' nibble unpack produces.  Whole block, H % 8 == 0.
-__device__ void split_row(const float *__restrict__ xr, int H, uint16_t *__restrict__ hi,
-                          uint16_t *__restrict__ lo, float *__restrict__ sc, float *red4) {
-  float m = 0.0f;
-  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
-    const float4 a = *reinterpret_cast<const float4 *>(xr + c);
-    const float4 b = *reinterpret_cast<const float4 *>(xr + c + 4);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-  }
-  m = wave_max(m);
-  if (threadIdx.x % kWave == 0) red4[threadIdx.x / kWave] = m;
-  __syncthreads();
-  m = red4[0];
-  for (int w = 1; w < int(blockDim.x / kWave); ++w) m = fmaxf(m, red4[w]);
-  __syncthreads();
-  int ex = 0;
-  (void)frexpf(m, &ex);
-  const int e = m > 0.0f ? max(ex - 15, -140) : 0;
-  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
-    const float4 a = *reinterpret_cast<const float4 *>(xr + c);
-    const float4 b = *reinterpret_cast<const float4 *>(xr + c + 4);
-    const float v[8] = {a.x, a.z, a.y, a.w, b.x, b.z, b.y, b.w};  // perm8 order
-    uint16_t h16[8], l16[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float s = ldexpf(v[k], -e);
-      const _Float16 h = _Float16(s);
-      h16[k] = __builtin_bit_cast(uint16_t, h);
-      l16[k] = __builtin_bit_cast(uint16_t, _Float16(s - float(h)));
-    }
-    uint4 ho, lw;
-    ho.x = h16[0] | (uint32_t(h16[1]) << 16); ho.y = h16[2] | (uint32_t(h16[3]) << 16);
-    ho.z = h16[4] | (uint32_t(h16[5]) << 16); ho.w = h16[6] | (uint32_t(h16[7]) << 16);
-    lw.x = l16[0] | (uint32_t(l16[1]) << 16); lw.y = l16[2] | (uint32_t(l16[3]) << 16);
-    lw.z = l16[4] | (uint32_t(l16[5]) << 16); lw.w = l16[6] | (uint32_t(l16[7]) << 16);
-    *reinterpret_cast<uint4 *>(hi + c) = ho;
-    *reinterpret_cast<uint4 *>(lo + c) = lw;
-  }
-  if (threadIdx.x == 0) *sc = ldexpf(1.0f, e);
-}
-
 // Load 8 consecutive elements (fp32 or bf16) as floats.
 template <bool kBf16>
 __device__ inline void load8(const void *base, size_t i, float out[8]) {
@@ -104,20 +59,12 @@ __device__ inline void load8(const void *base, size_t i, float out[8]) {
 // ---------------------------------------------------------------- logits (GEMV)
 // grid.x: groups of 4*RW expert rows; grid.y: groups of TT tokens.  Each lane
 // issues the loads of up to kBatch 512-column chunks before using them.
-// With do_split, blocks of grid row 0 first write the split copy of x
-// (token t on block t % grid.x).
 constexpr int kBatch = 8;
 
 template <int RW, int TT, bool kXbf, bool kWbf>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const void *__restrict__ x, int T, int H, const void *__restrict__ wr,
-    int E, const float *__restrict__ bias, float *__restrict__ logits, DecodeBufs xb,
-    int do_split) {
-  __shared__ float red4[4];
-  if (!kXbf && do_split && blockIdx.y == 0)
-    for (int t = blockIdx.x; t < T; t += gridDim.x)
-      split_row(reinterpret_cast<const float *>(x) + size_t(t) * H, H, xb.xh + size_t(t) * H,
-                xb.xl + size_t(t) * H, xb.xsc + t, red4);
+    int E, const float *__restrict__ bias, float *__restrict__ logits) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int e0 = (blockIdx.x * 4 + wave) * RW;
@@ -555,28 +502,18 @@ size_t permute_chunk_ints(int T, int E) {
 hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
                                 const void *wr, int w_bf16, int E,
                                 const float *bias, float *logits,
-                                const DecodeBufs *xb, hipStream_t s) {
-  DecodeBufs b;
-  int split = 0;
-  if (xb && !x_bf16) {
-    b = *xb;
-    split = 1;
-  } else {
-    b.xh = b.xl = b.hh = b.hl = nullptr;
-    b.xsc = b.hsc = nullptr;
-    b.slotmap = nullptr;
-  }
+                                hipStream_t s) {
 #define COLI_ROUTER_CASE(RW, TT)                                                  \
   {                                                                               \
     dim3 grid((E + 4 * RW - 1) / (4 * RW), (T + TT - 1) / TT);                   \
     if (x_bf16 && w_bf16)                                                         \
-      router_logits_kernel<RW, TT, true, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, b, split);  \
+      router_logits_kernel<RW, TT, true, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);  \
     else if (x_bf16)                                                              \
-      router_logits_kernel<RW, TT, true, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, b, split); \
+      router_logits_kernel<RW, TT, true, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits); \
     else if (w_bf16)                                                              \
-      router_logits_kernel<RW, TT, false, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, b, split); \
+      router_logits_kernel<RW, TT, false, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits); \
     else                                                                          \
-      router_logits_kernel<RW, TT, false, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, b, split);\
+      router_logits_kernel<RW, TT, false, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);\
   }
   if (T <= 2) COLI_ROUTER_CASE(1, 2)
   else COLI_ROUTER_CASE(4, 4)

@@ -78,7 +78,7 @@ def test_decode_small(cfg_id, T):
     oracle_check(cfg_id, L, x, y, idx, gates, DECODE)
 
 
-@pytest.mark.parametrize("cfg_id", [107, 108, 109, 110, 111, 112])
+@pytest.mark.parametrize("cfg_id", [107, 108, 109, 110, 111, 112, 113, 114])
 def test_decode_one_token(cfg_id):
     """Single-token decode on the int8 matrix-core path, several tokens per layer."""
     L = layer(cfg_id)

@@ -67,6 +67,12 @@ CONFIGS.update({
               bias="zipf", mode="decode", layers=1),
     112: dict(name="one_token_h4096", H=4096, I=2048, E=20, K=5, T=1, router="bf16", x="f32",
               bias=None, mode="decode", layers=1),
+    # single-token top-8 shapes whose gate/up and down kernels run the same block shape
+    # (I/8 blocks of I/256 waves): one wave per block, four waves per block
+    113: dict(name="one_token_fused_small", H=768, I=256, E=32, K=8, T=1, router="bf16",
+              x="f32", bias=None, mode="decode", layers=1),
+    114: dict(name="one_token_fused_h3072", H=3072, I=1024, E=64, K=8, T=1, router="f32",
+              x="f32", bias="zipf", mode="decode", layers=1),
 })
 
 WEIGHT_STD = 0.02
