@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcoli.so")
 
 SOURCES = ["coli.cpp", "quant.hip", "route.hip", "ffn_narrow.hip",
-           "ffn_prefill.hip",
+           "ffn_prefill.hip", "ffn_batch.hip",
            "rmsnorm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,9 +28,16 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
          "-fno-fast-math", "-Wall", "-Wno-unused-function"]
 
 
+# Per-source extra flags.
+EXTRA = {
+    # the decode-batch GEMM scales each group tile on the VALU: keep MFMA results in VGPRs
+    "ffn_batch.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

@@ -8,9 +8,9 @@
 // Batch union: page "Colibrì 深度解析", section 四.
 //
 // Kernels
-//   router_logits_kernel  GEMV-shaped logits for small T (decode): one wave
-//                         per (RW expert rows, TT tokens), 16-byte loads of
-//                         the router rows, fp32 FMA, butterfly reduction.
+//   router_logits_kernel  GEMV-shaped logits for small T (decode): one block
+//                         per (RW expert rows, TT tokens), its waves split H,
+//                         16-byte loads of the router rows, fp32 FMA.
 //   router_mfma_kernel    logits for large T (prefill): bf16 x bf16 -> fp32
 //                         on v_mfma_f32_16x16x32_bf16, operands loaded straight
 //                         from global memory (both operands are K-contiguous).
@@ -57,63 +57,71 @@ __device__ inline void load8(const void *base, size_t i, float out[8]) {
 }
 
 // ---------------------------------------------------------------- logits (GEMV)
-// grid.x: groups of 4*RW expert rows; grid.y: groups of TT tokens.  Each lane
-// issues the loads of up to kBatch 512-column chunks before using them.
-constexpr int kBatch = 8;
-
+// grid.x: groups of RW expert rows; grid.y: groups of TT tokens.  The block's 4
+// waves split H; a lane issues all loads of a batch of kB 8-column chunks
+// (router rows kept as raw bf16 or fp32, x as fp32) before using any, and the
+// wave partials meet in LDS in a fixed order.
 template <int RW, int TT, bool kXbf, bool kWbf>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const void *__restrict__ x, int T, int H, const void *__restrict__ wr,
     int E, const float *__restrict__ bias, float *__restrict__ logits) {
+  constexpr int kB = 2;
+  __shared__ float part[4][RW][TT];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int e0 = (blockIdx.x * 4 + wave) * RW;
+  const int e0 = blockIdx.x * RW;
   const int t0 = blockIdx.y * TT;
-  if (e0 >= E) return;
+  const int Hq = ((H / 4 + 7) / 8) * 8;
+  const int cb = wave * Hq, ce = min(H, cb + Hq);
   float acc[RW][TT];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[r][t] = 0.0f;
-
-  constexpr int kB = kBatch / RW > 0 ? kBatch / RW : 1;
-  for (int cb = 0; cb < H; cb += kB * kWave * 8) {
-    float wv[kB][RW][8];
+  for (int c0 = cb; c0 < ce; c0 += kB * kWave * 8) {
+    float wv[kB][RW][8], xv[kB][TT][8];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
-      const int c = cb + (b * kWave + lane) * 8;
+      const int c = c0 + (b * kWave + lane) * 8;
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
-        if (c < H && e0 + r < E) load8<kWbf>(wr, size_t(e0 + r) * H + c, wv[b][r]);
+        if (c < ce && e0 + r < E) load8<kWbf>(wr, size_t(e0 + r) * H + c, wv[b][r]);
         else
 #pragma unroll
           for (int k = 0; k < 8; ++k) wv[b][r][k] = 0.0f;
       }
-    }
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      if (t0 + t >= T) break;
+      for (int t = 0; t < TT; ++t) {
+        if (c < ce && t0 + t < T) load8<kXbf>(x, size_t(t0 + t) * H + c, xv[b][t]);
+        else
 #pragma unroll
-      for (int b = 0; b < kB; ++b) {
-        const int c = cb + (b * kWave + lane) * 8;
-        if (c >= H) break;
-        float xv[8];
-        load8<kXbf>(x, size_t(t0 + t) * H + c, xv);
-#pragma unroll
-        for (int r = 0; r < RW; ++r)
-#pragma unroll
-          for (int k = 0; k < 8; ++k) acc[r][t] = fmaf(wv[b][r][k], xv[k], acc[r][t]);
+          for (int k = 0; k < 8; ++k) xv[b][t][k] = 0.0f;
       }
     }
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[r][t] = fmaf(wv[b][r][k], xv[b][t][k], acc[r][t]);
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       const float v = wave_sum(acc[r][t]);
-      if (lane == 0 && e0 + r < E && t0 + t < T)
-        logits[size_t(t0 + t) * E + e0 + r] = v + (bias ? bias[e0 + r] : 0.0f);
+      if (lane == 0) part[wave][r][t] = v;
     }
+  __syncthreads();
+  if (int(threadIdx.x) < RW * TT) {
+    const int r = threadIdx.x / TT, t = threadIdx.x % TT;
+    if (e0 + r < E && t0 + t < T)
+      logits[size_t(t0 + t) * E + e0 + r] =
+          ((part[0][r][t] + part[1][r][t]) + (part[2][r][t] + part[3][r][t])) +
+          (bias ? bias[e0 + r] : 0.0f);
+  }
 }
 
 // ---------------------------------------------------------------- logits (one token)
@@ -505,7 +513,7 @@ hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
                                 hipStream_t s) {
 #define COLI_ROUTER_CASE(RW, TT)                                                  \
   {                                                                               \
-    dim3 grid((E + 4 * RW - 1) / (4 * RW), (T + TT - 1) / TT);                   \
+    dim3 grid((E + RW - 1) / RW, (T + TT - 1) / TT);                             \
     if (x_bf16 && w_bf16)                                                         \
       router_logits_kernel<RW, TT, true, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);  \
     else if (x_bf16)                                                              \
@@ -515,7 +523,7 @@ hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
     else                                                                          \
       router_logits_kernel<RW, TT, false, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);\
   }
-  if (T <= 2) COLI_ROUTER_CASE(1, 2)
+  if (T <= 2) COLI_ROUTER_CASE(4, 2)
   else COLI_ROUTER_CASE(4, 4)
 #undef COLI_ROUTER_CASE
   return hipGetLastError();
