@@ -291,9 +291,14 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
     return dev_status(e);
   }
   if (wbf) {
+    // the staged-x region is free until the activation conversion: it holds the
+    // router's K-split partial sums
+    const PrefillLayout pl = prefill_layout(L->H, L->I);
     e = launch_router_topk_mfma(reinterpret_cast<const uint16_t *>(x), T, L->H,
                                 reinterpret_cast<const uint16_t *>(L->w_router), L->E,
-                                L->router_bias, L->K, r.logits, r.idx, r.gates, s);
+                                L->router_bias, L->K, r.logits, r.idx, r.gates,
+                                reinterpret_cast<float *>(ws + w.xp),
+                                size_t(T) * pl.HP * 2, s);
     if (e != hipSuccess) return COLI_EDEVICE;
     e = launch_topk_permute(r, T, L->E, L->K, 0, s);
   } else {

@@ -87,11 +87,14 @@ hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
 hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
                                 const void *wr, int w_bf16, int E,
                                 const float *bias, float *logits, hipStream_t s);
-// Prefill router: bf16 x and bf16 Wr through MFMA, top-K fused.
+// Prefill router: bf16 x and bf16 Wr through MFMA, then the top-K.  part:
+// scratch for the K-split partial sums (part_bytes; a smaller split is used
+// when S * T * E floats do not fit).
 hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
                                    const uint16_t *wr, int E,
                                    const float *bias, int K, float *logits,
-                                   int32_t *idx, float *gates, hipStream_t s);
+                                   int32_t *idx, float *gates, float *part,
+                                   size_t part_bytes, hipStream_t s);
 // top-K + gates from logits, one wave per token.
 hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *idx,
                        float *gates, hipStream_t s);

@@ -13,7 +13,8 @@
 //                         16-byte loads of the router rows, fp32 FMA.
 //   router_mfma_kernel    logits for large T (prefill): bf16 x bf16 -> fp32
 //                         on v_mfma_f32_16x16x32_bf16, operands loaded straight
-//                         from global memory (both operands are K-contiguous).
+//                         from global memory (both operands are K-contiguous),
+//                         K split over grid.z with a fixed-order partial sum.
 //   topk_kernel           one wave per token: K rounds of wave argmax.
 //   topk_permute_small    one block: top-K for all tokens, then the permute
 //                         (decode: one launch for the whole route stage).
@@ -244,18 +245,24 @@ typedef short bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Block: 4 waves, tile 64 tokens x 64 experts; wave w owns tokens
-// 16*w..16*w+15 and all 64 experts (4 MFMA column fragments).
+// 16*w..16*w+15 and all 64 experts (4 MFMA column fragments).  grid.z splits
+// K: block z takes the 32-column k-steps z, z + S, z + 2S, .. (S = grid.z) and,
+// for S > 1, writes its partial sums to part[z][t][e] (router_sum_parts adds
+// them in a fixed order); for S == 1 it writes the logits.  Loads of four
+// k-steps are issued before their MFMAs.
 // v_mfma_f32_16x16x32_bf16 operand layout: lane l holds row (l % 16) and
 // k = 8*(l / 16) .. +7 of its 16x32 operand; the result lane l holds rows
 // 4*(l/16)+i, column l % 16.
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, int T, int H,
     const uint16_t *__restrict__ wr, int E, const float *__restrict__ bias,
-    float *__restrict__ logits) {
+    float *__restrict__ out) {
+  constexpr int kU = 4;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int m0 = blockIdx.x * 64 + wave * 16;
   const int n0 = blockIdx.y * 64;
+  const int S = gridDim.z, z = blockIdx.z;
   const int row = lane % 16, kq = (lane / 16) * 8;
   const int mrow = min(m0 + row, T - 1);  // clamp the ragged tail (not stored)
   f32x4 acc[4];
@@ -265,12 +272,24 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
   const uint16_t *wb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) wb[j] = wr + size_t(min(n0 + 16 * j + row, E - 1)) * H + kq;
-  for (int k = 0; k < H; k += 32) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xa + k);
+  const int nk = H / 32;  // k-steps
+  for (int k0 = z; k0 < nk; k0 += kU * S) {
+    bf16x8 a[kU], b[kU][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(wb[j] + k);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    for (int u = 0; u < kU; ++u) {
+      const int k = k0 + u * S;
+      const int kc = k < nk ? 32 * k : 0;  // past the end: any valid column, not used
+      a[u] = *reinterpret_cast<const bf16x8 *>(xa + kc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[u][j] = *reinterpret_cast<const bf16x8 *>(wb[j] + kc);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (k0 + u * S < nk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][j], acc[j], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -279,9 +298,24 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + (lane / 16) * 4 + i;
-      if (m < T && n < E) logits[size_t(m) * E + n] = acc[j][i] + (bias ? bias[n] : 0.0f);
+      if (m < T && n < E) {
+        if (S > 1) out[(size_t(z) * T + m) * E + n] = acc[j][i];
+        else out[size_t(m) * E + n] = acc[j][i] + (bias ? bias[n] : 0.0f);
+      }
     }
   }
+}
+
+// logits[t][e] = sum over z (in order) of part[z][t][e], plus bias[e]
+__global__ __launch_bounds__(256) void router_sum_parts(const float *__restrict__ part, int S,
+                                                        int T, int E,
+                                                        const float *__restrict__ bias,
+                                                        float *__restrict__ logits) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(T) * E) return;
+  float v = part[i];
+  for (int z = 1; z < S; ++z) v += part[int64_t(z) * T * E + i];
+  logits[i] = v + (bias ? bias[i % E] : 0.0f);
 }
 
 // grid: ceil(T/4) blocks of 4 waves; one wave per token.
@@ -545,9 +579,21 @@ hipError_t launch_router_narrow(const float *x, int T, int H, const void *wr, in
 hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
                                    const uint16_t *wr, int E,
                                    const float *bias, int K, float *logits,
-                                   int32_t *idx, float *gates, hipStream_t s) {
-  dim3 grid((T + 63) / 64, (E + 63) / 64);
-  router_mfma_kernel<<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);
+                                   int32_t *idx, float *gates, float *part,
+                                   size_t part_bytes, hipStream_t s) {
+  // K split: enough blocks to cover the GPU several times, as far as the
+  // partial-sum scratch allows
+  const int64_t tiles = int64_t((T + 63) / 64) * ((E + 63) / 64);
+  int S = int(tiles >= 1024 ? 1 : (1024 + tiles - 1) / tiles);
+  if (S > 8) S = 8;
+  if (S > H / 32) S = H / 32;
+  while (S > 1 && size_t(S) * T * E * 4 > part_bytes) --S;
+  dim3 grid((T + 63) / 64, (E + 63) / 64, S);
+  router_mfma_kernel<<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, S > 1 ? part : logits);
+  if (S > 1) {
+    const int64_t n = int64_t(T) * E;
+    router_sum_parts<<<dim3(unsigned((n + 255) / 256)), 256, 0, s>>>(part, S, T, E, bias, logits);
+  }
   topk_kernel<<<dim3((T + 3) / 4), 256, 0, s>>>(logits, T, E, K, idx, gates);
   return hipGetLastError();
 }
