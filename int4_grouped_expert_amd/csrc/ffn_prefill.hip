@@ -23,6 +23,10 @@
 // Scales: lane (h, n) loads groups 16i + 8h .. +7 of row n as two float4 per 4
 // super-steps; v_permlane32_swap between lane halves regroups them so that the
 // lane holds groups 4c + 2h, 4c + 2h + 1 for each super-step c of the block.
+// Depth: with up to 3 M fragments the weights of super-step ss + 2 are issued
+// at the end of super-step ss, after its last DMA, and stay in flight across
+// the barrier (vmcnt(8) and a fence-free s_barrier); with 4 fragments the
+// registers allow one super-step, issued one load per MFMA step.
 //
 // Dequant without the -8: for a 32-bit word d of nibbles, (d & 0x000F000F) |
 // 0x64006400 is the fp16 pair {1024 + u, 1024 + u'} and (d & 0x00F000F0) |
@@ -219,7 +223,6 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
   const int nss = (G + 3) >> 2;
   const uint32_t rowB = uint32_t(G) * 32u;
   const int nrows = it.je - it.jb;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(it.blob, uint32_t(L.lay.bytes));
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(pa.A, pa.a_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(pa.S, pa.s_bytes);
   // empty resource: every access reads zeros (loads of the last super-step)
@@ -237,6 +240,9 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
     wrow0 = it.ntile * 256 + 64 * wave;
     wvalid = wrow0 < L.H;
   }
+  // a wave past the matrix runs the same instruction stream on an empty weight
+  // resource (zeros) and stores nothing: no wave-dependent branch in the loop
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(it.blob, wvalid ? uint32_t(L.lay.bytes) : 0u);
   uint32_t xoff[2], soff[2];
 #pragma unroll
   for (int jn = 0; jn < 2; ++jn) {
@@ -327,13 +333,16 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
   // prologue: stage 0 (activations, correction block 0), scales of block 0, weights of
   // super-step 0
   float F[2][8] = {};
-  uint4 R[2][4] = {};
+  // weight registers: kDepth super-steps of loads in flight (two when the
+  // registers allow: the exchange of super-step ss then waits for loads issued
+  // two super-steps earlier)
+  constexpr int kDepth = NMF <= 3 ? 2 : 1;
+  uint4 Rb[kDepth][2][4] = {};
   dma_a(0, g_st0);
   dma_c(0, g_sc0);
-  if (wvalid) {
-    load_f(0, F);
-    load_b(0, R);
-  }
+  load_f(0, F);
+  load_b(0, Rb[0]);
+  if (kDepth == 2 && nss > 1) load_b(1, Rb[1]);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();
 
@@ -350,18 +359,20 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
   // super-step c at 2c, 2c + 1), rotated by two per super-step
   float U[2][8] = {};
   // one super-step: compute from (st, sc) while the DMA fills (stn, scn)
-  auto super_step = [&](int ss, const uint8_t *st, const uint8_t *sc, uint8_t *stn, uint8_t *scn) {
+  auto super_step = [&](int ss, int par, const uint8_t *st, const uint8_t *sc, uint8_t *stn,
+                        uint8_t *scn) {
     const bool more = ss + 1 < nss;
+    uint4(&R)[2][4] = Rb[kDepth == 2 ? par : 0];
     if (more && ((ss + 1) & 3) == 0) dma_c((ss + 1) >> 2, scn);
-    if (wvalid) {
+    {
       // this super-step's weights into MFMA lane order: register d of lane (h, n)
       // = part 4h + d of row n (exchange of the load index with lane bits 3, 4)
       uint4 D[2][4];
 #pragma unroll
       for (int jn = 0; jn < 2; ++jn) exchange_rows(R[jn], D[jn]);
-      // the next super-step's weights go out one load per step in steps 0..7
-      // (issued in one burst the four waves queue on the address unit)
-      const __amdgpu_buffer_rsrc_t rwn = more ? rw : rnull;
+      // depth 1: the next super-step's weights go out one load per step in
+      // steps 0..7 (issued in one burst the four waves queue on the address unit)
+      const __amdgpu_buffer_rsrc_t rwn = ss + kDepth < nss ? rw : rnull;
       if ((ss & 3) == 0) {
         // correction GEMM of block i = ss / 4: acc += S (hi, lo) x (-8 s, -8 s);
         // k-step kc, k-half h covers groups 16i + 8h + 4kc .. +3
@@ -458,10 +469,10 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
         // the last super-step the instruction reads out of range and writes zeros
         // into the unused stage, landed before the epilogue by the closing wait)
         dma16(ra, stn + (32 * wave + 2 * k) * kRowB, more ? aoff[k] : kOff, uint32_t(512 * (ss + 1)));
-        if (k < 8)
+        if (kDepth == 1 && k < 8)
           R[k >> 2][k & 3] = bload16(rwn, xoff[k >> 2], 128u * uint32_t(ss + 1) + 8u * uint32_t(k & 3) * rowB);
         if (k < 15) {
-          if (k < 8) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM (DMA, weights)
+          if (kDepth == 1 && k < 8) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM (DMA, weights)
           else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, NMF, 0);  // DS reads
 #pragma unroll
@@ -476,17 +487,38 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-    } else if (more) {
-      // rows past the matrix: staging only
-      dma_a(ss + 1, stn);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next stage's DMA and weights landed
-    __syncthreads();
+    if (kDepth == 2) {
+      // the weights of super-step ss + 2 go out after this super-step's last DMA
+      // (empty resource past the end: the count stays 8), so the wait below can
+      // leave exactly them in flight across the barrier
+      {
+        const __amdgpu_buffer_rsrc_t rwn2 = ss + 2 < nss ? rw : rnull;
+        uint4(&R2)[2][4] = Rb[par];
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+            R2[jn][a4] = bload16(rwn2, xoff[jn], 128u * uint32_t(ss + 2) + 8u * uint32_t(a4) * rowB);
+        __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): next stage landed
+      }
+      // a plain barrier: __syncthreads() would also wait for the loads left in
+      // flight (its workgroup release waits for every memory operation);
+      // the memory clobber keeps the compiler from moving LDS accesses across
+      asm volatile("s_barrier" ::: "memory");
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next stage's DMA and weights landed
+      __syncthreads();
+    }
   };
-  for (int ss = 0; ss < nss; ss += 2) {
-    super_step(ss, g_st0, g_sc0, g_st1, g_sc1);
-    if (ss + 1 < nss) super_step(ss + 1, g_st1, g_sc1, g_st0, g_sc0);
+  // pairs of super-steps with no branch inside the loop body (the compiler's
+  // load-counter bookkeeping then carries across the back edge), odd tail after
+  int ss = 0;
+  for (; ss + 1 < nss; ss += 2) {
+    super_step(ss, 0, g_st0, g_sc0, g_st1, g_sc1);
+    super_step(ss + 1, 1, g_st1, g_sc1, g_st0, g_sc0);
   }
+  if (ss < nss) super_step(ss, 0, g_st0, g_sc0, g_st1, g_sc1);
 
   // epilogue through an LDS tile (the stages are free: the last super-step ended
   // with a barrier), then 16-byte stores.  tid is made opaque so that the
