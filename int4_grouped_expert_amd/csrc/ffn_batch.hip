@@ -127,7 +127,10 @@ __device__ inline f16x8 unpack_u8(uint32_t d, uint32_t m1, uint32_t m2) {
   return f16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
-template <bool kGateUp>
+// kHalf: a chunk of at most 16 tokens, staged as one 32-row fragment (hi
+// rows 0..15, lo rows 16..31), so that each k-step takes one MFMA per weight
+// fragment instead of two; the hi and lo result rows are added at the end.
+template <bool kGateUp, bool kHalf>
 __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDev &L,
                                                                    const DecArgs &da,
                                                                    const Item &it) {
@@ -173,18 +176,20 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
   }
   // DMA roles: instruction i of this wave fills staged rows 16w + 2i, +1
   // (lane: row + lane/32, LDS chunk lane%32)
-  uint32_t aoff[8];
+  constexpr int kNdma = kHalf ? 4 : 8;        // DMA instructions per wave per stage
+  constexpr int kRowsW = 2 * kNdma;           // staged rows per wave
+  uint32_t aoff[kNdma];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 16 * wave + 2 * i + (lane >> 5);
+  for (int i = 0; i < kNdma; ++i) {
+    const int r = kRowsW * wave + 2 * i + (lane >> 5);
     const int ri = g_rowidx[r];
     const uint32_t chunk = uint32_t((lane & 31) ^ (r & 15));
     aoff[i] = ri >= 0 ? uint32_t(ri) * uint32_t(da.AP) * 2u + 16u * chunk : kOff;
   }
   auto dma_a = [&](int ss, uint8_t *st) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma16(ra, st + (16 * wave + 2 * i) * kRowB, aoff[i], uint32_t(512 * ss));
+    for (int i = 0; i < kNdma; ++i)
+      dma16(ra, st + (kRowsW * wave + 2 * i) * kRowB, aoff[i], uint32_t(512 * ss));
   };
   auto load_b = [&](int ss, uint4(&R)[2][4]) {
 #pragma unroll
@@ -240,23 +245,23 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
       if (more) load_s(ss + 1, Fn);
       // k-step k = 4 d + w: group d of the super-step, word w; lane half h
       // reads chunk 8 d + 4 h + w of its hi and lo rows
-      f16x8 ahi, alo;
+      f16x8 ahi, alo = {};
       {
         const uint32_t q = uint32_t(4 * h) ^ aswz;
         ahi = *reinterpret_cast<const f16x8 *>(st + abase + 16 * q);
-        alo = *reinterpret_cast<const f16x8 *>(st + abase + 32 * kRowB + 16 * q);
+        if (!kHalf) alo = *reinterpret_cast<const f16x8 *>(st + abase + 32 * kRowB + 16 * q);
       }
       f32x16 C[2];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int d = k >> 2, w = k & 3;
         __builtin_amdgcn_sched_barrier(0);
-        f16x8 ahn, aln;
+        f16x8 ahn, aln = {};
         if (k < 15) {
           const int k1 = k + 1;
           const uint32_t q = uint32_t(8 * (k1 >> 2) + 4 * h + (k1 & 3)) ^ aswz;
           ahn = *reinterpret_cast<const f16x8 *>(st + abase + 16 * q);
-          aln = *reinterpret_cast<const f16x8 *>(st + abase + 32 * kRowB + 16 * q);
+          if (!kHalf) aln = *reinterpret_cast<const f16x8 *>(st + abase + 32 * kRowB + 16 * q);
         }
         f16x8 b[2];
 #pragma unroll
@@ -268,9 +273,11 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
 #pragma unroll
         for (int jn = 0; jn < 2; ++jn)
           C[jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, b[jn], C[jn], 0, 0, 0);
+        if (!kHalf) {
 #pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-          C[jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, b[jn], C[jn], 0, 0, 0);
+          for (int jn = 0; jn < 2; ++jn)
+            C[jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, b[jn], C[jn], 0, 0, 0);
+        }
         if (w == 3) {
           // the group's tile, scaled by its fp32 scale
 #pragma unroll
@@ -280,13 +287,14 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
             for (int v = 0; v < 16; ++v) acc[jn][v] = fmaf(C[jn][v], sg, acc[jn][v]);
           }
         }
-        if ((k & 1) == 0)
-          dma16(ra, stn + (16 * wave + k) * kRowB, more ? aoff[k >> 1] : kOff, uint32_t(512 * (ss + 1)));
+        if ((k & (16 / kNdma - 1)) == 0)
+          dma16(ra, stn + (kRowsW * wave + 2 * (k / (16 / kNdma))) * kRowB,
+                more ? aoff[k / (16 / kNdma)] : kOff, uint32_t(512 * (ss + 1)));
         if (k < 8)
           R[k >> 2][k & 3] = bload16(rwn, xoff[k >> 2], 128u * uint32_t(ss + 1) + 8u * uint32_t(k & 3) * rowB);
         if (k < 15) {
           ahi = ahn;
-          alo = aln;
+          if (!kHalf) alo = aln;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -305,10 +313,18 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
     if (ss + 1 < nss) super_step(ss + 1, g_st1, g_st0);
   }
 
-  // epilogue: acc[jn][4j + i] is chunk token 8j + 4h + i, column n of fragment jn
+  // epilogue: acc[jn][4j + i] is staged row 8j + 4h + i, column n of fragment
+  // jn: chunk token 8j + 4h + i, or (kHalf) token m's hi row for v < 8 and its
+  // lo row at v + 8, added here
+  if (kHalf) {
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+      for (int v = 0; v < 8; ++v) acc[jn][v] += acc[jn][v + 8];
+  }
   if (wvalid) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
+    for (int v = 0; v < (kHalf ? 8 : 16); ++v) {
       const int m = 8 * (v >> 2) + 4 * h + (v & 3);
       if (m < nrows) {
         const float rs = g_rsc[m];
@@ -361,11 +377,15 @@ __global__ __launch_bounds__(kThreads, 2) void dec_gemm(LayerDev L, Routing r, i
       it.shared = __builtin_amdgcn_readfirstlane(int(it.shared)) != 0;
     }
     __syncthreads();  // the previous item is done with the row tables
+    // staged rows: chunks of up to 16 tokens take hi rows 0..15 and lo rows
+    // 16..31, larger ones hi rows 0..31 and lo rows 32..63
+    const bool small = it.je - it.jb <= kDMC / 2;
+    const int per = small ? kDMC / 2 : kDMC;
     if (threadIdx.x < 2 * kDMC) {
-      const int tok = threadIdx.x % kDMC, half = threadIdx.x / kDMC;
+      const int tok = threadIdx.x % per, half = threadIdx.x / per;
       const int j = it.jb + tok;
       int ri = -1;
-      if (j < it.je) {
+      if (j < it.je && half < 2) {
         int arow, orow;
         float gate = 1.0f;
         if (kGateUp) {
@@ -381,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void dec_gemm(LayerDev L, Routing r, i
             gate = r.gates[p];
           }
         }
-        ri = arow + half * da.lo_rows;
+        ri = half < 2 ? arow + half * da.lo_rows : -1;
         if (half == 0) {
           g_outrow[tok] = orow;
           g_gate[tok] = gate;
@@ -391,7 +411,10 @@ __global__ __launch_bounds__(kThreads, 2) void dec_gemm(LayerDev L, Routing r, i
       g_rowidx[threadIdx.x] = ri;
     }
     __syncthreads();
-    run_item_dec<kGateUp>(L, da, it);
+    if (small)
+      run_item_dec<kGateUp, true>(L, da, it);
+    else
+      run_item_dec<kGateUp, false>(L, da, it);
   }
 }
 
