@@ -78,6 +78,42 @@ def test_decode_small(cfg_id, T):
     oracle_check(cfg_id, L, x, y, idx, gates, DECODE)
 
 
+def test_decode_batch_row_scales():
+    """Decode batch rows spanning 2^-8 .. 2^12 and an all-zero row: each row's x and h
+    get their own power-of-two scale before the fp16 hi/lo split.  Power-of-two
+    factors scale the logits exactly, so every row keeps its routing margin (the
+    zero row's logits are exact ties or the bias, resolved the same way on both
+    sides); each row is compared with the oracle under its own magnitude."""
+    cfg_id = 0
+    L = layer(cfg_id)
+    c = W.CONFIGS[cfg_id]
+    x = margin_tokens(cfg_id, 5, host_array(L.w_router), L.bias_np, c["K"])
+    f = torch.tensor([1.0, 2.0 ** 4, 2.0 ** 12, 2.0 ** -8, 0.0], device=x.device)
+    x = (x * f[:, None]).contiguous()
+    y, idx, gates = L.forward(x, DECODE)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    for row in range(5):
+        log(f"row scale {float(f[row])}")
+        oracle_check(cfg_id, L, x, y, idx, gates, DECODE, rows=[row], check_bytes=(row == 0))
+
+
+def test_decode_one_token_scales():
+    """Single-token decode (int8 digit planes under one power-of-two scale per vector)
+    with the token scaled by 2^12, 2^-8 and 0."""
+    cfg_id = 107
+    L = layer(cfg_id)
+    c = W.CONFIGS[cfg_id]
+    x0 = margin_tokens(cfg_id, 1, host_array(L.w_router), L.bias_np, c["K"])
+    for f in (2.0 ** 12, 2.0 ** -8, 0.0):
+        log(f"one token scale {f}")
+        x = (x0 * f).contiguous()
+        y, idx, gates = L.forward(x, DECODE)
+        torch.cuda.synchronize()
+        assert torch.isfinite(y).all()
+        oracle_check(cfg_id, L, x, y, idx, gates, DECODE, check_bytes=(f == 2.0 ** 12))
+
+
 @pytest.mark.parametrize("cfg_id", [107, 108, 109, 110, 111, 112, 113, 114])
 def test_decode_one_token(cfg_id):
     """Single-token decode on the int8 matrix-core path, several tokens per layer."""
