@@ -20,7 +20,11 @@
 // scale.  Every element within a factor 16 of the vector's largest is
 // represented exactly, smaller ones to 2^-28 of it: the products are at least
 // as accurate as an fp32 dot product.  The unpack costs 3 32-bit operations
-// per 8 weights.
+// per 8 weights.  The down kernel digitises h' itself, in unbalanced digits
+// (d1..d3 in [0, 127], d0 = A >> 21 in [-64, 64]: one bit-field extract each),
+// and forms its -8 * sum_k d_k with two more products against a B operand of
+// -8 bytes; every plane sum stays below 2^16 in magnitude, so the recombined
+// value is the same exact integer and rounds the same way.
 //
 // MFMA layout (16x16x64 i8: lane l holds A row / B column l % 16 and 16
 // bytes of k for the k-quarter l / 16; the result lane l holds rows
@@ -50,10 +54,11 @@
 //                  h' = gate_weight * SiLU(gate) * up in fp32.
 //   down_narrow    persistent, output-stationary; item = 8 rows of y, all
 //                  units.  Wave w owns K chunk w (256 columns of I) of every
-//                  unit: it turns its slices of h' into digits in its own LDS
-//                  area once, then streams (item, unit) steps through a ring
-//                  one item deep.  The gates sit in h', so the combine is the
-//                  accumulation itself, in a fixed order (no atomics).
+//                  unit and streams (item, unit) steps through a register
+//                  ring two units deep; it turns unit u + 1's slice of h'
+//                  into digits in its own LDS area during step u, while the
+//                  weights are in flight.  The gates sit in h', so the combine
+//                  is the accumulation itself, in a fixed order (no atomics).
 #include <hip/hip_ext.h>
 
 #include "kernels.h"
@@ -128,6 +133,28 @@ __device__ inline float fold_rows(float v, int lane) {
   v += __shfl_xor(v, 16, kW);
   v += __shfl_xor(v, 32, kW);
   return v;
+}
+
+// Wave maximum of an unsigned value (every lane gets it).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, uint32_t(dpp_row_i<0xB1>(int(v))));
+  v = max(v, uint32_t(dpp_row_i<0x4E>(int(v))));
+  v = max(v, uint32_t(dpp_row_i<0x141>(int(v))));
+  v = max(v, uint32_t(dpp_row_i<0x140>(int(v))));
+  const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 0), r1 = __builtin_amdgcn_readlane(int(v), 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 32), r3 = __builtin_amdgcn_readlane(int(v), 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Plane p of four fixed-point values a_i (|a_i| <= 2^27) packed one byte per
+// value, in base-128 digits a = d0 2^21 + d1 2^14 + d2 2^7 + d3 with
+// d1..d3 in [0, 127] and d0 = a >> 21 in [-64, 64].
+__device__ inline uint32_t pack_digits(const int (&a)[4], int p) {
+  const uint32_t pos = p == 0 ? 21u : 7u * uint32_t(3 - p), w = p == 0 ? 8u : 7u;
+  uint32_t r = __builtin_amdgcn_ubfe(uint32_t(a[0]), pos, w);
+  r |= __builtin_amdgcn_ubfe(uint32_t(a[1]), pos, w) << 8;
+  r |= __builtin_amdgcn_ubfe(uint32_t(a[2]), pos, w) << 16;
+  return r | (__builtin_amdgcn_ubfe(uint32_t(a[3]), pos, w) << 24);
 }
 
 // ------------------------------------------------------------------ gate/up
@@ -282,11 +309,10 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
 }
 
 // ------------------------------------------------------------------ down
-// Per-wave LDS area: digits [NU][4 planes][4 groups][64], corrections
-// [NU][4 groups][4 planes] int32, then 32 zero bytes (the A rows of inactive
-// k-quarters read them).
+// Per-wave LDS area: digits [NU][4 planes][4 groups][64], then 32 zero bytes
+// (the A rows of inactive k-quarters read them).
 template <int NU>
-constexpr int down_wave_bytes() { return NU * (1024 + 64) + 32; }
+constexpr int down_wave_bytes() { return NU * 1024 + 32; }
 
 constexpr int kDownMaxWaves = 8;
 constexpr int kDownItems = 3;  // items per down block
@@ -305,8 +331,7 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
   if (int(blockIdx.x) >= n_items) return;
   uint8_t *my = dyn + wave * down_wave_bytes<NU>();
   int8_t *dig = reinterpret_cast<int8_t *>(my);
-  int32_t *corr = reinterpret_cast<int32_t *>(my + NU * 1024);
-  uint8_t *zero = my + NU * 1088;
+  uint8_t *zero = my + NU * 1024;
 
   const int n = lane % 16, q = lane / 16;
   const int r = n % 8, kap = n / 8;
@@ -335,6 +360,17 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
     lo[k] = loff(itk) * 32 + 16 * (q % 2);
     so[k] = sof(itk);
   }
+  // h' chunk `wave` of unit u.  Lane l holds elements 4l .. 4l+3 of the
+  // chunk: group l / 16, element 4 (l % 16).  Units 0..2 are loaded before
+  // the weight ring, unit u + 3 at the start of step u, ahead of that step's
+  // refills: the load counter retires in issue order, so waiting for a unit's
+  // h' never waits for weights that are not yet due.
+  float4 hv[NU];
+  auto load_h = [&](int u) {
+    hv[u] = *reinterpret_cast<const float4 *>(nb.hn + size_t(u) * I + 256 * wave + 4 * lane);
+  };
+#pragma unroll
+  for (int u = 0; u < 3 && u < NU; ++u) load_h(u);
   uint4 rw[2][kDownItems];
   float rs[2][kDownItems];
 #pragma unroll
@@ -345,55 +381,49 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
       rw[h][k] = *reinterpret_cast<const uint4 *>(blob[u] + L.lay.dq + lo[k]);
       rs[h][k] = reinterpret_cast<const float *>(blob[u] + L.lay.ds)[so[k]];
     }
+  if (lane < 8) reinterpret_cast<uint32_t *>(zero)[lane] = 0u;
 
-  // h' chunk `wave` of every unit -> digits in this wave's LDS area.  Lane l
-  // holds elements 4l .. 4l+3 of the chunk: group l / 16, element 4 (l % 16).
+  // unit u's slice of h' -> digits in this wave's LDS area.  Unit 0 goes
+  // before the stream starts; unit u + 1 during step u, while unit u's
+  // weights are still in flight.
   float sa[NU];
-  {
-    float4 hv[NU];
+  const int gl = lane / 16, pos = aorder_pos(4 * (lane % 16));
+  auto digitise = [&](int u) {
+    const float v[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+    // max |v| on the bit patterns: NaN > Inf > every finite value
+    uint32_t mb = 0;
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
-      hv[u] = *reinterpret_cast<const float4 *>(nb.hn + size_t(u) * I + 256 * wave + 4 * lane);
-    if (lane < 8) reinterpret_cast<uint32_t *>(zero)[lane] = 0u;
-    const int gl = lane / 16, pos = aorder_pos(4 * (lane % 16));
+    for (int i = 0; i < 4; ++i) mb = max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    mb = wave_max_u32(mb);
+    const int e = digit_exponent(__uint_as_float(mb));
+    sa[u] = mb >= 0x7F800000u ? __builtin_nanf("") : ldexpf(1.0f, -e);
+    int a[4];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const float v[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
-      float m = 0.0f;
-      bool bad = false;
+    for (int i = 0; i < 4; ++i)
+      a[i] = int(rintf(fminf(fmaxf(ldexpf(v[i], e), -134217728.0f), 134217728.0f)));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        m = fmaxf(m, fabsf(v[i]));
-        bad |= !__builtin_isfinite(v[i]);
-      }
-      m = wave_max(m);
-      bad = __any(bad);
-      const int e = digit_exponent(m);
-      sa[u] = bad ? __builtin_nanf("") : ldexpf(1.0f, -e);
-      int d[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) digits4(v[i], e, d[i]);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        *reinterpret_cast<uint32_t *>(dig + ((u * 4 + p) * 4 + gl) * 64 + pos) = pack_plane(d, p);
-        const int sum = row16_sum_i(d[0][p] + d[1][p] + d[2][p] + d[3][p]);
-        if ((lane % 16) == 0) corr[(u * 4 + gl) * 4 + p] = -8 * sum;
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<uint32_t *>(dig + ((u * 4 + p) * 4 + gl) * 64 + pos) = pack_digits(a, p);
+  };
+  // the wave's own LDS writes, visible to its reads that follow
+  auto lds_wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  };
+  digitise(0);
 
   // A-row LDS addresses (inactive k-quarters read the zero bytes) and the
   // correction of the result lane's slot (group q of the chunk)
   const int sA = n / 4, pA = n % 4;
   const bool actA = (q / 2) == (sA % 2);
   const int gA = 2 * (sA / 2) + (sA % 2);
-  const int a_base = actA ? ((pA * 4 + gA) * 64 + 16 * (2 * (q % 2))) : NU * 1088;
+  const int a_base = actA ? ((pA * 4 + gA) * 64 + 16 * (2 * (q % 2))) : NU * 1024;
+  // B operand of the correction products: -8 in every byte
+  const i32x4 m8 = {int(0xF8F8F8F8u), int(0xF8F8F8F8u), int(0xF8F8F8F8u), int(0xF8F8F8F8u)};
+  const i32x4 z4 = {0, 0, 0, 0};
   const int a_step = actA ? 1024 : 0;
 
-  wait_all_loads();
   float acc[kDownItems];
 #pragma unroll
   for (int k = 0; k < kDownItems; ++k) acc[k] = 0.0f;
@@ -401,10 +431,15 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
   for (int u = 0; u < NU; ++u) {
     const int h = u & 1;
     const int un = u + 2 < NU ? u + 2 : NU - 1;  // refill: two units ahead
+    if (u + 3 < NU) load_h(u + 3);
+    if (u + 1 < NU) digitise(u + 1);
+    lds_wave_sync();
     const int8_t *ap = dig + a_base + u * a_step;
     const i32x4 a0 = *reinterpret_cast<const i32x4 *>(ap);
     const i32x4 a1 = *reinterpret_cast<const i32x4 *>(ap + 16);
-    const i32x4 c0 = *reinterpret_cast<const i32x4 *>(corr + (u * 4 + q) * 4);
+    // -8 times each A row's digit sum, in the result layout: the accumulator
+    // start of every item of this unit
+    const i32x4 c0 = mfma_i8(a1, m8, mfma_i8(a0, m8, z4));
 #pragma unroll
     for (int k = 0; k < kDownItems; ++k) {
       const i32x4 b0 = unpack_half(rw[h][k].x, rw[h][k].y);
@@ -475,7 +510,7 @@ bool narrow_supported(const LayerDev &L, int T) {
   if (!gateup_waves(L.H, &nc)) return false;
   const int nw = L.I / 256;
   if (nw > kDownMaxWaves) return false;
-  const size_t lds = size_t(nw) * size_t((L.K + 1) * (1024 + 64) + 32);
+  const size_t lds = size_t(nw) * size_t((L.K + 1) * 1024 + 32);
   return lds + sizeof(float) * 2 * kMaxWaves * 8 <= 160 * 1024;
 }
 
