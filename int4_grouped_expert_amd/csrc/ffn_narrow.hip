@@ -135,17 +135,6 @@ __device__ inline float fold_rows(float v, int lane) {
   return v;
 }
 
-// Wave maximum of an unsigned value (every lane gets it).
-__device__ inline uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, uint32_t(dpp_row_i<0xB1>(int(v))));
-  v = max(v, uint32_t(dpp_row_i<0x4E>(int(v))));
-  v = max(v, uint32_t(dpp_row_i<0x141>(int(v))));
-  v = max(v, uint32_t(dpp_row_i<0x140>(int(v))));
-  const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 0), r1 = __builtin_amdgcn_readlane(int(v), 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 32), r3 = __builtin_amdgcn_readlane(int(v), 48);
-  return max(max(r0, r1), max(r2, r3));
-}
-
 // Plane p of four fixed-point values a_i (|a_i| <= 2^27) packed one byte per
 // value, in base-128 digits a = d0 2^21 + d1 2^14 + d2 2^7 + d3 with
 // d1..d3 in [0, 127] and d0 = a >> 21 in [-64, 64].

@@ -70,36 +70,26 @@ __device__ inline void wave_argmax(float &bv, int &bi) {
   bi = i;
 }
 
-// Arg-max keys: (order-preserving bits of the value) << 32 | ~id, so that the
-// unsigned maximum is the largest value and, among equal values, the lowest
-// id; 0 means "no candidate" (NaN values and ids >= E never get a key).
-__device__ inline uint64_t topk_key(float v, int id) {
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return (uint64_t(o) << 32) | uint64_t(~uint32_t(id));
-}
-__device__ inline uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 template <int kCtrl>
-__device__ inline uint64_t dpp_u64(uint64_t k) {
-  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(k)), kCtrl, 0xF, 0xF, false));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(k >> 32)), kCtrl, 0xF, 0xF, false));
-  return (uint64_t(hi) << 32) | lo;
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kCtrl, 0xF, 0xF, false));
 }
-__device__ inline uint64_t rdlane_u64(uint64_t k, int l) {
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(k)), l));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(k >> 32)), l));
-  return (uint64_t(hi) << 32) | lo;
+// Wave maximum of an unsigned value (same DPP pattern as wave_max).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 0), r1 = __builtin_amdgcn_readlane(int(v), 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 32), r3 = __builtin_amdgcn_readlane(int(v), 48);
+  return max(max(r0, r1), max(r2, r3));
 }
-// Wave maximum of a key (same DPP pattern as wave_max; every lane gets it).
-__device__ inline uint64_t wave_max_key(uint64_t k) {
-  k = max_u64(k, dpp_u64<0xB1>(k));
-  k = max_u64(k, dpp_u64<0x4E>(k));
-  k = max_u64(k, dpp_u64<0x141>(k));
-  k = max_u64(k, dpp_u64<0x140>(k));
-  return max_u64(max_u64(rdlane_u64(k, 0), rdlane_u64(k, 16)),
-                 max_u64(rdlane_u64(k, 32), rdlane_u64(k, 48)));
+// Order-preserving bits of a float: the unsigned order of the results is the
+// order of the values (-0 just below +0); never 0 for a non-NaN value.
+__device__ inline uint32_t order_bits(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-
 // Wave-wide top-K of one token, PL logits per lane (E <= 64 PL).  Writes
 // idx/gates in ascending id order.  Each lane keeps the key of its best
 // untaken candidate; a round is one wave key maximum, after which only the
@@ -120,22 +110,43 @@ template <int PL>
 __device__ __attribute__((always_inline)) inline void topk_select(
     const float (&v)[PL], int E, int K, int lane, int32_t *__restrict__ idx_out,
     float *__restrict__ gate_out) {
+  // Each lane keeps its best untaken candidate: the order bits of the value
+  // (0: none; NaN values and ids >= E are never candidates) and its slot j,
+  // the lowest among equal values.  A round is a wave maximum of the order
+  // bits; the lane holding it wins, and when several lanes hold it the lowest
+  // id among them does (the rare tie path), so the pick is the largest value,
+  // ties to the lowest id.
   uint32_t taken = 0;
-  uint64_t lk = 0;
+  uint32_t lk = 0;
+  int lj = 0;
   auto rescan = [&]() {
     lk = 0;
+    lj = 0;
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
       const int e = lane + kWaveLanes * j;
       const bool cand = e < E && !__builtin_isnan(v[j]) && !((taken >> j) & 1u);
-      lk = max_u64(lk, cand ? topk_key(v[j], e) : 0ull);
+      const uint32_t o = cand ? order_bits(v[j]) : 0u;
+      lj = o > lk ? j : lj;
+      lk = o > lk ? o : lk;
     }
   };
   rescan();
   for (int round = 0; round < K; ++round) {
-    const uint64_t wk = wave_max_key(lk);
-    int bi = int(~uint32_t(wk));
-    if (wk == 0) {
+    const uint32_t wk = wave_max_u32(lk);
+    int bi;
+    if (wk != 0) {
+      const uint64_t hold = __ballot(lk == wk);
+      if (__popcll(hold) == 1) {
+        const int wl = __ffsll((unsigned long long)hold) - 1;
+        bi = wl + kWaveLanes * __builtin_amdgcn_readlane(lj, wl);
+      } else {
+        int id = lk == wk ? lane + kWaveLanes * lj : 0x7fffffff;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) id = min(id, __shfl_xor(id, m, kWaveLanes));
+        bi = id;
+      }
+    } else {
       // No valid candidate: id `round` if free, else the lowest free id.
       int free_lo = 0x7fffffff;
 #pragma unroll
