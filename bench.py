@@ -271,6 +271,10 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise kernel (clamp) that reads and writes "
                          "MIB MiB, the reference for scaling HBM byte counters")
+    ap.add_argument("--stack", action="store_true",
+                    help="only the 40-layer T=8 stack (218 GB resident) and the quantiser "
+                         "timing; prints its own JSON line")
+    ap.add_argument("--stack-cfg", type=int, default=4, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -292,6 +296,13 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy probe: clamp kernel, {args.copy_probe} MiB read + written, 3 launches")
         del a, b
+
+    if args.stack:
+        log("[bench] stack: building 40 layers")
+        steps = args.steps if args.steps != 3000 else 20
+        warmup = args.warmup if args.warmup != 300 else 3
+        print(json.dumps(run_stack(coli, W, steps, warmup, cfg_id=args.stack_cfg)), flush=True)
+        return
 
     log(f"[bench] building layer ({args.replicas} replicas)")
     layers, nb = build_layer(coli, W, 1, args.replicas)
@@ -346,6 +357,91 @@ def main():
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(coli, W)
     print(json.dumps(result), flush=True)
+
+
+def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4):
+    """The 40-layer stack at T=8: all layers resident, RMSNorm between layers.
+
+    Every expert of every layer is quantised by the library from its own seeded
+    N(0, 0.02) draw; the 256 routed experts of layer 0 time the quantiser (events
+    around each coli_quant_expert call, the draws outside).  A step feeds one batch
+    of 8 tokens through the 40 layers; U per layer is measured on the last step."""
+    import torch
+    c = W.CONFIGS[cfg_id]
+    H, I, E, K, T, NL = c["H"], c["I"], c["E"], c["K"], c["T"], c["layers"]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    layers, qev = [], []
+    for l in range(NL):
+        experts, shared, nb = coli.alloc_layer_blobs(H, I, E)
+        for e in range(E + 1):
+            wg, wu, wd = W.expert_weights(cfg_id, e, "cuda", l)
+            ptr = shared.data_ptr() if e == E else experts.data_ptr() + e * nb
+            if l == 0 and e < E:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev[0].record()
+                coli.coli_quant_expert(ptr, H, I, wg, wu, wd, status)
+                ev[1].record()
+                qev.append(ev)
+            else:
+                coli.coli_quant_expert(ptr, H, I, wg, wu, wd, status)
+            del wg, wu, wd
+        wr = W.router_weights(cfg_id, "cuda", l).contiguous()
+        b = torch.from_numpy(W.router_bias(cfg_id, l)).cuda()
+        layers.append(coli.MoELayer(H, I, E, K, wr, experts, shared, b))
+        if l % 10 == 9:
+            log(f"[bench] stack: {l + 1} layers resident")
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    q_ms = sum(a.elapsed_time(b) for a, b in qev)
+    q_bytes = E * (3 * H * I * 4 + nb)  # fp32 weights in, blob out
+    pool = W.token_pool(cfg_id, pool_n * T, "cuda").reshape(pool_n, T, H).contiguous()
+    x = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    ws = torch.empty(layers[0].workspace_bytes(T, coli.COLI_DECODE), dtype=torch.uint8,
+                     device="cuda")
+    idx = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in range(NL)]
+    gates = [torch.empty((T, K), dtype=torch.float32, device="cuda") for _ in range(NL)]
+    callers = [Caller(coli, layers[l], coli.COLI_DECODE, x, y, ws, idx[l], gates[l])
+               for l in range(NL)]
+
+    def step(i):
+        x.copy_(pool[i % pool_n])
+        for l in range(NL):
+            callers[l]()
+            if l + 1 < NL:
+                coli.coli_rmsnorm_f32(y, x, 1e-6)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    U = [int(torch.unique(t).numel()) for t in idx]
+    rbytes = E * H * (2 if c["router"] == "bf16" else 4)
+    step_bytes = sum(rbytes + (u + 1) * nb + 2 * T * H * 4 for u in U)
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "stack decode: ms per step (one batch of tokens through every layer); "
+                  "quantiser ms for one layer's routed experts",
+        "workload": f"stack: {NL} resident layers of H={H} I={I}, {E} experts top-{K} + 1 "
+                    f"shared, int4-g64 planar, Zipf router bias per layer, RMSNorm between "
+                    f"layers, T={T} fp32 tokens",
+        "resident_bytes": NL * (E + 1) * nb, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "unique_experts_per_layer": {"mean": round(sum(U) / NL, 1), "min": min(U),
+                                     "max": max(U)},
+        "hbm": {"bytes_per_step": step_bytes, "gbps": round(gbps, 1),
+                "frac": round(gbps / HBM_PEAK_GBS, 4)},
+        "quantiser": {"experts": E, "ms": round(q_ms, 3), "bytes": q_bytes,
+                      "gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+                      "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "data": "synthetic", "dtype": "f32",
+    }
 
 
 def build_layer_bias(coli, W, layers):

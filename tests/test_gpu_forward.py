@@ -205,16 +205,31 @@ def test_forward_deterministic_and_t0():
     assert y.shape == (0, 256)
 
 
-def test_rmsnorm_parity():
+# H = 6144 (8 float4 per thread), 256/1000 (1, ragged), 2048 (2), 4000 (4), 8192 (8,
+# full); 8196 (beyond the register rows), 6 (H % 4 != 0): the strided kernel
+@pytest.mark.parametrize("H", [6144, 256, 1000, 2048, 4000, 8192, 8196, 6])
+def test_rmsnorm_parity(H):
     import int4_grouped_expert_amd as coli
     g = torch.Generator(device="cuda").manual_seed(3)
-    x = torch.randn((9, 6144), generator=g, device="cuda") * 3.0
+    x = torch.randn((9, H), generator=g, device="cuda") * 3.0
     y = torch.empty_like(x)
     coli.coli_rmsnorm_f32(x, y, 1e-6)
     ref = oracle.rmsnorm(x.cpu().double().numpy(), 1e-6)
     assert_close(y.cpu().numpy(), ref, 1e-5, what="rmsnorm")
     coli.coli_rmsnorm_f32(x, x, 1e-6)  # in place
     assert torch.equal(x, y)
+
+
+def test_rmsnorm_unaligned_rows():
+    """Rows that are not 16-byte aligned take the strided kernel."""
+    import int4_grouped_expert_amd as coli
+    g = torch.Generator(device="cuda").manual_seed(4)
+    buf = torch.randn(5 * 512 + 1, generator=g, device="cuda")
+    x = buf[1:].view(5, 512)  # 4-byte offset
+    y = torch.empty((5, 512), device="cuda")
+    coli.coli_rmsnorm_f32(x, y, 1e-6)
+    ref = oracle.rmsnorm(x.cpu().double().numpy(), 1e-6)
+    assert_close(y.cpu().numpy(), ref, 1e-5, what="rmsnorm unaligned")
 
 
 def stack_check(cfg_id, nlayers, T, e2e_layers):
