@@ -359,7 +359,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4):
+def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
     """The 40-layer stack at T=8: all layers resident, RMSNorm between layers.
 
     Every expert of every layer is quantised by the library from its own seeded
@@ -368,7 +368,8 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4):
     of 8 tokens through the 40 layers; U per layer is measured on the last step."""
     import torch
     c = W.CONFIGS[cfg_id]
-    H, I, E, K, T, NL = c["H"], c["I"], c["E"], c["K"], c["T"], c["layers"]
+    H, I, E, K, T = c["H"], c["I"], c["E"], c["K"], c["T"]
+    NL = c["layers"] if layers is None else layers
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     layers, qev = [], []
     for l in range(NL):

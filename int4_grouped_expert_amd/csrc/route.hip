@@ -57,16 +57,47 @@ __device__ inline void load8(const void *base, size_t i, float out[8]) {
   }
 }
 
+// 8 consecutive router-row elements as loaded (bf16: one 16-byte word; fp32:
+// two), widened to fp32 only where used.
+template <bool kBf16>
+struct Raw8 {
+  uint4 v[kBf16 ? 1 : 2];
+};
+__device__ inline uint32_t u4_word(const uint4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+template <bool kBf16>
+__device__ inline Raw8<kBf16> load_raw8(const void *base, size_t i) {
+  Raw8<kBf16> r;
+  if (kBf16) {
+    r.v[0] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + i);
+  } else {
+    const float *f = reinterpret_cast<const float *>(base) + i;
+    r.v[0] = *reinterpret_cast<const uint4 *>(f);
+    r.v[kBf16 ? 0 : 1] = *reinterpret_cast<const uint4 *>(f + 4);
+  }
+  return r;
+}
+template <bool kBf16>
+__device__ inline float raw8_at(const Raw8<kBf16> &r, int k) {
+  if (kBf16) {
+    const uint32_t w = u4_word(r.v[0], k >> 1);
+    return __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+  return __uint_as_float(u4_word(r.v[(k >> 2) & (kBf16 ? 0 : 1)], k & 3));
+}
+
 // ---------------------------------------------------------------- logits (GEMV)
 // grid.x: groups of RW expert rows; grid.y: groups of TT tokens.  The block's 4
 // waves split H; a lane issues all loads of a batch of kB 8-column chunks
-// (router rows kept as raw bf16 or fp32, x as fp32) before using any, and the
-// wave partials meet in LDS in a fixed order.
+// (router rows kept as loaded, x as fp32) before using any, and the wave
+// partials meet in LDS in a fixed order.  kB = 3 covers a quarter of H = 6144
+// in one batch: one memory round trip.
 template <int RW, int TT, bool kXbf, bool kWbf>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const void *__restrict__ x, int T, int H, const void *__restrict__ wr,
     int E, const float *__restrict__ bias, float *__restrict__ logits) {
-  constexpr int kB = 2;
+  constexpr int kB = 3;
   __shared__ float part[4][RW][TT];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -80,16 +111,17 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[r][t] = 0.0f;
   for (int c0 = cb; c0 < ce; c0 += kB * kWave * 8) {
-    float wv[kB][RW][8], xv[kB][TT][8];
+    Raw8<kWbf> wv[kB][RW];
+    float xv[kB][TT][8];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
       const int c = c0 + (b * kWave + lane) * 8;
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
-        if (c < ce && e0 + r < E) load8<kWbf>(wr, size_t(e0 + r) * H + c, wv[b][r]);
+        if (c < ce && e0 + r < E) wv[b][r] = load_raw8<kWbf>(wr, size_t(e0 + r) * H + c);
         else
 #pragma unroll
-          for (int k = 0; k < 8; ++k) wv[b][r][k] = 0.0f;
+          for (int k = 0; k < (kWbf ? 1 : 2); ++k) wv[b][r].v[k] = uint4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
@@ -106,7 +138,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
         for (int t = 0; t < TT; ++t)
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc[r][t] = fmaf(wv[b][r][k], xv[b][t][k], acc[r][t]);
+          for (int k = 0; k < 8; ++k) acc[r][t] = fmaf(raw8_at(wv[b][r], k), xv[b][t][k], acc[r][t]);
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r)
