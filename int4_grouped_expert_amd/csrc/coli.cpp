@@ -273,12 +273,6 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
       return dev_status(launch_ffn_narrow(d, nb, r.logits, r.idx, r.gates,
                                           reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr));
     }
-    if (ev) (void)hipEventRecord(ev[0], s);
-    e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, L->router_bias, r.logits, s);
-    if (e != hipSuccess) return COLI_EDEVICE;
-    e = launch_route_decode(r, T, L->E, L->K, slotmap, s);
-    if (e != hipSuccess) return COLI_EDEVICE;
-    if (ev) (void)hipEventRecord(ev[1], s);
     BatchBufs bb;
     bb.xp = reinterpret_cast<uint16_t *>(ws + w.bxp);
     bb.xs = reinterpret_cast<float *>(ws + w.bxs);
@@ -286,8 +280,16 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
     bb.h16 = reinterpret_cast<uint16_t *>(ws + w.bh16);
     bb.hs = reinterpret_cast<float *>(ws + w.bhs);
     bb.slot = reinterpret_cast<float *>(ws + w.bslot);
+    if (ev) (void)hipEventRecord(ev[0], s);
+    // the router launch also writes x's staged rows for the batch GEMM
+    e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, L->router_bias, r.logits, s,
+                             bb.xp, bb.xs, prefill_layout(L->H, L->I).HP);
+    if (e != hipSuccess) return COLI_EDEVICE;
+    e = launch_route_decode(r, T, L->E, L->K, slotmap, s);
+    if (e != hipSuccess) return COLI_EDEVICE;
+    if (ev) (void)hipEventRecord(ev[1], s);
     e = launch_ffn_batch(d, reinterpret_cast<const float *>(x), T, r, bb,
-                         reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr);
+                         reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr, true);
     return dev_status(e);
   }
   if (wbf) {

@@ -34,6 +34,7 @@
 //   down: gate * (Wd h) in fp32 per slot row; combine_f32 sums a token's slots.
 #include "gemm_stream.h"
 #include "kernels.h"
+#include "stage_rows.h"
 
 #include <hip/hip_fp16.h>
 
@@ -61,46 +62,8 @@ __global__ __launch_bounds__(256) void split_rows(const float *__restrict__ src,
                                                   float *__restrict__ sc) {
   __shared__ float red[4];
   const int r = blockIdx.x;
-  const float *row = src + int64_t(r) * W;
-  float m = 0.0f;
-  for (int c = 4 * int(threadIdx.x); c < W; c += 4 * 256) {
-    const float4 v = *reinterpret_cast<const float4 *>(row + c);
-    m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  int ex = 0;
-  (void)frexpf(m, &ex);
-  const int e = m > 0.0f ? max(ex - 15, -140) : 0;
-  const float down = ldexpf(1.0f, -e);
-  if (threadIdx.x == 0) sc[r] = ldexpf(1.0f, e);
-  const int G = W / 64, runs = (WP / 64) * 8;
-  for (int i = threadIdx.x; i < runs; i += 256) {
-    const int g = i >> 3, c = i & 7;
-    uint4 hi = uint4{0u, 0u, 0u, 0u}, lo = hi;
-    if (g < G) {
-      const int o = 64 * g + 16 * (c >> 2) + 4 * (c & 3);
-      const float4 a = *reinterpret_cast<const float4 *>(row + o);
-      const float4 b = *reinterpret_cast<const float4 *>(row + o + 32);
-      // staged order o + {0, 2, 32, 34, 1, 3, 33, 35}
-      const float v[8] = {a.x, a.z, b.x, b.z, a.y, a.w, b.y, b.w};
-      uint32_t ph[4], pl[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float v0 = v[2 * k] * down, v1 = v[2 * k + 1] * down;
-        const _Float16 h0 = _Float16(v0), h1 = _Float16(v1);
-        ph[k] = pack_f16x2(h0, h1);
-        pl[k] = pack_f16x2(_Float16(v0 - float(h0)), _Float16(v1 - float(h1)));
-      }
-      hi = uint4{ph[0], ph[1], ph[2], ph[3]};
-      lo = uint4{pl[0], pl[1], pl[2], pl[3]};
-    }
-    *reinterpret_cast<uint4 *>(dst + int64_t(r) * WP + 8 * i) = hi;
-    *reinterpret_cast<uint4 *>(dst + (int64_t(rows) + r) * WP + 8 * i) = lo;
-  }
+  stage_row(src + int64_t(r) * W, W, WP, dst + int64_t(r) * WP, dst + (int64_t(rows) + r) * WP,
+            sc + r, red);
 }
 
 struct DecArgs {
@@ -449,7 +412,8 @@ hipError_t launch_dec_gemm(const LayerDev &L, const Routing &r, int T, const Dec
 }  // namespace
 
 hipError_t launch_ffn_batch(const LayerDev &L, const float *x, int T, const Routing &r,
-                            const BatchBufs &b, float *y, hipStream_t s, hipEvent_t *ev) {
+                            const BatchBufs &b, float *y, hipStream_t s, hipEvent_t *ev,
+                            bool x_staged) {
   const PrefillLayout pl = prefill_layout(L.H, L.I);
   const int64_t TK = int64_t(T) * L.K, R = TK + T;
   if (int64_t(2) * T * pl.HP * 2 >= (int64_t(1) << 31) || 2 * R * pl.IP * 2 >= (int64_t(1) << 31) ||
@@ -459,7 +423,7 @@ hipError_t launch_ffn_batch(const LayerDev &L, const float *x, int T, const Rout
   // sum over units of ceil(n_u / 32) <= TK / 32 + routed units + shared chunks
   const int64_t max_chunks = TK / kDMC + max_units + (T + kDMC - 1) / kDMC;
   if (ev) (void)hipEventRecord(ev[0], s);
-  split_rows<<<dim3(unsigned(T)), 256, 0, s>>>(x, T, L.H, pl.HP, b.xp, b.xs);
+  if (!x_staged) split_rows<<<dim3(unsigned(T)), 256, 0, s>>>(x, T, L.H, pl.HP, b.xp, b.xs);
   hipError_t e;
   {
     DecArgs da{b.xp, b.xs, b.hf, pl.HP, L.I, T, uint32_t(int64_t(2) * T * pl.HP * 2)};

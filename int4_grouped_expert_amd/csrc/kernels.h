@@ -84,9 +84,13 @@ hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
 
 // ---- route.hip ----------------------------------------------------------
 // logits[t, e] = x[t] . Wr[e] + b[e]; x fp32 (x_bf16 = 0) or bf16.
+// xp, xs (optional, fp32 x only): the decode batch's staged hi/lo rows of x
+// ([2T][HP] fp16, stage_rows.h) and row scales, written by extra blocks of the
+// same launch.
 hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
                                 const void *wr, int w_bf16, int E,
-                                const float *bias, float *logits, hipStream_t s);
+                                const float *bias, float *logits, hipStream_t s,
+                                uint16_t *xp = nullptr, float *xs = nullptr, int HP = 0);
 // Prefill router: bf16 x and bf16 Wr through MFMA, then the top-K.  part:
 // scratch for the K-split partial sums (part_bytes; a smaller split is used
 // when S * T * E floats do not fit).
@@ -159,8 +163,10 @@ struct BatchBufs {
 };
 // r: routing with 32-token M-chunk prefix (launch_route_decode).  ev: optional
 // (NULL or 4: start and stop of the gate/up step, of the down step).
+// x_staged: xp / xs already hold x's staged rows (launch_router_logits did them).
 hipError_t launch_ffn_batch(const LayerDev &L, const float *x, int T, const Routing &r,
-                            const BatchBufs &b, float *y, hipStream_t s, hipEvent_t *ev);
+                            const BatchBufs &b, float *y, hipStream_t s, hipEvent_t *ev,
+                            bool x_staged = false);
 
 // ---- rmsnorm.hip --------------------------------------------------------
 hipError_t launch_rmsnorm_f32(const float *x, float *y, int T, int H,

@@ -24,6 +24,7 @@
 #include <hip/hip_ext.h>
 
 #include "kernels.h"
+#include "stage_rows.h"
 #include "wave.h"
 
 namespace coli {
@@ -93,16 +94,28 @@ __device__ inline float raw8_at(const Raw8<kBf16> &r, int k) {
 // (router rows kept as loaded, x as fp32) before using any, and the wave
 // partials meet in LDS in a fixed order.  kB = 3 covers a quarter of H = 6144
 // in one batch: one memory round trip.
+//
+// With xp set (fp32 x), the TT blocks past the expert groups of each grid row
+// write the staged hi/lo rows of its tokens for the decode batch GEMM instead
+// (stage_rows.h), in the same launch.
 template <int RW, int TT, bool kXbf, bool kWbf>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const void *__restrict__ x, int T, int H, const void *__restrict__ wr,
-    int E, const float *__restrict__ bias, float *__restrict__ logits) {
+    int E, const float *__restrict__ bias, float *__restrict__ logits,
+    uint16_t *__restrict__ xp, float *__restrict__ xs, int HP) {
   constexpr int kB = 3;
   __shared__ float part[4][RW][TT];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int e0 = blockIdx.x * RW;
   const int t0 = blockIdx.y * TT;
+  if (!kXbf && e0 >= E) {
+    const int t = t0 + (e0 - ((E + RW - 1) / RW) * RW) / RW;
+    if (xp && t < T)
+      stage_row(reinterpret_cast<const float *>(x) + size_t(t) * H, H, HP,
+                xp + size_t(t) * HP, xp + (size_t(T) + t) * HP, xs + t, &part[0][0][0]);
+    return;
+  }
   const int Hq = ((H / 4 + 7) / 8) * 8;
   const int cb = wave * Hq, ce = min(H, cb + Hq);
   float acc[RW][TT];
@@ -576,18 +589,19 @@ size_t permute_chunk_ints(int T, int E) {
 hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
                                 const void *wr, int w_bf16, int E,
                                 const float *bias, float *logits,
-                                hipStream_t s) {
+                                hipStream_t s, uint16_t *xp, float *xs, int HP) {
+  if (x_bf16) xp = nullptr;  // the staged rows are made from fp32 x only
 #define COLI_ROUTER_CASE(RW, TT)                                                  \
   {                                                                               \
-    dim3 grid((E + RW - 1) / RW, (T + TT - 1) / TT);                             \
+    dim3 grid((E + RW - 1) / RW + (xp ? TT : 0), (T + TT - 1) / TT);             \
     if (x_bf16 && w_bf16)                                                         \
-      router_logits_kernel<RW, TT, true, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);  \
+      router_logits_kernel<RW, TT, true, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, xp, xs, HP);  \
     else if (x_bf16)                                                              \
-      router_logits_kernel<RW, TT, true, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits); \
+      router_logits_kernel<RW, TT, true, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, xp, xs, HP); \
     else if (w_bf16)                                                              \
-      router_logits_kernel<RW, TT, false, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits); \
+      router_logits_kernel<RW, TT, false, true><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, xp, xs, HP); \
     else                                                                          \
-      router_logits_kernel<RW, TT, false, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits);\
+      router_logits_kernel<RW, TT, false, false><<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, logits, xp, xs, HP);\
   }
   if (T <= 2) COLI_ROUTER_CASE(4, 2)
   else COLI_ROUTER_CASE(4, 4)
