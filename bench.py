@@ -363,28 +363,37 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
     """The 40-layer stack at T=8: all layers resident, RMSNorm between layers.
 
     Every expert of every layer is quantised by the library from its own seeded
-    N(0, 0.02) draw; the 256 routed experts of layer 0 time the quantiser (events
-    around each coli_quant_expert call, the draws outside).  A step feeds one batch
+    N(0, 0.02) draw; the 256 routed experts of layer 0 time the quantiser (all
+    drawn first, then quantised back to back between one pair of events).  A step feeds one batch
     of 8 tokens through the 40 layers; U per layer is measured on the last step."""
     import torch
     c = W.CONFIGS[cfg_id]
     H, I, E, K, T = c["H"], c["I"], c["E"], c["K"], c["T"]
     NL = c["layers"] if layers is None else layers
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    layers, qev = [], []
+    layers = []
+    # the quantiser: layer 0's routed experts, drawn first (fp32, all resident),
+    # then quantised back to back between one pair of events
+    experts0, shared0, nb = coli.alloc_layer_blobs(H, I, E)
+    draws = [W.expert_weights(cfg_id, e, "cuda", 0) for e in range(E)]
+    torch.cuda.synchronize()
+    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    q0.record()
+    for e in range(E):
+        coli.coli_quant_expert(experts0.data_ptr() + e * nb, H, I, *draws[e], status)
+    q1.record()
+    torch.cuda.synchronize()
+    q_ms = q0.elapsed_time(q1)
+    del draws
+    torch.cuda.empty_cache()
     for l in range(NL):
-        experts, shared, nb = coli.alloc_layer_blobs(H, I, E)
+        experts, shared, nb = (experts0, shared0, nb) if l == 0 else coli.alloc_layer_blobs(H, I, E)
         for e in range(E + 1):
+            if l == 0 and e < E:
+                continue
             wg, wu, wd = W.expert_weights(cfg_id, e, "cuda", l)
             ptr = shared.data_ptr() if e == E else experts.data_ptr() + e * nb
-            if l == 0 and e < E:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                ev[0].record()
-                coli.coli_quant_expert(ptr, H, I, wg, wu, wd, status)
-                ev[1].record()
-                qev.append(ev)
-            else:
-                coli.coli_quant_expert(ptr, H, I, wg, wu, wd, status)
+            coli.coli_quant_expert(ptr, H, I, wg, wu, wd, status)
             del wg, wu, wd
         wr = W.router_weights(cfg_id, "cuda", l).contiguous()
         b = torch.from_numpy(W.router_bias(cfg_id, l)).cuda()
@@ -393,7 +402,6 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
             log(f"[bench] stack: {l + 1} layers resident")
     torch.cuda.synchronize()
     assert int(status.item()) == 0
-    q_ms = sum(a.elapsed_time(b) for a, b in qev)
     q_bytes = E * (3 * H * I * 4 + nb)  # fp32 weights in, blob out
     pool = W.token_pool(cfg_id, pool_n * T, "cuda").reshape(pool_n, T, H).contiguous()
     x = torch.empty((T, H), dtype=torch.float32, device="cuda")

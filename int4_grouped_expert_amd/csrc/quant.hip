@@ -10,9 +10,11 @@
 // output bytes 4j..4j+3 are complete in registers and leave as one 32-bit
 // store; a team writes its group's 32 bytes contiguously and a wave covers 8
 // groups.  amax and the non-finite flag are reduced over the team with lane
-// shuffles.  Bit-exactness: s = amax / 7.0f and w / s are IEEE fp32 divides
-// (this translation unit is compiled without fast-math and with fp32
-// denormals preserved), rint is round-half-to-even (v_rndne_f32).
+// shuffles.  Bit-exactness: s = amax / 7.0f is an IEEE fp32 divide (this
+// translation unit is compiled without fast-math and with fp32 denormals
+// preserved), rint is round-half-to-even (v_rndne_f32), and each nibble is
+// rint(fl32(w / s)): through a reciprocal product where that provably rounds
+// the same way, else through the IEEE divide (near_half below).
 #include "kernels.h"
 
 namespace coli {
@@ -32,10 +34,21 @@ __device__ inline int team_or(int v) {
   return v;
 }
 
-__device__ inline uint32_t nibble(float w, float s) {
-  float q = __builtin_rintf(w / s);
-  q = fminf(fmaxf(q, -8.0f), 7.0f);
+__device__ inline uint32_t nibble_of(float quot) {
+  const float q = fminf(fmaxf(__builtin_rintf(quot), -8.0f), 7.0f);
   return uint32_t(int(q) + 8);
+}
+
+// rint(fl32(w / s)) without a divide for almost every element.  qa = w * rcp(s)
+// is within 3 ulp of 8, about 2.4e-6, of the exact quotient when |w / s| <= 8
+// and s is a normal number away from the range ends (v_rcp_f32: 1 ulp).  Every
+// half-integer up to 8.5 is an fp32 number, so when qa lies farther than 2^-17
+// from all of them, the exact quotient and its fp32 rounding lie on the same
+// side of each, and the three round to the same integer.  The rest (a guard
+// band of about 1.5e-5 per unit of quotient) take the IEEE divide.
+__device__ inline bool near_half(float qa) {
+  const float t = fabsf(qa);
+  return fabsf((t - floorf(t)) - 0.5f) < 0x1p-17f;
 }
 
 template <bool kVec>
@@ -77,12 +90,31 @@ __global__ __launch_bounds__(kBlock) void quant_int4_g64_kernel(
   if (!live) return;
 
   const float s = bad ? __builtin_nanf("") : amax / 7.0f;
+  const bool quant = !bad && s != 0.0f;
+  const bool fast = s >= 0x1p-125f && s <= 0x1p125f;  // false for NaN
+  const float rs = __builtin_amdgcn_rcpf(fast ? s : 1.0f);
+  float ql[4], qh[4];
+  bool slow = quant && !fast;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ql[i] = lo[i] * rs;
+    qh[i] = hi[i] * rs;
+    slow |= quant && (near_half(ql[i]) || near_half(qh[i]));
+  }
+  // wave-uniform branch: the divides run only in waves that need them
+  if (__builtin_amdgcn_ballot_w64(slow) != 0 && slow) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ql[i] = lo[i] / s;
+      qh[i] = hi[i] / s;
+    }
+  }
   uint32_t word = 0x88888888u;
-  if (!bad && s != 0.0f) {
+  if (quant) {
     word = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      word |= (nibble(lo[i], s) | (nibble(hi[i], s) << 4)) << (8 * i);
+      word |= (nibble_of(ql[i]) | (nibble_of(qh[i]) << 4)) << (8 * i);
   }
   *reinterpret_cast<uint32_t *>(packed + r * G * 32 + g * 32 + 4 * j) = word;
   if (j == 0) {

@@ -70,6 +70,32 @@ def test_ties_and_scales():
     assert_same(w)
 
 
+def test_quotients_near_rounding_boundaries():
+    """Quotients w/s within a few ulp of every half-integer in [-6.5, 6.5] (inside the
+    band where the library divides) and about 2^-17 from it (the edge of that band),
+    for scales spanning 2^-60 .. 2^60: every nibble is rint(fl32(w/s)) as the oracle
+    rounds it."""
+    rng = np.random.default_rng(5)
+    rows = 4096
+    amax = rng.uniform(1e-6, 1e3, size=rows).astype(np.float32)
+    amax[:1024] = (2.0 ** rng.integers(-60, 60, size=1024) *
+                   rng.uniform(1.0, 2.0, size=1024)).astype(np.float32)
+    s = (amax / np.float32(7.0)).astype(np.float32)
+    half = rng.integers(-7, 7, size=(rows, 63)).astype(np.float64) + 0.5
+    band = np.where(rng.random((rows, 63)) < 0.5, -1.0, 1.0) * 2.0 ** -17
+    band *= rng.uniform(0.9, 1.1, size=(rows, 63))
+    quot = np.where(np.arange(rows)[:, None] < rows // 4, half + band, half)
+    t = (quot * s[:, None].astype(np.float64)).astype(np.float32)
+    ulps = rng.integers(-6, 7, size=(rows, 63)).astype(np.int32)
+    ulps[: rows // 4] = 0
+    t = (t.view(np.int32) + ulps).view(np.float32)
+    w = np.empty((rows, 64), dtype=np.float32)
+    w[:, 0] = amax
+    w[:, 1:] = t
+    assert np.all(np.abs(w[:, 1:]) < amax[:, None])
+    assert_same(w)
+
+
 def test_subnormal_and_extreme_magnitudes():
     rng = np.random.default_rng(2)
     bits = rng.integers(1, 0x7F7FFFFF, size=(256, 64), dtype=np.uint32)
