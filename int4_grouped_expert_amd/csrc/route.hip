@@ -541,6 +541,61 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(Routing r, int T, in
   }
 }
 
+// Decode with T <= 64 and T * K <= kSmallPairs: one block, one bitmap chunk.
+// The top-K writes the ids to LDS; per-expert token bitmaps give the counts,
+// the stable placement (rank = offset + tokens before t with that expert) and
+// the (unit, token) -> h-row map directly, with no read-back of global memory.
+constexpr int kSmallPairs = 2048;
+
+__global__ __launch_bounds__(1024) void route_decode_small(Routing r, int T, int E, int K,
+                                                           int32_t *__restrict__ slotmap) {
+  __shared__ int32_t sidx[kSmallPairs];
+  __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
+  __shared__ int cursor[COLI_MAX_EXPERTS];
+  __shared__ int uidx[COLI_MAX_EXPERTS];
+  __shared__ int ulist[COLI_MAX_EXPERTS];
+  __shared__ int wave_tot[16];
+  __shared__ int total;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) bm[e] = 0ull;
+  for (int t = wave; t < T; t += blockDim.x / kWave)
+    wave_topk(r.logits + size_t(t) * E, E, K, lane, sidx + t * K, r.gates + size_t(t) * K);
+  __syncthreads();
+  for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
+    const int e = sidx[p];
+    r.idx[p] = e;
+    if (e >= 0 && e < E) atomicOr(&bm[e], 1ull << (p / K));
+  }
+  __syncthreads();
+  const int ce = threadIdx.x < E ? __popcll(bm[threadIdx.x]) : 0;
+  int excl = 0;
+  finish_counts(r, T, K, E, ce, wave_tot, &total, &excl, uidx);
+  const int nr = total;
+  if (threadIdx.x < E) {
+    cursor[threadIdx.x] = excl;
+    if (ce > 0) ulist[uidx[threadIdx.x]] = threadIdx.x;
+  }
+  // M-chunk prefix over units in unique order (ascending expert id)
+  const int nch = (threadIdx.x < E && ce > 0) ? (ce + kDecMC - 1) / kDecMC : 0;
+  const int cpos = block_exclusive_scan(nch, wave_tot, &total);
+  if (threadIdx.x < E && ce > 0) r.chunk[uidx[threadIdx.x]] = cpos;
+  if (threadIdx.x == 0) {
+    r.chunk[nr] = total;
+    r.chunk[nr + 1] = total + (T + kDecMC - 1) / kDecMC;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
+    const int e = sidx[p], t = p / K;
+    if (e < 0 || e >= E) continue;
+    r.perm[cursor[e] + __popcll(bm[e] & ((1ull << t) - 1ull))] = p;
+  }
+  for (int i = threadIdx.x; i < nr * T; i += blockDim.x) {
+    const int u = i / T, t = i - u * T, e = ulist[u];
+    const unsigned long long b = bm[e];
+    slotmap[i] = (b >> t) & 1ull ? cursor[e] + __popcll(b & ((1ull << t) - 1ull)) : -1;
+  }
+}
+
 // Large T: per-chunk counts -> r.chunk[c*E + e].
 __global__ __launch_bounds__(256) void permute_count(Routing r, int T, int K, int E) {
   __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
@@ -646,7 +701,10 @@ hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
 
 hipError_t launch_route_decode(const Routing &r, int T, int E, int K, int32_t *slotmap,
                                hipStream_t s) {
-  route_decode_kernel<<<1, 1024, 0, s>>>(r, T, E, K, slotmap);
+  if (T <= 64 && T * K <= kSmallPairs)
+    route_decode_small<<<1, 1024, 0, s>>>(r, T, E, K, slotmap);
+  else
+    route_decode_kernel<<<1, 1024, 0, s>>>(r, T, E, K, slotmap);
   return hipGetLastError();
 }
 

@@ -66,8 +66,10 @@ def oracle_check(cfg_id, L, x, y, idx, gates, mode, rows=None, check_bytes=True,
     return assert_close(yg, yr, PRE_TOL, floor_one=False, what="y")
 
 
+# T <= 64 takes the one-chunk decode route (T = 64 sets bit 63 of its token
+# bitmaps), T = 65 and 256 the chunked one
 @pytest.mark.parametrize("cfg_id,T", [(0, 1), (0, 7), (101, 40), (102, 5), (103, 3), (106, 3),
-                                      (0, 256), (101, 1)])
+                                      (0, 256), (101, 1), (101, 64), (101, 65)])
 def test_decode_small(cfg_id, T):
     log(f"decode small cfg {cfg_id} T {T}")
     L = layer(cfg_id)
