@@ -351,6 +351,16 @@ def main():
             "frac": round(b32 / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "stage_ms": [round(s, 4) for s in d32["stage_ms"]]}
         del zl
+        log("[bench] tiny T=1")
+        tl, _ = build_layer(coli, W, 0, 1)
+        dt = run_decode(coli, W, tl, 0, 1, max(1000, args.steps // 3), 100)
+        mst = dt["ms"] / dt["steps"]
+        result["tiny_t1"] = {
+            "workload": "tiny: H=256 I=128, 16 experts top-4 + 1 shared, T=1 fp32 token "
+                        "(launch and latency bound; no roofline)",
+            "us_per_step": round(mst * 1e3, 2), "tokens_per_s": round(1.0 / (mst * 1e-3), 1),
+            "stage_us": [round(1e3 * x, 2) for x in dt["stage_ms"]]}
+        del tl
         log("[bench] prefill T=2048")
         result["prefill"] = run_prefill(coli, W, layers[0])
     if not args.no_cpu_baseline:
