@@ -248,7 +248,8 @@ int coli_moe_forward_timed(const coli_moe_layer *L, coli_mode mode,
 /*
  * RMSNorm with unit weight between stacked layers:
  *   y[t] = x[t] / sqrt(mean(x[t]^2) + eps), fp32 [T, H]; x == y allowed.
- * Errors: EINVAL (NULL, eps < 0 or not finite), ESHAPE.  T == 0 is a no-op.
+ * Errors: EINVAL (NULL, eps < 0 or not finite), ESHAPE, EALIGN (x or y not
+ * 4-byte aligned).  T == 0 is a no-op.
  */
 int coli_rmsnorm_f32(const float *x, float *y, int T, int H, float eps,
                      void *stream);
