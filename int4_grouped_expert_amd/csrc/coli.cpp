@@ -209,6 +209,13 @@ int coli_expert_views(const uint8_t *blob, int H, int I, coli_q4 *gate, coli_q4 
   return COLI_OK;
 }
 
+int coli_expert_finish(uint8_t *blob, int H, int I, void *stream) {
+  if (!blob) return COLI_EINVAL;
+  if (H < 1 || H > COLI_MAX_DIM || I < 1 || I > COLI_MAX_DIM) return COLI_ESHAPE;
+  if (!aligned(blob, 256)) return COLI_EALIGN;
+  return dev_status(launch_expert_finish(blob, blob_layout(H, I), H, I, as_stream(stream)));
+}
+
 size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int T, coli_mode mode) {
   if (!L || !layer_shape_ok(L->H, L->I, L->E, L->K)) return 0;
   if (mode != COLI_DECODE && mode != COLI_PREFILL) return 0;

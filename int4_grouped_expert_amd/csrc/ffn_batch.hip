@@ -125,17 +125,18 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
     if (kGateUp) {
       row = wrow0;
       qsec = uint32_t(jn == 0 ? L.lay.gq : L.lay.uq);
-      ssec = uint32_t(jn == 0 ? L.lay.gs : L.lay.us);
+      ssec = uint32_t(jn == 0 ? L.lay.gsT : L.lay.usT);
     } else {
       row = wrow0 + 32 * jn;
       qsec = uint32_t(L.lay.dq);
-      ssec = uint32_t(L.lay.ds);
+      ssec = uint32_t(L.lay.dsT);
     }
     // load a of lane (h, n): row 8a + n%8, part 2 (n / 8) + h (past G in the
     // last super-step: the next bytes of the blob, scale 0)
     xoff[jn] = qsec + uint32_t(row + (n & 7)) * rowB + 16u * uint32_t(2 * (n >> 3) + h);
-    // scales of row n: groups 4 ss .. 4 ss + 3 (both lane halves)
-    soff[jn] = ssec + uint32_t(row + n) * uint32_t(G) * 4u;
+    // scales of row n, group-major: group g at soff + g * rows * 4 (both lane
+    // halves; one load covers 32 consecutive rows, a single cache line)
+    soff[jn] = ssec + uint32_t(row + n) * 4u;
   }
   // DMA roles: instruction i of this wave fills staged rows 16w + 2i, +1
   // (lane: row + lane/32, LDS chunk lane%32)
@@ -161,21 +162,16 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
       for (int a4 = 0; a4 < 4; ++a4)
         R[jn][a4] = bload16(rw, xoff[jn], 128u * uint32_t(ss) + 8u * uint32_t(a4) * rowB);
   };
+  // scales of groups 4 ss .. 4 ss + 3 from the group-major sections: four
+  // 4-byte loads per fragment, each one cache line for the wave (groups past
+  // the row end read zeros through the empty offset)
+  const uint32_t srow4 = uint32_t(kGateUp ? L.I : L.H) * 4u;
   auto load_s = [&](int ss, float (&F)[2][4]) {
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn) {
-      const uint32_t o = soff[jn] + 16u * uint32_t(ss);
-      if (4 * ss + 3 < G) {
-        const uint4 w = bload16(rw, o, 0);
-        F[jn][0] = __uint_as_float(w.x);
-        F[jn][1] = __uint_as_float(w.y);
-        F[jn][2] = __uint_as_float(w.z);
-        F[jn][3] = __uint_as_float(w.w);
-      } else {
+    for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) F[jn][c] = bload4f(rw, 4 * ss + c < G ? o + 4u * c : kOff);
-      }
-    }
+      for (int c = 0; c < 4; ++c)
+        F[jn][c] = bload4f(rw, 4 * ss + c < G ? soff[jn] + uint32_t(4 * ss + c) * srow4 : kOff);
   };
 
   f32x16 acc[2];

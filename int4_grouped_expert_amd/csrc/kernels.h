@@ -23,7 +23,9 @@ inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // Offsets of the six sections of an expert blob (see coli.h).
 struct BlobLayout {
-  size_t gq, uq, dq, gs, us, ds, bytes;
+  size_t gq, uq, dq, gs, us, ds;
+  size_t gsT, usT, dsT;  // the scales again, group-major ([G][rows]; coli_expert_finish)
+  size_t bytes;
   int64_t GH, GI;  // groups per row of gate/up (input H) and of down (input I)
 };
 inline BlobLayout blob_layout(int H, int I) {
@@ -37,6 +39,9 @@ inline BlobLayout blob_layout(int H, int I) {
   b.gs = o; o += align256(size_t(I) * b.GH * 4);
   b.us = o; o += align256(size_t(I) * b.GH * 4);
   b.ds = o; o += align256(size_t(H) * b.GI * 4);
+  b.gsT = o; o += align256(size_t(I) * b.GH * 4);
+  b.usT = o; o += align256(size_t(I) * b.GH * 4);
+  b.dsT = o; o += align256(size_t(H) * b.GI * 4);
   b.bytes = o;
   return b;
 }
@@ -167,6 +172,10 @@ struct BatchBufs {
 hipError_t launch_ffn_batch(const LayerDev &L, const float *x, int T, const Routing &r,
                             const BatchBufs &b, float *y, hipStream_t s, hipEvent_t *ev,
                             bool x_staged = false);
+
+// Group-major copies of a blob's three scale sections (gs -> gsT etc.).
+hipError_t launch_expert_finish(uint8_t *blob, const BlobLayout &lay, int H, int I,
+                                hipStream_t s);
 
 // ---- rmsnorm.hip --------------------------------------------------------
 hipError_t launch_rmsnorm_f32(const float *x, float *y, int T, int H,

@@ -123,7 +123,44 @@ __global__ __launch_bounds__(kBlock) void quant_int4_g64_kernel(
   }
 }
 
+// Scales [rows][G] -> [G][rows] through 32 x 33 LDS tiles (coalesced reads
+// and writes).  Block (32, 8): tile (blockIdx.x: groups, blockIdx.y: rows).
+__global__ __launch_bounds__(256) void scales_group_major(const float *__restrict__ src,
+                                                          float *__restrict__ dst,
+                                                          int rows, int G) {
+  __shared__ float tile[32][33];
+  const int g0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x, ty = threadIdx.y;
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    const int r = r0 + ty + i, g = g0 + tx;
+    if (r < rows && g < G) tile[ty + i][tx] = src[int64_t(r) * G + g];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    const int g = g0 + ty + i, r = r0 + tx;
+    if (g < G && r < rows) dst[int64_t(g) * rows + r] = tile[tx][ty + i];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_expert_finish(uint8_t *blob, const BlobLayout &lay, int H, int I,
+                                hipStream_t s) {
+  struct {
+    size_t src, dst;
+    int rows, G;
+  } m[3] = {{lay.gs, lay.gsT, I, int(lay.GH)}, {lay.us, lay.usT, I, int(lay.GH)},
+            {lay.ds, lay.dsT, H, int(lay.GI)}};
+  for (const auto &x : m) {
+    const dim3 grid(unsigned((x.G + 31) / 32), unsigned((x.rows + 31) / 32));
+    scales_group_major<<<grid, dim3(32, 8), 0, s>>>(reinterpret_cast<const float *>(blob + x.src),
+                                                     reinterpret_cast<float *>(blob + x.dst),
+                                                     x.rows, x.G);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
                                  uint8_t *packed, float *scales,

@@ -98,6 +98,11 @@ def device_sections(blob: np.ndarray, H: int, I: int) -> dict:
     for name, rows, G in (("gs", I, GH), ("us", I, GH), ("ds", H, GI)):
         out[name] = blob[o:o + rows * G * 4].view(np.float32).reshape(rows, G)
         o += a256(rows * G * 4)
+    # the same scales group-major ([G][rows])
+    for name, rows, G in (("gsT", I, GH), ("usT", I, GH), ("dsT", H, GI)):
+        out[name] = blob[o:o + rows * G * 4].view(np.float32).reshape(G, rows)
+        o += a256(rows * G * 4)
+    assert o == blob.size, (o, blob.size)
     return out
 
 
@@ -117,6 +122,8 @@ def oracle_expert(cfg_id: int, e: int, layer: int = 0, device="cuda",
             assert np.array_equal(dev[k], ref[k]), (cfg_id, e, k)
         for k in ("gs", "us", "ds"):
             assert np.array_equal(dev[k].view(np.uint32), ref[k].view(np.uint32)), (cfg_id, e, k)
+            assert np.array_equal(dev[k + "T"].view(np.uint32), ref[k].T.view(np.uint32)), \
+                (cfg_id, e, k + "T")
     return ex
 
 

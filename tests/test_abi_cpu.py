@@ -38,9 +38,10 @@ def test_format_sizes():
     assert coli.coli_int4_g64_packed_bytes(3, 65) == 3 * 2 * 32
     assert coli.coli_int4_g64_packed_bytes(0, 10) == 0
     assert coli.coli_int4_g64_packed_bytes(4, 0) == 0
-    # 21,233,664 bytes per expert at H=6144, I=2048 (nibbles + fp32 scales)
-    assert coli.coli_expert_blob_bytes(6144, 2048) == 21233664
-    assert coli.coli_expert_blob_bytes(256, 128) == 55296
+    # 21,233,664 bytes per expert at H=6144, I=2048 (nibbles + fp32 scales), plus
+    # the scales again group-major (3 x 786,432)
+    assert coli.coli_expert_blob_bytes(6144, 2048) == 21233664 + 3 * 786432
+    assert coli.coli_expert_blob_bytes(256, 128) == 55296 + 3 * 2048
     assert coli.coli_expert_blob_bytes(0, 128) == 0
 
 
@@ -51,6 +52,14 @@ def test_expert_views_offsets():
     assert gs - base == 3 * 6291456 and us - gs == 786432 and ds - us == 786432
     for a in (gq, gs, uq, us, dq, ds):
         assert (a - base) % 256 == 0
+
+
+def test_expert_finish_rejects_before_launch():
+    L = coli.lib
+    assert L.coli_expert_finish(None, 256, 128, None) == coli.COLI_EINVAL
+    assert L.coli_expert_finish(ctypes.c_void_p(1 << 40), 0, 128, None) == coli.COLI_ESHAPE
+    assert L.coli_expert_finish(ctypes.c_void_p(1 << 40), 256, 1 << 20, None) == coli.COLI_ESHAPE
+    assert L.coli_expert_finish(ctypes.c_void_p((1 << 40) + 64), 256, 128, None) == coli.COLI_EALIGN
 
 
 def test_workspace_bytes():

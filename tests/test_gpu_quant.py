@@ -96,6 +96,25 @@ def test_quotients_near_rounding_boundaries():
     assert_same(w)
 
 
+@pytest.mark.parametrize("H,I", [(200, 72), (64, 33), (6144, 2048)])
+def test_expert_finish_group_major_copies(H, I):
+    """coli_quant_expert fills the blob's group-major scale copies: sT[g][o] = s[o][g]."""
+    import int4_grouped_expert_amd as coli
+    from tests.harness import device_sections
+    blob = torch.zeros(coli.coli_expert_blob_bytes(H, I), dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(H * 7 + I)
+    wg = torch.randn((I, H), generator=g, device="cuda")
+    wu = torch.randn((I, H), generator=g, device="cuda")
+    wd = torch.randn((H, I), generator=g, device="cuda")
+    coli.coli_quant_expert(blob.data_ptr(), H, I, wg, wu, wd)
+    torch.cuda.synchronize()
+    sec = device_sections(blob.cpu().numpy(), H, I)
+    for k in ("gs", "us", "ds"):
+        assert np.array_equal(sec[k + "T"].view(np.uint32), sec[k].T.view(np.uint32)), k
+    ref = oracle.quant_int4_g64(wd.cpu().numpy())
+    assert np.array_equal(sec["ds"].view(np.uint32), ref[1].view(np.uint32))
+
+
 def test_subnormal_and_extreme_magnitudes():
     rng = np.random.default_rng(2)
     bits = rng.integers(1, 0x7F7FFFFF, size=(256, 64), dtype=np.uint32)
