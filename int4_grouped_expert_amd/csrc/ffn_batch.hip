@@ -162,30 +162,44 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
       for (int a4 = 0; a4 < 4; ++a4)
         R[jn][a4] = bload16(rw, xoff[jn], 128u * uint32_t(ss) + 8u * uint32_t(a4) * rowB);
   };
-  // scales of groups 4 ss .. 4 ss + 3 from the group-major sections: four
-  // 4-byte loads per fragment, each one cache line for the wave (groups past
-  // the row end read zeros through the empty offset)
+  // scales of groups 4 ss .. 4 ss + 3 from the group-major sections: lane half
+  // h loads groups 2h and 2h + 1 (two 4-byte loads per fragment, each one cache
+  // line for the half; groups past the row end read zeros through the empty
+  // offset), and spread() passes each half's pair to the other
   const uint32_t srow4 = uint32_t(kGateUp ? L.I : L.H) * 4u;
-  auto load_s = [&](int ss, float (&F)[2][4]) {
+  auto load_s = [&](int ss, float (&Fr)[2][2]) {
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        F[jn][c] = bload4f(rw, 4 * ss + c < G ? soff[jn] + uint32_t(4 * ss + c) * srow4 : kOff);
+      for (int c = 0; c < 2; ++c) {
+        const int g = 4 * ss + 2 * h + c;
+        Fr[jn][c] = bload4f(rw, g < G ? soff[jn] + uint32_t(g) * srow4 : kOff);
+      }
+  };
+  auto spread = [&](const float (&Fr)[2][2], float (&F)[2][4]) {
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float mine = Fr[jn][c], theirs = __shfl_xor(mine, 32, kWave);
+        F[jn][c] = h ? theirs : mine;
+        F[jn][2 + c] = h ? mine : theirs;
+      }
   };
 
   f32x16 acc[2];
 #pragma unroll
   for (int jn = 0; jn < 2; ++jn) acc[jn] = f32x16{};
-  float F[2][4] = {}, Fn[2][4] = {};
+  float F[2][4] = {}, Fr[2][2] = {}, Frn[2][2] = {};
   uint4 R[2][4] = {};
   dma_a(0, g_st0);
   if (wvalid) {
-    load_s(0, F);
+    load_s(0, Fr);
     load_b(0, R);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
+  spread(Fr, F);
 
   uint32_t m1, m2;
   asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m1));
@@ -201,7 +215,7 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
 #pragma unroll
       for (int jn = 0; jn < 2; ++jn) exchange_rows(R[jn], D[jn]);
       const __amdgpu_buffer_rsrc_t rwn = more ? rw : rnull;
-      if (more) load_s(ss + 1, Fn);
+      if (more) load_s(ss + 1, Frn);
       // k-step k = 4 d + w: group d of the super-step, word w; lane half h
       // reads chunk 8 d + 4 h + w of its hi and lo rows
       f16x8 ahi, alo = {};
@@ -257,10 +271,7 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) F[jn][c] = Fn[jn][c];
+      spread(Frn, F);
     } else if (more) {
       dma_a(ss + 1, stn);
     }
