@@ -124,22 +124,30 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[r][t] = 0.0f;
   for (int c0 = cb; c0 < ce; c0 += kB * kWave * 8) {
+    // every load of the batch is issued before any is used: chunks past the
+    // slice read its first columns (zeroed below, before their use), rows
+    // past E and tokens past T re-read the last ones (never stored)
     Raw8<kWbf> wv[kB][RW];
     float xv[kB][TT][8];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
       const int c = c0 + (b * kWave + lane) * 8;
+      const int cl = c < ce ? c : cb;
 #pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        if (c < ce && e0 + r < E) wv[b][r] = load_raw8<kWbf>(wr, size_t(e0 + r) * H + c);
-        else
+      for (int r = 0; r < RW; ++r)
+        wv[b][r] = load_raw8<kWbf>(wr, size_t(min(e0 + r, E - 1)) * H + cl);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) load8<kXbf>(x, size_t(min(t0 + t, T - 1)) * H + cl, xv[b][t]);
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      if (c0 + (b * kWave + lane) * 8 >= ce) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
 #pragma unroll
           for (int k = 0; k < (kWbf ? 1 : 2); ++k) wv[b][r].v[k] = uint4{0u, 0u, 0u, 0u};
-      }
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        if (c < ce && t0 + t < T) load8<kXbf>(x, size_t(t0 + t) * H + c, xv[b][t]);
-        else
+        for (int t = 0; t < TT; ++t)
 #pragma unroll
           for (int k = 0; k < 8; ++k) xv[b][t][k] = 0.0f;
       }
@@ -172,26 +180,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 
 // ---------------------------------------------------------------- logits (one token)
 // grid: E + H/64 blocks of 256 threads.  Block e < E computes the logits of
-// expert e for every token (T <= 4): its 4 waves split H (16-byte loads, up to
-// kNB per lane issued before use, fp32 FMA), partial sums meet in a fixed
+// expert e for every token (T <= 4): its 4 waves split H, a lane reads 8
+// router columns per slot (kNB slots), fp32 FMA, partial sums meet in a fixed
 // order.  Block E + g writes group g of x as digit planes (see ffn_narrow.hip),
 // in parallel with the logit blocks: it finds the token's max |x| itself,
-// token t by wave t (lanes 0..15, four elements each).
-constexpr int kNB = 8;
-
-template <bool kWbf>
-__device__ inline void load4(const void *base, size_t i, float out[4]) {
-  if (kWbf) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(base) + i);
-    out[0] = __uint_as_float(v.x << 16);
-    out[1] = __uint_as_float(v.x & 0xFFFF0000u);
-    out[2] = __uint_as_float(v.y << 16);
-    out[3] = __uint_as_float(v.y & 0xFFFF0000u);
-  } else {
-    const float4 a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + i);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-  }
-}
+// token t by wave t (lanes 0..15, four elements each).  Every load of a round
+// is issued before any is used (slots past the end read a valid address and
+// are ignored at the use), so a round costs one memory round trip.
+constexpr int kNB = 4;   // 8-column router slots per lane and round
+constexpr int kXR = 8;   // float4 loads of x per thread and round (max scan)
 
 template <bool kWbf>
 __global__ __launch_bounds__(256) void router_narrow_kernel(
@@ -204,14 +201,29 @@ __global__ __launch_bounds__(256) void router_narrow_kernel(
     // blocks E .. E + H/64 - 1: the x digit planes of group blockIdx.x - E, in
     // parallel with the logit blocks (each finds the token maxima itself)
     const int g = int(blockIdx.x) - E;
+    const int el = 4 * lane, pos = aorder_pos(el);
+    const bool writer = wave < T && lane < 16;
+    float4 gv = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (writer) gv = *reinterpret_cast<const float4 *>(x + size_t(wave) * H + 64 * g + el);
     for (int t = 0; t < T; ++t) {
       float m = 0.0f;
       int bd = 0;
-      for (int c = 4 * int(threadIdx.x); c < H; c += 4 * int(blockDim.x)) {
-        const float4 xv = *reinterpret_cast<const float4 *>(x + size_t(t) * H + c);
-        m = fmaxf(fmaxf(m, fmaxf(fabsf(xv.x), fabsf(xv.y))), fmaxf(fabsf(xv.z), fabsf(xv.w)));
-        bd |= !__builtin_isfinite(xv.x) | !__builtin_isfinite(xv.y) | !__builtin_isfinite(xv.z) |
-              !__builtin_isfinite(xv.w);
+      for (int c0 = 4 * int(threadIdx.x); c0 < H; c0 += 4 * int(blockDim.x) * kXR) {
+        float4 xv[kXR];
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) {
+          const int c = c0 + 4 * int(blockDim.x) * j;
+          xv[j] = *reinterpret_cast<const float4 *>(x + size_t(t) * H + (c < H ? c : 0));
+        }
+        // slots past the end re-read the row's first elements: the max and
+        // the non-finite flag are unchanged by them
+#pragma unroll
+        for (int j = 0; j < kXR; ++j) {
+          m = fmaxf(fmaxf(m, fmaxf(fabsf(xv[j].x), fabsf(xv[j].y))),
+                    fmaxf(fabsf(xv[j].z), fabsf(xv[j].w)));
+          bd |= !__builtin_isfinite(xv[j].x) | !__builtin_isfinite(xv[j].y) |
+                !__builtin_isfinite(xv[j].z) | !__builtin_isfinite(xv[j].w);
+        }
       }
       m = wave_max(m);
       bd = __any(bd);
@@ -221,16 +233,14 @@ __global__ __launch_bounds__(256) void router_narrow_kernel(
       }
     }
     __syncthreads();
-    if (wave < T && lane < 16) {
+    if (writer) {
       const int t = wave;
       const float m = fmaxf(fmaxf(smax[0][t], smax[1][t]), fmaxf(smax[2][t], smax[3][t]));
       const bool bd = sbad[0][t] | sbad[1][t] | sbad[2][t] | sbad[3][t];
       const int ex = digit_exponent(m);
       if (g == 0 && lane == 0) nb.xsc[t] = bd ? __builtin_nanf("") : ldexpf(1.0f, -ex);
       const int GH = H / 64;
-      const int el = 4 * lane, pos = aorder_pos(el);
-      const float4 v = *reinterpret_cast<const float4 *>(x + size_t(t) * H + 64 * g + el);
-      const float va[4] = {v.x, v.y, v.z, v.w};
+      const float va[4] = {gv.x, gv.y, gv.z, gv.w};
       int d[4][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) digits4(va[i], ex, d[i]);
@@ -248,27 +258,33 @@ __global__ __launch_bounds__(256) void router_narrow_kernel(
   const int Hq = H / 4;
   const int cb = wave * Hq, ce = cb + Hq;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = cb + 4 * lane; c0 < ce; c0 += 4 * kWave * kNB) {
-    float wv[kNB][4];
+  for (int c0 = cb + 8 * lane; c0 < ce; c0 += 8 * kWave * kNB) {
+    Raw8<kWbf> wv[kNB];
+    int cc[kNB];
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
-      const int c = c0 + 4 * kWave * b;
-      if (c < ce) load4<kWbf>(wr, size_t(e) * H + c, wv[b]);
-      else
-#pragma unroll
-        for (int k = 0; k < 4; ++k) wv[b][k] = 0.0f;
+      const int c = c0 + 8 * kWave * b;
+      cc[b] = c < ce ? c : cb;
+      wv[b] = load_raw8<kWbf>(wr, size_t(e) * H + cc[b]);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (t >= T) break;
+      float4 xv[kNB][2];
 #pragma unroll
       for (int b = 0; b < kNB; ++b) {
-        const int c = c0 + 4 * kWave * b;
-        if (c >= ce) break;
-        const float4 xv = *reinterpret_cast<const float4 *>(x + size_t(t) * H + c);
-        const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+        const float *xp = x + size_t(t) * H + cc[b];
+        xv[b][0] = *reinterpret_cast<const float4 *>(xp);
+        xv[b][1] = *reinterpret_cast<const float4 *>(xp + 4);
+      }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[t] = fmaf(wv[b][k], xa[k], acc[t]);
+      for (int b = 0; b < kNB; ++b) {
+        const float xa[8] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
+                             xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w};
+        float a = acc[t];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a = fmaf(raw8_at(wv[b], k), xa[k], a);
+        acc[t] = c0 + 8 * kWave * b < ce ? a : acc[t];
       }
     }
   }
