@@ -178,21 +178,28 @@ typedef struct {
  * Size of one expert blob.  Layout (each section starts on a 256-byte
  * boundary): gate.q [I][GH*32] | up.q [I][GH*32] | down.q [H][GI*32] |
  * gate.s [I][GH] | up.s [I][GH] | down.s [H][GI] | gate.sT [GH][I] |
- * up.sT [GH][I] | down.sT [GI][H], with GH = ceil(H/64), GI = ceil(I/64).
+ * up.sT [GH][I] | down.sT [GI][H] | gate.sB [I8/8][GH][8] |
+ * up.sB [I8/8][GH][8] | down.sB [H8/8][GI][8], with GH = ceil(H/64),
+ * GI = ceil(I/64), I8 and H8 = I and H rounded up to a multiple of 8.
  * gate/up are [I, H] (input dim H); down is [H, I].  The .sT sections hold
- * the same scales group-major (see coli_expert_finish).
+ * the same scales group-major, the .sB sections blocked by 8 rows
+ * (sB[b][g][r] = s[8b + r][g], zero past the last row; see
+ * coli_expert_finish).
  * Returns 0 if H or I is outside [1, MAX_DIM].
  */
 size_t coli_expert_blob_bytes(int H, int I);
 
 /*
- * Fill the blob's group-major scale sections (gate.sT, up.sT, down.sT) from
- * its row-major ones: sT[g][o] = s[o][g], bit for bit.  Call it once the
+ * Fill the blob's group-major scale sections (gate.sT, up.sT, down.sT) and
+ * its 8-row blocked ones (gate.sB, up.sB, down.sB) from its row-major ones:
+ * sT[g][o] = s[o][g] and sB[o/8][g][o%8] = s[o][g], bit for bit (the padding
+ * rows of the last block are written as 0).  Call it once the
  * three matrices are in the blob (quantised by coli_quant_int4_g64 into the
  * coli_expert_views pointers, or written from stored bytes) and before the
  * blob is used by coli_moe_forward: the decode batch path (1 < T <= 256)
  * reads the scales group-major (one cache line per 32 rows and group), the
- * single-token and prefill paths row-major.  Asynchronous on `stream`.
+ * single-token path blocked (one 8-row item's groups are contiguous), the
+ * prefill path row-major.  Asynchronous on `stream`.
  * The blob is the layout above, of [P2] 权重转换's sections.
  * Errors: EINVAL (NULL), ESHAPE, EALIGN (blob not 256-byte aligned),
  * EDEVICE.

@@ -159,8 +159,8 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   __shared__ int32_t sidx[COLI_NARROW_MAX_K];
   __shared__ float sgate[COLI_NARROW_MAX_K];
   __shared__ float red[kGateupItems][kGateupMaxWaves][2][8];
-  // per wave, double-buffered: the item's group scales [frag][row][4 NC]
-  __shared__ __align__(16) float ssc[kGateupMaxWaves][2][2][8][4 * NC];
+  // per wave, double-buffered: the item's group scales [frag][4 NC groups][8 rows]
+  __shared__ __align__(16) float ssc[kGateupMaxWaves][2][2][32 * NC];
   const int lane = threadIdx.x % kW, wave = threadIdx.x / kW;
   const int nw = blockDim.x / kW;
   const int I = L.I, E = L.E, K = L.K;
@@ -190,11 +190,13 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   const float xs = nb.xsc[0];
 
   // item -> this lane's weight pointers (chunk 0 of its K slice; B lane group
-  // 4c + 2 kappa + q / 2) and its scale run: lane (r, i = 4 kappa + q) loads
-  // the 4 scales of chunk min(i, NC - 1) of row r (one contiguous 16 bytes).
+  // 4c + 2 kappa + q / 2) and its scale run.  The item's scales of the K slice
+  // are one contiguous run of 8 NC float4 in the 8-row blocked copy
+  // ([group][row]); lane l < 8 NC loads float4 l of it (the others re-load
+  // float4 0 and keep it).
   const size_t goff = size_t(wave) * NC * 4 + 2 * kap + q / 2;
-  const int si = 4 * kap + q;
-  const size_t soff = size_t(wave) * NC * 4 + 4 * size_t(si < NC ? si : NC - 1);
+  const int sl = lane < 8 * NC ? lane : 0;
+  const size_t soff = size_t(wave) * NC * 4 * 8 + 4 * size_t(sl);
   struct Ptrs {
     const uint8_t *wg, *wu;
     const float *sg, *su;
@@ -208,8 +210,8 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     Ptrs p;
     p.wg = blob + L.lay.gq + (row * GH + goff) * 32 + 16 * (q % 2);
     p.wu = blob + L.lay.uq + (row * GH + goff) * 32 + 16 * (q % 2);
-    p.sg = reinterpret_cast<const float *>(blob + L.lay.gs) + row * GH + soff;
-    p.su = reinterpret_cast<const float *>(blob + L.lay.us) + row * GH + soff;
+    p.sg = reinterpret_cast<const float *>(blob + L.lay.gsB) + size_t(rb) * GH * 8 + soff;
+    p.su = reinterpret_cast<const float *>(blob + L.lay.usB) + size_t(rb) * GH * 8 + soff;
     return p;
   };
 
@@ -245,9 +247,9 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     const int nx = it + int(gridDim.x) < n_items ? it + int(gridDim.x) : it;
     const Ptrs np = ptrs(nx);
     // this item's scales -> LDS, then the next item's scale loads
-    if (si < NC) {
-      *reinterpret_cast<float4 *>(&ssc[wave][buf][0][r][4 * si]) = scg;
-      *reinterpret_cast<float4 *>(&ssc[wave][buf][1][r][4 * si]) = scu;
+    if (lane < 8 * NC) {
+      *reinterpret_cast<float4 *>(&ssc[wave][buf][0][4 * lane]) = scg;
+      *reinterpret_cast<float4 *>(&ssc[wave][buf][1][4 * lane]) = scu;
     }
     scg = *reinterpret_cast<const float4 *>(np.sg);
     scu = *reinterpret_cast<const float4 *>(np.su);
@@ -256,7 +258,7 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sv[f][c] = ssc[wave][buf][f][r][4 * c + q];
+      for (int c = 0; c < NC; ++c) sv[f][c] = ssc[wave][buf][f][(4 * c + q) * 8 + r];
     float acc[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int f = 0; f < 2; ++f)
@@ -330,11 +332,12 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
     blob[u] = u < K ? L.experts + size_t(idx[u]) * L.lay.bytes : L.shared;
 
   // weights: the B lane's group (4 wave + 2 kappa + q / 2); scale: the result
-  // lane's slot (group 4 wave + q)
+  // lane's slot (group 4 wave + q), from the 8-row blocked copy, where a
+  // wave's 4 groups of an item are one 128-byte line
   const size_t goff = size_t(wave) * 4 + 2 * kap + q / 2;
   const size_t soff = size_t(wave) * 4 + q;
   auto loff = [&](int it) { return (size_t(it) * 8 + r) * GI + goff; };
-  auto sof = [&](int it) { return (size_t(it) * 8 + r) * GI + soff; };
+  auto sof = [&](int it) { return (size_t(it) * GI + soff) * 8 + r; };
   // Unit-major streaming: the block's items (at most kDownItems: b, b + G,
   // b + 2G) are visited unit by unit, so that at any time the whole grid reads
   // the rows of one or two experts (row-buffer locality).  Ring: the slots of
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
     for (int k = 0; k < kDownItems; ++k) {
       const int u = h < NU ? h : NU - 1;
       rw[h][k] = *reinterpret_cast<const uint4 *>(blob[u] + L.lay.dq + lo[k]);
-      rs[h][k] = reinterpret_cast<const float *>(blob[u] + L.lay.ds)[so[k]];
+      rs[h][k] = reinterpret_cast<const float *>(blob[u] + L.lay.dsB)[so[k]];
     }
   if (lane < 8) reinterpret_cast<uint32_t *>(zero)[lane] = 0u;
 
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
       const i32x4 b1 = unpack_half(rw[h][k].z, rw[h][k].w);
       const float sv = keep(rs[h][k]) * sa[u];
       rw[h][k] = *reinterpret_cast<const uint4 *>(blob[un] + L.lay.dq + lo[k]);
-      rs[h][k] = reinterpret_cast<const float *>(blob[un] + L.lay.ds)[so[k]];
+      rs[h][k] = reinterpret_cast<const float *>(blob[un] + L.lay.dsB)[so[k]];
       step_fence();
       i32x4 P = mfma_i8(a0, b0, c0);
       P = mfma_i8(a1, b1, P);

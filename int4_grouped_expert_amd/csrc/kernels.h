@@ -25,6 +25,7 @@ inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 struct BlobLayout {
   size_t gq, uq, dq, gs, us, ds;
   size_t gsT, usT, dsT;  // the scales again, group-major ([G][rows]; coli_expert_finish)
+  size_t gsB, usB, dsB;  // and blocked by 8 rows ([ceil(rows/8)][G][8]; coli_expert_finish)
   size_t bytes;
   int64_t GH, GI;  // groups per row of gate/up (input H) and of down (input I)
 };
@@ -42,6 +43,9 @@ inline BlobLayout blob_layout(int H, int I) {
   b.gsT = o; o += align256(size_t(I) * b.GH * 4);
   b.usT = o; o += align256(size_t(I) * b.GH * 4);
   b.dsT = o; o += align256(size_t(H) * b.GI * 4);
+  b.gsB = o; o += align256(size_t((I + 7) / 8) * 8 * b.GH * 4);
+  b.usB = o; o += align256(size_t((I + 7) / 8) * 8 * b.GH * 4);
+  b.dsB = o; o += align256(size_t((H + 7) / 8) * 8 * b.GI * 4);
   b.bytes = o;
   return b;
 }

@@ -144,6 +144,18 @@ __global__ __launch_bounds__(256) void scales_group_major(const float *__restric
   }
 }
 
+// Row-major scales [rows][G] -> blocked by 8 rows: dst[b][g][r] = src[8 b + r][g],
+// zero in the rows past `rows` of the last block.  One thread per element of dst.
+__global__ __launch_bounds__(256) void scales_blocked8(const float *__restrict__ src,
+                                                       float *__restrict__ dst, int rows, int G) {
+  const int64_t n = int64_t((rows + 7) / 8) * 8 * G;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t b = i / (int64_t(G) * 8), rem = i - b * int64_t(G) * 8;
+  const int64_t g = rem / 8, o = 8 * b + rem % 8;
+  dst[i] = o < rows ? src[o * G + g] : 0.0f;
+}
+
 }  // namespace
 
 hipError_t launch_expert_finish(uint8_t *blob, const BlobLayout &lay, int H, int I,
@@ -158,6 +170,13 @@ hipError_t launch_expert_finish(uint8_t *blob, const BlobLayout &lay, int H, int
     scales_group_major<<<grid, dim3(32, 8), 0, s>>>(reinterpret_cast<const float *>(blob + x.src),
                                                      reinterpret_cast<float *>(blob + x.dst),
                                                      x.rows, x.G);
+  }
+  const size_t bdst[3] = {lay.gsB, lay.usB, lay.dsB};
+  for (int k = 0; k < 3; ++k) {
+    const int64_t n = int64_t((m[k].rows + 7) / 8) * 8 * m[k].G;
+    scales_blocked8<<<dim3(unsigned((n + 255) / 256)), 256, 0, s>>>(
+        reinterpret_cast<const float *>(blob + m[k].src), reinterpret_cast<float *>(blob + bdst[k]),
+        m[k].rows, m[k].G);
   }
   return hipGetLastError();
 }

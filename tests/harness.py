@@ -102,8 +102,21 @@ def device_sections(blob: np.ndarray, H: int, I: int) -> dict:
     for name, rows, G in (("gsT", I, GH), ("usT", I, GH), ("dsT", H, GI)):
         out[name] = blob[o:o + rows * G * 4].view(np.float32).reshape(G, rows)
         o += a256(rows * G * 4)
+    # and blocked by 8 rows ([ceil(rows/8)][G][8], zero past the last row)
+    for name, rows, G in (("gsB", I, GH), ("usB", I, GH), ("dsB", H, GI)):
+        n = -(-rows // 8) * 8 * G
+        out[name] = blob[o:o + n * 4].view(np.float32).reshape(-1, G, 8)
+        o += a256(n * 4)
     assert o == blob.size, (o, blob.size)
     return out
+
+
+def blocked8(s: np.ndarray) -> np.ndarray:
+    """Row-major scales [rows, G] as [ceil(rows/8), G, 8]: b[i, g, r] = s[8 i + r, g]."""
+    rows, G = s.shape
+    pad = np.zeros((-(-rows // 8) * 8, G), dtype=s.dtype)
+    pad[:rows] = s
+    return np.ascontiguousarray(pad.reshape(-1, 8, G).transpose(0, 2, 1))
 
 
 def oracle_expert(cfg_id: int, e: int, layer: int = 0, device="cuda",
@@ -124,6 +137,8 @@ def oracle_expert(cfg_id: int, e: int, layer: int = 0, device="cuda",
             assert np.array_equal(dev[k].view(np.uint32), ref[k].view(np.uint32)), (cfg_id, e, k)
             assert np.array_equal(dev[k + "T"].view(np.uint32), ref[k].T.view(np.uint32)), \
                 (cfg_id, e, k + "T")
+            assert np.array_equal(dev[k + "B"].view(np.uint32),
+                                  blocked8(ref[k]).view(np.uint32)), (cfg_id, e, k + "B")
     return ex
 
 

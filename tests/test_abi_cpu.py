@@ -39,9 +39,9 @@ def test_format_sizes():
     assert coli.coli_int4_g64_packed_bytes(0, 10) == 0
     assert coli.coli_int4_g64_packed_bytes(4, 0) == 0
     # 21,233,664 bytes per expert at H=6144, I=2048 (nibbles + fp32 scales), plus
-    # the scales again group-major (3 x 786,432)
-    assert coli.coli_expert_blob_bytes(6144, 2048) == 21233664 + 3 * 786432
-    assert coli.coli_expert_blob_bytes(256, 128) == 55296 + 3 * 2048
+    # the scales again group-major and blocked by 8 rows (6 x 786,432)
+    assert coli.coli_expert_blob_bytes(6144, 2048) == 21233664 + 6 * 786432
+    assert coli.coli_expert_blob_bytes(256, 128) == 55296 + 6 * 2048
     assert coli.coli_expert_blob_bytes(0, 128) == 0
 
 

@@ -98,7 +98,8 @@ def test_quotients_near_rounding_boundaries():
 
 @pytest.mark.parametrize("H,I", [(200, 72), (64, 33), (6144, 2048)])
 def test_expert_finish_group_major_copies(H, I):
-    """coli_quant_expert fills the blob's group-major scale copies: sT[g][o] = s[o][g]."""
+    """coli_quant_expert fills the blob's group-major and 8-row blocked scale copies:
+    sT[g][o] = s[o][g], sB[o // 8][g][o % 8] = s[o][g] (zero past the last row)."""
     import int4_grouped_expert_amd as coli
     from tests.harness import device_sections
     blob = torch.zeros(coli.coli_expert_blob_bytes(H, I), dtype=torch.uint8, device="cuda")
@@ -109,8 +110,10 @@ def test_expert_finish_group_major_copies(H, I):
     coli.coli_quant_expert(blob.data_ptr(), H, I, wg, wu, wd)
     torch.cuda.synchronize()
     sec = device_sections(blob.cpu().numpy(), H, I)
+    from tests.harness import blocked8
     for k in ("gs", "us", "ds"):
         assert np.array_equal(sec[k + "T"].view(np.uint32), sec[k].T.view(np.uint32)), k
+        assert np.array_equal(sec[k + "B"].view(np.uint32), blocked8(sec[k]).view(np.uint32)), k
     ref = oracle.quant_int4_g64(wd.cpu().numpy())
     assert np.array_equal(sec["ds"].view(np.uint32), ref[1].view(np.uint32))
 
