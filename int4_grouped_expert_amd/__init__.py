@@ -231,7 +231,7 @@ def coli_rmsnorm_f32(x, y, eps=1e-6, stream=None):
 # ---------------------------------------------------------------- layer assembly
 
 def coli_expert_finish(blob_ptr: int, H: int, I: int, stream=None):
-    """The blob's group-major scale copies from its row-major scales."""
+    """The blob's group-major and 8-row blocked scale copies from its row-major scales."""
     return _check(lib.coli_expert_finish(ctypes.c_void_p(blob_ptr), H, I, _stream(stream)),
                   "coli_expert_finish")
 
@@ -239,7 +239,7 @@ def coli_expert_finish(blob_ptr: int, H: int, I: int, stream=None):
 def coli_quant_expert(blob_ptr: int, H: int, I: int, wg, wu, wd, status=None, stream=None,
                       finish=True):
     """Quantise fp32 gate [I,H], up [I,H], down [H,I] (device) into the blob at blob_ptr,
-    then (finish) fill its group-major scale copies."""
+    then (finish) fill its group-major and blocked scale copies."""
     views = coli_expert_views(blob_ptr, H, I)
     st = _stream(stream)
     for (qp, sp), w in zip(views, (wg, wu, wd)):
