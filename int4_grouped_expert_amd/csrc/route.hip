@@ -574,8 +574,26 @@ __global__ __launch_bounds__(1024) void route_decode_small(Routing r, int T, int
   __shared__ int total;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   for (int e = threadIdx.x; e < E; e += blockDim.x) bm[e] = 0ull;
-  for (int t = wave; t < T; t += blockDim.x / kWave)
-    wave_topk(r.logits + size_t(t) * E, E, K, lane, sidx + t * K, r.gates + size_t(t) * K);
+  const int nwv = int(blockDim.x) / kWave;
+  if (E > 128 && E <= 256 && T <= 4 * nwv) {
+    // the logits of all of the wave's tokens (at most 4) are loaded before the
+    // first selection, so the tokens share one load round trip (rows past T
+    // re-read row T - 1 and are not selected)
+    float lg[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = wave + nwv * j;
+      topk_load<4>(r.logits + size_t(t < T ? t : T - 1) * E, E, lane, lg[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = wave + nwv * j;
+      if (t < T) topk_select<4>(lg[j], E, K, lane, sidx + t * K, r.gates + size_t(t) * K);
+    }
+  } else {
+    for (int t = wave; t < T; t += nwv)
+      wave_topk(r.logits + size_t(t) * E, E, K, lane, sidx + t * K, r.gates + size_t(t) * K);
+  }
   __syncthreads();
   for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
     const int e = sidx[p];
