@@ -13,6 +13,7 @@ Every function names the passage it follows in the C source's comments:
   与.bin直映射实战", section 权重转换;
 * router top-K with renormalised gates -- page "Colibrì 深度解析", section 十一,
   and page "colibrì 路由遥测全解析", sections 分离计数与追踪 and 测试与 CI 保障;
+  the sigmoid router ("n_group=1 sigmoid + noaux_tc") of the same section 十一;
 * batch-union permute -- page "Colibrì 深度解析", section 四;
 * expert FFN, combine, RMSNorm -- the readings listed in the design doc.
 
@@ -66,12 +67,14 @@ def lib():
         L.orc_router_logits.argtypes = [p, i32, i32, i32, p, i32, i32, p, p]
         L.orc_topk.restype = i32
         L.orc_topk.argtypes = [p, i32, i32, i32, p, p]
+        L.orc_topk_sigmoid.restype = i32
+        L.orc_topk_sigmoid.argtypes = [p, i32, i32, i32, p, p, p]
         L.orc_permute.restype = i32
         L.orc_permute.argtypes = [p, i32, i32, i32, p, p, p, p]
         L.orc_expert_ffn.restype = None
         L.orc_expert_ffn.argtypes = [p, p, p, p, p, p, i32, i32, p, i32, p, p]
         L.orc_moe_forward.restype = i32
-        L.orc_moe_forward.argtypes = [p, i32, i32, i32, i32, i32, i32, p, i32, p,
+        L.orc_moe_forward.argtypes = [p, i32, i32, i32, i32, i32, i32, p, i32, p, i32,
                                       p, p, p, p, p]
         L.orc_rmsnorm.restype = None
         L.orc_rmsnorm.argtypes = [p, i32, i32, ctypes.c_double, p]
@@ -149,6 +152,21 @@ def topk(logits: np.ndarray, K: int):
     return idx, gates, int(fb)
 
 
+def topk_sigmoid(logits: np.ndarray, K: int, bias=None):
+    """Sigmoid router on raw logits, bias for the selection only.
+    -> (idx int32 [T,K] ascending, gates fp64 [T,K], n_fallback_rounds)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    idx = np.empty((T, K), dtype=np.int32)
+    gates = np.empty((T, K), dtype=np.float64)
+    fb = lib().orc_topk_sigmoid(_ptr(logits), T, E, K, _ptr(b), _ptr(idx), _ptr(gates))
+    return idx, gates, int(fb)
+
+
+SOFTMAX, SIGMOID = 0, 1
+
+
 def permute(idx: np.ndarray, E: int):
     """-> (counts [E], offsets [E+1], perm [T*K], unique [n])."""
     idx = np.ascontiguousarray(idx, dtype=np.int32)
@@ -198,8 +216,10 @@ def expert_ffn(ex: Expert, x: np.ndarray, H: int, I: int, want_h: bool = False):
 
 
 def moe_forward(x: np.ndarray, wr: np.ndarray, bias, experts: list, shared: Expert,
-                H: int, I: int, K: int):
+                H: int, I: int, K: int, scoring: int = SOFTMAX):
     """Whole layer.  experts: list of E entries (Expert or None if unused).
+    scoring: SOFTMAX (bias added to the logits) or SIGMOID (bias steers the
+    selection only).
 
     -> (y fp64 [T,H], idx int32 [T,K], gates fp64 [T,K]).
     """
@@ -217,7 +237,8 @@ def moe_forward(x: np.ndarray, wr: np.ndarray, bias, experts: list, shared: Expe
     idx = np.empty((T, K), dtype=np.int32)
     gates = np.empty((T, K), dtype=np.float64)
     rc = lib().orc_moe_forward(_ptr(x), _dtype_code(x), T, H, I, E, K, _ptr(wr),
-                               _dtype_code(wr), _ptr(b), ctypes.cast(arr, ctypes.c_void_p),
+                               _dtype_code(wr), _ptr(b), int(scoring),
+                               ctypes.cast(arr, ctypes.c_void_p),
                                ctypes.byref(sh), _ptr(y), _ptr(idx), _ptr(gates))
     if rc != 0:
         raise ValueError("oracle: a selected expert was not supplied")

@@ -34,7 +34,13 @@
  *     renormalised (which equals softmax over the K selected logits);
  *   - ties at the top-K boundary go to the lower expert id, NaN never wins,
  *     and the K ids are returned in ascending order;
- *   - h = SiLU(gate) * up, y = sum_k g_k Wd_k h_k + Wd_shared h_shared.
+ *   - h = SiLU(gate) * up, y = sum_k g_k Wd_k h_k + Wd_shared h_shared;
+ *   - the sigmoid router with no auxiliary loss ([P1] 十一: one expert group,
+ *     sigmoid scores, "noaux_tc" selection): score s_e = 1 / (1 + e^-l_e) of
+ *     the raw logit; the selection key is s_e + b_e, where the per-expert bias
+ *     b steers which experts are picked and nothing else; the gates are the
+ *     selected scores divided by their sum; with a single group the group
+ *     stage keeps every expert; no routed scaling factor (1).
  *
  * Arithmetic: everything is fp64 except where the quantiser must reproduce an
  * fp32 result exactly.  fp64 then fp32 rounding of a quotient of two fp32
@@ -224,6 +230,58 @@ int orc_topk(const double *logits, int T, int E, int K, int32_t *idx,
     return fallbacks;
 }
 
+/*
+ * The sigmoid router of [P1] 十一 ("n_group=1 sigmoid + noaux_tc"), per token:
+ *   1. score s_e = 1 / (1 + exp(-l_e)) for every expert (l: raw logits);
+ *   2. one expert group (n_group = 1): the group stage keeps all E experts;
+ *   3. key k_e = s_e + b_e (b: the selection bias, zero if NULL); take the K
+ *      largest keys by K rounds of argmax with the same rules as orc_topk
+ *      (strict >, so ties go to the lower id; NaN never wins; the [P4]
+ *      fallback for a round with no valid candidate);
+ *   4. ids in ascending order; gate_i = s_i / sum_{j selected} s_j (the bias
+ *      does not enter the gates).
+ * Returns the number of fallback rounds (0 for valid input).
+ */
+int orc_topk_sigmoid(const double *logits, int T, int E, int K, const float *bias,
+                     int32_t *idx, double *gates) {
+    int fallbacks = 0;
+    char *taken = (char *)malloc((size_t)E);
+    double *s = (double *)malloc(sizeof(double) * (size_t)E);
+    double *key = (double *)malloc(sizeof(double) * (size_t)E);
+    for (int t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        for (int e = 0; e < E; ++e) {
+            s[e] = 1.0 / (1.0 + exp(-l[e]));
+            key[e] = s[e] + (bias ? (double)bias[e] : 0.0);
+        }
+        memset(taken, 0, (size_t)E);
+        for (int round = 0; round < K; ++round) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e] || isnan(key[e])) continue;
+                if (best < 0 || key[e] > key[best]) best = e;
+            }
+            if (best < 0) {
+                ++fallbacks;
+                if (round < E && !taken[round]) best = round;
+                else
+                    for (int e = 0; e < E; ++e)
+                        if (!taken[e]) { best = e; break; }
+            }
+            taken[best] = 1;
+        }
+        int n = 0;
+        for (int e = 0; e < E; ++e)
+            if (taken[e]) idx[(size_t)t * K + n++] = e;
+        double z = 0.0;
+        for (int i = 0; i < K; ++i) z += s[idx[(size_t)t * K + i]];
+        for (int i = 0; i < K; ++i)
+            gates[(size_t)t * K + i] = s[idx[(size_t)t * K + i]] / z;
+    }
+    free(taken); free(s); free(key);
+    return fallbacks;
+}
+
 /* ------------------------------------------------------------------ */
 /* batch-union permute  [P1 四]                                        */
 /* ------------------------------------------------------------------ */
@@ -314,7 +372,9 @@ typedef struct {
 
 /*
  * y[t] = sum_k gates[t][k] * FFN_{idx[t][k]}(x[t]) + FFN_shared(x[t]).
- * The routing (logits, top-K, gates) is computed here from x, Wr and b.
+ * The routing (logits, top-K, gates) is computed here from x, Wr and b:
+ * scoring 0 is the softmax router (b added to the logits, orc_topk),
+ * scoring 1 the sigmoid router (b steers the selection, orc_topk_sigmoid).
  * experts[0..E) are the routed experts (an entry may have NULL pointers if
  * no token selects it; the call then returns -1 if one is selected);
  * shared is the shared expert, applied with weight 1.
@@ -322,14 +382,22 @@ typedef struct {
  */
 int orc_moe_forward(const void *x, int x_dtype, int T, int H, int I, int E,
                     int K, const void *wr, int w_dtype, const float *bias,
-                    const orc_expert *experts, const orc_expert *shared,
-                    double *y, int32_t *idx, double *gates) {
+                    int scoring, const orc_expert *experts,
+                    const orc_expert *shared, double *y, int32_t *idx,
+                    double *gates) {
     double *logits = (double *)malloc(sizeof(double) * (size_t)T * (size_t)E);
     double *xd = (double *)malloc(sizeof(double) * (size_t)H);
     double *o = (double *)malloc(sizeof(double) * (size_t)H);
     int rc = 0;
-    orc_router_logits(x, x_dtype, T, H, wr, w_dtype, E, bias, logits);
-    orc_topk(logits, T, E, K, idx, gates);
+    if (scoring == 0) {
+        /* softmax router: the bias is part of the logits */
+        orc_router_logits(x, x_dtype, T, H, wr, w_dtype, E, bias, logits);
+        orc_topk(logits, T, E, K, idx, gates);
+    } else {
+        /* sigmoid router: raw logits; the bias enters the selection only */
+        orc_router_logits(x, x_dtype, T, H, wr, w_dtype, E, NULL, logits);
+        orc_topk_sigmoid(logits, T, E, K, bias, idx, gates);
+    }
     for (int t = 0; t < T && rc == 0; ++t) {
         for (int h = 0; h < H; ++h) xd[h] = load_elem(x, x_dtype, (size_t)t * H + h);
         double *yt = y + (size_t)t * H;
