@@ -71,7 +71,7 @@ class Caller:
         self.coli, self.layer, self.mode = coli, layer, mode
         self.args = [ctypes.byref(layer.c), mode, ctypes.c_void_p(x.data_ptr()), x.shape[0],
                      ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
-                     ctypes.c_void_p(gates.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                     ctypes.c_void_p(gates.data_ptr()), None, ctypes.c_void_p(ws.data_ptr()),
                      ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)]
 
     def __call__(self):

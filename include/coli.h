@@ -30,6 +30,9 @@
  *   - Row-major layouts throughout.  Calls are reentrant: the library has no
  *     global mutable state; concurrent calls must not share output or
  *     workspace buffers.
+ *   - Data conditions found on the device (non-finite values, an operand out
+ *     of range, an unfinished expert blob) are OR-ed into an optional device
+ *     status flag; they never change the return value.
  */
 #ifndef COLI_H
 #define COLI_H
@@ -53,6 +56,30 @@ enum {
 
 typedef enum { COLI_F32 = 0, COLI_BF16 = 1 } coli_dtype;
 typedef enum { COLI_DECODE = 0, COLI_PREFILL = 1 } coli_mode;
+
+/* How the router turns logits into a selection and gates.
+ *   SOFTMAX: the K largest logits (an optional bias is added to the logits);
+ *            gates = softmax over the K selected logits.
+ *   SIGMOID: the router of page "Colibrì 深度解析", section 十一 (one expert
+ *            group, sigmoid scores, selection without an auxiliary loss):
+ *            score s_e = 1 / (1 + exp(-l_e)) of the raw logit; the K largest
+ *            keys s_e + b_e are selected, where the optional bias b only
+ *            steers the selection; gates = the selected scores divided by
+ *            their sum.  The returned logits are the raw ones. */
+typedef enum { COLI_SCORE_SOFTMAX = 0, COLI_SCORE_SIGMOID = 1 } coli_scoring;
+
+/* Bits of the optional device status flag of coli_moe_forward (OR-ed in by
+ * the kernels; the caller clears the flag).  Device-side data conditions are
+ * reported here, never through the return value. */
+#define COLI_STATUS_NONFINITE 1   /* y holds a non-finite value (a non-finite
+                                     x or weight reached it) */
+#define COLI_STATUS_RANGE 2       /* PREFILL: an fp16 operand (h or a
+                                     per-slot output, after the per-token
+                                     scaling) exceeded 65504; y is unreliable */
+#define COLI_STATUS_UNFINISHED 4  /* DECODE: an expert blob the call read has
+                                     no finish tag (coli_expert_finish was not
+                                     run on it); that expert's outputs, and so
+                                     y of its tokens, are NaN */
 
 #define COLI_GROUP 64           /* elements per quantisation group */
 #define COLI_MAX_EXPERTS 1024   /* upper bound for E (and K) */
@@ -101,28 +128,42 @@ int coli_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
 
 /*
  * Router logits and top-K with renormalised gates for T tokens.
- *   x        [T, H]  fp32 or bf16 (x_dtype), rows 16-byte aligned
+ *   x        [T, H]  fp32 or bf16 (x_dtype), row-major, any H
  *   w_router [E, H]  fp32 or bf16 (w_dtype)
- *   bias     [E]     fp32, or NULL (added to the logits; used for selection
- *                    and for the gates)
- *   logits   [T, E]  fp32 output (required)
+ *   bias     [E]     fp32, or NULL (SOFTMAX: added to the logits, so it
+ *                    steers the selection and enters the gates; SIGMOID: the
+ *                    selection bias of coli_scoring)
+ *   logits   [T, E]  fp32 output, or NULL: the logits are then kept on chip
+ *                    (one block per token) and not written
  *   topk_idx [T, K]  int32 output: the K selected expert ids of each token
  *                    in ascending id order
- *   topk_gate[T, K]  fp32 output: softmax over the K selected logits (equal
- *                    to the softmax over all E restricted to the selected
- *                    and renormalised to sum 1), same order as topk_idx
- * Selection: the K largest logits; on equal logits the lower id wins; NaN
- * never wins.  A slot with no valid candidate (every remaining logit NaN)
- * takes id k if free, else the lowest free id (page "colibrì 路由遥测全解析",
- * section 测试与 CI 保障); its gates are then unspecified.
- * Requires H % 8 == 0.  Errors: EINVAL, ESHAPE (T outside [0, MAX_TOKENS],
- * H outside [8, MAX_DIM] or H % 8, E outside [1, MAX_EXPERTS], K outside
- * [1, E]), EDTYPE, EALIGN.  T == 0 is a no-op.
+ *   topk_gate[T, K]  fp32 output, same order as topk_idx.  SOFTMAX: softmax
+ *                    over the K selected logits (equal to the softmax over
+ *                    all E restricted to the selected and renormalised to sum
+ *                    1); SIGMOID: see coli_scoring.
+ * Selection: the K largest keys (logits, or biased sigmoid scores); on equal
+ * keys the lower id wins; NaN never wins.  A slot with no valid candidate
+ * (every remaining key NaN) takes id k if free, else the lowest free id (page
+ * "colibrì 路由遥测全解析", section 测试与 CI 保障); its gates are then
+ * unspecified.
+ * x and w_router must be 4-byte (fp32) or 2-byte (bf16) aligned; 16-byte
+ * aligned rows with H % 8 == 0 take the vector kernels.
+ * Errors: EINVAL, ESHAPE (T outside [0, MAX_TOKENS], H outside [1, MAX_DIM],
+ * E outside [1, MAX_EXPERTS], K outside [1, E]), EDTYPE, EALIGN.
+ * T == 0 is a no-op.
  */
 int coli_router_topk(const void *x, coli_dtype x_dtype, int T, int H,
                      const void *w_router, coli_dtype w_dtype, int E,
                      const float *bias, int K, int32_t *topk_idx,
                      float *topk_gate, float *logits, void *stream);
+/* coli_router_topk with the scoring chosen (coli_router_topk is
+ * COLI_SCORE_SOFTMAX).  Errors: as coli_router_topk, plus EINVAL for an
+ * unknown scoring. */
+int coli_router_topk_scored(const void *x, coli_dtype x_dtype, int T, int H,
+                            const void *w_router, coli_dtype w_dtype, int E,
+                            const float *bias, int K, coli_scoring scoring,
+                            int32_t *topk_idx, float *topk_gate, float *logits,
+                            void *stream);
 
 /*
  * Batch-union permute (page "Colibrì 深度解析", section 四).
@@ -134,14 +175,15 @@ int coli_router_topk(const void *x, coli_dtype x_dtype, int T, int H,
  *   unique   [E]    int32: experts with count > 0, ascending; entries past
  *                   *n_unique are unspecified
  *   n_unique [1]    int32
- *   workspace: device scratch of coli_expert_permute_workspace_bytes(T, E)
- *              bytes (0 for small T; then workspace may be NULL).
+ *   workspace: device scratch of coli_expert_permute_workspace_bytes(T, K, E)
+ *              bytes (0 for T*K <= 2048; then workspace may be NULL).
  * Pairs whose id lies outside [0, E) are skipped (not counted, not placed);
- * offsets[E] is the number of pairs placed.
+ * offsets[E] is the number of pairs placed.  A row may name an expert more
+ * than once: every pair is counted and placed.
  * Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE.  T == 0 writes zero counts,
  * zero offsets and n_unique = 0.
  */
-size_t coli_expert_permute_workspace_bytes(int T, int E);
+size_t coli_expert_permute_workspace_bytes(int T, int K, int E);
 int coli_expert_permute(const int32_t *topk_idx, int T, int K, int E,
                         int32_t *counts, int32_t *offsets, int32_t *perm,
                         int32_t *unique, int32_t *n_unique, void *workspace,
@@ -164,6 +206,9 @@ typedef struct {
  *   experts: E expert blobs laid end to end, each coli_expert_blob_bytes(H,I)
  *            bytes; shared: one blob of the same layout (the shared expert,
  *            applied to every token with weight 1).  Both 256-byte aligned.
+ *   scoring: the router's coli_scoring (0, SOFTMAX, when left zero).
+ * H and I may be any value in [1, MAX_DIM]: a row whose length is not a
+ * multiple of 64 ends in a zero-padded group (the quantiser pads it so).
  */
 typedef struct {
     int H, I, E, K;
@@ -172,6 +217,7 @@ typedef struct {
     const float *router_bias;
     const uint8_t *experts;
     const uint8_t *shared;
+    coli_scoring scoring;
 } coli_moe_layer;
 
 /*
@@ -179,12 +225,12 @@ typedef struct {
  * boundary): gate.q [I][GH*32] | up.q [I][GH*32] | down.q [H][GI*32] |
  * gate.s [I][GH] | up.s [I][GH] | down.s [H][GI] | gate.sT [GH][I] |
  * up.sT [GH][I] | down.sT [GI][H] | gate.sB [I8/8][GH][8] |
- * up.sB [I8/8][GH][8] | down.sB [H8/8][GI][8], with GH = ceil(H/64),
+ * up.sB [I8/8][GH][8] | down.sB [H8/8][GI][8] | tag [16 B], with GH = ceil(H/64),
  * GI = ceil(I/64), I8 and H8 = I and H rounded up to a multiple of 8.
  * gate/up are [I, H] (input dim H); down is [H, I].  The .sT sections hold
  * the same scales group-major, the .sB sections blocked by 8 rows
  * (sB[b][g][r] = s[8b + r][g], zero past the last row; see
- * coli_expert_finish).
+ * coli_expert_finish); the tag section is written by coli_expert_finish.
  * Returns 0 if H or I is outside [1, MAX_DIM].
  */
 size_t coli_expert_blob_bytes(int H, int I);
@@ -193,18 +239,32 @@ size_t coli_expert_blob_bytes(int H, int I);
  * Fill the blob's group-major scale sections (gate.sT, up.sT, down.sT) and
  * its 8-row blocked ones (gate.sB, up.sB, down.sB) from its row-major ones:
  * sT[g][o] = s[o][g] and sB[o/8][g][o%8] = s[o][g], bit for bit (the padding
- * rows of the last block are written as 0).  Call it once the
- * three matrices are in the blob (quantised by coli_quant_int4_g64 into the
- * coli_expert_views pointers, or written from stored bytes) and before the
- * blob is used by coli_moe_forward: the decode batch path (1 < T <= 256)
- * reads the scales group-major (one cache line per 32 rows and group), the
- * single-token path blocked (one 8-row item's groups are contiguous), the
- * prefill path row-major.  Asynchronous on `stream`.
- * The blob is the layout above, of [P2] 权重转换's sections.
- * Errors: EINVAL (NULL), ESHAPE, EALIGN (blob not 256-byte aligned),
- * EDEVICE.
+ * rows of the last block are written as 0), then write the blob's finish tag,
+ * in stream order after the copies.  Call it once the three matrices are in
+ * the blob (quantised by coli_quant_int4_g64 into the coli_expert_views
+ * pointers, or written from stored bytes), and again after any change to
+ * them, before the blob is used by coli_moe_forward in DECODE mode: the decode
+ * batch path (1 < T) reads the scales group-major (one cache line per 32 rows
+ * and group), the single-token path blocked (one 8-row item's groups are
+ * contiguous).  The PREFILL path reads the format's row-major scales only.
+ * A DECODE forward that reads a blob without the tag gives NaN outputs for
+ * that expert and raises COLI_STATUS_UNFINISHED (fail closed).
+ * Asynchronous on `stream`.  The blob is the layout above, of [P2] 权重转换's
+ * sections.  Errors: EINVAL (NULL), ESHAPE, EALIGN (blob not 256-byte
+ * aligned), EDEVICE.
  */
 int coli_expert_finish(uint8_t *blob, int H, int I, void *stream);
+
+/*
+ * Quantise one expert into the blob at `blob` and finish it: gate [I, H],
+ * up [I, H] and down [H, I] fp32 (device, row-major, 4-byte aligned) go
+ * through coli_quant_int4_g64 into the coli_expert_views sections, then
+ * coli_expert_finish.  status: as coli_quant_int4_g64 (optional).
+ * Errors: as those two calls; nothing is launched on an argument error.
+ */
+int coli_quant_expert(uint8_t *blob, int H, int I, const float *w_gate,
+                      const float *w_up, const float *w_down, int32_t *status,
+                      void *stream);
 
 /* Views of the three matrices of the blob at `blob` (pure pointer
  * arithmetic on the host; nothing is read).  Errors: EINVAL, ESHAPE. */
@@ -217,35 +277,40 @@ size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int T, coli_mode mode);
 
 /*
  * One forward pass of the layer for T tokens:
- *   logits = x Wr^T + b; top-K with renormalised gates (as coli_router_topk);
+ *   logits = x Wr^T (+ b), top-K with renormalised gates (as
+ *     coli_router_topk_scored with L->scoring);
  *   batch-union permute (as coli_expert_permute);
  *   per selected (token, expert): h = SiLU(Wg x) * (Wu x), o = Wd h, with
  *     W = s * (u - 8) read from the planar bytes;
  *   y[t] = sum_k gate[t,k] * o[t,k] + Wd_sh (SiLU(Wg_sh x) * (Wu_sh x)).
- *   mode DECODE:  x, y fp32 [T, H], T <= 256; fp32-class products on the
- *                 matrix cores: weights as the exact integers u - 8 with the
- *                 fp32 group scale applied per group, x and h split into
- *                 fp16 hi + lo parts under a power-of-two scale per row
- *                 (T = 1: int8 digit planes), h and the per-slot outputs
- *                 held in fp32.
+ *   mode DECODE:  x, y fp32 [T, H]; fp32-class products on the matrix cores:
+ *                 weights as the exact integers u - 8 with the fp32 group
+ *                 scale applied per group, x and h split into fp16 hi + lo
+ *                 parts under a power-of-two scale per row (T = 1 with H and
+ *                 I multiples of 256: int8 digit planes), h and the per-slot
+ *                 outputs held in fp32.  T > 256 runs as consecutive 256-token
+ *                 batches (each reads its experts once).
  *   mode PREFILL: x, y bf16 [T, H], T <= COLI_MAX_TOKENS; grouped GEMMs on
- *                 the matrix cores with fp32 accumulation.  The products take
- *                 fp16 operands: x converted from bf16 (exact for
- *                 |x| in [2^-14, 65504]), weights s*(u-8) rounded once to
- *                 fp16, h held in fp16; per-slot outputs are rounded to fp16
- *                 before the combine.  Inputs or intermediates beyond the fp16
- *                 range are outside this mode's contract.
+ *                 the matrix cores with fp32 accumulation and fp16 operands:
+ *                 each token's x is scaled by a power of two 2^-e (its
+ *                 largest |x| then lies in [2, 4)) and its h by 2^-2e before
+ *                 the fp16 conversion, weights s*(u-8) enter with s rounded
+ *                 to fp16, per-slot outputs are fp16 before the fp32 combine,
+ *                 which undoes the scaling.  Group scales must stay below 64.
  *   topk_idx_out, topk_gate_out: optional [T, K] copies of the routing.
+ *   status: optional device int32 flag; COLI_STATUS_* bits are OR-ed in.
  *   workspace: device scratch of at least coli_moe_workspace_bytes bytes,
  *              256-byte aligned; its contents need no initialisation and are
  *              undefined afterwards.
- * Requires H % 64 == 0 and I % 64 == 0.  Errors: EINVAL, ESHAPE, EDTYPE,
- * EALIGN (x, y 16-byte, blobs and workspace 256-byte), EWORKSPACE, EDEVICE.
- * T == 0 is a no-op.
+ * Any H and I in [1, MAX_DIM].  Errors: EINVAL, ESHAPE (also when a buffer of
+ * the call would pass 2^31 bytes, the limit of the kernels' buffer offsets;
+ * coli_moe_workspace_bytes is then 0), EDTYPE, EALIGN (x, y 16-byte; blobs and
+ * workspace 256-byte; status 4-byte), EWORKSPACE, EDEVICE.  Every check runs
+ * before the first launch.  T == 0 is a no-op.
  */
 int coli_moe_forward(const coli_moe_layer *L, coli_mode mode, const void *x,
                      int T, void *y, int32_t *topk_idx_out,
-                     float *topk_gate_out, void *workspace,
+                     float *topk_gate_out, int32_t *status, void *workspace,
                      size_t workspace_bytes, void *stream);
 
 /*
@@ -259,14 +324,16 @@ int coli_moe_forward(const coli_moe_layer *L, coli_mode mode, const void *x,
  * launch, so elapsed(start, stop) is its execution time; elsewhere the events
  * are recorded on the stream before and after the stage's launches.
  * n_events must be at least 2 x the stage count (6 or 10).  Same work and
- * results as coli_moe_forward.
- * Errors: as coli_moe_forward, plus EINVAL for a NULL or short event array.
+ * results as coli_moe_forward; DECODE takes T <= 256 here.
+ * Errors: as coli_moe_forward, plus EINVAL for a NULL or short event array
+ * and ESHAPE for DECODE with T > 256.
  */
 int coli_moe_forward_timed(const coli_moe_layer *L, coli_mode mode,
                            const void *x, int T, void *y,
                            int32_t *topk_idx_out, float *topk_gate_out,
-                           void *workspace, size_t workspace_bytes,
-                           void *stream, void **events, int n_events);
+                           int32_t *status, void *workspace,
+                           size_t workspace_bytes, void *stream, void **events,
+                           int n_events);
 
 /*
  * RMSNorm with unit weight between stacked layers:

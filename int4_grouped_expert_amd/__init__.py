@@ -38,6 +38,8 @@ COLI_OK, COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN = 0, -1, -2, -3
 COLI_EDTYPE, COLI_EWORKSPACE, COLI_EDEVICE = -4, -5, -6
 COLI_F32, COLI_BF16 = 0, 1
 COLI_DECODE, COLI_PREFILL = 0, 1
+COLI_SCORE_SOFTMAX, COLI_SCORE_SIGMOID = 0, 1
+COLI_STATUS_NONFINITE, COLI_STATUS_RANGE, COLI_STATUS_UNFINISHED = 1, 2, 4
 COLI_MAX_EXPERTS = 1024
 COLI_MAX_DIM = 65536
 COLI_MAX_TOKENS = 65536
@@ -45,10 +47,10 @@ COLI_MAX_DECODE_T = 256
 
 EXPORTS = [
     "coli_strerror", "coli_int4_g64_packed_bytes", "coli_int4_g64_scale_count",
-    "coli_quant_int4_g64", "coli_router_topk", "coli_expert_permute_workspace_bytes",
-    "coli_expert_permute", "coli_expert_blob_bytes", "coli_expert_views", "coli_expert_finish",
-    "coli_moe_workspace_bytes", "coli_moe_forward", "coli_moe_forward_timed",
-    "coli_rmsnorm_f32",
+    "coli_quant_int4_g64", "coli_router_topk", "coli_router_topk_scored",
+    "coli_expert_permute_workspace_bytes", "coli_expert_permute", "coli_expert_blob_bytes",
+    "coli_expert_views", "coli_expert_finish", "coli_quant_expert", "coli_moe_workspace_bytes",
+    "coli_moe_forward", "coli_moe_forward_timed", "coli_rmsnorm_f32",
 ]
 
 _p = ctypes.c_void_p
@@ -63,7 +65,8 @@ class coli_q4(ctypes.Structure):
 
 class coli_moe_layer(ctypes.Structure):
     _fields_ = [("H", _i), ("I", _i), ("E", _i), ("K", _i), ("w_router", _p),
-                ("router_dtype", _i), ("router_bias", _p), ("experts", _p), ("shared", _p)]
+                ("router_dtype", _i), ("router_bias", _p), ("experts", _p), ("shared", _p),
+                ("scoring", _i)]
 
 
 def _proto(name, res, args):
@@ -78,17 +81,19 @@ _proto("coli_int4_g64_packed_bytes", _sz, [_i64, _i64])
 _proto("coli_int4_g64_scale_count", _sz, [_i64, _i64])
 _proto("coli_quant_int4_g64", _i, [_p, _i64, _i64, _p, _p, _p, _p])
 _proto("coli_router_topk", _i, [_p, _i, _i, _i, _p, _i, _i, _p, _i, _p, _p, _p, _p])
-_proto("coli_expert_permute_workspace_bytes", _sz, [_i, _i])
+_proto("coli_router_topk_scored", _i, [_p, _i, _i, _i, _p, _i, _i, _p, _i, _i, _p, _p, _p, _p])
+_proto("coli_expert_permute_workspace_bytes", _sz, [_i, _i, _i])
 _proto("coli_expert_permute", _i, [_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p])
 _proto("coli_expert_blob_bytes", _sz, [_i, _i])
 _proto("coli_expert_views", _i, [_p, _i, _i, ctypes.POINTER(coli_q4), ctypes.POINTER(coli_q4),
                                  ctypes.POINTER(coli_q4)])
 _proto("coli_expert_finish", _i, [_p, _i, _i, _p])
+_proto("coli_quant_expert", _i, [_p, _i, _i, _p, _p, _p, _p, _p])
 _proto("coli_moe_workspace_bytes", _sz, [ctypes.POINTER(coli_moe_layer), _i, _i])
-_proto("coli_moe_forward", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p, _p, _sz,
-                                _p])
+_proto("coli_moe_forward", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p, _p, _p,
+                                _sz, _p])
 _proto("coli_moe_forward_timed", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p,
-                                      _p, _sz, _p, ctypes.POINTER(_p), _i])
+                                      _p, _p, _sz, _p, ctypes.POINTER(_p), _i])
 _proto("coli_rmsnorm_f32", _i, [_p, _p, _i, _i, ctypes.c_float, _p])
 
 
@@ -155,17 +160,25 @@ def coli_quant_int4_g64(w, packed, scales, status=None, stream=None):
                                           _ptr(status), _stream(stream)), "coli_quant_int4_g64")
 
 
-def coli_router_topk(x, w_router, bias, K, topk_idx, topk_gate, logits, stream=None):
+def coli_router_topk(x, w_router, bias, K, topk_idx, topk_gate, logits=None, stream=None,
+                     scoring=COLI_SCORE_SOFTMAX):
+    """logits may be None (then kept on chip).  scoring: COLI_SCORE_SOFTMAX (the C
+    coli_router_topk) or COLI_SCORE_SIGMOID (coli_router_topk_scored)."""
     T, H = x.shape
     E = w_router.shape[0]
-    return _check(lib.coli_router_topk(_ptr(x), _dtype(x), T, H, _ptr(w_router),
-                                       _dtype(w_router), E, _ptr(bias), K, _ptr(topk_idx),
-                                       _ptr(topk_gate), _ptr(logits), _stream(stream)),
-                  "coli_router_topk")
+    if scoring == COLI_SCORE_SOFTMAX:
+        return _check(lib.coli_router_topk(_ptr(x), _dtype(x), T, H, _ptr(w_router),
+                                           _dtype(w_router), E, _ptr(bias), K, _ptr(topk_idx),
+                                           _ptr(topk_gate), _ptr(logits), _stream(stream)),
+                      "coli_router_topk")
+    return _check(lib.coli_router_topk_scored(_ptr(x), _dtype(x), T, H, _ptr(w_router),
+                                              _dtype(w_router), E, _ptr(bias), K, scoring,
+                                              _ptr(topk_idx), _ptr(topk_gate), _ptr(logits),
+                                              _stream(stream)), "coli_router_topk_scored")
 
 
-def coli_expert_permute_workspace_bytes(T: int, E: int) -> int:
-    return int(lib.coli_expert_permute_workspace_bytes(T, E))
+def coli_expert_permute_workspace_bytes(T: int, K: int, E: int) -> int:
+    return int(lib.coli_expert_permute_workspace_bytes(T, K, E))
 
 
 def coli_expert_permute(topk_idx, E, counts, offsets, perm, unique, n_unique, workspace=None,
@@ -182,15 +195,18 @@ class MoELayer:
     """A layer's device tensors and the C struct describing them.
 
     experts: uint8 tensor of E * coli_expert_blob_bytes(H, I) bytes (256-B aligned),
-    shared:  uint8 tensor of one blob; w_router: [E, H] fp32 or bf16; bias: [E] fp32 or None.
+    shared:  uint8 tensor of one blob; w_router: [E, H] fp32 or bf16; bias: [E] fp32 or None;
+    scoring: COLI_SCORE_SOFTMAX or COLI_SCORE_SIGMOID.
     """
 
-    def __init__(self, H, I, E, K, w_router, experts, shared, bias=None):
+    def __init__(self, H, I, E, K, w_router, experts, shared, bias=None,
+                 scoring=COLI_SCORE_SOFTMAX):
         self.H, self.I, self.E, self.K = H, I, E, K
         self.w_router, self.experts, self.shared, self.bias = w_router, experts, shared, bias
+        self.scoring = scoring
         self.c = coli_moe_layer(H, I, E, K, w_router.data_ptr(), _dtype(w_router),
                                 None if bias is None else bias.data_ptr(), experts.data_ptr(),
-                                shared.data_ptr())
+                                shared.data_ptr(), scoring)
 
     def workspace_bytes(self, T: int, mode: int) -> int:
         return int(lib.coli_moe_workspace_bytes(ctypes.byref(self.c), T, mode))
@@ -201,24 +217,27 @@ def coli_moe_workspace_bytes(layer: MoELayer, T: int, mode: int) -> int:
 
 
 def coli_moe_forward(layer: MoELayer, mode: int, x, y, workspace, topk_idx=None,
-                     topk_gate=None, stream=None):
+                     topk_gate=None, stream=None, status=None):
+    """status: optional int32 device tensor; COLI_STATUS_* bits are OR-ed into it."""
     T = x.shape[0]
     nbytes = workspace.numel() * workspace.element_size()
     return _check(lib.coli_moe_forward(ctypes.byref(layer.c), mode, _ptr(x), T, _ptr(y),
-                                       _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace), nbytes,
-                                       _stream(stream)), "coli_moe_forward")
+                                       _ptr(topk_idx), _ptr(topk_gate), _ptr(status),
+                                       _ptr(workspace), nbytes, _stream(stream)),
+                  "coli_moe_forward")
 
 
 def coli_moe_forward_timed(layer: MoELayer, mode: int, x, y, workspace, events, topk_idx=None,
-                           topk_gate=None, stream=None):
+                           topk_gate=None, stream=None, status=None):
     """events: torch.cuda.Event objects (timing enabled): a (start, stop) pair per stage,
     6 (decode) or 10 (prefill)."""
     T = x.shape[0]
     nbytes = workspace.numel() * workspace.element_size()
     arr = (_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
     return _check(lib.coli_moe_forward_timed(ctypes.byref(layer.c), mode, _ptr(x), T, _ptr(y),
-                                             _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace),
-                                             nbytes, _stream(stream), arr, len(events)),
+                                             _ptr(topk_idx), _ptr(topk_gate), _ptr(status),
+                                             _ptr(workspace), nbytes, _stream(stream), arr,
+                                             len(events)),
                   "coli_moe_forward_timed")
 
 
@@ -238,17 +257,21 @@ def coli_expert_finish(blob_ptr: int, H: int, I: int, stream=None):
 
 def coli_quant_expert(blob_ptr: int, H: int, I: int, wg, wu, wd, status=None, stream=None,
                       finish=True):
-    """Quantise fp32 gate [I,H], up [I,H], down [H,I] (device) into the blob at blob_ptr,
-    then (finish) fill its group-major and blocked scale copies."""
-    views = coli_expert_views(blob_ptr, H, I)
+    """Quantise fp32 gate [I,H], up [I,H], down [H,I] (device) into the blob at blob_ptr and
+    finish it (the C coli_quant_expert).  finish=False runs only the three
+    coli_quant_int4_g64 calls into the coli_expert_views sections (no derived scale
+    copies, no finish tag)."""
     st = _stream(stream)
+    if finish:
+        return _check(lib.coli_quant_expert(ctypes.c_void_p(blob_ptr), H, I, _ptr(wg), _ptr(wu),
+                                            _ptr(wd), _ptr(status), st), "coli_quant_expert")
+    views = coli_expert_views(blob_ptr, H, I)
     for (qp, sp), w in zip(views, (wg, wu, wd)):
         rows, cols = w.shape
         _check(lib.coli_quant_int4_g64(_ptr(w), rows, cols, ctypes.c_void_p(qp),
                                        ctypes.c_void_p(sp), _ptr(status), st),
                "coli_quant_int4_g64")
-    if finish:
-        coli_expert_finish(blob_ptr, H, I, stream)
+    return COLI_OK
 
 
 def alloc_layer_blobs(H: int, I: int, E: int, device="cuda"):

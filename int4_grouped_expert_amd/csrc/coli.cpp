@@ -24,15 +24,26 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 inline int dev_status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
 
 bool layer_shape_ok(int H, int I, int E, int K) {
-  return H >= 64 && H <= COLI_MAX_DIM && H % 64 == 0 && I >= 64 && I <= COLI_MAX_DIM &&
-         I % 64 == 0 && E >= 1 && E <= COLI_MAX_EXPERTS && K >= 1 && K <= E;
+  return H >= 1 && H <= COLI_MAX_DIM && I >= 1 && I <= COLI_MAX_DIM && E >= 1 &&
+         E <= COLI_MAX_EXPERTS && K >= 1 && K <= E;
+}
+
+// Tokens of one decode sub-batch: longer decode calls run in sub-batches.
+inline int decode_chunk_t(int T) { return T < COLI_MAX_DECODE_T ? T : COLI_MAX_DECODE_T; }
+
+// Whether every buffer offset of a forward of T tokens fits 31 bits (the
+// kernels address their buffers through 32-bit buffer-resource offsets whose
+// top bit masks lanes).
+bool offsets_ok(int H, int I, int K, int T, coli_mode mode) {
+  const size_t blob = blob_layout(H, I).bytes;
+  if (mode == COLI_PREFILL) return prefill_offsets_ok(H, I, K, T, blob);
+  return batch_offsets_ok(H, I, K, decode_chunk_t(T), blob);
 }
 
 // Workspace carve-up (byte offsets, each section 256-byte aligned).
 struct WsLayout {
   size_t logits, idx, gates, counts, offsets, perm, unique, n_unique, chunk, h, slot;
-  size_t xp, sx, sh;                          // prefill only
-  size_t slotmap;                             // decode only
+  size_t xp, sx, sh, xe;                      // prefill only
   size_t xdig, xcorr, nxsc, hn;               // decode, single-token path
   size_t bxp, bxs, bhf, bh16, bhs, bslot;     // decode batch path
   size_t total;
@@ -49,11 +60,11 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
   w.perm = o; o += align256(TK * 4);
   w.unique = o; o += align256(size_t(E) * 4);
   w.n_unique = o; o += 256;
-  size_t chunk = permute_chunk_ints(T, E);
+  size_t chunk = permute_chunk_ints(T, K, E);
   if (chunk < size_t(E) + 2) chunk = size_t(E) + 2;
   w.chunk = o; o += align256(chunk * 4);
-  w.xp = w.sx = w.sh = 0;
-  w.h = w.slot = w.slotmap = 0;
+  w.xp = w.sx = w.sh = w.xe = 0;
+  w.h = w.slot = 0;
   w.xdig = w.xcorr = w.nxsc = w.hn = 0;
   w.bxp = w.bxs = w.bhf = w.bh16 = w.bhs = w.bslot = 0;
   if (mode == COLI_PREFILL) {
@@ -62,10 +73,10 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
     w.sx = o; o += align256(size_t(T) * pl.CSX * 2);
     w.h = o; o += align256((TK + T) * size_t(pl.IP) * 2);
     w.sh = o; o += align256((TK + T) * size_t(pl.CSI) * 2);
-    w.slot = o; o += align256((TK + T) * size_t(H) * 2);
+    w.slot = o; o += align256((TK + T) * size_t(prefill_slot_stride(H)) * 2);
+    w.xe = o; o += align256(size_t(T) * 4);
   } else {
     const size_t units = TK < size_t(E) ? TK : size_t(E);
-    w.slotmap = o; o += align256(units * size_t(T) * 4);
     const size_t GH = size_t(groups_of(H));
     w.xdig = o; o += align256(size_t(T) * GH * 256);
     w.xcorr = o; o += align256(size_t(T) * GH * 16);
@@ -78,7 +89,7 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
     w.bhf = o; o += align256(R * size_t(I) * 4);
     w.bh16 = o; o += align256(2 * R * size_t(pl.IP) * 2);
     w.bhs = o; o += align256(R * 4);
-    w.bslot = o; o += align256(R * size_t(H) * 4);
+    w.bslot = o; o += align256(R * size_t(batch_slot_stride(H)) * 4);
   }
   w.total = o;
   return w;
@@ -138,31 +149,64 @@ int coli_quant_int4_g64(const float *w, int64_t rows, int64_t cols, uint8_t *pac
       launch_quant_int4_g64(w, rows, cols, packed, scales, status, as_stream(stream)));
 }
 
-int coli_router_topk(const void *x, coli_dtype x_dtype, int T, int H, const void *w_router,
-                     coli_dtype w_dtype, int E, const float *bias, int K, int32_t *topk_idx,
-                     float *topk_gate, float *logits, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int router_topk_impl(const void *x, coli_dtype x_dtype, int T, int H, const void *w_router,
+                     coli_dtype w_dtype, int E, const float *bias, int K, coli_scoring scoring,
+                     int32_t *topk_idx, float *topk_gate, float *logits, void *stream) {
   if (!w_router) return COLI_EINVAL;
-  if ((!x || !topk_idx || !topk_gate || !logits) && T != 0) return COLI_EINVAL;
-  if (T < 0 || T > COLI_MAX_TOKENS || H < 8 || H > COLI_MAX_DIM || H % 8 || E < 1 ||
+  if ((!x || !topk_idx || !topk_gate) && T != 0) return COLI_EINVAL;
+  if (scoring != COLI_SCORE_SOFTMAX && scoring != COLI_SCORE_SIGMOID) return COLI_EINVAL;
+  if (T < 0 || T > COLI_MAX_TOKENS || H < 1 || H > COLI_MAX_DIM || E < 1 ||
       E > COLI_MAX_EXPERTS || K < 1 || K > E)
     return COLI_ESHAPE;
   if ((x_dtype != COLI_F32 && x_dtype != COLI_BF16) ||
       (w_dtype != COLI_F32 && w_dtype != COLI_BF16))
     return COLI_EDTYPE;
-  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(topk_idx, 4) ||
-      !aligned(topk_gate, 4) || !aligned(logits, 4) || (bias && !aligned(bias, 4)))
+  const uintptr_t xa = x_dtype == COLI_BF16 ? 2 : 4, wa = w_dtype == COLI_BF16 ? 2 : 4;
+  if (!aligned(x, xa) || !aligned(w_router, wa) || !aligned(topk_idx, 4) ||
+      !aligned(topk_gate, 4) || (logits && !aligned(logits, 4)) || (bias && !aligned(bias, 4)))
     return COLI_EALIGN;
   if (T == 0) return COLI_OK;
   hipStream_t s = as_stream(stream);
-  hipError_t e = launch_router_logits(x, x_dtype == COLI_BF16, T, H, w_router,
-                                      w_dtype == COLI_BF16, E, bias, logits, s);
+  const int xb = x_dtype == COLI_BF16, wb = w_dtype == COLI_BF16;
+  const bool sig = scoring == COLI_SCORE_SIGMOID;
+  const Scoring sc{sig ? 1 : 0, sig ? bias : nullptr};
+  const float *lbias = sig ? nullptr : bias;  // the bias added to the logits
+  if (!logits)
+    return dev_status(launch_router_topk_fused(x, xb, T, H, w_router, wb, E, K, lbias, sc,
+                                               topk_idx, topk_gate, s));
+  hipError_t e = router_vec_ok(x, xb, H, w_router, wb)
+                     ? launch_router_logits(x, xb, T, H, w_router, wb, E, lbias, logits, s)
+                     : launch_router_any(x, xb, T, H, w_router, wb, E, lbias, logits, s);
   if (e != hipSuccess) return COLI_EDEVICE;
-  return dev_status(launch_topk(logits, T, E, K, topk_idx, topk_gate, s));
+  return dev_status(launch_topk(logits, T, E, K, topk_idx, topk_gate, sc, s));
 }
 
-size_t coli_expert_permute_workspace_bytes(int T, int E) {
-  if (T < 0 || T > COLI_MAX_TOKENS || E < 1 || E > COLI_MAX_EXPERTS) return 0;
-  return permute_chunk_ints(T, E) * 4;
+}  // namespace
+
+extern "C" {
+
+int coli_router_topk(const void *x, coli_dtype x_dtype, int T, int H, const void *w_router,
+                     coli_dtype w_dtype, int E, const float *bias, int K, int32_t *topk_idx,
+                     float *topk_gate, float *logits, void *stream) {
+  return router_topk_impl(x, x_dtype, T, H, w_router, w_dtype, E, bias, K, COLI_SCORE_SOFTMAX,
+                          topk_idx, topk_gate, logits, stream);
+}
+
+int coli_router_topk_scored(const void *x, coli_dtype x_dtype, int T, int H,
+                            const void *w_router, coli_dtype w_dtype, int E, const float *bias,
+                            int K, coli_scoring scoring, int32_t *topk_idx, float *topk_gate,
+                            float *logits, void *stream) {
+  return router_topk_impl(x, x_dtype, T, H, w_router, w_dtype, E, bias, K, scoring, topk_idx,
+                          topk_gate, logits, stream);
+}
+
+size_t coli_expert_permute_workspace_bytes(int T, int K, int E) {
+  if (T < 0 || T > COLI_MAX_TOKENS || E < 1 || E > COLI_MAX_EXPERTS || K < 1 || K > E) return 0;
+  return permute_chunk_ints(T, K, E) * 4;
 }
 
 int coli_expert_permute(const int32_t *topk_idx, int T, int K, int E, int32_t *counts,
@@ -176,7 +220,7 @@ int coli_expert_permute(const int32_t *topk_idx, int T, int K, int E, int32_t *c
       !aligned(perm, 4) || !aligned(unique, 4) || !aligned(n_unique, 4) ||
       (workspace && !aligned(workspace, 4)))
     return COLI_EALIGN;
-  const size_t need = permute_chunk_ints(T, E) * 4;
+  const size_t need = permute_chunk_ints(T, K, E) * 4;
   if (need && (!workspace || workspace_bytes < need)) return COLI_EWORKSPACE;
   Routing r;
   std::memset(&r, 0, sizeof(r));
@@ -216,41 +260,77 @@ int coli_expert_finish(uint8_t *blob, int H, int I, void *stream) {
   return dev_status(launch_expert_finish(blob, blob_layout(H, I), H, I, as_stream(stream)));
 }
 
+int coli_quant_expert(uint8_t *blob, int H, int I, const float *w_gate, const float *w_up,
+                      const float *w_down, int32_t *status, void *stream) {
+  if (!blob || !w_gate || !w_up || !w_down) return COLI_EINVAL;
+  if (H < 1 || H > COLI_MAX_DIM || I < 1 || I > COLI_MAX_DIM) return COLI_ESHAPE;
+  if (!aligned(blob, 256) || !aligned(w_gate, 4) || !aligned(w_up, 4) || !aligned(w_down, 4) ||
+      (status && !aligned(status, 4)))
+    return COLI_EALIGN;
+  const BlobLayout b = blob_layout(H, I);
+  hipStream_t s = as_stream(stream);
+  const struct {
+    const float *w;
+    int rows, cols;
+    size_t q, sc;
+  } m[3] = {{w_gate, I, H, b.gq, b.gs}, {w_up, I, H, b.uq, b.us}, {w_down, H, I, b.dq, b.ds}};
+  for (const auto &x : m) {
+    const hipError_t e = launch_quant_int4_g64(x.w, x.rows, x.cols, blob + x.q,
+                                               reinterpret_cast<float *>(blob + x.sc), status, s);
+    if (e != hipSuccess) return COLI_EDEVICE;
+  }
+  return dev_status(launch_expert_finish(blob, b, H, I, s));
+}
+
 size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int T, coli_mode mode) {
   if (!L || !layer_shape_ok(L->H, L->I, L->E, L->K)) return 0;
   if (mode != COLI_DECODE && mode != COLI_PREFILL) return 0;
-  const int tmax = mode == COLI_DECODE ? COLI_MAX_DECODE_T : COLI_MAX_TOKENS;
-  if (T < 0 || T > tmax) return 0;
-  return ws_layout(L->H, L->I, L->E, L->K, T, mode).total;
+  if (T < 0 || T > COLI_MAX_TOKENS) return 0;
+  if (!offsets_ok(L->H, L->I, L->K, T, mode)) return 0;
+  const int tl = mode == COLI_DECODE ? decode_chunk_t(T) : T;
+  return ws_layout(L->H, L->I, L->E, L->K, tl, mode).total;
 }
+
+}  // extern "C"
 
 namespace {
 
-int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
-                     int32_t *topk_idx_out, float *topk_gate_out, void *workspace,
-                     size_t workspace_bytes, void *stream, hipEvent_t *ev) {
+// Argument checks shared by the forward entry points (no launch).  On success
+// *lay holds the workspace carve-up for the call.
+int forward_checks(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
+                   int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
+                   WsLayout *lay) {
   if (!L || !L->w_router || !L->experts || !L->shared) return COLI_EINVAL;
   if ((!x || !y) && T != 0) return COLI_EINVAL;
   if (mode != COLI_DECODE && mode != COLI_PREFILL) return COLI_EINVAL;
+  if (L->scoring != COLI_SCORE_SOFTMAX && L->scoring != COLI_SCORE_SIGMOID) return COLI_EINVAL;
   if (!layer_shape_ok(L->H, L->I, L->E, L->K)) return COLI_ESHAPE;
-  const int tmax = mode == COLI_DECODE ? COLI_MAX_DECODE_T : COLI_MAX_TOKENS;
-  if (T < 0 || T > tmax) return COLI_ESHAPE;
+  if (T < 0 || T > COLI_MAX_TOKENS) return COLI_ESHAPE;
+  if (!offsets_ok(L->H, L->I, L->K, T, mode)) return COLI_ESHAPE;
   if (L->router_dtype != COLI_F32 && L->router_dtype != COLI_BF16) return COLI_EDTYPE;
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(L->w_router, 16) ||
+  if (!aligned(x, 16) || !aligned(y, 16) ||
+      !aligned(L->w_router, L->router_dtype == COLI_BF16 ? 2 : 4) ||
       !aligned(L->experts, 256) || !aligned(L->shared, 256) ||
       (L->router_bias && !aligned(L->router_bias, 4)) ||
       (topk_idx_out && !aligned(topk_idx_out, 4)) ||
-      (topk_gate_out && !aligned(topk_gate_out, 4)))
+      (topk_gate_out && !aligned(topk_gate_out, 4)) || (status && !aligned(status, 4)))
     return COLI_EALIGN;
-  const WsLayout w = ws_layout(L->H, L->I, L->E, L->K, T, mode);
-  if (!workspace || workspace_bytes < w.total) return COLI_EWORKSPACE;
-  if (!aligned(workspace, 256)) return COLI_EALIGN;
-  if (T == 0) return COLI_OK;
+  const int tl = mode == COLI_DECODE ? decode_chunk_t(T) : T;
+  *lay = ws_layout(L->H, L->I, L->E, L->K, tl, mode);
+  return COLI_OK;
+}
 
-  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+// One forward of T tokens (DECODE: T <= COLI_MAX_DECODE_T) with every
+// argument already checked.
+int forward_launch(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
+                   int32_t *topk_idx_out, float *topk_gate_out, int32_t *status, uint8_t *ws,
+                   const WsLayout &w, hipStream_t s, hipEvent_t *ev) {
   Routing r = carve(ws, w);
   if (topk_idx_out) r.idx = topk_idx_out;
   if (topk_gate_out) r.gates = topk_gate_out;
+  const bool sig = L->scoring == COLI_SCORE_SIGMOID;
+  r.sc = Scoring{sig ? 1 : 0, sig ? L->router_bias : nullptr};
+  const float *lbias = sig ? nullptr : L->router_bias;  // the bias added to the logits
   LayerDev d;
   d.H = L->H;
   d.I = L->I;
@@ -259,13 +339,14 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
   d.experts = L->experts;
   d.shared = L->shared;
   d.lay = blob_layout(L->H, L->I);
-  hipStream_t s = as_stream(stream);
+  d.tag = finish_tag(L->H, L->I);
+  d.status = status;
+  d.sc = r.sc;
   const int wbf = L->router_dtype == COLI_BF16;
 
   hipError_t e;
   if (mode == COLI_PREFILL && ev) (void)hipEventRecord(ev[0], s);
   if (mode == COLI_DECODE) {
-    int32_t *slotmap = reinterpret_cast<int32_t *>(ws + w.slotmap);
     if (narrow_supported(d, T)) {
       NarrowBufs nb;
       nb.xdig = reinterpret_cast<int8_t *>(ws + w.xdig);
@@ -274,7 +355,7 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
       nb.hn = reinterpret_cast<float *>(ws + w.hn);
       // one kernel per stage: the events are stamped by the launches
       e = launch_router_narrow(reinterpret_cast<const float *>(x), T, L->H, L->w_router, wbf,
-                               L->E, L->router_bias, r.logits, nb, s, ev ? ev[0] : nullptr,
+                               L->E, lbias, r.logits, nb, s, ev ? ev[0] : nullptr,
                                ev ? ev[1] : nullptr);
       if (e != hipSuccess) return COLI_EDEVICE;
       return dev_status(launch_ffn_narrow(d, nb, r.logits, r.idx, r.gates,
@@ -288,33 +369,34 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
     bb.hs = reinterpret_cast<float *>(ws + w.bhs);
     bb.slot = reinterpret_cast<float *>(ws + w.bslot);
     if (ev) (void)hipEventRecord(ev[0], s);
-    // the router launch also writes x's staged rows for the batch GEMM
-    e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, L->router_bias, r.logits, s,
-                             bb.xp, bb.xs, prefill_layout(L->H, L->I).HP);
+    // the vector router launch also writes x's staged rows for the batch GEMM
+    const bool vec = router_vec_ok(x, 0, L->H, L->w_router, wbf);
+    e = vec ? launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, lbias, r.logits, s,
+                                   bb.xp, bb.xs, prefill_layout(L->H, L->I).HP)
+            : launch_router_any(x, 0, T, L->H, L->w_router, wbf, L->E, lbias, r.logits, s);
     if (e != hipSuccess) return COLI_EDEVICE;
-    e = launch_route_decode(r, T, L->E, L->K, slotmap, s);
+    e = launch_route_decode(r, T, L->E, L->K, s);
     if (e != hipSuccess) return COLI_EDEVICE;
     if (ev) (void)hipEventRecord(ev[1], s);
     e = launch_ffn_batch(d, reinterpret_cast<const float *>(x), T, r, bb,
-                         reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr, true);
+                         reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr, vec);
     return dev_status(e);
   }
-  if (wbf) {
+  if (wbf && L->H % 32 == 0 && router_vec_ok(x, 1, L->H, L->w_router, 1)) {
     // the staged-x region is free until the activation conversion: it holds the
     // router's K-split partial sums
     const PrefillLayout pl = prefill_layout(L->H, L->I);
-    e = launch_router_topk_mfma(reinterpret_cast<const uint16_t *>(x), T, L->H,
-                                reinterpret_cast<const uint16_t *>(L->w_router), L->E,
-                                L->router_bias, L->K, r.logits, r.idx, r.gates,
-                                reinterpret_cast<float *>(ws + w.xp),
-                                size_t(T) * pl.HP * 2, s);
-    if (e != hipSuccess) return COLI_EDEVICE;
-    e = launch_topk_permute(r, T, L->E, L->K, 0, s);
+    e = launch_router_mfma(reinterpret_cast<const uint16_t *>(x), T, L->H,
+                           reinterpret_cast<const uint16_t *>(L->w_router), L->E, lbias,
+                           r.logits, reinterpret_cast<float *>(ws + w.xp),
+                           size_t(T) * pl.HP * 2, s);
+  } else if (router_vec_ok(x, 1, L->H, L->w_router, wbf)) {
+    e = launch_router_logits(x, 1, T, L->H, L->w_router, wbf, L->E, lbias, r.logits, s);
   } else {
-    e = launch_router_logits(x, 1, T, L->H, L->w_router, 0, L->E, L->router_bias, r.logits, s);
-    if (e != hipSuccess) return COLI_EDEVICE;
-    e = launch_topk_permute(r, T, L->E, L->K, 1, s);
+    e = launch_router_any(x, 1, T, L->H, L->w_router, wbf, L->E, lbias, r.logits, s);
   }
+  if (e != hipSuccess) return COLI_EDEVICE;
+  e = launch_topk_permute(r, T, L->E, L->K, 1, s);
   if (e != hipSuccess) return COLI_EDEVICE;
   if (ev) (void)hipEventRecord(ev[1], s);
   PrefillBufs pb;
@@ -323,29 +405,61 @@ int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int
   pb.h = reinterpret_cast<uint16_t *>(ws + w.h);
   pb.sh = reinterpret_cast<uint16_t *>(ws + w.sh);
   pb.slot = reinterpret_cast<uint16_t *>(ws + w.slot);
+  pb.xe = reinterpret_cast<int *>(ws + w.xe);
   e = launch_ffn_prefill(d, reinterpret_cast<const uint16_t *>(x), T, r, pb,
                          reinterpret_cast<uint16_t *>(y), s, ev ? ev + 2 : nullptr);
   return dev_status(e);
 }
 
+int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
+                     int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
+                     void *workspace, size_t workspace_bytes, void *stream, hipEvent_t *ev) {
+  WsLayout w;
+  const int rc = forward_checks(L, mode, x, T, y, topk_idx_out, topk_gate_out, status, &w);
+  if (rc != COLI_OK) return rc;
+  if (!workspace || workspace_bytes < w.total) return COLI_EWORKSPACE;
+  if (!aligned(workspace, 256)) return COLI_EALIGN;
+  if (T == 0) return COLI_OK;
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  hipStream_t s = as_stream(stream);
+  if (mode == COLI_PREFILL || T <= COLI_MAX_DECODE_T)
+    return forward_launch(L, mode, x, T, y, topk_idx_out, topk_gate_out, status, ws, w, s, ev);
+  // decode of more than 256 tokens: consecutive 256-token sub-batches, each
+  // reading its experts once
+  const size_t H = size_t(L->H), K = size_t(L->K);
+  for (int t0 = 0; t0 < T; t0 += COLI_MAX_DECODE_T) {
+    const int n = T - t0 < COLI_MAX_DECODE_T ? T - t0 : COLI_MAX_DECODE_T;
+    const int r2 = forward_launch(
+        L, mode, reinterpret_cast<const float *>(x) + size_t(t0) * H, n,
+        reinterpret_cast<float *>(y) + size_t(t0) * H,
+        topk_idx_out ? topk_idx_out + size_t(t0) * K : nullptr,
+        topk_gate_out ? topk_gate_out + size_t(t0) * K : nullptr, status, ws, w, s, nullptr);
+    if (r2 != COLI_OK) return r2;
+  }
+  return COLI_OK;
+}
+
 }  // namespace
 
+extern "C" {
+
 int coli_moe_forward(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
-                     int32_t *topk_idx_out, float *topk_gate_out, void *workspace,
-                     size_t workspace_bytes, void *stream) {
-  return moe_forward_impl(L, mode, x, T, y, topk_idx_out, topk_gate_out, workspace,
+                     int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  return moe_forward_impl(L, mode, x, T, y, topk_idx_out, topk_gate_out, status, workspace,
                           workspace_bytes, stream, nullptr);
 }
 
 int coli_moe_forward_timed(const coli_moe_layer *L, coli_mode mode, const void *x, int T,
-                           void *y, int32_t *topk_idx_out, float *topk_gate_out,
+                           void *y, int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
                            void *workspace, size_t workspace_bytes, void *stream, void **events,
                            int n_events) {
   const int need = 2 * (mode == COLI_PREFILL ? 5 : 3);
   if (!events || n_events < need) return COLI_EINVAL;
   for (int i = 0; i < need; ++i)
     if (!events[i]) return COLI_EINVAL;
-  return moe_forward_impl(L, mode, x, T, y, topk_idx_out, topk_gate_out, workspace,
+  if (mode == COLI_DECODE && T > COLI_MAX_DECODE_T) return COLI_ESHAPE;
+  return moe_forward_impl(L, mode, x, T, y, topk_idx_out, topk_gate_out, status, workspace,
                           workspace_bytes, stream, reinterpret_cast<hipEvent_t *>(events));
 }
 

@@ -96,7 +96,7 @@ __device__ inline f16x8 unpack_u8(uint32_t d, uint32_t m1, uint32_t m2) {
 template <bool kGateUp, bool kHalf>
 __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDev &L,
                                                                    const DecArgs &da,
-                                                                   const Item &it) {
+                                                                   const Item &it, float poison) {
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
   const int h = lane >> 5, n = lane & 31;
@@ -293,19 +293,22 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
       for (int v = 0; v < 8; ++v) acc[jn][v] += acc[jn][v + 8];
   }
   if (wvalid) {
+    // rows past the matrix (a ragged last tile) are not stored
+    const int nrow = kGateUp ? L.I : L.H;
 #pragma unroll
     for (int v = 0; v < (kHalf ? 8 : 16); ++v) {
       const int m = 8 * (v >> 2) + 4 * h + (v & 3);
       if (m < nrows) {
-        const float rs = g_rsc[m];
+        const float rs = g_rsc[m] * poison;
         if (kGateUp) {
           const float gv = acc[0][v] * rs, uv = acc[1][v] * rs;
-          da.out[int64_t(g_outrow[m]) * da.OP + wrow0 + n] = silu(gv) * uv;
+          if (wrow0 + n < nrow) da.out[int64_t(g_outrow[m]) * da.OP + wrow0 + n] = silu(gv) * uv;
         } else {
           const float gs = rs * g_gate[m];
 #pragma unroll
           for (int jn = 0; jn < 2; ++jn)
-            da.out[int64_t(g_outrow[m]) * da.OP + wrow0 + 32 * jn + n] = acc[jn][v] * gs;
+            if (wrow0 + 32 * jn + n < nrow)
+              da.out[int64_t(g_outrow[m]) * da.OP + wrow0 + 32 * jn + n] = acc[jn][v] * gs;
         }
       }
     }
@@ -381,29 +384,53 @@ __global__ __launch_bounds__(kThreads, 2) void dec_gemm(LayerDev L, Routing r, i
       g_rowidx[threadIdx.x] = ri;
     }
     __syncthreads();
+    // a blob without the finish tag has no valid scale copies: its outputs
+    // become NaN and the status flag says why
+    const uint4 tg = *reinterpret_cast<const uint4 *>(it.blob + L.lay.tag);
+    const bool bad = tg.x != L.tag.x || tg.y != L.tag.y || tg.z != L.tag.z || tg.w != L.tag.w;
+    if (bad && threadIdx.x == 0) raise_status(L.status, COLI_STATUS_UNFINISHED);
+    const float poison = bad ? __builtin_nanf("") : 1.0f;
     if (small)
-      run_item_dec<kGateUp, true>(L, da, it);
+      run_item_dec<kGateUp, true>(L, da, it, poison);
     else
-      run_item_dec<kGateUp, false>(L, da, it);
+      run_item_dec<kGateUp, false>(L, da, it, poison);
   }
 }
 
 // y[t] = sum_k slot[t*K + k] + slot[T*K + t], fp32, fixed order (4 columns
-// per thread)
+// per thread; rows of any length: the slot rows have stride SP, a multiple of
+// 4; y rows stride H).  A non-finite y raises COLI_STATUS_NONFINITE.
 __global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ slot, int T, int H,
-                                                   int K, float *__restrict__ y) {
+                                                   int SP, int K, float *__restrict__ y,
+                                                   int32_t *status) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int per_row = H / 4;
-  if (i >= int64_t(T) * per_row) return;
-  const int t = int(i / per_row), c = int(i % per_row) * 4;
-  float4 acc = *reinterpret_cast<const float4 *>(slot + (int64_t(t) * K) * H + c);
-  for (int k = 1; k < K; ++k) {
-    const float4 v = *reinterpret_cast<const float4 *>(slot + (int64_t(t) * K + k) * H + c);
+  const int per_row = SP / 4;
+  bool bad = false;
+  if (i < int64_t(T) * per_row) {
+    const int t = int(i / per_row), c = int(i % per_row) * 4;
+    float4 acc = *reinterpret_cast<const float4 *>(slot + (int64_t(t) * K) * SP + c);
+    for (int k = 1; k < K; ++k) {
+      const float4 v = *reinterpret_cast<const float4 *>(slot + (int64_t(t) * K + k) * SP + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const float4 v = *reinterpret_cast<const float4 *>(slot + (int64_t(T) * K + t) * SP + c);
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    const float a[4] = {acc.x, acc.y, acc.z, acc.w};
+    float *yr = y + int64_t(t) * H;
+    if (c + 4 <= H && (H & 3) == 0) {
+      *reinterpret_cast<float4 *>(yr + c) = acc;
+      bad = !(__builtin_isfinite(a[0]) && __builtin_isfinite(a[1]) && __builtin_isfinite(a[2]) &&
+              __builtin_isfinite(a[3]));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c + k < H) {
+          yr[c + k] = a[k];
+          bad |= !__builtin_isfinite(a[k]);
+        }
+    }
   }
-  const float4 v = *reinterpret_cast<const float4 *>(slot + (int64_t(T) * K + t) * H + c);
-  acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-  *reinterpret_cast<float4 *>(y + int64_t(t) * H + c) = acc;
+  if (__any(bad) && (threadIdx.x % 64) == 0) raise_status(status, COLI_STATUS_NONFINITE);
 }
 
 template <bool kGateUp>
@@ -423,9 +450,7 @@ hipError_t launch_ffn_batch(const LayerDev &L, const float *x, int T, const Rout
                             bool x_staged) {
   const PrefillLayout pl = prefill_layout(L.H, L.I);
   const int64_t TK = int64_t(T) * L.K, R = TK + T;
-  if (int64_t(2) * T * pl.HP * 2 >= (int64_t(1) << 31) || 2 * R * pl.IP * 2 >= (int64_t(1) << 31) ||
-      L.lay.bytes >= (size_t(1) << 31))
-    return hipErrorInvalidValue;
+  const int SP = batch_slot_stride(L.H);
   const int max_units = int((TK < L.E ? TK : L.E) + 1);
   // sum over units of ceil(n_u / 32) <= TK / 32 + routed units + shared chunks
   const int64_t max_chunks = TK / kDMC + max_units + (T + kDMC - 1) / kDMC;
@@ -441,14 +466,25 @@ hipError_t launch_ffn_batch(const LayerDev &L, const float *x, int T, const Rout
   if (ev) (void)hipEventRecord(ev[2], s);
   split_rows<<<dim3(unsigned(R)), 256, 0, s>>>(b.hf, int(R), L.I, pl.IP, b.h16, b.hs);
   {
-    DecArgs da{b.h16, b.hs, b.slot, pl.IP, L.H, int(R), uint32_t(2 * R * pl.IP * 2)};
+    DecArgs da{b.h16, b.hs, b.slot, pl.IP, SP, int(R), uint32_t(2 * R * pl.IP * 2)};
     e = launch_dec_gemm<false>(L, r, T, da, max_chunks * ((L.H + 255) / 256), s);
     if (e != hipSuccess) return e;
   }
-  const int64_t nthr = int64_t(T) * (L.H / 4);
-  combine_f32<<<dim3(unsigned((nthr + 255) / 256)), 256, 0, s>>>(b.slot, T, L.H, L.K, y);
+  const int64_t nthr = int64_t(T) * (SP / 4);
+  combine_f32<<<dim3(unsigned((nthr + 255) / 256)), 256, 0, s>>>(b.slot, T, L.H, SP, L.K, y,
+                                                                 L.status);
   if (ev) (void)hipEventRecord(ev[3], s);
   return hipGetLastError();
 }
+
+bool batch_offsets_ok(int H, int I, int K, int T, size_t blob_bytes) {
+  const PrefillLayout pl = prefill_layout(H, I);
+  const int64_t R = int64_t(T) * K + T;
+  const int64_t lim = int64_t(1) << 31;  // buffer offsets: 32 bits, top bit masks
+  return int64_t(2) * T * pl.HP * 2 < lim && 2 * R * pl.IP * 2 < lim &&
+         int64_t(blob_bytes) < lim;
+}
+
+int batch_slot_stride(int H) { return (H + 3) & ~3; }
 
 }  // namespace coli

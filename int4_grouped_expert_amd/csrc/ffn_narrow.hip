@@ -233,7 +233,7 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   }
   // The first item is the shared expert's (the grid is I / 8 blocks), so its
   // loads are in flight while wave 0 picks the token's experts.
-  if (wave == 0) topk_select<4>(lg, E, K, lane, sidx, sgate);
+  if (wave == 0) topk_select<4>(lg, E, K, lane, sidx, sgate, L.sc);
   lds_barrier();
   if (blockIdx.x == 0 && int(threadIdx.x) < K) {
     idx_out[threadIdx.x] = sidx[threadIdx.x];
@@ -295,7 +295,14 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     const int v = itk / nrb, rb = itk - v * nrb;
     const int u = v > 0 ? v - 1 : K;  // h' rows: routed units in top-K order, shared last
     const float gw = v > 0 ? sgate[v - 1] : 1.0f;
-    nb.hn[size_t(u) * I + rb * 8 + rr] = gw * silu(g * xs) * (up * xs);
+    // a blob without the finish tag has no valid blocked scales: its h' rows
+    // become NaN (and so does y) and the status flag says why
+    const uint8_t *blob = v > 0 ? L.experts + size_t(sidx[v - 1]) * L.lay.bytes : L.shared;
+    const uint4 tg = *reinterpret_cast<const uint4 *>(blob + L.lay.tag);
+    const bool bad = tg.x != L.tag.x || tg.y != L.tag.y || tg.z != L.tag.z || tg.w != L.tag.w;
+    if (bad && rr == 0) raise_status(L.status, COLI_STATUS_UNFINISHED);
+    nb.hn[size_t(u) * I + rb * 8 + rr] =
+        bad ? __builtin_nanf("") : gw * silu(g * xs) * (up * xs);
   }
 }
 
@@ -452,12 +459,15 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
     if (k < nib && lane < 8) red[k][wave][lane] = v;
   }
   lds_barrier();
+  bool bad = false;
   for (int i = threadIdx.x; i < k_it * 8; i += blockDim.x) {
     const int k = i / 8, rr = i % 8;
     float t = 0.0f;
     for (int w = 0; w < nw; ++w) t += red[k][w][rr];
     y[(size_t(blockIdx.x) + size_t(k) * gridDim.x) * 8 + rr] = t;
+    bad |= !__builtin_isfinite(t);
   }
+  if (__any(bad) && lane == 0) raise_status(L.status, COLI_STATUS_NONFINITE);
 }
 
 int cu_count() {

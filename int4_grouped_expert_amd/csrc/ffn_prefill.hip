@@ -45,8 +45,12 @@
 // A operand is one 16-byte run.  Rows are padded to whole 4-group blocks; the
 // padding holds zeros.
 //
-// Numerics: fp16 operands, fp32 accumulation.  Activations must lie in fp16
-// range and scales below 64 (|w| < 448).
+// Numerics: fp16 operands, fp32 accumulation.  Each token's activations are
+// scaled by a power of two 2^-e (the row's largest |x| then lies in [2, 4))
+// before the fp16 conversion, and its h by 2^-2e, so rows of any magnitude
+// keep fp16 precision; the combine multiplies y back by 2^2e.  Group scales
+// must stay below 64 (|w| < 448) for the -1024 s constant; an fp16 operand
+// that would overflow (h or a slot output) raises COLI_STATUS_RANGE.
 //
 // Kernels: pf_prep (x bf16 -> fp16 staged copy + group sums), pf_pads (zero
 // the padding of the h and h-sum rows), prefill_tiles (M-chunk prefix over units),
@@ -55,6 +59,7 @@
 // token's slots + its shared output, bf16).
 #include "gemm_stream.h"
 #include "kernels.h"
+#include "wave.h"
 
 #include <hip/hip_fp16.h>
 
@@ -73,50 +78,87 @@ __device__ inline uint32_t split_f16(float v) {
 }
 
 // ------------------------------------------------------------------ prep
-// x bf16 [T, H] -> xp fp16 [T, HP] in the staged order, zero padding, and
-// sx [T, CSX]: the hi/lo fp16 pair of each group's sum of the fp16 values.
-// Thread = (token, group slot g < HP/64, 8-position run c); the 8 threads of
-// a group are consecutive lanes.
+// One block per token: x bf16 [T, H] (any H, any alignment) -> xp fp16 [T, HP]
+// in the staged order with zero padding, scaled by 2^-e (e chosen from the
+// row's largest |x| so that it lies in [2, 4)), and sx [T, CSX]: the hi/lo
+// fp16 pair of each group's sum of the scaled fp16 values.  xe[t] = e.  A
+// non-finite x raises COLI_STATUS_NONFINITE; a scaled value beyond the fp16
+// range cannot occur (the row's largest is below 4).
+// Thread = (group g, 8-position run c) slots of the row, strided by 256.
 __global__ __launch_bounds__(256) void pf_prep(const uint16_t *__restrict__ x, int T, int H,
                                                int HP, int CSX, uint16_t *__restrict__ xp,
-                                               uint16_t *__restrict__ sx) {
-  const int G = H / 64, GP = HP / 64;
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int c = int(i & 7);
-  const int64_t tg = i >> 3;
-  if (tg >= int64_t(T) * GP) return;  // whole groups of 8 lanes leave together
-  const int t = int(tg / GP), g = int(tg % GP);
-  const int o = 16 * (c >> 2) + 4 * (c & 3);
-  uint4 out = uint4{0u, 0u, 0u, 0u};
-  float sum = 0.0f;
-  if (g < G) {
-    const uint16_t *src = x + int64_t(t) * H + 64 * g + o;
-    const uint2 lo = *reinterpret_cast<const uint2 *>(src);
-    const uint2 hi = *reinterpret_cast<const uint2 *>(src + 32);
-    // b = elements o + {0, 1, 2, 3, 32, 33, 34, 35}
-    const uint16_t b[8] = {uint16_t(lo.x), uint16_t(lo.x >> 16), uint16_t(lo.y),
-                           uint16_t(lo.y >> 16), uint16_t(hi.x), uint16_t(hi.x >> 16),
-                           uint16_t(hi.y), uint16_t(hi.y >> 16)};
-    // staged order o + {0, 2, 32, 34, 1, 3, 33, 35}
-    const int ord[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-    _Float16 h[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      h[k] = _Float16(__uint_as_float(uint32_t(b[ord[k]]) << 16));
-      sum += float(h[k]);
-    }
-    out = uint4{pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3]), pack_f16x2(h[4], h[5]),
-                pack_f16x2(h[6], h[7])};
+                                               uint16_t *__restrict__ sx, int *__restrict__ xe,
+                                               int32_t *status) {
+  __shared__ float red[4];
+  __shared__ int rbad[4];
+  const int t = blockIdx.x;
+  const int G = (H + 63) / 64, GP = HP / 64;
+  const uint16_t *row = x + int64_t(t) * H;
+  // the row's largest |x| (bit patterns: NaN > Inf > every finite value)
+  uint32_t mb = 0;
+  for (int i = threadIdx.x; i < H; i += 256) mb = max(mb, uint32_t(row[i]) & 0x7FFFu);
+  const uint32_t wm = wave_max_u32(mb);
+  if (threadIdx.x % 64 == 0) {
+    red[threadIdx.x / 64] = __uint_as_float(wm << 16);
+    rbad[threadIdx.x / 64] = wm >= 0x7F80u;
   }
-  sum += __shfl_xor(sum, 1, 8);
-  sum += __shfl_xor(sum, 2, 8);
-  sum += __shfl_xor(sum, 4, 8);
-  *reinterpret_cast<uint4 *>(xp + int64_t(t) * HP + 64 * g + 8 * c) = out;
-  if (c == 0 && g < G)
-    *reinterpret_cast<uint32_t *>(sx + int64_t(t) * CSX + 2 * g) = split_f16(sum);
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const bool bad = rbad[0] | rbad[1] | rbad[2] | rbad[3];
+  int e = 0;
+  if (m > 0.0f && !bad) {
+    int ex = 0;
+    (void)frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
+    e = ex - 2;            // m * 2^-e in [2, 4)
+  }
+  if (threadIdx.x == 0) {
+    xe[t] = e;
+    if (bad) raise_status(status, COLI_STATUS_NONFINITE);
+  }
+  const bool fast = (H % 64) == 0 && (reinterpret_cast<uintptr_t>(row) & 7) == 0;
+  const int ord[8] = {0, 2, 4, 6, 1, 3, 5, 7};  // staged order o + {0, 2, 32, 34, 1, 3, 33, 35}
+  for (int i = threadIdx.x; i < GP * 8; i += 256) {
+    const int g = i >> 3, c = i & 7;
+    const int o = 16 * (c >> 2) + 4 * (c & 3);
+    uint4 out = uint4{0u, 0u, 0u, 0u};
+    float sum = 0.0f;
+    if (g < G) {
+      // b = elements o + {0, 1, 2, 3, 32, 33, 34, 35} of the group
+      uint16_t b[8];
+      const int base = 64 * g + o;
+      if (fast) {
+        const uint2 lo = *reinterpret_cast<const uint2 *>(row + base);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(row + base + 32);
+        b[0] = uint16_t(lo.x); b[1] = uint16_t(lo.x >> 16); b[2] = uint16_t(lo.y);
+        b[3] = uint16_t(lo.y >> 16); b[4] = uint16_t(hi.x); b[5] = uint16_t(hi.x >> 16);
+        b[6] = uint16_t(hi.y); b[7] = uint16_t(hi.y >> 16);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          b[k] = base + k < H ? row[base + k] : uint16_t(0);
+          b[4 + k] = base + 32 + k < H ? row[base + 32 + k] : uint16_t(0);
+        }
+      }
+      _Float16 h[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        h[k] = _Float16(ldexpf(__uint_as_float(uint32_t(b[ord[k]]) << 16), -e));
+        sum += float(h[k]);
+      }
+      out = uint4{pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3]), pack_f16x2(h[4], h[5]),
+                  pack_f16x2(h[6], h[7])};
+    }
+    // the 8 runs of a group are 8 consecutive lanes
+    sum += __shfl_xor(sum, 1, 8);
+    sum += __shfl_xor(sum, 2, 8);
+    sum += __shfl_xor(sum, 4, 8);
+    *reinterpret_cast<uint4 *>(xp + int64_t(t) * HP + 64 * g + 8 * c) = out;
+    if (c == 0 && g < G)
+      *reinterpret_cast<uint32_t *>(sx + int64_t(t) * CSX + 2 * g) = split_f16(sum);
+  }
   // the row's padding entries (groups G .. CSX/2 - 1) are zeros
-  if (c == 0 && g == 0)
-    for (int e = 2 * G; e < CSX; e += 2) *reinterpret_cast<uint32_t *>(sx + int64_t(t) * CSX + e) = 0u;
+  for (int k = 2 * G + 2 * int(threadIdx.x); k < CSX; k += 512)
+    *reinterpret_cast<uint32_t *>(sx + int64_t(t) * CSX + k) = 0u;
 }
 
 // Zero the padding of every h row (groups G..IP/64-1, all in the last 256-k
@@ -166,10 +208,12 @@ __global__ __launch_bounds__(1024) void prefill_tiles(Routing r, int T) {
 struct PfArgs {
   const uint16_t *A;  // staged activations, row stride AP (elements)
   const uint16_t *S;  // group-sum pairs, row stride CS
-  uint16_t *out;      // gate/up: h (row stride OP); down: slot (row stride OP = H)
+  uint16_t *out;      // gate/up: h (row stride OP); down: slot (row stride OP = H rounded
+                      // up to 8)
   uint16_t *sout;     // gate/up: sh (row stride SOP)
   int AP, CS, OP, SOP;
   uint32_t a_bytes, s_bytes;  // sizes of A and S (< 2^31)
+  const int *xe;              // per-token activation exponents (gate/up)
 };
 
 // m1 = 0x000F000F, m2 = 0x00F000F0 held in VGPRs: gfx9 VOP3 takes no literal
@@ -211,6 +255,7 @@ __shared__ __attribute__((aligned(16))) uint8_t g_sc1[kCorrB];
 __shared__ int g_rowidx[kMC];   // A / S row of each chunk row (-1: padding)
 __shared__ int g_outrow[kMC];   // output row
 __shared__ float g_gate[kMC];   // gate (down)
+__shared__ int g_xe[kMC];       // the token's activation exponent (gate/up)
 
 // One work item.  NMF = number of 32-row M fragments the chunk needs (1..4).
 template <bool kGateUp, int NMF>
@@ -529,18 +574,26 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
   int tid = int(threadIdx.x);
   asm volatile("" : "+v"(tid));
   const int eh = (tid & 63) >> 5, en = tid & 31;
+  bool range = false;  // an fp16 operand out of range: COLI_STATUS_RANGE
   if (kGateUp) {
-    // tile row m: the N-tile's 128 features of h in staged order (2 groups, 256 B)
+    // tile row m: the N-tile's 128 features of h in staged order (2 groups, 256 B).
+    // The row's activations were scaled by 2^-e: gate = 2^e acc_g, up = 2^e acc_u,
+    // and h is stored scaled by 2^-2e: SiLU(2^e acc_g) * acc_u * 2^-e.  Features
+    // past I (a ragged last group) are zeros.
     if (wvalid) {
       const int fl = 32 * wave + en;  // feature within the N-tile
       const int tpos = 2 * (64 * (fl >> 6) + grp_pos(fl & 63));
+      const bool fvalid = wrow0 + en < L.I;
 #pragma unroll
       for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = 32 * mf + 8 * (v >> 2) + 4 * eh + (v & 3);
-          const _Float16 hv = _Float16(silu(acc[mf][0][v]) * acc[mf][1][v]);
-          *reinterpret_cast<_Float16 *>(tile + m * 256 + tpos) = hv;
+          const int fe = g_xe[m];
+          float hf = silu(ldexpf(acc[mf][0][v], fe)) * ldexpf(acc[mf][1][v], -fe);
+          hf = fvalid ? hf : 0.0f;
+          range |= !(fabsf(hf) <= 65504.0f);
+          *reinterpret_cast<_Float16 *>(tile + m * 256 + tpos) = _Float16(hf);
         }
     }
     __syncthreads();
@@ -578,7 +631,8 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
       }
     }
   } else {
-    // tile row m: the N-tile's 256 gate-scaled outputs
+    // tile row m: the N-tile's 256 gate-scaled outputs (still scaled by the
+    // token's 2^-2e; the combine undoes it); outputs past H are zeros
     if (wvalid) {
 #pragma unroll
       for (int mf = 0; mf < NMF; ++mf)
@@ -587,9 +641,13 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
           const int m = 32 * mf + 8 * (v >> 2) + 4 * eh + (v & 3);
           const float gate = g_gate[m];
 #pragma unroll
-          for (int jn = 0; jn < 2; ++jn)
+          for (int jn = 0; jn < 2; ++jn) {
+            float o = gate * acc[mf][jn][v];
+            o = wrow0 + 32 * jn + en < L.H ? o : 0.0f;
+            range |= !(fabsf(o) <= 65504.0f);
             *reinterpret_cast<_Float16 *>(tile + m * 512 + 2 * (64 * wave + 32 * jn + en)) =
-                _Float16(gate * acc[mf][jn][v]);
+                _Float16(o);
+          }
         }
     }
     __syncthreads();
@@ -606,6 +664,7 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
       }
     }
   }
+  if (__any(range) && (threadIdx.x % kWave) == 0) raise_status(L.status, COLI_STATUS_RANGE);
 }
 
 // Persistent grouped GEMM: blocks walk (chunk, N-tile) items.  With a grid
@@ -667,6 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_gemm(LayerDev L, Routing r, in
       g_rowidx[threadIdx.x] = ri;
       g_outrow[threadIdx.x] = orow;
       g_gate[threadIdx.x] = gate;
+      g_xe[threadIdx.x] = (kGateUp && ri >= 0) ? pa.xe[ri] : 0;
     }
     __syncthreads();
     const int nmf = (it.je - it.jb + 31) / 32;
@@ -685,32 +745,50 @@ __device__ inline uint16_t f32_to_bf16_rne(float v) {
   return uint16_t((u + ((u >> 16) & 1u) + 0x7FFFu) >> 16);
 }
 
-// y[t] = sum_k slot[t*K + k] + slot[T*K + t]   (fp16 slots, fp32 sum, bf16 y;
-// 8 columns per thread)
+// y[t] = 2^(2 e_t) (sum_k slot[t*K + k] + slot[T*K + t])   (fp16 slots of
+// stride SP, a multiple of 8; fp32 sum; bf16 y of any H; 8 columns per
+// thread).  A non-finite y raises COLI_STATUS_NONFINITE.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ slot, int T,
-                                                      int H, int K, uint16_t *__restrict__ y) {
+                                                      int H, int SP, int K,
+                                                      const int *__restrict__ xe,
+                                                      uint16_t *__restrict__ y, int32_t *status) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int per_row = H / 8;
-  if (i >= int64_t(T) * per_row) return;
-  const int t = int(i / per_row), c = int(i % per_row) * 8;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k <= K; ++k) {
-    const int64_t row = k < K ? int64_t(t) * K + k : int64_t(T) * K + t;
-    const uint4 v = *reinterpret_cast<const uint4 *>(slot + row * H + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int per_row = SP / 8;
+  bool bad = false;
+  if (i < int64_t(T) * per_row) {
+    const int t = int(i / per_row), c = int(i % per_row) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k <= K; ++k) {
+      const int64_t row = k < K ? int64_t(t) * K + k : int64_t(T) * K + t;
+      const uint4 v = *reinterpret_cast<const uint4 *>(slot + row * SP + c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f16x2 hv = __builtin_bit_cast(f16x2, w[q]);
-      acc[2 * q] += float(hv[0]);
-      acc[2 * q + 1] += float(hv[1]);
+      for (int q = 0; q < 4; ++q) {
+        const f16x2 hv = __builtin_bit_cast(f16x2, w[q]);
+        acc[2 * q] += float(hv[0]);
+        acc[2 * q + 1] += float(hv[1]);
+      }
+    }
+    const int e2 = 2 * xe[t];
+    uint16_t o[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float v = ldexpf(acc[q], e2);
+      bad |= (c + q < H) && !__builtin_isfinite(v);
+      o[q] = f32_to_bf16_rne(v);
+    }
+    uint16_t *yr = y + int64_t(t) * H;
+    if ((H & 7) == 0) {
+      *reinterpret_cast<uint4 *>(yr + c) =
+          uint4{uint32_t(o[0]) | (uint32_t(o[1]) << 16), uint32_t(o[2]) | (uint32_t(o[3]) << 16),
+                uint32_t(o[4]) | (uint32_t(o[5]) << 16), uint32_t(o[6]) | (uint32_t(o[7]) << 16)};
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (c + q < H) yr[c + q] = o[q];
     }
   }
-  uint32_t o[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    o[q] = uint32_t(f32_to_bf16_rne(acc[2 * q])) |
-           (uint32_t(f32_to_bf16_rne(acc[2 * q + 1])) << 16);
-  *reinterpret_cast<uint4 *>(y + int64_t(t) * H + c) = uint4{o[0], o[1], o[2], o[3]};
+  if (__any(bad) && (threadIdx.x % 64) == 0) raise_status(status, COLI_STATUS_NONFINITE);
 }
 
 template <bool kGateUp>
@@ -738,19 +816,13 @@ hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T, const
                               const PrefillBufs &b, uint16_t *y, hipStream_t s, hipEvent_t *ev) {
   const PrefillLayout pl = prefill_layout(L.H, L.I);
   const int64_t TK = int64_t(T) * L.K;
-  // buffer-resource offsets are 32-bit with the top bit reserved for masking
-  if (int64_t(T) * pl.HP * 2 >= (int64_t(1) << 31) || (TK + T) * pl.IP * 2 >= (int64_t(1) << 31) ||
-      L.lay.bytes >= (size_t(1) << 31))
-    return hipErrorInvalidValue;
+  const int SP = prefill_slot_stride(L.H);
+  const int GI = int(groups_of(L.I));
   if (ev) (void)hipEventRecord(ev[0], s);
-  {
-    const int64_t n = int64_t(T) * (pl.HP / 64) * 8;
-    pf_prep<<<dim3(unsigned((n + 255) / 256)), 256, 0, s>>>(x, T, L.H, pl.HP, pl.CSX, b.xp, b.sx);
-  }
-  if (pl.IP > L.I || pl.CSI > 2 * (L.I / 64)) {
+  pf_prep<<<dim3(unsigned(T)), 256, 0, s>>>(x, T, L.H, pl.HP, pl.CSX, b.xp, b.sx, b.xe, L.status);
+  if (pl.IP > 64 * GI || pl.CSI > 2 * GI) {
     const int64_t rows = TK + T;
-    pf_pads<<<dim3(unsigned((rows + 255) / 256)), 256, 0, s>>>(b.h, b.sh, rows, L.I / 64, pl.IP,
-                                                               pl.CSI);
+    pf_pads<<<dim3(unsigned((rows + 255) / 256)), 256, 0, s>>>(b.h, b.sh, rows, GI, pl.IP, pl.CSI);
   }
   prefill_tiles<<<1, 1024, 0, s>>>(r, T);
   if (ev) (void)hipEventRecord(ev[1], s);
@@ -761,24 +833,35 @@ hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T, const
   if (ev) (void)hipEventRecord(ev[2], s);
   {
     PfArgs pa{b.xp, b.sx, b.h, b.sh, pl.HP, pl.CSX, pl.IP, pl.CSI,
-              uint32_t(int64_t(T) * pl.HP * 2), uint32_t(int64_t(T) * pl.CSX * 2)};
+              uint32_t(int64_t(T) * pl.HP * 2), uint32_t(int64_t(T) * pl.CSX * 2), b.xe};
     e = launch_gemm<true>(L, r, T, pa, max_chunks * ((L.I + 127) / 128), s);
     if (e != hipSuccess) return e;
   }
   if (ev) (void)hipEventRecord(ev[3], s);
   if (ev) (void)hipEventRecord(ev[4], s);
   {
-    PfArgs pa{b.h, b.sh, b.slot, nullptr, pl.IP, pl.CSI, L.H, 0,
-              uint32_t((TK + T) * pl.IP * 2), uint32_t((TK + T) * pl.CSI * 2)};
+    PfArgs pa{b.h, b.sh, b.slot, nullptr, pl.IP, pl.CSI, SP, 0,
+              uint32_t((TK + T) * pl.IP * 2), uint32_t((TK + T) * pl.CSI * 2), b.xe};
     e = launch_gemm<false>(L, r, T, pa, max_chunks * ((L.H + 255) / 256), s);
     if (e != hipSuccess) return e;
   }
   if (ev) (void)hipEventRecord(ev[5], s);
-  const int64_t nthr = int64_t(T) * (L.H / 8);
+  const int64_t nthr = int64_t(T) * (SP / 8);
   if (ev) (void)hipEventRecord(ev[6], s);
-  combine_kernel<<<dim3(unsigned((nthr + 255) / 256)), 256, 0, s>>>(b.slot, T, L.H, L.K, y);
+  combine_kernel<<<dim3(unsigned((nthr + 255) / 256)), 256, 0, s>>>(b.slot, T, L.H, SP, L.K, b.xe,
+                                                                    y, L.status);
   if (ev) (void)hipEventRecord(ev[7], s);
   return hipGetLastError();
 }
+
+bool prefill_offsets_ok(int H, int I, int K, int T, size_t blob_bytes) {
+  const PrefillLayout pl = prefill_layout(H, I);
+  const int64_t R = int64_t(T) * K + T;
+  const int64_t lim = int64_t(1) << 31;  // buffer offsets: 32 bits, top bit masks
+  return int64_t(T) * pl.HP * 2 < lim && R * pl.IP * 2 < lim &&
+         int64_t(T) * pl.CSX * 2 < lim && R * pl.CSI * 2 < lim && int64_t(blob_bytes) < lim;
+}
+
+int prefill_slot_stride(int H) { return (H + 7) & ~7; }
 
 }  // namespace coli

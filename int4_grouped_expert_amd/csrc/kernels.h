@@ -26,6 +26,7 @@ struct BlobLayout {
   size_t gq, uq, dq, gs, us, ds;
   size_t gsT, usT, dsT;  // the scales again, group-major ([G][rows]; coli_expert_finish)
   size_t gsB, usB, dsB;  // and blocked by 8 rows ([ceil(rows/8)][G][8]; coli_expert_finish)
+  size_t tag;            // 16-byte finish tag (coli_expert_finish; checked by the decode paths)
   size_t bytes;
   int64_t GH, GI;  // groups per row of gate/up (input H) and of down (input I)
 };
@@ -46,9 +47,20 @@ inline BlobLayout blob_layout(int H, int I) {
   b.gsB = o; o += align256(size_t((I + 7) / 8) * 8 * b.GH * 4);
   b.usB = o; o += align256(size_t((I + 7) / 8) * 8 * b.GH * 4);
   b.dsB = o; o += align256(size_t((H + 7) / 8) * 8 * b.GI * 4);
+  b.tag = o; o += 256;
   b.bytes = o;
   return b;
 }
+
+// Scoring of the router.  softmax (sigmoid == 0): the logits are the keys and
+// the gates are the softmax over the selected logits.  sigmoid (page "Colibrì
+// 深度解析", section 十一: one expert group, sigmoid scores, selection without
+// an auxiliary loss): score s = 1 / (1 + e^-l), key = s + bias[e] (the bias
+// only steers the selection), gates = the selected scores over their sum.
+struct Scoring {
+  int sigmoid;
+  const float *bias;  // selection bias [E] (sigmoid only; NULL = 0)
+};
 
 // Device-side view of the routing products, all inside the workspace.
 struct Routing {
@@ -61,6 +73,7 @@ struct Routing {
   int32_t *unique;   // [E]
   int32_t *n_unique; // [1]
   int32_t *chunk;    // [n_chunks * E] per-chunk counts / bases (large T)
+  Scoring sc;        // how the top-K scores the logits
 };
 
 
@@ -78,13 +91,33 @@ struct NarrowBufs {
 };
 #define COLI_NARROW_MAX_K 16
 
+// The finish tag of a blob of shape (H, I): written last by
+// coli_expert_finish, compared by every kernel that reads the derived scale
+// copies ('COLI', 'FIN1', H, I).
+inline uint4 finish_tag(int H, int I) {
+  uint4 t;
+  t.x = 0x494C4F43u;
+  t.y = 0x314E4946u;
+  t.z = uint32_t(H);
+  t.w = uint32_t(I);
+  return t;
+}
+
 // One layer as the kernels see it.
 struct LayerDev {
   int H, I, E, K;
   const uint8_t *experts;
   const uint8_t *shared;
   BlobLayout lay;
+  uint4 tag;        // finish_tag(H, I)
+  int32_t *status;  // optional device flag: COLI_STATUS_* bits OR-ed in
+  Scoring sc;       // router scoring (the fused single-token top-K)
 };
+
+// Device side of the status flag: OR bits into *status (if any) from one lane.
+__device__ inline void raise_status(int32_t *status, int bits) {
+  if (status) atomicOr(status, bits);
+}
 
 // ---- quant.hip ----------------------------------------------------------
 hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
@@ -100,28 +133,35 @@ hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
                                 const void *wr, int w_bf16, int E,
                                 const float *bias, float *logits, hipStream_t s,
                                 uint16_t *xp = nullptr, float *xs = nullptr, int HP = 0);
-// Prefill router: bf16 x and bf16 Wr through MFMA, then the top-K.  part:
-// scratch for the K-split partial sums (part_bytes; a smaller split is used
-// when S * T * E floats do not fit).
-hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
-                                   const uint16_t *wr, int E,
-                                   const float *bias, int K, float *logits,
-                                   int32_t *idx, float *gates, float *part,
-                                   size_t part_bytes, hipStream_t s);
+// Prefill router logits: bf16 x and bf16 Wr through MFMA (H % 32 == 0).
+// part: scratch for the K-split partial sums (part_bytes; a smaller split is
+// used when S * T * E floats do not fit).
+hipError_t launch_router_mfma(const uint16_t *x, int T, int H, const uint16_t *wr, int E,
+                              const float *bias, float *logits, float *part, size_t part_bytes,
+                              hipStream_t s);
+// Logits for any H and row alignment (element loads).
+hipError_t launch_router_any(const void *x, int x_bf16, int T, int H, const void *wr,
+                             int w_bf16, int E, const float *bias, float *logits,
+                             hipStream_t s);
+// Whether the 16-byte-load router kernels take these operands.
+bool router_vec_ok(const void *x, int x_bf16, int H, const void *wr, int w_bf16);
+// Logits and top-K per token in one launch, the logits kept on chip.
+hipError_t launch_router_topk_fused(const void *x, int x_bf16, int T, int H, const void *wr,
+                                    int w_bf16, int E, int K, const float *logit_bias,
+                                    Scoring sc, int32_t *idx, float *gates, hipStream_t s);
 // top-K + gates from logits, one wave per token.
 hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *idx,
-                       float *gates, hipStream_t s);
+                       float *gates, Scoring sc, hipStream_t s);
 // top-K + gates from logits (do_topk), then the batch-union permute.  For
-// T above a small threshold the permute uses r.chunk, permute_chunk_ints()
-// ints of scratch.
+// T * K above a small threshold the permute uses r.chunk,
+// permute_chunk_ints() ints of scratch.
 hipError_t launch_topk_permute(const Routing &r, int T, int E, int K,
                                int do_topk, hipStream_t s);
-// Decode: one block does top-K, the permute, the per-unit M-chunk prefix
-// (r.chunk, chunks of 32 tokens, the shared unit last) and the slot map.
-// Requires T <= COLI_MAX_DECODE_T.
-hipError_t launch_route_decode(const Routing &r, int T, int E, int K,
-                               int32_t *slotmap, hipStream_t s);
-size_t permute_chunk_ints(int T, int E);
+// Decode: one block does top-K, the permute and the per-unit M-chunk prefix
+// (r.chunk, chunks of 32 tokens, the shared unit last).  Requires
+// T <= COLI_MAX_DECODE_T.
+hipError_t launch_route_decode(const Routing &r, int T, int E, int K, hipStream_t s);
+size_t permute_chunk_ints(int T, int K, int E);
 // Single-token decode router: logits [T, E] and x as digit planes (nb.xdig,
 // nb.xcorr, nb.xsc).  Requires H % 256 == 0, T <= 4.
 // start/stop: optional events stamped at the kernel's start and end.
@@ -149,14 +189,19 @@ struct PrefillLayout {
 };
 PrefillLayout prefill_layout(int H, int I);
 // Prefill buffers (inside the workspace): xp [T, HP] fp16, sx [T, CSX],
-// h [T*K + T, IP] fp16, sh [T*K + T, CSI], slot [T*K + T, H] fp16.
+// h [T*K + T, IP] fp16, sh [T*K + T, CSI], slot [T*K + T, SP] fp16
+// (SP = prefill_slot_stride(H)), xe [T] the per-token activation exponents.
 struct PrefillBufs {
   uint16_t *xp, *sx, *h, *sh, *slot;
+  int *xe;
 };
 // ev: optional stage events (NULL or 8: start and stop of prep + tiles, gate/up,
 // down, combine).
 hipError_t launch_ffn_prefill(const LayerDev &L, const uint16_t *x, int T, const Routing &r,
                               const PrefillBufs &b, uint16_t *y, hipStream_t s, hipEvent_t *ev);
+// Whether every prefill buffer offset fits the 31 bits of a buffer resource.
+bool prefill_offsets_ok(int H, int I, int K, int T, size_t blob_bytes);
+int prefill_slot_stride(int H);
 
 // Decode batch (1 < T <= 256) on the same grouped-GEMM weight stream:
 // xp: x as staged fp16 hi/lo rows [2T][HP] (hi rows first), xs [T] row scales;
@@ -176,6 +221,10 @@ struct BatchBufs {
 hipError_t launch_ffn_batch(const LayerDev &L, const float *x, int T, const Routing &r,
                             const BatchBufs &b, float *y, hipStream_t s, hipEvent_t *ev,
                             bool x_staged = false);
+// Whether every decode-batch buffer offset fits the 31 bits of a buffer resource.
+bool batch_offsets_ok(int H, int I, int K, int T, size_t blob_bytes);
+// Row stride (floats) of the decode batch's per-slot outputs.
+int batch_slot_stride(int H);
 
 // Group-major copies of a blob's three scale sections (gs -> gsT etc.).
 hipError_t launch_expert_finish(uint8_t *blob, const BlobLayout &lay, int H, int I,

@@ -156,6 +156,11 @@ __global__ __launch_bounds__(256) void scales_blocked8(const float *__restrict__
   dst[i] = o < rows ? src[o * G + g] : 0.0f;
 }
 
+// The finish tag of a blob (one 16-byte vector store).
+__global__ void write_tag(uint4 *dst, uint4 tag) {
+  if (threadIdx.x == 0) *dst = tag;
+}
+
 }  // namespace
 
 hipError_t launch_expert_finish(uint8_t *blob, const BlobLayout &lay, int H, int I,
@@ -178,6 +183,8 @@ hipError_t launch_expert_finish(uint8_t *blob, const BlobLayout &lay, int H, int
         reinterpret_cast<const float *>(blob + m[k].src), reinterpret_cast<float *>(blob + bdst[k]),
         m[k].rows, m[k].G);
   }
+  // the tag goes last, in stream order after the copies it vouches for
+  write_tag<<<1, 64, 0, s>>>(reinterpret_cast<uint4 *>(blob + lay.tag), finish_tag(H, I));
   return hipGetLastError();
 }
 

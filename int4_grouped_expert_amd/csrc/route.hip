@@ -19,8 +19,12 @@
 //   topk_permute_small    one block: top-K for all tokens, then the permute
 //                         (decode: one launch for the whole route stage).
 //   permute_count/scan/place  the permute for large T in three launches:
-//                         per-chunk (64 tokens) expert bitmaps, a scan over
+//                         per-chunk (64 pairs) expert bitmaps, a scan over
 //                         chunks, then stable placement by bitmap popcount.
+//   router_logits_any     logits for any H and any row alignment (scalar
+//                         loads), the fallback of the vector kernels.
+//   router_topk_fused     logits of one token kept in LDS, then its top-K:
+//                         the router when the caller wants no logits array.
 #include <hip/hip_ext.h>
 
 #include "kernels.h"
@@ -379,19 +383,72 @@ __global__ __launch_bounds__(256) void router_sum_parts(const float *__restrict_
   logits[i] = v + (bias ? bias[i % E] : 0.0f);
 }
 
+// ---------------------------------------------------------------- logits (any H)
+__device__ inline float load_any(const void *base, int bf16, size_t i) {
+  return bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(base)[i])
+              : reinterpret_cast<const float *>(base)[i];
+}
+
+// grid (ceil(E / 4), T): wave w of block b computes the logit of expert 4b + w
+// for token blockIdx.y (lanes stride H, element loads, fixed-order wave sum).
+__global__ __launch_bounds__(256) void router_logits_any(const void *__restrict__ x, int x_bf16,
+                                                         int T, int H, const void *__restrict__ wr,
+                                                         int w_bf16, int E,
+                                                         const float *__restrict__ bias,
+                                                         float *__restrict__ logits) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int e = int(blockIdx.x) * 4 + wave, t = blockIdx.y;
+  if (e >= E) return;
+  float acc = 0.0f;
+  for (int h = lane; h < H; h += kWave)
+    acc = fmaf(load_any(wr, w_bf16, size_t(e) * H + h), load_any(x, x_bf16, size_t(t) * H + h),
+               acc);
+  acc = wave_sum(acc);
+  if (lane == 0) logits[size_t(t) * E + e] = acc + (bias ? bias[e] : 0.0f);
+}
+
+// One block per token: the E logits (any H) go to LDS, then wave 0 selects the
+// top-K from there; no logits array in memory.  logit_bias is added to the
+// logits (softmax scoring); sc.bias is the sigmoid scoring's selection bias.
+__global__ __launch_bounds__(256) void router_topk_fused(const void *__restrict__ x, int x_bf16,
+                                                         int H, const void *__restrict__ wr,
+                                                         int w_bf16, int E, int K,
+                                                         const float *__restrict__ logit_bias,
+                                                         Scoring sc, int32_t *__restrict__ idx,
+                                                         float *__restrict__ gates) {
+  __shared__ float lg[COLI_MAX_EXPERTS];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int t = blockIdx.x;
+  for (int e = wave; e < E; e += 4) {
+    float acc = 0.0f;
+    for (int h = lane; h < H; h += kWave)
+      acc = fmaf(load_any(wr, w_bf16, size_t(e) * H + h), load_any(x, x_bf16, size_t(t) * H + h),
+                 acc);
+    acc = wave_sum(acc);
+    if (lane == 0) lg[e] = acc + (logit_bias ? logit_bias[e] : 0.0f);
+  }
+  __syncthreads();
+  if (wave == 0) wave_topk(lg, E, K, lane, idx + size_t(t) * K, gates + size_t(t) * K, sc);
+}
+
 // grid: ceil(T/4) blocks of 4 waves; one wave per token.
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
                                                    int T, int E, int K,
                                                    int32_t *__restrict__ idx,
-                                                   float *__restrict__ gates) {
+                                                   float *__restrict__ gates, Scoring sc) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
-  wave_topk(logits + size_t(t) * E, E, K, lane, idx + size_t(t) * K, gates + size_t(t) * K);
+  wave_topk(logits + size_t(t) * E, E, K, lane, idx + size_t(t) * K, gates + size_t(t) * K, sc);
 }
 
 // ---------------------------------------------------------------- permute
-constexpr int kChunk = 64;  // tokens per bitmap chunk (one bit per token)
+// The permute walks the T*K (token, slot) pairs p = t*K + slot in chunks of 64
+// pairs: per chunk, bm[e] has bit (p - p0) set if pair p chose expert e, and a
+// pair's rank inside its expert's segment is the expert's base plus the pairs
+// of the chunk before it (a popcount).  Counting pairs, not tokens, keeps the
+// placement stable and complete when a row names the same expert twice.
+constexpr int kChunk = 64;  // pairs per bitmap chunk (one bit per pair)
 
 // Block-wide exclusive scan of one int per thread (blockDim.x <= 1024).
 __device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
@@ -420,34 +477,28 @@ __device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
   return res;
 }
 
-// Bitmap of one 64-token chunk: bm[e] bit (t - t0) set if token t chose e.
-__device__ void build_bitmap(const int32_t *__restrict__ idx, int T, int K, int E,
-                             int t0, unsigned long long *bm) {
+// Bitmap of the pair chunk starting at p0: bm[e] bit (p - p0) set if pair p
+// (p < P = T*K) chose e.
+__device__ void build_bitmap(const int32_t *__restrict__ idx, int P, int E, int p0,
+                             unsigned long long *bm) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) bm[e] = 0ull;
   __syncthreads();
-  const int tend = min(T, t0 + kChunk);
-  const int npairs = (tend - t0) * K;
-  for (int q = threadIdx.x; q < npairs; q += blockDim.x) {
-    const int p = t0 * K + q;
-    const int t = p / K;
+  const int pend = min(P, p0 + kChunk);
+  for (int p = p0 + int(threadIdx.x); p < pend; p += blockDim.x) {
     const int e = idx[p];
-    if (e >= 0 && e < E) atomicOr(&bm[e], 1ull << (t - t0));
+    if (e >= 0 && e < E) atomicOr(&bm[e], 1ull << (p - p0));
   }
   __syncthreads();
 }
 
-__device__ void place_chunk(const int32_t *__restrict__ idx, int T, int K, int E, int t0,
+__device__ void place_chunk(const int32_t *__restrict__ idx, int P, int E, int p0,
                             const unsigned long long *bm, const int *base,
                             int32_t *__restrict__ perm) {
-  const int tend = min(T, t0 + kChunk);
-  const int npairs = (tend - t0) * K;
-  for (int q = threadIdx.x; q < npairs; q += blockDim.x) {
-    const int p = t0 * K + q;
-    const int t = p / K;
+  const int pend = min(P, p0 + kChunk);
+  for (int p = p0 + int(threadIdx.x); p < pend; p += blockDim.x) {
     const int e = idx[p];
     if (e < 0 || e >= E) continue;  // ids outside [0, E) are skipped
-    const int rank = base[e] + __popcll(bm[e] & ((1ull << (t - t0)) - 1ull));
-    perm[rank] = p;
+    perm[base[e] + __popcll(bm[e] & ((1ull << (p - p0)) - 1ull))] = p;
   }
 }
 
@@ -482,11 +533,12 @@ __global__ __launch_bounds__(1024) void topk_permute_small(Routing r, int T, int
   if (do_topk)
     for (int t = wave; t < T; t += blockDim.x / kWave)
       wave_topk(r.logits + size_t(t) * E, E, K, lane, r.idx + size_t(t) * K,
-                r.gates + size_t(t) * K);
+                r.gates + size_t(t) * K, r.sc);
   __threadfence_block();
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
-  for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
+  const int P = T * K;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
     const int e = r.idx[p];
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
@@ -495,21 +547,20 @@ __global__ __launch_bounds__(1024) void topk_permute_small(Routing r, int T, int
   finish_counts(r, T, K, E, threadIdx.x < E ? cnt[threadIdx.x] : 0, wave_tot, &total, &excl);
   if (threadIdx.x < E) cursor[threadIdx.x] = excl;
   __syncthreads();
-  for (int t0 = 0; t0 < T; t0 += kChunk) {
-    build_bitmap(r.idx, T, K, E, t0, bm);
-    place_chunk(r.idx, T, K, E, t0, bm, cursor, r.perm);
+  for (int p0 = 0; p0 < P; p0 += kChunk) {
+    build_bitmap(r.idx, P, E, p0, bm);
+    place_chunk(r.idx, P, E, p0, bm, cursor, r.perm);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] += __popcll(bm[e]);
     __syncthreads();
   }
 }
 
-// Decode: one block of 1024 threads does top-K, the permute, the per-unit
-// M-chunk prefix and the (unit, token) -> h-row map.
+// Decode: one block of 1024 threads does top-K, the permute and the per-unit
+// M-chunk prefix.
 constexpr int kDecMC = 32;  // tokens per M-chunk of the decode expert kernels
 
-__global__ __launch_bounds__(1024) void route_decode_kernel(Routing r, int T, int E, int K,
-                                                            int32_t *__restrict__ slotmap) {
+__global__ __launch_bounds__(1024) void route_decode_kernel(Routing r, int T, int E, int K) {
   __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
   __shared__ int cursor[COLI_MAX_EXPERTS];
   __shared__ int cnt[COLI_MAX_EXPERTS];
@@ -519,10 +570,11 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(Routing r, int T, in
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   for (int t = wave; t < T; t += blockDim.x / kWave)
     wave_topk(r.logits + size_t(t) * E, E, K, lane, r.idx + size_t(t) * K,
-              r.gates + size_t(t) * K);
+              r.gates + size_t(t) * K, r.sc);
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
-  for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
+  const int P = T * K;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
     const int e = r.idx[p];
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
@@ -541,35 +593,27 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(Routing r, int T, in
     r.chunk[nr + 1] = total + (T + kDecMC - 1) / kDecMC;
   }
   __syncthreads();
-  for (int t0 = 0; t0 < T; t0 += kChunk) {
-    build_bitmap(r.idx, T, K, E, t0, bm);
-    place_chunk(r.idx, T, K, E, t0, bm, cursor, r.perm);
+  for (int p0 = 0; p0 < P; p0 += kChunk) {
+    build_bitmap(r.idx, P, E, p0, bm);
+    place_chunk(r.idx, P, E, p0, bm, cursor, r.perm);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] += __popcll(bm[e]);
     __syncthreads();
   }
-  for (int i = threadIdx.x; i < nr * T; i += blockDim.x) slotmap[i] = -1;
-  __syncthreads();
-  const int placed = r.offsets[E];
-  for (int j = threadIdx.x; j < placed; j += blockDim.x) {
-    const int p = r.perm[j];
-    slotmap[size_t(uidx[r.idx[p]]) * T + p / K] = j;
-  }
 }
 
 // Decode with T <= 64 and T * K <= kSmallPairs: one block, one bitmap chunk.
-// The top-K writes the ids to LDS; per-expert token bitmaps give the counts,
-// the stable placement (rank = offset + tokens before t with that expert) and
-// the (unit, token) -> h-row map directly, with no read-back of global memory.
+// The top-K writes the ids to LDS; per-expert token bitmaps give the counts and
+// the stable placement (rank = offset + tokens before t with that expert)
+// directly, with no read-back of global memory.  The ids of a token come from
+// its own top-K, so they are distinct and a token bitmap counts its pairs.
 constexpr int kSmallPairs = 2048;
 
-__global__ __launch_bounds__(1024) void route_decode_small(Routing r, int T, int E, int K,
-                                                           int32_t *__restrict__ slotmap) {
+__global__ __launch_bounds__(1024) void route_decode_small(Routing r, int T, int E, int K) {
   __shared__ int32_t sidx[kSmallPairs];
   __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
   __shared__ int cursor[COLI_MAX_EXPERTS];
   __shared__ int uidx[COLI_MAX_EXPERTS];
-  __shared__ int ulist[COLI_MAX_EXPERTS];
   __shared__ int wave_tot[16];
   __shared__ int total;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -588,11 +632,13 @@ __global__ __launch_bounds__(1024) void route_decode_small(Routing r, int T, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = wave + nwv * j;
-      if (t < T) topk_select<4>(lg[j], E, K, lane, sidx + t * K, r.gates + size_t(t) * K);
+      if (t < T)
+        topk_select<4>(lg[j], E, K, lane, sidx + t * K, r.gates + size_t(t) * K, r.sc);
     }
   } else {
     for (int t = wave; t < T; t += nwv)
-      wave_topk(r.logits + size_t(t) * E, E, K, lane, sidx + t * K, r.gates + size_t(t) * K);
+      wave_topk(r.logits + size_t(t) * E, E, K, lane, sidx + t * K, r.gates + size_t(t) * K,
+                r.sc);
   }
   __syncthreads();
   for (int p = threadIdx.x; p < T * K; p += blockDim.x) {
@@ -605,10 +651,7 @@ __global__ __launch_bounds__(1024) void route_decode_small(Routing r, int T, int
   int excl = 0;
   finish_counts(r, T, K, E, ce, wave_tot, &total, &excl, uidx);
   const int nr = total;
-  if (threadIdx.x < E) {
-    cursor[threadIdx.x] = excl;
-    if (ce > 0) ulist[uidx[threadIdx.x]] = threadIdx.x;
-  }
+  if (threadIdx.x < E) cursor[threadIdx.x] = excl;
   // M-chunk prefix over units in unique order (ascending expert id)
   const int nch = (threadIdx.x < E && ce > 0) ? (ce + kDecMC - 1) / kDecMC : 0;
   const int cpos = block_exclusive_scan(nch, wave_tot, &total);
@@ -623,18 +666,12 @@ __global__ __launch_bounds__(1024) void route_decode_small(Routing r, int T, int
     if (e < 0 || e >= E) continue;
     r.perm[cursor[e] + __popcll(bm[e] & ((1ull << t) - 1ull))] = p;
   }
-  for (int i = threadIdx.x; i < nr * T; i += blockDim.x) {
-    const int u = i / T, t = i - u * T, e = ulist[u];
-    const unsigned long long b = bm[e];
-    slotmap[i] = (b >> t) & 1ull ? cursor[e] + __popcll(b & ((1ull << t) - 1ull)) : -1;
-  }
 }
 
-// Large T: per-chunk counts -> r.chunk[c*E + e].
+// Large T: per-chunk counts -> r.chunk[c*E + e] (chunk c = pairs 64c .. 64c+63).
 __global__ __launch_bounds__(256) void permute_count(Routing r, int T, int K, int E) {
   __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
-  const int t0 = blockIdx.x * kChunk;
-  build_bitmap(r.idx, T, K, E, t0, bm);
+  build_bitmap(r.idx, T * K, E, int(blockIdx.x) * kChunk, bm);
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     r.chunk[size_t(blockIdx.x) * E + e] = __popcll(bm[e]);
 }
@@ -661,18 +698,20 @@ __global__ __launch_bounds__(1024) void permute_scan(Routing r, int T, int K, in
 __global__ __launch_bounds__(256) void permute_place(Routing r, int T, int K, int E) {
   __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
   __shared__ int base[COLI_MAX_EXPERTS];
-  const int t0 = blockIdx.x * kChunk;
   for (int e = threadIdx.x; e < E; e += blockDim.x) base[e] = r.chunk[size_t(blockIdx.x) * E + e];
-  build_bitmap(r.idx, T, K, E, t0, bm);  // contains the barrier for base[]
-  place_chunk(r.idx, T, K, E, t0, bm, base, r.perm);
+  const int p0 = int(blockIdx.x) * kChunk;
+  build_bitmap(r.idx, T * K, E, p0, bm);  // contains the barrier for base[]
+  place_chunk(r.idx, T * K, E, p0, bm, base, r.perm);
 }
 
-constexpr int kSmallT = 2 * kChunk;
+// One block does the whole permute up to this many pairs.
+constexpr int kSmallP = 2048;
 
 }  // namespace
 
-size_t permute_chunk_ints(int T, int E) {
-  return T > kSmallT ? size_t((T + kChunk - 1) / kChunk) * size_t(E) : 0;
+size_t permute_chunk_ints(int T, int K, int E) {
+  const int64_t P = int64_t(T) * K;
+  return P > kSmallP ? size_t((P + kChunk - 1) / kChunk) * size_t(E) : 0;
 }
 
 hipError_t launch_router_logits(const void *x, int x_bf16, int T, int H,
@@ -711,11 +750,9 @@ hipError_t launch_router_narrow(const float *x, int T, int H, const void *wr, in
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
-                                   const uint16_t *wr, int E,
-                                   const float *bias, int K, float *logits,
-                                   int32_t *idx, float *gates, float *part,
-                                   size_t part_bytes, hipStream_t s) {
+hipError_t launch_router_mfma(const uint16_t *x, int T, int H, const uint16_t *wr, int E,
+                              const float *bias, float *logits, float *part, size_t part_bytes,
+                              hipStream_t s) {
   // K split: enough blocks to cover the GPU several times, as far as the
   // partial-sum scratch allows
   const int64_t tiles = int64_t((T + 63) / 64) * ((E + 63) / 64);
@@ -729,34 +766,55 @@ hipError_t launch_router_topk_mfma(const uint16_t *x, int T, int H,
     const int64_t n = int64_t(T) * E;
     router_sum_parts<<<dim3(unsigned((n + 255) / 256)), 256, 0, s>>>(part, S, T, E, bias, logits);
   }
-  topk_kernel<<<dim3((T + 3) / 4), 256, 0, s>>>(logits, T, E, K, idx, gates);
   return hipGetLastError();
 }
 
-hipError_t launch_route_decode(const Routing &r, int T, int E, int K, int32_t *slotmap,
-                               hipStream_t s) {
+hipError_t launch_router_any(const void *x, int x_bf16, int T, int H, const void *wr,
+                             int w_bf16, int E, const float *bias, float *logits,
+                             hipStream_t s) {
+  router_logits_any<<<dim3((E + 3) / 4, T), 256, 0, s>>>(x, x_bf16, T, H, wr, w_bf16, E, bias,
+                                                         logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk_fused(const void *x, int x_bf16, int T, int H, const void *wr,
+                                    int w_bf16, int E, int K, const float *logit_bias,
+                                    Scoring sc, int32_t *idx, float *gates, hipStream_t s) {
+  router_topk_fused<<<dim3(T), 256, 0, s>>>(x, x_bf16, H, wr, w_bf16, E, K, logit_bias, sc, idx,
+                                            gates);
+  return hipGetLastError();
+}
+
+bool router_vec_ok(const void *x, int x_bf16, int H, const void *wr, int w_bf16) {
+  // 16-byte loads of both operands at every row start
+  const int xr = H * (x_bf16 ? 2 : 4), wrb = H * (w_bf16 ? 2 : 4);
+  return H % 8 == 0 && xr % 16 == 0 && wrb % 16 == 0 &&
+         (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (reinterpret_cast<uintptr_t>(wr) & 15) == 0;
+}
+
+hipError_t launch_route_decode(const Routing &r, int T, int E, int K, hipStream_t s) {
   if (T <= 64 && T * K <= kSmallPairs)
-    route_decode_small<<<1, 1024, 0, s>>>(r, T, E, K, slotmap);
+    route_decode_small<<<1, 1024, 0, s>>>(r, T, E, K);
   else
-    route_decode_kernel<<<1, 1024, 0, s>>>(r, T, E, K, slotmap);
+    route_decode_kernel<<<1, 1024, 0, s>>>(r, T, E, K);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *idx,
-                       float *gates, hipStream_t s) {
-  topk_kernel<<<dim3((T + 3) / 4), 256, 0, s>>>(logits, T, E, K, idx, gates);
+                       float *gates, Scoring sc, hipStream_t s) {
+  topk_kernel<<<dim3((T + 3) / 4), 256, 0, s>>>(logits, T, E, K, idx, gates, sc);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_permute(const Routing &r, int T, int E, int K,
                                int do_topk, hipStream_t s) {
-  if (T <= kSmallT) {
+  if (int64_t(T) * K <= kSmallP) {
     topk_permute_small<<<1, 1024, 0, s>>>(r, T, E, K, do_topk);
     return hipGetLastError();
   }
   if (do_topk)
-    topk_kernel<<<dim3((T + 3) / 4), 256, 0, s>>>(r.logits, T, E, K, r.idx, r.gates);
-  const int nc = (T + kChunk - 1) / kChunk;
+    topk_kernel<<<dim3((T + 3) / 4), 256, 0, s>>>(r.logits, T, E, K, r.idx, r.gates, r.sc);
+  const int nc = int((int64_t(T) * K + kChunk - 1) / kChunk);
   permute_count<<<nc, 256, 0, s>>>(r, T, K, E);
   permute_scan<<<1, 1024, 0, s>>>(r, T, K, E, nc);
   permute_place<<<nc, 256, 0, s>>>(r, T, K, E);

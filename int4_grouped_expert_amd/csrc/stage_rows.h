@@ -2,7 +2,8 @@
 // that the decode batch GEMMs read (see ffn_batch.hip): row * 2^-e = hi + lo
 // with max |row| * 2^-e in [2^14, 2^15), each 64-group written in the staged
 // k order o + {0, 2, 32, 34, 1, 3, 33, 35} (o = 16 (c / 4) + 4 (c % 4) for
-// 16-byte chunk c), zero padding up to WP.  Used by a whole block of 256
+// 16-byte chunk c), zero padding up to WP (also for the ragged tail of a row
+// whose length is not a multiple of 64).  Used by a whole block of 256
 // threads (blockDim.x == 256); red: 4 floats of LDS.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -59,13 +60,44 @@ __device__ inline int stage_exponent(float m) {
 
 constexpr int kStageRuns = 4;  // runs per thread held in registers (W <= 8192)
 
-// row fp32 [W] -> hi [WP], lo [WP] fp16; *sc = 2^e.  W % 64 == 0, WP % 256 == 0.
-// Rows of up to 256 * kStageRuns runs are read once, every load issued before
-// the first use (slots past the row re-read its first run: the max is
-// unchanged); longer rows take two passes.
+// Any W and row alignment: element loads, elements past W are zeros.
+__device__ inline void stage_row_any(const float *__restrict__ row, int W, int WP,
+                                     uint16_t *__restrict__ hi_out, uint16_t *__restrict__ lo_out,
+                                     float *__restrict__ sc, float *red) {
+  const int runs = (WP / 64) * 8;
+  float m = 0.0f;
+  for (int c = int(threadIdx.x); c < W; c += 256) m = fmaxf(m, fabsf(row[c]));
+  m = stage_block_max(m, red);
+  const int e = stage_exponent(m);
+  const float down = ldexpf(1.0f, -e);
+  if (threadIdx.x == 0) *sc = ldexpf(1.0f, e);
+  for (int i = threadIdx.x; i < runs; i += 256) {
+    const int o = stage_run_offset(i);
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = o + k < W ? row[o + k] : 0.0f;
+      v[4 + k] = o + 32 + k < W ? row[o + 32 + k] : 0.0f;
+    }
+    uint4 hi, lo;
+    stage_run(float4{v[0], v[1], v[2], v[3]}, float4{v[4], v[5], v[6], v[7]}, down, hi, lo);
+    *reinterpret_cast<uint4 *>(hi_out + 8 * i) = hi;
+    *reinterpret_cast<uint4 *>(lo_out + 8 * i) = lo;
+  }
+}
+
+// row fp32 [W] -> hi [WP], lo [WP] fp16; *sc = 2^e.  WP % 256 == 0.  With
+// W % 64 == 0 and a 16-byte aligned row: rows of up to 256 * kStageRuns runs
+// are read once, every load issued before the first use (slots past the row
+// re-read its first run: the max is unchanged); longer rows take two passes.
+// Other rows take stage_row_any.
 __device__ inline void stage_row(const float *__restrict__ row, int W, int WP,
                                  uint16_t *__restrict__ hi_out, uint16_t *__restrict__ lo_out,
                                  float *__restrict__ sc, float *red) {
+  if (W % 64 != 0 || (reinterpret_cast<uintptr_t>(row) & 15) != 0) {
+    stage_row_any(row, W, WP, hi_out, lo_out, sc, red);
+    return;
+  }
   const int G = W / 64, rv = G * 8, runs = (WP / 64) * 8;
   if (rv <= 256 * kStageRuns) {
     float4 a[kStageRuns], b[kStageRuns];

@@ -3,7 +3,8 @@
 // fixed order) and the per-token top-K with renormalised gates.
 //
 // Top-K: page "Colibrì 深度解析:用 12 万行纯 C 把 744B MoE 塞进 25GB 笔记本",
-// section 十一 (per-token top-k experts); gates normalised over the selected
+// section 十一 (per-token top-k experts; its GLM router scores with a sigmoid,
+// one expert group, a selection-only bias); gates normalised over the selected
 // experts (page "colibrì 路由遥测全解析", section 分离计数与追踪); NaN logits
 // never win (same page, section 测试与 CI 保障).
 #pragma once
@@ -108,8 +109,24 @@ __device__ __attribute__((always_inline)) inline void topk_load(const float *__r
 // Selection and gates from logits already in registers (see topk_load).
 template <int PL>
 __device__ __attribute__((always_inline)) inline void topk_select(
-    const float (&v)[PL], int E, int K, int lane, int32_t *__restrict__ idx_out,
-    float *__restrict__ gate_out) {
+    const float (&v_in)[PL], int E, int K, int lane, int32_t *__restrict__ idx_out,
+    float *__restrict__ gate_out, Scoring sc = Scoring{0, nullptr}) {
+  // keys of the selection (the logits themselves, or the biased sigmoid scores)
+  float v[PL], sgm[PL];
+  if (sc.sigmoid) {
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int e = lane + kWaveLanes * j;
+      sgm[j] = 1.0f / (1.0f + expf(-v_in[j]));
+      v[j] = sgm[j] + ((sc.bias && e < E) ? sc.bias[e] : 0.0f);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      v[j] = v_in[j];
+      sgm[j] = 0.0f;
+    }
+  }
   // Each lane keeps its best untaken candidate: the order bits of the value
   // (0: none; NaN values and ids >= E are never candidates) and its slot j,
   // the lowest among equal values.  A round is a wave maximum of the order
@@ -168,16 +185,26 @@ __device__ __attribute__((always_inline)) inline void topk_select(
       rescan();
     }
   }
-  // selected max and normaliser (butterfly: identical on every lane)
-  float m = -__builtin_inff();
+  // gate numerators: exp(l - m) over the selected logits (softmax), or the
+  // selected scores (sigmoid); the normaliser is their wave sum (identical on
+  // every lane)
+  float num[PL];
+  if (sc.sigmoid) {
 #pragma unroll
-  for (int j = 0; j < PL; ++j)
-    if ((taken >> j) & 1u) m = fmaxf(m, v[j]);
-  m = wave_max(m);
+    for (int j = 0; j < PL; ++j) num[j] = sgm[j];
+  } else {
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < PL; ++j)
+      if ((taken >> j) & 1u) m = fmaxf(m, v[j]);
+    m = wave_max(m);
+#pragma unroll
+    for (int j = 0; j < PL; ++j) num[j] = expf(v[j] - m);
+  }
   float z = 0.0f;
 #pragma unroll
   for (int j = 0; j < PL; ++j)
-    if ((taken >> j) & 1u) z += expf(v[j] - m);
+    if ((taken >> j) & 1u) z += num[j];
   z = wave_sum(z);
   int before = 0;
 #pragma unroll
@@ -186,7 +213,7 @@ __device__ __attribute__((always_inline)) inline void topk_select(
     if ((taken >> j) & 1u) {
       const int rank = before + __popcll(bal & ((1ull << lane) - 1ull));
       idx_out[rank] = lane + kWaveLanes * j;
-      gate_out[rank] = expf(v[j] - m) / z;
+      gate_out[rank] = num[j] / z;
     }
     before += __popcll(bal);
   }
@@ -195,21 +222,21 @@ __device__ __attribute__((always_inline)) inline void topk_select(
 template <int PL>
 __device__ __attribute__((always_inline)) inline void wave_topk_pl(
     const float *__restrict__ lrow, int E, int K, int lane, int32_t *__restrict__ idx_out,
-    float *__restrict__ gate_out) {
+    float *__restrict__ gate_out, Scoring sc) {
   float v[PL];
   topk_load<PL>(lrow, E, lane, v);
-  topk_select<PL>(v, E, K, lane, idx_out, gate_out);
+  topk_select<PL>(v, E, K, lane, idx_out, gate_out, sc);
 }
 
 // Dispatch on the logits per lane, ceil(E / 64) rounded up to 1, 2, 4, 8, 16.
 __device__ __attribute__((always_inline)) inline void wave_topk(
     const float *__restrict__ lrow, int E, int K, int lane, int32_t *__restrict__ idx_out,
-    float *__restrict__ gate_out) {
-  if (E <= 64) wave_topk_pl<1>(lrow, E, K, lane, idx_out, gate_out);
-  else if (E <= 128) wave_topk_pl<2>(lrow, E, K, lane, idx_out, gate_out);
-  else if (E <= 256) wave_topk_pl<4>(lrow, E, K, lane, idx_out, gate_out);
-  else if (E <= 512) wave_topk_pl<8>(lrow, E, K, lane, idx_out, gate_out);
-  else wave_topk_pl<16>(lrow, E, K, lane, idx_out, gate_out);
+    float *__restrict__ gate_out, Scoring sc = Scoring{0, nullptr}) {
+  if (E <= 64) wave_topk_pl<1>(lrow, E, K, lane, idx_out, gate_out, sc);
+  else if (E <= 128) wave_topk_pl<2>(lrow, E, K, lane, idx_out, gate_out, sc);
+  else if (E <= 256) wave_topk_pl<4>(lrow, E, K, lane, idx_out, gate_out, sc);
+  else if (E <= 512) wave_topk_pl<8>(lrow, E, K, lane, idx_out, gate_out, sc);
+  else wave_topk_pl<16>(lrow, E, K, lane, idx_out, gate_out, sc);
 }
 
 // ---- digit planes (single-token decode activations) ----------------------

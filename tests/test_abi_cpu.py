@@ -39,10 +39,14 @@ def test_format_sizes():
     assert coli.coli_int4_g64_packed_bytes(0, 10) == 0
     assert coli.coli_int4_g64_packed_bytes(4, 0) == 0
     # 21,233,664 bytes per expert at H=6144, I=2048 (nibbles + fp32 scales), plus
-    # the scales again group-major and blocked by 8 rows (6 x 786,432)
-    assert coli.coli_expert_blob_bytes(6144, 2048) == 21233664 + 6 * 786432
-    assert coli.coli_expert_blob_bytes(256, 128) == 55296 + 6 * 2048
+    # the scales again group-major and blocked by 8 rows (6 x 786,432) and the
+    # 256-byte finish tag section
+    assert coli.coli_expert_blob_bytes(6144, 2048) == 21233664 + 6 * 786432 + 256
+    assert coli.coli_expert_blob_bytes(256, 128) == 55296 + 6 * 2048 + 256
     assert coli.coli_expert_blob_bytes(0, 128) == 0
+    # ragged shapes: ceil(cols / 64) groups per row, every section 256-byte aligned
+    nb = coli.coli_expert_blob_bytes(200, 72)
+    assert nb > 0 and nb % 256 == 0
 
 
 def test_expert_views_offsets():
@@ -68,9 +72,27 @@ def test_workspace_bytes():
     assert d >= (8 + 1) * 2048 * 4
     p = coli.lib.coli_moe_workspace_bytes(ctypes.byref(lay), 2048, coli.COLI_PREFILL)
     assert p >= (2048 * 9) * (2048 + 6144) * 2
-    assert coli.lib.coli_moe_workspace_bytes(ctypes.byref(lay), 257, coli.COLI_DECODE) == 0
+    # decode beyond 256 tokens runs in 256-token sub-batches: the workspace of one
+    d256 = coli.lib.coli_moe_workspace_bytes(ctypes.byref(lay), 256, coli.COLI_DECODE)
+    assert coli.lib.coli_moe_workspace_bytes(ctypes.byref(lay), 257, coli.COLI_DECODE) == d256
+    assert coli.lib.coli_moe_workspace_bytes(ctypes.byref(lay), 5000, coli.COLI_DECODE) == d256
     bad = coli.coli_moe_layer(6144, 2048, 256, 300, 1, 1, None, 1, 1)
     assert coli.lib.coli_moe_workspace_bytes(ctypes.byref(bad), 1, coli.COLI_DECODE) == 0
+
+
+def test_buffer_offset_limit_rejected_before_launch():
+    """A prefill of 65536 tokens of the decode-shaped layer would need (T*K + T) *
+    I * 2 = 2.4e9 bytes of staged h: past the kernels' 2^31 buffer offsets.  The
+    size query says 0 and the forward returns ESHAPE before any launch (the
+    pointers here are not device memory: a launch would fault)."""
+    L = coli.lib
+    lay = coli.coli_moe_layer(6144, 2048, 256, 8, 1 << 20, coli.COLI_BF16, None, 1 << 30, 1 << 31)
+    assert L.coli_moe_workspace_bytes(ctypes.byref(lay), 65536, coli.COLI_PREFILL) == 0
+    assert L.coli_moe_workspace_bytes(ctypes.byref(lay), 8192, coli.COLI_PREFILL) > 0
+    a = P(1 << 20)
+    rc = L.coli_moe_forward(ctypes.byref(lay), coli.COLI_PREFILL, a, 65536, a, None, None, None,
+                            a, 1 << 40, None)
+    assert rc == coli.COLI_ESHAPE
 
 
 P = ctypes.c_void_p
@@ -100,11 +122,17 @@ def test_router_rejects_before_launch():
     assert call(K=17) == coli.COLI_ESHAPE
     assert call(K=0) == coli.COLI_ESHAPE
     assert call(E=1025, K=4) == coli.COLI_ESHAPE
-    assert call(H=60) == coli.COLI_ESHAPE
+    assert call(H=0) == coli.COLI_ESHAPE
     assert call(T=-1) == coli.COLI_ESHAPE
     assert call(xd=7) == coli.COLI_EDTYPE
-    assert call(x=P(4104)) == coli.COLI_EALIGN
+    assert call(x=P(4098)) == coli.COLI_EALIGN  # fp32 x: 4-byte aligned
+    assert call(x=P(4098), xd=1, T=0) == coli.COLI_OK  # bf16 x: 2-byte aligned
     assert call(T=0) == coli.COLI_OK
+    # scoring: unknown values are rejected
+    assert L.coli_router_topk_scored(a, 0, 1, 64, a, 0, 16, None, 4, 7, a, a, a, None) == \
+        coli.COLI_EINVAL
+    assert L.coli_router_topk_scored(a, 0, 0, 64, a, 0, 16, None, 4, 1, a, a, None, None) == \
+        coli.COLI_OK
     del ok
 
 
@@ -113,8 +141,10 @@ def test_permute_rejects_before_launch():
     a = P(4096)
     assert L.coli_expert_permute(None, 1, 2, 8, a, a, a, a, a, None, 0, None) == coli.COLI_EINVAL
     assert L.coli_expert_permute(a, 1, 9, 8, a, a, a, a, a, None, 0, None) == coli.COLI_ESHAPE
-    need = coli.coli_expert_permute_workspace_bytes(2048, 256)
-    assert need > 0 and coli.coli_expert_permute_workspace_bytes(32, 256) == 0
+    need = coli.coli_expert_permute_workspace_bytes(2048, 8, 256)
+    assert need == 256 * 256 * 4  # one count per (64-pair chunk, expert)
+    assert coli.coli_expert_permute_workspace_bytes(32, 8, 256) == 0
+    assert coli.coli_expert_permute_workspace_bytes(32, 9, 8) == 0  # K > E: invalid
     assert (L.coli_expert_permute(a, 2048, 8, 256, a, a, a, a, a, None, 0, None)
             == coli.COLI_EWORKSPACE)
     assert (L.coli_expert_permute(a, 2048, 8, 256, a, a, a, a, a, a, need - 4, None)
@@ -127,21 +157,25 @@ def test_forward_rejects_before_launch():
     lay = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22)
     need = L.coli_moe_workspace_bytes(ctypes.byref(lay), 1, coli.COLI_DECODE)
 
-    def call(layer=lay, mode=coli.COLI_DECODE, x=a, T=1, y=a, ws=a, nb=need):
-        return L.coli_moe_forward(ctypes.byref(layer), mode, x, T, y, None, None, ws, nb, None)
+    def call(layer=lay, mode=coli.COLI_DECODE, x=a, T=1, y=a, ws=a, nb=need, st=None):
+        return L.coli_moe_forward(ctypes.byref(layer), mode, x, T, y, None, None, st, ws, nb,
+                                  None)
     assert call(x=None) == coli.COLI_EINVAL
     assert call(mode=5) == coli.COLI_EINVAL
-    assert call(T=257) == coli.COLI_ESHAPE
+    assert call(T=65537) == coli.COLI_ESHAPE
+    assert call(st=P((1 << 20) + 2)) == coli.COLI_EALIGN
     assert call(ws=None) == coli.COLI_EWORKSPACE
     assert call(nb=need - 1) == coli.COLI_EWORKSPACE
     assert call(x=P((1 << 20) + 8)) == coli.COLI_EALIGN
     assert call(ws=P((1 << 20) + 128)) == coli.COLI_EALIGN
     assert call(T=0) == coli.COLI_OK
     assert call(T=0, x=None, y=None) == coli.COLI_OK
-    for H, I, E, K in [(250, 128, 16, 4), (256, 100, 16, 4), (256, 128, 0, 1), (256, 128, 16, 17),
-                       (256, 128, 2000, 4)]:
+    for H, I, E, K in [(0, 128, 16, 4), (256, 0, 16, 4), (256, 128, 0, 1), (256, 128, 16, 17),
+                       (256, 128, 2000, 4), (70000, 128, 16, 4)]:
         bad = coli.coli_moe_layer(H, I, E, K, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22)
         assert call(layer=bad) == coli.COLI_ESHAPE
+    badsc = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22, 5)
+    assert call(layer=badsc) == coli.COLI_EINVAL
     unal = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, coli.COLI_F32, None, (1 << 21) + 64,
                                1 << 22)
     assert call(layer=unal) == coli.COLI_EALIGN

@@ -8,8 +8,10 @@ section 权重转换) -> gate-weighted combine with the normalised gates (page "
 
 Every expert the oracle uses is quantised by the oracle itself from the same seeded
 fp32 draws; on the way its bytes are compared with the device blob (bit-exact).
-Bars: idx bit-exact; decode floats max|d| <= 2e-3 * max(1, rms); prefill (bf16)
-max|d| <= 2e-2 * rms.
+Bars: idx bit-exact; gates within the spec's 2e-3; y under the spec bars (decode
+max|d| <= 2e-3 * max(1, rms), prefill max|d| <= 2e-2 * rms) and, row by row, under
+bars relative to each row's own rms (tests/harness.py: check_rows), so that layers
+whose outputs are far below 1 are checked as strictly as the full-size ones.
 """
 import numpy as np
 import pytest
@@ -17,8 +19,9 @@ import torch
 
 import oracle
 import workloads as W
-from tests.harness import (DEC_TOL, PRE_TOL, DeviceLayer, Timer, assert_close, host_array,
-                           log, margin_tokens, oracle_expert, topk_gap, MARGIN)
+from tests.harness import (DEC_TOL, TIGHT_DEC, DeviceLayer, Timer, assert_close, check_rows,
+                           host_array, log, margin_tokens, oracle_expert, oracle_topk, topk_gap,
+                           MARGIN)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,31 +42,33 @@ def layer(cfg_id, l=0):
     return _layers[key]
 
 
-def oracle_check(cfg_id, L, x, y, idx, gates, mode, rows=None, check_bytes=True, l=0):
-    """Compare (sampled rows of) a forward with the oracle."""
+def oracle_check(cfg_id, L, x, y, idx, gates, mode, rows=None, check_bytes=True, l=0,
+                 what=""):
+    """Compare (sampled rows of) a forward with the oracle: ids bit-exact, gates under
+    the spec bar, y row by row (check_rows).  Returns the worst row err/rms."""
     c = W.CONFIGS[cfg_id]
     rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
     xh = host_array(x[torch.from_numpy(rows).to(x.device)])
     wr = host_array(L.w_router)
-    logits = oracle.router_logits(xh, wr, L.bias_np)
-    ridx, rg, _ = oracle.topk(logits, c["K"])
+    ridx, rg, _ = oracle_topk(cfg_id, xh, wr, L.bias_np, c["K"])
     need = sorted(set(ridx.reshape(-1).tolist()))
     experts = [None] * c["E"]
     with Timer(f"oracle experts {len(need)}"):
         for e in need:
             experts[e] = oracle_expert(cfg_id, e, l, "cuda", L if check_bytes else None)
         shared = oracle_expert(cfg_id, c["E"], l, "cuda", L if check_bytes else None)
-    with Timer("oracle forward"):
+    with Timer(f"oracle forward {len(rows)} rows"):
         yr, ridx2, rg2 = oracle.moe_forward(xh, wr, L.bias_np, experts, shared, c["H"], c["I"],
-                                            c["K"])
+                                            c["K"], scoring=W.scoring(cfg_id))
     assert np.array_equal(ridx, ridx2)
     gi = idx.cpu().numpy()[rows]
     assert np.array_equal(gi, ridx), "top-K ids differ from the oracle"
-    assert_close(gates.cpu().numpy()[rows], rg, DEC_TOL, what="gates")
+    gerr = assert_close(gates.cpu().numpy()[rows], rg, DEC_TOL, what="gates")
+    log(f"[parity] gates max err {gerr:.3e}")
     yg = y.float().cpu().numpy()[rows]
-    if mode == DECODE:
-        return assert_close(yg, yr, DEC_TOL, what="y")
-    return assert_close(yg, yr, PRE_TOL, floor_one=False, what="y")
+    tag = what or f"cfg {cfg_id} T {x.shape[0]} {'decode' if mode == DECODE else 'prefill'}"
+    return check_rows(yg, yr, mode == PREFILL, what=tag,
+                      tight=TIGHT_DEC if mode == DECODE else None)
 
 
 # T <= 64 takes the one-chunk decode route (T = 64 sets bit 63 of its token
@@ -85,7 +90,8 @@ def test_decode_batch_row_scales():
     get their own power-of-two scale before the fp16 hi/lo split.  Power-of-two
     factors scale the logits exactly, so every row keeps its routing margin (the
     zero row's logits are exact ties or the bias, resolved the same way on both
-    sides); each row is compared with the oracle under its own magnitude."""
+    sides).  Each row is held to a bar relative to its own rms (check_rows), and the
+    zero row must come out exactly zero."""
     cfg_id = 0
     L = layer(cfg_id)
     c = W.CONFIGS[cfg_id]
@@ -97,12 +103,15 @@ def test_decode_batch_row_scales():
     assert torch.isfinite(y).all()
     for row in range(5):
         log(f"row scale {float(f[row])}")
-        oracle_check(cfg_id, L, x, y, idx, gates, DECODE, rows=[row], check_bytes=(row == 0))
+        oracle_check(cfg_id, L, x, y, idx, gates, DECODE, rows=[row], check_bytes=(row == 0),
+                     what=f"batch row scale {float(f[row]):g}")
+    assert float(y[4].abs().max()) == 0.0
 
 
 def test_decode_one_token_scales():
     """Single-token decode (int8 digit planes under one power-of-two scale per vector)
-    with the token scaled by 2^12, 2^-8 and 0."""
+    with the token scaled by 2^12, 2^-8 and 0, each held to a bar relative to its own
+    output rms (the zero token must give exactly zero)."""
     cfg_id = 107
     L = layer(cfg_id)
     c = W.CONFIGS[cfg_id]
@@ -113,7 +122,10 @@ def test_decode_one_token_scales():
         y, idx, gates = L.forward(x, DECODE)
         torch.cuda.synchronize()
         assert torch.isfinite(y).all()
-        oracle_check(cfg_id, L, x, y, idx, gates, DECODE, check_bytes=(f == 2.0 ** 12))
+        oracle_check(cfg_id, L, x, y, idx, gates, DECODE, check_bytes=(f == 2.0 ** 12),
+                     what=f"one token scale {f:g}")
+        if f == 0.0:
+            assert float(y.abs().max()) == 0.0
 
 
 @pytest.mark.parametrize("cfg_id", [107, 108, 109, 110, 111, 112, 113, 114])
@@ -144,6 +156,24 @@ def test_prefill_small(cfg_id, T):
     oracle_check(cfg_id, L, x, y, idx, gates, PREFILL)
 
 
+def test_prefill_row_scales():
+    """Prefill rows scaled by 2^4 .. 2^-8 (bf16 x; power-of-two factors scale the
+    logits exactly, so the routing margin holds): each row under its own rms bar."""
+    cfg_id = 100
+    L = layer(cfg_id)
+    c = W.CONFIGS[cfg_id]
+    x = margin_tokens(cfg_id, 6, host_array(L.w_router), L.bias_np, c["K"])
+    f = torch.tensor([2.0 ** 4, 1.0, 2.0 ** -2, 2.0 ** -4, 2.0 ** -6, 2.0 ** -8], device=x.device)
+    # each token's x is scaled by its own power of two before the fp16 conversion
+    # (and its h by the square), so every row keeps the same relative accuracy
+    x = (x.float() * f[:, None]).to(torch.bfloat16).contiguous()
+    y, idx, gates = L.forward(x, PREFILL)
+    torch.cuda.synchronize()
+    for row in range(6):
+        oracle_check(cfg_id, L, x, y, idx, gates, PREFILL, rows=[row], check_bytes=(row == 0),
+                     what=f"prefill row scale {float(f[row]):g}")
+
+
 def test_decode_full_size_t1():
     """The decode workload: H=6144, I=2048, E=256, K=8, T=1, several tokens."""
     L = layer(1)
@@ -158,7 +188,7 @@ def test_decode_full_size_t1():
 
 
 def test_decode_full_size_t32_zipf():
-    """The Zipf decode batch: T=32; every token's ids, sampled tokens' outputs."""
+    """The Zipf decode batch: T=32; every token's ids and outputs."""
     L = layer(2)
     c = W.CONFIGS[2]
     x = margin_tokens(2, 32, host_array(L.w_router), L.bias_np, c["K"])
@@ -171,11 +201,32 @@ def test_decode_full_size_t32_zipf():
     U = len(set(ridx.reshape(-1).tolist()))
     log(f"zipf T=32 unique experts U={U}")
     assert U < 32 * 8
-    oracle_check(2, L, x, y, idx, gates, DECODE, rows=[0, 5, 17, 31])
+    oracle_check(2, L, x, y, idx, gates, DECODE)
+
+
+def cover_rows(ridx: np.ndarray, T: int, chunk: int) -> list:
+    """Rows of a prefill batch such that every routed expert with a token and every
+    chunk-row block of the shared expert's tokens appears at least once: one row per
+    shared block (the one adding the most new experts), then a greedy cover of the
+    experts left."""
+    left = set(ridx.reshape(-1).tolist())
+    rows = []
+    for b0 in range(0, T, chunk):
+        blk = range(b0, min(T, b0 + chunk))
+        best = max(blk, key=lambda t: len(left & set(ridx[t].tolist())))
+        rows.append(best)
+        left -= set(ridx[best].tolist())
+    while left:
+        best = max(range(T), key=lambda t: len(left & set(ridx[t].tolist())))
+        rows.append(best)
+        left -= set(ridx[best].tolist())
+    return sorted(set(rows))
 
 
 def test_prefill_full_size_sampled():
-    """The prefill workload: T=2048 bf16; all ids, sampled tokens' outputs."""
+    """The prefill workload: T=2048 bf16; all ids and gates, and the outputs of rows
+    that cover every routed expert with a token and every 128-token block of the
+    shared expert's tokens (the grouped GEMM's M-chunks)."""
     L = layer(3)
     c = W.CONFIGS[3]
     with Timer("margin tokens T=2048"):
@@ -189,7 +240,10 @@ def test_prefill_full_size_sampled():
     assert_close(gates.cpu().numpy(), rg, DEC_TOL, what="gates")
     counts = np.bincount(ridx.reshape(-1), minlength=c["E"])
     log(f"prefill tokens per expert min {counts.min()} max {counts.max()}")
-    oracle_check(3, L, x, y, idx, gates, PREFILL, rows=[0, 777, 2047], check_bytes=False)
+    rows = cover_rows(ridx, 2048, 128)
+    log(f"prefill rows checked: {len(rows)}")
+    assert set(ridx[rows].reshape(-1).tolist()) == set(ridx.reshape(-1).tolist())
+    oracle_check(3, L, x, y, idx, gates, PREFILL, rows=rows, check_bytes=False)
 
 
 def test_forward_deterministic_and_t0():
@@ -293,7 +347,8 @@ def stack_check(cfg_id, nlayers, T, e2e_layers):
         xl = torch.from_numpy(np.asarray(xs[l], dtype=np.float32)).cuda()
         y, _, _ = Ls[l].forward(xl, DECODE)
         torch.cuda.synchronize()
-        worst = max(worst, assert_close(y.cpu().numpy(), ys[l], DEC_TOL, what=f"layer {l}"))
+        worst = max(worst, check_rows(y.cpu().numpy(), ys[l], False, what=f"stack layer {l}",
+                                      tight=TIGHT_DEC))
     log(f"stack per-layer worst rel err {worst:.2e}")
 
     def gpu_chain(n):
@@ -310,8 +365,8 @@ def stack_check(cfg_id, nlayers, T, e2e_layers):
         torch.cuda.synchronize()
         return cur
     e2e = gpu_chain(e2e_layers)
-    err = assert_close(e2e.cpu().numpy(), ys[e2e_layers - 1], DEC_TOL,
-                       what=f"stack out after {e2e_layers} layers")
+    err = check_rows(e2e.cpu().numpy(), ys[e2e_layers - 1], False,
+                     what=f"stack out after {e2e_layers} layers")
     log(f"stack end-to-end {e2e_layers} layers rel err {err:.2e}")
     full = gpu_chain(nlayers)
     assert torch.all(torch.isfinite(full))

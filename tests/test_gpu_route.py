@@ -85,7 +85,7 @@ def run_permute(idx_np, E):
     perm = torch.full((max(T * K, 1),), -1, dtype=torch.int32, device="cuda")
     unique = torch.full((E,), -1, dtype=torch.int32, device="cuda")
     nu = torch.full((1,), -1, dtype=torch.int32, device="cuda")
-    nb = coli.coli_expert_permute_workspace_bytes(T, E)
+    nb = coli.coli_expert_permute_workspace_bytes(T, K, E)
     ws = torch.empty(max(nb, 4), dtype=torch.uint8, device="cuda") if nb else None
     coli.coli_expert_permute(idx, E, counts, offsets, perm, unique, nu, ws)
     torch.cuda.synchronize()

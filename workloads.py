@@ -73,6 +73,25 @@ CONFIGS.update({
               x="f32", bias=None, mode="decode", layers=1),
     114: dict(name="one_token_fused_h3072", H=3072, I=1024, E=64, K=8, T=1, router="f32",
               x="f32", bias="zipf", mode="decode", layers=1),
+    # the sigmoid router ("n_group=1 sigmoid + noaux_tc"): raw logits, a selection bias
+    115: dict(name="sigmoid_decode", H=384, I=192, E=24, K=6, T=40, router="bf16", x="f32",
+              bias="sel", mode="decode", layers=1, scoring="sigmoid"),
+    116: dict(name="sigmoid_one_token", H=512, I=512, E=16, K=4, T=1, router="f32", x="f32",
+              bias="sel", mode="decode", layers=1, scoring="sigmoid"),
+    117: dict(name="sigmoid_prefill", H=256, I=128, E=16, K=4, T=200, router="bf16", x="bf16",
+              bias="sel", mode="prefill", layers=1, scoring="sigmoid"),
+    118: dict(name="sigmoid_full", H=6144, I=2048, E=256, K=8, T=32, router="bf16", x="f32",
+              bias="sel", mode="decode", layers=1, scoring="sigmoid"),
+    # ragged shapes: H and I not multiples of 64 (zero-padded last groups), rows of
+    # any alignment
+    119: dict(name="ragged_decode", H=200, I=72, E=12, K=3, T=5, router="f32", x="f32",
+              bias=None, mode="decode", layers=1),
+    120: dict(name="ragged_prefill", H=100, I=70, E=10, K=2, T=77, router="bf16", x="bf16",
+              bias=None, mode="prefill", layers=1),
+    121: dict(name="ragged_decode_bf16", H=130, I=200, E=16, K=4, T=33, router="bf16", x="f32",
+              bias="zipf", mode="decode", layers=1),
+    122: dict(name="ragged_prefill_wide", H=1000, I=330, E=20, K=5, T=150, router="bf16",
+              x="bf16", bias="zipf", mode="prefill", layers=1),
 })
 
 WEIGHT_STD = 0.02
@@ -86,6 +105,9 @@ _TAGS = {"router": 1, "bias_perm": 2, "expert": 3, "x": 4}
 # "Same layer as the decode workload": these draw their router and experts from it.
 CONFIGS[2]["weights_from"] = 1
 CONFIGS[3]["weights_from"] = 1
+CONFIGS[118]["weights_from"] = 1
+
+SEL_BIAS_STD = 0.1  # the sigmoid router's selection bias: N(0, 0.1) per expert
 
 
 def seed_for(cfg_id: int, tag: str, layer: int = 0, index: int = 0) -> int:
@@ -118,16 +140,26 @@ def expert_weights(cfg_id: int, e: int, device="cpu", layer: int = 0, shape=None
     return wg, wu, wd
 
 
-def router_bias(cfg_id: int, layer: int = 0):
-    """fp32 [E] bias that makes selections follow Zipf(1.1), or None.
+def scoring(cfg_id: int) -> int:
+    """0: softmax router (bias added to the logits), 1: sigmoid router (bias steers
+    the selection only)."""
+    return 1 if CONFIGS[cfg_id].get("scoring") == "sigmoid" else 0
 
-    b_e = tau * ln p_{pi(e)}, p_r proportional to r^-s over ranks r = 1..E, pi a
-    seeded permutation of the experts (one per layer).
+
+def router_bias(cfg_id: int, layer: int = 0):
+    """fp32 [E] router bias, or None.
+
+    "zipf": b_e = tau * ln p_{pi(e)}, p_r proportional to r^-s over ranks r = 1..E, pi
+    a seeded permutation of the experts (one per layer): selections follow Zipf(1.1).
+    "sel": the sigmoid router's selection bias, N(0, SEL_BIAS_STD) per expert.
     """
     c = CONFIGS[cfg_id]
     if c["bias"] is None:
         return None
     E = c["E"]
+    if c["bias"] == "sel":
+        rng = np.random.default_rng(seed_for(cfg_id, "bias_perm", layer))
+        return (rng.standard_normal(E) * SEL_BIAS_STD).astype(np.float32)
     r = np.arange(1, E + 1, dtype=np.float64)
     p = r ** -ZIPF_S
     p /= p.sum()
