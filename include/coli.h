@@ -28,8 +28,9 @@
  *     error the call returns a negative status and writes nothing.
  *   - A launch failure reported by the HIP runtime returns COLI_EDEVICE.
  *   - Row-major layouts throughout.  Calls are reentrant: the library has no
- *     global mutable state; concurrent calls must not share output or
- *     workspace buffers.
+ *     global mutable state besides the per-device address of the no-alloc
+ *     scratch array (coli_moe_forward_noalloc); concurrent calls must not
+ *     share output or workspace buffers.
  *   - Data conditions found on the device (non-finite values, an operand out
  *     of range, an unfinished expert blob) are OR-ed into an optional device
  *     status flag; they never change the return value.
@@ -51,7 +52,8 @@ enum {
     COLI_EALIGN = -3,     /* a pointer is not aligned as required */
     COLI_EDTYPE = -4,     /* dtype not supported for this call / mode */
     COLI_EWORKSPACE = -5, /* workspace NULL or smaller than required */
-    COLI_EDEVICE = -6     /* the HIP runtime reported a launch error */
+    COLI_EDEVICE = -6,    /* the HIP runtime reported a launch error */
+    COLI_ESCRATCH = -7    /* the call needs more than the no-alloc scratch holds */
 };
 
 typedef enum { COLI_F32 = 0, COLI_BF16 = 1 } coli_dtype;
@@ -334,6 +336,30 @@ int coli_moe_forward_timed(const coli_moe_layer *L, coli_mode mode,
                            int32_t *status, void *workspace,
                            size_t workspace_bytes, void *stream, void **events,
                            int n_events);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as coli_moe_forward, with the workspace taken from a static device
+ * array of COLI_NOALLOC_SCRATCH_BYTES inside the library (each GPU the library
+ * runs on holds its own copy until the process ends).  The caller still passes
+ * x, y and the optional outputs.  No hipMalloc, hipFree or other allocation;
+ * the array's device address is looked up once per device, on the first call
+ * made with that device current (the stream must belong to the current
+ * device).  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other threads) race and give undefined results.
+ * The workspace needs no initialisation, so nothing is cleared between calls.
+ * Errors: as coli_moe_forward (argument errors take precedence), ESCRATCH when
+ * coli_moe_workspace_bytes(L, T, mode) exceeds COLI_NOALLOC_SCRATCH_BYTES (32
+ * MiB: the layer H=6144, I=2048, E=256, K=8 fits decode up to T = 74 and
+ * prefill up to T = 206), EDEVICE if the address lookup fails.  T == 0 is a
+ * no-op.
+ */
+#define COLI_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+int coli_moe_forward_noalloc(const coli_moe_layer *L, coli_mode mode,
+                             const void *x, int T, void *y,
+                             int32_t *topk_idx_out, float *topk_gate_out,
+                             int32_t *status, void *stream);
 
 /*
  * RMSNorm with unit weight between stacked layers:

@@ -35,7 +35,8 @@ except ImportError:  # pure C-ABI use without PyTorch
 lib = ctypes.CDLL(_LIB_PATH)
 
 COLI_OK, COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN = 0, -1, -2, -3
-COLI_EDTYPE, COLI_EWORKSPACE, COLI_EDEVICE = -4, -5, -6
+COLI_EDTYPE, COLI_EWORKSPACE, COLI_EDEVICE, COLI_ESCRATCH = -4, -5, -6, -7
+COLI_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 COLI_F32, COLI_BF16 = 0, 1
 COLI_DECODE, COLI_PREFILL = 0, 1
 COLI_SCORE_SOFTMAX, COLI_SCORE_SIGMOID = 0, 1
@@ -50,7 +51,8 @@ EXPORTS = [
     "coli_quant_int4_g64", "coli_router_topk", "coli_router_topk_scored",
     "coli_expert_permute_workspace_bytes", "coli_expert_permute", "coli_expert_blob_bytes",
     "coli_expert_views", "coli_expert_finish", "coli_quant_expert", "coli_moe_workspace_bytes",
-    "coli_moe_forward", "coli_moe_forward_timed", "coli_rmsnorm_f32",
+    "coli_moe_forward", "coli_moe_forward_timed", "coli_moe_forward_noalloc",
+    "coli_rmsnorm_f32",
 ]
 
 _p = ctypes.c_void_p
@@ -94,6 +96,8 @@ _proto("coli_moe_forward", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, 
                                 _sz, _p])
 _proto("coli_moe_forward_timed", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p,
                                       _p, _p, _sz, _p, ctypes.POINTER(_p), _i])
+_proto("coli_moe_forward_noalloc", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p,
+                                        _p, _p])
 _proto("coli_rmsnorm_f32", _i, [_p, _p, _i, _i, ctypes.c_float, _p])
 
 
@@ -239,6 +243,15 @@ def coli_moe_forward_timed(layer: MoELayer, mode: int, x, y, workspace, events, 
                                              _ptr(workspace), nbytes, _stream(stream), arr,
                                              len(events)),
                   "coli_moe_forward_timed")
+
+
+def coli_moe_forward_noalloc(layer: MoELayer, mode: int, x, y, topk_idx=None, topk_gate=None,
+                             stream=None, status=None):
+    """coli_moe_forward with the library's static scratch as workspace (no allocation)."""
+    T = x.shape[0]
+    return _check(lib.coli_moe_forward_noalloc(ctypes.byref(layer.c), mode, _ptr(x), T, _ptr(y),
+                                               _ptr(topk_idx), _ptr(topk_gate), _ptr(status),
+                                               _stream(stream)), "coli_moe_forward_noalloc")
 
 
 def coli_rmsnorm_f32(x, y, eps=1e-6, stream=None):

@@ -3,7 +3,8 @@
 // Host side only: validates every argument before the first launch (fail
 // closed: on error nothing is written), carves the caller's workspace, and
 // enqueues the HIP kernels on the caller's stream.  No allocation, no
-// synchronisation, no global mutable state.
+// synchronisation, no global mutable state.  (coli_moe_forward_noalloc, in
+// noalloc.hip, adds a per-device address cache for its static scratch.)
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -122,6 +123,7 @@ const char *coli_strerror(int status) {
     case COLI_EDTYPE: return "dtype not supported here";
     case COLI_EWORKSPACE: return "workspace missing or too small";
     case COLI_EDEVICE: return "HIP runtime reported a launch error";
+    case COLI_ESCRATCH: return "request larger than the no-alloc scratch array";
     default: return "unknown status";
   }
 }
@@ -410,6 +412,21 @@ int forward_launch(const coli_moe_layer *L, coli_mode mode, const void *x, int T
                          reinterpret_cast<uint16_t *>(y), s, ev ? ev + 2 : nullptr);
   return dev_status(e);
 }
+
+}  // namespace
+
+namespace coli {
+int forward_arg_check(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
+                      int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
+                      size_t *ws_need) {
+  WsLayout w;
+  const int rc = forward_checks(L, mode, x, T, y, topk_idx_out, topk_gate_out, status, &w);
+  *ws_need = rc == COLI_OK ? w.total : 0;
+  return rc;
+}
+}  // namespace coli
+
+namespace {
 
 int moe_forward_impl(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
                      int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,

@@ -119,6 +119,13 @@ __device__ inline void raise_status(int32_t *status, int bits) {
   if (status) atomicOr(status, bits);
 }
 
+// ---- coli.cpp ----------------------------------------------------------
+// The host-side argument checks of coli_moe_forward (no launch, no HIP call);
+// on COLI_OK *ws_need is the workspace the call needs.
+int forward_arg_check(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
+                      int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
+                      size_t *ws_need);
+
 // ---- quant.hip ----------------------------------------------------------
 hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
                                  uint8_t *packed, float *scales,

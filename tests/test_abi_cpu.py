@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_strerror_covers_codes():
-    for c in range(-6, 1):
+    for c in range(-7, 1):
         assert coli.lib.coli_strerror(c)
     assert coli.lib.coli_strerror(-99) == b"unknown status"
 
@@ -202,3 +202,31 @@ def test_product_does_not_import_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt.replace("oracle is", ""), f
     assert "int4_grouped_expert_amd" in sys.modules
+
+
+def test_noalloc_rejects_before_launch():
+    """The no-alloc forward reports argument errors as coli_moe_forward does, and a
+    call whose workspace exceeds the static scratch with ESCRATCH, before any HIP
+    call (the pointers here are not device memory)."""
+    L = coli.lib
+    a = P(1 << 20)
+    lay = coli.coli_moe_layer(6144, 2048, 256, 8, 1 << 20, coli.COLI_BF16, None, 1 << 30, 1 << 31)
+    assert L.coli_moe_forward_noalloc(None, 0, a, 1, a, None, None, None, None) == coli.COLI_EINVAL
+    assert L.coli_moe_forward_noalloc(ctypes.byref(lay), 0, None, 1, a, None, None, None,
+                                      None) == coli.COLI_EINVAL
+    # T = 2048 prefill of the decode-shaped layer needs far more than 32 MiB
+    assert L.coli_moe_workspace_bytes(ctypes.byref(lay), 2048, coli.COLI_PREFILL) > \
+        coli.COLI_NOALLOC_SCRATCH_BYTES
+    assert L.coli_moe_forward_noalloc(ctypes.byref(lay), coli.COLI_PREFILL, a, 2048, a, None,
+                                      None, None, None) == coli.COLI_ESCRATCH
+    # the documented limits: this layer fits decode up to T = 74, prefill up to 206
+    for mode, tmax in ((coli.COLI_DECODE, 74), (coli.COLI_PREFILL, 206)):
+        assert L.coli_moe_workspace_bytes(ctypes.byref(lay), tmax, mode) <= \
+            coli.COLI_NOALLOC_SCRATCH_BYTES
+        assert L.coli_moe_workspace_bytes(ctypes.byref(lay), tmax + 1, mode) > \
+            coli.COLI_NOALLOC_SCRATCH_BYTES
+    assert L.coli_moe_forward_noalloc(ctypes.byref(lay), coli.COLI_DECODE, a, 75, a, None,
+                                      None, None, None) == coli.COLI_ESCRATCH
+    assert L.coli_moe_forward_noalloc(ctypes.byref(lay), coli.COLI_DECODE, a, 0, a, None,
+                                      None, None, None) == coli.COLI_OK
+    assert L.coli_strerror(coli.COLI_ESCRATCH) != b"unknown status"
