@@ -53,7 +53,9 @@ enum {
     COLI_EDTYPE = -4,     /* dtype not supported for this call / mode */
     COLI_EWORKSPACE = -5, /* workspace NULL or smaller than required */
     COLI_EDEVICE = -6,    /* the HIP runtime reported a launch error */
-    COLI_ESCRATCH = -7    /* the call needs more than the no-alloc scratch holds */
+    COLI_ESCRATCH = -7,   /* the call needs more than the no-alloc scratch holds */
+    COLI_EUSAGE = -8,     /* a routing history refused (geometry, version, identity) */
+    COLI_EIO = -9         /* a routing history file could not be read or written */
 };
 
 typedef enum { COLI_F32 = 0, COLI_BF16 = 1 } coli_dtype;
@@ -360,6 +362,69 @@ int coli_moe_forward_noalloc(const coli_moe_layer *L, coli_mode mode,
                              const void *x, int T, void *y,
                              int32_t *topk_idx_out, float *topk_gate_out,
                              int32_t *status, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* routing history (page "colibrì 路由遥测全解析：.coli_usage专家历史、       */
+/* ROUTE_TRACE追踪流与route_trace.h统一格式")                               */
+/* ---------------------------------------------------------------------- */
+
+#define COLI_USAGE_VERSION 1
+
+/*
+ * Add one layer's routing decisions to device counters (section 历史文件: the
+ * engine counts, per layer, which experts each routing decision chose):
+ *   counts[layer][e] += number of (token, slot) pairs of topk_idx [T, K] with
+ *   id e.  counts: device uint64 [n_layers][n_experts], 8-byte aligned, kept
+ *   by the caller across calls.  Ids outside [0, n_experts) are not counted.
+ * Integer atomics: exact and order independent.  Errors: EINVAL, ESHAPE,
+ * EALIGN, EDEVICE.  T == 0 is a no-op.
+ */
+int coli_usage_count(const int32_t *topk_idx, int T, int K, int n_experts,
+                     int layer, int n_layers, uint64_t *counts, void *stream);
+
+/* The engine identity written in the history's "-2" record: the 32-bit
+ * FNV-1a hash of the engine's name (the page's glm_moe_dsa is 3815245270). */
+uint32_t coli_usage_engine_hash(const char *name);
+
+/*
+ * Write a routing history (host function; sections 历史文件, 头部记录为什么长这样,
+ * 三条铁律, 空历史 = 零字节文件, COLI_USAGE_DECAY).  counts: HOST uint64
+ * [n_layers][n_experts] (copied from the device counters by the caller).
+ * The file, text, one record of exactly three numbers per line:
+ *   -1 n_layers n_experts
+ *   -2 COLI_USAGE_VERSION engine_hash
+ *   layer expert count     (one per non-zero counter, ascending; counts above
+ *                           2^32 - 1 are written as 2^32 - 1)
+ * and nothing at all when every count is zero (a zero-byte file).  decay in
+ * (0, 1): each count becomes round(count * decay), a non-zero count never
+ * below 1; other values leave the counts as they are.  dropped: HOST
+ * [n_layers] flags or NULL; a dropped layer's counts are never written.  The
+ * file is written to "<path>.tmp.<pid>" and renamed over path; that
+ * temporary path is built, and rejected with EINVAL if it does not fit 4096
+ * bytes, before the file system is touched.  Errors: EINVAL, ESHAPE, EIO.
+ */
+int coli_usage_save(const char *path, const uint64_t *counts, int n_layers,
+                    int n_experts, uint32_t engine_hash, double decay,
+                    const uint8_t *dropped);
+
+/*
+ * Read a routing history into HOST counters (counts [n_layers][n_experts]
+ * are added to; section 可信读取 and 仍然兼容读取的旧布局).  A zero-byte file
+ * is an empty history.  Text files are read three numbers at a time: a "-1"
+ * record must carry these dimensions and a "-2" record this format version
+ * (both never relaxed) and engine_hash (relaxed when trusted != 0); records
+ * with another negative layer are skipped; a record whose layer or expert is
+ * out of range, or whose layer is dropped, is discarded.  Header-less legacy
+ * files are accepted as they are.  A file starting with the magic "IKU1" is
+ * the dense layout uint32 {magic, n_layers, n_experts} then uint32
+ * [n_layers][n_experts], read only when engine_hash is that of "inkling" and
+ * the dimensions match.  *accepted_total (optional) receives the sum of the
+ * accepted counts only.  On EUSAGE the counters may hold part of the file.
+ * Errors: EINVAL, ESHAPE, EIO (cannot open), EUSAGE (refused).
+ */
+int coli_usage_load(const char *path, uint64_t *counts, int n_layers,
+                    int n_experts, uint32_t engine_hash, int trusted,
+                    const uint8_t *dropped, uint64_t *accepted_total);
 
 /*
  * RMSNorm with unit weight between stacked layers:

@@ -36,6 +36,8 @@ lib = ctypes.CDLL(_LIB_PATH)
 
 COLI_OK, COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN = 0, -1, -2, -3
 COLI_EDTYPE, COLI_EWORKSPACE, COLI_EDEVICE, COLI_ESCRATCH = -4, -5, -6, -7
+COLI_EUSAGE, COLI_EIO = -8, -9
+COLI_USAGE_VERSION = 1
 COLI_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 COLI_F32, COLI_BF16 = 0, 1
 COLI_DECODE, COLI_PREFILL = 0, 1
@@ -52,6 +54,7 @@ EXPORTS = [
     "coli_expert_permute_workspace_bytes", "coli_expert_permute", "coli_expert_blob_bytes",
     "coli_expert_views", "coli_expert_finish", "coli_quant_expert", "coli_moe_workspace_bytes",
     "coli_moe_forward", "coli_moe_forward_timed", "coli_moe_forward_noalloc",
+    "coli_usage_count", "coli_usage_engine_hash", "coli_usage_save", "coli_usage_load",
     "coli_rmsnorm_f32",
 ]
 
@@ -99,6 +102,11 @@ _proto("coli_moe_forward_timed", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i
 _proto("coli_moe_forward_noalloc", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p,
                                         _p, _p])
 _proto("coli_rmsnorm_f32", _i, [_p, _p, _i, _i, ctypes.c_float, _p])
+_proto("coli_usage_count", _i, [_p, _i, _i, _i, _i, _i, _p, _p])
+_proto("coli_usage_engine_hash", ctypes.c_uint32, [ctypes.c_char_p])
+_proto("coli_usage_save", _i, [ctypes.c_char_p, _p, _i, _i, ctypes.c_uint32, ctypes.c_double, _p])
+_proto("coli_usage_load", _i, [ctypes.c_char_p, _p, _i, _i, ctypes.c_uint32, _i, _p,
+                               ctypes.POINTER(ctypes.c_uint64)])
 
 
 class ColiError(RuntimeError):
@@ -258,6 +266,44 @@ def coli_rmsnorm_f32(x, y, eps=1e-6, stream=None):
     T, H = x.shape
     return _check(lib.coli_rmsnorm_f32(_ptr(x), _ptr(y), T, H, ctypes.c_float(eps),
                                        _stream(stream)), "coli_rmsnorm_f32")
+
+
+# ---------------------------------------------------------------- routing history
+
+def coli_usage_count(topk_idx, n_experts: int, layer: int, counts, stream=None):
+    """counts: uint64-sized device tensor [n_layers, n_experts] (torch.int64)."""
+    T, K = topk_idx.shape
+    return _check(lib.coli_usage_count(_ptr(topk_idx), T, K, n_experts, layer, counts.shape[0],
+                                       _ptr(counts), _stream(stream)), "coli_usage_count")
+
+
+def coli_usage_engine_hash(name: str) -> int:
+    return int(lib.coli_usage_engine_hash(name.encode()))
+
+
+def coli_usage_save(path: str, counts, engine_hash: int, decay: float = 1.0, dropped=None):
+    """counts: host numpy uint64 [n_layers, n_experts]; dropped: host uint8 [n_layers]."""
+    import numpy as np
+    c = np.ascontiguousarray(counts, dtype=np.uint64)
+    d = None if dropped is None else np.ascontiguousarray(dropped, dtype=np.uint8)
+    return _check(lib.coli_usage_save(path.encode(), c.ctypes.data_as(_p), c.shape[0], c.shape[1],
+                                      engine_hash, decay,
+                                      None if d is None else d.ctypes.data_as(_p)),
+                  "coli_usage_save")
+
+
+def coli_usage_load(path: str, n_layers: int, n_experts: int, engine_hash: int, trusted=False,
+                    dropped=None):
+    """-> (counts numpy uint64 [n_layers, n_experts], accepted_total); raises ColiError."""
+    import numpy as np
+    c = np.zeros((n_layers, n_experts), dtype=np.uint64)
+    d = None if dropped is None else np.ascontiguousarray(dropped, dtype=np.uint8)
+    tot = ctypes.c_uint64(0)
+    _check(lib.coli_usage_load(path.encode(), c.ctypes.data_as(_p), n_layers, n_experts,
+                               engine_hash, int(bool(trusted)),
+                               None if d is None else d.ctypes.data_as(_p), ctypes.byref(tot)),
+           "coli_usage_load")
+    return c, int(tot.value)
 
 
 # ---------------------------------------------------------------- layer assembly

@@ -124,6 +124,8 @@ const char *coli_strerror(int status) {
     case COLI_EWORKSPACE: return "workspace missing or too small";
     case COLI_EDEVICE: return "HIP runtime reported a launch error";
     case COLI_ESCRATCH: return "request larger than the no-alloc scratch array";
+    case COLI_EUSAGE: return "routing history refused (geometry, version or identity)";
+    case COLI_EIO: return "routing history file could not be read or written";
     default: return "unknown status";
   }
 }

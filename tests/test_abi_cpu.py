@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_strerror_covers_codes():
-    for c in range(-7, 1):
+    for c in range(-9, 1):
         assert coli.lib.coli_strerror(c)
     assert coli.lib.coli_strerror(-99) == b"unknown status"
 
