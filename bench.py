@@ -140,9 +140,40 @@ def run_decode(coli, W, layers, cfg_id, T, steps, warmup, pool_n=64):
         for s_ in range(3):
             stage[s_] += ev[2 * s_].elapsed_time(ev[2 * s_ + 1])
     stage = [s_ / nst for s_ in stage]
-    nu = int(torch.unique(idx).numel())
-    return dict(ms=ms, wall=wall, steps=steps, stage_ms=stage, T=T, n_unique_last=nu,
-                idx_last=idx.cpu())
+    # the distribution of the plain step: blocks of `blk` back-to-back steps with
+    # an event between blocks (so the events barely touch the steps they time)
+    blk = 10
+    nblk = max(20, min(300, steps // blk))
+    bev = [torch.cuda.Event(enable_timing=True) for _ in range(nblk + 1)]
+    torch.cuda.synchronize()
+    bev[0].record()
+    for b in range(nblk):
+        for j in range(blk):
+            call(b * blk + j)
+        bev[b + 1].record()
+    torch.cuda.synchronize()
+    per_step = [bev[b].elapsed_time(bev[b + 1]) / blk for b in range(nblk)]
+    # unique experts of each pool batch (the timed loop cycles the pool): the
+    # algorithmic bytes of a step depend on it
+    uniq = []
+    for p in range(pool_n):
+        callers[0][p]()
+        uniq.append(int(torch.unique(idx).numel()))
+    u_mean = sum(uniq[i % pool_n] for i in range(warmup, warmup + steps)) / steps
+    return dict(ms=ms, wall=wall, steps=steps, stage_ms=stage, T=T, u_mean=u_mean,
+                step_ms=dist(per_step))
+
+
+def dist(v):
+    """Median, p10 and p90 of a list of times (ms), and how many (here: per-step
+    times of blocks of 10 back-to-back steps)."""
+    v = sorted(v)
+    n = len(v)
+
+    def q(f):
+        return v[min(n - 1, int(round(f * (n - 1))))]
+    return {"median": round(q(0.5), 5), "p10": round(q(0.1), 5), "p90": round(q(0.9), 5),
+            "n": n}
 
 
 def decode_bytes(c, U, T):
@@ -150,7 +181,7 @@ def decode_bytes(c, U, T):
     H, I, E = c["H"], c["I"], c["E"]
     blob = 3 * (I * (H // 64) * 32 + I * (H // 64) * 4)  # gate+up+down nibbles and scales
     router = E * H * (2 if c["router"] == "bf16" else 4)
-    return router + (U + 1) * blob + 2 * T * H * 4
+    return int(router + (U + 1) * blob + 2 * T * H * 4)
 
 
 def gateup_bytes(c, U, T):
@@ -204,25 +235,62 @@ def run_prefill(coli, W, layer, steps=10, warmup=2):
                 flops=flops_routed + flops_shared, dtype="fp16 MFMA operands (bf16 I/O)")
 
 
-def cpu_baseline(coli, W, budget_s=12.0, n_tok=6):
-    """The oracle (fp64, as committed) on a bounded sample of the decode workload:
-    n_tok tokens of the pool (their experts quantised by the oracle beforehand,
-    untimed), cycled through single-token forwards for about budget_s seconds."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_layer_experts(W, cfg_id, ids, layer=0):
+    """The oracle's own quantisation of the listed experts (and the shared one)."""
+    import oracle
+    E = W.CONFIGS[cfg_id]["E"]
+    experts = [None] * E
+    for e in ids:
+        experts[e] = oracle.Expert.quantise(
+            *(w.cpu().numpy() for w in W.expert_weights(cfg_id, e, "cuda", layer)))
+    shared = oracle.Expert.quantise(
+        *(w.cpu().numpy() for w in W.expert_weights(cfg_id, E, "cuda", layer)))
+    return experts, shared
+
+
+def cpu_baseline(coli, W, budget_s=6.0, n_tok=6):
+    """The oracle (fp64, as committed, OpenMP over the host cores) on bounded samples
+    of each workload, its experts quantised by the oracle beforehand (untimed):
+      decode T=1   -- n_tok tokens cycled for about budget_s seconds;
+      decode T=32  -- one Zipf batch of 32 tokens;
+      prefill      -- 64 of the 2048 tokens, scaled x 32 (the oracle's time per token
+                      does not depend on the batch);
+      stack step   -- layer 0 of the 40-layer stack on its 8 tokens, scaled x 40;
+      quantiser    -- 16 of one layer's 256 experts, scaled x 16.
+    The headline fields are the T=1 leg's; `legs` holds every leg."""
     import numpy as np
     import oracle
     import torch
     c = W.CONFIGS[1]
     H, I, E, K = c["H"], c["I"], c["E"], c["K"]
-    wr = W.router_weights(1, "cuda")
-    wr_h = wr.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    def bits(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
+            else t.cpu().numpy()
+    wr_h = bits(W.router_weights(1, "cuda"))
     pool = W.token_pool(1, 64, "cuda").cpu().numpy()
-    logits = oracle.router_logits(pool[:n_tok], wr_h, None)
-    idx, _, _ = oracle.topk(logits, K)
-    need = sorted(set(idx.reshape(-1).tolist()))
-    experts = [None] * E
-    for e in need:
-        experts[e] = oracle.Expert.quantise(*(w.cpu().numpy() for w in W.expert_weights(1, e, "cuda")))
-    shared = oracle.Expert.quantise(*(w.cpu().numpy() for w in W.expert_weights(1, E, "cuda")))
+    x32 = W.tokens(2, 32, "cuda").cpu().numpy()
+    b32 = W.router_bias(2)
+    xp = bits(W.tokens(3, 2048, "cuda"))[:64].copy()
+    need = set()
+    for xs, b in ((pool[:n_tok], None), (x32, b32), (xp, None)):
+        idx, _, _ = oracle.topk(oracle.router_logits(xs, wr_h, b), K)
+        need |= set(idx.reshape(-1).tolist())
+    t_prep = time.perf_counter()
+    experts, shared = oracle_layer_experts(W, 1, sorted(need))
+    log(f"[bench] cpu baseline: {len(need)} experts quantised by the oracle "
+        f"({time.perf_counter() - t_prep:.1f} s, untimed)")
+    legs = {}
     done = 0
     t0 = time.perf_counter()
     while (time.perf_counter() - t0) < budget_s:
@@ -230,12 +298,51 @@ def cpu_baseline(coli, W, budget_s=12.0, n_tok=6):
         oracle.moe_forward(pool[k:k + 1], wr_h, None, experts, shared, H, I, K)
         done += 1
     el = time.perf_counter() - t0
-    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"{done} single-token decode forwards of the same layer (H=6144, I=2048, "
-                      f"E=256, K=8 + shared), {n_tok} distinct tokens cycled, fp64, {el:.1f} s; "
-                      f"their {len(need)} experts + shared quantised by the oracle beforehand "
-                      f"(untimed)"}
+    legs["decode_t1"] = {"value": round(done / el, 3), "unit": "tokens/s",
+                         "sample": f"{done} single-token forwards, {n_tok} tokens cycled, "
+                                   f"{el:.1f} s"}
+    t0 = time.perf_counter()
+    oracle.moe_forward(x32, wr_h, b32, experts, shared, H, I, K)
+    el = time.perf_counter() - t0
+    legs["decode_t32_zipf"] = {"value": round(32 / el, 3), "unit": "tokens/s",
+                               "ms_per_step": round(el * 1e3, 1),
+                               "sample": f"one batch of 32 tokens, {el:.1f} s"}
+    t0 = time.perf_counter()
+    oracle.moe_forward(xp, wr_h, None, experts, shared, H, I, K)
+    el = time.perf_counter() - t0
+    legs["prefill_t2048"] = {"value": round(64 / el, 3), "unit": "tokens/s",
+                             "ms_per_forward": round(el * 1e3 * 2048 / 64, 1),
+                             "sample": f"64 of the 2048 tokens in {el:.1f} s, scaled x 32"}
+    # stack: layer 0 of the stack workload, its own experts and bias
+    cs = W.CONFIGS[4]
+    wr4 = bits(W.router_weights(4, "cuda", 0))
+    b4 = W.router_bias(4, 0)
+    x4 = W.tokens(4, cs["T"], "cuda").cpu().numpy()
+    idx4, _, _ = oracle.topk(oracle.router_logits(x4, wr4, b4), K)
+    ex4, sh4 = oracle_layer_experts(W, 4, sorted(set(idx4.reshape(-1).tolist())), 0)
+    t0 = time.perf_counter()
+    y4, _, _ = oracle.moe_forward(x4, wr4, b4, ex4, sh4, H, I, K)
+    oracle.rmsnorm(y4, 1e-6)
+    el = time.perf_counter() - t0
+    legs["stack_t8_40_layers"] = {"value": round(cs["T"] / (el * 40), 3), "unit": "tokens/s",
+                                  "ms_per_step": round(el * 1e3 * 40, 1),
+                                  "sample": f"layer 0 of 40 on 8 tokens in {el:.2f} s, "
+                                            f"scaled x 40"}
+    draws = [[w.cpu().numpy() for w in W.expert_weights(4, e, "cuda", 0)] for e in range(16)]
+    t0 = time.perf_counter()
+    for ws in draws:
+        for w in ws:
+            oracle.quant_int4_g64(w)
+    el = time.perf_counter() - t0
+    legs["quantise_one_layer"] = {"value": round(el * 1e3 * 16, 1), "unit": "ms per layer",
+                                  "sample": f"16 of 256 experts (48 matrices) in {el:.2f} s, "
+                                            f"scaled x 16"}
+    head = legs["decode_t1"]
+    return {"value": head["value"], "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"decode T=1: {head['sample']} (H=6144, I=2048, E=256, K=8 + shared, "
+                      f"fp64); experts quantised by the oracle beforehand (untimed)",
+            "legs": legs}
 
 
 def profiled_traffic(kernel_src, kernel):
@@ -328,6 +435,7 @@ def main():
                    "replicas": args.replicas, "token_pool": 64},
         "hbm": {"bytes_per_step": step_bytes, "gbps": round(gbps, 1),
                 "frac": round(gbps / HBM_PEAK_GBS, 4)},
+        "step_ms": d["step_ms"],
         "stage_ms": {"route": round(d["stage_ms"][0], 5), "gateup": round(d["stage_ms"][1], 5),
                      "down_combine": round(d["stage_ms"][2], 5)},
         "roofline": {"kernel": "gateup_narrow", "bound": "hbm",
@@ -338,15 +446,26 @@ def main():
                      "bytes_per_launch": gu_bytes, "avg_launch_ms": round(gu_ms, 5)},
     }
     if not args.no_extras:
+        log("[bench] decode T=1, one replica (its 191 MB fit the 256 MB Infinity Cache)")
+        d1 = run_decode(coli, W, layers[:1], 1, 1, max(1000, args.steps // 3), 100)
+        ms1 = d1["ms"] / d1["steps"]
+        result["single_replica_cached"] = {
+            "note": "the same step on one copy of the layer: weights may be served from "
+                    "the Infinity Cache, so this is not an HBM figure",
+            "tokens_per_s": round(1.0 / (ms1 * 1e-3), 1), "ms_per_step": round(ms1, 5),
+            "step_ms": d1["step_ms"],
+            "stage_ms": [round(x, 5) for x in d1["stage_ms"]]}
         log("[bench] decode T=32 zipf")
         zl, _ = build_layer_bias(coli, W, layers)
         d32 = run_decode(coli, W, zl, 2, 32, max(200, args.steps // 10), 20)
-        U32 = int(torch.unique(d32["idx_last"]).numel())
+        U32 = d32["u_mean"]
         ms32 = d32["ms"] / d32["steps"]
         b32 = decode_bytes(W.CONFIGS[2], U32, 32)
         result["decode_t32_zipf"] = {
             "tokens_per_s": round(32 / (ms32 * 1e-3), 1), "ms_per_step": round(ms32, 4),
-            "unique_experts_last_step": U32,
+            "step_ms": d32["step_ms"],
+            "unique_experts_mean": round(U32, 2),
+            "bytes_per_step": int(b32),
             "gbps": round(b32 / (ms32 * 1e-3) / 1e9, 1),
             "frac": round(b32 / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "stage_ms": [round(s, 4) for s in d32["stage_ms"]]}

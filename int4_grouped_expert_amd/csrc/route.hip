@@ -19,8 +19,8 @@
 //   topk_permute_small    one block: top-K for all tokens, then the permute
 //                         (decode: one launch for the whole route stage).
 //   permute_count/scan/place  the permute for large T in three launches:
-//                         per-chunk (64 pairs) expert bitmaps, a scan over
-//                         chunks, then stable placement by bitmap popcount.
+//                         per-chunk (256 pairs) expert bitmaps, a scan over
+//                         chunks, then stable placement by bitmap popcounts.
 //   router_logits_any     logits for any H and any row alignment (scalar
 //                         loads), the fallback of the vector kernels.
 //   router_topk_fused     logits of one token kept in LDS, then its top-K:
@@ -443,12 +443,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 }
 
 // ---------------------------------------------------------------- permute
-// The permute walks the T*K (token, slot) pairs p = t*K + slot in chunks of 64
-// pairs: per chunk, bm[e] has bit (p - p0) set if pair p chose expert e, and a
-// pair's rank inside its expert's segment is the expert's base plus the pairs
-// of the chunk before it (a popcount).  Counting pairs, not tokens, keeps the
-// placement stable and complete when a row names the same expert twice.
-constexpr int kChunk = 64;  // pairs per bitmap chunk (one bit per pair)
+// The permute walks the T*K (token, slot) pairs p = t*K + slot in chunks of 256
+// pairs: per chunk, bm[e] is a 256-bit set (four 64-bit words) with bit
+// (p - p0) set if pair p chose expert e, and a pair's rank inside its
+// expert's segment is the expert's base plus the pairs of the chunk before it
+// (popcounts).  Counting pairs, not tokens, keeps the placement stable and
+// complete when a row names the same expert twice.
+constexpr int kChunkW = 4;             // 64-bit words per expert and chunk
+constexpr int kChunk = 64 * kChunkW;   // pairs per bitmap chunk
 
 // Block-wide exclusive scan of one int per thread (blockDim.x <= 1024).
 __device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
@@ -477,28 +479,50 @@ __device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
   return res;
 }
 
-// Bitmap of the pair chunk starting at p0: bm[e] bit (p - p0) set if pair p
+typedef unsigned long long ChunkBits[kChunkW];
+
+// Bitmaps of the pair chunk starting at p0: bm[e] bit (p - p0) set if pair p
 // (p < P = T*K) chose e.
 __device__ void build_bitmap(const int32_t *__restrict__ idx, int P, int E, int p0,
-                             unsigned long long *bm) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) bm[e] = 0ull;
+                             ChunkBits *bm) {
+  for (int i = threadIdx.x; i < E * kChunkW; i += blockDim.x) bm[i / kChunkW][i % kChunkW] = 0ull;
   __syncthreads();
   const int pend = min(P, p0 + kChunk);
   for (int p = p0 + int(threadIdx.x); p < pend; p += blockDim.x) {
     const int e = idx[p];
-    if (e >= 0 && e < E) atomicOr(&bm[e], 1ull << (p - p0));
+    const int l = p - p0;
+    if (e >= 0 && e < E) atomicOr(&bm[e][l >> 6], 1ull << (l & 63));
   }
   __syncthreads();
 }
 
+// pairs of the chunk before local position l that chose e
+__device__ inline int rank_in_chunk(const ChunkBits &b, int l) {
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < kChunkW; ++w) {
+    if (w < (l >> 6)) r += __popcll(b[w]);
+    else if (w == (l >> 6)) r += __popcll(b[w] & ((1ull << (l & 63)) - 1ull));
+  }
+  return r;
+}
+__device__ inline int chunk_count(const ChunkBits &b) {
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < kChunkW; ++w) r += __popcll(b[w]);
+  return r;
+}
+
+// base: the rank of the chunk's first pair of each expert (LDS or global);
+// extra: added to it (the expert's offset when base holds chunk-relative values)
 __device__ void place_chunk(const int32_t *__restrict__ idx, int P, int E, int p0,
-                            const unsigned long long *bm, const int *base,
+                            const ChunkBits *bm, const int *base, const int32_t *extra,
                             int32_t *__restrict__ perm) {
   const int pend = min(P, p0 + kChunk);
   for (int p = p0 + int(threadIdx.x); p < pend; p += blockDim.x) {
     const int e = idx[p];
     if (e < 0 || e >= E) continue;  // ids outside [0, E) are skipped
-    perm[base[e] + __popcll(bm[e] & ((1ull << (p - p0)) - 1ull))] = p;
+    perm[base[e] + (extra ? extra[e] : 0) + rank_in_chunk(bm[e], p - p0)] = p;
   }
 }
 
@@ -524,7 +548,7 @@ __device__ void finish_counts(const Routing &r, int T, int K, int E, int cnt_e,
 // One block of 1024 threads: optional top-K, then the whole permute.
 __global__ __launch_bounds__(1024) void topk_permute_small(Routing r, int T, int E, int K,
                                                            int do_topk) {
-  __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
+  __shared__ ChunkBits bm[COLI_MAX_EXPERTS];
   __shared__ int cursor[COLI_MAX_EXPERTS];
   __shared__ int cnt[COLI_MAX_EXPERTS];
   __shared__ int wave_tot[16];
@@ -549,9 +573,9 @@ __global__ __launch_bounds__(1024) void topk_permute_small(Routing r, int T, int
   __syncthreads();
   for (int p0 = 0; p0 < P; p0 += kChunk) {
     build_bitmap(r.idx, P, E, p0, bm);
-    place_chunk(r.idx, P, E, p0, bm, cursor, r.perm);
+    place_chunk(r.idx, P, E, p0, bm, cursor, nullptr, r.perm);
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] += __popcll(bm[e]);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] += chunk_count(bm[e]);
     __syncthreads();
   }
 }
@@ -561,7 +585,7 @@ __global__ __launch_bounds__(1024) void topk_permute_small(Routing r, int T, int
 constexpr int kDecMC = 32;  // tokens per M-chunk of the decode expert kernels
 
 __global__ __launch_bounds__(1024) void route_decode_kernel(Routing r, int T, int E, int K) {
-  __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
+  __shared__ ChunkBits bm[COLI_MAX_EXPERTS];
   __shared__ int cursor[COLI_MAX_EXPERTS];
   __shared__ int cnt[COLI_MAX_EXPERTS];
   __shared__ int uidx[COLI_MAX_EXPERTS];
@@ -595,9 +619,9 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(Routing r, int T, in
   __syncthreads();
   for (int p0 = 0; p0 < P; p0 += kChunk) {
     build_bitmap(r.idx, P, E, p0, bm);
-    place_chunk(r.idx, P, E, p0, bm, cursor, r.perm);
+    place_chunk(r.idx, P, E, p0, bm, cursor, nullptr, r.perm);
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] += __popcll(bm[e]);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] += chunk_count(bm[e]);
     __syncthreads();
   }
 }
@@ -668,40 +692,46 @@ __global__ __launch_bounds__(1024) void route_decode_small(Routing r, int T, int
   }
 }
 
-// Large T: per-chunk counts -> r.chunk[c*E + e] (chunk c = pairs 64c .. 64c+63).
+// Large T: per-chunk counts -> r.chunk[c*E + e] (chunk c = pairs 256c .. +255).
 __global__ __launch_bounds__(256) void permute_count(Routing r, int T, int K, int E) {
-  __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
+  __shared__ ChunkBits bm[COLI_MAX_EXPERTS];
   build_bitmap(r.idx, T * K, E, int(blockIdx.x) * kChunk, bm);
   for (int e = threadIdx.x; e < E; e += blockDim.x)
-    r.chunk[size_t(blockIdx.x) * E + e] = __popcll(bm[e]);
+    r.chunk[size_t(blockIdx.x) * E + e] = chunk_count(bm[e]);
 }
 
 // One block of 1024: totals per expert, offsets, unique; chunk counts become
-// absolute bases.
+// bases relative to the expert's offset (permute_place adds the offset).  The
+// chunk column of an expert is read 16 entries at a time (the loads are
+// independent; only the running sum is serial).
 __global__ __launch_bounds__(1024) void permute_scan(Routing r, int T, int K, int E, int nc) {
   __shared__ int wave_tot[16];
   __shared__ int total;
+  constexpr int kB = 16;
   const int e = threadIdx.x;
   int run = 0;
   if (e < E)
-    for (int c = 0; c < nc; ++c) {
-      const int v = r.chunk[size_t(c) * E + e];
-      r.chunk[size_t(c) * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nc; c0 += kB) {
+      int v[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) v[j] = c0 + j < nc ? r.chunk[size_t(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (c0 + j < nc) r.chunk[size_t(c0 + j) * E + e] = run;
+        run += v[j];
+      }
     }
   int excl = 0;
   finish_counts(r, T, K, E, run, wave_tot, &total, &excl);
-  if (e < E)
-    for (int c = 0; c < nc; ++c) r.chunk[size_t(c) * E + e] += excl;
 }
 
 __global__ __launch_bounds__(256) void permute_place(Routing r, int T, int K, int E) {
-  __shared__ unsigned long long bm[COLI_MAX_EXPERTS];
+  __shared__ ChunkBits bm[COLI_MAX_EXPERTS];
   __shared__ int base[COLI_MAX_EXPERTS];
   for (int e = threadIdx.x; e < E; e += blockDim.x) base[e] = r.chunk[size_t(blockIdx.x) * E + e];
   const int p0 = int(blockIdx.x) * kChunk;
   build_bitmap(r.idx, T * K, E, p0, bm);  // contains the barrier for base[]
-  place_chunk(r.idx, T * K, E, p0, bm, base, r.perm);
+  place_chunk(r.idx, T * K, E, p0, bm, base, r.offsets, r.perm);
 }
 
 // One block does the whole permute up to this many pairs.

@@ -142,7 +142,7 @@ def test_permute_rejects_before_launch():
     assert L.coli_expert_permute(None, 1, 2, 8, a, a, a, a, a, None, 0, None) == coli.COLI_EINVAL
     assert L.coli_expert_permute(a, 1, 9, 8, a, a, a, a, a, None, 0, None) == coli.COLI_ESHAPE
     need = coli.coli_expert_permute_workspace_bytes(2048, 8, 256)
-    assert need == 256 * 256 * 4  # one count per (64-pair chunk, expert)
+    assert need == 64 * 256 * 4  # one count per (256-pair chunk, expert)
     assert coli.coli_expert_permute_workspace_bytes(32, 8, 256) == 0
     assert coli.coli_expert_permute_workspace_bytes(32, 9, 8) == 0  # K > E: invalid
     assert (L.coli_expert_permute(a, 2048, 8, 256, a, a, a, a, a, None, 0, None)
