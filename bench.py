@@ -128,6 +128,8 @@ def run_decode(coli, W, layers, cfg_id, T, steps, warmup, pool_n=64):
     # event pair on its stream; on the single-token path each stage is one
     # kernel and the pair is stamped by that kernel's launch
     nst = min(steps, 400)
+    if nst < steps and steps < 400:
+        nst = steps
     evs = [make_events(6) for _ in range(nst)]
     torch.cuda.synchronize()
     if hasattr(torch.cuda, "_sleep"):
@@ -447,7 +449,8 @@ def main():
     }
     if not args.no_extras:
         log("[bench] decode T=1, one replica (its 191 MB fit the 256 MB Infinity Cache)")
-        d1 = run_decode(coli, W, layers[:1], 1, 1, max(1000, args.steps // 3), 100)
+        d1 = run_decode(coli, W, layers[:1], 1, 1, max(100, args.steps // 3),
+                        min(100, args.warmup))
         ms1 = d1["ms"] / d1["steps"]
         result["single_replica_cached"] = {
             "note": "the same step on one copy of the layer: weights may be served from "
@@ -457,7 +460,7 @@ def main():
             "stage_ms": [round(x, 5) for x in d1["stage_ms"]]}
         log("[bench] decode T=32 zipf")
         zl, _ = build_layer_bias(coli, W, layers)
-        d32 = run_decode(coli, W, zl, 2, 32, max(200, args.steps // 10), 20)
+        d32 = run_decode(coli, W, zl, 2, 32, max(20, args.steps // 10), min(20, args.warmup))
         U32 = d32["u_mean"]
         ms32 = d32["ms"] / d32["steps"]
         b32 = decode_bytes(W.CONFIGS[2], U32, 32)
@@ -472,7 +475,7 @@ def main():
         del zl
         log("[bench] tiny T=1")
         tl, _ = build_layer(coli, W, 0, 1)
-        dt = run_decode(coli, W, tl, 0, 1, max(1000, args.steps // 3), 100)
+        dt = run_decode(coli, W, tl, 0, 1, max(100, args.steps // 3), min(100, args.warmup))
         mst = dt["ms"] / dt["steps"]
         result["tiny_t1"] = {
             "workload": "tiny: H=256 I=128, 16 experts top-4 + 1 shared, T=1 fp32 token "
@@ -481,7 +484,8 @@ def main():
             "stage_us": [round(1e3 * x, 2) for x in dt["stage_ms"]]}
         del tl
         log("[bench] prefill T=2048")
-        result["prefill"] = run_prefill(coli, W, layers[0])
+        result["prefill"] = run_prefill(coli, W, layers[0],
+                                        steps=max(2, min(10, args.steps // 300)))
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(coli, W)

@@ -257,12 +257,22 @@ __shared__ int g_outrow[kMC];   // output row
 __shared__ float g_gate[kMC];   // gate (down)
 __shared__ int g_xe[kMC];       // the token's activation exponent (gate/up)
 
+// Waves of a prefill GEMM block: two per SIMD.  The two waves on one SIMD
+// (w and w + 4) share the block's activation stage and split the N rows: wave
+// (simd, half) owns one 32-row weight fragment, so that one wave's dequant and
+// exchange VALU work runs beside the other wave's MFMAs.
+constexpr int kPW = 8;
+constexpr int kPThreads = kPW * kWave;
+constexpr int kRowsPW = kMC / kPW;      // staged rows each wave's DMA fills (16)
+constexpr int kDmaPW = kRowsPW / 2;     // DMA instructions per wave per stage (8)
+
 // One work item.  NMF = number of 32-row M fragments the chunk needs (1..4).
 template <bool kGateUp, int NMF>
 __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L, const PfArgs &pa,
                                                                const Item &it) {
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
+  const int sw = wave & 3, half = wave >> 2;  // SIMD slot, fragment of the pair
   const int h = lane >> 5, n = lane & 31;
   const int G = int(kGateUp ? L.lay.GH : L.lay.GI);
   const int nss = (G + 3) >> 2;
@@ -273,121 +283,98 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
   // empty resource: every access reads zeros (loads of the last super-step)
   const __amdgpu_buffer_rsrc_t rnull = make_rsrc(pa.A, 0);
 
-  // weight rows of this wave (all valid or all past the matrix: 64 | rows);
-  // fragment jn = gate (0) / up (1) rows wrow0 .. +31 for gate/up, rows
-  // wrow0 + 32 jn .. +31 for down
+  // this wave's 32 weight rows: gate/up: features wrow0 .. +31 of the N-tile's
+  // 128, gate (half 0) or up (half 1); down: rows wrow0 .. +31 of the 256
   int wrow0;
   bool wvalid;
+  uint32_t qsec, ssec;
   if (kGateUp) {
-    wrow0 = it.ntile * 128 + 32 * wave;
+    wrow0 = it.ntile * 128 + 32 * sw;
     wvalid = wrow0 < L.I;
+    qsec = uint32_t(half == 0 ? L.lay.gq : L.lay.uq);
+    ssec = uint32_t(half == 0 ? L.lay.gs : L.lay.us);
   } else {
-    wrow0 = it.ntile * 256 + 64 * wave;
+    wrow0 = it.ntile * 256 + 64 * sw + 32 * half;
     wvalid = wrow0 < L.H;
+    qsec = uint32_t(L.lay.dq);
+    ssec = uint32_t(L.lay.ds);
   }
   // a wave past the matrix runs the same instruction stream on an empty weight
   // resource (zeros) and stores nothing: no wave-dependent branch in the loop
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(it.blob, wvalid ? uint32_t(L.lay.bytes) : 0u);
-  uint32_t xoff[2], soff[2];
-#pragma unroll
-  for (int jn = 0; jn < 2; ++jn) {
-    int row;
-    uint32_t qsec, ssec;
-    if (kGateUp) {
-      row = wrow0;
-      qsec = uint32_t(jn == 0 ? L.lay.gq : L.lay.uq);
-      ssec = uint32_t(jn == 0 ? L.lay.gs : L.lay.us);
-    } else {
-      row = wrow0 + 32 * jn;
-      qsec = uint32_t(L.lay.dq);
-      ssec = uint32_t(L.lay.ds);
-    }
-    // load a (0..3) of lane (h, n): row 8a + n%8, part 4h + n/8.  In the last
-    // super-step lanes past G read the next bytes of the blob (a q section is
-    // always followed by another section); their scale is 0.
-    xoff[jn] = qsec + uint32_t(row + (n & 7)) * rowB + 16u * uint32_t(4 * h + (n >> 3));
-    // scales of lane (h, n): row n, groups 16i + 8h ..
-    soff[jn] = ssec + uint32_t(row + n) * uint32_t(G) * 4u + 32u * uint32_t(h);
-  }
+  // load a (0..3) of lane (h, n): row 8a + n%8, part 4h + n/8.  In the last
+  // super-step lanes past G read the next bytes of the blob (a q section is
+  // always followed by another section); their scale is 0.
+  const uint32_t xoff = qsec + uint32_t(wrow0 + (n & 7)) * rowB + 16u * uint32_t(4 * h + (n >> 3));
+  // scales of lane (h, n): row n, groups 16i + 8h ..
+  const uint32_t soff = ssec + uint32_t(wrow0 + n) * uint32_t(G) * 4u + 32u * uint32_t(h);
 
-  // DMA roles: instruction i of this wave fills staged rows 32w + 2i, 32w + 2i + 1
-  // (lane: row + lane/32, LDS chunk lane%32); correction instruction i fills
-  // rows 32w + 16i .. +15 (lane: row + lane/4, LDS chunk lane%4)
-  uint32_t aoff[16], coff[2];
+  // DMA roles: instruction i of this wave fills staged rows 16w + 2i, 16w + 2i + 1
+  // (lane: row + lane/32, LDS chunk lane%32); the correction instruction fills
+  // rows 16w .. 16w + 15 (lane: row + lane/4, LDS chunk lane%4)
+  uint32_t aoff[kDmaPW], coff;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 32 * wave + 2 * i + (lane >> 5);
+  for (int i = 0; i < kDmaPW; ++i) {
+    const int r = kRowsPW * wave + 2 * i + (lane >> 5);
     const int ri = g_rowidx[r];
     const uint32_t chunk = uint32_t((lane & 31) ^ (r & 15));
     aoff[i] = ri >= 0 ? uint32_t(ri) * uint32_t(pa.AP) * 2u + 16u * chunk : kOff;
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 32 * wave + 16 * i + (lane >> 2);
+  {
+    const int r = kRowsPW * wave + (lane >> 2);
     const int ri = g_rowidx[r];
     const uint32_t chunk = uint32_t((lane & 3) ^ ((r >> 2) & 3));
-    coff[i] = ri >= 0 ? uint32_t(ri) * uint32_t(pa.CS) * 2u + 16u * chunk : kOff;
+    coff = ri >= 0 ? uint32_t(ri) * uint32_t(pa.CS) * 2u + 16u * chunk : kOff;
   }
   auto dma_a = [&](int ss, uint8_t *st) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      dma16(ra, st + (32 * wave + 2 * i) * kRowB, aoff[i], uint32_t(512 * ss));
+    for (int i = 0; i < kDmaPW; ++i)
+      dma16(ra, st + (kRowsPW * wave + 2 * i) * kRowB, aoff[i], uint32_t(512 * ss));
   };
   // correction operand of block i: entries 32i .. 32i + 31 (groups 16i .. 16i + 15,
   // hi and lo); entries past the groups are zeros in memory
   auto dma_c = [&](int i, uint8_t *sc) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) dma16(rs, sc + (32 * wave + 16 * k) * 64, coff[k], uint32_t(64 * i));
+    dma16(rs, sc + (kRowsPW * wave) * 64, coff, uint32_t(64 * i));
   };
-  auto load_b = [&](int ss, uint4(&R)[2][4]) {
+  auto load_b = [&](int ss, uint4(&R)[4]) {
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-        R[jn][a4] = bload16(rw, xoff[jn], 128u * uint32_t(ss) + 8u * uint32_t(a4) * rowB);
+    for (int a4 = 0; a4 < 4; ++a4)
+      R[a4] = bload16(rw, xoff, 128u * uint32_t(ss) + 8u * uint32_t(a4) * rowB);
   };
   // scales of groups 16i + 8h + c (c = 0..7) of the lane's row; 0 past G
-  auto load_f = [&](int i, float (&F)[2][8]) {
+  auto load_f = [&](int i, float (&F)[8]) {
     const int g0 = 16 * i + 8 * h;
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn)
+    for (int f4 = 0; f4 < 2; ++f4) {
+      const int gq = g0 + 4 * f4;
+      const uint32_t o = soff + 64u * uint32_t(i) + 16u * uint32_t(f4);
+      if ((G & 3) == 0) {
+        const uint4 w = bload16(rw, gq < G ? o : kOff, 0);
+        F[4 * f4 + 0] = __uint_as_float(w.x);
+        F[4 * f4 + 1] = __uint_as_float(w.y);
+        F[4 * f4 + 2] = __uint_as_float(w.z);
+        F[4 * f4 + 3] = __uint_as_float(w.w);
+      } else {
 #pragma unroll
-      for (int f4 = 0; f4 < 2; ++f4) {
-        const int gq = g0 + 4 * f4;
-        const uint32_t o = soff[jn] + 64u * uint32_t(i) + 16u * uint32_t(f4);
-        if ((G & 3) == 0) {
-          const uint4 w = bload16(rw, gq < G ? o : kOff, 0);
-          F[jn][4 * f4 + 0] = __uint_as_float(w.x);
-          F[jn][4 * f4 + 1] = __uint_as_float(w.y);
-          F[jn][4 * f4 + 2] = __uint_as_float(w.z);
-          F[jn][4 * f4 + 3] = __uint_as_float(w.w);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            F[jn][4 * f4 + c] = bload4f(rw, gq + c < G ? o + 4u * c : kOff);
-        }
+        for (int c = 0; c < 4; ++c) F[4 * f4 + c] = bload4f(rw, gq + c < G ? o + 4u * c : kOff);
       }
+    }
   };
 
-  f32x16 acc[NMF][2];
+  f32x16 acc[NMF];
 #pragma unroll
-  for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-    for (int jn = 0; jn < 2; ++jn) acc[mf][jn] = f32x16{};
+  for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
 
   // prologue: stage 0 (activations, correction block 0), scales of block 0, weights of
-  // super-step 0
-  float F[2][8] = {};
-  // weight registers: kDepth super-steps of loads in flight (two when the
-  // registers allow: the exchange of super-step ss then waits for loads issued
-  // two super-steps earlier)
-  constexpr int kDepth = NMF <= 3 ? 2 : 1;
-  uint4 Rb[kDepth][2][4] = {};
+  // super-steps 0 and 1 (two super-steps of weight loads in flight: the exchange of
+  // super-step ss then waits for loads issued two super-steps earlier)
+  float F[8] = {};
+  uint4 Rb[2][4] = {};
   dma_a(0, g_st0);
   dma_c(0, g_sc0);
   load_f(0, F);
   load_b(0, Rb[0]);
-  if (kDepth == 2 && nss > 1) load_b(1, Rb[1]);
+  if (nss > 1) load_b(1, Rb[1]);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();
 
@@ -400,161 +387,130 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
   const uint32_t cbase = uint32_t(n * 64);
   const uint32_t cswz = uint32_t((n >> 2) & 3);
 
-  // U[jn][0..7]: the block's scales in super-step order (pairs e = 0, 1 of
+  // U[0..7]: the block's scales in super-step order (pairs e = 0, 1 of
   // super-step c at 2c, 2c + 1), rotated by two per super-step
-  float U[2][8] = {};
+  float U[8] = {};
   // one super-step: compute from (st, sc) while the DMA fills (stn, scn)
   auto super_step = [&](int ss, int par, const uint8_t *st, const uint8_t *sc, uint8_t *stn,
                         uint8_t *scn) {
     const bool more = ss + 1 < nss;
-    uint4(&R)[2][4] = Rb[kDepth == 2 ? par : 0];
+    uint4(&R)[4] = Rb[par];
     if (more && ((ss + 1) & 3) == 0) dma_c((ss + 1) >> 2, scn);
     {
       // this super-step's weights into MFMA lane order: register d of lane (h, n)
       // = part 4h + d of row n (exchange of the load index with lane bits 3, 4)
-      uint4 D[2][4];
-#pragma unroll
-      for (int jn = 0; jn < 2; ++jn) exchange_rows(R[jn], D[jn]);
-      // depth 1: the next super-step's weights go out one load per step in
-      // steps 0..7 (issued in one burst the four waves queue on the address unit)
-      const __amdgpu_buffer_rsrc_t rwn = ss + kDepth < nss ? rw : rnull;
+      uint4 D[4];
+      exchange_rows(R, D);
       if ((ss & 3) == 0) {
         // correction GEMM of block i = ss / 4: acc += S (hi, lo) x (-8 s, -8 s);
         // k-step kc, k-half h covers groups 16i + 8h + 4kc .. +3
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          f16x8 bc[2];
-#pragma unroll
-          for (int jn = 0; jn < 2; ++jn) {
-            const _Float16 h0 = _Float16(F[jn][4 * kc + 0]) * _Float16(-8.0f);
-            const _Float16 h1 = _Float16(F[jn][4 * kc + 1]) * _Float16(-8.0f);
-            const _Float16 h2 = _Float16(F[jn][4 * kc + 2]) * _Float16(-8.0f);
-            const _Float16 h3 = _Float16(F[jn][4 * kc + 3]) * _Float16(-8.0f);
-            bc[jn] = f16x8{h0, h0, h1, h1, h2, h2, h3, h3};
-          }
+          const _Float16 h0 = _Float16(F[4 * kc + 0]) * _Float16(-8.0f);
+          const _Float16 h1 = _Float16(F[4 * kc + 1]) * _Float16(-8.0f);
+          const _Float16 h2 = _Float16(F[4 * kc + 2]) * _Float16(-8.0f);
+          const _Float16 h3 = _Float16(F[4 * kc + 3]) * _Float16(-8.0f);
+          const f16x8 bc = f16x8{h0, h0, h1, h1, h2, h2, h3, h3};
 #pragma unroll
           for (int mf = 0; mf < NMF; ++mf) {
             const f16x8 a = *reinterpret_cast<const f16x8 *>(
                 sc + cbase + mf * 32 * 64 + 16 * ((uint32_t(2 * h + kc)) ^ cswz));
-#pragma unroll
-            for (int jn = 0; jn < 2; ++jn)
-              acc[mf][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bc[jn], acc[mf][jn], 0, 0, 0);
+            acc[mf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bc, acc[mf], 0, 0, 0);
           }
         }
         // regroup between lane halves: lane h then holds groups 4c + 2h, 4c + 2h + 1
+        float T[8];
 #pragma unroll
-        for (int jn = 0; jn < 2; ++jn) {
-          float T[8];
+        for (int c = 0; c < 8; ++c) T[c] = F[c];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) T[c] = F[jn][c];
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const auto p0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(T[c]), __float_as_uint(T[2 + c]), false, false);
-            const auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(T[4 + c]), __float_as_uint(T[6 + c]), false, false);
-            T[c] = __uint_as_float(uint32_t(p0[0]));
-            T[2 + c] = __uint_as_float(uint32_t(p0[1]));
-            T[4 + c] = __uint_as_float(uint32_t(p1[0]));
-            T[6 + c] = __uint_as_float(uint32_t(p1[1]));
-          }
-          // super-step order: c = 0: T0 T1, c = 1: T4 T5, c = 2: T2 T3, c = 3: T6 T7
-          U[jn][0] = T[0]; U[jn][1] = T[1]; U[jn][2] = T[4]; U[jn][3] = T[5];
-          U[jn][4] = T[2]; U[jn][5] = T[3]; U[jn][6] = T[6]; U[jn][7] = T[7];
+        for (int c = 0; c < 2; ++c) {
+          const auto p0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(T[c]), __float_as_uint(T[2 + c]), false, false);
+          const auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(T[4 + c]), __float_as_uint(T[6 + c]), false, false);
+          T[c] = __uint_as_float(uint32_t(p0[0]));
+          T[2 + c] = __uint_as_float(uint32_t(p0[1]));
+          T[4 + c] = __uint_as_float(uint32_t(p1[0]));
+          T[6 + c] = __uint_as_float(uint32_t(p1[1]));
         }
+        // super-step order: c = 0: T0 T1, c = 1: T4 T5, c = 2: T2 T3, c = 3: T6 T7
+        U[0] = T[0]; U[1] = T[1]; U[2] = T[4]; U[3] = T[5];
+        U[4] = T[2]; U[5] = T[3]; U[6] = T[6]; U[7] = T[7];
         if (ss + 4 < nss) load_f((ss >> 2) + 1, F);
       } else {
 #pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-          for (int c = 0; c < 6; ++c) U[jn][c] = U[jn][c + 2];
+        for (int c = 0; c < 6; ++c) U[c] = U[c + 2];
       }
-      // dequant constants per fragment and group half e of the super-step
-      f16x2 s2[2][2], c10[2][2], c6[2][2];
+      // dequant constants per group half e of the super-step
+      f16x2 s2[2], c10[2], c6[2];
 #pragma unroll
-      for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const _Float16 hs = _Float16(U[jn][e]);
-          s2[jn][e] = f16x2{hs, hs};
-          c10[jn][e] = s2[jn][e] * f16x2{_Float16(-1024.0f), _Float16(-1024.0f)};
-          c6[jn][e] = s2[jn][e] * f16x2{_Float16(-64.0f), _Float16(-64.0f)};
-        }
+      for (int e = 0; e < 2; ++e) {
+        const _Float16 hs = _Float16(U[e]);
+        s2[e] = f16x2{hs, hs};
+        c10[e] = s2[e] * f16x2{_Float16(-1024.0f), _Float16(-1024.0f)};
+        c6[e] = s2[e] * f16x2{_Float16(-64.0f), _Float16(-64.0f)};
+      }
       // 16 MFMA k-steps; the weights of step k + 1 are dequantised and its A
       // fragments read while the MFMAs of step k run (pinned with scheduling
       // group barriers: left alone, the scheduler sinks each A read next to its
       // first use and the LDS latency stalls every MFMA group).  The next
-      // stage's activations go out by DMA one instruction per step: issued in one
-      // burst after the barrier they would stall every wave on the address unit.
-      f16x8 a[NMF], b[2];
+      // stage's activations go out by DMA one instruction every other step: issued
+      // in one burst after the barrier they would stall every wave on the address
+      // unit.
+      f16x8 a[NMF], b;
 #pragma unroll
       for (int mf = 0; mf < NMF; ++mf)
         a[mf] = *reinterpret_cast<const f16x8 *>(st + abase + mf * 32 * kRowB + 16 * (0 ^ aswz));
-#pragma unroll
-      for (int jn = 0; jn < 2; ++jn) b[jn] = dequant(D[jn][0].x, m1, m2, s2[jn][0], c10[jn][0], c6[jn][0]);
+      b = dequant(D[0].x, m1, m2, s2[0], c10[0], c6[0]);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int k1 = k + 1;
         __builtin_amdgcn_sched_barrier(0);
-        f16x8 an[NMF], bn[2];
+        f16x8 an[NMF], bn;
         if (k < 15) {
 #pragma unroll
           for (int mf = 0; mf < NMF; ++mf)
             an[mf] = *reinterpret_cast<const f16x8 *>(st + abase + mf * 32 * kRowB +
                                                       16 * (uint32_t(k1) ^ aswz));
-#pragma unroll
-          for (int jn = 0; jn < 2; ++jn)
-            bn[jn] = dequant(word_of(D[jn][k1 >> 2], k1 & 3), m1, m2, s2[jn][k1 >> 3],
-                             c10[jn][k1 >> 3], c6[jn][k1 >> 3]);
+          bn = dequant(word_of(D[k1 >> 2], k1 & 3), m1, m2, s2[k1 >> 3], c10[k1 >> 3],
+                       c6[k1 >> 3]);
         }
 #pragma unroll
         for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-          for (int jn = 0; jn < 2; ++jn)
-            acc[mf][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mf], b[jn], acc[mf][jn], 0, 0, 0);
+          acc[mf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mf], b, acc[mf], 0, 0, 0);
         // (no branch: a branch here would split the step's scheduling region; in
         // the last super-step the instruction reads out of range and writes zeros
         // into the unused stage, landed before the epilogue by the closing wait)
-        dma16(ra, stn + (32 * wave + 2 * k) * kRowB, more ? aoff[k] : kOff, uint32_t(512 * (ss + 1)));
-        if (kDepth == 1 && k < 8)
-          R[k >> 2][k & 3] = bload16(rwn, xoff[k >> 2], 128u * uint32_t(ss + 1) + 8u * uint32_t(k & 3) * rowB);
+        if ((k & 1) == 0)
+          dma16(ra, stn + (kRowsPW * wave + k) * kRowB, more ? aoff[k >> 1] : kOff,
+                uint32_t(512 * (ss + 1)));
         if (k < 15) {
-          if (kDepth == 1 && k < 8) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM (DMA, weights)
-          else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          if ((k & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA)
           __builtin_amdgcn_sched_group_barrier(0x100, NMF, 0);  // DS reads
 #pragma unroll
-          for (int i = 0; i < 2 * NMF; ++i) {
+          for (int i = 0; i < NMF; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 20 / (2 * NMF) + 1, 0);  // VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, 10 / NMF + 1, 0);  // VALU
           }
 #pragma unroll
           for (int mf = 0; mf < NMF; ++mf) a[mf] = an[mf];
-#pragma unroll
-          for (int jn = 0; jn < 2; ++jn) b[jn] = bn[jn];
+          b = bn;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kDepth == 2) {
-      // the weights of super-step ss + 2 go out after this super-step's last DMA
-      // (empty resource past the end: the count stays 8), so the wait below can
-      // leave exactly them in flight across the barrier
-      {
-        const __amdgpu_buffer_rsrc_t rwn2 = ss + 2 < nss ? rw : rnull;
-        uint4(&R2)[2][4] = Rb[par];
+    // the weights of super-step ss + 2 go out after this super-step's last DMA
+    // (empty resource past the end: the count stays 4), so the wait below can
+    // leave exactly them in flight across the barrier
+    {
+      const __amdgpu_buffer_rsrc_t rwn2 = ss + 2 < nss ? rw : rnull;
 #pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4)
-            R2[jn][a4] = bload16(rwn2, xoff[jn], 128u * uint32_t(ss + 2) + 8u * uint32_t(a4) * rowB);
-        __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): next stage landed
-      }
-      // a plain barrier: __syncthreads() would also wait for the loads left in
-      // flight (its workgroup release waits for every memory operation);
-      // the memory clobber keeps the compiler from moving LDS accesses across
-      asm volatile("s_barrier" ::: "memory");
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next stage's DMA and weights landed
-      __syncthreads();
+      for (int a4 = 0; a4 < 4; ++a4)
+        R[a4] = bload16(rwn2, xoff, 128u * uint32_t(ss + 2) + 8u * uint32_t(a4) * rowB);
+      __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0): next stage landed
     }
+    // a plain barrier: __syncthreads() would also wait for the loads left in
+    // flight (its workgroup release waits for every memory operation);
+    // the memory clobber keeps the compiler from moving LDS accesses across
+    asm volatile("s_barrier" ::: "memory");
   };
   // pairs of super-steps with no branch inside the loop body (the compiler's
   // load-counter bookkeeping then carries across the back edge), odd tail after
@@ -564,24 +520,41 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
     super_step(ss + 1, 1, g_st1, g_sc1, g_st0, g_sc0);
   }
   if (ss < nss) super_step(ss, 0, g_st0, g_sc0, g_st1, g_sc1);
+  // the weights issued for super-steps past the end (empty resource) may still
+  // count as outstanding: nothing below reads them
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
 
-  // epilogue through an LDS tile (the stages are free: the last super-step ended
+  // epilogue through LDS tiles (the stages are free: the last super-step ended
   // with a barrier), then 16-byte stores.  tid is made opaque so that the
   // item-invariant addresses below are not hoisted to the kernel start (where
   // they would be spilled and reloaded from scratch, once per stored row).
-  // acc[mf][jn][4j + i] is row 32 mf + 8j + 4h + i, column n of fragment jn.
-  uint8_t *tile = g_st0;
+  // acc[mf][4j + i] is row 32 mf + 8j + 4h + i, column n of the wave's fragment.
   int tid = int(threadIdx.x);
   asm volatile("" : "+v"(tid));
   const int eh = (tid & 63) >> 5, en = tid & 31;
   bool range = false;  // an fp16 operand out of range: COLI_STATUS_RANGE
   if (kGateUp) {
-    // tile row m: the N-tile's 128 features of h in staged order (2 groups, 256 B).
-    // The row's activations were scaled by 2^-e: gate = 2^e acc_g, up = 2^e acc_u,
-    // and h is stored scaled by 2^-2e: SiLU(2^e acc_g) * acc_u * 2^-e.  Features
-    // past I (a ragged last group) are zeros.
-    if (wvalid) {
-      const int fl = 32 * wave + en;  // feature within the N-tile
+    // gate (half 0) -> fp32 tile [128 rows][128 features] in stage 0; the up wave
+    // of the same SIMD slot then forms h in the staged order (2 groups, 256 B per
+    // row) in stage 1.  The row's activations were scaled by 2^-e: gate = 2^e
+    // acc_g, up = 2^e acc_u, and h is stored scaled by 2^-2e: SiLU(2^e acc_g) *
+    // acc_u * 2^-e.  Features past I (a ragged last group, or a wave past the
+    // matrix) are zeros.
+    float *gtile = reinterpret_cast<float *>(g_st0);
+    uint8_t *htile = g_st1;
+    const int fl = 32 * sw + en;  // feature within the N-tile
+    if (half == 0 && wvalid) {
+#pragma unroll
+      for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = 32 * mf + 8 * (v >> 2) + 4 * eh + (v & 3);
+          gtile[m * 128 + fl] = acc[mf][v];
+        }
+    }
+    __syncthreads();
+    if (half == 1) {
       const int tpos = 2 * (64 * (fl >> 6) + grp_pos(fl & 63));
       const bool fvalid = wrow0 + en < L.I;
 #pragma unroll
@@ -590,10 +563,12 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
         for (int v = 0; v < 16; ++v) {
           const int m = 32 * mf + 8 * (v >> 2) + 4 * eh + (v & 3);
           const int fe = g_xe[m];
-          float hf = silu(ldexpf(acc[mf][0][v], fe)) * ldexpf(acc[mf][1][v], -fe);
-          hf = fvalid ? hf : 0.0f;
-          range |= !(fabsf(hf) <= 65504.0f);
-          *reinterpret_cast<_Float16 *>(tile + m * 256 + tpos) = _Float16(hf);
+          float hf = 0.0f;
+          if (fvalid) {
+            hf = silu(ldexpf(gtile[m * 128 + fl], fe)) * ldexpf(acc[mf][v], -fe);
+            range |= !(fabsf(hf) <= 65504.0f);
+          }
+          *reinterpret_cast<_Float16 *>(htile + m * 256 + tpos) = _Float16(hf);
         }
     }
     __syncthreads();
@@ -602,23 +577,23 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
       const int c = tid & 15;
       if (64 * (g0 + (c >> 3)) < L.I) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const int m = (tid >> 4) + 16 * p;
+        for (int p = 0; p < 4; ++p) {
+          const int m = (tid >> 4) + 32 * p;
           if (m < nrows) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(tile + m * 256 + 16 * c);
+            const uint4 v = *reinterpret_cast<const uint4 *>(htile + m * 256 + 16 * c);
             *reinterpret_cast<uint4 *>(pa.out + int64_t(g_outrow[m]) * pa.OP + 64 * g0 + 8 * c) = v;
           }
         }
       }
     }
     // group sums of h: thread (m, gsel) adds the 64 fp16 values of its group
-    {
+    if (tid < 2 * kMC) {
       const int m = tid & (kMC - 1), gsel = tid >> 7;
       if (m < nrows && 64 * (g0 + gsel) < L.I) {
         float sum = 0.0f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const uint4 v = *reinterpret_cast<const uint4 *>(tile + m * 256 + gsel * 128 + 16 * c);
+          const uint4 v = *reinterpret_cast<const uint4 *>(htile + m * 256 + gsel * 128 + 16 * c);
           const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
@@ -633,21 +608,18 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
   } else {
     // tile row m: the N-tile's 256 gate-scaled outputs (still scaled by the
     // token's 2^-2e; the combine undoes it); outputs past H are zeros
+    uint8_t *tile = g_st0;
     if (wvalid) {
 #pragma unroll
       for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = 32 * mf + 8 * (v >> 2) + 4 * eh + (v & 3);
-          const float gate = g_gate[m];
-#pragma unroll
-          for (int jn = 0; jn < 2; ++jn) {
-            float o = gate * acc[mf][jn][v];
-            o = wrow0 + 32 * jn + en < L.H ? o : 0.0f;
-            range |= !(fabsf(o) <= 65504.0f);
-            *reinterpret_cast<_Float16 *>(tile + m * 512 + 2 * (64 * wave + 32 * jn + en)) =
-                _Float16(o);
-          }
+          float o = g_gate[m] * acc[mf][v];
+          o = wrow0 + en < L.H ? o : 0.0f;
+          range |= !(fabsf(o) <= 65504.0f);
+          *reinterpret_cast<_Float16 *>(tile + m * 512 + 2 * (64 * sw + 32 * half + en)) =
+              _Float16(o);
         }
     }
     __syncthreads();
@@ -655,8 +627,8 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
     const int n0 = it.ntile * 256 + 8 * c;
     if (n0 < L.H) {
 #pragma unroll
-      for (int p = 0; p < 16; ++p) {
-        const int m = (tid >> 5) + 8 * p;
+      for (int p = 0; p < 8; ++p) {
+        const int m = (tid >> 5) + 16 * p;
         if (m < nrows) {
           const uint4 v = *reinterpret_cast<const uint4 *>(tile + m * 512 + 16 * c);
           *reinterpret_cast<uint4 *>(pa.out + int64_t(g_outrow[m]) * pa.OP + n0) = v;
@@ -672,7 +644,7 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
 // per XCD (the hardware deals consecutive blocks round-robin over the 8 XCDs),
 // so the N-tiles of one chunk, which share its activations, meet in one L2.
 template <bool kGateUp>
-__global__ __launch_bounds__(kThreads, 1) void pf_gemm(LayerDev L, Routing r, int T, PfArgs pa) {
+__global__ __launch_bounds__(kPThreads, 1) void pf_gemm(LayerDev L, Routing r, int T, PfArgs pa) {
   const int K = L.K;
   const int n_nt = kGateUp ? (L.I + 127) / 128 : (L.H + 255) / 256;
   const int nu = *r.n_unique + 1;
@@ -796,7 +768,7 @@ hipError_t launch_gemm(const LayerDev &L, const Routing &r, int T, const PfArgs 
                        int64_t max_items, hipStream_t s) {
   const int64_t cus = cus_of_device();
   const int64_t grid = max_items < cus ? max_items : cus;
-  pf_gemm<kGateUp><<<dim3(unsigned(grid)), dim3(kThreads), 0, s>>>(L, r, T, pa);
+  pf_gemm<kGateUp><<<dim3(unsigned(grid)), dim3(kPThreads), 0, s>>>(L, r, T, pa);
   return hipGetLastError();
 }
 
