@@ -84,6 +84,9 @@ typedef enum { COLI_SCORE_SOFTMAX = 0, COLI_SCORE_SIGMOID = 1 } coli_scoring;
                                      no finish tag (coli_expert_finish was not
                                      run on it); that expert's outputs, and so
                                      y of its tokens, are NaN */
+#define COLI_STATUS_NOT_RESIDENT 8 /* a routed expert has no slot in the
+                                     layer's slot_map (-1); its outputs, and so
+                                     y of its tokens, are NaN */
 
 #define COLI_GROUP 64           /* elements per quantisation group */
 #define COLI_MAX_EXPERTS 1024   /* upper bound for E (and K) */
@@ -211,6 +214,10 @@ typedef struct {
  *            bytes; shared: one blob of the same layout (the shared expert,
  *            applied to every token with weight 1).  Both 256-byte aligned.
  *   scoring: the router's coli_scoring (0, SOFTMAX, when left zero).
+ *   slot_map: device int32 [E] or NULL.  NULL: expert e's blob is blob e of
+ *            `experts`.  Otherwise `experts` holds cache slots and expert e's
+ *            blob is slot slot_map[e] (see coli_cache); an expert routed while
+ *            its entry is -1 gives NaN outputs and COLI_STATUS_NOT_RESIDENT.
  * H and I may be any value in [1, MAX_DIM]: a row whose length is not a
  * multiple of 64 ends in a zero-padded group (the quantiser pads it so).
  */
@@ -222,6 +229,7 @@ typedef struct {
     const uint8_t *experts;
     const uint8_t *shared;
     coli_scoring scoring;
+    const int32_t *slot_map;
 } coli_moe_layer;
 
 /*
@@ -338,6 +346,106 @@ int coli_moe_forward_timed(const coli_moe_layer *L, coli_mode mode,
                            int32_t *status, void *workspace,
                            size_t workspace_bytes, void *stream, void **events,
                            int n_events);
+
+/*
+ * The forward in two calls, so that the caller can act on the routing before
+ * the experts run: coli_moe_route does logits, top-K, gates and the batch
+ * union (and, on the single-token path, x's digit planes), leaving them in the
+ * workspace; coli_moe_experts then runs the expert FFNs and the combine from
+ * that workspace.  Between the two the caller may read the batch's expert list
+ * (unique_out, n_unique_out: optional device int32 [E] and [1], the unique
+ * routed experts in ascending id order) and place the experts (coli_cache).
+ * The pair gives the same results as coli_moe_forward when both calls take the
+ * same L, mode, x, T and workspace (untouched in between).  DECODE takes
+ * T <= 256 here.  Errors: as coli_moe_forward (ESHAPE for DECODE with
+ * T > 256).
+ */
+int coli_moe_route(const coli_moe_layer *L, coli_mode mode, const void *x, int T,
+                   int32_t *topk_idx_out, float *topk_gate_out,
+                   int32_t *unique_out, int32_t *n_unique_out, void *workspace,
+                   size_t workspace_bytes, void *stream);
+int coli_moe_experts(const coli_moe_layer *L, coli_mode mode, const void *x, int T,
+                     void *y, int32_t *topk_idx_out, float *topk_gate_out,
+                     int32_t *status, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* expert placement (page "Colibrì 深度解析", section 三; page "为什么Colibrì  */
+/* 越用越快", section 实时重固定REPIN)                                       */
+/* ---------------------------------------------------------------------- */
+
+/* 1 if an expert of heat `hot` may replace one of heat `cold`: hot > cold +
+ * cold/4 + 4, computed in 64 bits (a saturated 32-bit heat stays put). */
+int coli_tier_should_promote(uint32_t hot, uint32_t cold);
+/* LFRU score: heat * 256 + recent, recent = 255 - age if the age
+ * (clock - last, modulo 2^32) is below 255, else 0: one routing outweighs any
+ * recency. */
+uint64_t coli_tier_lfru_score(uint32_t heat, uint32_t last, uint32_t clock);
+
+/*
+ * An HBM cache of S expert blobs over host memory holding all E.  Host
+ * memory owned by the caller; the functions below read and write it only.
+ *   heat[E]      routings per expert (saturating), halved by coli_cache_decay
+ *   last[E]      the clock of the expert's last admission
+ *   slot_of[E]   the expert's slot, or -1
+ *   expert_of[S] the slot's expert, or -1
+ * 1 <= S <= E <= COLI_MAX_EXPERTS.
+ */
+typedef struct {
+    int E, S;
+    uint32_t clock;
+    uint32_t *heat;
+    uint32_t *last;
+    int32_t *slot_of;
+    int32_t *expert_of;
+} coli_cache;
+
+/* Zero the heat and clock, free every slot.  Errors: EINVAL, ESHAPE. */
+int coli_cache_init(coli_cache *c);
+/* Halve every heat (integer halving: the heat fades with time).  Errors:
+ * EINVAL, ESHAPE. */
+int coli_cache_decay(coli_cache *c);
+/*
+ * Admit the experts one batch needs (HOST ids `needed`, duplicates allowed):
+ * the clock advances by one; each needed expert's heat grows by one and its
+ * last becomes the clock; each needed expert without a slot takes a free slot
+ * (lowest index first), else the slot of the resident the batch does not need
+ * with the lowest LFRU score (ties: the lower id).  The loads to perform are
+ * written to load_expert / load_slot (HOST, room for S each), *n_loads their
+ * number, in the order the experts are first named.  Nothing changes on an
+ * error: EINVAL (NULL, an id outside [0, E)), ESHAPE (the batch needs more
+ * than S experts).
+ */
+int coli_cache_admit(coli_cache *c, const int32_t *needed, int n, int32_t *load_expert,
+                     int32_t *load_slot, int *n_loads);
+/*
+ * REPIN: rank the non-resident experts by LFRU score (highest first) and the
+ * residents (lowest first), pair them in that order and swap while the hot
+ * one may replace the cold one (coli_tier_should_promote on their heats), at
+ * most max_swaps times (the pages use 4).  Writes the swaps (HOST, room for
+ * max_swaps each): the admitted expert, its slot, the evicted expert.
+ * Errors: EINVAL, ESHAPE.
+ */
+int coli_cache_repin(coli_cache *c, int max_swaps, int32_t *load_expert, int32_t *load_slot,
+                     int32_t *evicted, int *n_swaps);
+/*
+ * Copy the planned loads: blob load_expert[i] of host_blobs (PINNED host
+ * memory, E blobs of blob_bytes) to slot load_slot[i] of `slots` (device, S
+ * blobs), asynchronously on `stream` (hipMemcpyAsync, host to device).  The
+ * ids are not checked against E and S (the caller's buffers): pass the lists
+ * coli_cache_admit / coli_cache_repin wrote.  A slot must not be overwritten
+ * while a kernel that reads it may still run: stage on the stream of the
+ * forward, or order the streams.  Errors: EINVAL (NULL, negative id), ESHAPE,
+ * EDEVICE.
+ */
+int coli_cache_stage(const uint8_t *host_blobs, uint8_t *slots, size_t blob_bytes,
+                     const int32_t *load_expert, const int32_t *load_slot, int n_loads,
+                     void *stream);
+/* Upload c->slot_of to the device slot map (int32 [E]) on `stream`, for
+ * coli_moe_layer.slot_map (hipMemcpyAsync, host to device: keep c->slot_of
+ * unchanged until the stream has passed the copy).  Errors: EINVAL, ESHAPE,
+ * EDEVICE. */
+int coli_cache_slot_map(const coli_cache *c, int32_t *slot_map, void *stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

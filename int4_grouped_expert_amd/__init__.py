@@ -43,6 +43,7 @@ COLI_F32, COLI_BF16 = 0, 1
 COLI_DECODE, COLI_PREFILL = 0, 1
 COLI_SCORE_SOFTMAX, COLI_SCORE_SIGMOID = 0, 1
 COLI_STATUS_NONFINITE, COLI_STATUS_RANGE, COLI_STATUS_UNFINISHED = 1, 2, 4
+COLI_STATUS_NOT_RESIDENT = 8
 COLI_MAX_EXPERTS = 1024
 COLI_MAX_DIM = 65536
 COLI_MAX_TOKENS = 65536
@@ -55,7 +56,9 @@ EXPORTS = [
     "coli_expert_views", "coli_expert_finish", "coli_quant_expert", "coli_moe_workspace_bytes",
     "coli_moe_forward", "coli_moe_forward_timed", "coli_moe_forward_noalloc",
     "coli_usage_count", "coli_usage_engine_hash", "coli_usage_save", "coli_usage_load",
-    "coli_rmsnorm_f32",
+    "coli_rmsnorm_f32", "coli_moe_route", "coli_moe_experts", "coli_tier_should_promote",
+    "coli_tier_lfru_score", "coli_cache_init", "coli_cache_decay", "coli_cache_admit",
+    "coli_cache_repin", "coli_cache_stage", "coli_cache_slot_map",
 ]
 
 _p = ctypes.c_void_p
@@ -71,7 +74,12 @@ class coli_q4(ctypes.Structure):
 class coli_moe_layer(ctypes.Structure):
     _fields_ = [("H", _i), ("I", _i), ("E", _i), ("K", _i), ("w_router", _p),
                 ("router_dtype", _i), ("router_bias", _p), ("experts", _p), ("shared", _p),
-                ("scoring", _i)]
+                ("scoring", _i), ("slot_map", _p)]
+
+
+class coli_cache(ctypes.Structure):
+    _fields_ = [("E", _i), ("S", _i), ("clock", ctypes.c_uint32), ("heat", _p), ("last", _p),
+                ("slot_of", _p), ("expert_of", _p)]
 
 
 def _proto(name, res, args):
@@ -102,6 +110,20 @@ _proto("coli_moe_forward_timed", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i
 _proto("coli_moe_forward_noalloc", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p,
                                         _p, _p])
 _proto("coli_rmsnorm_f32", _i, [_p, _p, _i, _i, ctypes.c_float, _p])
+_proto("coli_moe_route", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p, _p, _p,
+                              _sz, _p])
+_proto("coli_moe_experts", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p, _p, _p,
+                                _sz, _p])
+_proto("coli_tier_should_promote", _i, [ctypes.c_uint32, ctypes.c_uint32])
+_proto("coli_tier_lfru_score", ctypes.c_uint64, [ctypes.c_uint32, ctypes.c_uint32,
+                                                 ctypes.c_uint32])
+_proto("coli_cache_init", _i, [ctypes.POINTER(coli_cache)])
+_proto("coli_cache_decay", _i, [ctypes.POINTER(coli_cache)])
+_proto("coli_cache_admit", _i, [ctypes.POINTER(coli_cache), _p, _i, _p, _p,
+                                ctypes.POINTER(_i)])
+_proto("coli_cache_repin", _i, [ctypes.POINTER(coli_cache), _i, _p, _p, _p, ctypes.POINTER(_i)])
+_proto("coli_cache_stage", _i, [_p, _p, _sz, _p, _p, _i, _p])
+_proto("coli_cache_slot_map", _i, [ctypes.POINTER(coli_cache), _p, _p])
 _proto("coli_usage_count", _i, [_p, _i, _i, _i, _i, _i, _p, _p])
 _proto("coli_usage_engine_hash", ctypes.c_uint32, [ctypes.c_char_p])
 _proto("coli_usage_save", _i, [ctypes.c_char_p, _p, _i, _i, ctypes.c_uint32, ctypes.c_double, _p])
@@ -208,17 +230,20 @@ class MoELayer:
 
     experts: uint8 tensor of E * coli_expert_blob_bytes(H, I) bytes (256-B aligned),
     shared:  uint8 tensor of one blob; w_router: [E, H] fp32 or bf16; bias: [E] fp32 or None;
-    scoring: COLI_SCORE_SOFTMAX or COLI_SCORE_SIGMOID.
+    scoring: COLI_SCORE_SOFTMAX or COLI_SCORE_SIGMOID; slot_map: None, or an int32 device
+    tensor [E] mapping each expert to its blob in `experts` (then the cache slots; -1:
+    not resident).
     """
 
     def __init__(self, H, I, E, K, w_router, experts, shared, bias=None,
-                 scoring=COLI_SCORE_SOFTMAX):
+                 scoring=COLI_SCORE_SOFTMAX, slot_map=None):
         self.H, self.I, self.E, self.K = H, I, E, K
         self.w_router, self.experts, self.shared, self.bias = w_router, experts, shared, bias
-        self.scoring = scoring
+        self.scoring, self.slot_map = scoring, slot_map
         self.c = coli_moe_layer(H, I, E, K, w_router.data_ptr(), _dtype(w_router),
                                 None if bias is None else bias.data_ptr(), experts.data_ptr(),
-                                shared.data_ptr(), scoring)
+                                shared.data_ptr(), scoring,
+                                None if slot_map is None else slot_map.data_ptr())
 
     def workspace_bytes(self, T: int, mode: int) -> int:
         return int(lib.coli_moe_workspace_bytes(ctypes.byref(self.c), T, mode))
@@ -260,6 +285,28 @@ def coli_moe_forward_noalloc(layer: MoELayer, mode: int, x, y, topk_idx=None, to
     return _check(lib.coli_moe_forward_noalloc(ctypes.byref(layer.c), mode, _ptr(x), T, _ptr(y),
                                                _ptr(topk_idx), _ptr(topk_gate), _ptr(status),
                                                _stream(stream)), "coli_moe_forward_noalloc")
+
+
+def coli_moe_route(layer: MoELayer, mode: int, x, workspace, topk_idx=None, topk_gate=None,
+                   unique=None, n_unique=None, stream=None):
+    """First half of coli_moe_forward: the routing, left in `workspace`; unique / n_unique
+    (int32 device [E] / [1], optional) receive the batch's experts in ascending order."""
+    T = x.shape[0]
+    nbytes = workspace.numel() * workspace.element_size()
+    return _check(lib.coli_moe_route(ctypes.byref(layer.c), mode, _ptr(x), T, _ptr(topk_idx),
+                                     _ptr(topk_gate), _ptr(unique), _ptr(n_unique),
+                                     _ptr(workspace), nbytes, _stream(stream)), "coli_moe_route")
+
+
+def coli_moe_experts(layer: MoELayer, mode: int, x, y, workspace, topk_idx=None,
+                     topk_gate=None, stream=None, status=None):
+    """Second half: the expert FFNs and the combine from the routing in `workspace`."""
+    T = x.shape[0]
+    nbytes = workspace.numel() * workspace.element_size()
+    return _check(lib.coli_moe_experts(ctypes.byref(layer.c), mode, _ptr(x), T, _ptr(y),
+                                       _ptr(topk_idx), _ptr(topk_gate), _ptr(status),
+                                       _ptr(workspace), nbytes, _stream(stream)),
+                  "coli_moe_experts")
 
 
 def coli_rmsnorm_f32(x, y, eps=1e-6, stream=None):
@@ -304,6 +351,75 @@ def coli_usage_load(path: str, n_layers: int, n_experts: int, engine_hash: int, 
                                None if d is None else d.ctypes.data_as(_p), ctypes.byref(tot)),
            "coli_usage_load")
     return c, int(tot.value)
+
+
+# ---------------------------------------------------------------- expert placement
+
+def coli_tier_should_promote(hot: int, cold: int) -> bool:
+    return bool(lib.coli_tier_should_promote(hot, cold))
+
+
+def coli_tier_lfru_score(heat: int, last: int, clock: int) -> int:
+    return int(lib.coli_tier_lfru_score(heat, last, clock))
+
+
+class Cache:
+    """The C coli_cache over numpy arrays it owns (E experts, S slots)."""
+
+    def __init__(self, E: int, S: int):
+        import numpy as np
+        self.heat = np.zeros(E, dtype=np.uint32)
+        self.last = np.zeros(E, dtype=np.uint32)
+        self.slot_of = np.full(E, -1, dtype=np.int32)
+        self.expert_of = np.full(max(S, 0), -1, dtype=np.int32)
+        self.c = coli_cache(E, S, 0, self.heat.ctypes.data, self.last.ctypes.data,
+                            self.slot_of.ctypes.data, self.expert_of.ctypes.data)
+        self._buf = [np.zeros(max(S, 1), dtype=np.int32) for _ in range(3)]
+        _check(lib.coli_cache_init(ctypes.byref(self.c)), "coli_cache_init")
+
+    @property
+    def clock(self) -> int:
+        return int(self.c.clock)
+
+    def decay(self):
+        _check(lib.coli_cache_decay(ctypes.byref(self.c)), "coli_cache_decay")
+
+    def admit(self, needed) -> list:
+        """-> [(expert, slot)] loads (coli_cache_admit)."""
+        import numpy as np
+        nd = np.ascontiguousarray(needed, dtype=np.int32)
+        le, ls = self._buf[0], self._buf[1]
+        n = _i(0)
+        _check(lib.coli_cache_admit(ctypes.byref(self.c), nd.ctypes.data if nd.size else None,
+                                    int(nd.size), le.ctypes.data, ls.ctypes.data,
+                                    ctypes.byref(n)), "coli_cache_admit")
+        return [(int(le[i]), int(ls[i])) for i in range(n.value)]
+
+    def repin(self, max_swaps: int = 4) -> list:
+        """-> [(admitted expert, slot, evicted expert)] (coli_cache_repin)."""
+        import numpy as np
+        bufs = [np.zeros(max(max_swaps, 1), dtype=np.int32) for _ in range(3)]
+        n = _i(0)
+        _check(lib.coli_cache_repin(ctypes.byref(self.c), max_swaps, bufs[0].ctypes.data,
+                                    bufs[1].ctypes.data, bufs[2].ctypes.data, ctypes.byref(n)),
+               "coli_cache_repin")
+        return [(int(bufs[0][i]), int(bufs[1][i]), int(bufs[2][i])) for i in range(n.value)]
+
+    def slot_map(self, slot_map, stream=None):
+        """Upload slot_of to an int32 device tensor [E] (coli_cache_slot_map)."""
+        _check(lib.coli_cache_slot_map(ctypes.byref(self.c), _ptr(slot_map), _stream(stream)),
+               "coli_cache_slot_map")
+
+
+def coli_cache_stage(host_blobs, slots, blob_bytes: int, loads, stream=None):
+    """Copy blobs of pinned host uint8 tensor host_blobs to device slots: loads =
+    [(expert, slot), ...] (coli_cache_stage)."""
+    import numpy as np
+    le = np.ascontiguousarray([e for e, _ in loads] or [0], dtype=np.int32)
+    ls = np.ascontiguousarray([s for _, s in loads] or [0], dtype=np.int32)
+    return _check(lib.coli_cache_stage(_ptr(host_blobs), _ptr(slots), blob_bytes,
+                                       le.ctypes.data, ls.ctypes.data, len(loads),
+                                       _stream(stream)), "coli_cache_stage")
 
 
 # ---------------------------------------------------------------- layer assembly

@@ -316,7 +316,7 @@ int forward_checks(const coli_moe_layer *L, coli_mode mode, const void *x, int T
       !aligned(L->w_router, L->router_dtype == COLI_BF16 ? 2 : 4) ||
       !aligned(L->experts, 256) || !aligned(L->shared, 256) ||
       (L->router_bias && !aligned(L->router_bias, 4)) ||
-      (topk_idx_out && !aligned(topk_idx_out, 4)) ||
+      (L->slot_map && !aligned(L->slot_map, 4)) || (topk_idx_out && !aligned(topk_idx_out, 4)) ||
       (topk_gate_out && !aligned(topk_gate_out, 4)) || (status && !aligned(status, 4)))
     return COLI_EALIGN;
   const int tl = mode == COLI_DECODE ? decode_chunk_t(T) : T;
@@ -324,17 +324,8 @@ int forward_checks(const coli_moe_layer *L, coli_mode mode, const void *x, int T
   return COLI_OK;
 }
 
-// One forward of T tokens (DECODE: T <= COLI_MAX_DECODE_T) with every
-// argument already checked.
-int forward_launch(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
-                   int32_t *topk_idx_out, float *topk_gate_out, int32_t *status, uint8_t *ws,
-                   const WsLayout &w, hipStream_t s, hipEvent_t *ev) {
-  Routing r = carve(ws, w);
-  if (topk_idx_out) r.idx = topk_idx_out;
-  if (topk_gate_out) r.gates = topk_gate_out;
-  const bool sig = L->scoring == COLI_SCORE_SIGMOID;
-  r.sc = Scoring{sig ? 1 : 0, sig ? L->router_bias : nullptr};
-  const float *lbias = sig ? nullptr : L->router_bias;  // the bias added to the logits
+// The device view of a layer for one call.
+LayerDev layer_dev(const coli_moe_layer *L, int32_t *status, const Scoring &sc) {
   LayerDev d;
   d.H = L->H;
   d.I = L->I;
@@ -345,54 +336,86 @@ int forward_launch(const coli_moe_layer *L, coli_mode mode, const void *x, int T
   d.lay = blob_layout(L->H, L->I);
   d.tag = finish_tag(L->H, L->I);
   d.status = status;
-  d.sc = r.sc;
-  const int wbf = L->router_dtype == COLI_BF16;
+  d.sc = sc;
+  d.slot_map = L->slot_map;
+  return d;
+}
 
+// Buffers of one call inside the workspace.
+struct CallBufs {
+  Routing r;
+  NarrowBufs nb;
+  BatchBufs bb;
+  PrefillBufs pb;
+};
+CallBufs carve_call(const coli_moe_layer *L, uint8_t *ws, const WsLayout &w,
+                    int32_t *topk_idx_out, float *topk_gate_out) {
+  CallBufs c;
+  c.r = carve(ws, w);
+  if (topk_idx_out) c.r.idx = topk_idx_out;
+  if (topk_gate_out) c.r.gates = topk_gate_out;
+  const bool sig = L->scoring == COLI_SCORE_SIGMOID;
+  c.r.sc = Scoring{sig ? 1 : 0, sig ? L->router_bias : nullptr};
+  c.nb.xdig = reinterpret_cast<int8_t *>(ws + w.xdig);
+  c.nb.xcorr = reinterpret_cast<int32_t *>(ws + w.xcorr);
+  c.nb.xsc = reinterpret_cast<float *>(ws + w.nxsc);
+  c.nb.hn = reinterpret_cast<float *>(ws + w.hn);
+  c.bb.xp = reinterpret_cast<uint16_t *>(ws + w.bxp);
+  c.bb.xs = reinterpret_cast<float *>(ws + w.bxs);
+  c.bb.hf = reinterpret_cast<float *>(ws + w.bhf);
+  c.bb.h16 = reinterpret_cast<uint16_t *>(ws + w.bh16);
+  c.bb.hs = reinterpret_cast<float *>(ws + w.bhs);
+  c.bb.slot = reinterpret_cast<float *>(ws + w.bslot);
+  c.pb.xp = reinterpret_cast<uint16_t *>(ws + w.xp);
+  c.pb.sx = reinterpret_cast<uint16_t *>(ws + w.sx);
+  c.pb.h = reinterpret_cast<uint16_t *>(ws + w.h);
+  c.pb.sh = reinterpret_cast<uint16_t *>(ws + w.sh);
+  c.pb.slot = reinterpret_cast<uint16_t *>(ws + w.slot);
+  c.pb.xe = reinterpret_cast<int *>(ws + w.xe);
+  return c;
+}
+
+// The route part: logits, top-K, gates, the batch union (DECODE: T <= 256).
+// fused_topk: the single-token path leaves the top-K to its gate/up kernel.
+int route_launch(const coli_moe_layer *L, coli_mode mode, const void *x, int T,
+                 const CallBufs &c, const LayerDev &d, hipStream_t s, hipEvent_t *ev,
+                 bool fused_topk) {
+  const Routing &r = c.r;
+  const int wbf = L->router_dtype == COLI_BF16;
+  const float *lbias = r.sc.sigmoid ? nullptr : L->router_bias;  // bias added to the logits
   hipError_t e;
-  if (mode == COLI_PREFILL && ev) (void)hipEventRecord(ev[0], s);
   if (mode == COLI_DECODE) {
     if (narrow_supported(d, T)) {
-      NarrowBufs nb;
-      nb.xdig = reinterpret_cast<int8_t *>(ws + w.xdig);
-      nb.xcorr = reinterpret_cast<int32_t *>(ws + w.xcorr);
-      nb.xsc = reinterpret_cast<float *>(ws + w.nxsc);
-      nb.hn = reinterpret_cast<float *>(ws + w.hn);
       // one kernel per stage: the events are stamped by the launches
       e = launch_router_narrow(reinterpret_cast<const float *>(x), T, L->H, L->w_router, wbf,
-                               L->E, lbias, r.logits, nb, s, ev ? ev[0] : nullptr,
+                               L->E, lbias, r.logits, c.nb, s, ev ? ev[0] : nullptr,
                                ev ? ev[1] : nullptr);
       if (e != hipSuccess) return COLI_EDEVICE;
-      return dev_status(launch_ffn_narrow(d, nb, r.logits, r.idx, r.gates,
-                                          reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr));
+      if (fused_topk) return COLI_OK;
+      // two-phase: the top-K and the union now, for the caller to read
+      return dev_status(launch_topk_permute(r, T, L->E, L->K, 1, s));
     }
-    BatchBufs bb;
-    bb.xp = reinterpret_cast<uint16_t *>(ws + w.bxp);
-    bb.xs = reinterpret_cast<float *>(ws + w.bxs);
-    bb.hf = reinterpret_cast<float *>(ws + w.bhf);
-    bb.h16 = reinterpret_cast<uint16_t *>(ws + w.bh16);
-    bb.hs = reinterpret_cast<float *>(ws + w.bhs);
-    bb.slot = reinterpret_cast<float *>(ws + w.bslot);
     if (ev) (void)hipEventRecord(ev[0], s);
     // the vector router launch also writes x's staged rows for the batch GEMM
-    const bool vec = router_vec_ok(x, 0, L->H, L->w_router, wbf);
-    e = vec ? launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, lbias, r.logits, s,
-                                   bb.xp, bb.xs, prefill_layout(L->H, L->I).HP)
-            : launch_router_any(x, 0, T, L->H, L->w_router, wbf, L->E, lbias, r.logits, s);
+    if (router_vec_ok(x, 0, L->H, L->w_router, wbf))
+      e = launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, lbias, r.logits, s, c.bb.xp,
+                               c.bb.xs, prefill_layout(L->H, L->I).HP);
+    else
+      e = launch_router_any(x, 0, T, L->H, L->w_router, wbf, L->E, lbias, r.logits, s);
     if (e != hipSuccess) return COLI_EDEVICE;
     e = launch_route_decode(r, T, L->E, L->K, s);
     if (e != hipSuccess) return COLI_EDEVICE;
     if (ev) (void)hipEventRecord(ev[1], s);
-    e = launch_ffn_batch(d, reinterpret_cast<const float *>(x), T, r, bb,
-                         reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr, vec);
-    return dev_status(e);
+    return COLI_OK;
   }
+  if (ev) (void)hipEventRecord(ev[0], s);
   if (wbf && L->H % 32 == 0 && router_vec_ok(x, 1, L->H, L->w_router, 1)) {
     // the staged-x region is free until the activation conversion: it holds the
     // router's K-split partial sums
     const PrefillLayout pl = prefill_layout(L->H, L->I);
     e = launch_router_mfma(reinterpret_cast<const uint16_t *>(x), T, L->H,
                            reinterpret_cast<const uint16_t *>(L->w_router), L->E, lbias,
-                           r.logits, reinterpret_cast<float *>(ws + w.xp),
+                           r.logits, reinterpret_cast<float *>(c.pb.xp),
                            size_t(T) * pl.HP * 2, s);
   } else if (router_vec_ok(x, 1, L->H, L->w_router, wbf)) {
     e = launch_router_logits(x, 1, T, L->H, L->w_router, wbf, L->E, lbias, r.logits, s);
@@ -403,16 +426,40 @@ int forward_launch(const coli_moe_layer *L, coli_mode mode, const void *x, int T
   e = launch_topk_permute(r, T, L->E, L->K, 1, s);
   if (e != hipSuccess) return COLI_EDEVICE;
   if (ev) (void)hipEventRecord(ev[1], s);
-  PrefillBufs pb;
-  pb.xp = reinterpret_cast<uint16_t *>(ws + w.xp);
-  pb.sx = reinterpret_cast<uint16_t *>(ws + w.sx);
-  pb.h = reinterpret_cast<uint16_t *>(ws + w.h);
-  pb.sh = reinterpret_cast<uint16_t *>(ws + w.sh);
-  pb.slot = reinterpret_cast<uint16_t *>(ws + w.slot);
-  pb.xe = reinterpret_cast<int *>(ws + w.xe);
-  e = launch_ffn_prefill(d, reinterpret_cast<const uint16_t *>(x), T, r, pb,
-                         reinterpret_cast<uint16_t *>(y), s, ev ? ev + 2 : nullptr);
-  return dev_status(e);
+  return COLI_OK;
+}
+
+// The experts part: the FFNs and the combine from the routing in the workspace.
+int experts_launch(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
+                   const CallBufs &c, const LayerDev &d, hipStream_t s, hipEvent_t *ev,
+                   bool pre_routed) {
+  const Routing &r = c.r;
+  if (mode == COLI_DECODE) {
+    if (narrow_supported(d, T))
+      return dev_status(launch_ffn_narrow(d, c.nb, r.logits, r.idx, r.gates,
+                                          reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr,
+                                          pre_routed));
+    // the vector router staged x's rows in the route part
+    const bool staged = router_vec_ok(x, 0, L->H, L->w_router, L->router_dtype == COLI_BF16);
+    return dev_status(launch_ffn_batch(d, reinterpret_cast<const float *>(x), T, r, c.bb,
+                                       reinterpret_cast<float *>(y), s, ev ? ev + 2 : nullptr,
+                                       staged));
+  }
+  return dev_status(launch_ffn_prefill(d, reinterpret_cast<const uint16_t *>(x), T, r, c.pb,
+                                       reinterpret_cast<uint16_t *>(y), s,
+                                       ev ? ev + 2 : nullptr));
+}
+
+// One forward of T tokens (DECODE: T <= COLI_MAX_DECODE_T) with every
+// argument already checked.
+int forward_launch(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
+                   int32_t *topk_idx_out, float *topk_gate_out, int32_t *status, uint8_t *ws,
+                   const WsLayout &w, hipStream_t s, hipEvent_t *ev) {
+  const CallBufs c = carve_call(L, ws, w, topk_idx_out, topk_gate_out);
+  const LayerDev d = layer_dev(L, status, c.r.sc);
+  const int rc = route_launch(L, mode, x, T, c, d, s, ev, true);
+  if (rc != COLI_OK) return rc;
+  return experts_launch(L, mode, x, T, y, c, d, s, ev, false);
 }
 
 }  // namespace
@@ -480,6 +527,62 @@ int coli_moe_forward_timed(const coli_moe_layer *L, coli_mode mode, const void *
   if (mode == COLI_DECODE && T > COLI_MAX_DECODE_T) return COLI_ESHAPE;
   return moe_forward_impl(L, mode, x, T, y, topk_idx_out, topk_gate_out, status, workspace,
                           workspace_bytes, stream, reinterpret_cast<hipEvent_t *>(events));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks, workspace and carve-up shared by the two-phase entry points.
+int two_phase_setup(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
+                    int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
+                    void *workspace, size_t workspace_bytes, WsLayout *w) {
+  const int rc = forward_checks(L, mode, x, T, y, topk_idx_out, topk_gate_out, status, w);
+  if (rc != COLI_OK) return rc;
+  if (mode == COLI_DECODE && T > COLI_MAX_DECODE_T) return COLI_ESHAPE;
+  if (!workspace || workspace_bytes < w->total) return COLI_EWORKSPACE;
+  if (!aligned(workspace, 256)) return COLI_EALIGN;
+  return COLI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int coli_moe_route(const coli_moe_layer *L, coli_mode mode, const void *x, int T,
+                   int32_t *topk_idx_out, float *topk_gate_out, int32_t *unique_out,
+                   int32_t *n_unique_out, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+  WsLayout w;
+  // y is not written by this call: the checks take x in its place
+  int rc = two_phase_setup(L, mode, x, T, const_cast<void *>(x), topk_idx_out, topk_gate_out,
+                           nullptr, workspace, workspace_bytes, &w);
+  if (rc != COLI_OK) return rc;
+  if (!aligned(unique_out, 4) || !aligned(n_unique_out, 4)) return COLI_EALIGN;
+  if (T == 0) return COLI_OK;
+  hipStream_t s = as_stream(stream);
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  const CallBufs c = carve_call(L, ws, w, topk_idx_out, topk_gate_out);
+  const LayerDev d = layer_dev(L, nullptr, c.r.sc);
+  rc = route_launch(L, mode, x, T, c, d, s, nullptr, false);
+  if (rc != COLI_OK) return rc;
+  if (unique_out || n_unique_out)
+    return dev_status(launch_copy_union(c.r, L->E, unique_out, n_unique_out, s));
+  return COLI_OK;
+}
+
+int coli_moe_experts(const coli_moe_layer *L, coli_mode mode, const void *x, int T, void *y,
+                     int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  WsLayout w;
+  const int rc = two_phase_setup(L, mode, x, T, y, topk_idx_out, topk_gate_out, status,
+                                 workspace, workspace_bytes, &w);
+  if (rc != COLI_OK) return rc;
+  if (T == 0) return COLI_OK;
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  const CallBufs c = carve_call(L, ws, w, topk_idx_out, topk_gate_out);
+  const LayerDev d = layer_dev(L, status, c.r.sc);
+  return experts_launch(L, mode, x, T, y, c, d, as_stream(stream), nullptr, true);
 }
 
 int coli_rmsnorm_f32(const float *x, float *y, int T, int H, float eps, void *stream) {

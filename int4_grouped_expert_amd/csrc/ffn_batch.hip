@@ -387,9 +387,14 @@ __global__ __launch_bounds__(kThreads, 2) void dec_gemm(LayerDev L, Routing r, i
     // a blob without the finish tag has no valid scale copies: its outputs
     // become NaN and the status flag says why
     const uint4 tg = *reinterpret_cast<const uint4 *>(it.blob + L.lay.tag);
-    const bool bad = tg.x != L.tag.x || tg.y != L.tag.y || tg.z != L.tag.z || tg.w != L.tag.w;
-    if (bad && threadIdx.x == 0) raise_status(L.status, COLI_STATUS_UNFINISHED);
-    const float poison = bad ? __builtin_nanf("") : 1.0f;
+    const bool untagged =
+        tg.x != L.tag.x || tg.y != L.tag.y || tg.z != L.tag.z || tg.w != L.tag.w;
+    const bool missing = __builtin_amdgcn_readfirstlane(int(it.missing)) != 0;
+    if (threadIdx.x == 0) {
+      if (untagged && !missing) raise_status(L.status, COLI_STATUS_UNFINISHED);
+      if (missing) raise_status(L.status, COLI_STATUS_NOT_RESIDENT);
+    }
+    const float poison = (untagged || missing) ? __builtin_nanf("") : 1.0f;
     if (small)
       run_item_dec<kGateUp, true>(L, da, it, poison);
     else

@@ -155,7 +155,7 @@ constexpr int kGateupItems = COLI_NARROW_MAX_K + 1;  // one per unit
 template <int NC>
 __global__ __launch_bounds__(kW * 8) __attribute__((amdgpu_waves_per_eu(2)))
 void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
-                   int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
+                   int32_t *__restrict__ idx_out, float *__restrict__ gate_out, int pre_routed) {
   __shared__ int32_t sidx[COLI_NARROW_MAX_K];
   __shared__ float sgate[COLI_NARROW_MAX_K];
   __shared__ float red[kGateupItems][kGateupMaxWaves][2][8];
@@ -205,7 +205,8 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   // expert sidx[v - 1]), rows 8 rb .. 8 rb + 7 of I
   auto ptrs = [&](int it) {
     const int v = it / nrb, rb = it - v * nrb;
-    const uint8_t *blob = v > 0 ? L.experts + size_t(sidx[v - 1]) * L.lay.bytes : L.shared;
+    bool miss = false;
+    const uint8_t *blob = v > 0 ? expert_blob(L, sidx[v - 1], miss) : L.shared;
     const size_t row = size_t(rb) * 8 + r;
     Ptrs p;
     p.wg = blob + L.lay.gq + (row * GH + goff) * 32 + 16 * (q % 2);
@@ -218,7 +219,7 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   // the token's logits first: the top-K below then waits for them alone, not
   // for the weight loads issued after them
   float lg[4];
-  if (wave == 0) topk_load<4>(logits, E, lane, lg);
+  if (wave == 0 && !pre_routed) topk_load<4>(logits, E, lane, lg);
   uint4 rw[2][NC];
   float4 scg, scu;
   int it = blockIdx.x;
@@ -233,9 +234,17 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   }
   // The first item is the shared expert's (the grid is I / 8 blocks), so its
   // loads are in flight while wave 0 picks the token's experts.
-  if (wave == 0) topk_select<4>(lg, E, K, lane, sidx, sgate, L.sc);
+  if (pre_routed) {
+    // the token's top-K was selected beforehand (two-phase forward)
+    if (int(threadIdx.x) < K) {
+      sidx[threadIdx.x] = idx_out[threadIdx.x];
+      sgate[threadIdx.x] = gate_out[threadIdx.x];
+    }
+  } else if (wave == 0) {
+    topk_select<4>(lg, E, K, lane, sidx, sgate, L.sc);
+  }
   lds_barrier();
-  if (blockIdx.x == 0 && int(threadIdx.x) < K) {
+  if (!pre_routed && blockIdx.x == 0 && int(threadIdx.x) < K) {
     idx_out[threadIdx.x] = sidx[threadIdx.x];
     gate_out[threadIdx.x] = sgate[threadIdx.x];
   }
@@ -297,10 +306,13 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     const float gw = v > 0 ? sgate[v - 1] : 1.0f;
     // a blob without the finish tag has no valid blocked scales: its h' rows
     // become NaN (and so does y) and the status flag says why
-    const uint8_t *blob = v > 0 ? L.experts + size_t(sidx[v - 1]) * L.lay.bytes : L.shared;
+    bool miss = false;
+    const uint8_t *blob = v > 0 ? expert_blob(L, sidx[v - 1], miss) : L.shared;
     const uint4 tg = *reinterpret_cast<const uint4 *>(blob + L.lay.tag);
-    const bool bad = tg.x != L.tag.x || tg.y != L.tag.y || tg.z != L.tag.z || tg.w != L.tag.w;
-    if (bad && rr == 0) raise_status(L.status, COLI_STATUS_UNFINISHED);
+    const bool untagged = tg.x != L.tag.x || tg.y != L.tag.y || tg.z != L.tag.z || tg.w != L.tag.w;
+    const bool bad = untagged || miss;
+    if (rr == 0 && untagged && !miss) raise_status(L.status, COLI_STATUS_UNFINISHED);
+    if (rr == 0 && miss) raise_status(L.status, COLI_STATUS_NOT_RESIDENT);
     nb.hn[size_t(u) * I + rb * 8 + rr] =
         bad ? __builtin_nanf("") : gw * silu(g * xs) * (up * xs);
   }
@@ -335,8 +347,12 @@ __global__ __launch_bounds__(kW * kDownMaxWaves) void down_narrow(NarrowBufs nb,
   const int r = n % 8, kap = n / 8;
   const uint8_t *blob[NU];
 #pragma unroll
-  for (int u = 0; u < NU; ++u)
-    blob[u] = u < K ? L.experts + size_t(idx[u]) * L.lay.bytes : L.shared;
+  for (int u = 0; u < NU; ++u) {
+    // an expert without a slot reads the shared blob in its place; its h' rows
+    // are NaN already (the gate/up kernel poisoned them)
+    bool miss = false;
+    blob[u] = u < K ? expert_blob(L, idx[u], miss) : L.shared;
+  }
 
   // weights: the B lane's group (4 wave + 2 kappa + q / 2); scale: the result
   // lane's slot (group 4 wave + q), from the 8-row blocked copy, where a
@@ -518,7 +534,7 @@ bool narrow_supported(const LayerDev &L, int T) {
 
 hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const float *logits,
                              int32_t *idx, float *gates, float *y, hipStream_t s,
-                             hipEvent_t *ev) {
+                             hipEvent_t *ev, bool pre_routed) {
   const int cus = cu_count();
   int nc = 0;
   const int gw = gateup_waves(L.H, &nc);
@@ -530,7 +546,7 @@ hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const floa
 #define COLI_GU(NC)                                                                      \
   case NC:                                                                               \
     hipExtLaunchKernelGGL(gateup_narrow<NC>, dim3(ggrid), dim3(gw * kW), 0, s, e0, e1, 0, nb, L, \
-                          logits, idx, gates);                                           \
+                          logits, idx, gates, int(pre_routed));                          \
     break;
   switch (nc) {
     COLI_GU(1) COLI_GU(2) COLI_GU(3) COLI_GU(4) COLI_GU(5) COLI_GU(6)

@@ -269,7 +269,7 @@ constexpr int kDmaPW = kRowsPW / 2;     // DMA instructions per wave per stage (
 // One work item.  NMF = number of 32-row M fragments the chunk needs (1..4).
 template <bool kGateUp, int NMF>
 __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L, const PfArgs &pa,
-                                                               const Item &it) {
+                                                               const Item &it, float poison) {
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
   const int sw = wave & 3, half = wave >> 2;  // SIMD slot, fragment of the pair
@@ -567,6 +567,7 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
           if (fvalid) {
             hf = silu(ldexpf(gtile[m * 128 + fl], fe)) * ldexpf(acc[mf][v], -fe);
             range |= !(fabsf(hf) <= 65504.0f);
+            hf *= poison;
           }
           *reinterpret_cast<_Float16 *>(htile + m * 256 + tpos) = _Float16(hf);
         }
@@ -617,7 +618,7 @@ __device__ __attribute__((always_inline)) inline void run_item(const LayerDev &L
           const int m = 32 * mf + 8 * (v >> 2) + 4 * eh + (v & 3);
           float o = g_gate[m] * acc[mf][v];
           o = wrow0 + en < L.H ? o : 0.0f;
-          range |= !(fabsf(o) <= 65504.0f);
+          range |= fabsf(o) > 65504.0f;  // (NaN h of a poisoned expert is not a range fault)
           *reinterpret_cast<_Float16 *>(tile + m * 512 + 2 * (64 * sw + 32 * half + en)) =
               _Float16(o);
         }
@@ -702,11 +703,15 @@ __global__ __launch_bounds__(kPThreads, 1) void pf_gemm(LayerDev L, Routing r, i
     }
     __syncthreads();
     const int nmf = (it.je - it.jb + 31) / 32;
+    // a routed expert without a slot: its h (and so its outputs) become NaN
+    const bool missing = __builtin_amdgcn_readfirstlane(int(it.missing)) != 0;
+    if (missing && kGateUp && threadIdx.x == 0) raise_status(L.status, COLI_STATUS_NOT_RESIDENT);
+    const float poison = missing ? __builtin_nanf("") : 1.0f;
     switch (nmf) {
-      case 1: run_item<kGateUp, 1>(L, pa, it); break;
-      case 2: run_item<kGateUp, 2>(L, pa, it); break;
-      case 3: run_item<kGateUp, 3>(L, pa, it); break;
-      default: run_item<kGateUp, 4>(L, pa, it); break;
+      case 1: run_item<kGateUp, 1>(L, pa, it, poison); break;
+      case 2: run_item<kGateUp, 2>(L, pa, it, poison); break;
+      case 3: run_item<kGateUp, 3>(L, pa, it, poison); break;
+      default: run_item<kGateUp, 4>(L, pa, it, poison); break;
     }
   }
 }

@@ -40,6 +40,7 @@ __device__ inline int grp_pos(int e) {
 struct Item {
   int unit, mchunk, ntile;
   bool shared;
+  bool missing;  // a routed expert with no slot in the layer's slot map
   const uint8_t *blob;
   int jb, je;  // token rows of the chunk: j in [jb, je)
 };
@@ -57,9 +58,12 @@ __device__ inline void decode_item(const LayerDev &L, const Routing &r, int T, i
   it.mchunk = c - r.chunk[lo];
   it.shared = lo == nu - 1;
   int jb0, je0;
+  it.missing = false;
   if (!it.shared) {
     const int e = r.unique[lo];
-    it.blob = L.experts + size_t(e) * L.lay.bytes;
+    bool miss;
+    it.blob = expert_blob(L, e, miss);
+    it.missing = miss;
     jb0 = r.offsets[e];
     je0 = r.offsets[e + 1];
   } else {

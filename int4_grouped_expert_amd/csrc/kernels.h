@@ -112,7 +112,17 @@ struct LayerDev {
   uint4 tag;        // finish_tag(H, I)
   int32_t *status;  // optional device flag: COLI_STATUS_* bits OR-ed in
   Scoring sc;       // router scoring (the fused single-token top-K)
+  const int32_t *slot_map;  // expert -> cache slot of `experts`, or NULL (identity)
 };
+
+// Blob of routed expert e.  With a slot map, e's blob is its slot; an expert
+// without a slot sets `missing` and gets the shared blob's address in its place
+// (valid memory to read), and its outputs are to be poisoned by the caller.
+__device__ inline const uint8_t *expert_blob(const LayerDev &L, int e, bool &missing) {
+  const int s = L.slot_map ? L.slot_map[e] : e;
+  missing = s < 0;
+  return s < 0 ? L.shared : L.experts + size_t(s) * L.lay.bytes;
+}
 
 // Device side of the status flag: OR bits into *status (if any) from one lane.
 __device__ inline void raise_status(int32_t *status, int bits) {
@@ -169,6 +179,10 @@ hipError_t launch_topk_permute(const Routing &r, int T, int E, int K,
 // T <= COLI_MAX_DECODE_T.
 hipError_t launch_route_decode(const Routing &r, int T, int E, int K, hipStream_t s);
 size_t permute_chunk_ints(int T, int K, int E);
+// Copy the batch union (r.unique [E], r.n_unique) to caller buffers (either
+// may be NULL).
+hipError_t launch_copy_union(const Routing &r, int E, int32_t *unique, int32_t *n_unique,
+                             hipStream_t s);
 // Single-token decode router: logits [T, E] and x as digit planes (nb.xdig,
 // nb.xcorr, nb.xsc).  Requires H % 256 == 0, T <= 4.
 // start/stop: optional events stamped at the kernel's start and end.
@@ -183,9 +197,11 @@ bool narrow_supported(const LayerDev &L, int T);
 // Top-K of the token (from logits; idx/gates written), gate/up -> nb.hn, down
 // -> y.  ev: optional (NULL or 4: start and stop of the gate/up kernel, of the
 // down kernel, stamped by the kernel launches themselves).
+// pre_routed: idx/gates already hold the token's top-K (the gate/up kernel then
+// reads them instead of selecting).
 hipError_t launch_ffn_narrow(const LayerDev &L, const NarrowBufs &nb, const float *logits,
                              int32_t *idx, float *gates, float *y, hipStream_t s,
-                             hipEvent_t *ev);
+                             hipEvent_t *ev, bool pre_routed = false);
 
 // ---- ffn_prefill.hip ----------------------------------------------------
 // Row strides (elements) of the prefill activation buffers: staged x and h

@@ -737,7 +737,21 @@ __global__ __launch_bounds__(256) void permute_place(Routing r, int T, int K, in
 // One block does the whole permute up to this many pairs.
 constexpr int kSmallP = 2048;
 
+__global__ __launch_bounds__(256) void copy_union(Routing r, int E, int32_t *__restrict__ unique,
+                                                  int32_t *__restrict__ n_unique) {
+  const int n = *r.n_unique;
+  if (n_unique && threadIdx.x == 0) *n_unique = n;
+  if (unique)
+    for (int i = threadIdx.x; i < E; i += blockDim.x) unique[i] = i < n ? r.unique[i] : -1;
+}
+
 }  // namespace
+
+hipError_t launch_copy_union(const Routing &r, int E, int32_t *unique, int32_t *n_unique,
+                             hipStream_t s) {
+  copy_union<<<1, 256, 0, s>>>(r, E, unique, n_unique);
+  return hipGetLastError();
+}
 
 size_t permute_chunk_ints(int T, int K, int E) {
   const int64_t P = int64_t(T) * K;

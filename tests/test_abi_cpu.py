@@ -183,6 +183,34 @@ def test_forward_rejects_before_launch():
     assert call(layer=badt) == coli.COLI_EDTYPE
 
 
+def test_two_phase_rejects_before_launch():
+    L = coli.lib
+    a = P(1 << 20)
+    lay = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22)
+    need = L.coli_moe_workspace_bytes(ctypes.byref(lay), 8, coli.COLI_DECODE)
+
+    def route(layer=lay, mode=coli.COLI_DECODE, x=a, T=8, ws=a, nb=need, u=None):
+        return L.coli_moe_route(ctypes.byref(layer), mode, x, T, None, None, u, None, ws, nb,
+                                None)
+
+    def experts(layer=lay, mode=coli.COLI_DECODE, x=a, T=8, y=a, ws=a, nb=need):
+        return L.coli_moe_experts(ctypes.byref(layer), mode, x, T, y, None, None, None, ws, nb,
+                                  None)
+    for f in (route, experts):
+        assert f(x=None) == coli.COLI_EINVAL
+        assert f(mode=7) == coli.COLI_EINVAL
+        assert f(ws=None) == coli.COLI_EWORKSPACE
+        assert f(nb=need - 1) == coli.COLI_EWORKSPACE
+        assert f(T=257) == coli.COLI_ESHAPE  # decode: one chunk of at most 256 tokens
+        assert f(T=0) == coli.COLI_OK
+    assert experts(y=None) == coli.COLI_EINVAL
+    assert route(u=P((1 << 20) + 2)) == coli.COLI_EALIGN
+    sm = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22,
+                             0, (1 << 23) + 2)
+    assert route(layer=sm) == coli.COLI_EALIGN
+    assert experts(layer=sm) == coli.COLI_EALIGN
+
+
 def test_rmsnorm_rejects():
     L = coli.lib
     a = P(4096)
