@@ -472,6 +472,9 @@ def main():
             "gbps": round(b32 / (ms32 * 1e-3) / 1e9, 1),
             "frac": round(b32 / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "stage_ms": [round(s, 4) for s in d32["stage_ms"]]}
+        log("[bench] decode T=32 zipf through the HBM expert cache")
+        result["expert_cache_t32_zipf"] = run_cache(coli, W, zl[0],
+                                                    max(32, min(200, args.steps // 15)), 40)
         del zl
         log("[bench] tiny T=1")
         tl, _ = build_layer(coli, W, 0, 1)
@@ -589,6 +592,140 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
                       "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "data": "synthetic", "dtype": "f32",
     }
+
+
+def run_cache(coli, W, layer, steps, warmup, S=128, pool_n=16, repin_every=8,
+              decay_every=64):
+    """The T=32 Zipf decode with its routed experts in S HBM slots over pinned host
+    memory (coli_cache_*): every step routes the batch (coli_moe_route), plans the
+    loads (REPIN at the step boundary, then admission), stages the missing blobs
+    over PCIe and runs the experts (coli_moe_experts) from the slots.
+
+    Two batches are in flight: batch b routes on its own stream while batch b-1's
+    experts run, and b's blob copies run on a copy stream at the same time, except
+    the copies into a slot that batch b-1 still reads, which wait for it.  Workspace,
+    slot map and ids are double-buffered by batch parity."""
+    import numpy as np
+    import torch
+    c = W.CONFIGS[2]
+    T, H, I, E, K = c["T"], c["H"], c["I"], c["E"], c["K"]
+    nb = coli.coli_expert_blob_bytes(H, I)
+    host = torch.empty(E * nb, dtype=torch.uint8, pin_memory=True)
+    host.copy_(layer.experts)
+    slots = torch.empty(S * nb, dtype=torch.uint8, device="cuda")
+    smaps = [torch.full((E,), -1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    hmaps = [torch.empty(E, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    lays = [coli.MoELayer(H, I, E, K, layer.w_router, slots, layer.shared, layer.bias,
+                          slot_map=smaps[j]) for j in range(2)]
+    cache = coli.Cache(E, S)
+    pool = W.token_pool(2, pool_n * T, "cuda").reshape(pool_n, T, H).contiguous()
+    wsb = lays[0].workspace_bytes(T, coli.COLI_DECODE)
+    ws = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    idx = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in range(2)]
+    gates = [torch.empty((T, K), dtype=torch.float32, device="cuda") for _ in range(2)]
+    y = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in range(2)]
+    uq = [torch.empty(E + 1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    uq_h = [torch.empty(E + 1, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sR, sC, sP = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    c_ev = [None, None]          # experts done, per parity
+    used_prev = set()            # slots batch b-1 reads
+    stats = dict(needed=0, misses=0, swaps=0, deferred=0, loads=0)
+    torch.cuda.synchronize()
+
+    def step(b, count):
+        nonlocal used_prev
+        j = b % 2
+        x = pool[b % pool_n]
+        with torch.cuda.stream(sR):
+            if c_ev[j] is not None:
+                sR.wait_event(c_ev[j])  # batch b-2 done with this parity's buffers
+            coli.coli_moe_route(lays[j], coli.COLI_DECODE, x, ws[j], idx[j], gates[j],
+                                uq[j][:E], uq[j][E:], stream=sR)
+            uq_h[j].copy_(uq[j], non_blocking=True)
+            r_ev = torch.cuda.Event()
+            r_ev.record(sR)
+        r_ev.synchronize()
+        n = int(uq_h[j][E])
+        needed = uq_h[j].numpy()[:n]
+        loads = []
+        if b % decay_every == decay_every - 1:
+            cache.decay()
+        if b % repin_every == repin_every - 1:
+            sw = cache.repin(4)
+            loads += [(h, s_) for h, s_, _ in sw]
+            if count:
+                stats["swaps"] += len(sw)
+        adm = cache.admit(needed)
+        loads += adm
+        now = [ld for ld in loads if ld[1] not in used_prev]
+        later = [ld for ld in loads if ld[1] in used_prev]
+        if count:
+            stats["needed"] += n
+            stats["misses"] += len(adm)
+            stats["deferred"] += len(later)
+            stats["loads"] += len(loads)
+        hmaps[j].numpy()[:] = cache.slot_of
+        with torch.cuda.stream(sP):
+            if now:
+                coli.coli_cache_stage(host, slots, nb, now, stream=sP)
+            prev = c_ev[1 - j]
+            if prev is not None:
+                sP.wait_event(prev)  # batch b-1's experts: its slots and map are free
+            if later:
+                coli.coli_cache_stage(host, slots, nb, later, stream=sP)
+            smaps[j].copy_(hmaps[j], non_blocking=True)
+            p_ev = torch.cuda.Event()
+            p_ev.record(sP)
+        with torch.cuda.stream(sC):
+            sC.wait_event(p_ev)
+            sC.wait_event(r_ev)
+            coli.coli_moe_experts(lays[j], coli.COLI_DECODE, x, y[j], ws[j], idx[j], gates[j],
+                                  stream=sC, status=status)
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(sC)
+            c_ev[j] = ev
+        used_prev = {int(cache.slot_of[e]) for e in needed}
+        return ev
+
+    for b in range(warmup):
+        step(b, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    first = step(warmup, True)
+    for b in range(warmup + 1, warmup + steps):
+        last = step(b, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = first.elapsed_time(last) / (steps - 1)
+    assert int(status.item()) == 0, "a routed expert was not resident"
+    # the PCIe ceiling: one large pinned host -> device copy
+    big = min(E, 64) * nb
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    slots[:min(big, S * nb)].copy_(host[:min(big, S * nb)], non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    h2d = min(big, S * nb) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    staged = stats["loads"] * nb
+    out = dict(
+        workload=f"T=32 Zipf decode of the decode-shaped layer with {S} of {E} expert blobs "
+                 f"in HBM slots, all {E} in pinned host memory; REPIN every {repin_every} "
+                 f"steps, heat halved every {decay_every}",
+        slots=S, blob_bytes=nb, steps=steps, warmup=warmup,
+        ms_per_step=round(ms, 4), wall_ms_per_step=round(1e3 * wall / steps, 4),
+        tokens_per_s=round(T / (ms * 1e-3), 1),
+        unique_experts_mean=round(stats["needed"] / steps, 2),
+        hit_rate=round(1.0 - stats["misses"] / max(1, stats["needed"]), 4),
+        misses_per_step=round(stats["misses"] / steps, 3),
+        repin_swaps_per_step=round(stats["swaps"] / steps, 3),
+        deferred_frac=round(stats["deferred"] / max(1, stats["loads"]), 4),
+        staged_gbps=round(staged / (ms * 1e-3 * steps) / 1e9, 2),
+        h2d_copy_gbps=round(h2d, 2))
+    del host, slots
+    torch.cuda.empty_cache()
+    return out
 
 
 def build_layer_bias(coli, W, layers):
