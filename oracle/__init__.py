@@ -17,6 +17,11 @@ Every function names the passage it follows in the C source's comments:
 * batch-union permute -- page "Colibrì 深度解析", section 四;
 * expert FFN, combine, RMSNorm -- the readings listed in the design doc.
 
+Plain-Python modules beside it: ``tier.py`` (expert placement), ``usage.py`` (the
+.coli_usage history) and ``formats.py`` (the sibling weight formats of the
+registry: byte arithmetic, inference from byte counts, int3-g64, MXFP4 and
+fp8-e4m3-b128).
+
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 except the composition of a whole layer's float output, which the pages give
 no numbers for ("parity unpinned" beyond its pinned parts and the reductions
