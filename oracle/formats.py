@@ -192,26 +192,18 @@ def quant_mxfp4(w: np.ndarray):
     pad = np.zeros((O, NB * 32), dtype=np.float32)
     pad[:, :I] = w
     blk = pad.reshape(O, NB, 32)
-    packed = np.zeros((O, NB, 16), dtype=np.uint8)
-    scales = np.zeros((O, NB), dtype=np.uint8)
-    for o in range(O):
-        for b in range(NB):
-            v = blk[o, b]
-            if not np.isfinite(v).all():
-                scales[o, b] = 255
-                continue
-            amax = float(np.abs(v).max())
-            if amax == 0.0:
-                scales[o, b] = 0
-                continue
-            m, ex = math.frexp(amax)          # amax = m 2^ex, m in [0.5, 1)
-            shared = min(127, max(-127, (ex - 1) - 2))
-            scales[o, b] = shared + 127
-            # v / 2^shared, exact: a multiplication by the normal number 2^-shared
-            r = (v * np.float32(2.0 ** -shared)).astype(np.float32)
-            codes = e2m1_encode(r).astype(np.int64)
-            packed[o, b] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
-    return packed.reshape(O, NB * 16), scales
+    finite = np.isfinite(blk).all(axis=2)
+    amax = np.where(finite, np.abs(np.where(np.isfinite(blk), blk, 0)).max(axis=2), 0)
+    m, ex = np.frexp(amax.astype(np.float64))        # amax = m 2^ex, m in [0.5, 1)
+    shared = np.clip((ex - 1) - 2, -127, 127)        # floor(log2 amax) - 2
+    E = np.where(~finite, 255, np.where(amax == 0, 0, shared + 127)).astype(np.uint8)
+    # v / 2^shared, exact: a multiplication by the normal number 2^-shared
+    inv = np.ldexp(np.float32(1.0), (-shared).astype(np.int32)).astype(np.float32)
+    r = (blk * inv[:, :, None]).astype(np.float32)
+    codes = e2m1_encode(r).astype(np.int64)
+    codes[~finite | (amax == 0)] = 0
+    packed = (codes[:, :, 0::2] | (codes[:, :, 1::2] << 4)).astype(np.uint8)
+    return packed.reshape(O, NB * 16), E
 
 
 def dequant_mxfp4(packed: np.ndarray, scales: np.ndarray, I: int) -> np.ndarray:
