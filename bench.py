@@ -486,6 +486,8 @@ def main():
             "us_per_step": round(mst * 1e3, 2), "tokens_per_s": round(1.0 / (mst * 1e-3), 1),
             "stage_us": [round(1e3 * x, 2) for x in dt["stage_ms"]]}
         del tl
+        log("[bench] sibling-format matrix-vector products")
+        result["formats_matvec_t1"] = run_formats(coli, W)
         log("[bench] prefill T=2048")
         result["prefill"] = run_prefill(coli, W, layers[0],
                                         steps=max(2, min(10, args.steps // 300)))
@@ -726,6 +728,54 @@ def run_cache(coli, W, layer, steps, warmup, S=128, pool_n=16, repin_every=8,
     del host, slots
     torch.cuda.empty_cache()
     return out
+
+
+def run_formats(coli, W, steps=50, warmup=5):
+    """The dequantising matrix-vector product of each weight format on the gate and
+    up rows of one single-token step (9 units x 2 x 2048 rows, I = 6144), T = 1:
+    HBM GB/s of the packed bytes + scales per launch.  Copies of the matrix are
+    rotated so that at least 1 GiB is streamed between reuses (the 256 MB
+    Infinity Cache cannot serve it)."""
+    import torch
+    O, I = 9 * 2 * 2048, 6144
+    out = {}
+    w = torch.randn((O, I), device="cuda") * 0.02
+    x = torch.randn((1, I), device="cuda")
+    y = torch.empty((1, O), device="cuda")
+    for fmt, name in ((4, "int4-g64"), (5, "int3-g64"), (7, "mxfp4"), (8, "fp8-e4m3-b128")):
+        nw, ns = coli.coli_fmt_bytes(fmt, O, I)
+        ncopy = max(2, -(-(1 << 30) // (nw + ns)))
+        pk = [torch.empty(nw, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+        sc = [torch.empty(max(ns, 16), dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+        coli.coli_quant_fmt(fmt, w, pk[0], sc[0])
+        for j in range(1, ncopy):
+            pk[j].copy_(pk[0])
+            sc[j].copy_(sc[0])
+        args = [(fmt, ctypes.c_void_p(pk[j].data_ptr()), ctypes.c_void_p(sc[j].data_ptr()), O, I,
+                 ctypes.c_void_p(x.data_ptr()), 1, ctypes.c_void_p(y.data_ptr()),
+                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                for j in range(ncopy)]
+        for i in range(warmup):
+            coli.lib.coli_matvec_fmt(*args[i % ncopy])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            st = coli.lib.coli_matvec_fmt(*args[i % ncopy])
+            if st:
+                raise RuntimeError(f"coli_matvec_fmt: {st}")
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nbytes = nw + ns + I * 4 + O * 4
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us_per_launch": round(1e3 * ms, 2), "bytes_per_launch": nbytes,
+                     "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBS, 4),
+                     "bits_per_weight": round(8.0 * (nw + ns) / (O * I), 3)}
+        del pk, sc
+    torch.cuda.empty_cache()
+    return {"workload": f"y = W^ x, W [{O}, {I}] (the gate and up rows of 9 units), T = 1 "
+                        "fp32 token", "formats": out}
 
 
 def build_layer_bias(coli, W, layers):

@@ -447,6 +447,63 @@ int coli_cache_stage(const uint8_t *host_blobs, uint8_t *slots, size_t blob_byte
  * EDEVICE. */
 int coli_cache_slot_map(const coli_cache *c, int32_t *slot_map, void *stream);
 
+/* ---------------------------------------------------------------------- */
+/* sibling weight formats (page "从源码开始colibri纯C引擎的编译、权重转换与   */
+/* .bin直映射实战", section 权重转换: the format registry, a tensor's format    */
+/* inferred from its byte counts; page "Colibrì 深度解析", sections 八, 十    */
+/* and 十五)                                                                  */
+/* ---------------------------------------------------------------------- */
+
+/* The registry's ordinals. */
+typedef enum {
+    COLI_FMT_F32 = 0,           /* 4 O I bytes, no scale array                   */
+    COLI_FMT_INT8_ROW = 1,      /* O I bytes + one f32 per row                   */
+    COLI_FMT_INT4_ROW = 2,      /* O ceil(I/2) bytes + one f32 per row           */
+    COLI_FMT_INT2_ROW = 3,      /* O ceil(I/4) bytes + one f32 per row           */
+    COLI_FMT_INT4_G64 = 4,      /* this library's int4-g64 planar format         */
+    COLI_FMT_INT3_G64 = 5,      /* 24 bytes per 64 (three bit planes of u = q+4) */
+                                /* + one f32 per 64: s = amax/3, q in [-4, 3]    */
+    COLI_FMT_E8_IQ3 = 6,        /* layout not known here: never inferred         */
+    COLI_FMT_MXFP4 = 7,         /* OCP MX: 16 bytes per 32 (E2M1 nibbles, element */
+                                /* 2j low) + one E8M0 byte per 32                */
+    COLI_FMT_FP8_E4M3_B128 = 8  /* OCP E4M3 bytes [O, I] + one f32 per 128x128   */
+                                /* tile: s = amax/448                            */
+} coli_fmt;
+
+#define COLI_EFORMAT (-10)         /* no registry format, or more than one, has  */
+                                   /* these byte counts                         */
+#define COLI_FMT_MAX_ROWS 1048576  /* O limit of the format calls               */
+#define COLI_MATVEC_MAX_T 8
+
+/* Weight and scale byte counts of an [O, I] tensor in `fmt` (HOST outputs).
+ * Errors: EINVAL (NULL, fmt 6 or unknown), ESHAPE (O or I outside
+ * [1, FMT_MAX_ROWS] x [1, MAX_DIM]). */
+int coli_fmt_bytes(int fmt, int64_t O, int64_t I, uint64_t *weight_bytes,
+                   uint64_t *scale_bytes);
+/* The format whose byte counts are these, from the counts and [O, I] alone.
+ * Returns the ordinal (>= 0) when exactly one format matches, else
+ * COLI_EFORMAT (fail closed: some shapes give two formats the same counts,
+ * e.g. int4-row and int4-g64 at I = 64); *candidates (optional, HOST) gets the
+ * bit set of the matching ordinals.  ESHAPE for O or I out of range. */
+int coli_resolve_fmt(int64_t O, int64_t I, uint64_t weight_bytes, uint64_t scale_bytes,
+                     uint32_t *candidates);
+/* Quantise fp32 w [O, I] (device) into `packed` / `scales` (device, sizes from
+ * coli_fmt_bytes) in fmt 4, 5, 7 or 8, bit-exact to the rules above (round to
+ * nearest even; zero-padded ragged groups and blocks; a group, block or tile
+ * holding a non-finite value gets the NaN scale (E8M0 255), neutral codes and
+ * status bit 1).  Alignment: w 4, packed 8 (int3) or 4, scales 4.  Errors:
+ * EINVAL (NULL, other fmt), ESHAPE, EALIGN, EDEVICE. */
+int coli_quant_fmt(int fmt, const float *w, int64_t O, int64_t I, void *packed,
+                   void *scales, int32_t *status, void *stream);
+/* Dequantising matrix-vector product for decode: y[t, o] = sum_i W^[o, i] x[t, i]
+ * for t < T <= 8, W^ the dequantised [O, I] tensor in fmt 4, 5, 7 or 8 (fmt 4
+ * with its row-major scales), x fp32 [T, I], y fp32 [T, O] (device), fp32
+ * accumulation.  Limits: T * (I rounded up to the format's group) <= 24576;
+ * fp8 rows a multiple of 16 bytes (I % 16 == 0).  Alignment: packed 16 (8 for
+ * int3), scales, x and y 4.  Errors: EINVAL, ESHAPE, EALIGN, EDEVICE. */
+int coli_matvec_fmt(int fmt, const void *packed, const void *scales, int64_t O, int64_t I,
+                    const float *x, int T, float *y, void *stream);
+
 /*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same

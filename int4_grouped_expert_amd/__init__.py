@@ -36,7 +36,7 @@ lib = ctypes.CDLL(_LIB_PATH)
 
 COLI_OK, COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN = 0, -1, -2, -3
 COLI_EDTYPE, COLI_EWORKSPACE, COLI_EDEVICE, COLI_ESCRATCH = -4, -5, -6, -7
-COLI_EUSAGE, COLI_EIO = -8, -9
+COLI_EUSAGE, COLI_EIO, COLI_EFORMAT = -8, -9, -10
 COLI_USAGE_VERSION = 1
 COLI_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 COLI_F32, COLI_BF16 = 0, 1
@@ -48,6 +48,10 @@ COLI_MAX_EXPERTS = 1024
 COLI_MAX_DIM = 65536
 COLI_MAX_TOKENS = 65536
 COLI_MAX_DECODE_T = 256
+(COLI_FMT_F32, COLI_FMT_INT8_ROW, COLI_FMT_INT4_ROW, COLI_FMT_INT2_ROW, COLI_FMT_INT4_G64,
+ COLI_FMT_INT3_G64, COLI_FMT_E8_IQ3, COLI_FMT_MXFP4, COLI_FMT_FP8_E4M3_B128) = range(9)
+COLI_FMT_MAX_ROWS = 1048576
+COLI_MATVEC_MAX_T = 8
 
 EXPORTS = [
     "coli_strerror", "coli_int4_g64_packed_bytes", "coli_int4_g64_scale_count",
@@ -58,7 +62,8 @@ EXPORTS = [
     "coli_usage_count", "coli_usage_engine_hash", "coli_usage_save", "coli_usage_load",
     "coli_rmsnorm_f32", "coli_moe_route", "coli_moe_experts", "coli_tier_should_promote",
     "coli_tier_lfru_score", "coli_cache_init", "coli_cache_decay", "coli_cache_admit",
-    "coli_cache_repin", "coli_cache_stage", "coli_cache_slot_map",
+    "coli_cache_repin", "coli_cache_stage", "coli_cache_slot_map", "coli_fmt_bytes",
+    "coli_resolve_fmt", "coli_quant_fmt", "coli_matvec_fmt",
 ]
 
 _p = ctypes.c_void_p
@@ -124,6 +129,12 @@ _proto("coli_cache_admit", _i, [ctypes.POINTER(coli_cache), _p, _i, _p, _p,
 _proto("coli_cache_repin", _i, [ctypes.POINTER(coli_cache), _i, _p, _p, _p, ctypes.POINTER(_i)])
 _proto("coli_cache_stage", _i, [_p, _p, _sz, _p, _p, _i, _p])
 _proto("coli_cache_slot_map", _i, [ctypes.POINTER(coli_cache), _p, _p])
+_proto("coli_fmt_bytes", _i, [_i, _i64, _i64, ctypes.POINTER(ctypes.c_uint64),
+                              ctypes.POINTER(ctypes.c_uint64)])
+_proto("coli_resolve_fmt", _i, [_i64, _i64, ctypes.c_uint64, ctypes.c_uint64,
+                                ctypes.POINTER(ctypes.c_uint32)])
+_proto("coli_quant_fmt", _i, [_i, _p, _i64, _i64, _p, _p, _p, _p])
+_proto("coli_matvec_fmt", _i, [_i, _p, _p, _i64, _i64, _p, _i, _p, _p])
 _proto("coli_usage_count", _i, [_p, _i, _i, _i, _i, _i, _p, _p])
 _proto("coli_usage_engine_hash", ctypes.c_uint32, [ctypes.c_char_p])
 _proto("coli_usage_save", _i, [ctypes.c_char_p, _p, _i, _i, ctypes.c_uint32, ctypes.c_double, _p])
@@ -420,6 +431,39 @@ def coli_cache_stage(host_blobs, slots, blob_bytes: int, loads, stream=None):
     return _check(lib.coli_cache_stage(_ptr(host_blobs), _ptr(slots), blob_bytes,
                                        le.ctypes.data, ls.ctypes.data, len(loads),
                                        _stream(stream)), "coli_cache_stage")
+
+
+# ---------------------------------------------------------------- sibling formats
+
+def coli_fmt_bytes(fmt: int, O: int, I: int):
+    """-> (weight bytes, scale bytes) of an [O, I] tensor in `fmt`."""
+    w, sc = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    _check(lib.coli_fmt_bytes(fmt, O, I, ctypes.byref(w), ctypes.byref(sc)), "coli_fmt_bytes")
+    return int(w.value), int(sc.value)
+
+
+def coli_resolve_fmt(O: int, I: int, weight_bytes: int, scale_bytes: int):
+    """-> (fmt or None, sorted list of the matching ordinals)."""
+    m = ctypes.c_uint32(0)
+    r = lib.coli_resolve_fmt(O, I, weight_bytes, scale_bytes, ctypes.byref(m))
+    if r not in (COLI_EFORMAT,) and r < 0:
+        _check(r, "coli_resolve_fmt")
+    cands = [f for f in range(9) if (m.value >> f) & 1]
+    return (r if r >= 0 else None), cands
+
+
+def coli_quant_fmt(fmt: int, w, packed, scales, status=None, stream=None):
+    """Quantise fp32 w [O, I] (device) into packed / scales (device uint8 tensors)."""
+    O, I = w.shape
+    return _check(lib.coli_quant_fmt(fmt, _ptr(w), O, I, _ptr(packed), _ptr(scales),
+                                     _ptr(status), _stream(stream)), "coli_quant_fmt")
+
+
+def coli_matvec_fmt(fmt: int, packed, scales, O: int, I: int, x, y, stream=None):
+    """y [T, O] = x [T, I] W^T with W the dequantised [O, I] tensor (device)."""
+    T = x.shape[0]
+    return _check(lib.coli_matvec_fmt(fmt, _ptr(packed), _ptr(scales), O, I, _ptr(x), T,
+                                      _ptr(y), _stream(stream)), "coli_matvec_fmt")
 
 
 # ---------------------------------------------------------------- layer assembly

@@ -126,6 +126,7 @@ const char *coli_strerror(int status) {
     case COLI_ESCRATCH: return "request larger than the no-alloc scratch array";
     case COLI_EUSAGE: return "routing history refused (geometry, version or identity)";
     case COLI_EIO: return "routing history file could not be read or written";
+    case COLI_EFORMAT: return "no single registry format has these byte counts";
     default: return "unknown status";
   }
 }

@@ -1,0 +1,649 @@
+// formats.hip -- the sibling weight formats of the registry: byte arithmetic,
+// inference of a tensor's format from its byte counts, quantisers, and a
+// dequantising matrix-vector product for decode (y[t] = W^ x[t], T <= 8).
+//
+// Registry and inference: page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战",
+// section 权重转换 (0 f32, 1 int8-row, 2 int4-row, 3 int2-row, 4 int4-grouped,
+// 5 int3-g64, 6 E8/IQ3, 7 MXFP4, 8 fp8-e4m3-b128; the format follows from the
+// weight bytes, the scale bytes and [O, I] alone).  Raw f32 has no scale array
+// (page "Colibrì 深度解析", section 十五).  int3 with a per-group scale is 3.5 bits
+// per weight (same page, section 八); the quantised matrix kernels from int4 to
+// MXFP4: section 十.  MXFP4 follows the OCP Microscaling (MX) v1.0 specification
+// (32 E2M1 elements, one E8M0 scale, the shared exponent floor(log2 amax) - 2,
+// elements rounded to nearest even and saturated at 6); E4M3 the OCP FP8
+// specification (bias 7, largest finite 448).
+//
+// Layouts (the formats' names fix no byte order; these are this library's):
+//   int3-g64: a group of 64 codes u = q + 4 is 24 bytes, three little-endian
+//             64-bit bit planes (bit j of plane p = bit p of u[j]); f32 scale
+//             per group, s = amax / 3, q = clip(rint(w / s), -4, 3).
+//   MXFP4:    a block of 32 is 16 bytes, element 2j in the low nibble of byte j;
+//             nibble = sign << 3 | E2M1 code; one E8M0 byte per block.
+//   fp8-b128: E4M3 codes row-major [O, I]; one f32 scale per 128 x 128 tile,
+//             s = amax / 448.
+// Non-finite inputs: the group / block / tile gets the NaN scale (E8M0 255) and
+// neutral codes, and the status flag bit 1 is raised.
+//
+// The matrix-vector product streams each row's bytes once with 16-byte (8-byte
+// for int3) loads; x sits in LDS; a wave works on four rows at a time so that
+// each x value read from LDS serves four rows; the per-chunk (= per scale) sums
+// are scaled once; every lane reduces in a fixed order, so results are
+// deterministic.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "coli.h"
+#include "wave.h"
+
+namespace coli {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxT = 8;
+constexpr int kRows = 4;         // rows per wave step
+constexpr int kXFloats = 24576;  // T * padded I: 96 KiB of LDS
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool fmt_sizes(int fmt, int64_t O, int64_t I, uint64_t *w, uint64_t *s) {
+  const int64_t G = cdiv(I, 64);
+  switch (fmt) {
+    case COLI_FMT_F32: *w = uint64_t(4 * O * I); *s = 0; return true;
+    case COLI_FMT_INT8_ROW: *w = uint64_t(O * I); *s = uint64_t(4 * O); return true;
+    case COLI_FMT_INT4_ROW: *w = uint64_t(O * cdiv(I, 2)); *s = uint64_t(4 * O); return true;
+    case COLI_FMT_INT2_ROW: *w = uint64_t(O * cdiv(I, 4)); *s = uint64_t(4 * O); return true;
+    case COLI_FMT_INT4_G64: *w = uint64_t(32 * O * G); *s = uint64_t(4 * O * G); return true;
+    case COLI_FMT_INT3_G64: *w = uint64_t(24 * O * G); *s = uint64_t(4 * O * G); return true;
+    case COLI_FMT_MXFP4: *w = uint64_t(16 * O * cdiv(I, 32)); *s = uint64_t(O * cdiv(I, 32));
+      return true;
+    case COLI_FMT_FP8_E4M3_B128: *w = uint64_t(O * I);
+      *s = uint64_t(4 * cdiv(O, 128) * cdiv(I, 128)); return true;
+    default: return false;  // E8/IQ3 and unknown ordinals
+  }
+}
+
+bool dims_ok(int64_t O, int64_t I) {
+  return O >= 1 && O <= COLI_FMT_MAX_ROWS && I >= 1 && I <= COLI_MAX_DIM;
+}
+
+// ------------------------------------------------------------------ quantisers
+
+// int3-g64: one wave per group; lane j holds element j.  The bit planes are
+// the ballots of each code bit.
+__global__ __launch_bounds__(256) void quant_int3(const float *__restrict__ w, int64_t O, int I,
+                                                  int G, uint8_t *__restrict__ packed,
+                                                  float *__restrict__ scales,
+                                                  int32_t *__restrict__ status) {
+  const int lane = threadIdx.x & 63;
+  const int64_t grp = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (grp >= O * G) return;  // whole waves
+  const int64_t o = grp / G;
+  const int g = int(grp - o * G);
+  const int col = g * 64 + lane;
+  const float v = col < I ? w[o * I + col] : 0.0f;
+  const bool bad = __ballot(!__builtin_isfinite(v)) != 0;
+  const float amax = wave_max(fabsf(v));
+  const float s = bad ? __builtin_nanf("") : amax / 3.0f;
+  int u = 4;
+  if (!bad && s != 0.0f) u = int(fminf(fmaxf(rintf(v / s), -4.0f), 3.0f)) + 4;
+  const uint64_t p0 = __ballot(u & 1), p1 = __ballot(u & 2), p2 = __ballot(u & 4);
+  uint64_t *dst = reinterpret_cast<uint64_t *>(packed + grp * 24);
+  if (lane == 0) dst[0] = p0;
+  if (lane == 1) dst[1] = p1;
+  if (lane == 2) dst[2] = p2;
+  if (lane == 3) scales[grp] = s;
+  if (lane == 4 && bad && status) atomicOr(status, 1);
+}
+
+// E2M1 magnitude code of a (|v| / X, >= 0), round to nearest even, saturating.
+__device__ inline uint32_t e2m1_code(float a) {
+  return uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) +
+         uint32_t(a >= 1.75f) + uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+}
+
+// MXFP4: one half-wave per block of 32; lane i holds element i.
+__global__ __launch_bounds__(256) void quant_mxfp4(const float *__restrict__ w, int64_t O, int I,
+                                                   int NB, uint8_t *__restrict__ packed,
+                                                   uint8_t *__restrict__ scales,
+                                                   int32_t *__restrict__ status) {
+  const int lane = threadIdx.x & 63, li = lane & 31;
+  const int64_t blk = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  const bool live = blk < O * NB;
+  const int64_t o = live ? blk / NB : 0;
+  const int b = live ? int(blk - o * NB) : 0;
+  const int col = b * 32 + li;
+  const float v = (live && col < I) ? w[o * I + col] : 0.0f;
+  int bad = !__builtin_isfinite(v);
+  float amax = fabsf(v);
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) {  // within the half-wave
+    bad |= __shfl_xor(bad, m, 64);
+    amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  }
+  uint32_t E = 0, nib = 0;
+  if (bad) {
+    E = 255;
+  } else if (amax != 0.0f) {
+    const int ef = int((__float_as_uint(amax) >> 23) & 255u);
+    const int fl = ef ? ef - 127 : -127;  // floor(log2 amax), subnormals clamp below
+    const int shared = fl - 2 < -127 ? -127 : fl - 2;
+    E = uint32_t(shared + 127);
+    const float inv = __uint_as_float(uint32_t(127 - shared) << 23);  // 2^-shared, normal
+    const float r = v * inv;  // exact: a power-of-two scaling
+    nib = (__float_as_uint(v) >> 31) << 3 | e2m1_code(fminf(fabsf(r), 6.0f));
+  }
+  // eight nibbles per 32-bit word: lanes 8m .. 8m+7 -> word m of the block
+  uint32_t word = nib << (4 * (li & 7));
+#pragma unroll
+  for (int m = 1; m <= 4; m <<= 1) word |= __shfl_xor(word, m, 64);
+  if (live && (li & 7) == 0)
+    reinterpret_cast<uint32_t *>(packed + blk * 16)[li >> 3] = word;
+  if (live && li == 0) {
+    scales[blk] = uint8_t(E);
+    if (bad && status) atomicOr(status, 1);
+  }
+}
+
+// fp8-b128, pass 1: one block per 128 x 128 tile -> its scale.
+__global__ __launch_bounds__(256) void fp8_tile_scales(const float *__restrict__ w, int64_t O,
+                                                       int I, int TI, float *__restrict__ scales,
+                                                       int32_t *__restrict__ status) {
+  const int64_t ta = blockIdx.x / TI;
+  const int tb = int(blockIdx.x - ta * TI);
+  const int64_t r0 = ta * 128;
+  const int c0 = tb * 128;
+  const int nr = int(O - r0 < 128 ? O - r0 : 128), nc = I - c0 < 128 ? I - c0 : 128;
+  float amax = 0.0f;
+  int bad = 0;
+  for (int i = threadIdx.x; i < nr * 128; i += 256) {
+    const int r = i >> 7, c = i & 127;
+    if (c < nc) {
+      const float v = w[(r0 + r) * I + c0 + c];
+      bad |= !__builtin_isfinite(v);
+      amax = fmaxf(amax, fabsf(v));
+    }
+  }
+  __shared__ float sm[4];
+  __shared__ int sb[4];
+  amax = wave_max(amax);
+  bad = __ballot(bad) != 0;
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[wv] = amax;
+    sb[wv] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float a = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    const int anybad = sb[0] | sb[1] | sb[2] | sb[3];
+    scales[blockIdx.x] = anybad ? __builtin_nanf("") : a / 448.0f;
+    if (anybad && status) atomicOr(status, 1);
+  }
+}
+
+// E4M3 code of a in [0, 448], round to nearest even.
+__device__ inline uint32_t e4m3_code(float a) {
+  if (a < 0x1p-6f) return uint32_t(rintf(a * 512.0f));  // subnormal steps of 2^-9
+  const uint32_t b = __float_as_uint(a);
+  return ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+}
+
+// fp8-b128, pass 2: one thread per element.
+__global__ __launch_bounds__(256) void fp8_codes(const float *__restrict__ w, int64_t O, int I,
+                                                 int TI, const float *__restrict__ scales,
+                                                 uint8_t *__restrict__ codes) {
+  const int64_t n = O * I;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / I;
+    const int c = int(i - r * I);
+    const float s = scales[(r >> 7) * TI + (c >> 7)];
+    uint32_t code = 0;
+    if (s > 0.0f) {  // false for a zero or NaN scale
+      const float v = w[i];
+      code = (__float_as_uint(v) >> 31) << 7 | e4m3_code(fminf(fabsf(v / s), 448.0f));
+    }
+    codes[i] = uint8_t(code);
+  }
+}
+
+// ------------------------------------------------------------------ matvec
+
+template <int FMT>
+struct Chunk;  // one lane's unit of a row: bytes, weights, one scale
+template <>
+struct Chunk<COLI_FMT_FP8_E4M3_B128> {
+  static constexpr int kBytes = 16, kW = 16;
+};
+template <>
+struct Chunk<COLI_FMT_MXFP4> {
+  static constexpr int kBytes = 16, kW = 32;
+};
+template <>
+struct Chunk<COLI_FMT_INT3_G64> {
+  static constexpr int kBytes = 24, kW = 64;
+};
+template <>
+struct Chunk<COLI_FMT_INT4_G64> {
+  static constexpr int kBytes = 32, kW = 64;
+};
+
+// The chunk's raw bytes (as 32-bit words).
+template <int FMT>
+struct Raw {
+  uint32_t v[Chunk<FMT>::kBytes / 4];
+};
+
+template <int FMT>
+__device__ inline Raw<FMT> load_chunk(const uint8_t *p) {
+  Raw<FMT> r;
+  if constexpr (Chunk<FMT>::kBytes % 16 == 0) {
+#pragma unroll
+    for (int q = 0; q < Chunk<FMT>::kBytes / 16; ++q) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(p + 16 * q);
+      r.v[4 * q] = u.x;
+      r.v[4 * q + 1] = u.y;
+      r.v[4 * q + 2] = u.z;
+      r.v[4 * q + 3] = u.w;
+    }
+  } else {  // int3: three 8-byte planes
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const uint2 u = *reinterpret_cast<const uint2 *>(p + 8 * q);
+      r.v[2 * q] = u.x;
+      r.v[2 * q + 1] = u.y;
+    }
+  }
+  return r;
+}
+
+// Byte K of u as a float (one v_cvt_f32_ubyteK).
+template <int K>
+__device__ inline float ubyte(uint32_t u) { return float((u >> (8 * K)) & 0xFFu); }
+
+// 4 three-bit codes -> one byte each: bits 4m..4m+3 of the three planes.
+__device__ inline uint32_t int3_bytes(const uint32_t (&v)[6], int m) {
+  const int word = m >> 3, sh = 4 * (m & 7);
+  uint32_t out = 0;
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const uint32_t nib = (v[2 * p + word] >> sh) & 15u;
+    out |= ((nib * 0x00204081u) & 0x01010101u) << p;  // bit k -> byte k
+  }
+  return out;
+}
+
+// sum_k code_k * x_k over the chunk (code in the format's own units), for T
+// tokens; x at xs + t * ldx.
+template <int FMT, int T>
+__device__ inline void chunk_dot(const Raw<FMT> &r, const float *xs, int ldx, float (&d)[T]) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) d[t] = 0.0f;
+  if constexpr (FMT == COLI_FMT_FP8_E4M3_B128) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(r.v[q], false);
+      const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(r.v[q], true);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float4 x = *reinterpret_cast<const float4 *>(xs + t * ldx + 4 * q);
+        d[t] = fmaf(a.x, x.x, fmaf(a.y, x.y, fmaf(b.x, x.z, fmaf(b.y, x.w, d[t]))));
+      }
+    }
+  } else if constexpr (FMT == COLI_FMT_MXFP4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 0);
+      const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 1);
+      const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 2);
+      const f32x2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 3);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(xs + t * ldx + 8 * q);
+        const float4 x1 = *reinterpret_cast<const float4 *>(xs + t * ldx + 8 * q + 4);
+        float s = d[t];
+        s = fmaf(a.x, x0.x, s);
+        s = fmaf(a.y, x0.y, s);
+        s = fmaf(b.x, x0.z, s);
+        s = fmaf(b.y, x0.w, s);
+        s = fmaf(c.x, x1.x, s);
+        s = fmaf(c.y, x1.y, s);
+        s = fmaf(e.x, x1.z, s);
+        s = fmaf(e.y, x1.w, s);
+        d[t] = s;
+      }
+    }
+  } else if constexpr (FMT == COLI_FMT_INT3_G64) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const uint32_t u = int3_bytes(r.v, m);
+      const float u0 = ubyte<0>(u), u1 = ubyte<1>(u);
+      const float u2 = ubyte<2>(u), u3 = ubyte<3>(u);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float4 x = *reinterpret_cast<const float4 *>(xs + t * ldx + 4 * m);
+        d[t] = fmaf(u0, x.x, fmaf(u1, x.y, fmaf(u2, x.z, fmaf(u3, x.w, d[t]))));
+      }
+    }
+  } else {  // int4-g64 planar: byte k holds element k (low) and k + 32 (high)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t lo = r.v[q] & 0x0F0F0F0Fu, hi = (r.v[q] >> 4) & 0x0F0F0F0Fu;
+      const float l0 = ubyte<0>(lo), l1 = ubyte<1>(lo);
+      const float l2 = ubyte<2>(lo), l3 = ubyte<3>(lo);
+      const float h0 = ubyte<0>(hi), h1 = ubyte<1>(hi);
+      const float h2 = ubyte<2>(hi), h3 = ubyte<3>(hi);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float4 xl = *reinterpret_cast<const float4 *>(xs + t * ldx + 4 * q);
+        const float4 xh = *reinterpret_cast<const float4 *>(xs + t * ldx + 32 + 4 * q);
+        float s = d[t];
+        s = fmaf(l0, xl.x, s);
+        s = fmaf(l1, xl.y, s);
+        s = fmaf(l2, xl.z, s);
+        s = fmaf(l3, xl.w, s);
+        s = fmaf(h0, xh.x, s);
+        s = fmaf(h1, xh.y, s);
+        s = fmaf(h2, xh.z, s);
+        s = fmaf(h3, xh.w, s);
+        d[t] = s;
+      }
+    }
+  }
+}
+
+struct MatvecArgs {
+  const uint8_t *packed;
+  const void *scales;
+  int64_t O;
+  int I, ldx;        // ldx: padded row length of x in LDS (chunks * weights)
+  int chunks;        // chunks per row
+  int64_t row_bytes;
+  int scale_cols;    // fp8: tiles per row of tiles; others: scales per row
+  const float *x;
+  float *y;
+};
+
+// y[t, o] = sum_i W^[o, i] x[t, i].  A wave takes four rows at a time; lane l
+// takes the row chunks l, l + 64, ...; the per-chunk dot products are scaled
+// by the chunk's scale (and, for the offset formats, corrected by the chunk's
+// x sum times the code offset), then reduced over the wave.
+template <int FMT, int T>
+__global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
+  constexpr int CW = Chunk<FMT>::kW, CB = Chunk<FMT>::kBytes;
+  constexpr bool kOffset = FMT == COLI_FMT_INT3_G64 || FMT == COLI_FMT_INT4_G64;
+  constexpr float kOff = FMT == COLI_FMT_INT3_G64 ? 4.0f : 8.0f;
+  extern __shared__ float xs[];  // [T][ldx], then the chunk sums [T][chunks]
+  float *xsum = xs + T * a.ldx;
+  for (int i = threadIdx.x; i < T * a.ldx; i += 256) {
+    const int t = i / a.ldx, k = i - t * a.ldx;
+    xs[i] = k < a.I ? a.x[size_t(t) * a.I + k] : 0.0f;
+  }
+  __syncthreads();
+  if constexpr (kOffset) {
+    for (int i = threadIdx.x; i < T * a.chunks; i += 256) {
+      const int t = i / a.chunks, c = i - t * a.chunks;
+      const float *p = xs + t * a.ldx + c * CW;
+      float s = 0.0f;
+      for (int k = 0; k < CW; ++k) s += p[k];  // fixed order
+      xsum[i] = s;
+    }
+    __syncthreads();
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t groups = (a.O + kRows - 1) / kRows;
+  for (int64_t g = int64_t(blockIdx.x) * 4 + wave; g < groups; g += int64_t(gridDim.x) * 4) {
+    int64_t row[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int64_t o = g * kRows + r;
+      row[r] = o < a.O ? o : a.O - 1;  // past the end: re-read the last row, never stored
+    }
+    float acc[kRows][T];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t] = 0.0f;
+    for (int c = lane; c < a.chunks; c += 64) {
+      Raw<FMT> raw[kRows];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r)
+        raw[r] = load_chunk<FMT>(a.packed + row[r] * a.row_bytes + int64_t(c) * CB);
+      float sc[kRows];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        if constexpr (FMT == COLI_FMT_FP8_E4M3_B128) {
+          sc[r] = reinterpret_cast<const float *>(a.scales)[(row[r] >> 7) * a.scale_cols +
+                                                            ((c * CW) >> 7)];
+        } else if constexpr (FMT == COLI_FMT_MXFP4) {
+          const uint32_t E = reinterpret_cast<const uint8_t *>(a.scales)[row[r] * a.scale_cols + c];
+          sc[r] = E == 255u ? __builtin_nanf("")
+                            : (E ? __uint_as_float(E << 23) : __uint_as_float(0x00400000u));
+        } else {
+          sc[r] = reinterpret_cast<const float *>(a.scales)[row[r] * a.scale_cols + c];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        float d[T];
+        chunk_dot<FMT, T>(raw[r], xs + c * CW, a.ldx, d);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          if constexpr (kOffset) d[t] = fmaf(-kOff, xsum[t * a.chunks + c], d[t]);
+          acc[r][t] = fmaf(sc[r], d[t], acc[r][t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float v = wave_sum(acc[r][t]);
+        const int64_t o = g * kRows + r;
+        if (lane == r * T + t && o < a.O) a.y[size_t(t) * a.O + o] = v;
+      }
+  }
+}
+
+template <int FMT>
+hipError_t launch_matvec_t(const MatvecArgs &a, int T, size_t lds, int grid, hipStream_t s) {
+  switch (T) {
+#define COLI_MV_CASE(TT)                                                            \
+  case TT:                                                                          \
+    hipLaunchKernelGGL((matvec_kernel<FMT, TT>), dim3(grid), dim3(256), lds, s, a); \
+    break;
+    COLI_MV_CASE(1)
+    COLI_MV_CASE(2)
+    COLI_MV_CASE(3)
+    COLI_MV_CASE(4)
+    COLI_MV_CASE(5)
+    COLI_MV_CASE(6)
+    COLI_MV_CASE(7)
+    COLI_MV_CASE(8)
+#undef COLI_MV_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+void allow_lds_once() {
+  // the x stage may take up to 96 KiB + the chunk sums
+#define COLI_MV_ATTR(TT)                                                             \
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&matvec_kernel<FMT, TT>), \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  COLI_MV_ATTR(1)
+  COLI_MV_ATTR(2)
+  COLI_MV_ATTR(3)
+  COLI_MV_ATTR(4)
+  COLI_MV_ATTR(5)
+  COLI_MV_ATTR(6)
+  COLI_MV_ATTR(7)
+  COLI_MV_ATTR(8)
+#undef COLI_MV_ATTR
+}
+
+template <int FMT>
+void allow_lds() {
+  static const bool done = (allow_lds_once<FMT>(), true);  // once per process
+  (void)done;
+}
+
+bool aligned_to(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+}  // namespace coli
+
+using namespace coli;
+
+extern "C" {
+
+int coli_fmt_bytes(int fmt, int64_t O, int64_t I, uint64_t *weight_bytes,
+                   uint64_t *scale_bytes) {
+  if (!weight_bytes || !scale_bytes) return COLI_EINVAL;
+  if (!dims_ok(O, I)) return COLI_ESHAPE;
+  uint64_t w, s;
+  if (!fmt_sizes(fmt, O, I, &w, &s)) return COLI_EINVAL;
+  *weight_bytes = w;
+  *scale_bytes = s;
+  return COLI_OK;
+}
+
+int coli_resolve_fmt(int64_t O, int64_t I, uint64_t weight_bytes, uint64_t scale_bytes,
+                     uint32_t *candidates) {
+  if (!dims_ok(O, I)) return COLI_ESHAPE;
+  uint32_t mask = 0;
+  int found = -1;
+  for (int f = 0; f <= COLI_FMT_FP8_E4M3_B128; ++f) {
+    uint64_t w, s;
+    if (fmt_sizes(f, O, I, &w, &s) && w == weight_bytes && s == scale_bytes) {
+      mask |= 1u << f;
+      found = f;
+    }
+  }
+  if (candidates) *candidates = mask;
+  return __builtin_popcount(mask) == 1 ? found : COLI_EFORMAT;
+}
+
+int coli_quant_fmt(int fmt, const float *w, int64_t O, int64_t I, void *packed, void *scales,
+                   int32_t *status, void *stream) {
+  if (!w || !packed || !scales) return COLI_EINVAL;
+  if (!dims_ok(O, I)) return COLI_ESHAPE;
+  if (!aligned_to(w, 4) || (status && !aligned_to(status, 4))) return COLI_EALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int Ii = int(I);
+  switch (fmt) {
+    case COLI_FMT_INT4_G64:
+      return coli_quant_int4_g64(w, O, I, reinterpret_cast<uint8_t *>(packed),
+                                 reinterpret_cast<float *>(scales), status, stream);
+    case COLI_FMT_INT3_G64: {
+      if (!aligned_to(packed, 8) || !aligned_to(scales, 4)) return COLI_EALIGN;
+      const int G = int(cdiv(I, 64));
+      const int64_t groups = O * G;
+      quant_int3<<<dim3(unsigned(cdiv(groups, 4))), 256, 0, s>>>(
+          w, O, Ii, G, reinterpret_cast<uint8_t *>(packed), reinterpret_cast<float *>(scales),
+          status);
+      break;
+    }
+    case COLI_FMT_MXFP4: {
+      if (!aligned_to(packed, 4)) return COLI_EALIGN;
+      const int NB = int(cdiv(I, 32));
+      const int64_t blocks = O * NB;
+      quant_mxfp4<<<dim3(unsigned(cdiv(blocks, 8))), 256, 0, s>>>(
+          w, O, Ii, NB, reinterpret_cast<uint8_t *>(packed), reinterpret_cast<uint8_t *>(scales),
+          status);
+      break;
+    }
+    case COLI_FMT_FP8_E4M3_B128: {
+      if (!aligned_to(scales, 4)) return COLI_EALIGN;
+      const int TI = int(cdiv(I, 128));
+      const int64_t tiles = cdiv(O, 128) * TI;
+      fp8_tile_scales<<<dim3(unsigned(tiles)), 256, 0, s>>>(
+          w, O, Ii, TI, reinterpret_cast<float *>(scales), status);
+      const int64_t n = O * I;
+      const int64_t gb = cdiv(n, 256);
+      fp8_codes<<<dim3(unsigned(gb < 65536 ? gb : 65536)), 256, 0, s>>>(
+          w, O, Ii, TI, reinterpret_cast<const float *>(scales),
+          reinterpret_cast<uint8_t *>(packed));
+      break;
+    }
+    default:
+      return COLI_EINVAL;
+  }
+  return hipGetLastError() == hipSuccess ? COLI_OK : COLI_EDEVICE;
+}
+
+int coli_matvec_fmt(int fmt, const void *packed, const void *scales, int64_t O, int64_t I,
+                    const float *x, int T, float *y, void *stream) {
+  if (!packed || !scales || ((!x || !y) && T > 0)) return COLI_EINVAL;
+  if (!dims_ok(O, I) || T < 0 || T > kMaxT) return COLI_ESHAPE;
+  if (fmt != COLI_FMT_INT4_G64 && fmt != COLI_FMT_INT3_G64 && fmt != COLI_FMT_MXFP4 &&
+      fmt != COLI_FMT_FP8_E4M3_B128)
+    return COLI_EINVAL;
+  if (fmt == COLI_FMT_FP8_E4M3_B128 && I % 16 != 0) return COLI_ESHAPE;  // 16-byte rows
+  if (!aligned_to(x, 4) || !aligned_to(y, 4) || !aligned_to(scales, 4) ||
+      !aligned_to(packed, fmt == COLI_FMT_INT3_G64 ? 8 : 16))
+    return COLI_EALIGN;
+  if (T == 0) return COLI_OK;
+  MatvecArgs a;
+  a.packed = reinterpret_cast<const uint8_t *>(packed);
+  a.scales = scales;
+  a.O = O;
+  a.I = int(I);
+  a.x = x;
+  a.y = y;
+  int cw;
+  switch (fmt) {
+    case COLI_FMT_FP8_E4M3_B128:
+      cw = 16;
+      a.row_bytes = I;
+      a.scale_cols = int(cdiv(I, 128));
+      break;
+    case COLI_FMT_MXFP4:
+      cw = 32;
+      a.row_bytes = 16 * cdiv(I, 32);
+      a.scale_cols = int(cdiv(I, 32));
+      break;
+    case COLI_FMT_INT3_G64:
+      cw = 64;
+      a.row_bytes = 24 * cdiv(I, 64);
+      a.scale_cols = int(cdiv(I, 64));
+      break;
+    default:
+      cw = 64;
+      a.row_bytes = 32 * cdiv(I, 64);
+      a.scale_cols = int(cdiv(I, 64));
+      break;
+  }
+  a.chunks = int(cdiv(I, cw));
+  a.ldx = a.chunks * cw;
+  if (int64_t(T) * a.ldx > kXFloats) return COLI_ESHAPE;
+  const size_t lds = size_t(T) * a.ldx * 4 + size_t(T) * a.chunks * 4;
+  const int64_t groups = (O + kRows - 1) / kRows;
+  const int64_t want = cdiv(groups, 4);
+  const int grid = int(want < 1024 ? want : 1024);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (fmt) {
+    case COLI_FMT_FP8_E4M3_B128:
+      allow_lds<COLI_FMT_FP8_E4M3_B128>();
+      e = launch_matvec_t<COLI_FMT_FP8_E4M3_B128>(a, T, lds, grid, s);
+      break;
+    case COLI_FMT_MXFP4:
+      allow_lds<COLI_FMT_MXFP4>();
+      e = launch_matvec_t<COLI_FMT_MXFP4>(a, T, lds, grid, s);
+      break;
+    case COLI_FMT_INT3_G64:
+      allow_lds<COLI_FMT_INT3_G64>();
+      e = launch_matvec_t<COLI_FMT_INT3_G64>(a, T, lds, grid, s);
+      break;
+    default:
+      allow_lds<COLI_FMT_INT4_G64>();
+      e = launch_matvec_t<COLI_FMT_INT4_G64>(a, T, lds, grid, s);
+      break;
+  }
+  return e == hipSuccess ? COLI_OK : COLI_EDEVICE;
+}
+
+}  // extern "C"

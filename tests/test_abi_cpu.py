@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_strerror_covers_codes():
-    for c in range(-9, 1):
+    for c in range(-10, 1):
         assert coli.lib.coli_strerror(c)
     assert coli.lib.coli_strerror(-99) == b"unknown status"
 
@@ -209,6 +209,50 @@ def test_two_phase_rejects_before_launch():
                              0, (1 << 23) + 2)
     assert route(layer=sm) == coli.COLI_EALIGN
     assert experts(layer=sm) == coli.COLI_EALIGN
+
+
+def test_format_bytes_and_inference_match_the_oracle():
+    """The registry's byte arithmetic and inference from byte counts are host code:
+    they must agree with the oracle on every shape, including the ambiguous ones."""
+    from oracle import formats as F
+    rng = __import__("numpy").random.default_rng(11)
+    shapes = [(2048, 6144), (6144, 2048), (1, 1), (1, 100), (10, 64), (3, 128), (72, 200),
+              (129, 257), (1000, 330), (65536, 128)]
+    shapes += [(int(rng.integers(1, 5000)), int(rng.integers(1, 9000))) for _ in range(200)]
+    for O, I in shapes:
+        for fmt in range(9):
+            want = F.sizes(fmt, O, I)
+            if want is None:
+                with pytest.raises(coli.ColiError):
+                    coli.coli_fmt_bytes(fmt, O, I)
+                continue
+            assert coli.coli_fmt_bytes(fmt, O, I) == want
+            assert coli.coli_resolve_fmt(O, I, *want) == F.resolve(O, I, *want)
+        assert coli.coli_resolve_fmt(O, I, 7, 3) == (None, [])
+    assert coli.lib.coli_resolve_fmt(0, 5, 0, 0, None) == coli.COLI_ESHAPE
+    assert coli.coli_resolve_fmt(10, 64, 320, 40) == (None, [2, 4])
+
+
+def test_format_calls_reject_before_launch():
+    L = coli.lib
+    a = P(1 << 20)
+    assert L.coli_quant_fmt(5, None, 4, 64, a, a, None, None) == coli.COLI_EINVAL
+    assert L.coli_quant_fmt(6, a, 4, 64, a, a, None, None) == coli.COLI_EINVAL
+    assert L.coli_quant_fmt(1, a, 4, 64, a, a, None, None) == coli.COLI_EINVAL
+    assert L.coli_quant_fmt(5, a, 0, 64, a, a, None, None) == coli.COLI_ESHAPE
+    assert L.coli_quant_fmt(5, a, 4, 65537, a, a, None, None) == coli.COLI_ESHAPE
+    assert L.coli_quant_fmt(5, a, 4, 64, P((1 << 20) + 4), a, None, None) == coli.COLI_EALIGN
+    assert L.coli_quant_fmt(7, P((1 << 20) + 2), 4, 64, a, a, None, None) == coli.COLI_EALIGN
+
+    def mv(fmt=7, O=16, I=6144, x=a, T=1, y=a, pk=a):
+        return L.coli_matvec_fmt(fmt, pk, a, O, I, x, T, y, None)
+    assert mv(x=None) == coli.COLI_EINVAL
+    assert mv(fmt=6) == coli.COLI_EINVAL and mv(fmt=0) == coli.COLI_EINVAL
+    assert mv(T=9) == coli.COLI_ESHAPE and mv(T=-1) == coli.COLI_ESHAPE
+    assert mv(T=5) == coli.COLI_ESHAPE  # 5 x 6144 floats exceed the x stage
+    assert mv(fmt=8, I=100) == coli.COLI_ESHAPE  # fp8 rows must be 16-byte multiples
+    assert mv(pk=P((1 << 20) + 8)) == coli.COLI_EALIGN
+    assert mv(T=0, x=None, y=None) == coli.COLI_OK
 
 
 def test_rmsnorm_rejects():

@@ -1,0 +1,185 @@
+"""GPU parity of the sibling weight formats against the oracle (oracle/formats.py):
+
+* coli_quant_fmt bit-exact (packed bytes and scale bits) for int3-g64, MXFP4 and
+  fp8-e4m3-b128: N(0, 0.02) weights of the decode layer's shapes and ragged ones,
+  rows scaled over many binades, exact ties, all-zero groups, and non-finite
+  inputs (NaN scale, neutral codes, status bit 1);
+* coli_matvec_fmt against the oracle's fp64 product on the ORACLE's packed bytes
+  (never the kernel's own), for T = 1..8, including every code of each element
+  format (checks the hardware conversions the kernels use), with the per-token bar
+  max|gpu - oracle| <= 2e-5 * rms(oracle y[t]) for the float element formats and
+  1e-4 for the offset-integer ones (their kernels take sum u x - 8 sum x (4 for
+  int3) per group: fp32 cancellation of about one decimal digit), next to the
+  decode tolerance 2e-3 * max(1, rms).
+Page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战", section 权重转换 (the
+registry); OCP MX v1.0 and OCP FP8 for the element formats.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from tests.harness import log
+
+pytestmark = pytest.mark.gpu
+
+FMTS = (5, 7, 8)
+NAMES = {4: "int4-g64", 5: "int3-g64", 7: "mxfp4", 8: "fp8-e4m3-b128"}
+TIGHT = {4: 1e-4, 5: 1e-4, 7: 2e-5, 8: 2e-5}
+
+
+def weights(O, I, seed, spread=False):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((O, I)) * 0.02).astype(np.float32)
+    if spread:  # rows over many binades
+        w *= (2.0 ** rng.integers(-30, 30, size=(O, 1))).astype(np.float32)
+    return w
+
+
+def gpu_quant(fmt, w, status=None):
+    import int4_grouped_expert_amd as coli
+    O, I = w.shape
+    nw, ns = coli.coli_fmt_bytes(fmt, O, I)
+    pk = torch.zeros(max(nw, 16), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros(max(ns, 16), dtype=torch.uint8, device="cuda")
+    coli.coli_quant_fmt(fmt, torch.from_numpy(w).cuda(), pk, sc, status=status)
+    torch.cuda.synchronize()
+    return pk[:nw].cpu().numpy(), sc[:ns].cpu().numpy()
+
+
+def oracle_bytes(fmt, w):
+    pk, sc = F.quant(fmt, w)
+    return np.ascontiguousarray(pk).reshape(-1).view(np.uint8), \
+        np.ascontiguousarray(sc).reshape(-1).view(np.uint8)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("O,I,spread", [(2048, 6144, False), (6144, 2048, False),
+                                        (72, 200, True), (130, 1000, True), (3, 17, False)])
+def test_quant_bit_exact(fmt, O, I, spread):
+    if fmt == 8 and O * I > 4_000_000:
+        O = 512  # the fp8 tiles of a 2048-row matrix are 128 rows apart: a slab is enough
+    log(f"quant {NAMES[fmt]} O {O} I {I} spread {spread}")
+    w = weights(O, I, 1000 * fmt + O + I, spread)
+    g_pk, g_sc = gpu_quant(fmt, w)
+    o_pk, o_sc = oracle_bytes(fmt, w)
+    assert np.array_equal(g_sc, o_sc), "scales differ"
+    bad = np.nonzero(g_pk != o_pk)[0]
+    assert bad.size == 0, f"{bad.size} packed bytes differ, first at {bad[:5]}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quant_special_values(fmt):
+    # ties of each rounding, exact grid values, zero groups, tiny and huge rows
+    O, I = 256, 256
+    w = weights(O, I, 7 + fmt)
+    w[0, :] = 0.0
+    if fmt == 5:  # s = 1: quotients on the half-integers
+        w[1, :64] = np.tile(np.array([3.0, -3.0, 0.5, 1.5, 2.5, -2.5, -3.5, -0.5],
+                                     np.float32), 8)
+    if fmt == 7:  # X = 1: the E2M1 midpoints
+        w[1, :32] = np.tile(np.array([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0],
+                                     np.float32), 4)
+    if fmt == 8:  # s = 1: every E4M3 value and midpoint of the first tile's row 1
+        vals = np.concatenate([F.E4M3, (F.E4M3[1:] + F.E4M3[:-1]) / 2])
+        w[1, :128] = vals[:128].astype(np.float32)
+        w[1, 127] = 448.0
+        w[2:128, :128] = 0.0
+    w[3, :] *= np.float32(2.0 ** -100)
+    w[4, :] *= np.float32(2.0 ** 100)
+    g_pk, g_sc = gpu_quant(fmt, w)
+    o_pk, o_sc = oracle_bytes(fmt, w)
+    assert np.array_equal(g_sc, o_sc)
+    assert np.array_equal(g_pk, o_pk)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quant_non_finite(fmt):
+    import int4_grouped_expert_amd as coli
+    w = weights(200, 300, 9)
+    w[5, 70] = np.nan
+    w[150, 299] = -np.inf
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g_pk, g_sc = gpu_quant(fmt, w, status=st)
+    assert int(st.item()) & coli.COLI_STATUS_NONFINITE
+    o_pk, o_sc = oracle_bytes(fmt, w)
+    if fmt == 7:
+        assert np.array_equal(g_sc, o_sc)
+    else:  # NaN scales: compare the bit patterns' NaN-ness and the rest exactly
+        gs, os_ = g_sc.view(np.float32), o_sc.view(np.float32)
+        assert np.array_equal(np.isnan(gs), np.isnan(os_)) and np.isnan(os_).any()
+        assert np.array_equal(gs[~np.isnan(os_)], os_[~np.isnan(os_)])
+    assert np.array_equal(g_pk, o_pk)
+    st.zero_()
+    gpu_quant(fmt, weights(64, 64, 10), status=st)
+    assert int(st.item()) == 0
+
+
+def gpu_matvec(fmt, pk, sc, O, I, x):
+    import int4_grouped_expert_amd as coli
+    pk_d = torch.from_numpy(np.ascontiguousarray(pk).reshape(-1).view(np.uint8).copy()).cuda()
+    sc_d = torch.from_numpy(np.ascontiguousarray(sc).reshape(-1).view(np.uint8).copy()).cuda()
+    x_d = torch.from_numpy(x).cuda()
+    y = torch.full((x.shape[0], O), float("nan"), dtype=torch.float32, device="cuda")
+    coli.coli_matvec_fmt(fmt, pk_d, sc_d, O, I, x_d, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def check(yg, yr, what, tight):
+    rms = np.sqrt(np.mean(yr * yr, axis=1, keepdims=True))
+    err = np.abs(yg - yr).max(axis=1, keepdims=True)
+    worst = float((err / np.maximum(rms, 1e-300)).max())
+    log(f"[parity] matvec {what}: worst token err/rms {worst:.3e}; bar/rms {tight}")
+    assert worst <= tight, what
+    assert float((err / np.maximum(1.0, rms)).max()) <= 2e-3
+
+
+@pytest.mark.parametrize("fmt", (4,) + FMTS)
+@pytest.mark.parametrize("O,I,T", [(2048, 6144, 1), (6144, 2048, 1), (2048, 6144, 4),
+                                   (300, 2048, 8), (70, 200, 3), (129, 1000, 2),
+                                   (5, 64, 1)])
+def test_matvec_parity(fmt, O, I, T):
+    if fmt == 8 and I % 16:
+        I = (I + 15) // 16 * 16
+    log(f"matvec {NAMES[fmt]} O {O} I {I} T {T}")
+    w = weights(O, I, 31 * O + I + fmt, spread=O < 200)
+    if fmt == 4:
+        import oracle
+        pk, sc, _ = oracle.quant_int4_g64(w)
+        W = oracle.dequant_int4_g64(pk, sc, I)
+    else:
+        pk, sc = F.quant(fmt, w)
+        W = F.dequant(fmt, pk, sc, O, I)
+    x = np.random.default_rng(O + T).standard_normal((T, I)).astype(np.float32)
+    yr = F.matvec(W, x)
+    yg = gpu_matvec(fmt, pk, sc, O, I, x)
+    check(yg, yr, f"{NAMES[fmt]} O {O} I {I} T {T}", TIGHT[fmt])
+
+
+@pytest.mark.parametrize("fmt", (7, 8))
+def test_matvec_every_code(fmt):
+    """One-hot x reads single weights back: every code of the element format,
+    both signs, decodes as the oracle says (the kernels use the gfx950
+    conversion instructions)."""
+    O, I = 16, 256
+    if fmt == 8:
+        codes = np.arange(256, dtype=np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0  # the NaN codes are never produced
+        pk = np.zeros((O, I), np.uint8)
+        pk[0, :] = codes
+        pk[1, :] = codes[::-1]
+        sc = np.full((1, 2), 0.5, np.float32)
+    else:
+        nib = np.arange(16, dtype=np.uint8)
+        row = np.tile(nib, I // 16)
+        pk = np.zeros((O, I // 2), np.uint8)
+        pk[0, :] = (row[0::2] | (row[1::2] << 4)).astype(np.uint8)
+        pk[1, :] = (row[1::2] | (row[0::2] << 4)).astype(np.uint8)
+        sc = np.full((O, I // 32), 127, np.uint8)
+        sc[:, 3] = 120
+    W = F.dequant(fmt, pk, sc, O, I)
+    for start in range(0, I, 8):
+        xs = np.eye(I, dtype=np.float32)[start:start + 8]
+        yg = gpu_matvec(fmt, pk, sc, O, I, xs)
+        assert np.array_equal(yg, F.matvec(W, xs)), f"codes {start}..{start + 7}"
