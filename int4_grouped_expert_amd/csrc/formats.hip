@@ -25,10 +25,10 @@
 // neutral codes, and the status flag bit 1 is raised.
 //
 // The matrix-vector product streams each row's bytes once with 16-byte (8-byte
-// for int3) loads; x sits in LDS; a wave works on four rows at a time so that
-// each x value read from LDS serves four rows; the per-chunk (= per scale) sums
-// are scaled once; every lane reduces in a fixed order, so results are
-// deterministic.
+// for int3) loads, one chunk ahead; x sits in LDS; a wave works on four or
+// eight rows at a time so that each x value read from LDS serves them all; the
+// per-chunk (= per scale) sums are scaled once; every lane reduces in a fixed
+// order, so results are deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,7 +41,6 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxT = 8;
-constexpr int kRows = 4;         // rows per wave step
 constexpr int kXFloats = 24576;  // T * padded I: 96 KiB of LDS
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -274,81 +273,101 @@ __device__ inline uint32_t int3_bytes(const uint32_t (&v)[6], int m) {
   return out;
 }
 
-// sum_k code_k * x_k over the chunk (code in the format's own units), for T
-// tokens; x at xs + t * ldx.
-template <int FMT, int T>
-__device__ inline void chunk_dot(const Raw<FMT> &r, const float *xs, int ldx, float (&d)[T]) {
+// Codes of the chunk as floats, piece by piece (4 or 8 weights), in the
+// format's own units (E2M1 / E4M3 values, or the unsigned integer codes).
+template <int FMT>
+struct Piece;
+template <>
+struct Piece<COLI_FMT_FP8_E4M3_B128> {  // 4 pieces of 4 weights
+  static constexpr int kN = 4, kW = 4;
+  __device__ static void get(const Raw<COLI_FMT_FP8_E4M3_B128> &r, int q, float (&f)[4]) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(r.v[q], false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(r.v[q], true);
+    f[0] = a.x;
+    f[1] = a.y;
+    f[2] = b.x;
+    f[3] = b.y;
+  }
+  __device__ static int xoff(int q, int k) { return 4 * q + k; }
+};
+template <>
+struct Piece<COLI_FMT_MXFP4> {  // 4 pieces of 8 weights
+  static constexpr int kN = 4, kW = 8;
+  __device__ static void get(const Raw<COLI_FMT_MXFP4> &r, int q, float (&f)[8]) {
+    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 0);
+    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 1);
+    const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 2);
+    const f32x2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 3);
+    f[0] = a.x;
+    f[1] = a.y;
+    f[2] = b.x;
+    f[3] = b.y;
+    f[4] = c.x;
+    f[5] = c.y;
+    f[6] = e.x;
+    f[7] = e.y;
+  }
+  __device__ static int xoff(int q, int k) { return 8 * q + k; }
+};
+template <>
+struct Piece<COLI_FMT_INT3_G64> {  // 16 pieces of 4 weights
+  static constexpr int kN = 16, kW = 4;
+  __device__ static void get(const Raw<COLI_FMT_INT3_G64> &r, int m, float (&f)[4]) {
+    const uint32_t u = int3_bytes(r.v, m);
+    f[0] = ubyte<0>(u);
+    f[1] = ubyte<1>(u);
+    f[2] = ubyte<2>(u);
+    f[3] = ubyte<3>(u);
+  }
+  __device__ static int xoff(int m, int k) { return 4 * m + k; }
+};
+template <>
+struct Piece<COLI_FMT_INT4_G64> {  // 8 pieces of 8 weights: 4 low nibbles (k..k+3), 4 high (k+32..)
+  static constexpr int kN = 8, kW = 8;
+  __device__ static void get(const Raw<COLI_FMT_INT4_G64> &r, int q, float (&f)[8]) {
+    const uint32_t lo = r.v[q] & 0x0F0F0F0Fu, hi = (r.v[q] >> 4) & 0x0F0F0F0Fu;
+    f[0] = ubyte<0>(lo);
+    f[1] = ubyte<1>(lo);
+    f[2] = ubyte<2>(lo);
+    f[3] = ubyte<3>(lo);
+    f[4] = ubyte<0>(hi);
+    f[5] = ubyte<1>(hi);
+    f[6] = ubyte<2>(hi);
+    f[7] = ubyte<3>(hi);
+  }
+  __device__ static int xoff(int q, int k) { return k < 4 ? 4 * q + k : 32 + 4 * q + (k - 4); }
+};
+
+// d[r][t] = sum_k code[r]_k * x[t]_k over one chunk of R rows: each piece of x
+// is read from LDS once and serves the R rows.
+template <int FMT, int T, int R>
+__device__ inline void chunk_dot_rows(const Raw<FMT> (&raw)[R], const float *xs, int ldx,
+                                      float (&d)[R][T]) {
+  using P = Piece<FMT>;
 #pragma unroll
-  for (int t = 0; t < T; ++t) d[t] = 0.0f;
-  if constexpr (FMT == COLI_FMT_FP8_E4M3_B128) {
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(r.v[q], false);
-      const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(r.v[q], true);
+    for (int t = 0; t < T; ++t) d[r][t] = 0.0f;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float4 x = *reinterpret_cast<const float4 *>(xs + t * ldx + 4 * q);
-        d[t] = fmaf(a.x, x.x, fmaf(a.y, x.y, fmaf(b.x, x.z, fmaf(b.y, x.w, d[t]))));
+  for (int q = 0; q < P::kN; ++q) {
+    float f[R][P::kW];
+#pragma unroll
+    for (int r = 0; r < R; ++r) P::get(raw[r], q, f[r]);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float x[P::kW];
+#pragma unroll
+      for (int k = 0; k < P::kW; k += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(xs + t * ldx + P::xoff(q, k));
+        x[k] = v.x;
+        x[k + 1] = v.y;
+        x[k + 2] = v.z;
+        x[k + 3] = v.w;
       }
-    }
-  } else if constexpr (FMT == COLI_FMT_MXFP4) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 0);
-      const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 1);
-      const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 2);
-      const f32x2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v[q], 1.0f, 3);
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(xs + t * ldx + 8 * q);
-        const float4 x1 = *reinterpret_cast<const float4 *>(xs + t * ldx + 8 * q + 4);
-        float s = d[t];
-        s = fmaf(a.x, x0.x, s);
-        s = fmaf(a.y, x0.y, s);
-        s = fmaf(b.x, x0.z, s);
-        s = fmaf(b.y, x0.w, s);
-        s = fmaf(c.x, x1.x, s);
-        s = fmaf(c.y, x1.y, s);
-        s = fmaf(e.x, x1.z, s);
-        s = fmaf(e.y, x1.w, s);
-        d[t] = s;
-      }
-    }
-  } else if constexpr (FMT == COLI_FMT_INT3_G64) {
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const uint32_t u = int3_bytes(r.v, m);
-      const float u0 = ubyte<0>(u), u1 = ubyte<1>(u);
-      const float u2 = ubyte<2>(u), u3 = ubyte<3>(u);
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float4 x = *reinterpret_cast<const float4 *>(xs + t * ldx + 4 * m);
-        d[t] = fmaf(u0, x.x, fmaf(u1, x.y, fmaf(u2, x.z, fmaf(u3, x.w, d[t]))));
-      }
-    }
-  } else {  // int4-g64 planar: byte k holds element k (low) and k + 32 (high)
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t lo = r.v[q] & 0x0F0F0F0Fu, hi = (r.v[q] >> 4) & 0x0F0F0F0Fu;
-      const float l0 = ubyte<0>(lo), l1 = ubyte<1>(lo);
-      const float l2 = ubyte<2>(lo), l3 = ubyte<3>(lo);
-      const float h0 = ubyte<0>(hi), h1 = ubyte<1>(hi);
-      const float h2 = ubyte<2>(hi), h3 = ubyte<3>(hi);
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float4 xl = *reinterpret_cast<const float4 *>(xs + t * ldx + 4 * q);
-        const float4 xh = *reinterpret_cast<const float4 *>(xs + t * ldx + 32 + 4 * q);
-        float s = d[t];
-        s = fmaf(l0, xl.x, s);
-        s = fmaf(l1, xl.y, s);
-        s = fmaf(l2, xl.z, s);
-        s = fmaf(l3, xl.w, s);
-        s = fmaf(h0, xh.x, s);
-        s = fmaf(h1, xh.y, s);
-        s = fmaf(h2, xh.z, s);
-        s = fmaf(h3, xh.w, s);
-        d[t] = s;
-      }
+        for (int k = 0; k < P::kW; ++k) d[r][t] = fmaf(f[r][k], x[k], d[r][t]);
     }
   }
 }
@@ -365,20 +384,80 @@ struct MatvecArgs {
   float *y;
 };
 
-// y[t, o] = sum_i W^[o, i] x[t, i].  A wave takes four rows at a time; lane l
-// takes the row chunks l, l + 64, ...; the per-chunk dot products are scaled
-// by the chunk's scale (and, for the offset formats, corrected by the chunk's
-// x sum times the code offset), then reduced over the wave.
+// The scale of chunk c of row o0 + rr as a float (E8M0 decoded; 255 is NaN).
+// o0 is wave-uniform and a multiple of the rows per step (4 or 8), so an fp8
+// group of rows never straddles a 128-row tile.
+template <int FMT>
+__device__ inline float chunk_scale(const MatvecArgs &a, int64_t o0, int rr, int c) {
+  constexpr int CW = Chunk<FMT>::kW;
+  if constexpr (FMT == COLI_FMT_FP8_E4M3_B128) {
+    const float *base = reinterpret_cast<const float *>(a.scales) + (o0 >> 7) * a.scale_cols;
+    return base[(c * CW) >> 7];
+  } else if constexpr (FMT == COLI_FMT_MXFP4) {
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(a.scales) + o0 * a.scale_cols;
+    const uint32_t E = base[uint32_t(rr * a.scale_cols + c)];
+    return E == 255u ? __builtin_nanf("")
+                     : (E ? __uint_as_float(E << 23) : __uint_as_float(0x00400000u));
+  } else {
+    const float *base = reinterpret_cast<const float *>(a.scales) + o0 * a.scale_cols;
+    return base[uint32_t(rr * a.scale_cols + c)];
+  }
+}
+
+// Rows per wave step: eight for fp8 at T <= 2 (16 weights per 16-byte chunk),
+// else four (the register budget of the wider chunks).
+template <int FMT, int T>
+constexpr int rows_per_step() {
+  return (FMT == COLI_FMT_FP8_E4M3_B128 && T <= 2) ? 8 : 4;
+}
+
+// y[t, o] = sum_i W^[o, i] x[t, i].  A wave takes R rows at a time; lane l
+// takes the row chunks l, l + 64, ... (kc steps, the same count on every lane;
+// lanes past the row's end re-read its last chunk and add nothing).  The
+// next step's chunks and scales are loaded before the current step is
+// computed.  Per-chunk dot products are scaled by the chunk's scale (and, for
+// the offset formats, corrected by the chunk's x sum times the code offset),
+// then reduced over the wave.
 template <int FMT, int T>
 __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
   constexpr int CW = Chunk<FMT>::kW, CB = Chunk<FMT>::kBytes;
+  constexpr int R = rows_per_step<FMT, T>();
   constexpr bool kOffset = FMT == COLI_FMT_INT3_G64 || FMT == COLI_FMT_INT4_G64;
   constexpr float kOff = FMT == COLI_FMT_INT3_G64 ? 4.0f : 8.0f;
   extern __shared__ float xs[];  // [T][ldx], then the chunk sums [T][chunks]
   float *xsum = xs + T * a.ldx;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t groups = (a.O + R - 1) / R;
+  const int64_t gstride = int64_t(gridDim.x) * 4;
+  const int kc = (a.chunks + 63) / 64;
+  int64_t g = int64_t(blockIdx.x) * 4 + wave;
+  int k = 0;
+
+  Raw<FMT> cur[R], nxt[R];
+  float csc[R], nsc[R];
+  // Loads of step (gg, kk): a wave-uniform 64-bit base for the group's first
+  // row, 32-bit offsets for the rows (clamped to the last row: rows past the
+  // end are re-read, never stored) and the chunk (clamped to the row's last
+  // chunk on lanes past the row's end).
+  auto fetch = [&](int64_t gg, int kk, Raw<FMT>(&dst)[R], float(&sc)[R]) {
+    const int64_t o0 = gg * R;
+    const uint8_t *base = a.packed + o0 * a.row_bytes;
+    const int last = int(a.O - 1 - o0);  // rows of the group that exist: r <= last
+    const int c0 = lane + 64 * kk;
+    const int c = c0 < a.chunks ? c0 : a.chunks - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int rr = r < last ? r : last;
+      dst[r] = load_chunk<FMT>(base + uint32_t(rr * int(a.row_bytes) + c * CB));
+      sc[r] = chunk_scale<FMT>(a, o0, rr, c);
+    }
+  };
+  // the first weights are in flight while x is staged
+  if (g < groups) fetch(g, 0, cur, csc);
+
   for (int i = threadIdx.x; i < T * a.ldx; i += 256) {
-    const int t = i / a.ldx, k = i - t * a.ldx;
-    xs[i] = k < a.I ? a.x[size_t(t) * a.I + k] : 0.0f;
+    const int t = i / a.ldx, kx = i - t * a.ldx;
+    xs[i] = kx < a.I ? a.x[size_t(t) * a.I + kx] : 0.0f;
   }
   __syncthreads();
   if constexpr (kOffset) {
@@ -386,72 +465,80 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
       const int t = i / a.chunks, c = i - t * a.chunks;
       const float *p = xs + t * a.ldx + c * CW;
       float s = 0.0f;
-      for (int k = 0; k < CW; ++k) s += p[k];  // fixed order
+      for (int j = 0; j < CW; ++j) s += p[j];  // fixed order
       xsum[i] = s;
     }
     __syncthreads();
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t groups = (a.O + kRows - 1) / kRows;
-  for (int64_t g = int64_t(blockIdx.x) * 4 + wave; g < groups; g += int64_t(gridDim.x) * 4) {
-    int64_t row[kRows];
+  if (g >= groups) return;
+
+  float acc[R][T];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const int64_t o = g * kRows + r;
-      row[r] = o < a.O ? o : a.O - 1;  // past the end: re-read the last row, never stored
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[r][t] = 0.0f;
+  while (true) {
+    int64_t g2 = g;
+    int k2 = k + 1;
+    if (k2 == kc) {
+      k2 = 0;
+      g2 += gstride;
     }
-    float acc[kRows][T];
+    const bool more = g2 < groups;
+    // past the last step: load the current step again (valid addresses, unused)
+    fetch(more ? g2 : g, more ? k2 : k, nxt, nsc);
+    const int c0 = lane + 64 * k;
+    const bool valid = c0 < a.chunks;
+    const int c = valid ? c0 : a.chunks - 1;
+    {
+      float d[R][T];
+      chunk_dot_rows<FMT, T, R>(cur, xs + c * CW, a.ldx, d);
 #pragma unroll
-    for (int r = 0; r < kRows; ++r)
-#pragma unroll
-      for (int t = 0; t < T; ++t) acc[r][t] = 0.0f;
-    for (int c = lane; c < a.chunks; c += 64) {
-      Raw<FMT> raw[kRows];
-#pragma unroll
-      for (int r = 0; r < kRows; ++r)
-        raw[r] = load_chunk<FMT>(a.packed + row[r] * a.row_bytes + int64_t(c) * CB);
-      float sc[kRows];
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        if constexpr (FMT == COLI_FMT_FP8_E4M3_B128) {
-          sc[r] = reinterpret_cast<const float *>(a.scales)[(row[r] >> 7) * a.scale_cols +
-                                                            ((c * CW) >> 7)];
-        } else if constexpr (FMT == COLI_FMT_MXFP4) {
-          const uint32_t E = reinterpret_cast<const uint8_t *>(a.scales)[row[r] * a.scale_cols + c];
-          sc[r] = E == 255u ? __builtin_nanf("")
-                            : (E ? __uint_as_float(E << 23) : __uint_as_float(0x00400000u));
-        } else {
-          sc[r] = reinterpret_cast<const float *>(a.scales)[row[r] * a.scale_cols + c];
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        float d[T];
-        chunk_dot<FMT, T>(raw[r], xs + c * CW, a.ldx, d);
+      for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          if constexpr (kOffset) d[t] = fmaf(-kOff, xsum[t * a.chunks + c], d[t]);
-          acc[r][t] = fmaf(sc[r], d[t], acc[r][t]);
+          float v = d[r][t];
+          if constexpr (kOffset) v = fmaf(-kOff, xsum[t * a.chunks + c], v);
+          v = csc[r] * v;
+          acc[r][t] += valid ? v : 0.0f;
         }
-      }
     }
+    if (k == kc - 1) {
 #pragma unroll
-    for (int r = 0; r < kRows; ++r)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float v = wave_sum(acc[r][t]);
-        const int64_t o = g * kRows + r;
-        if (lane == r * T + t && o < a.O) a.y[size_t(t) * a.O + o] = v;
-      }
+        for (int t = 0; t < T; ++t) {
+          const float v = wave_sum(acc[r][t]);
+          acc[r][t] = 0.0f;
+          const int64_t o = g * R + r;
+          if (lane == (r * T + t) % 64 && o < a.O) a.y[size_t(t) * a.O + o] = v;
+        }
+    }
+    if (!more) break;
+    g = g2;
+    k = k2;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      cur[r] = nxt[r];
+      csc[r] = nsc[r];
+    }
   }
 }
 
+template <int FMT, int T>
+int matvec_grid(int64_t O) {
+  const int64_t groups = (O + rows_per_step<FMT, T>() - 1) / rows_per_step<FMT, T>();
+  const int64_t want = cdiv(groups, 4);
+  return int(want < 1024 ? want : 1024);
+}
+
 template <int FMT>
-hipError_t launch_matvec_t(const MatvecArgs &a, int T, size_t lds, int grid, hipStream_t s) {
+hipError_t launch_matvec_t(const MatvecArgs &a, int T, size_t lds, hipStream_t s) {
   switch (T) {
-#define COLI_MV_CASE(TT)                                                            \
-  case TT:                                                                          \
-    hipLaunchKernelGGL((matvec_kernel<FMT, TT>), dim3(grid), dim3(256), lds, s, a); \
+#define COLI_MV_CASE(TT)                                                               \
+  case TT:                                                                             \
+    hipLaunchKernelGGL((matvec_kernel<FMT, TT>), dim3(matvec_grid<FMT, TT>(a.O)), dim3(256), \
+                       lds, s, a);                                                     \
     break;
     COLI_MV_CASE(1)
     COLI_MV_CASE(2)
@@ -620,27 +707,24 @@ int coli_matvec_fmt(int fmt, const void *packed, const void *scales, int64_t O, 
   a.ldx = a.chunks * cw;
   if (int64_t(T) * a.ldx > kXFloats) return COLI_ESHAPE;
   const size_t lds = size_t(T) * a.ldx * 4 + size_t(T) * a.chunks * 4;
-  const int64_t groups = (O + kRows - 1) / kRows;
-  const int64_t want = cdiv(groups, 4);
-  const int grid = int(want < 1024 ? want : 1024);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   switch (fmt) {
     case COLI_FMT_FP8_E4M3_B128:
       allow_lds<COLI_FMT_FP8_E4M3_B128>();
-      e = launch_matvec_t<COLI_FMT_FP8_E4M3_B128>(a, T, lds, grid, s);
+      e = launch_matvec_t<COLI_FMT_FP8_E4M3_B128>(a, T, lds, s);
       break;
     case COLI_FMT_MXFP4:
       allow_lds<COLI_FMT_MXFP4>();
-      e = launch_matvec_t<COLI_FMT_MXFP4>(a, T, lds, grid, s);
+      e = launch_matvec_t<COLI_FMT_MXFP4>(a, T, lds, s);
       break;
     case COLI_FMT_INT3_G64:
       allow_lds<COLI_FMT_INT3_G64>();
-      e = launch_matvec_t<COLI_FMT_INT3_G64>(a, T, lds, grid, s);
+      e = launch_matvec_t<COLI_FMT_INT3_G64>(a, T, lds, s);
       break;
     default:
       allow_lds<COLI_FMT_INT4_G64>();
-      e = launch_matvec_t<COLI_FMT_INT4_G64>(a, T, lds, grid, s);
+      e = launch_matvec_t<COLI_FMT_INT4_G64>(a, T, lds, s);
       break;
   }
   return e == hipSuccess ? COLI_OK : COLI_EDEVICE;
