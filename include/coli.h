@@ -55,7 +55,9 @@ enum {
     COLI_EDEVICE = -6,    /* the HIP runtime reported a launch error */
     COLI_ESCRATCH = -7,   /* the call needs more than the no-alloc scratch holds */
     COLI_EUSAGE = -8,     /* a routing history refused (geometry, version, identity) */
-    COLI_EIO = -9         /* a routing history file could not be read or written */
+    COLI_EIO = -9,        /* a routing history file could not be read or written */
+    COLI_EFORMAT = -10    /* no registry format, or more than one, has the byte
+                             counts given to coli_resolve_fmt */
 };
 
 typedef enum { COLI_F32 = 0, COLI_BF16 = 1 } coli_dtype;
@@ -470,8 +472,6 @@ typedef enum {
                                 /* tile: s = amax/448                            */
 } coli_fmt;
 
-#define COLI_EFORMAT (-10)         /* no registry format, or more than one, has  */
-                                   /* these byte counts                         */
 #define COLI_FMT_MAX_ROWS 1048576  /* O limit of the format calls               */
 #define COLI_MATVEC_MAX_T 8
 

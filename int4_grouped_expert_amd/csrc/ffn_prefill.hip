@@ -8,10 +8,13 @@
 //
 // Work item = (unit, M-chunk of <= 128 of the unit's tokens, N-tile of 256
 // weight rows).  A unit is a unique routed expert of the batch or the shared
-// expert.  One block of 4 waves (one per SIMD) per CU walks its items; wave w
-// owns 64 weight rows (2 column fragments of 32) and all 32-row M fragments of
-// the chunk, on v_mfma_f32_32x32x16_f16 (on gfx950 the 16x16x32 form needs far
-// more independent accumulators per wave to approach the matrix-core rate).
+// expert.  One block of 8 waves (two per SIMD) per CU walks its items; each
+// wave owns one 32-row weight fragment (gate or up rows of the same 32
+// features; or 32 down rows) and all 32-row M fragments of the chunk, on
+// v_mfma_f32_32x32x16_f16 (on gfx950 the 16x16x32 form needs far more
+// independent accumulators per wave to approach the matrix-core rate).  The
+// two waves on a SIMD share the block's activation stage, so one wave's
+// dequant and exchange VALU work runs beside the other's MFMAs.
 //
 // Weight stream.  A super-step covers 256 k = 4 groups = 128 contiguous bytes
 // of every weight row.  Per 32-row fragment four 16-byte loads per lane, load a
