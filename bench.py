@@ -376,7 +376,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the T=32 and prefill legs")
+    ap.add_argument("--no-extras", action="store_true", help="skip every leg after the T=1 one")
+    ap.add_argument("--legs", default="single,t32,cache,tiny,formats,prefill",
+                    help="comma list of the legs after the T=1 one (default: all)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise kernel (clamp) that reads and writes "
                          "MIB MiB, the reference for scaling HBM byte counters")
@@ -447,7 +449,8 @@ def main():
                                                  "gateup_narrow"),
                      "bytes_per_launch": gu_bytes, "avg_launch_ms": round(gu_ms, 5)},
     }
-    if not args.no_extras:
+    legs = set() if args.no_extras else set(args.legs.split(","))
+    if "single" in legs:
         log("[bench] decode T=1, one replica (its 191 MB fit the 256 MB Infinity Cache)")
         d1 = run_decode(coli, W, layers[:1], 1, 1, max(100, args.steps // 3),
                         min(100, args.warmup))
@@ -458,8 +461,10 @@ def main():
             "tokens_per_s": round(1.0 / (ms1 * 1e-3), 1), "ms_per_step": round(ms1, 5),
             "step_ms": d1["step_ms"],
             "stage_ms": [round(x, 5) for x in d1["stage_ms"]]}
-        log("[bench] decode T=32 zipf")
+    if "t32" in legs or "cache" in legs:
         zl, _ = build_layer_bias(coli, W, layers)
+    if "t32" in legs:
+        log("[bench] decode T=32 zipf")
         d32 = run_decode(coli, W, zl, 2, 32, max(20, args.steps // 10), min(20, args.warmup))
         U32 = d32["u_mean"]
         ms32 = d32["ms"] / d32["steps"]
@@ -472,10 +477,13 @@ def main():
             "gbps": round(b32 / (ms32 * 1e-3) / 1e9, 1),
             "frac": round(b32 / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "stage_ms": [round(s, 4) for s in d32["stage_ms"]]}
+    if "cache" in legs:
         log("[bench] decode T=32 zipf through the HBM expert cache")
         result["expert_cache_t32_zipf"] = run_cache(coli, W, zl[0],
                                                     max(32, min(200, args.steps // 15)), 40)
+    if "t32" in legs or "cache" in legs:
         del zl
+    if "tiny" in legs:
         log("[bench] tiny T=1")
         tl, _ = build_layer(coli, W, 0, 1)
         dt = run_decode(coli, W, tl, 0, 1, max(100, args.steps // 3), min(100, args.warmup))
@@ -486,8 +494,10 @@ def main():
             "us_per_step": round(mst * 1e3, 2), "tokens_per_s": round(1.0 / (mst * 1e-3), 1),
             "stage_us": [round(1e3 * x, 2) for x in dt["stage_ms"]]}
         del tl
+    if "formats" in legs:
         log("[bench] sibling-format matrix-vector products")
         result["formats_matvec_t1"] = run_formats(coli, W)
+    if "prefill" in legs:
         log("[bench] prefill T=2048")
         result["prefill"] = run_prefill(coli, W, layers[0],
                                         steps=max(2, min(10, args.steps // 300)))

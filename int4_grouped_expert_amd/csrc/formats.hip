@@ -257,9 +257,18 @@ __device__ inline Raw<FMT> load_chunk(const uint8_t *p) {
   return r;
 }
 
-// Byte K of u as a float (one v_cvt_f32_ubyteK).
+// Byte K of u as a float: one v_cvt_f32_ubyteK (written out, since the
+// compiler otherwise folds a preceding mask into a bit-field extract plus a
+// conversion).  A plain VALU instruction, no memory access.
 template <int K>
-__device__ inline float ubyte(uint32_t u) { return float((u >> (8 * K)) & 0xFFu); }
+__device__ inline float ubyte(uint32_t u) {
+  float f;
+  if constexpr (K == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(u));
+  else if constexpr (K == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(u));
+  else if constexpr (K == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(u));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(u));
+  return f;
+}
 
 // 4 three-bit codes -> one byte each: bits 4m..4m+3 of the three planes.
 __device__ inline uint32_t int3_bytes(const uint32_t (&v)[6], int m) {
@@ -339,10 +348,15 @@ struct Piece<COLI_FMT_INT4_G64> {  // 8 pieces of 8 weights: 4 low nibbles (k..k
 };
 
 // d[r][t] = sum_k code[r]_k * x[t]_k over one chunk of R rows: each piece of x
-// is read from LDS once and serves the R rows.
+// is read from LDS once and serves the R rows.  x is held piece-major in LDS:
+// float4 piece p (elements 4p .. 4p+3) of chunk c of token t at
+// x4[(t * pieces + p) * chunks + c], so the 64 lanes (64 consecutive chunks)
+// read 64 consecutive float4s, free of bank conflicts.  xc = x4 + c; pstride =
+// chunks.
 template <int FMT, int T, int R>
-__device__ inline void chunk_dot_rows(const Raw<FMT> (&raw)[R], const float *xs, int ldx,
+__device__ inline void chunk_dot_rows(const Raw<FMT> (&raw)[R], const float4 *xc, int pstride,
                                       float (&d)[R][T]) {
+  constexpr int kPieces = Chunk<FMT>::kW / 4;
   using P = Piece<FMT>;
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -358,7 +372,7 @@ __device__ inline void chunk_dot_rows(const Raw<FMT> (&raw)[R], const float *xs,
       float x[P::kW];
 #pragma unroll
       for (int k = 0; k < P::kW; k += 4) {
-        const float4 v = *reinterpret_cast<const float4 *>(xs + t * ldx + P::xoff(q, k));
+        const float4 v = xc[(t * kPieces + P::xoff(q, k) / 4) * pstride];
         x[k] = v.x;
         x[k + 1] = v.y;
         x[k + 2] = v.z;
@@ -384,23 +398,34 @@ struct MatvecArgs {
   float *y;
 };
 
-// The scale of chunk c of row o0 + rr as a float (E8M0 decoded; 255 is NaN).
-// o0 is wave-uniform and a multiple of the rows per step (4 or 8), so an fp8
-// group of rows never straddles a 128-row tile.
+// The raw scale of chunk c of row o0 + rr: the f32 bits, or the E8M0 byte
+// (decoded at use by scale_value, so that the load is not waited for when it
+// is issued).  o0 is wave-uniform and a multiple of the rows per step (4 or
+// 8), so an fp8 group of rows never straddles a 128-row tile.
 template <int FMT>
-__device__ inline float chunk_scale(const MatvecArgs &a, int64_t o0, int rr, int c) {
+__device__ inline uint32_t chunk_scale(const MatvecArgs &a, int64_t o0, int rr, int c) {
   constexpr int CW = Chunk<FMT>::kW;
   if constexpr (FMT == COLI_FMT_FP8_E4M3_B128) {
-    const float *base = reinterpret_cast<const float *>(a.scales) + (o0 >> 7) * a.scale_cols;
+    const uint32_t *base =
+        reinterpret_cast<const uint32_t *>(a.scales) + (o0 >> 7) * a.scale_cols;
     return base[(c * CW) >> 7];
   } else if constexpr (FMT == COLI_FMT_MXFP4) {
     const uint8_t *base = reinterpret_cast<const uint8_t *>(a.scales) + o0 * a.scale_cols;
-    const uint32_t E = base[uint32_t(rr * a.scale_cols + c)];
-    return E == 255u ? __builtin_nanf("")
-                     : (E ? __uint_as_float(E << 23) : __uint_as_float(0x00400000u));
-  } else {
-    const float *base = reinterpret_cast<const float *>(a.scales) + o0 * a.scale_cols;
     return base[uint32_t(rr * a.scale_cols + c)];
+  } else {
+    const uint32_t *base = reinterpret_cast<const uint32_t *>(a.scales) + o0 * a.scale_cols;
+    return base[uint32_t(rr * a.scale_cols + c)];
+  }
+}
+
+// The scale as a float.  E8M0: 2^(E - 127); E = 0 is 2^-127 (an fp32
+// subnormal, bit 22), E = 255 NaN (the exponent field all ones plus bit 22).
+template <int FMT>
+__device__ inline float scale_value(uint32_t raw) {
+  if constexpr (FMT == COLI_FMT_MXFP4) {
+    return __uint_as_float((raw << 23) | ((raw == 0u || raw == 255u) ? 0x00400000u : 0u));
+  } else {
+    return __uint_as_float(raw);
   }
 }
 
@@ -424,7 +449,7 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
   constexpr int R = rows_per_step<FMT, T>();
   constexpr bool kOffset = FMT == COLI_FMT_INT3_G64 || FMT == COLI_FMT_INT4_G64;
   constexpr float kOff = FMT == COLI_FMT_INT3_G64 ? 4.0f : 8.0f;
-  extern __shared__ float xs[];  // [T][ldx], then the chunk sums [T][chunks]
+  extern __shared__ float xs[];  // x piece-major [T][pieces][chunks][4], then the chunk sums [T][chunks]
   float *xsum = xs + T * a.ldx;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t groups = (a.O + R - 1) / R;
@@ -434,12 +459,12 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
   int k = 0;
 
   Raw<FMT> cur[R], nxt[R];
-  float csc[R], nsc[R];
+  uint32_t csc[R], nsc[R];
   // Loads of step (gg, kk): a wave-uniform 64-bit base for the group's first
   // row, 32-bit offsets for the rows (clamped to the last row: rows past the
   // end are re-read, never stored) and the chunk (clamped to the row's last
   // chunk on lanes past the row's end).
-  auto fetch = [&](int64_t gg, int kk, Raw<FMT>(&dst)[R], float(&sc)[R]) {
+  auto fetch = [&](int64_t gg, int kk, Raw<FMT>(&dst)[R], uint32_t(&sc)[R]) {
     const int64_t o0 = gg * R;
     const uint8_t *base = a.packed + o0 * a.row_bytes;
     const int last = int(a.O - 1 - o0);  // rows of the group that exist: r <= last
@@ -455,17 +480,33 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
   // the first weights are in flight while x is staged
   if (g < groups) fetch(g, 0, cur, csc);
 
-  for (int i = threadIdx.x; i < T * a.ldx; i += 256) {
-    const int t = i / a.ldx, kx = i - t * a.ldx;
-    xs[i] = kx < a.I ? a.x[size_t(t) * a.I + kx] : 0.0f;
+  // x -> LDS piece-major (see chunk_dot_rows); the zero padding past I
+  // completes the last chunk
+  constexpr int kPieces = CW / 4;
+  float4 *x4 = reinterpret_cast<float4 *>(xs);
+  for (int i = threadIdx.x; i < T * kPieces * a.chunks; i += 256) {
+    const int c = i % a.chunks, tp = i / a.chunks;
+    const int t = tp / kPieces, pc = tp - t * kPieces;
+    const int k0 = c * CW + 4 * pc;
+    float4 v;
+    v.x = k0 < a.I ? a.x[size_t(t) * a.I + k0] : 0.0f;
+    v.y = k0 + 1 < a.I ? a.x[size_t(t) * a.I + k0 + 1] : 0.0f;
+    v.z = k0 + 2 < a.I ? a.x[size_t(t) * a.I + k0 + 2] : 0.0f;
+    v.w = k0 + 3 < a.I ? a.x[size_t(t) * a.I + k0 + 3] : 0.0f;
+    x4[i] = v;
   }
   __syncthreads();
   if constexpr (kOffset) {
     for (int i = threadIdx.x; i < T * a.chunks; i += 256) {
       const int t = i / a.chunks, c = i - t * a.chunks;
-      const float *p = xs + t * a.ldx + c * CW;
       float s = 0.0f;
-      for (int j = 0; j < CW; ++j) s += p[j];  // fixed order
+      for (int pc = 0; pc < kPieces; ++pc) {  // fixed order
+        const float4 v = x4[(t * kPieces + pc) * a.chunks + c];
+        s += v.x;
+        s += v.y;
+        s += v.z;
+        s += v.w;
+      }
       xsum[i] = s;
     }
     __syncthreads();
@@ -477,7 +518,11 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[r][t] = 0.0f;
-  while (true) {
+  // One step: load the next step's chunks into (nr, ns), then compute the
+  // current one from (cr, cs).  Two buffers alternate, so the next loads stay
+  // in flight for a whole step and no register copy waits for them.
+  auto step = [&](Raw<FMT>(&cr)[R], uint32_t(&cs)[R], Raw<FMT>(&nr)[R],
+                  uint32_t(&ns)[R]) -> bool {
     int64_t g2 = g;
     int k2 = k + 1;
     if (k2 == kc) {
@@ -486,23 +531,21 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
     }
     const bool more = g2 < groups;
     // past the last step: load the current step again (valid addresses, unused)
-    fetch(more ? g2 : g, more ? k2 : k, nxt, nsc);
+    fetch(more ? g2 : g, more ? k2 : k, nr, ns);
     const int c0 = lane + 64 * k;
     const bool valid = c0 < a.chunks;
     const int c = valid ? c0 : a.chunks - 1;
-    {
-      float d[R][T];
-      chunk_dot_rows<FMT, T, R>(cur, xs + c * CW, a.ldx, d);
+    float d[R][T];
+    chunk_dot_rows<FMT, T, R>(cr, x4 + c, a.chunks, d);
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          float v = d[r][t];
-          if constexpr (kOffset) v = fmaf(-kOff, xsum[t * a.chunks + c], v);
-          v = csc[r] * v;
-          acc[r][t] += valid ? v : 0.0f;
-        }
-    }
+      for (int t = 0; t < T; ++t) {
+        float v = d[r][t];
+        if constexpr (kOffset) v = fmaf(-kOff, xsum[t * a.chunks + c], v);
+        v = scale_value<FMT>(cs[r]) * v;
+        acc[r][t] += valid ? v : 0.0f;
+      }
     if (k == kc - 1) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
@@ -514,14 +557,11 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
           if (lane == (r * T + t) % 64 && o < a.O) a.y[size_t(t) * a.O + o] = v;
         }
     }
-    if (!more) break;
     g = g2;
     k = k2;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      cur[r] = nxt[r];
-      csc[r] = nsc[r];
-    }
+    return more;
+  };
+  while (step(cur, csc, nxt, nsc) && step(nxt, nsc, cur, csc)) {
   }
 }
 

@@ -183,3 +183,29 @@ def test_matvec_every_code(fmt):
         xs = np.eye(I, dtype=np.float32)[start:start + 8]
         yg = gpu_matvec(fmt, pk, sc, O, I, xs)
         assert np.array_equal(yg, F.matvec(W, xs)), f"codes {start}..{start + 7}"
+
+
+@pytest.mark.parametrize("fmt", (4,) + FMTS)
+def test_matvec_non_finite_group_poisons_its_rows(fmt):
+    """A group, block or tile stored with the NaN scale (non-finite weights) makes
+    exactly the outputs it feeds NaN, as the oracle's fp64 product says; every
+    other output stays within the bar."""
+    O, I, T = 260, 512, 2
+    w = weights(O, I, 77 + fmt)
+    w[3, 100] = np.nan
+    w[200, 511] = np.inf
+    if fmt == 4:
+        import oracle
+        pk, sc, _ = oracle.quant_int4_g64(w)
+        W = oracle.dequant_int4_g64(pk, sc, I)
+    else:
+        pk, sc = F.quant(fmt, w)
+        W = F.dequant(fmt, pk, sc, O, I)
+    x = np.random.default_rng(5).standard_normal((T, I)).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        yr = F.matvec(W, x)
+    yg = gpu_matvec(fmt, pk, sc, O, I, x)
+    bad = np.isnan(yr)
+    assert bad.any() and np.array_equal(np.isnan(yg), bad)
+    keep = ~bad.any(axis=0)
+    check(yg[:, keep], yr[:, keep], f"{NAMES[fmt]} finite rows", TIGHT[fmt])
