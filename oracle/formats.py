@@ -268,3 +268,61 @@ def quant(fmt: int, w):
 def matvec(W: np.ndarray, x: np.ndarray) -> np.ndarray:
     """y [T, O] = x [T, I] W^T in fp64 (W already dequantised)."""
     return np.asarray(x, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+
+
+# ---------------------------------------------------------------- a layer in a format
+
+def quant_expert(fmt: int, wg, wu, wd):
+    """The three matrices of one expert in fmt: [(packed, scales)] for gate [I, H],
+    up [I, H], down [H, I]."""
+    if fmt == 4:
+        import oracle
+        return [oracle.quant_int4_g64(w)[:2] for w in (wg, wu, wd)]
+    return [quant(fmt, w) for w in (wg, wu, wd)]
+
+
+def dequant_expert(fmt: int, ex, H: int, I: int):
+    """-> (Wg [I, H], Wu [I, H], Wd [H, I]) fp64, exactly dequantised."""
+    shapes = ((I, H), (I, H), (H, I))
+    out = []
+    for (pk, sc), (O, C) in zip(ex, shapes):
+        if fmt == 4:
+            import oracle
+            out.append(oracle.dequant_int4_g64(pk, sc, C))
+        else:
+            out.append(dequant(fmt, pk, sc, O, C))
+    return out
+
+
+def moe_forward_fmt(fmt: int, x, wr, bias, experts: list, shared, H: int, I: int, K: int,
+                    scoring: int = 0):
+    """The layer with its experts in fmt: the routing of the oracle's layer (softmax
+    or sigmoid scoring), then per token y = sum_k g_k FFN_{e_k}(x) + FFN_shared(x),
+    FFN(x) = Wd (silu(Wg x) * (Wu x)), silu(z) = z / (1 + e^-z), all fp64 on the
+    exactly dequantised matrices.  experts: E entries of quant_expert output (None
+    where unused).  -> (y fp64 [T, H], idx [T, K], gates fp64 [T, K])."""
+    import oracle
+    logits = oracle.router_logits(x, wr, bias if scoring == 0 else None)
+    if scoring == 0:
+        idx, gates, _ = oracle.topk(logits, K)
+    else:
+        idx, gates, _ = oracle.topk_sigmoid(logits, K, bias)
+    xf = np.asarray(x, dtype=np.float64) if np.asarray(x).dtype != np.uint16 else \
+        (np.asarray(x, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    def ffn(ex, v):
+        Wg, Wu, Wd = dequant_expert(fmt, ex, H, I)
+        g = Wg @ v
+        u = Wu @ v
+        return Wd @ (g / (1.0 + np.exp(-g)) * u)
+
+    T = xf.shape[0]
+    y = np.zeros((T, H), dtype=np.float64)
+    for t in range(T):
+        for k in range(K):
+            ex = experts[int(idx[t, k])]
+            if ex is None:
+                raise ValueError("a selected expert was not supplied")
+            y[t] += gates[t, k] * ffn(ex, xf[t])
+        y[t] += ffn(shared, xf[t])
+    return y, idx, gates

@@ -267,3 +267,42 @@ def test_matvec_exact_rational():
                             for i in range(70))
                 assert abs(Fraction(float(y[t, o])) - exact) <= abs(exact) * Fraction(1, 2 ** 45) \
                     + Fraction(1, 2 ** 80)
+
+
+# ---------------------------------------------------------------- a layer in a format
+
+def test_layer_in_int4_matches_the_c_oracle():
+    """The format layer (numpy composition) with int4-g64 experts equals the C
+    oracle's fp64 layer on the same bytes: two independent statements of the same
+    routing and FFN."""
+    import oracle
+    rng = np.random.default_rng(12)
+    H, I, E, K, T = 128, 64, 8, 3, 4
+    ws = [[(rng.standard_normal(s) * 0.02).astype(np.float32) for s in ((I, H), (I, H), (H, I))]
+          for _ in range(E + 1)]
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    fx = [F.quant_expert(4, *w) for w in ws]
+    cx = [oracle.Expert(fx[e][0][0], fx[e][0][1], fx[e][1][0], fx[e][1][1], fx[e][2][0],
+                        fx[e][2][1]) for e in range(E + 1)]
+    for scoring, bias in ((0, None), (1, (rng.standard_normal(E) * 0.1).astype(np.float32))):
+        y1, i1, g1 = F.moe_forward_fmt(4, x, wr, bias, fx[:E], fx[E], H, I, K, scoring)
+        y2, i2, g2 = oracle.moe_forward(x, wr, bias, cx[:E], cx[E], H, I, K, scoring)
+        assert np.array_equal(i1, i2)
+        assert np.allclose(g1, g2, rtol=1e-14, atol=0)
+        assert np.allclose(y1, y2, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("fmt", (5, 7, 8))
+def test_layer_closed_forms(fmt):
+    rng = np.random.default_rng(13)
+    H, I, E, K, T = 128, 64, 6, 2, 3
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    zero = F.quant_expert(fmt, np.zeros((I, H), np.float32), np.zeros((I, H), np.float32),
+                          np.zeros((H, I), np.float32))
+    y, idx, g = F.moe_forward_fmt(fmt, x, wr, None, [zero] * E, zero, H, I, K)
+    assert not y.any()  # all-zero experts give y = 0
+    assert np.allclose(g.sum(axis=1), 1.0)
+    # the composition itself is the one pinned against the C oracle with int4 experts;
+    # here each format's dequantised matrices enter it (dequant is pinned above)
