@@ -504,6 +504,34 @@ int coli_quant_fmt(int fmt, const float *w, int64_t O, int64_t I, void *packed,
 int coli_matvec_fmt(int fmt, const void *packed, const void *scales, int64_t O, int64_t I,
                     const float *x, int T, float *y, void *stream);
 
+/* A layer whose routed and shared experts are in a sibling format (fmt 4, 5,
+ * 7 or 8), decode only.  One expert blob in fmt: gate.q | up.q | down.q |
+ * gate.s | up.s | down.s (the coli_fmt_bytes arrays of gate [I, H], up [I, H]
+ * and down [H, I]), each section 256-byte aligned; 0 for another fmt. */
+size_t coli_fmt_blob_bytes(int fmt, int H, int I);
+/* Quantise fp32 gate [I, H], up [I, H], down [H, I] (device) into a blob
+ * (256-byte aligned) with coli_quant_fmt.  Errors: as coli_quant_fmt. */
+int coli_quant_expert_fmt(int fmt, uint8_t *blob, int H, int I, const float *w_gate,
+                          const float *w_up, const float *w_down, int32_t *status,
+                          void *stream);
+/* Workspace of coli_moe_forward_fmt (0 for an unsupported fmt or shape). */
+size_t coli_moe_fmt_workspace_bytes(const coli_moe_layer *L, int fmt, int T);
+/*
+ * The layer a1-a6 with experts in fmt (L->experts: E blobs at a stride of
+ * coli_fmt_blob_bytes, L->shared: one blob; L->slot_map must be NULL), DECODE:
+ * x fp32 [T, H] -> y fp32 [T, H], T <= 4 with T * H and T * I (each rounded up
+ * to the format's group) at most 24576.  The routing is the one of
+ * coli_moe_forward (softmax or sigmoid scoring, ids and gates optional
+ * outputs); per unique routed expert and the shared one: h = SiLU(W^g x) *
+ * (W^u x) * gate weight, then W^d h, summed in unit order (fp32 products as in
+ * coli_matvec_fmt).  Errors: as coli_moe_forward, plus EINVAL for another fmt
+ * or a slot map, ESHAPE for T or H, I beyond those limits (fp8: H and I
+ * multiples of 16).
+ */
+int coli_moe_forward_fmt(const coli_moe_layer *L, int fmt, const float *x, int T, float *y,
+                         int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same

@@ -63,7 +63,8 @@ EXPORTS = [
     "coli_rmsnorm_f32", "coli_moe_route", "coli_moe_experts", "coli_tier_should_promote",
     "coli_tier_lfru_score", "coli_cache_init", "coli_cache_decay", "coli_cache_admit",
     "coli_cache_repin", "coli_cache_stage", "coli_cache_slot_map", "coli_fmt_bytes",
-    "coli_resolve_fmt", "coli_quant_fmt", "coli_matvec_fmt",
+    "coli_resolve_fmt", "coli_quant_fmt", "coli_matvec_fmt", "coli_fmt_blob_bytes",
+    "coli_quant_expert_fmt", "coli_moe_fmt_workspace_bytes", "coli_moe_forward_fmt",
 ]
 
 _p = ctypes.c_void_p
@@ -135,6 +136,11 @@ _proto("coli_resolve_fmt", _i, [_i64, _i64, ctypes.c_uint64, ctypes.c_uint64,
                                 ctypes.POINTER(ctypes.c_uint32)])
 _proto("coli_quant_fmt", _i, [_i, _p, _i64, _i64, _p, _p, _p, _p])
 _proto("coli_matvec_fmt", _i, [_i, _p, _p, _i64, _i64, _p, _i, _p, _p])
+_proto("coli_fmt_blob_bytes", _sz, [_i, _i, _i])
+_proto("coli_quant_expert_fmt", _i, [_i, _p, _i, _i, _p, _p, _p, _p, _p])
+_proto("coli_moe_fmt_workspace_bytes", _sz, [ctypes.POINTER(coli_moe_layer), _i, _i])
+_proto("coli_moe_forward_fmt", _i, [ctypes.POINTER(coli_moe_layer), _i, _p, _i, _p, _p, _p, _p,
+                                    _p, _sz, _p])
 _proto("coli_usage_count", _i, [_p, _i, _i, _i, _i, _i, _p, _p])
 _proto("coli_usage_engine_hash", ctypes.c_uint32, [ctypes.c_char_p])
 _proto("coli_usage_save", _i, [ctypes.c_char_p, _p, _i, _i, ctypes.c_uint32, ctypes.c_double, _p])
@@ -464,6 +470,33 @@ def coli_matvec_fmt(fmt: int, packed, scales, O: int, I: int, x, y, stream=None)
     T = x.shape[0]
     return _check(lib.coli_matvec_fmt(fmt, _ptr(packed), _ptr(scales), O, I, _ptr(x), T,
                                       _ptr(y), _stream(stream)), "coli_matvec_fmt")
+
+
+def coli_fmt_blob_bytes(fmt: int, H: int, I: int) -> int:
+    return int(lib.coli_fmt_blob_bytes(fmt, H, I))
+
+
+def coli_quant_expert_fmt(fmt: int, blob_ptr: int, H: int, I: int, wg, wu, wd, status=None,
+                          stream=None):
+    """Quantise fp32 gate [I,H], up [I,H], down [H,I] (device) into a blob of fmt."""
+    return _check(lib.coli_quant_expert_fmt(fmt, ctypes.c_void_p(blob_ptr), H, I, _ptr(wg),
+                                            _ptr(wu), _ptr(wd), _ptr(status), _stream(stream)),
+                  "coli_quant_expert_fmt")
+
+
+def coli_moe_fmt_workspace_bytes(layer: "MoELayer", fmt: int, T: int) -> int:
+    return int(lib.coli_moe_fmt_workspace_bytes(ctypes.byref(layer.c), fmt, T))
+
+
+def coli_moe_forward_fmt(layer: "MoELayer", fmt: int, x, y, workspace, topk_idx=None,
+                         topk_gate=None, stream=None, status=None):
+    """The decode layer with experts in fmt (layer.experts: E blobs of coli_fmt_blob_bytes)."""
+    T = x.shape[0]
+    nbytes = workspace.numel() * workspace.element_size()
+    return _check(lib.coli_moe_forward_fmt(ctypes.byref(layer.c), fmt, _ptr(x), T, _ptr(y),
+                                           _ptr(topk_idx), _ptr(topk_gate), _ptr(status),
+                                           _ptr(workspace), nbytes, _stream(stream)),
+                  "coli_moe_forward_fmt")
 
 
 # ---------------------------------------------------------------- layer assembly

@@ -586,6 +586,85 @@ int coli_moe_experts(const coli_moe_layer *L, coli_mode mode, const void *x, int
   return experts_launch(L, mode, x, T, y, c, d, as_stream(stream), nullptr, true);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of the sibling-format forward: the routing sections of the decode
+// layout, then h [units][T][I] and the per-unit outputs [units][T][H].
+struct FmtWs {
+  WsLayout w;
+  size_t h, part, total;
+};
+FmtWs fmt_ws(const coli_moe_layer *L, int T) {
+  FmtWs f;
+  f.w = ws_layout(L->H, L->I, L->E, L->K, T, COLI_DECODE);
+  const size_t units = size_t(L->E < T * L->K ? L->E : T * L->K) + 1;
+  f.h = align256(f.w.total);
+  f.part = f.h + align256(units * T * L->I * 4);
+  f.total = f.part + align256(units * T * L->H * 4);
+  return f;
+}
+
+int fmt_forward_checks(const coli_moe_layer *L, int fmt, const void *x, int T, void *y,
+                       int32_t *topk_idx_out, float *topk_gate_out, int32_t *status) {
+  WsLayout w;
+  const int rc = forward_checks(L, COLI_DECODE, x, T, y, topk_idx_out, topk_gate_out, status, &w);
+  if (rc != COLI_OK) return rc;
+  if (!fmt_layer_supported(fmt) || L->slot_map) return COLI_EINVAL;
+  if (T != 0 && !fmt_layer_shape_ok(fmt, L->H, L->I, T)) return COLI_ESHAPE;
+  return COLI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t coli_moe_fmt_workspace_bytes(const coli_moe_layer *L, int fmt, int T) {
+  if (!L || !layer_shape_ok(L->H, L->I, L->E, L->K) || !fmt_layer_supported(fmt)) return 0;
+  if (T < 1 || !fmt_layer_shape_ok(fmt, L->H, L->I, T)) return 0;
+  return fmt_ws(L, T).total;
+}
+
+int coli_moe_forward_fmt(const coli_moe_layer *L, int fmt, const float *x, int T, float *y,
+                         int32_t *topk_idx_out, float *topk_gate_out, int32_t *status,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = fmt_forward_checks(L, fmt, x, T, y, topk_idx_out, topk_gate_out, status);
+  if (rc != COLI_OK) return rc;
+  if (T == 0) return COLI_OK;
+  const FmtWs f = fmt_ws(L, T);
+  if (!workspace || workspace_bytes < f.total) return COLI_EWORKSPACE;
+  if (!aligned(workspace, 256)) return COLI_EALIGN;
+  hipStream_t s = as_stream(stream);
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  Routing r = carve(ws, f.w);
+  if (topk_idx_out) r.idx = topk_idx_out;
+  if (topk_gate_out) r.gates = topk_gate_out;
+  const bool sig = L->scoring == COLI_SCORE_SIGMOID;
+  r.sc = Scoring{sig ? 1 : 0, sig ? L->router_bias : nullptr};
+  const float *lbias = sig ? nullptr : L->router_bias;
+  const int wbf = L->router_dtype == COLI_BF16;
+  hipError_t e = router_vec_ok(x, 0, L->H, L->w_router, wbf)
+                     ? launch_router_logits(x, 0, T, L->H, L->w_router, wbf, L->E, lbias,
+                                            r.logits, s)
+                     : launch_router_any(x, 0, T, L->H, L->w_router, wbf, L->E, lbias,
+                                         r.logits, s);
+  if (e != hipSuccess) return COLI_EDEVICE;
+  e = launch_route_decode(r, T, L->E, L->K, s);
+  if (e != hipSuccess) return COLI_EDEVICE;
+  FmtLayer fl;
+  fl.fmt = fmt;
+  fl.H = L->H;
+  fl.I = L->I;
+  fl.E = L->E;
+  fl.K = L->K;
+  fl.experts = L->experts;
+  fl.shared = L->shared;
+  fl.blob_bytes = fmt_blob_layout(fmt, L->H, L->I, fl.q_off, fl.s_off);
+  return dev_status(launch_fmt_experts(fl, r, x, T, reinterpret_cast<float *>(ws + f.h),
+                                       reinterpret_cast<float *>(ws + f.part), y, status, s));
+}
+
 int coli_rmsnorm_f32(const float *x, float *y, int T, int H, float eps, void *stream) {
   if (((!x || !y) && T != 0) || !(eps >= 0.0f) || !std::isfinite(eps)) return COLI_EINVAL;
   if (T < 0 || T > COLI_MAX_TOKENS || H < 1 || H > COLI_MAX_DIM) return COLI_ESHAPE;

@@ -389,32 +389,45 @@ __device__ inline void chunk_dot_rows(const Raw<FMT> (&raw)[R], const float4 *xc
 struct MatvecArgs {
   const uint8_t *packed;
   const void *scales;
-  int64_t O;
-  int I, ldx;        // ldx: padded row length of x in LDS (chunks * weights)
+  int64_t O;         // rows (gate/up mode: features)
+  int I, ldx;        // I: row length; ldx: padded row length of x in LDS (chunks * weights)
   int chunks;        // chunks per row
   int64_t row_bytes;
   int scale_cols;    // fp8: tiles per row of tiles; others: scales per row
   const float *x;
   float *y;
+  // grouped modes (one unit per blockIdx.y: the batch's unique experts in
+  // ascending id, then the shared expert)
+  const uint8_t *experts, *shared;
+  size_t blob_bytes;
+  size_t q_off[2], s_off[2];  // gate/up mode: gate and up sections; down: [0]
+  const int32_t *unique, *n_unique;
+  const int32_t *idx;         // [T][K] routed ids and their gates
+  const float *gates;
+  int K;
+  float *h;                   // [units][T][I_ffn]: gate/up output, down input
+  float *part;                // [units][T][H]: down output
 };
+
+enum { kModePlain = 0, kModeGateUp = 1, kModeDown = 2 };
 
 // The raw scale of chunk c of row o0 + rr: the f32 bits, or the E8M0 byte
 // (decoded at use by scale_value, so that the load is not waited for when it
 // is issued).  o0 is wave-uniform and a multiple of the rows per step (4 or
 // 8), so an fp8 group of rows never straddles a 128-row tile.
 template <int FMT>
-__device__ inline uint32_t chunk_scale(const MatvecArgs &a, int64_t o0, int rr, int c) {
+__device__ inline uint32_t chunk_scale(const void *sbase, int scale_cols, int64_t o0, int rr,
+                                       int c) {
   constexpr int CW = Chunk<FMT>::kW;
   if constexpr (FMT == COLI_FMT_FP8_E4M3_B128) {
-    const uint32_t *base =
-        reinterpret_cast<const uint32_t *>(a.scales) + (o0 >> 7) * a.scale_cols;
+    const uint32_t *base = reinterpret_cast<const uint32_t *>(sbase) + (o0 >> 7) * scale_cols;
     return base[(c * CW) >> 7];
   } else if constexpr (FMT == COLI_FMT_MXFP4) {
-    const uint8_t *base = reinterpret_cast<const uint8_t *>(a.scales) + o0 * a.scale_cols;
-    return base[uint32_t(rr * a.scale_cols + c)];
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(sbase) + o0 * scale_cols;
+    return base[uint32_t(rr * scale_cols + c)];
   } else {
-    const uint32_t *base = reinterpret_cast<const uint32_t *>(a.scales) + o0 * a.scale_cols;
-    return base[uint32_t(rr * a.scale_cols + c)];
+    const uint32_t *base = reinterpret_cast<const uint32_t *>(sbase) + o0 * scale_cols;
+    return base[uint32_t(rr * scale_cols + c)];
   }
 }
 
@@ -443,16 +456,55 @@ constexpr int rows_per_step() {
 // computed.  Per-chunk dot products are scaled by the chunk's scale (and, for
 // the offset formats, corrected by the chunk's x sum times the code offset),
 // then reduced over the wave.
-template <int FMT, int T>
+//
+// MODE kModePlain: one matrix (packed, scales), x [T][I] -> y [T][O].
+// MODE kModeGateUp: unit blockIdx.y of a layer; a step takes R/2 features of
+//   the gate matrix and the same features of the up matrix, x = the tokens
+//   [T][H], and writes h[unit][t][f] = SiLU(gate) * up * w_t (w_t: the token's
+//   gate weight for this unit, 0 when the token did not route to it, 1 for the
+//   shared expert).
+// MODE kModeDown: unit blockIdx.y; the down matrix, x = h[unit] [T][I], writes
+//   part[unit][t][o].
+template <int FMT, int T, int MODE>
 __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
   constexpr int CW = Chunk<FMT>::kW, CB = Chunk<FMT>::kBytes;
   constexpr int R = rows_per_step<FMT, T>();
+  constexpr int RM = MODE == kModeGateUp ? R / 2 : R;  // rows of one matrix per step
   constexpr bool kOffset = FMT == COLI_FMT_INT3_G64 || FMT == COLI_FMT_INT4_G64;
   constexpr float kOff = FMT == COLI_FMT_INT3_G64 ? 4.0f : 8.0f;
   extern __shared__ float xs[];  // x piece-major [T][pieces][chunks][4], then the chunk sums [T][chunks]
+  __shared__ float wtok[T];      // gate/up mode: the tokens' gate weights for the unit
   float *xsum = xs + T * a.ldx;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t groups = (a.O + R - 1) / R;
+
+  // the matrices of this block
+  const uint8_t *pk[2] = {a.packed, a.packed};
+  const void *sb[2] = {a.scales, a.scales};
+  const float *xsrc = a.x;
+  int unit = 0;
+  if constexpr (MODE != kModePlain) {
+    unit = int(blockIdx.y);
+    const int nu = *a.n_unique;
+    if (unit > nu) return;  // whole block, before any barrier
+    const int e = unit < nu ? a.unique[unit] : -1;
+    const uint8_t *blob = e >= 0 ? a.experts + size_t(e) * a.blob_bytes : a.shared;
+    pk[0] = blob + a.q_off[0];
+    sb[0] = blob + a.s_off[0];
+    pk[1] = blob + a.q_off[1];
+    sb[1] = blob + a.s_off[1];
+    if constexpr (MODE == kModeGateUp) {
+      if (threadIdx.x < T) {
+        float w = e < 0 ? 1.0f : 0.0f;
+        for (int k = 0; k < a.K; ++k)
+          if (e >= 0 && a.idx[threadIdx.x * a.K + k] == e) w = a.gates[threadIdx.x * a.K + k];
+        wtok[threadIdx.x] = w;
+      }
+    } else {
+      xsrc = a.h + size_t(unit) * T * a.I;
+    }
+  }
+
+  const int64_t groups = (a.O + RM - 1) / RM;
   const int64_t gstride = int64_t(gridDim.x) * 4;
   const int kc = (a.chunks + 63) / 64;
   int64_t g = int64_t(blockIdx.x) * 4 + wave;
@@ -461,20 +513,22 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
   Raw<FMT> cur[R], nxt[R];
   uint32_t csc[R], nsc[R];
   // Loads of step (gg, kk): a wave-uniform 64-bit base for the group's first
-  // row, 32-bit offsets for the rows (clamped to the last row: rows past the
-  // end are re-read, never stored) and the chunk (clamped to the row's last
-  // chunk on lanes past the row's end).
+  // row of each matrix, 32-bit offsets for the rows (clamped to the last row:
+  // rows past the end are re-read, never stored) and the chunk (clamped to the
+  // row's last chunk on lanes past the row's end).
   auto fetch = [&](int64_t gg, int kk, Raw<FMT>(&dst)[R], uint32_t(&sc)[R]) {
-    const int64_t o0 = gg * R;
-    const uint8_t *base = a.packed + o0 * a.row_bytes;
+    const int64_t o0 = gg * RM;
     const int last = int(a.O - 1 - o0);  // rows of the group that exist: r <= last
     const int c0 = lane + 64 * kk;
     const int c = c0 < a.chunks ? c0 : a.chunks - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int rr = r < last ? r : last;
+      const int m = r / RM;  // 0: gate (or the only matrix), 1: up
+      const int ri = r - m * RM;
+      const int rr = ri < last ? ri : last;
+      const uint8_t *base = pk[m] + o0 * a.row_bytes;
       dst[r] = load_chunk<FMT>(base + uint32_t(rr * int(a.row_bytes) + c * CB));
-      sc[r] = chunk_scale<FMT>(a, o0, rr, c);
+      sc[r] = chunk_scale<FMT>(sb[m], a.scale_cols, o0, rr, c);
     }
   };
   // the first weights are in flight while x is staged
@@ -489,10 +543,10 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
     const int t = tp / kPieces, pc = tp - t * kPieces;
     const int k0 = c * CW + 4 * pc;
     float4 v;
-    v.x = k0 < a.I ? a.x[size_t(t) * a.I + k0] : 0.0f;
-    v.y = k0 + 1 < a.I ? a.x[size_t(t) * a.I + k0 + 1] : 0.0f;
-    v.z = k0 + 2 < a.I ? a.x[size_t(t) * a.I + k0 + 2] : 0.0f;
-    v.w = k0 + 3 < a.I ? a.x[size_t(t) * a.I + k0 + 3] : 0.0f;
+    v.x = k0 < a.I ? xsrc[size_t(t) * a.I + k0] : 0.0f;
+    v.y = k0 + 1 < a.I ? xsrc[size_t(t) * a.I + k0 + 1] : 0.0f;
+    v.z = k0 + 2 < a.I ? xsrc[size_t(t) * a.I + k0 + 2] : 0.0f;
+    v.w = k0 + 3 < a.I ? xsrc[size_t(t) * a.I + k0 + 3] : 0.0f;
     x4[i] = v;
   }
   __syncthreads();
@@ -547,15 +601,41 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
         acc[r][t] += valid ? v : 0.0f;
       }
     if (k == kc - 1) {
+      float tot[R][T];
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          const float v = wave_sum(acc[r][t]);
+          tot[r][t] = wave_sum(acc[r][t]);
           acc[r][t] = 0.0f;
-          const int64_t o = g * R + r;
-          if (lane == (r * T + t) % 64 && o < a.O) a.y[size_t(t) * a.O + o] = v;
         }
+      if constexpr (MODE == kModeGateUp) {
+        // h = SiLU(gate) * up * w_t for the RM features of the step
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const int64_t f = g * RM + r;
+            if (lane == (r * T + t) % 64 && f < a.O) {
+              const float gv = tot[r][t], uv = tot[r + RM][t];
+              const float hv = gv / (1.0f + expf(-gv)) * uv * wtok[t];
+              a.h[(size_t(unit) * T + t) * a.O + f] = hv;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const int64_t o = g * R + r;
+            if (lane == (r * T + t) % 64 && o < a.O) {
+              if constexpr (MODE == kModeDown)
+                a.part[(size_t(unit) * T + t) * a.O + o] = tot[r][t];
+              else
+                a.y[size_t(t) * a.O + o] = tot[r][t];
+            }
+          }
+      }
     }
     g = g2;
     k = k2;
@@ -565,61 +645,194 @@ __global__ __launch_bounds__(256) void matvec_kernel(MatvecArgs a) {
   }
 }
 
-template <int FMT, int T>
+// Layer combine: y[t][o] = sum over units, in unit order, of part[unit][t][o]
+// (units past the batch's count are skipped).
+__global__ __launch_bounds__(256) void fmt_combine(const float *__restrict__ part,
+                                                   const int32_t *__restrict__ n_unique, int T,
+                                                   int H, float *__restrict__ y,
+                                                   int32_t *__restrict__ status) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(T) * H) return;
+  const int nu = *n_unique;
+  float s = 0.0f;
+  for (int u = 0; u <= nu; ++u) s += part[size_t(u) * T * H + i];
+  y[i] = s;
+  if (status && !__builtin_isfinite(s)) atomicOr(status, COLI_STATUS_NONFINITE);
+}
+
+template <int FMT, int T, int MODE>
 int matvec_grid(int64_t O) {
-  const int64_t groups = (O + rows_per_step<FMT, T>() - 1) / rows_per_step<FMT, T>();
+  constexpr int RM = MODE == kModeGateUp ? rows_per_step<FMT, T>() / 2 : rows_per_step<FMT, T>();
+  const int64_t groups = (O + RM - 1) / RM;
   const int64_t want = cdiv(groups, 4);
   return int(want < 1024 ? want : 1024);
 }
 
-template <int FMT>
-hipError_t launch_matvec_t(const MatvecArgs &a, int T, size_t lds, hipStream_t s) {
+template <int FMT, int MODE, int TT>
+void launch_one(const MatvecArgs &a, int units, size_t lds, hipStream_t s) {
+  static const bool done = [] {
+    // the x stage may take up to 96 KiB + the chunk sums (6 KiB); the limit
+    // leaves room for the kernel's static LDS within the 160 KiB of a CU
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&matvec_kernel<FMT, TT, MODE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    return true;
+  }();  // once per process
+  (void)done;
+  hipLaunchKernelGGL((matvec_kernel<FMT, TT, MODE>),
+                     dim3(matvec_grid<FMT, TT, MODE>(a.O), unsigned(units)), dim3(256), lds, s, a);
+}
+
+template <int FMT, int MODE>
+hipError_t launch_matvec_t(const MatvecArgs &a, int T, int units, size_t lds, hipStream_t s) {
   switch (T) {
-#define COLI_MV_CASE(TT)                                                               \
-  case TT:                                                                             \
-    hipLaunchKernelGGL((matvec_kernel<FMT, TT>), dim3(matvec_grid<FMT, TT>(a.O)), dim3(256), \
-                       lds, s, a);                                                     \
-    break;
-    COLI_MV_CASE(1)
-    COLI_MV_CASE(2)
-    COLI_MV_CASE(3)
-    COLI_MV_CASE(4)
-    COLI_MV_CASE(5)
-    COLI_MV_CASE(6)
-    COLI_MV_CASE(7)
-    COLI_MV_CASE(8)
-#undef COLI_MV_CASE
-    default: return hipErrorInvalidValue;
+    case 1: launch_one<FMT, MODE, 1>(a, units, lds, s); break;
+    case 2: launch_one<FMT, MODE, 2>(a, units, lds, s); break;
+    case 3: launch_one<FMT, MODE, 3>(a, units, lds, s); break;
+    case 4: launch_one<FMT, MODE, 4>(a, units, lds, s); break;
+    default:
+      if constexpr (MODE == kModePlain) {
+        switch (T) {
+          case 5: launch_one<FMT, MODE, 5>(a, units, lds, s); break;
+          case 6: launch_one<FMT, MODE, 6>(a, units, lds, s); break;
+          case 7: launch_one<FMT, MODE, 7>(a, units, lds, s); break;
+          case 8: launch_one<FMT, MODE, 8>(a, units, lds, s); break;
+          default: return hipErrorInvalidValue;
+        }
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
   }
   return hipGetLastError();
 }
 
-template <int FMT>
-void allow_lds_once() {
-  // the x stage may take up to 96 KiB + the chunk sums
-#define COLI_MV_ATTR(TT)                                                             \
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&matvec_kernel<FMT, TT>), \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  COLI_MV_ATTR(1)
-  COLI_MV_ATTR(2)
-  COLI_MV_ATTR(3)
-  COLI_MV_ATTR(4)
-  COLI_MV_ATTR(5)
-  COLI_MV_ATTR(6)
-  COLI_MV_ATTR(7)
-  COLI_MV_ATTR(8)
-#undef COLI_MV_ATTR
+template <int MODE>
+hipError_t launch_matvec_fmt(int fmt, const MatvecArgs &a, int T, int units, size_t lds,
+                             hipStream_t s) {
+  switch (fmt) {
+    case COLI_FMT_FP8_E4M3_B128:
+      return launch_matvec_t<COLI_FMT_FP8_E4M3_B128, MODE>(a, T, units, lds, s);
+    case COLI_FMT_MXFP4: return launch_matvec_t<COLI_FMT_MXFP4, MODE>(a, T, units, lds, s);
+    case COLI_FMT_INT3_G64: return launch_matvec_t<COLI_FMT_INT3_G64, MODE>(a, T, units, lds, s);
+    default: return launch_matvec_t<COLI_FMT_INT4_G64, MODE>(a, T, units, lds, s);
+  }
 }
 
-template <int FMT>
-void allow_lds() {
-  static const bool done = (allow_lds_once<FMT>(), true);  // once per process
-  (void)done;
+// Row geometry of an [O, I] matrix in fmt: chunk weights, row bytes, scales
+// per row (fp8: tiles per row of tiles).
+void fmt_geometry(int fmt, int64_t I, int *cw, int64_t *row_bytes, int *scale_cols) {
+  switch (fmt) {
+    case COLI_FMT_FP8_E4M3_B128:
+      *cw = 16;
+      *row_bytes = I;
+      *scale_cols = int(cdiv(I, 128));
+      break;
+    case COLI_FMT_MXFP4:
+      *cw = 32;
+      *row_bytes = 16 * cdiv(I, 32);
+      *scale_cols = int(cdiv(I, 32));
+      break;
+    case COLI_FMT_INT3_G64:
+      *cw = 64;
+      *row_bytes = 24 * cdiv(I, 64);
+      *scale_cols = int(cdiv(I, 64));
+      break;
+    default:
+      *cw = 64;
+      *row_bytes = 32 * cdiv(I, 64);
+      *scale_cols = int(cdiv(I, 64));
+      break;
+  }
 }
 
 bool aligned_to(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 }  // namespace
+
+// ------------------------------------------------------------------ layer
+
+size_t fmt_blob_layout(int fmt, int H, int I, size_t q_off[3], size_t s_off[3]) {
+  auto a256 = [](uint64_t n) { return (n + 255) / 256 * 256; };
+  uint64_t wq[3], ws[3];
+  if (!fmt_sizes(fmt, I, H, &wq[0], &ws[0])) return 0;  // gate [I, H]
+  wq[1] = wq[0];
+  ws[1] = ws[0];                                       // up [I, H]
+  fmt_sizes(fmt, H, I, &wq[2], &ws[2]);                // down [H, I]
+  uint64_t o = 0;
+  for (int m = 0; m < 3; ++m) {
+    q_off[m] = size_t(o);
+    o += a256(wq[m]);
+  }
+  for (int m = 0; m < 3; ++m) {
+    s_off[m] = size_t(o);
+    o += a256(ws[m] ? ws[m] : 1);
+  }
+  return size_t(o);
+}
+
+bool fmt_layer_supported(int fmt) {
+  return fmt == COLI_FMT_INT4_G64 || fmt == COLI_FMT_INT3_G64 || fmt == COLI_FMT_MXFP4 ||
+         fmt == COLI_FMT_FP8_E4M3_B128;
+}
+
+bool fmt_layer_shape_ok(int fmt, int H, int I, int T) {
+  if (T < 1 || T > kFmtLayerMaxT) return false;
+  if (fmt == COLI_FMT_FP8_E4M3_B128 && (H % 16 || I % 16)) return false;
+  int cw;
+  int64_t rb;
+  int sc;
+  fmt_geometry(fmt, H, &cw, &rb, &sc);
+  if (int64_t(T) * cdiv(H, cw) * cw > kXFloats) return false;
+  fmt_geometry(fmt, I, &cw, &rb, &sc);
+  return int64_t(T) * cdiv(I, cw) * cw <= kXFloats;
+}
+
+hipError_t launch_fmt_experts(const FmtLayer &L, const Routing &r, const float *x, int T,
+                              float *h, float *part, float *y, int32_t *status, hipStream_t s) {
+  const int units = (L.E < T * L.K ? L.E : T * L.K) + 1;  // unique experts + the shared one
+  MatvecArgs a = {};
+  a.experts = L.experts;
+  a.shared = L.shared;
+  a.blob_bytes = L.blob_bytes;
+  a.unique = r.unique;
+  a.n_unique = r.n_unique;
+  a.idx = r.idx;
+  a.gates = r.gates;
+  a.K = L.K;
+  a.h = h;
+  a.part = part;
+  int cw;
+  // gate/up: rows are the I features, the row length H, x the tokens
+  fmt_geometry(L.fmt, L.H, &cw, &a.row_bytes, &a.scale_cols);
+  a.O = L.I;
+  a.I = L.H;
+  a.x = x;
+  a.chunks = int(cdiv(L.H, cw));
+  a.ldx = a.chunks * cw;
+  a.q_off[0] = L.q_off[0];
+  a.q_off[1] = L.q_off[1];
+  a.s_off[0] = L.s_off[0];
+  a.s_off[1] = L.s_off[1];
+  size_t lds = size_t(T) * a.ldx * 4 + size_t(T) * a.chunks * 4;
+  hipError_t e = launch_matvec_fmt<kModeGateUp>(L.fmt, a, T, units, lds, s);
+  if (e != hipSuccess) return e;
+  // down: rows are the H outputs, the row length I, x = h of the unit
+  fmt_geometry(L.fmt, L.I, &cw, &a.row_bytes, &a.scale_cols);
+  a.O = L.H;
+  a.I = L.I;
+  a.x = nullptr;
+  a.chunks = int(cdiv(L.I, cw));
+  a.ldx = a.chunks * cw;
+  a.q_off[0] = a.q_off[1] = L.q_off[2];
+  a.s_off[0] = a.s_off[1] = L.s_off[2];
+  lds = size_t(T) * a.ldx * 4 + size_t(T) * a.chunks * 4;
+  e = launch_matvec_fmt<kModeDown>(L.fmt, a, T, units, lds, s);
+  if (e != hipSuccess) return e;
+  const int64_t n = int64_t(T) * L.H;
+  fmt_combine<<<dim3(unsigned(cdiv(n, 256))), 256, 0, s>>>(part, r.n_unique, T, L.H, y, status);
+  return hipGetLastError();
+}
+
 }  // namespace coli
 
 using namespace coli;
@@ -701,6 +914,31 @@ int coli_quant_fmt(int fmt, const float *w, int64_t O, int64_t I, void *packed, 
   return hipGetLastError() == hipSuccess ? COLI_OK : COLI_EDEVICE;
 }
 
+size_t coli_fmt_blob_bytes(int fmt, int H, int I) {
+  if (!fmt_layer_supported(fmt) || H < 1 || I < 1 || H > COLI_MAX_DIM || I > COLI_MAX_DIM)
+    return 0;
+  size_t q[3], sc[3];
+  return fmt_blob_layout(fmt, H, I, q, sc);
+}
+
+int coli_quant_expert_fmt(int fmt, uint8_t *blob, int H, int I, const float *w_gate,
+                          const float *w_up, const float *w_down, int32_t *status, void *stream) {
+  if (!blob || !w_gate || !w_up || !w_down) return COLI_EINVAL;
+  if (!fmt_layer_supported(fmt)) return COLI_EINVAL;
+  if (H < 1 || I < 1 || H > COLI_MAX_DIM || I > COLI_MAX_DIM) return COLI_ESHAPE;
+  if (!aligned_to(blob, 256)) return COLI_EALIGN;
+  size_t q[3], sc[3];
+  fmt_blob_layout(fmt, H, I, q, sc);
+  const float *w[3] = {w_gate, w_up, w_down};
+  const int64_t rows[3] = {I, I, H}, cols[3] = {H, H, I};
+  for (int m = 0; m < 3; ++m) {
+    const int rc = coli_quant_fmt(fmt, w[m], rows[m], cols[m], blob + q[m], blob + sc[m], status,
+                                  stream);
+    if (rc != COLI_OK) return rc;
+  }
+  return COLI_OK;
+}
+
 int coli_matvec_fmt(int fmt, const void *packed, const void *scales, int64_t O, int64_t I,
                     const float *x, int T, float *y, void *stream) {
   if (!packed || !scales || ((!x || !y) && T > 0)) return COLI_EINVAL;
@@ -713,7 +951,7 @@ int coli_matvec_fmt(int fmt, const void *packed, const void *scales, int64_t O, 
       !aligned_to(packed, fmt == COLI_FMT_INT3_G64 ? 8 : 16))
     return COLI_EALIGN;
   if (T == 0) return COLI_OK;
-  MatvecArgs a;
+  MatvecArgs a = {};
   a.packed = reinterpret_cast<const uint8_t *>(packed);
   a.scales = scales;
   a.O = O;
@@ -721,52 +959,13 @@ int coli_matvec_fmt(int fmt, const void *packed, const void *scales, int64_t O, 
   a.x = x;
   a.y = y;
   int cw;
-  switch (fmt) {
-    case COLI_FMT_FP8_E4M3_B128:
-      cw = 16;
-      a.row_bytes = I;
-      a.scale_cols = int(cdiv(I, 128));
-      break;
-    case COLI_FMT_MXFP4:
-      cw = 32;
-      a.row_bytes = 16 * cdiv(I, 32);
-      a.scale_cols = int(cdiv(I, 32));
-      break;
-    case COLI_FMT_INT3_G64:
-      cw = 64;
-      a.row_bytes = 24 * cdiv(I, 64);
-      a.scale_cols = int(cdiv(I, 64));
-      break;
-    default:
-      cw = 64;
-      a.row_bytes = 32 * cdiv(I, 64);
-      a.scale_cols = int(cdiv(I, 64));
-      break;
-  }
+  fmt_geometry(fmt, I, &cw, &a.row_bytes, &a.scale_cols);
   a.chunks = int(cdiv(I, cw));
   a.ldx = a.chunks * cw;
   if (int64_t(T) * a.ldx > kXFloats) return COLI_ESHAPE;
   const size_t lds = size_t(T) * a.ldx * 4 + size_t(T) * a.chunks * 4;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (fmt) {
-    case COLI_FMT_FP8_E4M3_B128:
-      allow_lds<COLI_FMT_FP8_E4M3_B128>();
-      e = launch_matvec_t<COLI_FMT_FP8_E4M3_B128>(a, T, lds, s);
-      break;
-    case COLI_FMT_MXFP4:
-      allow_lds<COLI_FMT_MXFP4>();
-      e = launch_matvec_t<COLI_FMT_MXFP4>(a, T, lds, s);
-      break;
-    case COLI_FMT_INT3_G64:
-      allow_lds<COLI_FMT_INT3_G64>();
-      e = launch_matvec_t<COLI_FMT_INT3_G64>(a, T, lds, s);
-      break;
-    default:
-      allow_lds<COLI_FMT_INT4_G64>();
-      e = launch_matvec_t<COLI_FMT_INT4_G64>(a, T, lds, s);
-      break;
-  }
+  const hipError_t e = launch_matvec_fmt<kModePlain>(fmt, a, T, 1, lds,
+                                                     reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? COLI_OK : COLI_EDEVICE;
 }
 

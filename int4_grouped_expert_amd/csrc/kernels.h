@@ -179,6 +179,25 @@ hipError_t launch_topk_permute(const Routing &r, int T, int E, int K,
 // T <= COLI_MAX_DECODE_T.
 hipError_t launch_route_decode(const Routing &r, int T, int E, int K, hipStream_t s);
 size_t permute_chunk_ints(int T, int K, int E);
+// ---- formats.hip: a layer whose experts are in a sibling format ----------
+constexpr int kFmtLayerMaxT = 4;
+struct FmtLayer {
+  int fmt, H, I, E, K;
+  const uint8_t *experts, *shared;
+  size_t blob_bytes;
+  size_t q_off[3], s_off[3];  // gate, up, down sections of a blob
+};
+// Blob sections of one expert in fmt (gate.q | up.q | down.q | gate.s | up.s |
+// down.s, 256-byte aligned); returns the blob bytes, 0 for an unsupported fmt.
+size_t fmt_blob_layout(int fmt, int H, int I, size_t q_off[3], size_t s_off[3]);
+bool fmt_layer_supported(int fmt);
+bool fmt_layer_shape_ok(int fmt, int H, int I, int T);
+// The experts part of the layer from the routing in r: h = SiLU(gate) * up *
+// gate weight per (unit, token) -> h [units][T][I]; per-unit down outputs ->
+// part [units][T][H]; y [T][H] = their sum in unit order.
+hipError_t launch_fmt_experts(const FmtLayer &L, const Routing &r, const float *x, int T,
+                              float *h, float *part, float *y, int32_t *status, hipStream_t s);
+
 // Copy the batch union (r.unique [E], r.n_unique) to caller buffers (either
 // may be NULL).
 hipError_t launch_copy_union(const Routing &r, int E, int32_t *unique, int32_t *n_unique,

@@ -310,8 +310,12 @@ def moe_forward_fmt(fmt: int, x, wr, bias, experts: list, shared, H: int, I: int
     xf = np.asarray(x, dtype=np.float64) if np.asarray(x).dtype != np.uint16 else \
         (np.asarray(x, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
 
+    deq = {}  # each expert's matrices dequantised once per call
+
     def ffn(ex, v):
-        Wg, Wu, Wd = dequant_expert(fmt, ex, H, I)
+        if id(ex) not in deq:
+            deq[id(ex)] = dequant_expert(fmt, ex, H, I)
+        Wg, Wu, Wd = deq[id(ex)]
         g = Wg @ v
         u = Wu @ v
         return Wd @ (g / (1.0 + np.exp(-g)) * u)

@@ -255,6 +255,43 @@ def test_format_calls_reject_before_launch():
     assert mv(T=0, x=None, y=None) == coli.COLI_OK
 
 
+def test_format_layer_rejects_before_launch():
+    L = coli.lib
+    a = P(1 << 20)
+    lay = coli.coli_moe_layer(512, 512, 16, 4, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22)
+    need = L.coli_moe_fmt_workspace_bytes(ctypes.byref(lay), 7, 2)
+    assert need > 0
+    assert L.coli_moe_fmt_workspace_bytes(ctypes.byref(lay), 6, 2) == 0
+    assert L.coli_moe_fmt_workspace_bytes(ctypes.byref(lay), 7, 5) == 0  # T <= 4
+
+    def fwd(layer=lay, fmt=7, x=a, T=2, y=a, ws=a, nb=need):
+        return L.coli_moe_forward_fmt(ctypes.byref(layer), fmt, x, T, y, None, None, None, ws, nb,
+                                      None)
+    assert fwd(fmt=1) == coli.COLI_EINVAL and fwd(fmt=6) == coli.COLI_EINVAL
+    assert fwd(x=None) == coli.COLI_EINVAL
+    assert fwd(T=5) == coli.COLI_ESHAPE
+    assert fwd(nb=need - 1) == coli.COLI_EWORKSPACE
+    assert fwd(T=0) == coli.COLI_OK
+    sm = coli.coli_moe_layer(512, 512, 16, 4, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22,
+                             0, 1 << 23)
+    assert fwd(layer=sm) == coli.COLI_EINVAL  # no slot map on this path
+    big = coli.coli_moe_layer(6144, 2048, 256, 8, 1 << 20, coli.COLI_BF16, None, 1 << 21, 1 << 22)
+    assert L.coli_moe_fmt_workspace_bytes(ctypes.byref(big), 8, 4) > 0
+    assert L.coli_moe_forward_fmt(ctypes.byref(big), 8, a, 5, a, None, None, None, a, 1 << 30,
+                                  None) == coli.COLI_ESHAPE
+    ragged = coli.coli_moe_layer(200, 72, 16, 4, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22)
+    assert L.coli_moe_fmt_workspace_bytes(ctypes.byref(ragged), 8, 1) == 0  # fp8: 16-byte rows
+    assert L.coli_moe_fmt_workspace_bytes(ctypes.byref(ragged), 5, 1) > 0
+    assert coli.coli_fmt_blob_bytes(6, 512, 512) == 0
+    from oracle import formats as F
+    for fmt in (4, 5, 7, 8):
+        H, I = 6144, 2048
+        parts = [F.sizes(fmt, I, H)] * 2 + [F.sizes(fmt, H, I)]
+        a256 = lambda n: (n + 255) // 256 * 256
+        want = sum(a256(w) for w, _ in parts) + sum(a256(max(s, 1)) for _, s in parts)
+        assert coli.coli_fmt_blob_bytes(fmt, H, I) == want
+
+
 def test_rmsnorm_rejects():
     L = coli.lib
     a = P(4096)

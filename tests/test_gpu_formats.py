@@ -209,3 +209,119 @@ def test_matvec_non_finite_group_poisons_its_rows(fmt):
     assert bad.any() and np.array_equal(np.isnan(yg), bad)
     keep = ~bad.any(axis=0)
     check(yg[:, keep], yr[:, keep], f"{NAMES[fmt]} finite rows", TIGHT[fmt])
+
+
+# ---------------------------------------------------------------- the layer in a format
+
+class FmtLayer:
+    """A layer of a workload with its experts quantised by the library into fmt."""
+
+    def __init__(self, cfg_id, fmt):
+        import int4_grouped_expert_amd as coli
+        import workloads as W
+        c = W.CONFIGS[cfg_id]
+        self.cfg_id, self.fmt = cfg_id, fmt
+        self.H, self.I, self.E, self.K = H, I, E, K = c["H"], c["I"], c["E"], c["K"]
+        self.w_router = W.router_weights(cfg_id, "cuda").contiguous()
+        b = W.router_bias(cfg_id)
+        self.bias_np = b
+        self.bias = None if b is None else torch.from_numpy(b).cuda()
+        self.scoring = W.scoring(cfg_id)
+        self.nb = nb = coli.coli_fmt_blob_bytes(fmt, H, I)
+        self.experts = torch.empty(E * nb, dtype=torch.uint8, device="cuda")
+        self.shared = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for e in range(E + 1):
+            wg, wu, wd = W.expert_weights(cfg_id, e, "cuda")
+            ptr = self.shared.data_ptr() if e == E else self.experts.data_ptr() + e * nb
+            coli.coli_quant_expert_fmt(fmt, ptr, H, I, wg, wu, wd, st)
+            del wg, wu, wd
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        self.layer_c = coli.MoELayer(H, I, E, K, self.w_router, self.experts, self.shared,
+                                     self.bias, self.scoring)
+
+    def forward(self, x):
+        import int4_grouped_expert_amd as coli
+        T = x.shape[0]
+        ws = torch.empty(coli.coli_moe_fmt_workspace_bytes(self.layer_c, self.fmt, T),
+                         dtype=torch.uint8, device="cuda")
+        y = torch.full((T, self.H), float("nan"), device="cuda")
+        idx = torch.empty((T, self.K), dtype=torch.int32, device="cuda")
+        gates = torch.empty((T, self.K), dtype=torch.float32, device="cuda")
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        coli.coli_moe_forward_fmt(self.layer_c, self.fmt, x, y, ws, idx, gates, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        return y, idx, gates
+
+    def blob_sections(self, e):
+        """Host copies of expert e's six sections (e == E: the shared expert)."""
+        blob = (self.shared if e == self.E else
+                self.experts[e * self.nb:(e + 1) * self.nb]).cpu().numpy()
+        parts = [F.sizes(self.fmt, self.I, self.H)] * 2 + [F.sizes(self.fmt, self.H, self.I)]
+        a256 = lambda n: (n + 255) // 256 * 256
+        o, q, s = 0, [], []
+        for w, _ in parts:
+            q.append(blob[o:o + w])
+            o += a256(w)
+        for _, sc in parts:
+            s.append(blob[o:o + sc])
+            o += a256(max(sc, 1))
+        return q, s
+
+
+def oracle_fmt_check(L, x, y, idx, gates):
+    import workloads as W
+    from tests.harness import host_array
+    xh = host_array(x)
+    wr = host_array(L.w_router)
+    c = W.CONFIGS[L.cfg_id]
+    ids = sorted(set(idx.cpu().numpy().reshape(-1).tolist()))
+    experts = [None] * L.E
+    for e in ids + [L.E]:
+        wg, wu, wd = (t.cpu().numpy() for t in W.expert_weights(L.cfg_id, e, "cuda"))
+        ex = F.quant_expert(L.fmt, wg, wu, wd)
+        q, s = L.blob_sections(e)
+        for m in range(3):  # the library's bytes are the oracle's
+            assert np.array_equal(q[m], np.ascontiguousarray(ex[m][0]).reshape(-1).view(np.uint8))
+            assert np.array_equal(s[m], np.ascontiguousarray(ex[m][1]).reshape(-1).view(np.uint8))
+        if e == L.E:
+            shared = ex
+        else:
+            experts[e] = ex
+    yr, ridx, rg = F.moe_forward_fmt(L.fmt, xh, wr, L.bias_np, experts, shared, L.H, L.I,
+                                      c["K"], L.scoring)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(gates.cpu().numpy() - rg).max() <= 2e-3
+    check(y.cpu().numpy().astype(np.float64), yr, f"layer {NAMES[L.fmt]} cfg {L.cfg_id} "
+          f"T {x.shape[0]}", TIGHT[L.fmt])
+
+
+_fmt_layers = {}
+
+
+def fmt_layer(cfg_id, fmt):
+    key = (cfg_id, fmt)
+    if key not in _fmt_layers:
+        if cfg_id == 1:  # keep one full-size layer resident at a time
+            for k in [k for k in _fmt_layers if k[0] == 1]:
+                del _fmt_layers[k]
+            torch.cuda.empty_cache()
+        _fmt_layers[key] = FmtLayer(cfg_id, fmt)
+    return _fmt_layers[key]
+
+
+@pytest.mark.parametrize("fmt", (4,) + FMTS)
+@pytest.mark.parametrize("cfg_id,T", [(107, 1), (107, 3), (116, 2), (119, 4), (1, 1), (1, 4)])
+def test_layer_in_format(fmt, cfg_id, T):
+    import workloads as W
+    from tests.harness import host_array, margin_tokens
+    c = W.CONFIGS[cfg_id]
+    if fmt == 8 and (c["H"] % 16 or c["I"] % 16):
+        pytest.skip("fp8 rows must be whole 16-byte multiples (H and I % 16 == 0)")
+    log(f"layer {NAMES[fmt]} cfg {cfg_id} T {T}")
+    L = fmt_layer(cfg_id, fmt)
+    x = margin_tokens(cfg_id, T, host_array(L.w_router), L.bias_np, c["K"])
+    y, idx, gates = L.forward(x)
+    oracle_fmt_check(L, x, y, idx, gates)
