@@ -497,6 +497,8 @@ def main():
     if "formats" in legs:
         log("[bench] sibling-format matrix-vector products")
         result["formats_matvec_t1"] = run_formats(coli, W)
+        log("[bench] the decode layer in each format")
+        result["formats_layer_t1"] = run_format_layers(coli, W)
     if "prefill" in legs:
         log("[bench] prefill T=2048")
         result["prefill"] = run_prefill(coli, W, layers[0],
@@ -786,6 +788,60 @@ def run_formats(coli, W, steps=50, warmup=5):
     torch.cuda.empty_cache()
     return {"workload": f"y = W^ x, W [{O}, {I}] (the gate and up rows of 9 units), T = 1 "
                         "fp32 token", "formats": out}
+
+
+def run_format_layers(coli, W, steps=200, warmup=20, pool_n=64):
+    """The single-token decode layer with its experts in each sibling format
+    (coli_moe_forward_fmt): tokens/s and HBM GB/s over the algorithmic bytes of a
+    step (router, the 9 units' blobs in the format, x and y).  One copy of each
+    layer (257 blobs), rotating 64 tokens, so consecutive steps read different
+    experts and the Infinity Cache serves little."""
+    import torch
+    c = W.CONFIGS[1]
+    H, I, E, K = c["H"], c["I"], c["E"], c["K"]
+    wr = W.router_weights(1, "cuda").contiguous()
+    pool = W.token_pool(1, pool_n, "cuda").contiguous()
+    out = {}
+    for fmt, name in ((4, "int4-g64"), (5, "int3-g64"), (7, "mxfp4"), (8, "fp8-e4m3-b128")):
+        nb = coli.coli_fmt_blob_bytes(fmt, H, I)
+        experts = torch.empty(E * nb, dtype=torch.uint8, device="cuda")
+        shared = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        for e in range(E + 1):
+            wg, wu, wd = W.expert_weights(1, e, "cuda")
+            ptr = shared.data_ptr() if e == E else experts.data_ptr() + e * nb
+            coli.coli_quant_expert_fmt(fmt, ptr, H, I, wg, wu, wd)
+            del wg, wu, wd
+        L = coli.MoELayer(H, I, E, K, wr, experts, shared)
+        ws = torch.empty(coli.coli_moe_fmt_workspace_bytes(L, fmt, 1), dtype=torch.uint8,
+                         device="cuda")
+        y = torch.empty((1, H), device="cuda")
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        args = [(ctypes.byref(L.c), fmt, ctypes.c_void_p(pool[p:p + 1].data_ptr()), 1,
+                 ctypes.c_void_p(y.data_ptr()), None, None, None,
+                 ctypes.c_void_p(ws.data_ptr()), ws.numel(), st) for p in range(pool_n)]
+        for i in range(warmup):
+            coli.lib.coli_moe_forward_fmt(*args[i % pool_n])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            rc = coli.lib.coli_moe_forward_fmt(*args[i % pool_n])
+            if rc:
+                raise RuntimeError(f"coli_moe_forward_fmt: {rc}")
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        wq = 2 * sum(coli.coli_fmt_bytes(fmt, I, H)) + sum(coli.coli_fmt_bytes(fmt, H, I))
+        nbytes = E * H * 2 + (K + 1) * wq + 2 * H * 4
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us_per_step": round(1e3 * ms, 2), "tokens_per_s": round(1e3 / ms, 1),
+                     "bytes_per_step": nbytes, "gbps": round(gbps, 1),
+                     "frac": round(gbps / HBM_PEAK_GBS, 4)}
+        del experts, shared, L, ws
+        torch.cuda.empty_cache()
+    return {"workload": "decode T=1 of the H=6144 I=2048, 256 experts top-8 + 1 shared layer "
+                        "with its experts in each format (one copy, 64-token pool)",
+            "formats": out}
 
 
 def build_layer_bias(coli, W, layers):

@@ -660,12 +660,15 @@ __global__ __launch_bounds__(256) void fmt_combine(const float *__restrict__ par
   if (status && !__builtin_isfinite(s)) atomicOr(status, COLI_STATUS_NONFINITE);
 }
 
+// Blocks per matrix: about 1024 in all (four per CU), so that each block's x
+// stage serves many row groups; grouped launches split them over the units.
 template <int FMT, int T, int MODE>
-int matvec_grid(int64_t O) {
+int matvec_grid(int64_t O, int units) {
   constexpr int RM = MODE == kModeGateUp ? rows_per_step<FMT, T>() / 2 : rows_per_step<FMT, T>();
   const int64_t groups = (O + RM - 1) / RM;
   const int64_t want = cdiv(groups, 4);
-  return int(want < 1024 ? want : 1024);
+  const int64_t cap = cdiv(1024, units);
+  return int(want < cap ? want : cap);
 }
 
 template <int FMT, int MODE, int TT>
@@ -679,7 +682,7 @@ void launch_one(const MatvecArgs &a, int units, size_t lds, hipStream_t s) {
   }();  // once per process
   (void)done;
   hipLaunchKernelGGL((matvec_kernel<FMT, TT, MODE>),
-                     dim3(matvec_grid<FMT, TT, MODE>(a.O), unsigned(units)), dim3(256), lds, s, a);
+                     dim3(matvec_grid<FMT, TT, MODE>(a.O, units), unsigned(units)), dim3(256), lds, s, a);
 }
 
 template <int FMT, int MODE>
