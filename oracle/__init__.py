@@ -15,7 +15,10 @@ Every function names the passage it follows in the C source's comments:
   and page "colibrì 路由遥测全解析", sections 分离计数与追踪 and 测试与 CI 保障;
   the sigmoid router ("n_group=1 sigmoid + noaux_tc") of the same section 十一;
 * batch-union permute -- page "Colibrì 深度解析", section 四;
-* expert FFN, combine, RMSNorm -- the readings listed in the design doc.
+* expert FFN, combine, RMSNorm -- read as: h = SiLU(gate) * up with
+  SiLU(z) = z / (1 + e^-z), y = sum_k g_k * down_k(h_k) + the shared expert's
+  down(h) with weight 1 (no routed scaling factor), RMSNorm with unit weight,
+  eps 1e-6 and no residual (the pages name these stages without formulas).
 
 Plain-Python modules beside it: ``tier.py`` (expert placement), ``usage.py`` (the
 .coli_usage history) and ``formats.py`` (the sibling weight formats of the

@@ -21,7 +21,7 @@ Sources (page titles and sections):
 * fp8 e4m3: the OCP 8-bit floating point specification: E4M3 with bias 7, no
   infinities, largest finite 448, smallest subnormal 2^-9.
 
-Readings, where the pages give a format's name only (each listed in the design doc):
+Readings, where the pages give a format's name only:
 * F1 sizes, G = ceil(I / 64): 0 f32: 4 O I bytes, no scales; 1 int8-row: O I, f32
   per row; 2 int4-row: O ceil(I/2), f32 per row; 3 int2-row: O ceil(I/4), f32 per
   row; 4 int4-g64: 32 O G, f32 per group; 5 int3-g64: 24 O G (64 three-bit codes),

@@ -3,7 +3,8 @@
 Expert matmul on int4-g64 planar weights: page "从源码开始colibri纯C引擎的编译、权重转换与
 .bin直映射实战", section 权重转换 (the expert FFN consumes the converter's bytes
 directly; dequantised weight = s * (u - 8)).  SiLU(gate)*up then down, the
-gate-weighted combine and the shared expert are the readings listed in the design doc.
+gate-weighted combine and the shared expert with weight 1 are this build's reading
+of the stages the pages name without formulas.
 Each test reduces the oracle to library routines (torch fp64) or to closed forms.
 """
 import numpy as np
