@@ -533,10 +533,28 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
         coli.coli_quant_expert(experts0.data_ptr() + e * nb, H, I, *draws[e], status,
                                finish=False)
     q1.record()
+    # the same 768 matrices in two batched launches (gate and up [I, H], down [H, I])
+    views = [coli.coli_expert_views(experts0.data_ptr() + e * nb, H, I) for e in range(E)]
+
+    def ptrs(vals):
+        return torch.tensor(vals, dtype=torch.int64, device="cuda")
+    gu_w = ptrs([draws[e][m].data_ptr() for e in range(E) for m in (0, 1)])
+    gu_q = ptrs([views[e][m][0] for e in range(E) for m in (0, 1)])
+    gu_s = ptrs([views[e][m][1] for e in range(E) for m in (0, 1)])
+    d_w = ptrs([draws[e][2].data_ptr() for e in range(E)])
+    d_q = ptrs([views[e][2][0] for e in range(E)])
+    d_s = ptrs([views[e][2][1] for e in range(E)])
+    torch.cuda.synchronize()
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record()
+    coli.coli_quant_int4_g64_many(gu_w, gu_q, gu_s, 2 * E, I, H, status)
+    coli.coli_quant_int4_g64_many(d_w, d_q, d_s, E, H, I, status)
+    m1.record()
     for e in range(E):  # the group-major scale copies, outside the timed region
         coli.coli_expert_finish(experts0.data_ptr() + e * nb, H, I)
     torch.cuda.synchronize()
     q_ms = q0.elapsed_time(q1)
+    qm_ms = m0.elapsed_time(m1)
     del draws
     torch.cuda.empty_cache()
     for l in range(NL):
@@ -601,9 +619,11 @@ def run_stack(coli, W, steps, warmup, pool_n=4, cfg_id=4, layers=None):
                                      "max": max(U)},
         "hbm": {"bytes_per_step": step_bytes, "gbps": round(gbps, 1),
                 "frac": round(gbps / HBM_PEAK_GBS, 4)},
-        "quantiser": {"experts": E, "ms": round(q_ms, 3), "bytes": q_bytes,
-                      "gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
-                      "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "quantiser": {"experts": E, "launches": 2, "ms": round(qm_ms, 3), "bytes": q_bytes,
+                      "gbps": round(q_bytes / (qm_ms * 1e-3) / 1e9, 1),
+                      "frac": round(q_bytes / (qm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "per_matrix_launches": {"launches": 3 * E, "ms": round(q_ms, 3),
+                                              "gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)}},
         "data": "synthetic", "dtype": "f32",
     }
 

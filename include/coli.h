@@ -131,6 +131,19 @@ int coli_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
                         uint8_t *packed, float *scales, int32_t *status,
                         void *stream);
 
+/*
+ * The same quantiser over n matrices of one shape [rows, cols] in one launch
+ * (for whole layers: fewer launch tails than n calls).  w, packed, scales:
+ * DEVICE arrays of n device pointers (8-byte aligned); each matrix follows the
+ * rules and alignments of coli_quant_int4_g64 (an fp32 matrix that is not
+ * 16-byte aligned takes element loads).  Bytes are identical to n separate
+ * calls.  Errors: EINVAL (NULL arrays), ESHAPE (n outside [0, 65535], rows < 0,
+ * cols < 1), EALIGN, EDEVICE.
+ */
+int coli_quant_int4_g64_many(const float *const *w, uint8_t *const *packed,
+                             float *const *scales, int n, int64_t rows, int64_t cols,
+                             int32_t *status, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* route (page "Colibrì 深度解析", section 十一)                           */
 /* ---------------------------------------------------------------------- */

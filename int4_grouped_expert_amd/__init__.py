@@ -65,6 +65,7 @@ EXPORTS = [
     "coli_cache_repin", "coli_cache_stage", "coli_cache_slot_map", "coli_fmt_bytes",
     "coli_resolve_fmt", "coli_quant_fmt", "coli_matvec_fmt", "coli_fmt_blob_bytes",
     "coli_quant_expert_fmt", "coli_moe_fmt_workspace_bytes", "coli_moe_forward_fmt",
+    "coli_quant_int4_g64_many",
 ]
 
 _p = ctypes.c_void_p
@@ -99,6 +100,7 @@ _proto("coli_strerror", ctypes.c_char_p, [_i])
 _proto("coli_int4_g64_packed_bytes", _sz, [_i64, _i64])
 _proto("coli_int4_g64_scale_count", _sz, [_i64, _i64])
 _proto("coli_quant_int4_g64", _i, [_p, _i64, _i64, _p, _p, _p, _p])
+_proto("coli_quant_int4_g64_many", _i, [_p, _p, _p, _i, _i64, _i64, _p, _p])
 _proto("coli_router_topk", _i, [_p, _i, _i, _i, _p, _i, _i, _p, _i, _p, _p, _p, _p])
 _proto("coli_router_topk_scored", _i, [_p, _i, _i, _i, _p, _i, _i, _p, _i, _i, _p, _p, _p, _p])
 _proto("coli_expert_permute_workspace_bytes", _sz, [_i, _i, _i])
@@ -209,6 +211,15 @@ def coli_quant_int4_g64(w, packed, scales, status=None, stream=None):
     rows, cols = w.shape
     return _check(lib.coli_quant_int4_g64(_ptr(w), rows, cols, _ptr(packed), _ptr(scales),
                                           _ptr(status), _stream(stream)), "coli_quant_int4_g64")
+
+
+def coli_quant_int4_g64_many(w_ptrs, packed_ptrs, scale_ptrs, n: int, rows: int, cols: int,
+                             status=None, stream=None):
+    """n matrices of one shape in one launch: the three pointer arguments are int64
+    device tensors [n] holding the matrices' device addresses."""
+    return _check(lib.coli_quant_int4_g64_many(_ptr(w_ptrs), _ptr(packed_ptrs),
+                                               _ptr(scale_ptrs), n, rows, cols, _ptr(status),
+                                               _stream(stream)), "coli_quant_int4_g64_many")
 
 
 def coli_router_topk(x, w_router, bias, K, topk_idx, topk_gate, logits=None, stream=None,

@@ -265,6 +265,20 @@ int coli_expert_finish(uint8_t *blob, int H, int I, void *stream) {
   return dev_status(launch_expert_finish(blob, blob_layout(H, I), H, I, as_stream(stream)));
 }
 
+int coli_quant_int4_g64_many(const float *const *w, uint8_t *const *packed, float *const *scales,
+                             int n, int64_t rows, int64_t cols, int32_t *status, void *stream) {
+  if (!w || !packed || !scales) return COLI_EINVAL;
+  if (n < 0 || n > 65535 || rows < 0 || cols < 1 || rows > (int64_t(1) << 31) ||
+      cols > (int64_t(1) << 31))
+    return COLI_ESHAPE;
+  if (!aligned(w, 8) || !aligned(packed, 8) || !aligned(scales, 8) ||
+      (status && !aligned(status, 4)))
+    return COLI_EALIGN;
+  if (n == 0 || rows == 0) return COLI_OK;
+  return dev_status(launch_quant_int4_g64_many(w, packed, scales, n, rows, cols, status,
+                                               as_stream(stream)));
+}
+
 int coli_quant_expert(uint8_t *blob, int H, int I, const float *w_gate, const float *w_up,
                       const float *w_down, int32_t *status, void *stream) {
   if (!blob || !w_gate || !w_up || !w_down) return COLI_EINVAL;

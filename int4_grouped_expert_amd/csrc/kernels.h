@@ -140,6 +140,11 @@ int forward_arg_check(const coli_moe_layer *L, coli_mode mode, const void *x, in
 hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
                                  uint8_t *packed, float *scales,
                                  int32_t *status, hipStream_t s);
+// n matrices of one shape [rows, cols] in one launch; the pointer arrays are
+// device memory.
+hipError_t launch_quant_int4_g64_many(const float *const *w, uint8_t *const *packed,
+                                      float *const *scales, int n, int64_t rows, int64_t cols,
+                                      int32_t *status, hipStream_t s);
 
 // ---- route.hip ----------------------------------------------------------
 // logits[t, e] = x[t] . Wr[e] + b[e]; x fp32 (x_bf16 = 0) or bf16.

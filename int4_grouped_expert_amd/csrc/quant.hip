@@ -51,13 +51,12 @@ __device__ inline bool near_half(float qa) {
   return fabsf((t - floorf(t)) - 0.5f) < 0x1p-17f;
 }
 
+// One team's 64-group (unit = group index over rows * G).
 template <bool kVec>
-__global__ __launch_bounds__(kBlock) void quant_int4_g64_kernel(
+__device__ __attribute__((always_inline)) inline void quant_group(
     const float *__restrict__ w, int64_t rows, int64_t cols, int64_t G,
-    uint8_t *__restrict__ packed, float *__restrict__ scales,
-    int32_t *__restrict__ status) {
-  const int64_t unit = (int64_t(blockIdx.x) * kBlock + threadIdx.x) / kTeam;
-  const int j = threadIdx.x % kTeam;
+    uint8_t *__restrict__ packed, float *__restrict__ scales, int32_t *__restrict__ status,
+    int64_t unit, int j) {
   const bool live = unit < rows * G;
   const int64_t r = live ? unit / G : 0;
   const int64_t g = live ? unit % G : 0;
@@ -123,6 +122,32 @@ __global__ __launch_bounds__(kBlock) void quant_int4_g64_kernel(
   }
 }
 
+template <bool kVec>
+__global__ __launch_bounds__(kBlock) void quant_int4_g64_kernel(
+    const float *__restrict__ w, int64_t rows, int64_t cols, int64_t G,
+    uint8_t *__restrict__ packed, float *__restrict__ scales,
+    int32_t *__restrict__ status) {
+  quant_group<kVec>(w, rows, cols, G, packed, scales, status,
+                    (int64_t(blockIdx.x) * kBlock + threadIdx.x) / kTeam, threadIdx.x % kTeam);
+}
+
+// Many matrices of one shape in one launch: matrix blockIdx.y, its pointers
+// read from the device arrays (the 16-byte loads where that matrix allows).
+__global__ __launch_bounds__(kBlock) void quant_int4_g64_many(
+    const float *const *__restrict__ w, uint8_t *const *__restrict__ packed,
+    float *const *__restrict__ scales, int64_t rows, int64_t cols, int64_t G,
+    int32_t *__restrict__ status) {
+  const float *wm = w[blockIdx.y];
+  uint8_t *pm = packed[blockIdx.y];
+  float *sm = scales[blockIdx.y];
+  const int64_t unit = (int64_t(blockIdx.x) * kBlock + threadIdx.x) / kTeam;
+  const int j = threadIdx.x % kTeam;
+  if ((cols % 4) == 0 && (reinterpret_cast<uintptr_t>(wm) & 15) == 0)
+    quant_group<true>(wm, rows, cols, G, pm, sm, status, unit, j);
+  else
+    quant_group<false>(wm, rows, cols, G, pm, sm, status, unit, j);
+}
+
 // Scales [rows][G] -> [G][rows] through 32 x 33 LDS tiles (coalesced reads
 // and writes).  Block (32, 8): tile (blockIdx.x: groups, blockIdx.y: rows).
 __global__ __launch_bounds__(256) void scales_group_major(const float *__restrict__ src,
@@ -162,6 +187,19 @@ __global__ void write_tag(uint4 *dst, uint4 tag) {
 }
 
 }  // namespace
+
+hipError_t launch_quant_int4_g64_many(const float *const *w, uint8_t *const *packed,
+                                      float *const *scales, int n, int64_t rows, int64_t cols,
+                                      int32_t *status, hipStream_t s) {
+  const int64_t G = groups_of(cols);
+  const int64_t units = rows * G;
+  if (units == 0 || n == 0) return hipSuccess;
+  const int64_t per_block = kBlock / kTeam;
+  const int64_t blocks = (units + per_block - 1) / per_block;
+  quant_int4_g64_many<<<dim3(unsigned(blocks), unsigned(n)), kBlock, 0, s>>>(
+      w, packed, scales, rows, cols, G, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_expert_finish(uint8_t *blob, const BlobLayout &lay, int H, int I,
                                 hipStream_t s) {

@@ -292,6 +292,19 @@ def test_format_layer_rejects_before_launch():
         assert coli.coli_fmt_blob_bytes(fmt, H, I) == want
 
 
+def test_quant_many_rejects_before_launch():
+    L = coli.lib
+    a = P(1 << 20)
+    assert L.coli_quant_int4_g64_many(None, a, a, 3, 64, 64, None, None) == coli.COLI_EINVAL
+    assert L.coli_quant_int4_g64_many(a, a, a, -1, 64, 64, None, None) == coli.COLI_ESHAPE
+    assert L.coli_quant_int4_g64_many(a, a, a, 70000, 64, 64, None, None) == coli.COLI_ESHAPE
+    assert L.coli_quant_int4_g64_many(a, a, a, 3, 64, 0, None, None) == coli.COLI_ESHAPE
+    assert L.coli_quant_int4_g64_many(P((1 << 20) + 4), a, a, 3, 64, 64, None, None) == \
+        coli.COLI_EALIGN
+    assert L.coli_quant_int4_g64_many(a, a, a, 0, 64, 64, None, None) == coli.COLI_OK
+    assert L.coli_quant_int4_g64_many(a, a, a, 3, 0, 64, None, None) == coli.COLI_OK
+
+
 def test_rmsnorm_rejects():
     L = coli.lib
     a = P(4096)

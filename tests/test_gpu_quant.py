@@ -167,3 +167,37 @@ def test_deterministic_twice():
     a = gpu_quant(w)
     b = gpu_quant(w)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("n,rows,cols,offset", [(5, 96, 320, 0), (3, 33, 200, 1), (12, 256, 6144, 0)])
+def test_many_matrices_in_one_launch(n, rows, cols, offset):
+    """coli_quant_int4_g64_many: every matrix's bytes and scale bits equal the oracle's
+    (and so the single-matrix calls'); one matrix starts 4 bytes past 16-byte
+    alignment when offset is set (the element-load path inside the batched launch);
+    a non-finite element in one matrix sets the status flag."""
+    import int4_grouped_expert_amd as coli
+    log(f"quant many n {n} rows {rows} cols {cols} offset {offset}")
+    rng = np.random.default_rng(n * 1000 + rows + cols)
+    ws = [(rng.standard_normal((rows, cols)) * 0.02 * 2.0 ** rng.integers(-8, 8)).astype(np.float32)
+          for _ in range(n)]
+    ws[0][1, 3] = np.nan
+    G = -(-cols // 64)
+    buf = torch.empty(n * rows * cols + 4, dtype=torch.float32, device="cuda")
+    wd = []
+    for i, w in enumerate(ws):
+        base = i * rows * cols + (1 if (offset and i == n - 1) else 0)
+        t = buf[base:base + rows * cols].view(rows, cols)
+        t.copy_(torch.from_numpy(w))
+        wd.append(t)
+    packed = [torch.full((rows, G * 32), 0x5A, dtype=torch.uint8, device="cuda")
+              for _ in range(n)]
+    scales = [torch.full((rows, G), 7.0, dtype=torch.float32, device="cuda") for _ in range(n)]
+    ptr = lambda ts: torch.tensor([t.data_ptr() for t in ts], dtype=torch.int64, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    coli.coli_quant_int4_g64_many(ptr(wd), ptr(packed), ptr(scales), n, rows, cols, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 1
+    for i, w in enumerate(ws):
+        pr, sr, _ = oracle.quant_int4_g64(w)
+        assert np.array_equal(packed[i].cpu().numpy(), pr), i
+        assert np.array_equal(scales[i].cpu().numpy().view(np.uint32), sr.view(np.uint32)), i
