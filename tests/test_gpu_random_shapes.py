@@ -58,3 +58,31 @@ def test_random_shape(cfg_id, cfg):
     y, idx, gates = L.forward(x, mode)
     torch.cuda.synchronize()
     oracle_check(cfg_id, L, x, y, idx, gates, mode)
+
+
+CACHE_CASES = [c for c in CASES if c[1]["T"] * c[1]["K"] < c[1]["E"] or c[1]["T"] <= 3][:8]
+
+
+@pytest.mark.parametrize("cfg_id,cfg", CACHE_CASES, ids=[c[1]["name"] for c in CACHE_CASES])
+def test_random_shape_through_cache(cfg_id, cfg):
+    """The same shapes through the two-phase forward and an expert cache of fewer
+    slots than experts where the batch allows: bit-identical to the resident
+    forward over a few batches."""
+    import int4_grouped_expert_amd as coli
+    from tests.test_gpu_cache import CachedLayer, same
+    W.CONFIGS[cfg_id] = cfg
+    c = cfg
+    mode = PREFILL if c["mode"] == "prefill" else DECODE
+    S = min(c["E"], max(1, c["T"] * c["K"]) + 1)
+    log(f"random shape through cache {c['name']}: E {c['E']} S {S} T {c['T']} {c['mode']}")
+    L = DeviceLayer(cfg_id)
+    cl = CachedLayer(coli, L, S)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for b in range(4):
+        x = W.tokens(cfg_id, c["T"], "cuda", draw=40 + b)
+        y_ref, idx_ref, _ = L.forward(x, mode)
+        y, idx, _ = cl.forward(x, mode, st, repin=(b == 2))
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert torch.equal(idx, idx_ref)
+        assert same(y, y_ref), f"batch {b}"
