@@ -233,6 +233,12 @@ typedef struct {
  *            `experts`.  Otherwise `experts` holds cache slots and expert e's
  *            blob is slot slot_map[e] (see coli_cache); an expert routed while
  *            its entry is -1 gives NaN outputs and COLI_STATUS_NOT_RESIDENT.
+ *   usage: device uint64 [E] or NULL.  When set, every forward (and
+ *            coli_moe_route) adds to usage[e] the number of its (token, slot)
+ *            routing decisions that chose expert e, inside its routing kernels
+ *            (the counters of the .coli_usage history, page "colibrì 路由遥测
+ *            全解析", section 历史文件 .coli_usage: point it at this layer's row of
+ *            the counts coli_usage_save writes).  8-byte aligned.
  * H and I may be any value in [1, MAX_DIM]: a row whose length is not a
  * multiple of 64 ends in a zero-padded group (the quantiser pads it so).
  */
@@ -245,6 +251,7 @@ typedef struct {
     const uint8_t *shared;
     coli_scoring scoring;
     const int32_t *slot_map;
+    uint64_t *usage;
 } coli_moe_layer;
 
 /*

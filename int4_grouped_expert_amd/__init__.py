@@ -81,7 +81,7 @@ class coli_q4(ctypes.Structure):
 class coli_moe_layer(ctypes.Structure):
     _fields_ = [("H", _i), ("I", _i), ("E", _i), ("K", _i), ("w_router", _p),
                 ("router_dtype", _i), ("router_bias", _p), ("experts", _p), ("shared", _p),
-                ("scoring", _i), ("slot_map", _p)]
+                ("scoring", _i), ("slot_map", _p), ("usage", _p)]
 
 
 class coli_cache(ctypes.Structure):
@@ -260,18 +260,20 @@ class MoELayer:
     shared:  uint8 tensor of one blob; w_router: [E, H] fp32 or bf16; bias: [E] fp32 or None;
     scoring: COLI_SCORE_SOFTMAX or COLI_SCORE_SIGMOID; slot_map: None, or an int32 device
     tensor [E] mapping each expert to its blob in `experts` (then the cache slots; -1:
-    not resident).
+    not resident); usage: None, or an int64 device tensor [E] (uint64 counters) that
+    every forward adds its routing decisions to.
     """
 
     def __init__(self, H, I, E, K, w_router, experts, shared, bias=None,
-                 scoring=COLI_SCORE_SOFTMAX, slot_map=None):
+                 scoring=COLI_SCORE_SOFTMAX, slot_map=None, usage=None):
         self.H, self.I, self.E, self.K = H, I, E, K
         self.w_router, self.experts, self.shared, self.bias = w_router, experts, shared, bias
-        self.scoring, self.slot_map = scoring, slot_map
+        self.scoring, self.slot_map, self.usage = scoring, slot_map, usage
         self.c = coli_moe_layer(H, I, E, K, w_router.data_ptr(), _dtype(w_router),
                                 None if bias is None else bias.data_ptr(), experts.data_ptr(),
                                 shared.data_ptr(), scoring,
-                                None if slot_map is None else slot_map.data_ptr())
+                                None if slot_map is None else slot_map.data_ptr(),
+                                None if usage is None else usage.data_ptr())
 
     def workspace_bytes(self, T: int, mode: int) -> int:
         return int(lib.coli_moe_workspace_bytes(ctypes.byref(self.c), T, mode))

@@ -98,6 +98,7 @@ WsLayout ws_layout(int H, int I, int E, int K, int T, coli_mode mode) {
 
 Routing carve(uint8_t *ws, const WsLayout &w) {
   Routing r;
+  r.usage = nullptr;
   r.logits = reinterpret_cast<float *>(ws + w.logits);
   r.idx = reinterpret_cast<int32_t *>(ws + w.idx);
   r.gates = reinterpret_cast<float *>(ws + w.gates);
@@ -331,7 +332,8 @@ int forward_checks(const coli_moe_layer *L, coli_mode mode, const void *x, int T
       !aligned(L->w_router, L->router_dtype == COLI_BF16 ? 2 : 4) ||
       !aligned(L->experts, 256) || !aligned(L->shared, 256) ||
       (L->router_bias && !aligned(L->router_bias, 4)) ||
-      (L->slot_map && !aligned(L->slot_map, 4)) || (topk_idx_out && !aligned(topk_idx_out, 4)) ||
+      (L->slot_map && !aligned(L->slot_map, 4)) || (L->usage && !aligned(L->usage, 8)) ||
+      (topk_idx_out && !aligned(topk_idx_out, 4)) ||
       (topk_gate_out && !aligned(topk_gate_out, 4)) || (status && !aligned(status, 4)))
     return COLI_EALIGN;
   const int tl = mode == COLI_DECODE ? decode_chunk_t(T) : T;
@@ -353,6 +355,7 @@ LayerDev layer_dev(const coli_moe_layer *L, int32_t *status, const Scoring &sc) 
   d.status = status;
   d.sc = sc;
   d.slot_map = L->slot_map;
+  d.usage = reinterpret_cast<unsigned long long *>(L->usage);
   return d;
 }
 
@@ -371,6 +374,7 @@ CallBufs carve_call(const coli_moe_layer *L, uint8_t *ws, const WsLayout &w,
   if (topk_gate_out) c.r.gates = topk_gate_out;
   const bool sig = L->scoring == COLI_SCORE_SIGMOID;
   c.r.sc = Scoring{sig ? 1 : 0, sig ? L->router_bias : nullptr};
+  c.r.usage = reinterpret_cast<unsigned long long *>(L->usage);
   c.nb.xdig = reinterpret_cast<int8_t *>(ws + w.xdig);
   c.nb.xcorr = reinterpret_cast<int32_t *>(ws + w.xcorr);
   c.nb.xsc = reinterpret_cast<float *>(ws + w.nxsc);
@@ -656,6 +660,7 @@ int coli_moe_forward_fmt(const coli_moe_layer *L, int fmt, const float *x, int T
   if (topk_gate_out) r.gates = topk_gate_out;
   const bool sig = L->scoring == COLI_SCORE_SIGMOID;
   r.sc = Scoring{sig ? 1 : 0, sig ? L->router_bias : nullptr};
+  r.usage = reinterpret_cast<unsigned long long *>(L->usage);
   const float *lbias = sig ? nullptr : L->router_bias;
   const int wbf = L->router_dtype == COLI_BF16;
   hipError_t e = router_vec_ok(x, 0, L->H, L->w_router, wbf)

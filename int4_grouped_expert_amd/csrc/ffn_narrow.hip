@@ -247,6 +247,8 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   if (!pre_routed && blockIdx.x == 0 && int(threadIdx.x) < K) {
     idx_out[threadIdx.x] = sidx[threadIdx.x];
     gate_out[threadIdx.x] = sgate[threadIdx.x];
+    // the routing history: one decision per selected expert
+    if (L.usage) atomicAdd(L.usage + sidx[threadIdx.x], 1ull);
   }
   wait_all_loads();
   int buf = 0, k_it = 0;

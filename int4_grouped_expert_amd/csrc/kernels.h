@@ -74,6 +74,7 @@ struct Routing {
   int32_t *n_unique; // [1]
   int32_t *chunk;    // [n_chunks * E] per-chunk counts / bases (large T)
   Scoring sc;        // how the top-K scores the logits
+  unsigned long long *usage;  // [E] routing-history counters to add the counts to, or NULL
 };
 
 
@@ -113,6 +114,7 @@ struct LayerDev {
   int32_t *status;  // optional device flag: COLI_STATUS_* bits OR-ed in
   Scoring sc;       // router scoring (the fused single-token top-K)
   const int32_t *slot_map;  // expert -> cache slot of `experts`, or NULL (identity)
+  unsigned long long *usage;  // routing-history counters [E] (the fused top-K adds), or NULL
 };
 
 // Blob of routed expert e.  With a slot map, e's blob is its slot; an expert

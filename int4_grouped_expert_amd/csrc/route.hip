@@ -535,6 +535,7 @@ __device__ void finish_counts(const Routing &r, int T, int K, int E, int cnt_e,
   if (e < E) {
     r.counts[e] = v;
     r.offsets[e] = excl;
+    if (r.usage && v > 0) atomicAdd(r.usage + e, (unsigned long long)v);  // the history
   }
   if (e == 0) r.offsets[E] = *total;
   const int flag = (e < E && v > 0) ? 1 : 0;

@@ -181,6 +181,9 @@ def test_forward_rejects_before_launch():
     assert call(layer=unal) == coli.COLI_EALIGN
     badt = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, 3, None, 1 << 21, 1 << 22)
     assert call(layer=badt) == coli.COLI_EDTYPE
+    badu = coli.coli_moe_layer(256, 128, 16, 4, 1 << 20, coli.COLI_F32, None, 1 << 21, 1 << 22,
+                               0, None, (1 << 23) + 4)
+    assert call(layer=badu) == coli.COLI_EALIGN  # routing-history counters: 8-byte aligned
 
 
 def test_two_phase_rejects_before_launch():
