@@ -347,6 +347,33 @@ def cpu_baseline(coli, W, budget_s=6.0, n_tok=6):
             "legs": legs}
 
 
+def profile_fields(path, kernel_src):
+    """The machine-read fields of a committed profile summary, or None when that
+    summary was taken on a different version of the kernel's source file."""
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    src = open(os.path.join(ROOT, kernel_src), "rb").read()
+    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return fields
+
+
+def profiled_launch_ms(kernel_src):
+    """gateup_narrow's kernel-trace average (ms) from profiles/decode_t1_kernels.md, or
+    None when the summary is of another source version."""
+    f = profile_fields(os.path.join(ROOT, "profiles", "decode_t1_kernels.md"), kernel_src)
+    try:
+        return None if f is None else float(f["gateup_narrow_avg_us"]) * 1e-3
+    except (KeyError, ValueError):
+        return None
+
+
 def profiled_traffic(kernel_src, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (profiles/<kernel>_decode_t1_traffic.md), or None when that summary was taken
@@ -449,6 +476,11 @@ def main():
                                                  "gateup_narrow"),
                      "bytes_per_launch": gu_bytes, "avg_launch_ms": round(gu_ms, 5)},
     }
+    prof_ms = profiled_launch_ms("int4_grouped_expert_amd/csrc/ffn_narrow.hip")
+    if prof_ms is not None:
+        # the committed kernel-trace average of the same source (profiles/)
+        result["roofline"]["profiled_avg_launch_ms"] = round(prof_ms, 5)
+        result["roofline"]["profiled_frac"] = round(gu_bytes / prof_ms * 1e-6 / HBM_PEAK_GBS, 4)
     legs = set() if args.no_extras else set(args.legs.split(","))
     if "single" in legs:
         log("[bench] decode T=1, one replica (its 191 MB fit the 256 MB Infinity Cache)")
