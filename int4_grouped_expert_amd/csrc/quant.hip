@@ -47,19 +47,30 @@ __device__ inline uint32_t nibble_of(float quot) {
 // side of each, and the three round to the same integer.  The rest (a guard
 // band of about 1.5e-5 per unit of quotient) take the IEEE divide.
 __device__ inline bool near_half(float qa) {
-  const float t = fabsf(qa);
-  return fabsf((t - floorf(t)) - 0.5f) < 0x1p-17f;
+  // v_fract_f32 of |qa| (<= 8.5 here) is exactly |qa| - floor(|qa|)
+  return fabsf(__builtin_amdgcn_fractf(fabsf(qa)) - 0.5f) < 0x1p-17f;
 }
 
-// One team's 64-group (unit = group index over rows * G).
-template <bool kVec>
+// One team's 64-group (unit = group index over rows * G).  k32: rows * G
+// < 2^32, so the group's row and column come from a 32-bit divide (a 64-bit
+// one is a long software sequence, a large share of this kernel's ALU work).
+template <bool kVec, bool k32>
 __device__ __attribute__((always_inline)) inline void quant_group(
     const float *__restrict__ w, int64_t rows, int64_t cols, int64_t G,
     uint8_t *__restrict__ packed, float *__restrict__ scales, int32_t *__restrict__ status,
     int64_t unit, int j) {
   const bool live = unit < rows * G;
-  const int64_t r = live ? unit / G : 0;
-  const int64_t g = live ? unit % G : 0;
+  int64_t r = 0, g = 0;
+  if (live) {
+    if (k32) {
+      const uint32_t u = uint32_t(unit), G32 = uint32_t(G), q = u / G32;
+      r = q;
+      g = u - q * G32;
+    } else {
+      r = unit / G;
+      g = unit % G;
+    }
+  }
   const float *src = w + r * cols + g * 64;
 
   float lo[4], hi[4];
@@ -122,17 +133,19 @@ __device__ __attribute__((always_inline)) inline void quant_group(
   }
 }
 
-template <bool kVec>
+template <bool kVec, bool k32>
 __global__ __launch_bounds__(kBlock) void quant_int4_g64_kernel(
     const float *__restrict__ w, int64_t rows, int64_t cols, int64_t G,
     uint8_t *__restrict__ packed, float *__restrict__ scales,
     int32_t *__restrict__ status) {
-  quant_group<kVec>(w, rows, cols, G, packed, scales, status,
-                    (int64_t(blockIdx.x) * kBlock + threadIdx.x) / kTeam, threadIdx.x % kTeam);
+  quant_group<kVec, k32>(w, rows, cols, G, packed, scales, status,
+                         (int64_t(blockIdx.x) * kBlock + threadIdx.x) / kTeam,
+                         threadIdx.x % kTeam);
 }
 
 // Many matrices of one shape in one launch: matrix blockIdx.y, its pointers
 // read from the device arrays (the 16-byte loads where that matrix allows).
+template <bool k32>
 __global__ __launch_bounds__(kBlock) void quant_int4_g64_many(
     const float *const *__restrict__ w, uint8_t *const *__restrict__ packed,
     float *const *__restrict__ scales, int64_t rows, int64_t cols, int64_t G,
@@ -143,9 +156,9 @@ __global__ __launch_bounds__(kBlock) void quant_int4_g64_many(
   const int64_t unit = (int64_t(blockIdx.x) * kBlock + threadIdx.x) / kTeam;
   const int j = threadIdx.x % kTeam;
   if ((cols % 4) == 0 && (reinterpret_cast<uintptr_t>(wm) & 15) == 0)
-    quant_group<true>(wm, rows, cols, G, pm, sm, status, unit, j);
+    quant_group<true, k32>(wm, rows, cols, G, pm, sm, status, unit, j);
   else
-    quant_group<false>(wm, rows, cols, G, pm, sm, status, unit, j);
+    quant_group<false, k32>(wm, rows, cols, G, pm, sm, status, unit, j);
 }
 
 // Scales [rows][G] -> [G][rows] through 32 x 33 LDS tiles (coalesced reads
@@ -196,8 +209,12 @@ hipError_t launch_quant_int4_g64_many(const float *const *w, uint8_t *const *pac
   if (units == 0 || n == 0) return hipSuccess;
   const int64_t per_block = kBlock / kTeam;
   const int64_t blocks = (units + per_block - 1) / per_block;
-  quant_int4_g64_many<<<dim3(unsigned(blocks), unsigned(n)), kBlock, 0, s>>>(
-      w, packed, scales, rows, cols, G, status);
+  if (units < (int64_t(1) << 32))
+    quant_int4_g64_many<true><<<dim3(unsigned(blocks), unsigned(n)), kBlock, 0, s>>>(
+        w, packed, scales, rows, cols, G, status);
+  else
+    quant_int4_g64_many<false><<<dim3(unsigned(blocks), unsigned(n)), kBlock, 0, s>>>(
+        w, packed, scales, rows, cols, G, status);
   return hipGetLastError();
 }
 
@@ -235,12 +252,16 @@ hipError_t launch_quant_int4_g64(const float *w, int64_t rows, int64_t cols,
   const int64_t per_block = kBlock / kTeam;
   const int64_t blocks = (units + per_block - 1) / per_block;
   const bool vec = (cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0);
-  if (vec)
-    quant_int4_g64_kernel<true><<<dim3(unsigned(blocks)), kBlock, 0, s>>>(
-        w, rows, cols, G, packed, scales, status);
+  const bool i32 = units < (int64_t(1) << 32);
+  const dim3 grid{unsigned(blocks)};
+  if (vec && i32)
+    quant_int4_g64_kernel<true, true><<<grid, kBlock, 0, s>>>(w, rows, cols, G, packed, scales, status);
+  else if (vec)
+    quant_int4_g64_kernel<true, false><<<grid, kBlock, 0, s>>>(w, rows, cols, G, packed, scales, status);
+  else if (i32)
+    quant_int4_g64_kernel<false, true><<<grid, kBlock, 0, s>>>(w, rows, cols, G, packed, scales, status);
   else
-    quant_int4_g64_kernel<false><<<dim3(unsigned(blocks)), kBlock, 0, s>>>(
-        w, rows, cols, G, packed, scales, status);
+    quant_int4_g64_kernel<false, false><<<grid, kBlock, 0, s>>>(w, rows, cols, G, packed, scales, status);
   return hipGetLastError();
 }
 
