@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector, TFLOP/s
 METRIC = "MoE-layer decode tokens/s + HBM GB/s (% of peak); prefill MFMA util"
 
 
@@ -186,6 +187,17 @@ def decode_bytes(c, U, T):
     return int(router + (U + 1) * blob + 2 * T * H * 4)
 
 
+def t32_compute_ceiling(c):
+    """The batch's second roofline: its algorithmic multiply-adds (router + K routed +
+    the shared expert's three matrices per token) at the fp32 vector peak.  The GEMMs
+    run on the fp16 matrix cores (exact u - 8 weights, hi/lo activations), whose
+    padded 32-row tiles do more work than this count; HBM is the bound that binds."""
+    H, I, E, K, T = c["H"], c["I"], c["E"], c["K"], c["T"]
+    fma = T * (H * E + (K + 1) * 3 * H * I)
+    return {"fma": fma, "fp32_vector_peak_tflops": FP32_PEAK_TFLOPS,
+            "us_at_peak": round(2 * fma / (FP32_PEAK_TFLOPS * 1e12) * 1e6, 1)}
+
+
 def gateup_bytes(c, U, T):
     H, I = c["H"], c["I"]
     per = 2 * (I * (H // 64) * 32 + I * (H // 64) * 4)
@@ -268,7 +280,8 @@ def cpu_baseline(coli, W, budget_s=6.0, n_tok=6):
       prefill      -- 64 of the 2048 tokens, scaled x 32 (the oracle's time per token
                       does not depend on the batch);
       stack step   -- layer 0 of the 40-layer stack on its 8 tokens, scaled x 40;
-      quantiser    -- 16 of one layer's 256 experts, scaled x 16.
+      quantiser    -- 16 of one layer's 256 experts, scaled x 16;
+      tiny T=1     -- the tiny layer (all 16 experts), 8 tokens cycled for about 0.5 s.
     The headline fields are the T=1 leg's; `legs` holds every leg."""
     import numpy as np
     import oracle
@@ -339,6 +352,20 @@ def cpu_baseline(coli, W, budget_s=6.0, n_tok=6):
     legs["quantise_one_layer"] = {"value": round(el * 1e3 * 16, 1), "unit": "ms per layer",
                                   "sample": f"16 of 256 experts (48 matrices) in {el:.2f} s, "
                                             f"scaled x 16"}
+    c0 = W.CONFIGS[0]
+    wr0 = bits(W.router_weights(0, "cuda"))
+    pool0 = W.token_pool(0, 8, "cuda").cpu().numpy()
+    ex0, sh0 = oracle_layer_experts(W, 0, list(range(c0["E"])))
+    done0 = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) < 0.5:
+        k = done0 % 8
+        oracle.moe_forward(pool0[k:k + 1], wr0, None, ex0, sh0, c0["H"], c0["I"], c0["K"])
+        done0 += 1
+    el = time.perf_counter() - t0
+    legs["tiny_t1"] = {"value": round(done0 / el, 1), "unit": "tokens/s",
+                       "sample": f"{done0} single-token forwards of the tiny layer, "
+                                 f"8 tokens cycled, {el:.2f} s"}
     head = legs["decode_t1"]
     return {"value": head["value"], "unit": "tokens/s", "cores": oracle.threads(),
             "kind": "oracle", "cpu_model": cpu_model(),
@@ -508,7 +535,8 @@ def main():
             "bytes_per_step": int(b32),
             "gbps": round(b32 / (ms32 * 1e-3) / 1e9, 1),
             "frac": round(b32 / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "stage_ms": [round(s, 4) for s in d32["stage_ms"]]}
+            "stage_ms": [round(s, 4) for s in d32["stage_ms"]],
+            "compute_ceiling": t32_compute_ceiling(W.CONFIGS[2])}
     if "cache" in legs:
         log("[bench] decode T=32 zipf through the HBM expert cache")
         result["expert_cache_t32_zipf"] = run_cache(coli, W, zl[0],

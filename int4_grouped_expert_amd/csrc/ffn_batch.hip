@@ -76,6 +76,9 @@ struct DecArgs {
 };
 
 __shared__ float g_rsc[kDMC];  // scale of each chunk token's activation row
+// the batch's chunk prefix (r.chunk[0 .. units + 1]), read once per block: the
+// item decode's binary search then costs no memory round trips
+__shared__ int g_chunk[COLI_MAX_EXPERTS + 2];
 
 // u - 8 as fp16 for the 8 nibbles of word d, in the staged k order
 __device__ inline f16x8 unpack_u8(uint32_t d, uint32_t m1, uint32_t m2) {
@@ -93,10 +96,13 @@ __device__ inline f16x8 unpack_u8(uint32_t d, uint32_t m1, uint32_t m2) {
 // kHalf: a chunk of at most 16 tokens, staged as one 32-row fragment (hi
 // rows 0..15, lo rows 16..31), so that each k-step takes one MFMA per weight
 // fragment instead of two; the hi and lo result rows are added at the end.
+// The item's blob finish tag is loaded with its first weights (its latency
+// hides behind theirs); a blob without the tag, or an expert without a slot,
+// poisons the item's outputs (NaN) and raises the status flag.
 template <bool kGateUp, bool kHalf>
 __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDev &L,
                                                                    const DecArgs &da,
-                                                                   const Item &it, float poison) {
+                                                                   const Item &it, bool missing) {
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x / kWave));
   const int h = lane >> 5, n = lane & 31;
@@ -193,6 +199,7 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
   float F[2][4] = {}, Fr[2][2] = {}, Frn[2][2] = {};
   uint4 R[2][4] = {};
   dma_a(0, g_st0);
+  const uint4 tg = *reinterpret_cast<const uint4 *>(it.blob + L.lay.tag);
   if (wvalid) {
     load_s(0, Fr);
     load_b(0, R);
@@ -200,6 +207,13 @@ __device__ __attribute__((always_inline)) inline void run_item_dec(const LayerDe
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   spread(Fr, F);
+  const bool untagged =
+      tg.x != L.tag.x || tg.y != L.tag.y || tg.z != L.tag.z || tg.w != L.tag.w;
+  if (threadIdx.x == 0) {
+    if (untagged && !missing) raise_status(L.status, COLI_STATUS_UNFINISHED);
+    if (missing) raise_status(L.status, COLI_STATUS_NOT_RESIDENT);
+  }
+  const float poison = (untagged || missing) ? __builtin_nanf("") : 1.0f;
 
   uint32_t m1, m2;
   asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m1));
@@ -324,7 +338,9 @@ __global__ __launch_bounds__(kThreads, 2) void dec_gemm(LayerDev L, Routing r, i
   const int K = L.K;
   const int n_nt = kGateUp ? (L.I + 127) / 128 : (L.H + 255) / 256;
   const int nu = *r.n_unique + 1;
-  const int n_items = r.chunk[nu] * n_nt;
+  for (int i = threadIdx.x; i <= nu; i += kThreads) g_chunk[i] = r.chunk[i];
+  __syncthreads();
+  const int n_items = g_chunk[nu] * n_nt;
   int it0, it1, step;
   if ((gridDim.x & 7) == 0) {
     const int xcd = blockIdx.x & 7, nb = gridDim.x >> 3;
@@ -338,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 2) void dec_gemm(LayerDev L, Routing r, i
   }
   for (int item = it0; item < it1; item += step) {
     Item it;
-    decode_item(L, r, T, item, n_nt, it, kDMC);
+    decode_item(L, r, T, item, n_nt, it, kDMC, g_chunk, nu);
     {
       const uint64_t bp = reinterpret_cast<uint64_t>(it.blob);
       const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(bp));
@@ -385,20 +401,13 @@ __global__ __launch_bounds__(kThreads, 2) void dec_gemm(LayerDev L, Routing r, i
     }
     __syncthreads();
     // a blob without the finish tag has no valid scale copies: its outputs
-    // become NaN and the status flag says why
-    const uint4 tg = *reinterpret_cast<const uint4 *>(it.blob + L.lay.tag);
-    const bool untagged =
-        tg.x != L.tag.x || tg.y != L.tag.y || tg.z != L.tag.z || tg.w != L.tag.w;
+    // become NaN and the status flag says why (checked inside, with the item's
+    // first loads)
     const bool missing = __builtin_amdgcn_readfirstlane(int(it.missing)) != 0;
-    if (threadIdx.x == 0) {
-      if (untagged && !missing) raise_status(L.status, COLI_STATUS_UNFINISHED);
-      if (missing) raise_status(L.status, COLI_STATUS_NOT_RESIDENT);
-    }
-    const float poison = (untagged || missing) ? __builtin_nanf("") : 1.0f;
     if (small)
-      run_item_dec<kGateUp, true>(L, da, it, poison);
+      run_item_dec<kGateUp, true>(L, da, it, missing);
     else
-      run_item_dec<kGateUp, false>(L, da, it, poison);
+      run_item_dec<kGateUp, false>(L, da, it, missing);
   }
 }
 

@@ -666,7 +666,7 @@ __global__ __launch_bounds__(kPThreads, 1) void pf_gemm(LayerDev L, Routing r, i
   }
   for (int item = it0; item < it1; item += step) {
     Item it;
-    decode_item(L, r, T, item, n_nt, it, kMC);
+    decode_item(L, r, T, item, n_nt, it, kMC, r.chunk, *r.n_unique + 1);
     // the item is the same for every lane: keep it in scalar registers
     {
       const uint64_t bp = reinterpret_cast<uint64_t>(it.blob);

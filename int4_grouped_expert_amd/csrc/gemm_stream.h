@@ -36,7 +36,8 @@ __device__ inline int grp_pos(int e) {
   return 8 * c + i;
 }
 
-// Item decode shared by the two GEMMs.
+// Item decode shared by the two GEMMs.  chunk: the batch's per-unit chunk
+// prefix (r.chunk, or a copy of it in LDS), nu = units + 1 (the shared one last).
 struct Item {
   int unit, mchunk, ntile;
   bool shared;
@@ -45,17 +46,16 @@ struct Item {
   int jb, je;  // token rows of the chunk: j in [jb, je)
 };
 __device__ inline void decode_item(const LayerDev &L, const Routing &r, int T, int item, int n_nt,
-                                   Item &it, int mc) {
-  const int nu = *r.n_unique + 1;
+                                   Item &it, int mc, const int *chunk, int nu) {
   const int c = item / n_nt;
   it.ntile = item % n_nt;
   int lo = 0, hi = nu - 1;  // last u with chunk[u] <= c
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (r.chunk[mid] <= c) lo = mid; else hi = mid - 1;
+    if (chunk[mid] <= c) lo = mid; else hi = mid - 1;
   }
   it.unit = lo;
-  it.mchunk = c - r.chunk[lo];
+  it.mchunk = c - chunk[lo];
   it.shared = lo == nu - 1;
   int jb0, je0;
   it.missing = false;
