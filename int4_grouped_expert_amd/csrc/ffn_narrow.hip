@@ -157,6 +157,7 @@ __global__ __launch_bounds__(kW * 8) __attribute__((amdgpu_waves_per_eu(2)))
 void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
                    int32_t *__restrict__ idx_out, float *__restrict__ gate_out, int pre_routed) {
   __shared__ int32_t sidx[COLI_NARROW_MAX_K];
+  __shared__ int32_t sslot[COLI_NARROW_MAX_K];  // with a slot map: the experts' slots (-1: none)
   __shared__ float sgate[COLI_NARROW_MAX_K];
   __shared__ float red[kGateupItems][kGateupMaxWaves][2][8];
   // per wave, double-buffered: the item's group scales [frag][4 NC groups][8 rows]
@@ -203,10 +204,16 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
   };
   // item it = (v, rb): unit v (0 = the shared expert, v >= 1 the routed
   // expert sidx[v - 1]), rows 8 rb .. 8 rb + 7 of I
+  // the blob of unit v (an expert without a slot reads the shared blob: valid
+  // memory, its h' rows are poisoned below)
+  auto unit_blob = [&](int v) {
+    if (v == 0) return L.shared;
+    const int sl = L.slot_map ? sslot[v - 1] : sidx[v - 1];
+    return sl < 0 ? L.shared : L.experts + size_t(sl) * L.lay.bytes;
+  };
   auto ptrs = [&](int it) {
     const int v = it / nrb, rb = it - v * nrb;
-    bool miss = false;
-    const uint8_t *blob = v > 0 ? expert_blob(L, sidx[v - 1], miss) : L.shared;
+    const uint8_t *blob = unit_blob(v);
     const size_t row = size_t(rb) * 8 + r;
     Ptrs p;
     p.wg = blob + L.lay.gq + (row * GH + goff) * 32 + 16 * (q % 2);
@@ -244,6 +251,12 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     topk_select<4>(lg, E, K, lane, sidx, sgate, L.sc);
   }
   lds_barrier();
+  if (L.slot_map) {
+    // the selected experts' slots, looked up once (not per item: a global load
+    // inside the item loop would drain the weight ring every trip)
+    if (int(threadIdx.x) < K) sslot[threadIdx.x] = L.slot_map[sidx[threadIdx.x]];
+    lds_barrier();
+  }
   if (!pre_routed && blockIdx.x == 0 && int(threadIdx.x) < K) {
     idx_out[threadIdx.x] = sidx[threadIdx.x];
     gate_out[threadIdx.x] = sgate[threadIdx.x];
@@ -308,8 +321,8 @@ void gateup_narrow(NarrowBufs nb, LayerDev L, const float *__restrict__ logits,
     const float gw = v > 0 ? sgate[v - 1] : 1.0f;
     // a blob without the finish tag has no valid blocked scales: its h' rows
     // become NaN (and so does y) and the status flag says why
-    bool miss = false;
-    const uint8_t *blob = v > 0 ? expert_blob(L, sidx[v - 1], miss) : L.shared;
+    const bool miss = v > 0 && L.slot_map && sslot[v - 1] < 0;
+    const uint8_t *blob = unit_blob(v);
     const uint4 tg = *reinterpret_cast<const uint4 *>(blob + L.lay.tag);
     const bool untagged = tg.x != L.tag.x || tg.y != L.tag.y || tg.z != L.tag.z || tg.w != L.tag.w;
     const bool bad = untagged || miss;
