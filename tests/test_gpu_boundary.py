@@ -2,8 +2,8 @@
 the oracle: the permute with repeated ids, the router without a logits array, the
 sigmoid router ("n_group=1 sigmoid + noaux_tc", page "Colibrì 深度解析", section 十一),
 ragged H and I (zero-padded last groups, page "从源码开始colibri纯C引擎的编译、权重转换
-与.bin直映射实战", section 权重转换: ngroups = ceil(I / 64)), decode batches longer than
-256 tokens, and the device status flag (fail closed: page "colibrì 路由遥测全解析",
+与.bin直映射实战", section 权重转换: ngroups = ceil(I / 64)), the largest expert count,
+decode batches longer than 256 tokens, and the device status flag (fail closed: page "colibrì 路由遥测全解析",
 section 测试与 CI 保障).
 """
 import numpy as np
@@ -136,6 +136,20 @@ def test_forward_ragged(cfg_id, T, mode):
     # a bf16 draw passed as fp32 keeps its values (and its routing margin)
     assert c["x"] == "bf16" or mode == DECODE
     x = x.to(torch.bfloat16 if mode == PREFILL else torch.float32).contiguous()
+    y, idx, gates = L.forward(x, mode)
+    torch.cuda.synchronize()
+    oracle_check(cfg_id, L, x, y, idx, gates, mode)
+
+
+@pytest.mark.parametrize("cfg_id,T,mode", [(123, 1, DECODE), (123, 5, DECODE),
+                                           (124, 1, DECODE), (124, 2, DECODE),
+                                           (125, 300, PREFILL), (125, 1, PREFILL)])
+def test_forward_max_experts(cfg_id, T, mode):
+    """E = 1024, the largest expert count the boundary accepts, with top-8 and with
+    K = E (every expert selected: the gates are the softmax over all 1024 logits)."""
+    log(f"max experts forward cfg {cfg_id} T {T} mode {mode}")
+    L = layer(cfg_id)
+    x = margin_tokens(cfg_id, T, host_array(L.w_router), L.bias_np, L.K)
     y, idx, gates = L.forward(x, mode)
     torch.cuda.synchronize()
     oracle_check(cfg_id, L, x, y, idx, gates, mode)

@@ -92,6 +92,14 @@ CONFIGS.update({
               bias="zipf", mode="decode", layers=1),
     122: dict(name="ragged_prefill_wide", H=1000, I=330, E=20, K=5, T=150, router="bf16",
               x="bf16", bias="zipf", mode="prefill", layers=1),
+    # the largest expert count the boundary accepts (E = 1024), with top-8 and with
+    # every expert selected (K = E)
+    123: dict(name="max_experts", H=256, I=128, E=1024, K=8, T=5, router="bf16", x="f32",
+              bias=None, mode="decode", layers=1),
+    124: dict(name="max_experts_all_selected", H=128, I=64, E=1024, K=1024, T=2, router="f32",
+              x="f32", bias=None, mode="decode", layers=1),
+    125: dict(name="max_experts_prefill", H=256, I=128, E=1024, K=8, T=300, router="bf16",
+              x="bf16", bias=None, mode="prefill", layers=1),
 })
 
 WEIGHT_STD = 0.02
