@@ -2,7 +2,7 @@
 the oracle: the permute with repeated ids, the router without a logits array, the
 sigmoid router ("n_group=1 sigmoid + noaux_tc", page "Colibrì 深度解析", section 十一),
 ragged H and I (zero-padded last groups, page "从源码开始colibri纯C引擎的编译、权重转换
-与.bin直映射实战", section 权重转换: ngroups = ceil(I / 64)), the largest expert count,
+与.bin直映射实战", section 权重转换: ngroups = ceil(I / 64)), the largest expert count and dimensions,
 decode batches longer than 256 tokens, and the device status flag (fail closed: page "colibrì 路由遥测全解析",
 section 测试与 CI 保障).
 """
@@ -148,6 +148,19 @@ def test_forward_max_experts(cfg_id, T, mode):
     """E = 1024, the largest expert count the boundary accepts, with top-8 and with
     K = E (every expert selected: the gates are the softmax over all 1024 logits)."""
     log(f"max experts forward cfg {cfg_id} T {T} mode {mode}")
+    L = layer(cfg_id)
+    x = margin_tokens(cfg_id, T, host_array(L.w_router), L.bias_np, L.K)
+    y, idx, gates = L.forward(x, mode)
+    torch.cuda.synchronize()
+    oracle_check(cfg_id, L, x, y, idx, gates, mode)
+
+
+@pytest.mark.parametrize("cfg_id,T,mode", [(126, 3, DECODE), (126, 1, DECODE),
+                                           (127, 3, DECODE), (128, 40, PREFILL),
+                                           (129, 40, PREFILL)])
+def test_forward_max_dims(cfg_id, T, mode):
+    """H = 65536 or I = 65536, the largest dimension the boundary accepts."""
+    log(f"max dims forward cfg {cfg_id} T {T} mode {mode}")
     L = layer(cfg_id)
     x = margin_tokens(cfg_id, T, host_array(L.w_router), L.bias_np, L.K)
     y, idx, gates = L.forward(x, mode)

@@ -100,6 +100,15 @@ CONFIGS.update({
               x="f32", bias=None, mode="decode", layers=1),
     125: dict(name="max_experts_prefill", H=256, I=128, E=1024, K=8, T=300, router="bf16",
               x="bf16", bias=None, mode="prefill", layers=1),
+    # the largest H and I the boundary accepts (65536), each beside a small other side
+    126: dict(name="max_hidden", H=65536, I=128, E=8, K=2, T=3, router="bf16", x="f32",
+              bias=None, mode="decode", layers=1),
+    127: dict(name="max_intermediate", H=128, I=65536, E=4, K=2, T=3, router="f32", x="f32",
+              bias=None, mode="decode", layers=1),
+    128: dict(name="max_hidden_prefill", H=65536, I=64, E=4, K=2, T=40, router="bf16",
+              x="bf16", bias=None, mode="prefill", layers=1),
+    129: dict(name="max_intermediate_prefill", H=64, I=65536, E=4, K=2, T=40, router="bf16",
+              x="bf16", bias=None, mode="prefill", layers=1),
 })
 
 WEIGHT_STD = 0.02
