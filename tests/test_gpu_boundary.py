@@ -168,6 +168,22 @@ def test_forward_max_dims(cfg_id, T, mode):
     oracle_check(cfg_id, L, x, y, idx, gates, mode)
 
 
+@pytest.mark.parametrize("cfg_id,T,mode", [(130, 1024, PREFILL), (131, 256, DECODE),
+                                           (131, 100, DECODE)])
+def test_forward_many_chunks(cfg_id, T, mode):
+    """Four experts, top-2, hundreds of tokens: each routed expert spans several
+    M-chunks of the grouped GEMMs (and the shared expert many more)."""
+    log(f"many chunks forward cfg {cfg_id} T {T} mode {mode}")
+    L = layer(cfg_id)
+    x = margin_tokens(cfg_id, T, host_array(L.w_router), L.bias_np, L.K)
+    y, idx, gates = L.forward(x, mode)
+    torch.cuda.synchronize()
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=L.E)
+    log(f"tokens per expert {counts.tolist()}")
+    assert counts.min() > (128 if mode == PREFILL else 32)
+    oracle_check(cfg_id, L, x, y, idx, gates, mode)
+
+
 @pytest.mark.parametrize("cfg_id,T", [(0, 300), (101, 600)])
 def test_decode_longer_than_256(cfg_id, T):
     """Decode batches beyond 256 tokens run as consecutive 256-token batches."""

@@ -109,6 +109,12 @@ CONFIGS.update({
               x="bf16", bias=None, mode="prefill", layers=1),
     129: dict(name="max_intermediate_prefill", H=64, I=65536, E=4, K=2, T=40, router="bf16",
               x="bf16", bias=None, mode="prefill", layers=1),
+    # few experts, many tokens: every routed expert spans several M-chunks (128 tokens
+    # in prefill, 32 in a decode batch)
+    130: dict(name="many_chunks_prefill", H=256, I=128, E=4, K=2, T=1024, router="bf16",
+              x="bf16", bias=None, mode="prefill", layers=1),
+    131: dict(name="many_chunks_decode", H=256, I=128, E=4, K=2, T=256, router="f32",
+              x="f32", bias=None, mode="decode", layers=1),
 })
 
 WEIGHT_STD = 0.02
