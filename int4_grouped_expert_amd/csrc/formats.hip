@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "coli.h"
 #include "wave.h"
 
@@ -673,14 +675,20 @@ int matvec_grid(int64_t O, int units) {
 
 template <int FMT, int MODE, int TT>
 void launch_one(const MatvecArgs &a, int units, size_t lds, hipStream_t s) {
-  static const bool done = [] {
-    // the x stage may take up to 96 KiB + the chunk sums (6 KiB); the limit
-    // leaves room for the kernel's static LDS within the 160 KiB of a CU
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&matvec_kernel<FMT, TT, MODE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
-    return true;
-  }();  // once per process
-  (void)done;
+  // The x stage may take up to 96 KiB + the chunk sums (6 KiB); the limit leaves
+  // room for the kernel's static LDS within the 160 KiB of a CU.  A function's
+  // attributes are per device: set once on each device the library launches on
+  // (every time past the 64 devices the mask tracks); a failure shows as the
+  // launch's error.
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  const bool known = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+  const uint64_t bit = known ? (uint64_t(1) << dev) : 0;
+  if (!known || !(done.load(std::memory_order_relaxed) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&matvec_kernel<FMT, TT, MODE>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024) == hipSuccess)
+      done.fetch_or(bit, std::memory_order_relaxed);
+  }
   hipLaunchKernelGGL((matvec_kernel<FMT, TT, MODE>),
                      dim3(matvec_grid<FMT, TT, MODE>(a.O, units), unsigned(units)), dim3(256), lds, s, a);
 }
