@@ -86,54 +86,22 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return max(max(r0, r1), max(r2, r3));
 }
 // Order-preserving bits of a float: the unsigned order of the results is the
-// order of the values (-0 just below +0); never 0 for a non-NaN value.
+// order of the values, and equal values (-0 and +0 included: v + 0 turns -0
+// into +0) give equal bits; never 0 for a non-NaN value.
 __device__ inline uint32_t order_bits(float v) {
-  const uint32_t b = __float_as_uint(v);
+  const uint32_t b = __float_as_uint(v + 0.0f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-// Wave-wide top-K of one token, PL logits per lane (E <= 64 PL).  Writes
-// idx/gates in ascending id order.  Each lane keeps the key of its best
-// untaken candidate; a round is one wave key maximum, after which only the
-// winner's lane rescans its PL values.
-// The token's logits, PL per lane (lane l holds ids l, l + 64, ...).
+// K rounds of wave arg-max over the keys v (PL per lane, lane l holds ids
+// l, l + 64, ...): a round takes the largest key not yet taken, ties to the
+// lowest id; a round with no valid candidate left (NaN keys) takes id `round`
+// if free, else the lowest free id.  Sets bit j of `taken` for each pick of
+// this lane.  Each lane keeps its best untaken candidate (order bits, 0 for
+// none, and its slot j); after a round only the winner's lane rescans.
 template <int PL>
-__device__ __attribute__((always_inline)) inline void topk_load(const float *__restrict__ lrow,
-                                                                 int E, int lane, float (&v)[PL]) {
-#pragma unroll
-  for (int j = 0; j < PL; ++j) {
-    const int e = lane + kWaveLanes * j;
-    v[j] = e < E ? lrow[e] : 0.0f;
-  }
-}
-
-// Selection and gates from logits already in registers (see topk_load).
-template <int PL>
-__device__ __attribute__((always_inline)) inline void topk_select(
-    const float (&v_in)[PL], int E, int K, int lane, int32_t *__restrict__ idx_out,
-    float *__restrict__ gate_out, Scoring sc = Scoring{0, nullptr}) {
-  // keys of the selection (the logits themselves, or the biased sigmoid scores)
-  float v[PL], sgm[PL];
-  if (sc.sigmoid) {
-#pragma unroll
-    for (int j = 0; j < PL; ++j) {
-      const int e = lane + kWaveLanes * j;
-      sgm[j] = 1.0f / (1.0f + expf(-v_in[j]));
-      v[j] = sgm[j] + ((sc.bias && e < E) ? sc.bias[e] : 0.0f);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < PL; ++j) {
-      v[j] = v_in[j];
-      sgm[j] = 0.0f;
-    }
-  }
-  // Each lane keeps its best untaken candidate: the order bits of the value
-  // (0: none; NaN values and ids >= E are never candidates) and its slot j,
-  // the lowest among equal values.  A round is a wave maximum of the order
-  // bits; the lane holding it wins, and when several lanes hold it the lowest
-  // id among them does (the rare tie path), so the pick is the largest value,
-  // ties to the lowest id.
-  uint32_t taken = 0;
+__device__ __attribute__((always_inline)) inline void topk_rounds(const float (&v)[PL], int E,
+                                                                   int K, int lane,
+                                                                   uint32_t &taken) {
   uint32_t lk = 0;
   int lj = 0;
   auto rescan = [&]() {
@@ -184,6 +152,120 @@ __device__ __attribute__((always_inline)) inline void topk_select(
       taken |= 1u << (bi / kWaveLanes);
       rescan();
     }
+  }
+}
+
+// Wave maximum of an unsigned value, in every lane, without leaving the VGPRs:
+// the DPP row steps of wave_max_u32, then the row pairs (v_permlane16_swap) and
+// the wave halves (v_permlane32_swap).
+__device__ inline uint32_t wave_max_u32_v(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(uint32_t(a[0]), uint32_t(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(uint32_t(b[0]), uint32_t(b[1]));
+}
+
+// K picks over keys with at least K nonzero (order bits; 0 = no candidate),
+// PL <= 4 per lane (lane l holds ids l, l + 64, ...): largest key first, equal
+// keys to the lowest id.  Each lane sorts its (key, slot) pairs once, largest
+// key first and equal keys by slot; a round is the wave maximum of the lanes'
+// head keys, its holder (the lowest id among several: rare) records the head's
+// slot in `taken` and pops it.
+template <int PL>
+__device__ __attribute__((always_inline)) inline void topk_sorted_heads(const uint32_t (&key)[PL],
+                                                                         int K, int lane,
+                                                                         uint32_t &taken) {
+  // composite (key, PL - 1 - slot): a larger composite is the better candidate
+  uint64_t c[PL];
+#pragma unroll
+  for (int j = 0; j < PL; ++j) c[j] = (uint64_t(key[j]) << 8) | uint64_t(PL - 1 - j);
+  auto cas = [&](int a, int b) {
+    const uint64_t hi = c[a] > c[b] ? c[a] : c[b], lo = c[a] > c[b] ? c[b] : c[a];
+    c[a] = hi;
+    c[b] = lo;
+  };
+  if (PL == 2) cas(0, 1);
+  if (PL == 4) {
+    cas(0, 1); cas(2, 3); cas(0, 2); cas(1, 3); cas(1, 2);
+  }
+  for (int round = 0; round < K; ++round) {
+    const uint32_t hk = uint32_t(c[0] >> 8);
+    const uint32_t wk = wave_max_u32_v(hk);  // nonzero: K candidates exist
+    const uint64_t hold = __ballot(hk == wk);
+    int wl;
+    if (__popcll(hold) == 1) {
+      wl = __ffsll((unsigned long long)hold) - 1;
+    } else {
+      // equal keys in several lanes: the lowest id among them
+      int id = hk == wk ? lane + kWaveLanes * (PL - 1 - int(c[0] & 0xFF)) : 0x7fffffff;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) id = min(id, __shfl_xor(id, m, kWaveLanes));
+      wl = id % kWaveLanes;
+    }
+    if (lane == wl) {
+      taken |= 1u << (PL - 1 - int(c[0] & 0xFF));
+#pragma unroll
+      for (int j = 0; j + 1 < PL; ++j) c[j] = c[j + 1];
+      c[PL - 1] = 0;
+    }
+  }
+}
+
+// Wave-wide top-K of one token, PL logits per lane (E <= 64 PL).  Writes
+// idx/gates in ascending id order.
+// The token's logits, PL per lane (lane l holds ids l, l + 64, ...).
+template <int PL>
+__device__ __attribute__((always_inline)) inline void topk_load(const float *__restrict__ lrow,
+                                                                 int E, int lane, float (&v)[PL]) {
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int e = lane + kWaveLanes * j;
+    v[j] = e < E ? lrow[e] : 0.0f;
+  }
+}
+
+// Selection and gates from logits already in registers (see topk_load).
+template <int PL>
+__device__ __attribute__((always_inline)) inline void topk_select(
+    const float (&v_in)[PL], int E, int K, int lane, int32_t *__restrict__ idx_out,
+    float *__restrict__ gate_out, Scoring sc = Scoring{0, nullptr}) {
+  // keys of the selection (the logits themselves, or the biased sigmoid scores)
+  float v[PL], sgm[PL];
+  if (sc.sigmoid) {
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int e = lane + kWaveLanes * j;
+      sgm[j] = 1.0f / (1.0f + expf(-v_in[j]));
+      v[j] = sgm[j] + ((sc.bias && e < E) ? sc.bias[e] : 0.0f);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      v[j] = v_in[j];
+      sgm[j] = 0.0f;
+    }
+  }
+  // Keys are the order bits (0: no candidate, for NaN and ids >= E).  With at
+  // least K candidates and PL <= 4 each lane sorts its keys once (largest
+  // first, equal keys by slot), so a round is a wave maximum of the lanes'
+  // head keys and a pop in the winning lane; otherwise the rounds rescan.
+  uint32_t taken = 0;
+  int nvalid = 0;
+  uint32_t key[PL];
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int e = lane + kWaveLanes * j;
+    key[j] = (e < E && !__builtin_isnan(v[j])) ? order_bits(v[j]) : 0u;
+    nvalid += __popcll(__ballot(key[j] != 0u));
+  }
+  if (PL <= 4 && nvalid >= K) {
+    topk_sorted_heads<PL>(key, K, lane, taken);
+  } else {
+    topk_rounds<PL>(v, E, K, lane, taken);
   }
   // gate numerators: exp(l - m) over the selected logits (softmax), or the
   // selected scores (sigmoid); the normaliser is their wave sum (identical on

@@ -121,3 +121,114 @@ def test_permute_skips_out_of_range_ids():
     assert list(offsets) == [0, 1, 2, 3, 6, 6, 6, 6, 7]
     assert list(perm[:7]) == [0, 3, 6, 1, 4, 8, 7]
     assert list(unique) == [0, 1, 2, 3, 7]
+
+
+def crafted_logits(E, K, seed):
+    """Logit vectors whose top-K is decided by the tie and NaN rules (page "Colibrì
+    深度解析", section 十一, lower id on equal values; page "colibrì 路由遥测全解析",
+    section 测试与 CI 保障, NaN never selected, fallback ids): integers from a few
+    values; all equal; the K-th largest repeated at ids on both sides of it and
+    across 64-id slots; integers with infinities; NaN everywhere but K + 1 ids; NaN
+    everywhere but K - 2 ids (the fallback).  Every value is exact in fp32, so the
+    logits are the same on both sides."""
+    rng = np.random.default_rng(seed)
+    out = [("ints", rng.integers(-2, 3, E).astype(np.float32)),
+           ("equal", np.full(E, 0.25, np.float32))]
+    v = np.round(rng.standard_normal(E) * 64).astype(np.float32) / 64
+    kth = np.sort(v)[::-1][K - 1]
+    v[rng.choice(E, min(E, 3 * K + 2), replace=False)] = kth
+    out.append(("kth_ties", v))
+    w = rng.integers(-3, 4, E).astype(np.float32)
+    w[rng.choice(E, max(1, E // 5), replace=False)] = np.inf
+    w[rng.choice(E, max(1, E // 5), replace=False)] = -np.inf
+    out.append(("inf", w))
+    n = np.full(E, np.nan, np.float32)
+    keep = rng.choice(E, min(E, K + 1), replace=False)
+    n[keep] = rng.integers(-4, 5, keep.size).astype(np.float32)
+    out.append(("nan_some", n))
+    if K >= 2:
+        f = np.full(E, np.nan, np.float32)
+        keep = rng.choice(E, K - 2, replace=False)
+        f[keep] = rng.integers(-4, 5, keep.size).astype(np.float32)
+        out.append(("nan_fallback", f))
+    return out
+
+
+def check_crafted(name, col, idx, gates, K):
+    ref = col[None, :].astype(np.float64)
+    ridx, rg, fb = oracle.topk(ref, K)
+    assert (fb > 0) == (name == "nan_fallback"), name
+    assert np.array_equal(idx.reshape(-1), ridx.reshape(-1)), (name, idx, ridx)
+    if np.isfinite(col[ridx[0]]).all():
+        assert np.allclose(gates.reshape(-1), rg.reshape(-1), rtol=1e-6, atol=1e-7), name
+
+
+@pytest.mark.parametrize("E,K", [(12, 4), (100, 7), (256, 8), (256, 1), (300, 16), (1024, 8),
+                                 (1024, 16), (16, 16)])
+def test_router_topk_crafted(E, K):
+    """coli_router_topk on crafted logits: the router reads one-hot tokens, so each
+    token's logits are exactly one column of the router matrix."""
+    H = 64
+    for name, col in crafted_logits(E, K, E * 131 + K):
+        log(f"router crafted {name} E {E} K {K}")
+        wr = torch.zeros((E, H), dtype=torch.float32, device="cuda")
+        wr[:, 0] = torch.from_numpy(col).cuda()
+        x = torch.zeros((1, H), dtype=torch.float32, device="cuda")
+        x[0, 0] = 1.0
+        idx, gates, logits = run_router(x, wr, None, K)
+        assert np.array_equal(logits[0], col, equal_nan=True), name
+        check_crafted(name, col, idx, gates, K)
+
+
+def small_layer(H, I, E, K, wr, seed=5):
+    """A layer of E random experts (N(0, 0.02), quantised by the library) under the
+    router matrix wr."""
+    import int4_grouped_expert_amd as coli
+    experts, shared, nb = coli.alloc_layer_blobs(H, I, E)
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for e in range(E + 1):
+        wg = torch.randn((I, H), generator=g, device="cuda") * 0.02
+        wu = torch.randn((I, H), generator=g, device="cuda") * 0.02
+        wd = torch.randn((H, I), generator=g, device="cuda") * 0.02
+        coli.coli_quant_expert(shared.data_ptr() if e == E else experts.data_ptr() + e * nb,
+                               H, I, wg, wu, wd, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    return coli.MoELayer(H, I, E, K, wr, experts, shared), (experts, shared)
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_forward_topk_crafted(T):
+    """The decode forward's own top-K on crafted logits: at T = 1 the selection fused
+    into the single-token gate/up kernel (E = 256, K = 8), at T = 3 the batch route
+    kernel.  Token t is one-hot at feature t, so its logits are column t of the
+    router matrix; columns with infinities or NaN go one at a time (0 times them is
+    NaN for the other tokens)."""
+    import int4_grouped_expert_amd as coli
+    H, I, E, K = 256, 256, 256, 8
+    cases = crafted_logits(E, K, 77 + T)
+    finite = [c for c in cases if np.isfinite(c[1]).all()]
+    groups = [finite[i:i + T] for i in range(0, len(finite), T)]
+    groups += [[c] for c in cases if not np.isfinite(c[1]).all()]
+    wr = torch.zeros((E, H), dtype=torch.float32, device="cuda")
+    layer, keep = small_layer(H, I, E, K, wr)
+    for grp in groups:
+        n = len(grp)
+        log(f"forward crafted T {n}: {[c[0] for c in grp]}")
+        wr.zero_()
+        x = torch.zeros((n, H), dtype=torch.float32, device="cuda")
+        for t, (_, col) in enumerate(grp):
+            wr[:, t] = torch.from_numpy(col).cuda()
+            x[t, t] = 1.0
+        y = torch.empty((n, H), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(layer.workspace_bytes(n, coli.COLI_DECODE), 256), dtype=torch.uint8,
+                         device="cuda")
+        idx = torch.full((n, K), -7, dtype=torch.int32, device="cuda")
+        gates = torch.empty((n, K), dtype=torch.float32, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        coli.coli_moe_forward(layer, coli.COLI_DECODE, x, y, ws, idx, gates, status=status)
+        torch.cuda.synchronize()
+        idx_h, g_h = idx.cpu().numpy(), gates.cpu().numpy()
+        for t, (name, col) in enumerate(grp):
+            check_crafted(name, col, idx_h[t], g_h[t], K)
