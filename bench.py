@@ -374,10 +374,24 @@ def cpu_baseline(coli, W, budget_s=6.0, n_tok=6):
             "legs": legs}
 
 
-def profile_fields(path, kernel_src):
-    """The machine-read fields of a committed profile summary, or None when that
-    summary was taken on a different version of the kernel's source file."""
+# The single-token kernels' sources: the kernel file and the headers it compiles in.
+# A committed profile summary carries the sha256 of their concatenation.
+NARROW_SRC = ("int4_grouped_expert_amd/csrc/ffn_narrow.hip", "int4_grouped_expert_amd/csrc/wave.h",
+              "int4_grouped_expert_amd/csrc/kernels.h")
+
+
+def source_sha256(paths):
     import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()
+
+
+def profile_fields(path, kernel_src):
+    """The machine-read fields ("- key: value" lines) of a committed profile summary,
+    or None when that summary was taken on a different version of the kernel's
+    sources."""
     if not os.path.exists(path):
         return None
     fields = {}
@@ -385,8 +399,7 @@ def profile_fields(path, kernel_src):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    src = open(os.path.join(ROOT, kernel_src), "rb").read()
-    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    if fields.get("source_sha256") != source_sha256(kernel_src):
         return None
     return fields
 
@@ -404,21 +417,11 @@ def profiled_launch_ms(kernel_src):
 def profiled_traffic(kernel_src, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (profiles/<kernel>_decode_t1_traffic.md), or None when that summary was taken
-    on a different version of the kernel's source file."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}_decode_t1_traffic.md")
-    if not os.path.exists(path):
-        return None
-    fields = {}
-    for line in open(path):
-        if line.startswith("- ") and ":" in line:
-            k, v = line[2:].split(":", 1)
-            fields[k.strip()] = v.strip().strip("`")
-    src = open(os.path.join(ROOT, kernel_src), "rb").read()
-    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
-        return None
+    on a different version of the kernel's sources."""
+    f = profile_fields(os.path.join(ROOT, "profiles", f"{kernel}_decode_t1_traffic.md"),
+                       kernel_src)
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return None if f is None else int(f["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -499,11 +502,10 @@ def main():
         "roofline": {"kernel": "gateup_narrow", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": profiled_traffic("int4_grouped_expert_amd/csrc/ffn_narrow.hip",
-                                                 "gateup_narrow"),
+                     "traffic": profiled_traffic(NARROW_SRC, "gateup_narrow"),
                      "bytes_per_launch": gu_bytes, "avg_launch_ms": round(gu_ms, 5)},
     }
-    prof_ms = profiled_launch_ms("int4_grouped_expert_amd/csrc/ffn_narrow.hip")
+    prof_ms = profiled_launch_ms(NARROW_SRC)
     if prof_ms is not None:
         # the committed kernel-trace average of the same source (profiles/)
         result["roofline"]["profiled_avg_launch_ms"] = round(prof_ms, 5)
