@@ -180,6 +180,7 @@ __device__ __attribute__((always_inline)) inline void topk_sorted_heads(const ui
                                                                          int K, int lane,
                                                                          uint32_t &taken) {
   // composite (key, PL - 1 - slot): a larger composite is the better candidate
+  static_assert(PL == 1 || PL == 2 || PL == 4, "sorted heads: 1, 2 or 4 keys per lane");
   uint64_t c[PL];
 #pragma unroll
   for (int j = 0; j < PL; ++j) c[j] = (uint64_t(key[j]) << 8) | uint64_t(PL - 1 - j);
@@ -262,8 +263,11 @@ __device__ __attribute__((always_inline)) inline void topk_select(
     key[j] = (e < E && !__builtin_isnan(v[j])) ? order_bits(v[j]) : 0u;
     nvalid += __popcll(__ballot(key[j] != 0u));
   }
-  if (PL <= 4 && nvalid >= K) {
-    topk_sorted_heads<PL>(key, K, lane, taken);
+  if constexpr (PL <= 4) {
+    if (nvalid >= K)
+      topk_sorted_heads<PL>(key, K, lane, taken);
+    else
+      topk_rounds<PL>(v, E, K, lane, taken);
   } else {
     topk_rounds<PL>(v, E, K, lane, taken);
   }
