@@ -163,7 +163,7 @@ def check_crafted(name, col, idx, gates, K):
         assert np.allclose(gates.reshape(-1), rg.reshape(-1), rtol=1e-6, atol=1e-7), name
 
 
-@pytest.mark.parametrize("E,K", [(12, 4), (100, 7), (256, 8), (256, 1), (300, 16), (1024, 8),
+@pytest.mark.parametrize("E,K", [(12, 4), (100, 7), (256, 8), (256, 1), (256, 16), (200, 13), (300, 16), (1024, 8),
                                  (1024, 16), (16, 16)])
 def test_router_topk_crafted(E, K):
     """coli_router_topk on crafted logits: the router reads one-hot tokens, so each
