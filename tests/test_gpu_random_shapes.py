@@ -1,7 +1,8 @@
 """Seeded random layer shapes through coli_moe_forward, each against the oracle:
 H in [1, 700], I in [1, 320], E in [1, 40], K in [1, min(E, 8)], decode T in [1, 70]
 and prefill T in [1, 150], fp32 or bf16 routers, no bias, a Zipf bias or a sigmoid
-router's selection bias.  A few draws put H and I on multiples of 256 at T = 1 (the
+router's selection bias; a second set with E in [41, 300] and K up to 16 (the
+top-K's 2, 4 and 8 logits per lane).  A few draws put H and I on multiples of 256 at T = 1 (the
 single-token int8 path); the rest take the batch and prefill paths with ragged
 groups and rows of any alignment.  Every case checks ids bit-exact, gates and y row
 by row (the same bars as the named workloads)."""
@@ -16,6 +17,7 @@ from tests.test_gpu_forward import DECODE, PREFILL, oracle_check
 pytestmark = pytest.mark.gpu
 
 N_CASES = 24
+N_WIDE = 12
 BASE_ID = 300
 
 
@@ -40,6 +42,26 @@ def draw_cases():
         if kind == "sel":
             cfg["scoring"] = "sigmoid"
         cases.append((BASE_ID + i, cfg))
+    # wider routers: E in [41, 300], K up to 16
+    rng = np.random.default_rng(20261203)
+    for i in range(N_WIDE):
+        mode = "prefill" if i % 4 == 3 else "decode"
+        E = int(rng.integers(41, 301))
+        K = int(rng.integers(1, min(E, 16) + 1))
+        if i % 4 == 1 and E <= 256:  # single-token int8 path
+            H, I = 256 * int(rng.integers(1, 3)), 256 * int(rng.integers(1, 3))
+            T = 1
+        else:
+            H, I = int(rng.integers(64, 513)), int(rng.integers(1, 257))
+            T = int(rng.integers(1, 49 if mode == "decode" else 121))
+        kind = ("none", "zipf", "sel")[i % 3]
+        cfg = dict(name=f"random_wide_{i}", H=H, I=I, E=E, K=K, T=T,
+                   router="bf16" if rng.integers(0, 2) else "f32",
+                   x="bf16" if mode == "prefill" else "f32",
+                   bias=None if kind == "none" else kind, mode=mode, layers=1)
+        if kind == "sel":
+            cfg["scoring"] = "sigmoid"
+        cases.append((BASE_ID + N_CASES + i, cfg))
     return cases
 
 
