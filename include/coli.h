@@ -164,7 +164,7 @@ int coli_quant_int4_g64_many(const float *const *w, uint8_t *const *packed,
  *                    all E restricted to the selected and renormalised to sum
  *                    1); SIGMOID: see coli_scoring.
  * Selection: the K largest keys (logits, or biased sigmoid scores); on equal
- * keys the lower id wins; NaN never wins.  A slot with no valid candidate
+ * keys (-0 and +0 are equal) the lower id wins; NaN never wins.  A slot with no valid candidate
  * (every remaining key NaN) takes id k if free, else the lowest free id (page
  * "colibrì 路由遥测全解析", section 测试与 CI 保障); its gates are then
  * unspecified.
