@@ -61,6 +61,8 @@
 //                  is the accumulation itself, in a fixed order (no atomics).
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "kernels.h"
 #include "wave.h"
 
@@ -527,9 +529,19 @@ hipError_t launch_down(const LayerDev &L, const NarrowBufs &nb, const int32_t *i
                        int grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const int nw = L.I / 256;
   const size_t lds = size_t(nw) * down_wave_bytes<NU>();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_narrow<NU>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  if (e != hipSuccess) return e;
+  // the kernel's dynamic-LDS limit, raised once per device to what the largest
+  // block (kDownMaxWaves waves) needs (function attributes are per device)
+  static std::atomic<uint64_t> done{0};
+  int dev = -1;
+  const bool known = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+  const uint64_t bit = known ? (uint64_t(1) << dev) : 0;
+  if (!known || !(done.load(std::memory_order_relaxed) & bit)) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&down_narrow<NU>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, int(kDownMaxWaves * down_wave_bytes<NU>()));
+    if (e != hipSuccess) return e;
+    done.fetch_or(bit, std::memory_order_relaxed);
+  }
   hipExtLaunchKernelGGL(down_narrow<NU>, dim3(grid), dim3(nw * kW), uint32_t(lds), s, start, stop,
                         0, nb, L, idx, y);
   return hipGetLastError();
