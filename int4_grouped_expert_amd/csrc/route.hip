@@ -11,10 +11,12 @@
 //   router_logits_kernel  GEMV-shaped logits for small T (decode): one block
 //                         per (RW expert rows, TT tokens), its waves split H,
 //                         16-byte loads of the router rows, fp32 FMA.
-//   router_mfma_kernel    logits for large T (prefill): bf16 x bf16 -> fp32
-//                         on v_mfma_f32_16x16x32_bf16, operands loaded straight
-//                         from global memory (both operands are K-contiguous),
-//                         K split over grid.z with a fixed-order partial sum.
+//   router_mfma_lds       logits for large T (prefill), H % 64 == 0: bf16 x bf16 ->
+//                         fp32 on v_mfma_f32_16x16x32_bf16, 128 x 64 tiles staged
+//                         through LDS, K split over grid.z with a fixed-order
+//                         partial sum (router_sum_parts).
+//   router_mfma_kernel    the same for H % 32 == 0, operands loaded straight from
+//                         global memory (both operands are K-contiguous).
 //   topk_kernel           one wave per token: K rounds of wave argmax.
 //   topk_permute_small    one block: top-K for all tokens, then the permute
 //                         (decode: one launch for the whole route stage).
@@ -369,6 +371,123 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
       }
     }
   }
+}
+
+// The same logits through LDS (H % 64 == 0): a block computes a 128 x 64 tile
+// (tokens x experts) over the k-stages z, z + S, ... of 64 columns.  Each stage
+// is read from global memory once per block, as whole 128-byte row segments
+// (16 bytes per thread and load), two stages ahead of its use, and written to
+// an LDS buffer while the other buffer feeds the matrix cores; wave w takes tokens 32w .. 32w + 31 of
+// the tile against all 64 experts (8 accumulator tiles of 16 x 16).  Rows are
+// padded to 72 elements, so the 16 rows of an operand read land in distinct
+// banks.  Output as router_mfma_kernel (partials when S > 1).
+__global__ __launch_bounds__(256) void router_mfma_lds(
+    const uint16_t *__restrict__ x, int T, int H,
+    const uint16_t *__restrict__ wr, int E, const float *__restrict__ bias,
+    float *__restrict__ out) {
+  constexpr int BM = 128, BN = 64, BK = 64, LD = BK + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][BN * LD];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int S = gridDim.z, z = blockIdx.z;
+  const int nks = H / BK;
+  // loader: A stage = 128 rows x 8 pieces of 16 bytes (4 per thread), B stage
+  // = 64 rows x 8 pieces (2 per thread); rows past T or E re-read the last one.
+  // Two register sets: the stages one and two ahead are in flight together.
+  // one 16-byte piece of a stage: A pieces q < 4 (128 rows x 8), B pieces q >= 4
+  // (64 rows x 8); rows past T or E re-read the last one
+  auto piece_src = [&](int ks, int q) __attribute__((always_inline)) {
+    const int id = tid + 256 * (q & 3), r = id >> 3, c = id & 7;
+    return q < 4 ? x + size_t(min(m0 + r, T - 1)) * H + ks * BK + 8 * c
+                 : wr + size_t(min(n0 + r, E - 1)) * H + ks * BK + 8 * c;
+  };
+  auto piece_dst = [&](int buf, int q) __attribute__((always_inline)) {
+    const int id = tid + 256 * (q & 3), r = id >> 3, c = id & 7;
+    return q < 4 ? &sa[buf][r * LD + 8 * c] : &sb[buf][r * LD + 8 * c];
+  };
+#define COLI_RMLDS_LOAD(ks, P)                                                 \
+  {                                                                            \
+    const int ks_ = (ks);                                                      \
+    P##0 = *reinterpret_cast<const uint4 *>(piece_src(ks_, 0));                \
+    P##1 = *reinterpret_cast<const uint4 *>(piece_src(ks_, 1));                \
+    P##2 = *reinterpret_cast<const uint4 *>(piece_src(ks_, 2));                \
+    P##3 = *reinterpret_cast<const uint4 *>(piece_src(ks_, 3));                \
+    P##4 = *reinterpret_cast<const uint4 *>(piece_src(ks_, 4));                \
+    P##5 = *reinterpret_cast<const uint4 *>(piece_src(ks_, 5));                \
+  }
+#define COLI_RMLDS_STORE(P, buf)                                               \
+  {                                                                            \
+    *reinterpret_cast<uint4 *>(piece_dst(buf, 0)) = P##0;                      \
+    *reinterpret_cast<uint4 *>(piece_dst(buf, 1)) = P##1;                      \
+    *reinterpret_cast<uint4 *>(piece_dst(buf, 2)) = P##2;                      \
+    *reinterpret_cast<uint4 *>(piece_dst(buf, 3)) = P##3;                      \
+    *reinterpret_cast<uint4 *>(piece_dst(buf, 4)) = P##4;                      \
+    *reinterpret_cast<uint4 *>(piece_dst(buf, 5)) = P##5;                      \
+  }
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int row = lane % 16, kq = (lane / 16) * 8;
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      bf16x8 a[2], b[4];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        a[mi] = *reinterpret_cast<const bf16x8 *>(&sa[buf][(32 * wave + 16 * mi + row) * LD + 32 * kk + kq]);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        b[ni] = *reinterpret_cast<const bf16x8 *>(&sb[buf][(16 * ni + row) * LD + 32 * kk + kq]);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+  // stage ks is in LDS buffer (its index along the block's stages) & 1; the
+  // register sets alternate the same way, two stages ahead
+  uint4 u0, u1, u2, u3, u4, u5, v0, v1, v2, v3, v4, v5;  // register sets u, v
+  // the block's stages z + j S, j < nmy (nmy >= 1: z < S <= nks); loads past
+  // the last stage re-read it (valid addresses, never stored)
+  const int nmy = (nks - z + S - 1) / S;
+  auto stg = [&](int j) { return min(z + j * S, nks - 1); };
+  COLI_RMLDS_LOAD(stg(0), u)
+  COLI_RMLDS_LOAD(stg(1), v)
+  COLI_RMLDS_STORE(u, 0)
+  __syncthreads();
+  for (int j = 0; j < nmy; j += 2) {
+    // stage j in buffer 0, set v holds stage j + 1, set u takes stage j + 2
+    COLI_RMLDS_LOAD(stg(j + 2), u)
+    compute(0);
+    if (j + 1 < nmy) COLI_RMLDS_STORE(v, 1)
+    __syncthreads();
+    if (j + 1 < nmy) {  // block-uniform
+      COLI_RMLDS_LOAD(stg(j + 3), v)
+      compute(1);
+      if (j + 2 < nmy) COLI_RMLDS_STORE(u, 0)
+      __syncthreads();
+    }
+  }
+#undef COLI_RMLDS_LOAD
+#undef COLI_RMLDS_STORE
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int n = n0 + 16 * ni + row;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 32 * wave + 16 * mi + (lane / 16) * 4 + i;
+        if (m < T && n < E) {
+          if (S > 1) out[(size_t(z) * T + m) * E + n] = acc[mi][ni][i];
+          else out[size_t(m) * E + n] = acc[mi][ni][i] + (bias ? bias[n] : 0.0f);
+        }
+      }
+    }
 }
 
 // logits[t][e] = sum over z (in order) of part[z][t][e], plus bias[e]
@@ -798,6 +917,23 @@ hipError_t launch_router_narrow(const float *x, int T, int H, const void *wr, in
 hipError_t launch_router_mfma(const uint16_t *x, int T, int H, const uint16_t *wr, int E,
                               const float *bias, float *logits, float *part, size_t part_bytes,
                               hipStream_t s) {
+  if (H % 64 == 0) {
+    // tiles of 128 tokens x 64 experts through LDS; K split into S parts so that
+    // the grid covers the GPU about twice, as far as the partial-sum scratch
+    // allows
+    const int64_t tiles = int64_t((T + 127) / 128) * ((E + 63) / 64);
+    int S = int(tiles >= 512 ? 1 : (512 + tiles - 1) / tiles);
+    if (S > 8) S = 8;
+    if (S > H / 64) S = H / 64;
+    while (S > 1 && size_t(S) * T * E * 4 > part_bytes) --S;
+    dim3 grid((T + 127) / 128, (E + 63) / 64, S);
+    router_mfma_lds<<<grid, 256, 0, s>>>(x, T, H, wr, E, bias, S > 1 ? part : logits);
+    if (S > 1) {
+      const int64_t n = int64_t(T) * E;
+      router_sum_parts<<<dim3(unsigned((n + 255) / 256)), 256, 0, s>>>(part, S, T, E, bias, logits);
+    }
+    return hipGetLastError();
+  }
   // K split: enough blocks to cover the GPU several times, as far as the
   // partial-sum scratch allows
   const int64_t tiles = int64_t((T + 63) / 64) * ((E + 63) / 64);
