@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libcoli.so")
 
 SOURCES = ["coli.cpp", "quant.hip", "route.hip", "ffn_narrow.hip",
            "ffn_prefill.hip", "ffn_batch.hip",
-           "rmsnorm.hip", "noalloc.hip", "usage.hip", "tier.cpp", "formats.hip"]
+           "rmsnorm.hip", "noalloc.hip", "usage.hip", "tier.cpp", "formats.hip",
+           "ffn_mx.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -835,7 +835,8 @@ hipError_t launch_fmt_experts(const FmtLayer &L, const Routing &r, const float *
   a.s_off[0] = L.s_off[0];
   a.s_off[1] = L.s_off[1];
   size_t lds = size_t(T) * a.ldx * 4 + size_t(T) * a.chunks * 4;
-  hipError_t e = launch_matvec_fmt<kModeGateUp>(L.fmt, a, T, units, lds, s);
+  hipError_t e = mx_gateup_ok(L, x, T) ? launch_mx_gateup(L, r, x, T, h, s)
+                                       : launch_matvec_fmt<kModeGateUp>(L.fmt, a, T, units, lds, s);
   if (e != hipSuccess) return e;
   // down: rows are the H outputs, the row length I, x = h of the unit
   fmt_geometry(L.fmt, L.I, &cw, &a.row_bytes, &a.scale_cols);

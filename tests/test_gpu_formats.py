@@ -10,7 +10,12 @@
   max|gpu - oracle| <= 2e-5 * rms(oracle y[t]) for the float element formats and
   1e-4 for the offset-integer ones (their kernels take sum u x - 8 sum x (4 for
   int3) per group: fp32 cancellation of about one decimal digit), next to the
-  decode tolerance 2e-3 * max(1, rms).
+  decode tolerance 2e-3 * max(1, rms);
+* the layer with its experts in each format against the oracle's fp64 layer, with
+  the same bars, except the MXFP4 layer's gate/up on the scaled matrix cores
+  (T <= 2, H a multiple of 256): 1e-4, as those sum each 128-term block product
+  with about 2^-15 of its largest term (measured against a host product), well
+  inside the decode tolerance.
 Page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战", section 权重转换 (the
 registry); OCP MX v1.0 and OCP FP8 for the element formats.
 """
@@ -26,6 +31,7 @@ pytestmark = pytest.mark.gpu
 FMTS = (5, 7, 8)
 NAMES = {4: "int4-g64", 5: "int3-g64", 7: "mxfp4", 8: "fp8-e4m3-b128"}
 TIGHT = {4: 1e-4, 5: 1e-4, 7: 2e-5, 8: 2e-5}
+MX_MFMA_TIGHT = 1e-4  # the MXFP4 layer's gate/up on the scaled matrix cores
 
 
 def weights(O, I, seed, spread=False):
@@ -294,8 +300,9 @@ def oracle_fmt_check(L, x, y, idx, gates):
                                       c["K"], L.scoring)
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert np.abs(gates.cpu().numpy() - rg).max() <= 2e-3
+    mfma = L.fmt == 7 and x.shape[0] <= 2 and L.H % 256 == 0
     check(y.cpu().numpy().astype(np.float64), yr, f"layer {NAMES[L.fmt]} cfg {L.cfg_id} "
-          f"T {x.shape[0]}", TIGHT[L.fmt])
+          f"T {x.shape[0]}", MX_MFMA_TIGHT if mfma else TIGHT[L.fmt])
 
 
 _fmt_layers = {}
