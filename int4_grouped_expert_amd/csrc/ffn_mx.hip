@@ -1,5 +1,5 @@
-// ffn_mx.hip -- the gate/up stage of a decode layer whose experts are stored
-// in MXFP4, for one or two tokens, on the gfx950 scaled matrix cores.
+// ffn_mx.hip -- the experts of a decode layer stored in MXFP4, for one or two
+// tokens, on the gfx950 scaled matrix cores.
 //
 // Method: the expert FFN of page "Colibrì 深度解析" (sections 四 and 十一):
 // h = w_t * SiLU(x Wg^T) * (x Wu^T) per (unit, token), w_t the token's gate
@@ -35,13 +35,21 @@
 // column n is meaningful where h(m) = h(n), and the four planes of one
 // (token, weight row, h) are the four values one result lane holds.
 //
-// Kernel mx_gateup: block b takes row group b (8 rows of I) of every unit, the
-// shared expert first (its blob needs no routing, so its loads leave first);
-// the 8 waves split the 256-element chunks of H and keep their planes of x in
-// registers; a register ring one item deep; per-item partials meet in LDS and
-// are reduced once, at the end.
+// Kernels
+//   mx_gateup   block b takes row group b (8 rows of I) of every unit, the
+//               shared expert first (its blob needs no routing, so its loads
+//               leave first); the 8 waves split the 256-element chunks of H and
+//               keep their planes of x in registers; a register ring of two
+//               items; per-item partials meet in LDS and are reduced once, at
+//               the end, into h = w_t SiLU(gate) up.
+//   mx_down     one token: output-stationary over row groups of H, every
+//               unit in turn (the gate weights are in h, so the combine is
+//               the accumulation); h's planes in LDS; writes y and flags a
+//               non-finite output.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "coli.h"
 #include "kernels.h"
@@ -112,6 +120,59 @@ __device__ inline f32x4 mfma_mx(const i32x8 &a, const uint4 &b, const f32x4 &c, 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 0, 4, 0, sa, 0, sb);
 }
 
+// The exponent e of a 32-element block (its largest |x| times 2^-e in
+// [64, 128), kept >= -115 so that the last plane's scale 2^(e - 12) is an
+// E8M0 value) and the four E4M3 planes of this lane's 8 elements.  The block
+// is held by 4 consecutive lanes (all active).  A block holding a NaN or an
+// infinity gets e = 0 and NaN codes.
+__device__ inline int block_planes(float v[8], uint2 pl[4]) {
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mb = max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  mb = max(mb, uint32_t(__shfl_xor(int(mb), 1)));
+  mb = max(mb, uint32_t(__shfl_xor(int(mb), 2)));
+  if (mb >= 0x7F800000u) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) pl[p] = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    return 0;
+  }
+  const int ef = int(mb >> 23) < 1 ? 1 : int(mb >> 23);
+  const int e = ef - 133 < -115 ? -115 : ef - 133;
+  const float f = pow2f(-e);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] *= f;
+  e4m3_planes(v, pl);
+  return e;
+}
+
+// Fold of one item's result: the four planes, then the two halves of the
+// chunks (result lanes 16 t + r and 16 t + r + 40 hold h = 0 and h = 1 of
+// token t, weight row r).  Valid on lanes 0..7 and 16..23.
+__device__ inline float fold_item(const f32x4 &acc, int lane) {
+  float v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  return v + __shfl(v, (lane + 40) & 63);
+}
+
+// E8M0 scales.  The scales of a row's 256-element chunks c0 .. c0 + nc - 1
+// are 8 nc consecutive bytes; lane (n = r + 8 h, q) loads dword 2 q + h of
+// them (dword 0 past the end), and the scale of chunk c for lane (r, h, q) --
+// byte 4 h + q of chunk c, so byte q of dword 2 c + h -- comes from lane
+// (n, c) of the same row.
+__device__ inline uint32_t scale_dword(const uint8_t *slice, int nc, int hh, int q) {
+  const int d = 2 * q + hh;
+  return *reinterpret_cast<const uint32_t *>(slice + 4 * (d < 2 * nc ? d : 0));
+}
+__device__ inline int scale_of(uint32_t dw, int c, int lane, int q) {
+  const uint32_t v = uint32_t(__shfl(int(dw), (lane & 15) + 16 * c));
+  return int((v >> (8 * q)) & 0xFFu);
+}
+
+template <int CPW>
+struct GuSlot {
+  uint4 wg[CPW], wu[CPW];
+  uint32_t sdg, sdu;
+};
+
 template <int CPW>
 __global__ __launch_bounds__(64 * kMxWaves) void mx_gateup(MxArgs a) {
   // the prologue's planes of x and the loop's partials share the LDS
@@ -132,31 +193,34 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_gateup(MxArgs a) {
   const int r = n & 7, hh = n >> 3;
   const size_t row = size_t(blockIdx.x) * 8 + r;
   const size_t woff = row * size_t(H / 2) + size_t(c0) * 128 + 64 * hh + 16 * q;
-  const size_t soff = row * size_t(H / 32) + size_t(c0) * 8 + 4 * hh + q;
+  const size_t soff = row * size_t(H / 32) + size_t(c0) * 8;
 
-  // the shared expert's gate/up blocks first
-  uint4 wg[CPW], wu[CPW];
-  uint32_t sg[CPW], su[CPW];
-  {
-    const uint8_t *b = a.shared;
+  auto load = [&](GuSlot<CPW> &sl, const uint8_t *b) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
       if (c < nchw) {
-        wg[c] = *reinterpret_cast<const uint4 *>(b + a.q_off[0] + woff + 128 * c);
-        wu[c] = *reinterpret_cast<const uint4 *>(b + a.q_off[1] + woff + 128 * c);
-        sg[c] = b[a.s_off[0] + soff + 8 * c];
-        su[c] = b[a.s_off[1] + soff + 8 * c];
+        sl.wg[c] = *reinterpret_cast<const uint4 *>(b + a.q_off[0] + woff + 128 * c);
+        sl.wu[c] = *reinterpret_cast<const uint4 *>(b + a.q_off[1] + woff + 128 * c);
       }
-  }
+    if (nchw > 0) {
+      sl.sdg = scale_dword(b + a.s_off[0] + soff, nchw, hh, q);
+      sl.sdu = scale_dword(b + a.s_off[1] + soff, nchw, hh, q);
+    }
+  };
+  // items: 0 the shared expert (its loads leave first), k >= 1 unit k - 1;
+  // a ring of two items in flight
+  GuSlot<CPW> s0, s1;
+  load(s0, a.shared);
   const int nu = *a.n_unique;
-  const int nitems = nu + 1;  // item 0: the shared expert; item k: unit k - 1
+  const int nitems = nu + 1;
+  const uint8_t *blob1 = nu > 0 ? a.experts + size_t(a.unique[0]) * a.blob_bytes : a.shared;
   if (int(threadIdx.x) < nitems)
     sblob[threadIdx.x] = threadIdx.x == 0
                              ? a.shared
                              : a.experts + size_t(a.unique[threadIdx.x - 1]) * a.blob_bytes;
 
   // planes of x over this wave's chunks: 4 lanes per 32-element block, 8
-  // elements per lane, blocks (token, block) in passes of 16
+  // elements per lane, in passes of 16 blocks
   {
     const int nb = nchw * 8;  // 32-blocks per token in the slice
     for (int j = lane; j < 4 * T * nb; j += 64) {
@@ -166,33 +230,15 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_gateup(MxArgs a) {
                                                            blk * 32 + sub * 8);
       const float4 p0 = src[0], p1 = src[1];
       float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      uint32_t mb = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mb = max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-      mb = max(mb, uint32_t(__shfl_xor(int(mb), 1)));
-      mb = max(mb, uint32_t(__shfl_xor(int(mb), 2)));
-      // e: the block's largest |x| times 2^-e in [64, 128); kept >= -115 so
-      // that the last plane's scale 2^(e - 12) is an E8M0 value
-      const int ef = int(mb >> 23) < 1 ? 1 : int(mb >> 23);
-      int e = ef - 133;
-      e = e < -115 ? -115 : e;
       uint2 pl[4];
-      if (mb >= 0x7F800000u) {
-        e = 0;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) pl[p] = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-      } else {
-        const float f = pow2f(-e);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] *= f;
-        e4m3_planes(v, pl);
-      }
+      const int e = block_planes(v, pl);
 #pragma unroll
       for (int p = 0; p < 4; ++p)
         *reinterpret_cast<uint2 *>(&xpl[wave][t][p][blk * 32 + sub * 8]) = pl[p];
       if (sub == 0) sexp[wave][t][blk] = e;
     }
   }
+  if (nitems > 1) load(s1, blob1);
   lds_barrier();
   // A operands: row m = 8 h + 4 t + j (plane j of token t, elements 128 h ..)
   i32x8 A[CPW];
@@ -216,36 +262,44 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_gateup(MxArgs a) {
   }
   lds_barrier();  // the planes' LDS becomes the partials'
 
-  for (int k = 0; k < nitems; ++k) {
-    const bool more = k + 1 < nitems;
-    const uint8_t *nb = sblob[more ? k + 1 : k];
+  // item k from slot sl, which then takes item k + 2
+  auto run = [&](GuSlot<CPW> &sl, int k) __attribute__((always_inline)) {
+    const bool more = k + 2 < nitems;
+    const uint8_t *nb = sblob[more ? k + 2 : k];
     f32x4 accg = {0.0f, 0.0f, 0.0f, 0.0f}, accu = {0.0f, 0.0f, 0.0f, 0.0f};
+    int scg[CPW], scu[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      scg[c] = scale_of(sl.sdg, c, lane, q);
+      scu[c] = scale_of(sl.sdu, c, lane, q);
+    }
+    if (more && nchw > 0) {
+      sl.sdg = scale_dword(nb + a.s_off[0] + soff, nchw, hh, q);
+      sl.sdu = scale_dword(nb + a.s_off[1] + soff, nchw, hh, q);
+    }
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       if (c < nchw) {
-        // consume the slot, then refill it with the next item's block
-        const uint4 bg = wg[c], bu = wu[c];
-        const int scg = int(sg[c]), scu = int(su[c]);
+        // consume the slot, then refill it
+        const uint4 bg = sl.wg[c], bu = sl.wu[c];
         if (more) {
-          wg[c] = *reinterpret_cast<const uint4 *>(nb + a.q_off[0] + woff + 128 * c);
-          wu[c] = *reinterpret_cast<const uint4 *>(nb + a.q_off[1] + woff + 128 * c);
-          sg[c] = nb[a.s_off[0] + soff + 8 * c];
-          su[c] = nb[a.s_off[1] + soff + 8 * c];
+          sl.wg[c] = *reinterpret_cast<const uint4 *>(nb + a.q_off[0] + woff + 128 * c);
+          sl.wu[c] = *reinterpret_cast<const uint4 *>(nb + a.q_off[1] + woff + 128 * c);
         }
         step_fence();
-        accg = mfma_mx(A[c], bg, accg, sA[c], scg);
-        accu = mfma_mx(A[c], bu, accu, sA[c], scu);
+        accg = mfma_mx(A[c], bg, accg, sA[c], scg[c]);
+        accu = mfma_mx(A[c], bu, accu, sA[c], scu[c]);
       }
     }
-    // the four planes, then the two halves of the 256-element chunks
-    float vg = (accg[0] + accg[1]) + (accg[2] + accg[3]);
-    float vu = (accu[0] + accu[1]) + (accu[2] + accu[3]);
-    vg += __shfl(vg, (lane + 40) & 63);
-    vu += __shfl(vu, (lane + 40) & 63);
+    const float vg = fold_item(accg, lane), vu = fold_item(accu, lane);
     if (lane < 24 && (lane & 15) < 8) {
       red[k][wave][0][lane >> 4][lane & 7] = vg;
       red[k][wave][1][lane >> 4][lane & 7] = vu;
     }
+  };
+  for (int k = 0; k < nitems; k += 2) {
+    run(s0, k);
+    if (k + 1 < nitems) run(s1, k + 1);
   }
   lds_barrier();
   for (int i = threadIdx.x; i < nitems * T * 8; i += blockDim.x) {
@@ -268,14 +322,184 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_gateup(MxArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ down
+// One token.  Output-stationary: block b takes row groups b, b + G, ... (8
+// rows of H each, at most kMxDownItems) and, for each, every unit in turn;
+// its 8 waves split the 256-element chunks of I.  The gate weights are in h,
+// so the combine over units is the accumulation itself, in unit order.  Each
+// wave first turns its chunks of every unit's h into E4M3 planes in its own
+// LDS area (the h loads of all its passes issued first); the weight blocks of
+// the first steps are in flight meanwhile; then a ring of up to
+// 8 steps.
+constexpr int kMxDownItems = 4;
+// steps in flight per wave: 8 KB of weight blocks at most
+template <int CPW>
+constexpr int mx_down_depth() { return 8 / CPW > 2 ? 8 / CPW : 2; }
+constexpr int kMxDownMaxUC = 18;  // units x chunks per wave (the LDS area)
+constexpr int kMxDownPasses = kMxDownMaxUC * 32 / 64;
+
+struct MxDownArgs {
+  const uint8_t *experts, *shared;
+  size_t blob_bytes, q_off, s_off;  // the down section of a blob
+  const int32_t *unique, *n_unique;
+  const float *h;  // [units][I]
+  float *y;        // [H]
+  int32_t *status;
+  int H, I, umax;  // umax: the units the LDS areas are sized for
+};
+
+template <int CPW>
+constexpr int mx_down_unit_bytes() { return CPW * (4 * 256 + 8 * 4); }
+
+template <int CPW>
+__global__ __launch_bounds__(64 * kMxWaves) void mx_down(MxDownArgs a) {
+  extern __shared__ __align__(16) uint8_t dyn[];  // per wave: planes, then exponents
+  __shared__ float red[kMxDownItems][kMxWaves][8];
+  __shared__ const uint8_t *sblob[kMxMaxItems];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = a.H, I = a.I;
+  const int nch = I / 256;
+  const int c0 = wave * CPW;
+  const int nchw = c0 < nch ? (nch - c0 < CPW ? nch - c0 : CPW) : 0;
+  const int n = lane & 15, q = lane >> 4;
+  const int r = n & 7, hh = n >> 3;
+  const int ah = n >> 3, aj = n & 3;
+  const bool arow = ((n >> 2) & 1) == 0;  // A rows of token 0
+  const int groups = H / 8;
+  int nj = 0;
+  for (int g = blockIdx.x; g < groups && nj < kMxDownItems; g += gridDim.x) ++nj;
+  const int nu = *a.n_unique;
+  const int units = nu + 1;  // unit u < nu: routed, u == nu: the shared expert
+  if (int(threadIdx.x) < units)
+    sblob[threadIdx.x] = int(threadIdx.x) < nu
+                             ? a.experts + size_t(a.unique[threadIdx.x]) * a.blob_bytes
+                             : a.shared;
+  uint8_t *apl = dyn + size_t(wave) * a.umax * mx_down_unit_bytes<CPW>();
+  int *aex = reinterpret_cast<int *>(apl + size_t(a.umax) * CPW * 1024);
+  lds_barrier();
+  const int total = nj * units;
+
+  // the ring: kMxDownDepth steps in flight
+  constexpr int kMxDownDepth = mx_down_depth<CPW>();
+  uint4 rw[kMxDownDepth][CPW];
+  uint32_t rsd[kMxDownDepth];
+  auto load = [&](int k, int s) __attribute__((always_inline)) {
+    const int j = s / units, u = s - j * units;
+    const size_t row = (size_t(blockIdx.x) + size_t(j) * gridDim.x) * 8 + r;
+    const uint8_t *b = sblob[u];
+    const uint8_t *wp = b + a.q_off + row * size_t(I / 2) + size_t(c0) * 128 + 64 * hh + 16 * q;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      if (c < nchw) rw[k][c] = *reinterpret_cast<const uint4 *>(wp + 128 * c);
+    if (nchw > 0)
+      rsd[k] = scale_dword(b + a.s_off + row * size_t(I / 32) + size_t(c0) * 8, nchw, hh, q);
+  };
+#pragma unroll
+  for (int i = 0; i < kMxDownDepth; ++i)
+    if (i < total) load(i, i);
+
+  // planes of h over this wave's chunks of every unit: 4 lanes per 32-block
+  {
+    const int tasks = units * nchw * 32;
+    float4 hv[kMxDownPasses][2];
+#pragma unroll
+    for (int i = 0; i < kMxDownPasses; ++i) {
+      const int j = lane + 64 * i;
+      if (j < tasks) {
+        const int sub = j & 3, blk = (j >> 2) & 7, uc = j >> 5;
+        const int u = uc / nchw, c = uc - u * nchw;
+        const float4 *src = reinterpret_cast<const float4 *>(
+            a.h + size_t(u) * I + size_t(c0 + c) * 256 + blk * 32 + sub * 8);
+        hv[i][0] = src[0];
+        hv[i][1] = src[1];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMxDownPasses; ++i) {
+      const int j = lane + 64 * i;
+      if (j < tasks) {
+        const int sub = j & 3, blk = (j >> 2) & 7, uc = j >> 5;
+        const int u = uc / nchw, c = uc - u * nchw;
+        float v[8] = {hv[i][0].x, hv[i][0].y, hv[i][0].z, hv[i][0].w,
+                      hv[i][1].x, hv[i][1].y, hv[i][1].z, hv[i][1].w};
+        uint2 pl[4];
+        const int e = block_planes(v, pl);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          *reinterpret_cast<uint2 *>(apl + ((u * CPW + c) * 4 + p) * 256 + blk * 32 + sub * 8) =
+              pl[p];
+        if (sub == 0) aex[(u * CPW + c) * 8 + blk] = e;
+      }
+    }
+  }
+  lds_barrier();
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // step s from slot k, which then takes step s + kMxDownDepth
+  auto run = [&](int k, int s) __attribute__((always_inline)) {
+    const int j = s / units, u = s - j * units;
+    int sw[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) sw[c] = scale_of(rsd[k], c, lane, q);
+    uint4 w[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) w[c] = rw[k][c];
+    if (s + kMxDownDepth < total) load(k, s + kMxDownDepth);
+    step_fence();
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      if (c < nchw) {
+        const uint8_t *pp = apl + ((u * CPW + c) * 4 + aj) * 256 + 128 * ah + 16 * q;
+        const uint4 lo = *reinterpret_cast<const uint4 *>(pp);
+        const uint4 hi = *reinterpret_cast<const uint4 *>(pp + 64);
+        const int ea = aex[(u * CPW + c) * 8 + 4 * ah + q];
+        const i32x8 av = arow ? i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x),
+                                      int(hi.y), int(hi.z), int(hi.w)}
+                              : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        // each block product summed in fp32 here, not in the matrix core's
+        // accumulator (which keeps about 2^-15 of its largest term)
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc += mfma_mx(av, w[c], z, arow ? ea - 4 * aj + 127 : 127, sw[c]);
+      }
+    if (u == units - 1) {
+      const float v = fold_item(acc, lane);
+      if (lane < 8) red[j][wave][lane] = v;
+      acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  for (int s = 0; s < total; s += kMxDownDepth) {
+#pragma unroll
+    for (int i = 0; i < kMxDownDepth; ++i)
+      if (s + i < total) run(i, s + i);
+  }
+  lds_barrier();
+  for (int i = threadIdx.x; i < nj * 8; i += blockDim.x) {
+    const int j = i >> 3, rr = i & 7;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMxWaves; ++w) v += red[j][w][rr];
+    a.y[(size_t(blockIdx.x) + size_t(j) * gridDim.x) * 8 + rr] = v;
+    if (a.status && !__builtin_isfinite(v)) atomicOr(a.status, COLI_STATUS_NONFINITE);
+  }
+}
+
 }  // namespace
 
 bool mx_gateup_ok(const FmtLayer &L, const float *x, int T) {
   const int units = (L.E < T * L.K ? L.E : T * L.K) + 1;
   return L.fmt == COLI_FMT_MXFP4 && T >= 1 && T <= 2 && L.H % 256 == 0 &&
-         L.H <= 256 * kMxWaves * kMxMaxCpw && L.I % 8 == 0 && L.I / 8 <= 65535 &&
-         units <= kMxMaxItems && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
-         L.q_off[0] % 16 == 0 && L.q_off[1] % 16 == 0 && L.blob_bytes % 16 == 0;
+         L.H <= 256 * kMxWaves * kMxMaxCpw && L.I % 8 == 0 && units <= kMxMaxItems &&
+         reinterpret_cast<uintptr_t>(x) % 16 == 0 && L.q_off[0] % 16 == 0 &&
+         L.q_off[1] % 16 == 0 && L.s_off[0] % 4 == 0 && L.s_off[1] % 4 == 0 &&
+         L.blob_bytes % 16 == 0;
+}
+
+bool mx_down_ok(const FmtLayer &L, int T) {
+  const int units = (L.E < L.K ? L.E : L.K) + 1;
+  const int cpw = (L.I / 256 + kMxWaves - 1) / kMxWaves;
+  return L.fmt == COLI_FMT_MXFP4 && T == 1 && L.I % 256 == 0 && cpw <= kMxMaxCpw &&
+         units * cpw <= kMxDownMaxUC && L.H % 8 == 0 && L.H / 8 <= 256 * kMxDownItems &&
+         L.q_off[2] % 16 == 0 && L.s_off[2] % 4 == 0 && L.blob_bytes % 16 == 0;
 }
 
 hipError_t launch_mx_gateup(const FmtLayer &L, const Routing &r, const float *x, int T, float *h,
@@ -299,14 +523,58 @@ hipError_t launch_mx_gateup(const FmtLayer &L, const Routing &r, const float *x,
   a.I = L.I;
   a.K = L.K;
   const dim3 grid(unsigned(L.I / 8)), block(64 * kMxWaves);
-  const int cpw = (L.H / 256 + kMxWaves - 1) / kMxWaves;
-  switch (cpw) {
+  switch ((L.H / 256 + kMxWaves - 1) / kMxWaves) {
     case 1: mx_gateup<1><<<grid, block, 0, s>>>(a); break;
     case 2: mx_gateup<2><<<grid, block, 0, s>>>(a); break;
     case 3: mx_gateup<3><<<grid, block, 0, s>>>(a); break;
     default: mx_gateup<4><<<grid, block, 0, s>>>(a); break;
   }
   return hipGetLastError();
+}
+
+template <int CPW>
+static hipError_t launch_down_t(const MxDownArgs &d, int G, hipStream_t s) {
+  static std::atomic<uint64_t> done{0};  // devices whose LDS attribute is set (bit per device)
+  const size_t lds = size_t(kMxWaves) * d.umax * mx_down_unit_bytes<CPW>();
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (!bit || !(done.load() & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mx_down<CPW>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            int(size_t(kMxWaves) * kMxDownMaxUC / CPW * mx_down_unit_bytes<CPW>()));
+    if (e != hipSuccess) return e;
+    done.fetch_or(bit);
+  }
+  mx_down<CPW><<<dim3(unsigned(G)), dim3(64 * kMxWaves), lds, s>>>(d);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_down(const FmtLayer &L, const Routing &r, const float *h, float *y,
+                          int32_t *status, hipStream_t s) {
+  MxDownArgs d;
+  d.experts = L.experts;
+  d.shared = L.shared;
+  d.blob_bytes = L.blob_bytes;
+  d.q_off = L.q_off[2];
+  d.s_off = L.s_off[2];
+  d.unique = r.unique;
+  d.n_unique = r.n_unique;
+  d.h = h;
+  d.y = y;
+  d.status = status;
+  d.H = L.H;
+  d.I = L.I;
+  d.umax = (L.E < L.K ? L.E : L.K) + 1;
+  const int groups = L.H / 8;  // at most 256 * kMxDownItems (mx_down_ok)
+  const int G = groups < 256 ? groups : 256;
+  switch ((L.I / 256 + kMxWaves - 1) / kMxWaves) {
+    case 1: return launch_down_t<1>(d, G, s);
+    case 2: return launch_down_t<2>(d, G, s);
+    case 3: return launch_down_t<3>(d, G, s);
+    default: return launch_down_t<4>(d, G, s);
+  }
 }
 
 }  // namespace coli

@@ -835,9 +835,12 @@ hipError_t launch_fmt_experts(const FmtLayer &L, const Routing &r, const float *
   a.s_off[0] = L.s_off[0];
   a.s_off[1] = L.s_off[1];
   size_t lds = size_t(T) * a.ldx * 4 + size_t(T) * a.chunks * 4;
-  hipError_t e = mx_gateup_ok(L, x, T) ? launch_mx_gateup(L, r, x, T, h, s)
-                                       : launch_matvec_fmt<kModeGateUp>(L.fmt, a, T, units, lds, s);
+  // MXFP4 with one or two tokens: the scaled matrix cores
+  const bool mxg = mx_gateup_ok(L, x, T);
+  hipError_t e = mxg ? launch_mx_gateup(L, r, x, T, h, s)
+                     : launch_matvec_fmt<kModeGateUp>(L.fmt, a, T, units, lds, s);
   if (e != hipSuccess) return e;
+  if (mxg && mx_down_ok(L, T)) return launch_mx_down(L, r, h, y, status, s);
   // down: rows are the H outputs, the row length I, x = h of the unit
   fmt_geometry(L.fmt, L.I, &cw, &a.row_bytes, &a.scale_cols);
   a.O = L.H;

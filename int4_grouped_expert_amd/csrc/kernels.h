@@ -204,13 +204,19 @@ bool fmt_layer_shape_ok(int fmt, int H, int I, int T);
 // part [units][T][H]; y [T][H] = their sum in unit order.
 hipError_t launch_fmt_experts(const FmtLayer &L, const Routing &r, const float *x, int T,
                               float *h, float *part, float *y, int32_t *status, hipStream_t s);
-// ---- ffn_mx.hip: the MXFP4 layer's gate/up on the scaled matrix cores ------
-// Whether it takes this call: MXFP4, T <= 2, H % 256 == 0 and H <= 8192,
-// I % 8 == 0, at most 40 units, x 16-byte aligned.
+// ---- ffn_mx.hip: an MXFP4 layer's experts on the scaled matrix cores ------
+// Whether the gate/up takes this call (MXFP4, T <= 2, H % 256 == 0 and
+// H <= 8192, I % 8 == 0, at most 40 units, x 16-byte aligned), and the down
+// (T == 1, I % 256 == 0, units x ceil(I / 2048) <= 18, H <= 8192).
 bool mx_gateup_ok(const FmtLayer &L, const float *x, int T);
+bool mx_down_ok(const FmtLayer &L, int T);
 // h [units][T][I] as launch_fmt_experts defines it.
 hipError_t launch_mx_gateup(const FmtLayer &L, const Routing &r, const float *x, int T, float *h,
                             hipStream_t s);
+// One token: y [H] from h [units][I] (status: COLI_STATUS_NONFINITE for a
+// non-finite output).
+hipError_t launch_mx_down(const FmtLayer &L, const Routing &r, const float *h, float *y,
+                          int32_t *status, hipStream_t s);
 
 // Copy the batch union (r.unique [E], r.n_unique) to caller buffers (either
 // may be NULL).

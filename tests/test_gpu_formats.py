@@ -12,9 +12,10 @@
   int3) per group: fp32 cancellation of about one decimal digit), next to the
   decode tolerance 2e-3 * max(1, rms);
 * the layer with its experts in each format against the oracle's fp64 layer, with
-  the same bars, except the MXFP4 layer's gate/up on the scaled matrix cores
-  (T <= 2, H a multiple of 256): 1e-4, as those sum each 128-term block product
-  with about 2^-15 of its largest term (measured against a host product), well
+  the same bars, except the MXFP4 layer on the scaled matrix cores (gate/up for
+  T <= 2, down for T = 1, H a multiple of 256): 2e-4, as those sum each 128-term
+  block product with about 2^-15 of its largest term (measured against a host
+  product; worst seen 7.4e-5 over the two matrix-core products), ten times
   inside the decode tolerance.
 Page "从源码开始colibri纯C引擎的编译、权重转换与.bin直映射实战", section 权重转换 (the
 registry); OCP MX v1.0 and OCP FP8 for the element formats.
@@ -31,7 +32,7 @@ pytestmark = pytest.mark.gpu
 FMTS = (5, 7, 8)
 NAMES = {4: "int4-g64", 5: "int3-g64", 7: "mxfp4", 8: "fp8-e4m3-b128"}
 TIGHT = {4: 1e-4, 5: 1e-4, 7: 2e-5, 8: 2e-5}
-MX_MFMA_TIGHT = 1e-4  # the MXFP4 layer's gate/up on the scaled matrix cores
+MX_MFMA_TIGHT = 2e-4  # the MXFP4 layer on the scaled matrix cores
 
 
 def weights(O, I, seed, spread=False):
