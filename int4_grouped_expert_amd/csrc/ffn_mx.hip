@@ -120,6 +120,28 @@ __device__ inline f32x4 mfma_mx(const i32x8 &a, const uint4 &b, const f32x4 &c, 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 0, 4, 0, sa, 0, sb);
 }
 
+// fp8-e4m3-b128 weights: B E4M3 (format 0) with the neutral E8M0 scale; the
+// tile's f32 scale is applied to the product afterwards
+__device__ inline f32x4 mfma_f8(const i32x8 &a, const uint4 &b0, const uint4 &b1, int sa) {
+  const i32x8 bb = {int(b0.x), int(b0.y), int(b0.z), int(b0.w),
+                    int(b1.x), int(b1.y), int(b1.z), int(b1.w)};
+  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, z, 0, 0, 0, sa, 0, 127);
+}
+
+// The weight side of a format, per 256-element chunk of a row: its bytes,
+// the 16-byte loads of a lane (B column n = r + 8 h, quarter q; load i at
+// byte 64 i further on) and where the first one starts.  MXFP4: one MX block
+// (elements 128 h + 32 q ..); E4M3 (B holds k = 16 q .. and 64 + 16 q ..):
+// elements 128 h + 16 q .. and 128 h + 64 + 16 q ...
+template <int FMT>
+struct Wt {
+  static constexpr bool kMx = FMT == COLI_FMT_MXFP4;
+  static constexpr int kChunkBytes = kMx ? 128 : 256;
+  static constexpr int kLoads = kMx ? 1 : 2;
+  __device__ static int off(int hh, int q) { return (kMx ? 64 : 128) * hh + 16 * q; }
+};
+
 // The exponent e of a 32-element block (its largest |x| times 2^-e in
 // [64, 128), kept >= -115 so that the last plane's scale 2^(e - 12) is an
 // E8M0 value) and the four E4M3 planes of this lane's 8 elements.  The block
@@ -167,14 +189,22 @@ __device__ inline int scale_of(uint32_t dw, int c, int lane, int q) {
   return int((v >> (8 * q)) & 0xFFu);
 }
 
-template <int CPW>
+template <int FMT, int CPW>
 struct GuSlot {
-  uint4 wg[CPW], wu[CPW];
-  uint32_t sdg, sdu;
+  uint4 wg[CPW][Wt<FMT>::kLoads], wu[CPW][Wt<FMT>::kLoads];
+  uint32_t sdg, sdu;     // MXFP4: the row slice's scale dwords
+  float sfg[CPW], sfu[CPW];  // fp8: the chunks' tile scales
 };
 
-template <int CPW>
+// fp8 tile scale of chunk c0 + c, column half h, for rows of tile row rt:
+// tiles [rows / 128][K / 128], two per chunk
+__device__ inline float tile_scale(const uint8_t *sec, size_t rt, int ktiles, int c, int hh) {
+  return reinterpret_cast<const float *>(sec)[rt * ktiles + 2 * c + hh];
+}
+
+template <int FMT, int CPW>
 __global__ __launch_bounds__(64 * kMxWaves) void mx_gateup(MxArgs a) {
+  using W = Wt<FMT>;
   // the prologue's planes of x and the loop's partials share the LDS
   constexpr int kPlaneBytes = kMxWaves * 2 * 4 * CPW * 256;
   constexpr int kRedBytes = kMxMaxItems * kMxWaves * 2 * 2 * 8 * 4;
@@ -192,24 +222,38 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_gateup(MxArgs a) {
   const int n = lane & 15, q = lane >> 4;
   const int r = n & 7, hh = n >> 3;
   const size_t row = size_t(blockIdx.x) * 8 + r;
-  const size_t woff = row * size_t(H / 2) + size_t(c0) * 128 + 64 * hh + 16 * q;
-  const size_t soff = row * size_t(H / 32) + size_t(c0) * 8;
+  const size_t woff = row * size_t(H / 256) * W::kChunkBytes + size_t(c0) * W::kChunkBytes +
+                      W::off(hh, q);
+  const size_t soff = row * size_t(H / 32) + size_t(c0) * 8;  // MXFP4 scale slice
+  const size_t rt = row >> 7;                                 // fp8 tile row
+  const int ktiles = H / 128;
 
-  auto load = [&](GuSlot<CPW> &sl, const uint8_t *b) __attribute__((always_inline)) {
+  auto load = [&](GuSlot<FMT, CPW> &sl, const uint8_t *b) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
       if (c < nchw) {
-        sl.wg[c] = *reinterpret_cast<const uint4 *>(b + a.q_off[0] + woff + 128 * c);
-        sl.wu[c] = *reinterpret_cast<const uint4 *>(b + a.q_off[1] + woff + 128 * c);
+#pragma unroll
+        for (int i = 0; i < W::kLoads; ++i) {
+          sl.wg[c][i] = *reinterpret_cast<const uint4 *>(b + a.q_off[0] + woff +
+                                                         W::kChunkBytes * c + 64 * i);
+          sl.wu[c][i] = *reinterpret_cast<const uint4 *>(b + a.q_off[1] + woff +
+                                                         W::kChunkBytes * c + 64 * i);
+        }
+        if constexpr (!W::kMx) {
+          sl.sfg[c] = tile_scale(b + a.s_off[0], rt, ktiles, c0 + c, hh);
+          sl.sfu[c] = tile_scale(b + a.s_off[1], rt, ktiles, c0 + c, hh);
+        }
       }
-    if (nchw > 0) {
-      sl.sdg = scale_dword(b + a.s_off[0] + soff, nchw, hh, q);
-      sl.sdu = scale_dword(b + a.s_off[1] + soff, nchw, hh, q);
+    if constexpr (W::kMx) {
+      if (nchw > 0) {
+        sl.sdg = scale_dword(b + a.s_off[0] + soff, nchw, hh, q);
+        sl.sdu = scale_dword(b + a.s_off[1] + soff, nchw, hh, q);
+      }
     }
   };
   // items: 0 the shared expert (its loads leave first), k >= 1 unit k - 1;
   // a ring of two items in flight
-  GuSlot<CPW> s0, s1;
+  GuSlot<FMT, CPW> s0, s1;
   load(s0, a.shared);
   const int nu = *a.n_unique;
   const int nitems = nu + 1;
@@ -263,32 +307,59 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_gateup(MxArgs a) {
   lds_barrier();  // the planes' LDS becomes the partials'
 
   // item k from slot sl, which then takes item k + 2
-  auto run = [&](GuSlot<CPW> &sl, int k) __attribute__((always_inline)) {
+  auto run = [&](GuSlot<FMT, CPW> &sl, int k) __attribute__((always_inline)) {
     const bool more = k + 2 < nitems;
     const uint8_t *nb = sblob[more ? k + 2 : k];
     f32x4 accg = {0.0f, 0.0f, 0.0f, 0.0f}, accu = {0.0f, 0.0f, 0.0f, 0.0f};
+    // consume the slot (scales first), then refill it
     int scg[CPW], scu[CPW];
+    float sfg[CPW], sfu[CPW];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      scg[c] = scale_of(sl.sdg, c, lane, q);
-      scu[c] = scale_of(sl.sdu, c, lane, q);
+      if constexpr (W::kMx) {
+        scg[c] = scale_of(sl.sdg, c, lane, q);
+        scu[c] = scale_of(sl.sdu, c, lane, q);
+      } else {
+        sfg[c] = sl.sfg[c];
+        sfu[c] = sl.sfu[c];
+      }
     }
-    if (more && nchw > 0) {
-      sl.sdg = scale_dword(nb + a.s_off[0] + soff, nchw, hh, q);
-      sl.sdu = scale_dword(nb + a.s_off[1] + soff, nchw, hh, q);
+    if constexpr (W::kMx) {
+      if (more && nchw > 0) {
+        sl.sdg = scale_dword(nb + a.s_off[0] + soff, nchw, hh, q);
+        sl.sdu = scale_dword(nb + a.s_off[1] + soff, nchw, hh, q);
+      }
     }
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       if (c < nchw) {
-        // consume the slot, then refill it
-        const uint4 bg = sl.wg[c], bu = sl.wu[c];
+        uint4 bg[W::kLoads], bu[W::kLoads];
+#pragma unroll
+        for (int i = 0; i < W::kLoads; ++i) {
+          bg[i] = sl.wg[c][i];
+          bu[i] = sl.wu[c][i];
+        }
         if (more) {
-          sl.wg[c] = *reinterpret_cast<const uint4 *>(nb + a.q_off[0] + woff + 128 * c);
-          sl.wu[c] = *reinterpret_cast<const uint4 *>(nb + a.q_off[1] + woff + 128 * c);
+#pragma unroll
+          for (int i = 0; i < W::kLoads; ++i) {
+            sl.wg[c][i] = *reinterpret_cast<const uint4 *>(nb + a.q_off[0] + woff +
+                                                           W::kChunkBytes * c + 64 * i);
+            sl.wu[c][i] = *reinterpret_cast<const uint4 *>(nb + a.q_off[1] + woff +
+                                                           W::kChunkBytes * c + 64 * i);
+          }
+          if constexpr (!W::kMx) {
+            sl.sfg[c] = tile_scale(nb + a.s_off[0], rt, ktiles, c0 + c, hh);
+            sl.sfu[c] = tile_scale(nb + a.s_off[1], rt, ktiles, c0 + c, hh);
+          }
         }
         step_fence();
-        accg = mfma_mx(A[c], bg, accg, sA[c], scg[c]);
-        accu = mfma_mx(A[c], bu, accu, sA[c], scu[c]);
+        if constexpr (W::kMx) {
+          accg = mfma_mx(A[c], bg[0], accg, sA[c], scg[c]);
+          accu = mfma_mx(A[c], bu[0], accu, sA[c], scu[c]);
+        } else {
+          accg += sfg[c] * mfma_f8(A[c], bg[0], bg[1], sA[c]);
+          accu += sfu[c] * mfma_f8(A[c], bu[0], bu[1], sA[c]);
+        }
       }
     }
     const float vg = fold_item(accg, lane), vu = fold_item(accu, lane);
@@ -328,13 +399,15 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_gateup(MxArgs a) {
 // its 8 waves split the 256-element chunks of I.  The gate weights are in h,
 // so the combine over units is the accumulation itself, in unit order.  Each
 // wave first turns its chunks of every unit's h into E4M3 planes in its own
-// LDS area (the h loads of all its passes issued first); the weight blocks of
-// the first steps are in flight meanwhile; then a ring of up to
-// 8 steps.
+// LDS area (the h loads of all its passes issued first, then the weight
+// blocks of the first steps, which stream in meanwhile); then a ring of up
+// to 8 steps.
 constexpr int kMxDownItems = 4;
 // steps in flight per wave: 8 KB of weight blocks at most
-template <int CPW>
-constexpr int mx_down_depth() { return 8 / CPW > 2 ? 8 / CPW : 2; }
+template <int FMT, int CPW>
+constexpr int mx_down_depth() {
+  return 8 / (CPW * Wt<FMT>::kLoads) > 2 ? 8 / (CPW * Wt<FMT>::kLoads) : 2;
+}
 constexpr int kMxDownMaxUC = 18;  // units x chunks per wave (the LDS area)
 constexpr int kMxDownPasses = kMxDownMaxUC * 32 / 64;
 
@@ -351,8 +424,9 @@ struct MxDownArgs {
 template <int CPW>
 constexpr int mx_down_unit_bytes() { return CPW * (4 * 256 + 8 * 4); }
 
-template <int CPW>
+template <int FMT, int CPW>
 __global__ __launch_bounds__(64 * kMxWaves) void mx_down(MxDownArgs a) {
+  using W = Wt<FMT>;
   extern __shared__ __align__(16) uint8_t dyn[];  // per wave: planes, then exponents
   __shared__ float red[kMxDownItems][kMxWaves][8];
   __shared__ const uint8_t *sblob[kMxMaxItems];
@@ -380,25 +454,33 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_down(MxDownArgs a) {
   const int total = nj * units;
 
   // the ring: kMxDownDepth steps in flight
-  constexpr int kMxDownDepth = mx_down_depth<CPW>();
-  uint4 rw[kMxDownDepth][CPW];
-  uint32_t rsd[kMxDownDepth];
+  constexpr int kMxDownDepth = mx_down_depth<FMT, CPW>();
+  uint4 rw[kMxDownDepth][CPW][W::kLoads];
+  uint32_t rsd[kMxDownDepth];     // MXFP4: the row slice's scale dword
+  float rsf[kMxDownDepth][CPW];   // fp8: the chunks' tile scales
+  const int ktiles = I / 128;
   auto load = [&](int k, int s) __attribute__((always_inline)) {
     const int j = s / units, u = s - j * units;
     const size_t row = (size_t(blockIdx.x) + size_t(j) * gridDim.x) * 8 + r;
     const uint8_t *b = sblob[u];
-    const uint8_t *wp = b + a.q_off + row * size_t(I / 2) + size_t(c0) * 128 + 64 * hh + 16 * q;
+    const uint8_t *wp = b + a.q_off + row * size_t(I / 256) * W::kChunkBytes +
+                        size_t(c0) * W::kChunkBytes + W::off(hh, q);
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
-      if (c < nchw) rw[k][c] = *reinterpret_cast<const uint4 *>(wp + 128 * c);
-    if (nchw > 0)
-      rsd[k] = scale_dword(b + a.s_off + row * size_t(I / 32) + size_t(c0) * 8, nchw, hh, q);
-  };
+      if (c < nchw) {
 #pragma unroll
-  for (int i = 0; i < kMxDownDepth; ++i)
-    if (i < total) load(i, i);
-
-  // planes of h over this wave's chunks of every unit: 4 lanes per 32-block
+        for (int i = 0; i < W::kLoads; ++i)
+          rw[k][c][i] = *reinterpret_cast<const uint4 *>(wp + W::kChunkBytes * c + 64 * i);
+        if constexpr (!W::kMx) rsf[k][c] = tile_scale(b + a.s_off, row >> 7, ktiles, c0 + c, hh);
+      }
+    if constexpr (W::kMx) {
+      if (nchw > 0)
+        rsd[k] = scale_dword(b + a.s_off + row * size_t(I / 32) + size_t(c0) * 8, nchw, hh, q);
+    }
+  };
+  // planes of h over this wave's chunks of every unit: 4 lanes per 32-block.
+  // The h loads go first, then the first steps' weight blocks, so that the
+  // conversion waits for h alone and runs while the weights stream in.
   {
     const int tasks = units * nchw * 32;
     float4 hv[kMxDownPasses][2];
@@ -414,6 +496,9 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_down(MxDownArgs a) {
         hv[i][1] = src[1];
       }
     }
+#pragma unroll
+    for (int i = 0; i < kMxDownDepth; ++i)
+      if (i < total) load(i, i);
 #pragma unroll
     for (int i = 0; i < kMxDownPasses; ++i) {
       const int j = lane + 64 * i;
@@ -439,11 +524,17 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_down(MxDownArgs a) {
   auto run = [&](int k, int s) __attribute__((always_inline)) {
     const int j = s / units, u = s - j * units;
     int sw[CPW];
+    float sf[CPW];
+    uint4 w[CPW][W::kLoads];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) sw[c] = scale_of(rsd[k], c, lane, q);
-    uint4 w[CPW];
+    for (int c = 0; c < CPW; ++c) {
+      if constexpr (W::kMx)
+        sw[c] = scale_of(rsd[k], c, lane, q);
+      else
+        sf[c] = rsf[k][c];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) w[c] = rw[k][c];
+      for (int i = 0; i < W::kLoads; ++i) w[c][i] = rw[k][c][i];
+    }
     if (s + kMxDownDepth < total) load(k, s + kMxDownDepth);
     step_fence();
 #pragma unroll
@@ -458,8 +549,13 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_down(MxDownArgs a) {
                               : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
         // each block product summed in fp32 here, not in the matrix core's
         // accumulator (which keeps about 2^-15 of its largest term)
-        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc += mfma_mx(av, w[c], z, arow ? ea - 4 * aj + 127 : 127, sw[c]);
+        const int sa = arow ? ea - 4 * aj + 127 : 127;
+        if constexpr (W::kMx) {
+          const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+          acc += mfma_mx(av, w[c][0], z, sa, sw[c]);
+        } else {
+          acc += sf[c] * mfma_f8(av, w[c][0], w[c][1], sa);
+        }
       }
     if (u == units - 1) {
       const float v = fold_item(acc, lane);
@@ -485,9 +581,11 @@ __global__ __launch_bounds__(64 * kMxWaves) void mx_down(MxDownArgs a) {
 
 }  // namespace
 
+static bool mx_fmt(int fmt) { return fmt == COLI_FMT_MXFP4 || fmt == COLI_FMT_FP8_E4M3_B128; }
+
 bool mx_gateup_ok(const FmtLayer &L, const float *x, int T) {
   const int units = (L.E < T * L.K ? L.E : T * L.K) + 1;
-  return L.fmt == COLI_FMT_MXFP4 && T >= 1 && T <= 2 && L.H % 256 == 0 &&
+  return mx_fmt(L.fmt) && T >= 1 && T <= 2 && L.H % 256 == 0 &&
          L.H <= 256 * kMxWaves * kMxMaxCpw && L.I % 8 == 0 && units <= kMxMaxItems &&
          reinterpret_cast<uintptr_t>(x) % 16 == 0 && L.q_off[0] % 16 == 0 &&
          L.q_off[1] % 16 == 0 && L.s_off[0] % 4 == 0 && L.s_off[1] % 4 == 0 &&
@@ -497,9 +595,19 @@ bool mx_gateup_ok(const FmtLayer &L, const float *x, int T) {
 bool mx_down_ok(const FmtLayer &L, int T) {
   const int units = (L.E < L.K ? L.E : L.K) + 1;
   const int cpw = (L.I / 256 + kMxWaves - 1) / kMxWaves;
-  return L.fmt == COLI_FMT_MXFP4 && T == 1 && L.I % 256 == 0 && cpw <= kMxMaxCpw &&
+  return mx_fmt(L.fmt) && T == 1 && L.I % 256 == 0 && cpw <= kMxMaxCpw &&
          units * cpw <= kMxDownMaxUC && L.H % 8 == 0 && L.H / 8 <= 256 * kMxDownItems &&
          L.q_off[2] % 16 == 0 && L.s_off[2] % 4 == 0 && L.blob_bytes % 16 == 0;
+}
+
+template <int FMT>
+static void launch_gateup_f(const MxArgs &a, int cpw, dim3 grid, dim3 block, hipStream_t s) {
+  switch (cpw) {
+    case 1: mx_gateup<FMT, 1><<<grid, block, 0, s>>>(a); break;
+    case 2: mx_gateup<FMT, 2><<<grid, block, 0, s>>>(a); break;
+    case 3: mx_gateup<FMT, 3><<<grid, block, 0, s>>>(a); break;
+    default: mx_gateup<FMT, 4><<<grid, block, 0, s>>>(a); break;
+  }
 }
 
 hipError_t launch_mx_gateup(const FmtLayer &L, const Routing &r, const float *x, int T, float *h,
@@ -523,16 +631,15 @@ hipError_t launch_mx_gateup(const FmtLayer &L, const Routing &r, const float *x,
   a.I = L.I;
   a.K = L.K;
   const dim3 grid(unsigned(L.I / 8)), block(64 * kMxWaves);
-  switch ((L.H / 256 + kMxWaves - 1) / kMxWaves) {
-    case 1: mx_gateup<1><<<grid, block, 0, s>>>(a); break;
-    case 2: mx_gateup<2><<<grid, block, 0, s>>>(a); break;
-    case 3: mx_gateup<3><<<grid, block, 0, s>>>(a); break;
-    default: mx_gateup<4><<<grid, block, 0, s>>>(a); break;
-  }
+  const int cpw = (L.H / 256 + kMxWaves - 1) / kMxWaves;
+  if (L.fmt == COLI_FMT_MXFP4)
+    launch_gateup_f<COLI_FMT_MXFP4>(a, cpw, grid, block, s);
+  else
+    launch_gateup_f<COLI_FMT_FP8_E4M3_B128>(a, cpw, grid, block, s);
   return hipGetLastError();
 }
 
-template <int CPW>
+template <int FMT, int CPW>
 static hipError_t launch_down_t(const MxDownArgs &d, int G, hipStream_t s) {
   static std::atomic<uint64_t> done{0};  // devices whose LDS attribute is set (bit per device)
   const size_t lds = size_t(kMxWaves) * d.umax * mx_down_unit_bytes<CPW>();
@@ -541,14 +648,24 @@ static hipError_t launch_down_t(const MxDownArgs &d, int G, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
   if (!bit || !(done.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mx_down<CPW>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mx_down<FMT, CPW>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             int(size_t(kMxWaves) * kMxDownMaxUC / CPW * mx_down_unit_bytes<CPW>()));
     if (e != hipSuccess) return e;
     done.fetch_or(bit);
   }
-  mx_down<CPW><<<dim3(unsigned(G)), dim3(64 * kMxWaves), lds, s>>>(d);
+  mx_down<FMT, CPW><<<dim3(unsigned(G)), dim3(64 * kMxWaves), lds, s>>>(d);
   return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_down_f(const MxDownArgs &d, int cpw, int G, hipStream_t s) {
+  switch (cpw) {
+    case 1: return launch_down_t<FMT, 1>(d, G, s);
+    case 2: return launch_down_t<FMT, 2>(d, G, s);
+    case 3: return launch_down_t<FMT, 3>(d, G, s);
+    default: return launch_down_t<FMT, 4>(d, G, s);
+  }
 }
 
 hipError_t launch_mx_down(const FmtLayer &L, const Routing &r, const float *h, float *y,
@@ -569,12 +686,9 @@ hipError_t launch_mx_down(const FmtLayer &L, const Routing &r, const float *h, f
   d.umax = (L.E < L.K ? L.E : L.K) + 1;
   const int groups = L.H / 8;  // at most 256 * kMxDownItems (mx_down_ok)
   const int G = groups < 256 ? groups : 256;
-  switch ((L.I / 256 + kMxWaves - 1) / kMxWaves) {
-    case 1: return launch_down_t<1>(d, G, s);
-    case 2: return launch_down_t<2>(d, G, s);
-    case 3: return launch_down_t<3>(d, G, s);
-    default: return launch_down_t<4>(d, G, s);
-  }
+  const int cpw = (L.I / 256 + kMxWaves - 1) / kMxWaves;
+  return L.fmt == COLI_FMT_MXFP4 ? launch_down_f<COLI_FMT_MXFP4>(d, cpw, G, s)
+                                 : launch_down_f<COLI_FMT_FP8_E4M3_B128>(d, cpw, G, s);
 }
 
 }  // namespace coli
