@@ -327,9 +327,11 @@ def _layer_cases():
     rejection (COLI_ESHAPE, no workspace) test_abi_cpu.py checks."""
     import workloads as W
     out = []
-    for cfg_id, T in [(107, 1), (107, 3), (116, 2), (119, 4), (1, 1), (1, 4)]:
+    for cfg_id, T in [(107, 1), (107, 3), (116, 2), (119, 4), (1, 1), (1, 2), (1, 4)]:
         c = W.CONFIGS[cfg_id]
         for fmt in (4,) + FMTS:
+            if (cfg_id, T) == (1, 2) and fmt not in (7, 8):
+                continue  # the full-size matrix-core gate/up with the generic down
             if fmt == 8 and (c["H"] % 16 or c["I"] % 16):
                 continue
             out.append((fmt, cfg_id, T))
@@ -346,3 +348,59 @@ def test_layer_in_format(fmt, cfg_id, T):
     x = margin_tokens(cfg_id, T, host_array(L.w_router), L.bias_np, c["K"])
     y, idx, gates = L.forward(x)
     oracle_fmt_check(L, x, y, idx, gates)
+
+
+def _forward_status(L, x):
+    """The format layer's forward with its status word returned (not asserted)."""
+    import int4_grouped_expert_amd as coli
+    T = x.shape[0]
+    ws = torch.empty(coli.coli_moe_fmt_workspace_bytes(L.layer_c, L.fmt, T),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.full((T, L.H), float("nan"), device="cuda")
+    idx = torch.empty((T, L.K), dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    coli.coli_moe_forward_fmt(L.layer_c, L.fmt, x, y, ws, idx, status=st)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), idx.cpu().numpy(), int(st.item())
+
+
+@pytest.mark.parametrize("fmt", (7, 8))
+def test_matrix_core_layer_nan_block(fmt):
+    """The matrix-core format layer (one token, H a multiple of 256) with one
+    gate block of an expert stored with the NaN scale (E8M0 255 for MXFP4, a NaN
+    tile scale for fp8): a token routed to that expert gets an all-NaN y and the
+    status bit COLI_STATUS_NONFINITE, as the oracle's fp64 layer says (the NaN
+    reaches every h' of that unit through its gate row, then every output through
+    the down); the same block in an expert the token did not pick changes nothing,
+    bit for bit.  The scale is restored afterwards."""
+    import workloads as W
+    from tests.harness import host_array, margin_tokens
+    c = W.CONFIGS[107]
+    log(f"matrix-core layer NaN block {NAMES[fmt]}")
+    L = fmt_layer(107, fmt)
+    x = margin_tokens(107, 1, host_array(L.w_router), L.bias_np, c["K"])
+    y0, idx, st0 = _forward_status(L, x)
+    assert st0 == 0 and np.isfinite(y0).all()
+    picked = int(idx[0, 0])
+    other = next(e for e in range(L.E) if e not in set(idx[0].tolist()))
+    a256 = lambda n: (n + 255) // 256 * 256
+    qbytes = [F.sizes(fmt, L.I, L.H)[0]] * 2 + [F.sizes(fmt, L.H, L.I)[0]]
+    gate_scales = sum(a256(n) for n in qbytes)  # the gate scale section of a blob
+    for e, expect_nan in ((other, False), (picked, True)):
+        base = e * L.nb + gate_scales
+        view = L.experts[base:base + 4]
+        keep = view.clone()
+        if fmt == 7:
+            view[0] = 255
+        else:
+            view.copy_(torch.tensor([0, 0, 0xC0, 0x7F], dtype=torch.uint8))  # NaN f32
+        try:
+            y, _, st = _forward_status(L, x)
+        finally:
+            view.copy_(keep)
+        if expect_nan:
+            assert np.isnan(y).all() and st & 1, (NAMES[fmt], st)
+        else:
+            assert st == 0 and np.array_equal(y, y0)
+    y1, _, st1 = _forward_status(L, x)
+    assert st1 == 0 and np.array_equal(y1, y0)
