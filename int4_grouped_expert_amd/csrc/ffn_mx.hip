@@ -1,15 +1,18 @@
-// ffn_mx.hip -- the experts of a decode layer stored in MXFP4, for one or two
-// tokens, on the gfx950 scaled matrix cores.
+// ffn_mx.hip -- the experts of a decode layer stored in MXFP4 or
+// fp8-e4m3-b128, for one or two tokens, on the gfx950 scaled matrix cores.
 //
 // Method: the expert FFN of page "Colibrì 深度解析" (sections 四 and 十一):
 // h = w_t * SiLU(x Wg^T) * (x Wu^T) per (unit, token), w_t the token's gate
 // weight for the unit (0 when it did not pick it, 1 for the shared expert);
 // the weights in the MXFP4 element format of section 十 (OCP Microscaling
-// v1.0: blocks of 32 E2M1 codes with one E8M0 power-of-two scale).
+// v1.0: blocks of 32 E2M1 codes with one E8M0 power-of-two scale) or as E4M3
+// codes with one f32 scale per 128 x 128 tile (OCP FP8).
 //
 // Arithmetic.  v_mfma_scale_f32_16x16x128_f8f6f4 multiplies an E4M3 A operand
-// by an E2M1 B operand and applies one E8M0 scale per 32 k on each side, so
-// the weight blocks enter exactly as stored, codes and scales.  The
+// by an E2M1 (or E4M3) B operand and applies one E8M0 scale per 32 k on each
+// side, so MXFP4 weight blocks enter exactly as stored, codes and scales; E4M3
+// codes enter with the neutral scale and each 128-k product is multiplied by
+// its tile's f32 scale in fp32.  The
 // activations enter as four E4M3 planes per 32-element block: with e the
 // block's exponent (its largest |x| times 2^-e lies in [64, 128)),
 // x 2^-e = p0 + p1 / 16 + p2 / 256 + p3 / 4096, each p the round-to-nearest-
